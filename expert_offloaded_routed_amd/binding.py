@@ -1,0 +1,337 @@
+"""ctypes binding of libmoe (include/moe.h): the same entry points, argument marshalling only.
+
+Every computation happens in the HIP library; this module converts torch tensors (device
+pointers), numpy arrays (host pointers), streams and events into C arguments and turns a
+non-OK status into an exception.  If libmoe.so is missing the import fails loudly: there is no
+other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_HIP = -3
+MOE_ERR_WORKSPACE = -4
+MOE_ERR_STATE = -5
+MOE_POLICY_LRU = 0
+MOE_POLICY_LFRU = 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func} failed with status {status}: {msg}")
+        self.status = status
+
+
+class moe_shape(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("inter", C.c_int32), ("n_experts", C.c_int32),
+                ("top_k", C.c_int32), ("n_slots", C.c_int32)]
+
+
+class moe_cache_config(C.Structure):
+    _fields_ = [("policy", C.c_int32), ("max_refills_per_step", C.c_int32),
+                ("lag_steps", C.c_int32), ("max_pending", C.c_int32),
+                ("decay_period", C.c_int32)]
+
+
+class moe_refill(C.Structure):
+    _fields_ = [("expert", C.c_int32), ("slot", C.c_int32), ("evicted", C.c_int32),
+                ("visible_step", C.c_int32)]
+
+
+class moe_cache_stats(C.Structure):
+    _fields_ = [("steps", C.c_int64), ("routes", C.c_int64), ("hits", C.c_int64),
+                ("refills", C.c_int64), ("evictions", C.c_int64)]
+
+
+_P = C.c_void_p
+_I32 = C.c_int32
+_SZ = C.c_size_t
+_SIGS = {
+    "moe_expert_image_bytes": [C.POINTER(moe_shape), C.POINTER(_SZ)],
+    "moe_pack_expert": [C.POINTER(moe_shape)] + [_P] * 7,
+    "moe_unpack_expert": [C.POINTER(moe_shape)] + [_P] * 7,
+    "moe_workspace_size": [C.POINTER(moe_shape), _I32, C.POINTER(_SZ)],
+    "moe_workspace_init": [C.POINTER(moe_shape), _P, _SZ, _P],
+    "moe_route": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _SZ, _P],
+    "moe_bucket_routes": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+    "moe_experts_forward": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                            _SZ, _P],
+    "moe_experts_gateup": [C.POINTER(moe_shape), _P, _I32, _P, _P, _SZ, _P],
+    "moe_experts_down": [C.POINTER(moe_shape), _I32, _P, _P, _P, _P, _SZ, _P],
+    "moe_slot_refill": [C.POINTER(moe_shape), _P, _P, _P, _P, _I32, _P, _P, _P],
+    "moe_cache_create": [C.POINTER(moe_shape), C.POINTER(moe_cache_config), _P,
+                         C.POINTER(_P)],
+    "moe_cache_policy_step": [_P, C.c_int64, _P, _I32, _P, C.POINTER(_I32), _P,
+                              C.POINTER(moe_cache_stats)],
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libmoe.so (once).  Raises if the library has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m expert_offloaded_routed_amd._build`")
+    lib = C.CDLL(path)
+    for name, argtypes in _SIGS.items():
+        f = getattr(lib, name)
+        f.argtypes = argtypes
+        f.restype = C.c_int
+    lib.moe_cache_destroy.argtypes = [_P]
+    lib.moe_cache_destroy.restype = None
+    lib.moe_last_error.argtypes = []
+    lib.moe_last_error.restype = C.c_char_p
+    _lib = lib
+    return lib
+
+
+def moe_last_error() -> str:
+    return load().moe_last_error().decode()
+
+
+def _check(status: int, func: str):
+    if status != MOE_OK:
+        raise MoeError(status, func, moe_last_error())
+
+
+# ---------------------------------------------------------------------------------------------
+# argument conversion
+# ---------------------------------------------------------------------------------------------
+def _ptr(a):
+    """torch tensor -> data_ptr, numpy array -> host address, int -> itself, None -> NULL."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    if isinstance(a, np.ndarray):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("numpy argument must be C-contiguous")
+        return a.ctypes.data
+    dp = getattr(a, "data_ptr", None)
+    if dp is not None:
+        if not a.is_contiguous():
+            raise ValueError("tensor argument must be contiguous")
+        return dp()
+    raise TypeError(f"cannot pass {type(a)} as a pointer")
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _nbytes(a):
+    if isinstance(a, np.ndarray):
+        return a.nbytes
+    return a.numel() * a.element_size()
+
+
+def make_shape(hidden, inter, n_experts, top_k, n_slots) -> moe_shape:
+    return moe_shape(hidden, inter, n_experts, top_k, n_slots)
+
+
+# ---------------------------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------------------------
+def moe_expert_image_bytes(shape: moe_shape) -> int:
+    out = _SZ(0)
+    _check(load().moe_expert_image_bytes(C.byref(shape), C.byref(out)), "moe_expert_image_bytes")
+    return out.value
+
+
+def moe_pack_expert(shape: moe_shape, expert: dict, image: np.ndarray | None = None) -> np.ndarray:
+    """Canonical MXFP4 dict (gate/up/down codes+scales, numpy uint8) -> image (numpy uint8)."""
+    n = moe_expert_image_bytes(shape)
+    if image is None:
+        image = np.empty(n, dtype=np.uint8)
+    if image.nbytes < n:
+        raise ValueError("image buffer too small")
+    args = [np.ascontiguousarray(expert[k], dtype=np.uint8) for k in
+            ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")]
+    _check(load().moe_pack_expert(C.byref(shape), *[_ptr(a) for a in args], _ptr(image)),
+           "moe_pack_expert")
+    return image
+
+
+def moe_unpack_expert(shape: moe_shape, image: np.ndarray) -> dict:
+    H, I = shape.hidden, shape.inter
+    out = {"gate_codes": np.empty((I, H // 2), np.uint8), "gate_scales": np.empty((I, H // 32), np.uint8),
+           "up_codes": np.empty((I, H // 2), np.uint8), "up_scales": np.empty((I, H // 32), np.uint8),
+           "down_codes": np.empty((H, I // 2), np.uint8), "down_scales": np.empty((H, I // 32), np.uint8)}
+    _check(load().moe_unpack_expert(C.byref(shape), _ptr(np.ascontiguousarray(image)),
+                                    *[_ptr(out[k]) for k in ("gate_codes", "gate_scales", "up_codes",
+                                                             "up_scales", "down_codes", "down_scales")]),
+           "moe_unpack_expert")
+    return out
+
+
+def moe_workspace_size(shape: moe_shape, max_M: int) -> int:
+    out = _SZ(0)
+    _check(load().moe_workspace_size(C.byref(shape), int(max_M), C.byref(out)), "moe_workspace_size")
+    return out.value
+
+
+def moe_workspace_init(shape, ws, stream=None):
+    _check(load().moe_workspace_init(C.byref(shape), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_workspace_init")
+
+
+def moe_route(shape, x, M, w_router, router_bias, topk_ids, topk_w, ws, stream=None):
+    _check(load().moe_route(C.byref(shape), _ptr(x), int(M), _ptr(w_router), _ptr(router_bias),
+                            _ptr(topk_ids), _ptr(topk_w), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_route")
+
+
+def moe_bucket_routes(shape, topk_ids, M, expert_to_slot, counts, offsets, perm, cold_count,
+                      cold_routes, ws, stream=None):
+    _check(load().moe_bucket_routes(C.byref(shape), _ptr(topk_ids), int(M), _ptr(expert_to_slot),
+                                    _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(cold_count),
+                                    _ptr(cold_routes), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_bucket_routes")
+
+
+def moe_experts_forward(shape, x, M, topk_ids, topk_w, expert_to_slot, slots, y, cold_count,
+                        cold_routes, ws, stream=None):
+    _check(load().moe_experts_forward(C.byref(shape), _ptr(x), int(M), _ptr(topk_ids),
+                                      _ptr(topk_w), _ptr(expert_to_slot), _ptr(slots), _ptr(y),
+                                      _ptr(cold_count), _ptr(cold_routes), _ptr(ws), _nbytes(ws),
+                                      _stream(stream)),
+           "moe_experts_forward")
+
+
+def moe_experts_gateup(shape, x, M, slots, ws, stream=None):
+    _check(load().moe_experts_gateup(C.byref(shape), _ptr(x), int(M), _ptr(slots), _ptr(ws),
+                                     _nbytes(ws), _stream(stream)), "moe_experts_gateup")
+
+
+def moe_experts_down(shape, M, topk_w, slots, y, ws, stream=None):
+    _check(load().moe_experts_down(C.byref(shape), int(M), _ptr(topk_w), _ptr(slots), _ptr(y),
+                                   _ptr(ws), _nbytes(ws), _stream(stream)), "moe_experts_down")
+
+
+def moe_slot_refill(shape, slots, host_bank, experts, slot_ids, copy_stream=None,
+                    wait_before=None, done=None):
+    ex = np.ascontiguousarray(experts, dtype=np.int32)
+    sl = np.ascontiguousarray(slot_ids, dtype=np.int32)
+    if ex.shape != sl.shape:
+        raise ValueError("experts and slot_ids differ in length")
+    _check(load().moe_slot_refill(C.byref(shape), _ptr(slots), _ptr(host_bank), _ptr(ex), _ptr(sl),
+                                  int(ex.size), _stream(copy_stream), wait_before, done),
+           "moe_slot_refill")
+
+
+class MoeCache:
+    """Owns one moe_cache object (host-only policy state for one layer)."""
+
+    def __init__(self, shape: moe_shape, policy=MOE_POLICY_LRU, max_refills_per_step=2,
+                 lag_steps=1, max_pending=2, decay_period=64, initial_slot_expert=None):
+        self.shape = shape
+        cfg = moe_cache_config(policy, max_refills_per_step, lag_steps, max_pending, decay_period)
+        init = None
+        if initial_slot_expert is not None:
+            init = np.ascontiguousarray(initial_slot_expert, dtype=np.int32)
+            if init.size != shape.n_slots:
+                raise ValueError("initial_slot_expert must have n_slots entries")
+        h = _P()
+        _check(load().moe_cache_create(C.byref(shape), C.byref(cfg), _ptr(init), C.byref(h)),
+               "moe_cache_create")
+        self._h = h
+        self._plan = (moe_refill * max(1, max_refills_per_step))()
+        self._map = np.empty(shape.n_experts, dtype=np.int32)
+
+    def moe_cache_policy_step(self, step: int, topk_ids=None):
+        """Returns (expert_to_slot int32 [E], [(expert, slot, evicted, visible_step)], stats dict)."""
+        ids = None if topk_ids is None else np.ascontiguousarray(topk_ids, dtype=np.int32)
+        M = 0 if ids is None else ids.size // self.shape.top_k
+        n = _I32(0)
+        st = moe_cache_stats()
+        _check(load().moe_cache_policy_step(self._h, int(step), _ptr(ids), M, C.addressof(self._plan),
+                                            C.byref(n), _ptr(self._map), C.byref(st)),
+               "moe_cache_policy_step")
+        plan = [(p.expert, p.slot, p.evicted, p.visible_step) for p in self._plan[: n.value]]
+        stats = {f: getattr(st, f) for f, _ in moe_cache_stats._fields_}
+        return self._map.copy(), plan, stats
+
+    def close(self):
+        if self._h:
+            load().moe_cache_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------------------------------------
+# HIP events (plumbing for refill ordering and kernel timing)
+# ---------------------------------------------------------------------------------------------
+_hip = None
+
+
+def hip():
+    global _hip
+    if _hip is None:
+        _hip = C.CDLL("libamdhip64.so")
+        _hip.hipEventCreateWithFlags.argtypes = [C.POINTER(_P), C.c_uint]
+        _hip.hipEventRecord.argtypes = [_P, _P]
+        _hip.hipEventSynchronize.argtypes = [_P]
+        _hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), _P, _P]
+        _hip.hipEventDestroy.argtypes = [_P]
+        _hip.hipStreamWaitEvent.argtypes = [_P, _P, C.c_uint]
+        _hip.hipEventQuery.argtypes = [_P]
+    return _hip
+
+
+def _hipcheck(err, what):
+    if err != 0:
+        raise RuntimeError(f"{what} failed with HIP error {err}")
+
+
+def event_create(timing: bool = False) -> int:
+    ev = _P()
+    _hipcheck(hip().hipEventCreateWithFlags(C.byref(ev), 0 if timing else 2), "hipEventCreateWithFlags")
+    return ev.value
+
+
+def event_record(ev: int, stream=None):
+    _hipcheck(hip().hipEventRecord(ev, _stream(stream)), "hipEventRecord")
+
+
+def event_synchronize(ev: int):
+    _hipcheck(hip().hipEventSynchronize(ev), "hipEventSynchronize")
+
+
+def event_done(ev: int) -> bool:
+    return hip().hipEventQuery(ev) == 0
+
+
+def event_elapsed_ms(start: int, stop: int) -> float:
+    ms = C.c_float(0)
+    _hipcheck(hip().hipEventElapsedTime(C.byref(ms), start, stop), "hipEventElapsedTime")
+    return ms.value
+
+
+def event_destroy(ev: int):
+    hip().hipEventDestroy(ev)
+
+
+def stream_wait_event(stream, ev: int):
+    _hipcheck(hip().hipStreamWaitEvent(_stream(stream), ev, 0), "hipStreamWaitEvent")

@@ -1,0 +1,222 @@
+// Slot-cache policy (host only): LRU / LFRU victims, bounded refills per step, fixed-lag
+// visibility.  The rules are spelled out in include/moe.h (moe_cache_policy_step).
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace moe {
+moe_status fail(moe_status st, const char* fmt, ...);
+moe_status ok();
+moe_status check_shape(const moe_shape* s);
+}  // namespace moe
+
+using namespace moe;
+
+struct moe_cache {
+  int E, S, K;
+  moe_cache_config cfg;
+  std::vector<int32_t> slot_expert;  // [S], -1 empty or being refilled
+  std::vector<int32_t> expert_slot;  // [E], -1 cold
+  std::vector<int64_t> last_use;     // [S], -1 never
+  std::vector<int64_t> freq;         // [E] (LFRU)
+  struct Pending {
+    int32_t expert, slot;
+    int64_t visible;
+  };
+  std::vector<Pending> pending;  // in planning order
+  moe_cache_stats stats;
+  int64_t last_step;
+  bool stepped;
+  // scratch
+  std::vector<int32_t> count;    // [E] routes of the observed step
+  std::vector<int32_t> touched;  // experts routed at this step
+  std::vector<uint8_t> used;     // [S]
+};
+
+static bool slot_pending(const moe_cache* c, int s) {
+  for (const auto& p : c->pending)
+    if (p.slot == s) return true;
+  return false;
+}
+
+static bool expert_pending(const moe_cache* c, int e) {
+  for (const auto& p : c->pending)
+    if (p.expert == e) return true;
+  return false;
+}
+
+static int choose_victim(const moe_cache* c) {
+  for (int s = 0; s < c->S; ++s)
+    if (c->slot_expert[s] < 0 && !slot_pending(c, s)) return s;
+  int best = -1;
+  int64_t bf = 0, bl = 0;
+  for (int s = 0; s < c->S; ++s) {
+    if (c->slot_expert[s] < 0 || c->used[s] || slot_pending(c, s)) continue;
+    const int64_t f = c->cfg.policy == MOE_POLICY_LFRU ? c->freq[c->slot_expert[s]] : 0;
+    const int64_t l = c->last_use[s];
+    // keys compare as (freq, last_use, slot); slot order is the scan order
+    if (best < 0 || f < bf || (f == bf && l < bl)) {
+      best = s;
+      bf = f;
+      bl = l;
+    }
+  }
+  return best;
+}
+
+extern "C" {
+
+moe_status moe_cache_create(const moe_shape* shape, const moe_cache_config* config,
+                            const int32_t* initial_slot_expert, moe_cache** out) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!config || !out) return fail(MOE_ERR_INVALID_ARG, "moe_cache_create: NULL config or out");
+  if (config->policy != MOE_POLICY_LRU && config->policy != MOE_POLICY_LFRU)
+    return fail(MOE_ERR_INVALID_ARG, "unknown policy %d", config->policy);
+  if (config->max_refills_per_step < 0 || config->lag_steps < 1 || config->max_pending < 1 ||
+      config->decay_period < 0)
+    return fail(MOE_ERR_INVALID_ARG, "cache config out of range (R=%d L=%d Q=%d decay=%d)",
+                config->max_refills_per_step, config->lag_steps, config->max_pending,
+                config->decay_period);
+  moe_cache* c = new moe_cache();
+  c->E = shape->n_experts;
+  c->S = shape->n_slots;
+  c->K = shape->top_k;
+  c->cfg = *config;
+  c->slot_expert.assign(c->S, -1);
+  c->expert_slot.assign(c->E, -1);
+  c->last_use.assign(c->S, -1);
+  c->freq.assign(c->E, 0);
+  c->count.assign(c->E, 0);
+  c->used.assign(c->S, 0);
+  memset(&c->stats, 0, sizeof(c->stats));
+  c->last_step = 0;
+  c->stepped = false;
+  if (initial_slot_expert) {
+    for (int s = 0; s < c->S; ++s) {
+      const int e = initial_slot_expert[s];
+      if (e < -1 || e >= c->E) {
+        delete c;
+        return fail(MOE_ERR_INVALID_ARG, "initial slot %d holds expert %d out of range", s, e);
+      }
+      if (e >= 0) {
+        if (c->expert_slot[e] >= 0) {
+          delete c;
+          return fail(MOE_ERR_INVALID_ARG, "expert %d placed twice", e);
+        }
+        c->slot_expert[s] = e;
+        c->expert_slot[e] = s;
+      }
+    }
+  }
+  *out = c;
+  return ok();
+}
+
+void moe_cache_destroy(moe_cache* cache) { delete cache; }
+
+moe_status moe_cache_policy_step(moe_cache* c, int64_t step, const int32_t* topk_ids, int32_t M,
+                                 moe_refill* plan, int32_t* n_plan, int32_t* expert_to_slot,
+                                 moe_cache_stats* stats) {
+  if (!c) return fail(MOE_ERR_INVALID_ARG, "cache is NULL");
+  if (!n_plan || !expert_to_slot)
+    return fail(MOE_ERR_INVALID_ARG, "n_plan and expert_to_slot are required");
+  if (M < 0) return fail(MOE_ERR_INVALID_ARG, "M < 0");
+  if (c->stepped && step <= c->last_step)
+    return fail(MOE_ERR_STATE, "step %lld does not follow step %lld", (long long)step,
+                (long long)c->last_step);
+  const bool observe = topk_ids != nullptr && M > 0;
+  const int n_routes = observe ? M * c->K : 0;
+  for (int r = 0; r < n_routes; ++r)
+    if (topk_ids[r] < 0 || topk_ids[r] >= c->E)
+      return fail(MOE_ERR_INVALID_ARG, "route %d: expert %d out of range", r, topk_ids[r]);
+  if (observe && !plan && c->cfg.max_refills_per_step > 0)
+    return fail(MOE_ERR_INVALID_ARG, "plan is NULL");
+  *n_plan = 0;
+  c->stepped = true;
+  c->last_step = step;
+
+  // 1. refills that become visible now
+  {
+    std::vector<moe_cache::Pending> keep;
+    for (const auto& p : c->pending) {
+      if (p.visible <= step) {
+        c->slot_expert[p.slot] = p.expert;
+        c->expert_slot[p.expert] = p.slot;
+      } else {
+        keep.push_back(p);
+      }
+    }
+    c->pending.swap(keep);
+  }
+  c->stats.steps += 1;
+
+  if (observe) {
+    // route counts of the observed step
+    c->touched.clear();
+    for (int r = 0; r < n_routes; ++r) {
+      const int e = topk_ids[r];
+      if (c->count[e]++ == 0) c->touched.push_back(e);
+    }
+    c->stats.routes += n_routes;
+    for (int r = 0; r < n_routes; ++r)
+      if (c->expert_slot[topk_ids[r]] >= 0) c->stats.hits += 1;
+    if (c->cfg.policy == MOE_POLICY_LFRU) {
+      if (c->cfg.decay_period > 0 && step > 0 && step % c->cfg.decay_period == 0)
+        for (auto& f : c->freq) f >>= 1;
+      for (int e : c->touched) c->freq[e] += c->count[e];
+    }
+    // 2. recency of the routed resident experts
+    std::fill(c->used.begin(), c->used.end(), 0);
+    for (int e : c->touched) {
+      const int s = c->expert_slot[e];
+      if (s >= 0) {
+        c->last_use[s] = step;
+        c->used[s] = 1;
+      }
+    }
+    // 3. admissions: cold, not in flight; by (count desc, id asc)
+    std::vector<int32_t> cands;
+    for (int e : c->touched)
+      if (c->expert_slot[e] < 0 && !expert_pending(c, e)) cands.push_back(e);
+    std::sort(cands.begin(), cands.end(), [c](int a, int b) {
+      return c->count[a] != c->count[b] ? c->count[a] > c->count[b] : a < b;
+    });
+    int admitted = 0;
+    for (int e : cands) {
+      if (admitted >= c->cfg.max_refills_per_step ||
+          (int)c->pending.size() >= c->cfg.max_pending)
+        break;
+      const int v = choose_victim(c);
+      if (v < 0) break;
+      const int old = c->slot_expert[v];
+      if (old >= 0) {
+        c->expert_slot[old] = -1;
+        c->stats.evictions += 1;
+      }
+      c->slot_expert[v] = -1;
+      c->last_use[v] = step;
+      const int64_t vis = step + c->cfg.lag_steps;
+      c->pending.push_back({e, v, vis});
+      plan[admitted].expert = e;
+      plan[admitted].slot = v;
+      plan[admitted].evicted = old;
+      plan[admitted].visible_step = (int32_t)vis;
+      ++admitted;
+      c->stats.refills += 1;
+    }
+    *n_plan = admitted;
+    for (int e : c->touched) c->count[e] = 0;
+  }
+  // 4. publish
+  memcpy(expert_to_slot, c->expert_slot.data(), sizeof(int32_t) * c->E);
+  if (stats) *stats = c->stats;
+  return ok();
+}
+
+}  // extern "C"

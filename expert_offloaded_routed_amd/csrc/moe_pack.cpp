@@ -1,0 +1,91 @@
+// Expert image packing: canonical MXFP4 matrices <-> the kernel layout described in
+// moe_internal.h.  Pure host code.
+#include <string.h>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+namespace moe {
+moe_status fail(moe_status st, const char* fmt, ...);
+moe_status ok();
+moe_status check_shape(const moe_shape* s);
+
+// Copy direction: pack (canonical -> image) or unpack (image -> canonical).
+template <bool PACK>
+static void tiles(uint8_t* img, int n_tiles, int rows_per_lane_group, int nb, int ng,
+                  size_t tile_bytes, uint8_t* const* codes, uint8_t* const* scales, int K) {
+  // rows_per_lane_group = 32 for gate/up (two matrices), 64 for down (one matrix)
+  const size_t row_code_bytes = (size_t)K / 2;
+  const size_t row_scale_bytes = (size_t)K / 32;
+  for (int t = 0; t < n_tiles; ++t) {
+    uint8_t* tb = img + (size_t)t * tile_bytes;
+    for (int lane = 0; lane < 64; ++lane) {
+      const int mat = rows_per_lane_group == 32 ? (lane >> 5) : 0;
+      const int row = t * rows_per_lane_group + (rows_per_lane_group == 32 ? (lane & 31) : lane);
+      uint8_t* c = codes[mat] + (size_t)row * row_code_bytes;
+      uint8_t* s = scales[mat] + (size_t)row * row_scale_bytes;
+      for (int b = 0; b < nb; ++b) {
+        uint8_t* dst = tb + ((size_t)b * 64 + lane) * 16;
+        if (PACK)
+          memcpy(dst, c + (size_t)b * 16, 16);
+        else
+          memcpy(c + (size_t)b * 16, dst, 16);
+      }
+      for (int q = 0; q < ng; ++q) {
+        uint8_t* dst = tb + (size_t)nb * 1024 + ((size_t)q * 64 + lane) * 4;
+        for (int i = 0; i < 4; ++i) {
+          const int b = 4 * q + i;
+          if (PACK)
+            dst[i] = b < nb ? s[b] : 127;
+          else if (b < nb)
+            s[b] = dst[i];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+moe_status moe_pack_expert(const moe_shape* shape, const uint8_t* gate_codes,
+                           const uint8_t* gate_scales, const uint8_t* up_codes,
+                           const uint8_t* up_scales, const uint8_t* down_codes,
+                           const uint8_t* down_scales, uint8_t* image) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!gate_codes || !gate_scales || !up_codes || !up_scales || !down_codes || !down_scales || !image)
+    return fail(MOE_ERR_INVALID_ARG, "moe_pack_expert: NULL pointer");
+  const ImageLayout L = image_layout(shape->hidden, shape->inter);
+  memset(image, 0, L.image_bytes);
+  uint8_t* gc[2] = {const_cast<uint8_t*>(gate_codes), const_cast<uint8_t*>(up_codes)};
+  uint8_t* gs[2] = {const_cast<uint8_t*>(gate_scales), const_cast<uint8_t*>(up_scales)};
+  tiles<true>(image, L.gu_tiles, 32, L.nb_h, L.ng_h, L.gu_tile_bytes, gc, gs, L.H);
+  uint8_t* dc[1] = {const_cast<uint8_t*>(down_codes)};
+  uint8_t* ds[1] = {const_cast<uint8_t*>(down_scales)};
+  tiles<true>(image + L.gu_bytes, L.dn_tiles, 64, L.nb_i, L.ng_i, L.dn_tile_bytes, dc, ds, L.I);
+  return ok();
+}
+
+moe_status moe_unpack_expert(const moe_shape* shape, const uint8_t* image, uint8_t* gate_codes,
+                             uint8_t* gate_scales, uint8_t* up_codes, uint8_t* up_scales,
+                             uint8_t* down_codes, uint8_t* down_scales) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!gate_codes || !gate_scales || !up_codes || !up_scales || !down_codes || !down_scales || !image)
+    return fail(MOE_ERR_INVALID_ARG, "moe_unpack_expert: NULL pointer");
+  const ImageLayout L = image_layout(shape->hidden, shape->inter);
+  uint8_t* img = const_cast<uint8_t*>(image);
+  uint8_t* gc[2] = {gate_codes, up_codes};
+  uint8_t* gs[2] = {gate_scales, up_scales};
+  tiles<false>(img, L.gu_tiles, 32, L.nb_h, L.ng_h, L.gu_tile_bytes, gc, gs, L.H);
+  uint8_t* dc[1] = {down_codes};
+  uint8_t* ds[1] = {down_scales};
+  tiles<false>(img + L.gu_bytes, L.dn_tiles, 64, L.nb_i, L.ng_i, L.dn_tile_bytes, dc, ds, L.I);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,244 @@
+/*
+ * moe.h -- C ABI of libmoe: one routed Mixture-of-Experts layer whose experts live in a GPU
+ * slot cache backed by pinned host memory, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (page title, section):
+ *   [MoE expert offload]  xinfer documentation "MoE expert offload": intro, "How it works",
+ *                         "Options", "Supported".
+ *   [ninfer v0.4.0]       "NInfer-Offload v0.4.0 -- expert cache: faster Flash-Next decode",
+ *                         section "New".
+ *   [ORT hybrid PR]       "[CUDA/CPU] Add hybrid GPU/CPU expert offload for MoEPacked
+ *                         block-packed weights", sections "Key Changes" and "Table A".
+ *   [tinyserve]           "tinyserve -- MoE Expert Offloading for Consumer GPUs", sections
+ *                         "How it works" and "Configuration".
+ *   [OCP MX v1.0]         OCP Microscaling Formats Specification v1.0 (MXFP4 = 32-element
+ *                         blocks of FP4 E2M1 values sharing one E8M0 scale).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked [host].  The caller allocates and owns every
+ *     buffer, stream and event; the library allocates no device memory.
+ *   - GPU calls only enqueue work on the given stream (asynchronous); none synchronises the
+ *     device.  Argument and shape errors are detected on the host before anything is enqueued
+ *     and leave every output untouched.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Every call returns a moe_status; moe_last_error() gives a message for the calling thread.
+ *   - Supported shapes: hidden % 64 == 0, inter % 32 == 0, 1 <= top_k <= min(n_experts, 32),
+ *     n_experts <= 1024, hidden <= 8192, n_slots >= 1.  x, w_router: 16-byte aligned;
+ *     slot arrays and workspaces: 256-byte aligned.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, bad size, out-of-range value */
+  MOE_ERR_UNSUPPORTED = -2, /* shape outside the supported set above */
+  MOE_ERR_HIP = -3,         /* a HIP runtime call failed (message has the HIP error) */
+  MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_workspace_size() */
+  MOE_ERR_STATE = -5        /* cache object used inconsistently (e.g. step not increasing) */
+} moe_status;
+
+/* Layer shape.  hidden = H, inter = I (per-expert intermediate size), n_experts = E,
+ * top_k = k, n_slots = S (GPU slots; S >= E means every expert can be resident). */
+typedef struct {
+  int32_t hidden;
+  int32_t inter;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t n_slots;
+} moe_shape;
+
+/* ---------------------------------------------------------------------------------------
+ * Expert images.  One expert = gate [I,H], up [I,H] and down [H,I] MXFP4 matrices
+ * [OCP MX v1.0].  Canonical layout (the caller's): row-major [N,K] with blocks of 32 along K;
+ * codes [N][K/2] with element 2c in the low nibble of byte c and 2c+1 in the high nibble;
+ * scales [N][K/32] as E8M0 bytes.  The library keeps each expert as one contiguous "image"
+ * in its own kernel layout, so that a GPU slot holds exactly one image and a refill from the
+ * pinned host bank is one copy [MoE expert offload, "How it works": the GEMMs read
+ * [num_slots, N, K] slot tensors].  Slot s of a slot array starts at s * image_bytes.
+ * --------------------------------------------------------------------------------------- */
+
+/* Bytes of one expert image (a multiple of 256).  [host] out. */
+moe_status moe_expert_image_bytes(const moe_shape* shape, size_t* bytes);
+
+/* Convert one expert from the canonical layout to its image.  All pointers [host]; the
+ * image buffer must hold moe_expert_image_bytes() bytes.  Pure host code. */
+moe_status moe_pack_expert(const moe_shape* shape,
+                           const uint8_t* gate_codes, const uint8_t* gate_scales,
+                           const uint8_t* up_codes, const uint8_t* up_scales,
+                           const uint8_t* down_codes, const uint8_t* down_scales,
+                           uint8_t* image);
+
+/* Inverse of moe_pack_expert (round-trip check, debugging).  All pointers [host]. */
+moe_status moe_unpack_expert(const moe_shape* shape, const uint8_t* image,
+                             uint8_t* gate_codes, uint8_t* gate_scales,
+                             uint8_t* up_codes, uint8_t* up_scales,
+                             uint8_t* down_codes, uint8_t* down_scales);
+
+/* ---------------------------------------------------------------------------------------
+ * Workspace.  One device buffer shared by moe_route / moe_bucket_routes /
+ * moe_experts_forward for calls with M <= max_M.  Its first bytes hold arrival counters that
+ * must be zero before the first call (allocate it zero-filled or call moe_workspace_init);
+ * every call leaves them at zero again.  Calls that share a workspace must be ordered on one
+ * stream; concurrent calls need separate workspaces.
+ * --------------------------------------------------------------------------------------- */
+moe_status moe_workspace_size(const moe_shape* shape, int32_t max_M, size_t* bytes /*[host]*/);
+
+/* Zero the workspace's counters with a fill kernel on `stream` (safe under graph capture). */
+moe_status moe_workspace_init(const moe_shape* shape, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Router [ninfer v0.4.0, "New": the router is no longer a single thread block;
+ * ORT hybrid PR, "Notes" 2: one fp32-accumulating router contract for any token count].
+ *   logits[m,e] = sum_h x[m,h] * W_r[e,h] + bias[e]   (bf16 inputs, fp32 accumulation)
+ *   then per token: the k largest logits (ties to the lower expert id), ordered by value
+ *   descending, and their softmax, which equals softmax over all E followed by top-k and
+ *   renormalisation.
+ * x [M,H] bf16; w_router [E,H] bf16 row-major; router_bias [E] fp32 or NULL (zero);
+ * topk_ids [M,k] int32 and topk_w [M,k] fp32 are written.  0 <= M <= max_M of the workspace;
+ * M = 0 enqueues nothing.
+ * --------------------------------------------------------------------------------------- */
+moe_status moe_route(const moe_shape* shape, const uint16_t* x, int32_t M,
+                     const uint16_t* w_router, const float* router_bias,
+                     int32_t* topk_ids, float* topk_w,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Route resolve and bucketing [ORT hybrid PR, "Key Changes": expert_to_slot, slot < 0 is
+ * cold; tinyserve, "How it works" item 6: group tokens by expert so that each expert is
+ * loaded once per call].
+ *   For each route r = m*k + j with expert e = topk_ids[r]:
+ *     slot = expert_to_slot ? expert_to_slot[e] : e;  cold iff slot < 0.
+ *   counts[e] = routes to e; offsets[e] = sum of counts below e (offsets[E] = M*k);
+ *   perm[offsets[e] .. offsets[e+1]) = the routes of e (order inside a bucket unspecified);
+ *   cold_count = number of cold routes; cold_routes = their r in ascending order.
+ * expert_to_slot [E] int32 or NULL (identity, needs E <= S).  Routes with an id outside
+ * [0,E) are cold and not bucketed; routes whose expert maps to a slot outside [-1,S) are
+ * cold (and bucketed).  counts [E], offsets [E+1],
+ * perm [M*k], cold_count [1], cold_routes [M*k] are written; any of them may be NULL.
+ * moe_experts_forward runs this step itself; the entry point exposes it on its own.
+ * --------------------------------------------------------------------------------------- */
+moe_status moe_bucket_routes(const moe_shape* shape, const int32_t* topk_ids, int32_t M,
+                             const int32_t* expert_to_slot,
+                             int32_t* counts, int32_t* offsets, int32_t* perm,
+                             int32_t* cold_count, int32_t* cold_routes,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Expert FFNs and combine over the slot cache [MoE expert offload, "How it works";
+ * ORT hybrid PR, "Key Changes"; tinyserve, "How it works" item 2: fused dequant + matmul
+ * on the native quantised weights, no bf16 weight copy].
+ *   For every hot route r = (m, j) with expert e in slot s:
+ *     g = Wg_e x_m, u = Wu_e x_m (fp32 accumulation over exactly decoded MXFP4 weights),
+ *     h = bf16(silu(g) * u), d_r = Wd_e h.
+ *   y[m] = sum over j = 0..k-1 of the hot routes, in ascending j, of topk_w[m,j] * d_(m,j).
+ *   Cold routes are skipped and reported: y is the hot-only partial output.
+ * x [M,H] bf16; topk_ids/topk_w [M,k]; expert_to_slot as in moe_bucket_routes;
+ * slots = the device slot array (n_slots images); y [M,H] fp32 is overwritten (zeros for a
+ * token whose routes are all cold); cold_count [1] / cold_routes [M*k] may be NULL.
+ * Deterministic: the result does not depend on slot numbering, bucket order or timing.
+ * --------------------------------------------------------------------------------------- */
+moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_t M,
+                               const int32_t* topk_ids, const float* topk_w,
+                               const int32_t* expert_to_slot, const uint8_t* slots,
+                               float* y, int32_t* cold_count, int32_t* cold_routes,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The two kernel stages of moe_experts_forward, on their own (for timing a stage or for
+ * callers that interleave other work).  Both read the route buckets that the LAST
+ * moe_bucket_routes or moe_experts_forward call on the same workspace left there, so that call
+ * (with the same topk_ids, M and expert_to_slot) must precede them on the same stream.
+ *   moe_experts_gateup: h = bf16(silu(Wg x) * (Wu x)) for every hot route, kept in the
+ *                       workspace [tinyserve, "How it works" item 2: gate and up fused here].
+ *   moe_experts_down:   y = ordered sum over hot routes of topk_w * (Wd h), as in
+ *                       moe_experts_forward; needs a preceding moe_experts_gateup.
+ * moe_bucket_routes + moe_experts_gateup + moe_experts_down == moe_experts_forward. */
+moe_status moe_experts_gateup(const moe_shape* shape, const uint16_t* x, int32_t M,
+                              const uint8_t* slots, void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_experts_down(const moe_shape* shape, int32_t M, const float* topk_w,
+                            const uint8_t* slots, float* y, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
+ * Slot refill [ninfer v0.4.0, "New": experts are copied to the GPU in the background;
+ * MoE expert offload, intro: routed experts stay in pinned host RAM; ORT hybrid PR,
+ * "Key Changes": pinned staging ordered by timing-disabled events].
+ *   For i < n: copy expert images host_bank[experts[i]] -> slots[slot_ids[i]] with
+ *   hipMemcpyAsync on copy_stream.  If wait_before is not NULL, copy_stream first waits for it
+ *   (e.g. the event recorded after the last kernels that read those slots); if done is not
+ *   NULL it is recorded on copy_stream after the copies (the compute stream waits on it
+ *   before the refilled experts become visible).
+ * host_bank [host, pinned]: E images back to back; experts, slot_ids [host].
+ * --------------------------------------------------------------------------------------- */
+moe_status moe_slot_refill(const moe_shape* shape, uint8_t* slots, const uint8_t* host_bank,
+                           const int32_t* experts, const int32_t* slot_ids, int32_t n,
+                           hipStream_t copy_stream, hipEvent_t wait_before, hipEvent_t done);
+
+/* ---------------------------------------------------------------------------------------
+ * Slot-cache policy, host only [MoE expert offload, "How it works": per-layer LRU table,
+ * misses take least-recently-used slots; ninfer v0.4.0, "New": at most two refills per
+ * layer and call, in the background, replacing the least used; tinyserve, "How it works"
+ * item 3 and "Configuration": LFRU eviction].
+ * One cache object per layer.  moe_cache_policy_step(step t, observed routes):
+ *   1. refills planned with visible_step <= t become resident;
+ *   2. for the observed routes: route/hit counters, LFRU frequencies (+1 per route, all
+ *      halved every decay_period steps), last_use = t for routed resident experts;
+ *   3. routed experts that are cold and not in flight, by (route count desc, id asc), are
+ *      admitted while fewer than max_refills_per_step were admitted at t and fewer than
+ *      max_pending are in flight: victim = lowest empty slot, else among resident slots not
+ *      in flight and not routed at t the smallest (last_use, slot) [LRU] or
+ *      (freq, last_use, slot) [LFRU]; the old expert is cold at once, the slot's last_use
+ *      becomes t and the new expert becomes visible at t + lag_steps;
+ *   4. the map expert -> slot (or -1) for step t is written to expert_to_slot [host, E].
+ * topk_ids [host] [M,k] are the routes the caller observed (M = 0 or NULL: none).
+ * plan [host] receives up to max_refills_per_step entries; *n_plan their number.
+ * Steps must strictly increase.  Pure host code, deterministic.
+ * --------------------------------------------------------------------------------------- */
+typedef struct moe_cache moe_cache;
+
+enum { MOE_POLICY_LRU = 0, MOE_POLICY_LFRU = 1 };
+
+typedef struct {
+  int32_t policy;               /* MOE_POLICY_LRU or MOE_POLICY_LFRU */
+  int32_t max_refills_per_step; /* >= 0 (0 = static placement) */
+  int32_t lag_steps;            /* >= 1 */
+  int32_t max_pending;          /* >= 1 */
+  int32_t decay_period;         /* LFRU halving period in steps, 0 = never */
+} moe_cache_config;
+
+typedef struct {
+  int32_t expert;       /* expert to copy in */
+  int32_t slot;         /* destination slot */
+  int32_t evicted;      /* expert that held the slot, or -1 */
+  int32_t visible_step; /* first step whose map contains the new expert */
+} moe_refill;
+
+typedef struct {
+  int64_t steps, routes, hits, refills, evictions;
+} moe_cache_stats;
+
+/* initial_slot_expert [host] [S]: expert held by each slot, -1 = empty (NULL = all empty). */
+moe_status moe_cache_create(const moe_shape* shape, const moe_cache_config* config,
+                            const int32_t* initial_slot_expert, moe_cache** out);
+moe_status moe_cache_policy_step(moe_cache* cache, int64_t step, const int32_t* topk_ids,
+                                 int32_t M, moe_refill* plan, int32_t* n_plan,
+                                 int32_t* expert_to_slot, moe_cache_stats* stats);
+void moe_cache_destroy(moe_cache* cache);
+
+/* Message describing the last failure of a call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,168 @@
+"""The C ABI without a GPU: every declared symbol is exported, the host-only calls (image
+packing, cache policy, argument checks) behave as documented.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synthetic
+from expert_offloaded_routed_amd import binding as B
+from oracle.cache_policy import LFRU, LRU, SlotCachePolicy
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return B.load()
+
+
+def _declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^\s*(?:moe_status|void|const char\*)\s+(moe_\w+)\s*\(", text, re.M)
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    names = _declared_functions()
+    assert set(names) >= {"moe_route", "moe_experts_forward", "moe_bucket_routes", "moe_slot_refill",
+                          "moe_cache_create", "moe_cache_policy_step", "moe_cache_destroy",
+                          "moe_pack_expert", "moe_unpack_expert", "moe_expert_image_bytes",
+                          "moe_workspace_size", "moe_workspace_init", "moe_last_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+    # no torch in the exported signatures: the header includes only C/HIP headers
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert "torch" not in hdr and "at::" not in hdr
+
+
+@pytest.mark.parametrize("name", ["tiny", "gptoss20b_decode", "e512_verify_stack"])
+def test_pack_unpack_round_trip(name):
+    _lib()
+    wl = synthetic.WORKLOADS[name]
+    shape = B.make_shape(wl.hidden, wl.inter, wl.n_experts, wl.top_k, wl.n_slots)
+    ex = synthetic.expert_canonical(wl, 0, 1)
+    img = B.moe_pack_expert(shape, ex)
+    assert img.size == B.moe_expert_image_bytes(shape) and img.size % 256 == 0
+    back = B.moe_unpack_expert(shape, img)
+    for k, v in ex.items():
+        assert np.array_equal(back[k], v), k
+    # the image holds each code byte exactly once plus padding scale bytes only
+    alg = sum(v.nbytes for v in ex.values())
+    assert alg <= img.size <= alg * 1.01 + 256
+
+
+def test_pack_layout_lane_order():
+    _lib()
+    shape = B.make_shape(64, 32, 2, 1, 2)
+    H, I = 64, 32
+    ex = {"gate_codes": np.zeros((I, H // 2), np.uint8), "gate_scales": np.full((I, 2), 120, np.uint8),
+          "up_codes": np.zeros((I, H // 2), np.uint8), "up_scales": np.full((I, 2), 121, np.uint8),
+          "down_codes": np.zeros((H, I // 2), np.uint8), "down_scales": np.full((H, 1), 122, np.uint8)}
+    ex["gate_codes"][5, 16:32] = np.arange(16)      # gate row 5, block 1
+    ex["up_codes"][7, 0:16] = np.arange(16) + 100   # up row 7, block 0
+    img = B.moe_pack_expert(shape, ex)
+    # gate/up tile 0: block b, lane l at (b*64 + l)*16; lanes 32.. are the up rows
+    assert np.array_equal(img[(1 * 64 + 5) * 16:(1 * 64 + 5) * 16 + 16], np.arange(16))
+    assert np.array_equal(img[(0 * 64 + 39) * 16:(0 * 64 + 39) * 16 + 16], np.arange(16) + 100)
+    # scales after the 2 code blocks: one group, lane word, bytes = blocks 0,1 then padding 127
+    s0 = 2 * 1024
+    assert list(img[s0 + 5 * 4: s0 + 5 * 4 + 4]) == [120, 120, 127, 127]
+    assert list(img[s0 + 39 * 4: s0 + 39 * 4 + 4]) == [121, 121, 127, 127]
+
+
+def _cache_pair(policy, E=32, S=8, k=4, R=2, L=3, Q=2, decay=8):
+    shape = B.make_shape(256, 512, E, k, S)
+    init = np.arange(S, dtype=np.int32)
+    init[-2:] = -1
+    lib_cache = B.MoeCache(shape, policy=policy, max_refills_per_step=R, lag_steps=L, max_pending=Q,
+                           decay_period=decay, initial_slot_expert=init)
+    ref = SlotCachePolicy(E, S, init, policy=policy, max_refills=R, lag=L, max_pending=Q,
+                          decay_period=decay)
+    return lib_cache, ref
+
+
+@pytest.mark.parametrize("policy", [LRU, LFRU])
+@pytest.mark.parametrize("L,Q,R", [(1, 2, 2), (3, 2, 2), (5, 4, 3), (2, 1, 1)])
+def test_host_policy_matches_oracle(policy, L, Q, R):
+    _lib()
+    E, S, k = 32, 8, 4
+    lib_cache, ref = _cache_pair(policy, E, S, k, R, L, Q)
+    rng = np.random.default_rng(L * 10 + Q + policy)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    perm = rng.permutation(E)
+    for t in range(200):
+        if t % 32 == 0:
+            perm = np.roll(perm, 1)
+        M = 1 + (t % 3)
+        ids = np.stack([perm[rng.choice(E, size=k, replace=False, p=p)] for _ in range(M)]).astype(np.int32)
+        obs = None if t % 7 == 3 else ids
+        m_lib, plan_lib, stats = lib_cache.moe_cache_policy_step(t, obs)
+        m_ref, plan_ref = ref.step(t, obs)
+        assert np.array_equal(m_lib, m_ref), t
+        assert plan_lib == plan_ref, t
+        assert stats == ref.stats, t
+    lib_cache.close()
+
+
+def test_host_policy_errors():
+    _lib()
+    shape = B.make_shape(256, 512, 8, 2, 4)
+    c = B.MoeCache(shape, initial_slot_expert=[0, 1, 2, 3])
+    c.moe_cache_policy_step(5, np.array([[0, 1]]))
+    with pytest.raises(B.MoeError) as e:
+        c.moe_cache_policy_step(5, np.array([[0, 1]]))
+    assert e.value.status == B.MOE_ERR_STATE
+    with pytest.raises(B.MoeError) as e:
+        c.moe_cache_policy_step(6, np.array([[0, 9]]))
+    assert e.value.status == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoeError):
+        B.MoeCache(shape, initial_slot_expert=[0, 0, 1, 2])
+    with pytest.raises(B.MoeError):
+        B.MoeCache(shape, lag_steps=0)
+
+
+def test_argument_checks_return_status_before_any_launch():
+    lib = _lib()
+    good = B.make_shape(2880, 2880, 32, 4, 32)
+    out = ctypes.c_size_t(0)
+    for bad, code in ((B.make_shape(2880, 2880, 32, 4, 0), B.MOE_ERR_INVALID_ARG),
+                      (B.make_shape(2880 + 32, 2880, 32, 4, 32), B.MOE_ERR_UNSUPPORTED),
+                      (B.make_shape(2880, 2880 + 16, 32, 4, 32), B.MOE_ERR_UNSUPPORTED),
+                      (B.make_shape(2880, 2880, 2048, 4, 32), B.MOE_ERR_UNSUPPORTED),
+                      (B.make_shape(2880, 2880, 32, 33, 32), B.MOE_ERR_UNSUPPORTED),
+                      (B.make_shape(2880, 2880, 3, 4, 32), B.MOE_ERR_UNSUPPORTED)):
+        assert lib.moe_expert_image_bytes(ctypes.byref(bad), ctypes.byref(out)) == code
+        assert B.moe_last_error() != ""
+    assert lib.moe_workspace_size(ctypes.byref(good), 1, ctypes.byref(out)) == B.MOE_OK
+    need = out.value
+    # undersized / misaligned / NULL workspaces are refused on the host
+    assert lib.moe_route(ctypes.byref(good), 16, 1, 16, None, 16, 16, 256, need - 1, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(good), 16, 1, 16, None, 16, 16, 257, need, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(good), 16, 1, 16, None, 16, 16, None, need, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(good), 16, -1, 16, None, 16, 16, 256, need, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(good), None, 1, 16, None, 16, 16, 256, need, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_experts_forward(ctypes.byref(good), 16, 1, 16, 16, None, 260, 16, None, None,
+                                   256, need, None) == B.MOE_ERR_INVALID_ARG  # slots misaligned
+    ident = B.make_shape(2880, 2880, 32, 4, 8)  # identity map impossible with 8 slots
+    lib.moe_workspace_size(ctypes.byref(ident), 4, ctypes.byref(out))
+    assert lib.moe_bucket_routes(ctypes.byref(ident), 16, 1, None, None, None, None, None, None,
+                                 256, out.value, None) == B.MOE_ERR_INVALID_ARG
+    experts = np.array([0, 40], np.int32)
+    slots = np.array([0, 1], np.int32)
+    assert lib.moe_slot_refill(ctypes.byref(good), 256, 256, experts.ctypes.data, slots.ctypes.data, 2,
+                               None, None, None) == B.MOE_ERR_INVALID_ARG
+    slots2 = np.array([3, 3], np.int32)
+    experts2 = np.array([0, 1], np.int32)
+    assert lib.moe_slot_refill(ctypes.byref(good), 256, 256, experts2.ctypes.data, slots2.ctypes.data, 2,
+                               None, None, None) == B.MOE_ERR_INVALID_ARG
