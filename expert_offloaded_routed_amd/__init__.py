@@ -17,10 +17,10 @@ from .binding import (  # noqa: F401
     moe_experts_gateup,
     moe_expert_image_bytes,
     moe_last_error,
+    moe_layer_forward,
     moe_pack_expert,
     moe_route,
     moe_slot_refill,
     moe_unpack_expert,
-    moe_workspace_init,
     moe_workspace_size,
 )

@@ -60,13 +60,14 @@ _SIGS = {
     "moe_pack_expert": [C.POINTER(moe_shape)] + [_P] * 7,
     "moe_unpack_expert": [C.POINTER(moe_shape)] + [_P] * 7,
     "moe_workspace_size": [C.POINTER(moe_shape), _I32, C.POINTER(_SZ)],
-    "moe_workspace_init": [C.POINTER(moe_shape), _P, _SZ, _P],
     "moe_route": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_bucket_routes": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_experts_forward": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                             _SZ, _P],
-    "moe_experts_gateup": [C.POINTER(moe_shape), _P, _I32, _P, _P, _SZ, _P],
-    "moe_experts_down": [C.POINTER(moe_shape), _I32, _P, _P, _P, _P, _SZ, _P],
+    "moe_layer_forward": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                          _P, _SZ, _P],
+    "moe_experts_gateup": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _SZ, _P],
+    "moe_experts_down": [C.POINTER(moe_shape), _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_slot_refill": [C.POINTER(moe_shape), _P, _P, _P, _P, _I32, _P, _P, _P],
     "moe_cache_create": [C.POINTER(moe_shape), C.POINTER(moe_cache_config), _P,
                          C.POINTER(_P)],
@@ -187,11 +188,6 @@ def moe_workspace_size(shape: moe_shape, max_M: int) -> int:
     return out.value
 
 
-def moe_workspace_init(shape, ws, stream=None):
-    _check(load().moe_workspace_init(C.byref(shape), _ptr(ws), _nbytes(ws), _stream(stream)),
-           "moe_workspace_init")
-
-
 def moe_route(shape, x, M, w_router, router_bias, topk_ids, topk_w, ws, stream=None):
     _check(load().moe_route(C.byref(shape), _ptr(x), int(M), _ptr(w_router), _ptr(router_bias),
                             _ptr(topk_ids), _ptr(topk_w), _ptr(ws), _nbytes(ws), _stream(stream)),
@@ -215,14 +211,25 @@ def moe_experts_forward(shape, x, M, topk_ids, topk_w, expert_to_slot, slots, y,
            "moe_experts_forward")
 
 
-def moe_experts_gateup(shape, x, M, slots, ws, stream=None):
-    _check(load().moe_experts_gateup(C.byref(shape), _ptr(x), int(M), _ptr(slots), _ptr(ws),
-                                     _nbytes(ws), _stream(stream)), "moe_experts_gateup")
+def moe_layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids, topk_w,
+                      y, cold_count, cold_routes, ws, stream=None):
+    _check(load().moe_layer_forward(C.byref(shape), _ptr(x), int(M), _ptr(w_router),
+                                    _ptr(router_bias), _ptr(expert_to_slot), _ptr(slots),
+                                    _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(cold_count),
+                                    _ptr(cold_routes), _ptr(ws), _nbytes(ws), _stream(stream)),
+           "moe_layer_forward")
 
 
-def moe_experts_down(shape, M, topk_w, slots, y, ws, stream=None):
-    _check(load().moe_experts_down(C.byref(shape), int(M), _ptr(topk_w), _ptr(slots), _ptr(y),
-                                   _ptr(ws), _nbytes(ws), _stream(stream)), "moe_experts_down")
+def moe_experts_gateup(shape, x, M, topk_ids, topk_w, expert_to_slot, slots, ws, stream=None):
+    _check(load().moe_experts_gateup(C.byref(shape), _ptr(x), int(M), _ptr(topk_ids), _ptr(topk_w),
+                                     _ptr(expert_to_slot), _ptr(slots), _ptr(ws), _nbytes(ws),
+                                     _stream(stream)), "moe_experts_gateup")
+
+
+def moe_experts_down(shape, M, topk_ids, topk_w, expert_to_slot, slots, y, ws, stream=None):
+    _check(load().moe_experts_down(C.byref(shape), int(M), _ptr(topk_ids), _ptr(topk_w),
+                                   _ptr(expert_to_slot), _ptr(slots), _ptr(y), _ptr(ws),
+                                   _nbytes(ws), _stream(stream)), "moe_experts_down")
 
 
 def moe_slot_refill(shape, slots, host_bank, experts, slot_ids, copy_stream=None,

@@ -1,5 +1,5 @@
-// Host side of the libmoe C ABI: argument validation, workspace layout, kernel launches,
-// expert image packing and slot refills.  See include/moe.h for the contract of each call.
+// Host side of the libmoe C ABI: argument validation, workspace layout, kernel launches and
+// slot refills.  See include/moe.h for the contract of each call.
 #include <hip/hip_runtime_api.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -11,25 +11,6 @@
 #include "moe_internal.h"
 
 namespace moe {
-hipError_t launch_fill_u32(unsigned* p, int n, unsigned v, hipStream_t s);
-hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, int k, float* logits, unsigned* ticket, int32_t* ids, float* w,
-                         hipStream_t s);
-hipError_t launch_bucket(const int32_t* ids, int Mk, int E, int S, const int32_t* e2s,
-                         int32_t* route_slot, int32_t* ws_perm, int32_t* meta, int32_t* dist_expert,
-                         int32_t* dist_slot, int32_t* dist_off, int32_t* dist_cnt, int nd_max,
-                         int32_t* cold_list, int32_t* u_counts, int32_t* u_offsets,
-                         int32_t* u_perm, int32_t* u_cold_count, int32_t* u_cold_routes,
-                         hipStream_t s);
-hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, int E, int k,
-                         const uint8_t* slots, const ImageLayout& L, const int32_t* meta,
-                         const int32_t* dist_slot, const int32_t* dist_off, const int32_t* dist_cnt,
-                         const int32_t* perm, uint16_t* hbuf, hipStream_t s);
-hipError_t launch_down(int M, int H, int I, int E, int k, const uint8_t* slots,
-                       const ImageLayout& L, const int32_t* meta, const int32_t* dist_slot,
-                       const int32_t* dist_off, const int32_t* dist_cnt, const int32_t* perm,
-                       const int32_t* route_slot, const uint16_t* hbuf, const float* topk_w,
-                       float* pdn, unsigned* tickets, float* y, hipStream_t s);
 
 thread_local std::string g_last_error;
 
@@ -58,6 +39,8 @@ moe_status check_shape(const moe_shape* s) {
                 s->hidden, s->inter);
   if (s->hidden > kMaxHidden)
     return fail(MOE_ERR_UNSUPPORTED, "hidden %d > %d", s->hidden, kMaxHidden);
+  if (s->inter > kMaxInter)
+    return fail(MOE_ERR_UNSUPPORTED, "inter %d > %d", s->inter, kMaxInter);
   if (s->n_experts > kMaxExperts)
     return fail(MOE_ERR_UNSUPPORTED, "n_experts %d > %d", s->n_experts, kMaxExperts);
   if (s->top_k > kMaxTopK || s->top_k > s->n_experts)
@@ -69,9 +52,13 @@ static moe_status hip_fail(hipError_t e, const char* what) {
   return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Bound on routes per call (one bucketing workgroup walks them all).
+constexpr int kMaxRoutesPerCall = 1 << 20;
+
 static moe_status check_ws(const moe_shape* s, int M, void* ws, size_t ws_bytes, WsLayout* W) {
   if (M < 0) return fail(MOE_ERR_INVALID_ARG, "M = %d < 0", M);
-  if ((size_t)M * s->top_k > (size_t)1 << 24) return fail(MOE_ERR_UNSUPPORTED, "M*k too large");
+  if ((size_t)M * s->top_k > (size_t)kMaxRoutesPerCall)
+    return fail(MOE_ERR_UNSUPPORTED, "M * top_k > %d", kMaxRoutesPerCall);
   if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
     return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -86,8 +73,115 @@ static T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off);
 }
 
-// Large-M token batches reuse the bucketing kernel's single workgroup; bound its work.
-constexpr int kMaxRoutesPerCall = 1 << 20;
+static BucketOut bucket_out(void* ws, const WsLayout& W, int32_t* counts, int32_t* offsets,
+                            int32_t* perm, int32_t* cold_count, int32_t* cold_routes) {
+  BucketOut o;
+  o.route_slot = at<int32_t>(ws, W.route_slot);
+  o.ws_perm = at<int32_t>(ws, W.perm);
+  o.meta = at<int32_t>(ws, W.meta);
+  o.dist_expert = at<int32_t>(ws, W.dist_expert);
+  o.dist_slot = at<int32_t>(ws, W.dist_slot);
+  o.dist_off = at<int32_t>(ws, W.dist_off);
+  o.dist_cnt = at<int32_t>(ws, W.dist_cnt);
+  o.cold_list = at<int32_t>(ws, W.cold_list);
+  o.u_counts = counts;
+  o.u_offsets = offsets;
+  o.u_perm = perm;
+  o.u_cold_count = cold_count;
+  o.u_cold_routes = cold_routes;
+  return o;
+}
+
+static moe_status check_map(const moe_shape* s, const int32_t* e2s) {
+  if (!e2s && s->n_experts > s->n_slots)
+    return fail(MOE_ERR_INVALID_ARG, "identity expert_to_slot needs n_slots >= n_experts");
+  return MOE_OK;
+}
+
+static moe_status check_x_slots(const uint16_t* x, const uint8_t* slots) {
+  if (!x || !slots) return fail(MOE_ERR_INVALID_ARG, "x and slots are required");
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(slots) & 255))
+    return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte and slots 256-byte aligned");
+  return MOE_OK;
+}
+
+// Route arguments of a call: top-k from `logits` (or the given ids / weights), the expert map.
+static RouteArgs route_args(const moe_shape* sh, int M, const float* logits, const int32_t* ids,
+                            const float* w, const int32_t* e2s, int32_t* out_ids, float* out_w,
+                            int32_t* cold_count, int32_t* cold_routes) {
+  RouteArgs a;
+  a.logits = logits;
+  a.ids_in = ids;
+  a.w_in = w;
+  a.e2s = e2s;
+  a.M = M;
+  a.k = sh->top_k;
+  a.E = sh->n_experts;
+  a.S = sh->n_slots;
+  a.topk_ids = out_ids;
+  a.topk_w = out_w;
+  a.cold_count = cold_count;
+  a.cold_routes = cold_routes;
+  return a;
+}
+
+static RouteWs route_ws(void* ws, const WsLayout& W) {
+  RouteWs r;
+  r.meta = at<int32_t>(ws, W.meta);
+  r.dist_slot = at<int32_t>(ws, W.dist_slot);
+  r.dist_off = at<int32_t>(ws, W.dist_off);
+  r.dist_cnt = at<int32_t>(ws, W.dist_cnt);
+  r.perm = at<int32_t>(ws, W.perm);
+  r.route_slot = at<int32_t>(ws, W.route_slot);
+  return r;
+}
+
+// The expert stages of a call.  Routes come from `logits` (top-k inside) or from ids / w.
+// Small calls rebuild the route table inside every expert workgroup; larger ones run the
+// top-k / bucketing kernel first.  do_gateup / do_down select the stages.
+static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, const float* logits,
+                              int32_t* ids, float* w, const int32_t* e2s, const uint8_t* slots,
+                              float* y, int32_t* cold_count, int32_t* cold_routes, void* ws,
+                              const WsLayout& W, bool do_gateup, bool do_down, hipStream_t stream) {
+  const ImageLayout L = image_layout(sh->hidden, sh->inter);
+  const ExpertPlan p = plan_experts(L, M, sh->n_experts, sh->top_k);
+  const RouteWs rw = route_ws(ws, W);
+  hipError_t e;
+  if (!p.prologue) {
+    const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, cold_routes);
+    e = launch_topk_bucket(logits, M, sh->top_k, ids, w, true, ids, sh->n_experts, sh->n_slots, e2s,
+                           o, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k / bucket launch");
+    logits = nullptr;  // ids / w are final from here on
+  }
+  if (do_gateup) {
+    // the writer workgroup publishes top-k results and the cold report
+    const RouteArgs ra = route_args(sh, M, logits, ids, w, e2s, logits ? ids : nullptr,
+                                    logits ? w : nullptr, p.prologue ? cold_count : nullptr,
+                                    p.prologue ? cold_routes : nullptr);
+    e = launch_gateup(x, M, sh->hidden, sh->inter, slots, L, p, ra, rw, at<uint16_t>(ws, W.hbuf),
+                      stream);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+  }
+  if (do_down) {
+    const RouteArgs ra = route_args(sh, M, nullptr, ids, w, e2s, nullptr, nullptr, nullptr, nullptr);
+    e = launch_down(M, sh->hidden, sh->inter, slots, L, p, ra, rw, at<uint16_t>(ws, W.hbuf),
+                    at<float>(ws, W.pdn), y, stream);
+    if (e != hipSuccess) return hip_fail(e, "down launch");
+  }
+  return MOE_OK;
+}
+
+// Cold report of an empty call (M = 0).
+static moe_status empty_call(const moe_shape* sh, const int32_t* e2s, int32_t* cold_count,
+                             void* ws, const WsLayout& W, hipStream_t stream) {
+  if (!cold_count) return MOE_OK;
+  const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, nullptr);
+  hipError_t e = launch_topk_bucket(nullptr, 0, sh->top_k, nullptr, nullptr, true, nullptr,
+                                    sh->n_experts, sh->n_slots, e2s, o, stream);
+  if (e != hipSuccess) return hip_fail(e, "bucket launch");
+  return MOE_OK;
+}
 
 }  // namespace moe
 
@@ -116,17 +210,6 @@ moe_status moe_workspace_size(const moe_shape* shape, int32_t max_M, size_t* byt
   return ok();
 }
 
-moe_status moe_workspace_init(const moe_shape* shape, void* ws, size_t ws_bytes, hipStream_t stream) {
-  moe_status st = check_shape(shape);
-  if (st != MOE_OK) return st;
-  WsLayout W;
-  st = check_ws(shape, 0, ws, ws_bytes, &W);
-  if (st != MOE_OK) return st;
-  hipError_t e = launch_fill_u32(at<unsigned>(ws, 0), (int)(W.counters_end / 4), 0u, stream);
-  if (e != hipSuccess) return hip_fail(e, "fill kernel");
-  return ok();
-}
-
 moe_status moe_route(const moe_shape* shape, const uint16_t* x, int32_t M, const uint16_t* w_router,
                      const float* router_bias, int32_t* topk_ids, float* topk_w, void* ws,
                      size_t ws_bytes, hipStream_t stream) {
@@ -140,30 +223,15 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, int32_t M, const
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x, w_router, topk_ids and topk_w are required");
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w_router)) & 15)
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x and w_router must be 16-byte aligned");
-  hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden,
-                               shape->top_k, at<float>(ws, W.logits), at<unsigned>(ws, W.route_ticket),
-                               topk_ids, topk_w, stream);
+  float* logits = at<float>(ws, W.logits);
+  hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
+                               stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
+  const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
+  e = launch_topk_bucket(logits, M, shape->top_k, topk_ids, topk_w, false, topk_ids,
+                         shape->n_experts, shape->n_slots, nullptr, o, stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
   return ok();
-}
-
-static moe_status bucket_common(const moe_shape* shape, const int32_t* topk_ids, int32_t M,
-                                const int32_t* e2s, int32_t* counts, int32_t* offsets,
-                                int32_t* perm, int32_t* cold_count, int32_t* cold_routes,
-                                void* ws, const WsLayout& W, hipStream_t stream) {
-  if (!e2s && shape->n_experts > shape->n_slots)
-    return fail(MOE_ERR_INVALID_ARG, "identity expert_to_slot needs n_slots >= n_experts");
-  const int Mk = M * shape->top_k;
-  if (Mk > kMaxRoutesPerCall) return fail(MOE_ERR_UNSUPPORTED, "M * top_k > %d", kMaxRoutesPerCall);
-  const int nd_max = Mk < shape->n_experts ? Mk : shape->n_experts;
-  hipError_t e = launch_bucket(topk_ids, Mk, shape->n_experts, shape->n_slots, e2s,
-                               at<int32_t>(ws, W.route_slot), at<int32_t>(ws, W.perm),
-                               at<int32_t>(ws, W.meta), at<int32_t>(ws, W.dist_expert),
-                               at<int32_t>(ws, W.dist_slot), at<int32_t>(ws, W.dist_off),
-                               at<int32_t>(ws, W.dist_cnt), nd_max, at<int32_t>(ws, W.cold_list),
-                               counts, offsets, perm, cold_count, cold_routes, stream);
-  if (e != hipSuccess) return hip_fail(e, "bucket launch");
-  return MOE_OK;
 }
 
 moe_status moe_bucket_routes(const moe_shape* shape, const int32_t* topk_ids, int32_t M,
@@ -176,48 +244,13 @@ moe_status moe_bucket_routes(const moe_shape* shape, const int32_t* topk_ids, in
   st = check_ws(shape, M, ws, ws_bytes, &W);
   if (st != MOE_OK) return st;
   if (M > 0 && !topk_ids) return fail(MOE_ERR_INVALID_ARG, "topk_ids is NULL");
-  st = bucket_common(shape, topk_ids, M, expert_to_slot, counts, offsets, perm, cold_count,
-                     cold_routes, ws, W, stream);
+  st = check_map(shape, expert_to_slot);
   if (st != MOE_OK) return st;
+  const BucketOut o = bucket_out(ws, W, counts, offsets, perm, cold_count, cold_routes);
+  hipError_t e = launch_topk_bucket(nullptr, M, shape->top_k, nullptr, nullptr, true, topk_ids,
+                                    shape->n_experts, shape->n_slots, expert_to_slot, o, stream);
+  if (e != hipSuccess) return hip_fail(e, "bucket launch");
   return ok();
-}
-
-static moe_status check_expert_args(const moe_shape* shape, const uint16_t* x, int32_t M,
-                                    const uint8_t* slots, void* ws, size_t ws_bytes, WsLayout* W) {
-  moe_status st = check_shape(shape);
-  if (st != MOE_OK) return st;
-  st = check_ws(shape, M, ws, ws_bytes, W);
-  if (st != MOE_OK) return st;
-  if (M > 0 && (!x || !slots)) return fail(MOE_ERR_INVALID_ARG, "x and slots are required");
-  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(slots) & 255))
-    return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte and slots 256-byte aligned");
-  return MOE_OK;
-}
-
-static moe_status gateup_common(const moe_shape* shape, const uint16_t* x, int32_t M,
-                                const uint8_t* slots, void* ws, const WsLayout& W,
-                                hipStream_t stream) {
-  const ImageLayout L = image_layout(shape->hidden, shape->inter);
-  hipError_t e = launch_gateup(x, M, shape->hidden, shape->inter, shape->n_experts, shape->top_k,
-                               slots, L, at<int32_t>(ws, W.meta), at<int32_t>(ws, W.dist_slot),
-                               at<int32_t>(ws, W.dist_off), at<int32_t>(ws, W.dist_cnt),
-                               at<int32_t>(ws, W.perm), at<uint16_t>(ws, W.hbuf), stream);
-  if (e != hipSuccess) return hip_fail(e, "gate/up launch");
-  return MOE_OK;
-}
-
-static moe_status down_common(const moe_shape* shape, int32_t M, const float* topk_w,
-                              const uint8_t* slots, float* y, void* ws, const WsLayout& W,
-                              hipStream_t stream) {
-  const ImageLayout L = image_layout(shape->hidden, shape->inter);
-  hipError_t e = launch_down(M, shape->hidden, shape->inter, shape->n_experts, shape->top_k, slots, L,
-                             at<int32_t>(ws, W.meta), at<int32_t>(ws, W.dist_slot),
-                             at<int32_t>(ws, W.dist_off), at<int32_t>(ws, W.dist_cnt),
-                             at<int32_t>(ws, W.perm), at<int32_t>(ws, W.route_slot),
-                             at<uint16_t>(ws, W.hbuf), topk_w, at<float>(ws, W.pdn),
-                             at<unsigned>(ws, W.dn_tickets), y, stream);
-  if (e != hipSuccess) return hip_fail(e, "down launch");
-  return MOE_OK;
 }
 
 moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_t M,
@@ -225,47 +258,99 @@ moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_
                                const int32_t* expert_to_slot, const uint8_t* slots, float* y,
                                int32_t* cold_count, int32_t* cold_routes, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
   WsLayout W;
-  moe_status st = check_expert_args(shape, x, M, slots, ws, ws_bytes, &W);
+  st = check_ws(shape, M, ws, ws_bytes, &W);
   if (st != MOE_OK) return st;
-  if (M > 0 && (!topk_ids || !topk_w || !y))
+  st = check_map(shape, expert_to_slot);
+  if (st != MOE_OK) return st;
+  if (M == 0) {
+    st = empty_call(shape, expert_to_slot, cold_count, ws, W, stream);
+    return st != MOE_OK ? st : ok();
+  }
+  st = check_x_slots(x, slots);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !topk_w || !y)
     return fail(MOE_ERR_INVALID_ARG, "moe_experts_forward: topk_ids, topk_w and y are required");
-  st = bucket_common(shape, topk_ids, M, expert_to_slot, nullptr, nullptr, nullptr, cold_count,
-                     cold_routes, ws, W, stream);
+  st = run_experts(shape, x, M, nullptr, const_cast<int32_t*>(topk_ids), const_cast<float*>(topk_w),
+                   expert_to_slot, slots, y, cold_count, cold_routes, ws, W, true, true, stream);
+  return st != MOE_OK ? st : ok();
+}
+
+moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t M,
+                             const uint16_t* w_router, const float* router_bias,
+                             const int32_t* expert_to_slot, const uint8_t* slots,
+                             int32_t* topk_ids, float* topk_w, float* y, int32_t* cold_count,
+                             int32_t* cold_routes, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
-  if (M == 0) return ok();
-  st = gateup_common(shape, x, M, slots, ws, W, stream);
+  WsLayout W;
+  st = check_ws(shape, M, ws, ws_bytes, &W);
   if (st != MOE_OK) return st;
-  st = down_common(shape, M, topk_w, slots, y, ws, W, stream);
+  st = check_map(shape, expert_to_slot);
   if (st != MOE_OK) return st;
-  return ok();
+  if (M == 0) {
+    st = empty_call(shape, expert_to_slot, cold_count, ws, W, stream);
+    return st != MOE_OK ? st : ok();
+  }
+  st = check_x_slots(x, slots);
+  if (st != MOE_OK) return st;
+  if (!w_router || !topk_ids || !topk_w || !y)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_layer_forward: w_router, topk_ids, topk_w and y are required");
+  if (reinterpret_cast<uintptr_t>(w_router) & 15)
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: w_router must be 16-byte aligned");
+  float* logits = at<float>(ws, W.logits);
+  hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
+                               stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  st = run_experts(shape, x, M, logits, topk_ids, topk_w, expert_to_slot, slots, y, cold_count,
+                   cold_routes, ws, W, true, true, stream);
+  return st != MOE_OK ? st : ok();
 }
 
 moe_status moe_experts_gateup(const moe_shape* shape, const uint16_t* x, int32_t M,
-                              const uint8_t* slots, void* ws, size_t ws_bytes, hipStream_t stream) {
+                              const int32_t* topk_ids, const float* topk_w,
+                              const int32_t* expert_to_slot, const uint8_t* slots, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
   WsLayout W;
-  moe_status st = check_expert_args(shape, x, M, slots, ws, ws_bytes, &W);
-  if (st != MOE_OK) return st;
-  if (M == 0) return ok();
-  st = gateup_common(shape, x, M, slots, ws, W, stream);
-  if (st != MOE_OK) return st;
-  return ok();
-}
-
-moe_status moe_experts_down(const moe_shape* shape, int32_t M, const float* topk_w,
-                            const uint8_t* slots, float* y, void* ws, size_t ws_bytes,
-                            hipStream_t stream) {
-  WsLayout W;
-  moe_status st = check_expert_args(shape, nullptr, 0, slots, ws, ws_bytes, &W);
-  if (st != MOE_OK) return st;
   st = check_ws(shape, M, ws, ws_bytes, &W);
   if (st != MOE_OK) return st;
-  if (M == 0) return ok();
-  if (!topk_w || !y || !slots)
-    return fail(MOE_ERR_INVALID_ARG, "moe_experts_down: topk_w, slots and y are required");
-  st = down_common(shape, M, topk_w, slots, y, ws, W, stream);
+  st = check_map(shape, expert_to_slot);
   if (st != MOE_OK) return st;
-  return ok();
+  if (M == 0) return ok();
+  st = check_x_slots(x, slots);
+  if (st != MOE_OK) return st;
+  if (!topk_ids || !topk_w)
+    return fail(MOE_ERR_INVALID_ARG, "moe_experts_gateup: topk_ids and topk_w are required");
+  st = run_experts(shape, x, M, nullptr, const_cast<int32_t*>(topk_ids), const_cast<float*>(topk_w),
+                   expert_to_slot, slots, nullptr, nullptr, nullptr, ws, W, true, false, stream);
+  return st != MOE_OK ? st : ok();
+}
+
+moe_status moe_experts_down(const moe_shape* shape, int32_t M, const int32_t* topk_ids,
+                            const float* topk_w, const int32_t* expert_to_slot,
+                            const uint8_t* slots, float* y, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  WsLayout W;
+  st = check_ws(shape, M, ws, ws_bytes, &W);
+  if (st != MOE_OK) return st;
+  st = check_map(shape, expert_to_slot);
+  if (st != MOE_OK) return st;
+  if (M == 0) return ok();
+  if (!topk_ids || !topk_w || !y || !slots)
+    return fail(MOE_ERR_INVALID_ARG, "moe_experts_down: topk_ids, topk_w, slots and y are required");
+  if (reinterpret_cast<uintptr_t>(slots) & 255)
+    return fail(MOE_ERR_INVALID_ARG, "slots must be 256-byte aligned");
+  st = run_experts(shape, nullptr, M, nullptr, const_cast<int32_t*>(topk_ids),
+                   const_cast<float*>(topk_w), expert_to_slot, slots, y, nullptr, nullptr, ws, W,
+                   false, true, stream);
+  return st != MOE_OK ? st : ok();
 }
 
 moe_status moe_slot_refill(const moe_shape* shape, uint8_t* slots, const uint8_t* host_bank,

@@ -78,12 +78,10 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 }
 
 // ---- number formats ---------------------------------------------------------------------------
-// E8M0 scale byte -> fp32: 2^(x-127); x = 0 is the fp32 subnormal 2^-127; x = 255 is NaN.
+// E8M0 scale byte -> fp32: 2^(x-127) (x = 0 gives the fp32 subnormal 2^-127); x = 255 is NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t x) {
-  uint32_t bits = x << 23;
-  bits = x == 0 ? 0x00400000u : bits;
-  bits = x == 255 ? 0x7FC00000u : bits;
-  return __uint_as_float(bits);
+  const float v = __builtin_amdgcn_ldexpf(1.0f, (int)x - 127);
+  return x == 255 ? __uint_as_float(0x7FC00000u) : v;
 }
 
 // fp32 -> bf16, round to nearest even (NaN stays NaN).

@@ -11,14 +11,21 @@
 //             canonical nibble order).  One wave-wide 16-byte load = 1 KiB contiguous.
 //     scales: ng groups x 64 lanes x 4 B; byte i of a lane's word in group q is the E8M0
 //             scale of block 4q+i of that lane's row (127 = 1.0 past the last block).
-//   down section: H/64 tiles.  Tile t covers down rows 64t..64t+63 over K = I, same scheme
-//   with lane l holding row 64t+l.
+//   down section: H/RD tiles of RD = 64/S rows over K = I (nb = I/32 blocks), S chosen per
+//   shape (dn_segments below).  Lane l = r*S + s owns row r of the tile and K segment s; at
+//   step t it holds block t*S + s of its row.  Steps with all lanes active are 1 KiB each
+//   (lane-major, 16 B per lane); the final partial step (when S does not divide nb) stores
+//   only its active lanes, row by row (index r*(nb % S) + s).  Then ceil(T/4) words per lane
+//   of scale bytes: byte i of word q is the scale of the lane's block at step 4q+i (127 past
+//   the end).
 //
-// Every lane of a wave works on its own output row and all lanes of a wave walk the same
-// input block at the same time, so the activation block is uniform across the wave and is
-// read through the scalar unit (no LDS and no vector-memory traffic for activations).
+// In the gate/up section every lane of a wave owns one output row and all lanes walk the same
+// input block at the same time, so the activation block is uniform across the wave and is read
+// through the scalar unit.  The down section trades that for more, smaller tiles so that one
+// workgroup can own a few output rows for every routed expert and combine them on its own.
 #pragma once
 
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -27,19 +34,39 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxHidden = 8192;
-constexpr int kMaxKC = 4;            // max K-chunks (workgroups) per down tile
-constexpr int kWavesPerGroup = 4;    // waves per workgroup in the expert kernels
-constexpr int kRouterWaves = 4;      // waves per workgroup in the router
-constexpr int kBucketThreads = 1024; // threads of the single bucketing workgroup
+constexpr int kMaxInter = 4096;      // down steps per lane stay <= 16 with S = 8
+constexpr int kBucketThreads = 1024; // threads of the top-k / bucketing workgroup
+constexpr size_t kDownLdsBudget = 48 * 1024;  // dynamic LDS of the down kernel
 
 struct ImageLayout {
   int H, I;
   int nb_h, ng_h;  // gate/up: blocks and groups along K = H
-  int nb_i, ng_i;  // down: blocks and groups along K = I
+  int nb_i;        // down: blocks along K = I
+  int dn_seg;      // S: lanes (K segments) per down row
+  int dn_rows;     // RD = 64 / S rows per down tile
+  int dn_steps;    // T = ceil(nb_i / S) steps per lane
+  int dn_scale_words;  // ceil(T / 4) scale words per lane
   int gu_tiles, dn_tiles;
-  size_t gu_tile_bytes, dn_tile_bytes;
+  size_t gu_tile_bytes, dn_code_bytes, dn_tile_bytes;
   size_t gu_bytes, dn_bytes, image_bytes;
 };
+
+// S for the down tiles: the fewest padding scale bytes with at most 16 steps per lane, ties to
+// the larger S (more, smaller tiles).
+inline int dn_segments(int nb) {
+  int best = 1;
+  long best_pad = -1;
+  for (int S = 8; S >= 1; S /= 2) {
+    const int T = (nb + S - 1) / S;
+    if (T > 16) continue;
+    const long pad = (long)((T + 3) / 4) * 256 - (long)nb * (64 / S);
+    if (best_pad < 0 || pad < best_pad) {
+      best = S;
+      best_pad = pad;
+    }
+  }
+  return best;
+}
 
 inline ImageLayout image_layout(int H, int I) {
   ImageLayout L;
@@ -48,22 +75,24 @@ inline ImageLayout image_layout(int H, int I) {
   L.nb_h = H / 32;
   L.ng_h = (L.nb_h + 3) / 4;
   L.nb_i = I / 32;
-  L.ng_i = (L.nb_i + 3) / 4;
+  L.dn_seg = dn_segments(L.nb_i);
+  L.dn_rows = 64 / L.dn_seg;
+  L.dn_steps = (L.nb_i + L.dn_seg - 1) / L.dn_seg;
+  L.dn_scale_words = (L.dn_steps + 3) / 4;
   L.gu_tiles = I / 32;
-  L.dn_tiles = H / 64;
+  L.dn_tiles = H / L.dn_rows;
   L.gu_tile_bytes = (size_t)L.nb_h * 1024 + (size_t)L.ng_h * 256;
-  L.dn_tile_bytes = (size_t)L.nb_i * 1024 + (size_t)L.ng_i * 256;
+  const int full = L.nb_i / L.dn_seg, rem = L.nb_i % L.dn_seg;
+  L.dn_code_bytes = ((size_t)full * 64 + (size_t)L.dn_rows * rem) * 16;
+  L.dn_tile_bytes = L.dn_code_bytes + (size_t)L.dn_scale_words * 256;
   L.gu_bytes = L.gu_tile_bytes * L.gu_tiles;
   L.dn_bytes = L.dn_tile_bytes * L.dn_tiles;
   L.image_bytes = (L.gu_bytes + L.dn_bytes + 255) / 256 * 256;
   return L;
 }
 
-// Workspace: a fixed counter block, then per-call arrays sized for M tokens.
+// Workspace: per-call arrays sized for M tokens (nothing survives between calls).
 struct WsLayout {
-  size_t route_ticket;   // uint32 [1]
-  size_t dn_tickets;     // uint32 [dn_tiles]
-  size_t counters_end;
   size_t logits;         // f32 [M][E]
   size_t route_slot;     // i32 [M*k]
   size_t counts;         // i32 [E]
@@ -76,7 +105,7 @@ struct WsLayout {
   size_t dist_cnt;       // i32 [nd_max]
   size_t cold_list;      // i32 [M*k]
   size_t hbuf;           // bf16 [M*k][I]
-  size_t pdn;            // f32 [M*k][kMaxKC][H]
+  size_t pdn;            // f32 [M*k][H]: down partial sums when they do not fit in LDS
   size_t total;
 };
 
@@ -87,13 +116,8 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   const ImageLayout L = image_layout(H, I);
   const size_t Mk = (size_t)M * k;
   const size_t nd = Mk < (size_t)E ? Mk : (size_t)E;
+  (void)L;
   size_t o = 0;
-  W.route_ticket = o;
-  o += 4;
-  W.dn_tickets = o;
-  o += 4 * (size_t)L.dn_tiles;
-  o = align256(o);
-  W.counters_end = o;
   W.logits = o;      o = align256(o + 4 * (size_t)M * E);
   W.route_slot = o;  o = align256(o + 4 * Mk);
   W.counts = o;      o = align256(o + 4 * (size_t)E);
@@ -106,12 +130,66 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   W.dist_cnt = o;    o = align256(o + 4 * nd);
   W.cold_list = o;   o = align256(o + 4 * Mk);
   W.hbuf = o;        o = align256(o + 2 * Mk * I);
-  W.pdn = o;         o = align256(o + 4 * Mk * kMaxKC * (size_t)H);
+  W.pdn = o;         o = align256(o + 4 * Mk * (size_t)H);
   W.total = o;
   return W;
 }
 
 // Error flags raised by the device in meta[2].
 enum : int32_t { kErrBadId = 1, kErrBadSlot = 2 };
+
+// Outputs of the resolve / bucketing stage (workspace arrays, then optional caller arrays).
+struct BucketOut {
+  int32_t *route_slot, *ws_perm, *meta, *dist_expert, *dist_slot, *dist_off, *dist_cnt;
+  int32_t *cold_list, *u_counts, *u_offsets, *u_perm, *u_cold_count, *u_cold_routes;
+};
+
+// Launch shape of the expert kernels for one call.
+struct ExpertPlan {
+  int nd_max;        // upper bound of distinct hot experts (gate/up grid.y)
+  bool prologue;     // every expert workgroup rebuilds the route table (M*k <= kProMaxRoutes)
+  int gu_waves;      // waves per gate/up workgroup
+  int gu_groups;     // most K groups (of 4 blocks) any gate/up wave holds
+  bool h_in_lds;     // down: h of every route staged in LDS
+  bool part_in_lds;  // down: per-route row sums in LDS (else in the workspace)
+  size_t dn_lds;     // down: dynamic LDS bytes
+};
+
+// Routes of a call as the expert kernels see them (kernel arguments, passed by value).
+struct RouteArgs {
+  const float* logits;      // top-k from these (NULL: use ids_in / w_in)
+  const int32_t* ids_in;    // [M*k]
+  const float* w_in;        // [M*k]
+  const int32_t* e2s;       // [E] or NULL (identity)
+  int M, k, E, S;
+  int32_t* topk_ids;        // outputs of the writer workgroup, [M*k] or NULL
+  float* topk_w;
+  int32_t* cold_count;      // [1] or NULL
+  int32_t* cold_routes;     // [M*k] or NULL
+};
+
+// Route table left in the workspace by the bucketing kernel (large calls).
+struct RouteWs {
+  const int32_t* meta;
+  const int32_t* dist_slot;
+  const int32_t* dist_off;
+  const int32_t* dist_cnt;
+  const int32_t* perm;
+  const int32_t* route_slot;
+};
+
+// Kernel launchers (moe_kernels.hip).
+hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
+                         int H, float* logits, hipStream_t s);
+hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
+                              bool do_bucket, const int32_t* ids, int E, int S,
+                              const int32_t* e2s, const BucketOut& o, hipStream_t s);
+ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k);
+hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
+                         const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
+                         const RouteWs& rw, uint16_t* hbuf, hipStream_t s);
+hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
+                       const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
+                       const uint16_t* hbuf, float* pdn, float* y, hipStream_t s);
 
 }  // namespace moe

@@ -11,10 +11,11 @@ moe_status ok();
 moe_status check_shape(const moe_shape* s);
 
 // Copy direction: pack (canonical -> image) or unpack (image -> canonical).
+// Gate/up tiles: lane l < 32 is gate row 32t+l, lane l >= 32 up row 32t+l-32; block b of the
+// lane's row at (b*64 + l)*16, scale words after the codes (see moe_internal.h).
 template <bool PACK>
 static void tiles(uint8_t* img, int n_tiles, int rows_per_lane_group, int nb, int ng,
                   size_t tile_bytes, uint8_t* const* codes, uint8_t* const* scales, int K) {
-  // rows_per_lane_group = 32 for gate/up (two matrices), 64 for down (one matrix)
   const size_t row_code_bytes = (size_t)K / 2;
   const size_t row_scale_bytes = (size_t)K / 32;
   for (int t = 0; t < n_tiles; ++t) {
@@ -45,6 +46,46 @@ static void tiles(uint8_t* img, int n_tiles, int rows_per_lane_group, int nb, in
   }
 }
 
+// Down tiles: lane l = r*S + s holds, at step t, block t*S + s of row r (see moe_internal.h).
+template <bool PACK>
+static void down_tiles(uint8_t* img, const ImageLayout& L, uint8_t* codes, uint8_t* scales) {
+  const int S = L.dn_seg, RD = L.dn_rows, nb = L.nb_i;
+  const int full = nb / S, rem = nb % S;
+  const size_t row_code_bytes = (size_t)L.I / 2;
+  const size_t row_scale_bytes = (size_t)L.I / 32;
+  for (int t = 0; t < L.dn_tiles; ++t) {
+    uint8_t* tb = img + (size_t)t * L.dn_tile_bytes;
+    for (int lane = 0; lane < 64; ++lane) {
+      const int r = lane / S, sg = lane % S;
+      const int row = t * RD + r;
+      uint8_t* c = codes + (size_t)row * row_code_bytes;
+      uint8_t* sc = scales + (size_t)row * row_scale_bytes;
+      for (int st = 0; st < L.dn_steps; ++st) {
+        const int b = st * S + sg;
+        if (b >= nb) continue;
+        const size_t idx = st < full ? (size_t)st * 64 + lane : (size_t)full * 64 + (size_t)r * rem + sg;
+        uint8_t* dst = tb + idx * 16;
+        if (PACK)
+          memcpy(dst, c + (size_t)b * 16, 16);
+        else
+          memcpy(c + (size_t)b * 16, dst, 16);
+      }
+      for (int q = 0; q < L.dn_scale_words; ++q) {
+        uint8_t* dst = tb + L.dn_code_bytes + ((size_t)q * 64 + lane) * 4;
+        for (int i = 0; i < 4; ++i) {
+          const int st = 4 * q + i;
+          const int b = st * S + sg;
+          const bool ok = st < L.dn_steps && b < nb;
+          if (PACK)
+            dst[i] = ok ? sc[b] : 127;
+          else if (ok)
+            sc[b] = dst[i];
+        }
+      }
+    }
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -64,9 +105,8 @@ moe_status moe_pack_expert(const moe_shape* shape, const uint8_t* gate_codes,
   uint8_t* gc[2] = {const_cast<uint8_t*>(gate_codes), const_cast<uint8_t*>(up_codes)};
   uint8_t* gs[2] = {const_cast<uint8_t*>(gate_scales), const_cast<uint8_t*>(up_scales)};
   tiles<true>(image, L.gu_tiles, 32, L.nb_h, L.ng_h, L.gu_tile_bytes, gc, gs, L.H);
-  uint8_t* dc[1] = {const_cast<uint8_t*>(down_codes)};
-  uint8_t* ds[1] = {const_cast<uint8_t*>(down_scales)};
-  tiles<true>(image + L.gu_bytes, L.dn_tiles, 64, L.nb_i, L.ng_i, L.dn_tile_bytes, dc, ds, L.I);
+  down_tiles<true>(image + L.gu_bytes, L, const_cast<uint8_t*>(down_codes),
+                   const_cast<uint8_t*>(down_scales));
   return ok();
 }
 
@@ -82,9 +122,7 @@ moe_status moe_unpack_expert(const moe_shape* shape, const uint8_t* image, uint8
   uint8_t* gc[2] = {gate_codes, up_codes};
   uint8_t* gs[2] = {gate_scales, up_scales};
   tiles<false>(img, L.gu_tiles, 32, L.nb_h, L.ng_h, L.gu_tile_bytes, gc, gs, L.H);
-  uint8_t* dc[1] = {down_codes};
-  uint8_t* ds[1] = {down_scales};
-  tiles<false>(img + L.gu_bytes, L.dn_tiles, 64, L.nb_i, L.ng_i, L.dn_tile_bytes, dc, ds, L.I);
+  down_tiles<false>(img + L.gu_bytes, L, down_codes, down_scales);
   return ok();
 }
 

@@ -23,7 +23,7 @@
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Every call returns a moe_status; moe_last_error() gives a message for the calling thread.
  *   - Supported shapes: hidden % 64 == 0, inter % 32 == 0, 1 <= top_k <= min(n_experts, 32),
- *     n_experts <= 1024, hidden <= 8192, n_slots >= 1.  x, w_router: 16-byte aligned;
+ *     n_experts <= 1024, hidden <= 8192, inter <= 4096, n_slots >= 1.  x, w_router: 16-byte aligned;
  *     slot arrays and workspaces: 256-byte aligned.
  */
 #ifndef MOE_H
@@ -85,16 +85,13 @@ moe_status moe_unpack_expert(const moe_shape* shape, const uint8_t* image,
                              uint8_t* down_codes, uint8_t* down_scales);
 
 /* ---------------------------------------------------------------------------------------
- * Workspace.  One device buffer shared by moe_route / moe_bucket_routes /
- * moe_experts_forward for calls with M <= max_M.  Its first bytes hold arrival counters that
- * must be zero before the first call (allocate it zero-filled or call moe_workspace_init);
- * every call leaves them at zero again.  Calls that share a workspace must be ordered on one
- * stream; concurrent calls need separate workspaces.
+ * Workspace.  One device buffer (256-byte aligned) used by moe_route, moe_bucket_routes,
+ * moe_experts_forward and moe_layer_forward for calls with M <= max_M.  It carries logits,
+ * route buckets, h and partial sums from one kernel of a call to the next; nothing survives
+ * between calls, so it needs no initialisation.  Calls sharing a workspace must be ordered on
+ * one stream; concurrent calls need separate workspaces.
  * --------------------------------------------------------------------------------------- */
 moe_status moe_workspace_size(const moe_shape* shape, int32_t max_M, size_t* bytes /*[host]*/);
-
-/* Zero the workspace's counters with a fill kernel on `stream` (safe under graph capture). */
-moe_status moe_workspace_init(const moe_shape* shape, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Router [ninfer v0.4.0, "New": the router is no longer a single thread block;
@@ -153,18 +150,33 @@ moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_
                                float* y, int32_t* cold_count, int32_t* cold_routes,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Whole layer in one call: moe_route followed by moe_experts_forward.  For M*k <= 256 the
+ * top-k, slot resolve and bucketing run inside the expert kernels (three launches: router
+ * GEMV, gate/up, down + combine).  Same arguments, outputs and numerics as the two calls;
+ * topk_ids [M,k] and topk_w [M,k] are written too.
+ * --------------------------------------------------------------------------------------- */
+moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t M,
+                             const uint16_t* w_router, const float* router_bias,
+                             const int32_t* expert_to_slot, const uint8_t* slots,
+                             int32_t* topk_ids, float* topk_w, float* y,
+                             int32_t* cold_count, int32_t* cold_routes,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* The two kernel stages of moe_experts_forward, on their own (for timing a stage or for
- * callers that interleave other work).  Both read the route buckets that the LAST
- * moe_bucket_routes or moe_experts_forward call on the same workspace left there, so that call
- * (with the same topk_ids, M and expert_to_slot) must precede them on the same stream.
+ * callers that interleave other work).  Arguments as in moe_experts_forward.
  *   moe_experts_gateup: h = bf16(silu(Wg x) * (Wu x)) for every hot route, kept in the
  *                       workspace [tinyserve, "How it works" item 2: gate and up fused here].
  *   moe_experts_down:   y = ordered sum over hot routes of topk_w * (Wd h), as in
- *                       moe_experts_forward; needs a preceding moe_experts_gateup.
- * moe_bucket_routes + moe_experts_gateup + moe_experts_down == moe_experts_forward. */
+ *                       moe_experts_forward; needs the h that the last moe_experts_gateup (or
+ *                       moe_experts_forward) with the same routes left in this workspace.
+ * moe_experts_gateup + moe_experts_down == moe_experts_forward (without the cold report). */
 moe_status moe_experts_gateup(const moe_shape* shape, const uint16_t* x, int32_t M,
-                              const uint8_t* slots, void* ws, size_t ws_bytes, hipStream_t stream);
-moe_status moe_experts_down(const moe_shape* shape, int32_t M, const float* topk_w,
+                              const int32_t* topk_ids, const float* topk_w,
+                              const int32_t* expert_to_slot, const uint8_t* slots,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+moe_status moe_experts_down(const moe_shape* shape, int32_t M, const int32_t* topk_ids,
+                            const float* topk_w, const int32_t* expert_to_slot,
                             const uint8_t* slots, float* y, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 

@@ -37,7 +37,8 @@ def test_library_exports_every_declared_symbol():
     assert set(names) >= {"moe_route", "moe_experts_forward", "moe_bucket_routes", "moe_slot_refill",
                           "moe_cache_create", "moe_cache_policy_step", "moe_cache_destroy",
                           "moe_pack_expert", "moe_unpack_expert", "moe_expert_image_bytes",
-                          "moe_workspace_size", "moe_workspace_init", "moe_last_error"}
+                          "moe_workspace_size", "moe_layer_forward", "moe_last_error",
+                          "moe_experts_gateup", "moe_experts_down"}
     for n in names:
         assert hasattr(lib, n), n
     # no torch in the exported signatures: the header includes only C/HIP headers
@@ -141,6 +142,7 @@ def test_argument_checks_return_status_before_any_launch():
                       (B.make_shape(2880, 2880 + 16, 32, 4, 32), B.MOE_ERR_UNSUPPORTED),
                       (B.make_shape(2880, 2880, 2048, 4, 32), B.MOE_ERR_UNSUPPORTED),
                       (B.make_shape(2880, 2880, 32, 33, 32), B.MOE_ERR_UNSUPPORTED),
+                      (B.make_shape(2880, 4096 + 32, 32, 4, 32), B.MOE_ERR_UNSUPPORTED),
                       (B.make_shape(2880, 2880, 3, 4, 32), B.MOE_ERR_UNSUPPORTED)):
         assert lib.moe_expert_image_bytes(ctypes.byref(bad), ctypes.byref(out)) == code
         assert B.moe_last_error() != ""
@@ -166,3 +168,37 @@ def test_argument_checks_return_status_before_any_launch():
     experts2 = np.array([0, 1], np.int32)
     assert lib.moe_slot_refill(ctypes.byref(good), 256, 256, experts2.ctypes.data, slots2.ctypes.data, 2,
                                None, None, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_pack_down_layout_segments_and_partial_step():
+    """Down rows of a 2880-wide intermediate: 8 lanes (K segments) per row, 12 steps, the last
+    step partial (90 = 11*8 + 2 blocks).  Check where one block and one scale byte land."""
+    _lib()
+    H, I = 64, 2880
+    shape = B.make_shape(H, I, 2, 1, 2)
+    rng = np.random.default_rng(0)
+    ex = {"gate_codes": rng.integers(0, 256, (I, H // 2), dtype=np.uint8),
+          "gate_scales": rng.integers(100, 140, (I, H // 32), dtype=np.uint8),
+          "up_codes": rng.integers(0, 256, (I, H // 2), dtype=np.uint8),
+          "up_scales": rng.integers(100, 140, (I, H // 32), dtype=np.uint8),
+          "down_codes": rng.integers(0, 256, (H, I // 2), dtype=np.uint8),
+          "down_scales": rng.integers(100, 140, (H, I // 32), dtype=np.uint8)}
+    img = B.moe_pack_expert(shape, ex)
+    gu_tile = 2 * 1024 + 1 * 256            # H=64: 2 blocks, 1 scale group per tile
+    gu_bytes = gu_tile * (I // 32)
+    S, RD, nb, T = 8, 8, 90, 12
+    code_bytes = (11 * 64 + RD * 2) * 16
+    dn_tile = code_bytes + 3 * 256
+    assert img.size == -(-(gu_bytes + dn_tile * (H // RD)) // 256) * 256
+    # row 21 = tile 2, r = 5; block 43 = step 5, segment 3 (full step): lane 5*8+3
+    off = gu_bytes + 2 * dn_tile + (5 * 64 + 43) * 16
+    assert np.array_equal(img[off:off + 16], ex["down_codes"][21, 43 * 16:44 * 16])
+    # block 89 = step 11 (partial, 2 active segments), segment 1: index 11*64 + r*2 + 1
+    off = gu_bytes + 2 * dn_tile + (11 * 64 + 5 * 2 + 1) * 16
+    assert np.array_equal(img[off:off + 16], ex["down_codes"][21, 89 * 16:90 * 16])
+    # scale of block 43 (step 5 -> word 1, byte 1) of lane 43
+    soff = gu_bytes + 2 * dn_tile + code_bytes + (1 * 64 + 43) * 4 + 1
+    assert img[soff] == ex["down_scales"][21, 43]
+    # step 11 of segment 5 does not exist: padding byte 127 (word 2, byte 3)
+    soff = gu_bytes + 2 * dn_tile + code_bytes + (2 * 64 + 5 * 8 + 5) * 4 + 3
+    assert img[soff] == 127

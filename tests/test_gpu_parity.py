@@ -367,3 +367,41 @@ def test_slot_cache_pipeline_bookkeeping():
         else:
             assert not ys[t].any()
     cache.close()
+
+
+def test_layer_forward_equals_route_plus_experts_and_stages(gptoss):
+    """moe_layer_forward == moe_route + moe_experts_forward == bucket + gateup + down, bitwise,
+    and all of them match the oracle; also with a cold expert map."""
+    wl = gptoss.wl
+    shape = gptoss.shape
+    bias = synthetic.zipf_bias(wl)
+    for M in (1, 3):
+        say("layer_forward equivalence, M =", M)
+        x = _dev(synthetic.activations(wl, M, 500 + M))
+        wr = _dev(gptoss.wr)
+        bd = _dev(bias)
+        e2s_np = np.arange(wl.n_experts, dtype=np.int32)
+        e2s_np[[1, 5, 9, 30]] = -1
+        for e2s in (None, _dev(e2s_np)):
+            a, b, c = L.Buffers(shape, M), L.Buffers(shape, M), L.Buffers(shape, M)
+            B.moe_layer_forward(shape, x, M, wr, bd, e2s, gptoss.slots, a.ids, a.w, a.y, a.cold_count,
+                                a.cold_routes, a.ws)
+            B.moe_route(shape, x, M, wr, bd, b.ids, b.w, b.ws)
+            B.moe_experts_forward(shape, x, M, b.ids, b.w, e2s, gptoss.slots, b.y, b.cold_count,
+                                  b.cold_routes, b.ws)
+            B.moe_route(shape, x, M, wr, bd, c.ids, c.w, c.ws)
+            B.moe_bucket_routes(shape, c.ids, M, e2s, None, None, None, c.cold_count, c.cold_routes, c.ws)
+            B.moe_experts_gateup(shape, x, M, c.ids, c.w, e2s, gptoss.slots, c.ws)
+            B.moe_experts_down(shape, M, c.ids, c.w, e2s, gptoss.slots, c.y, c.ws)
+            torch.cuda.synchronize()
+            for other in (b, c):
+                assert torch.equal(a.ids[:M], other.ids[:M]) and torch.equal(a.w[:M], other.w[:M])
+                assert torch.equal(a.y[:M], other.y[:M])
+                assert torch.equal(a.cold_count, other.cold_count)
+            xn = synthetic.activations(wl, M, 500 + M)
+            _, ids_ref, w_ref = compare_routes(a.ids[:M].cpu().numpy(), a.w[:M].cpu().numpy(),
+                                               O.router_logits(xn, gptoss.wr, bias), wl.top_k)
+            ref = O.layer_forward(xn, ids_ref, w_ref, gptoss.experts,
+                                  None if e2s is None else e2s_np)
+            close_enough(a.y[:M].cpu().numpy(), ref["y_hot"], f"layer_forward M={M}")
+            assert int(a.cold_count.item()) == len(ref["cold_routes"])
