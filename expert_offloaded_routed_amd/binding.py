@@ -85,6 +85,9 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m expert_offloaded_routed_amd._build`")
+    # torch carries its own HIP runtime; load it first so that libmoe binds to the same one
+    # (two runtimes in one process do not share devices, streams or allocations).
+    import torch  # noqa: F401
     lib = C.CDLL(path)
     for name, argtypes in _SIGS.items():
         f = getattr(lib, name)
