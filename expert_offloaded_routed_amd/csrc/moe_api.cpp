@@ -79,10 +79,7 @@ static BucketOut bucket_out(void* ws, const WsLayout& W, int32_t* counts, int32_
   o.route_slot = at<int32_t>(ws, W.route_slot);
   o.ws_perm = at<int32_t>(ws, W.perm);
   o.meta = at<int32_t>(ws, W.meta);
-  o.dist_expert = at<int32_t>(ws, W.dist_expert);
-  o.dist_slot = at<int32_t>(ws, W.dist_slot);
-  o.dist_off = at<int32_t>(ws, W.dist_off);
-  o.dist_cnt = at<int32_t>(ws, W.dist_cnt);
+  o.dist = at<int4>(ws, W.dist);
   o.cold_list = at<int32_t>(ws, W.cold_list);
   o.u_counts = counts;
   o.u_offsets = offsets;
@@ -128,34 +125,43 @@ static RouteArgs route_args(const moe_shape* sh, int M, const float* logits, con
 static RouteWs route_ws(void* ws, const WsLayout& W) {
   RouteWs r;
   r.meta = at<int32_t>(ws, W.meta);
-  r.dist_slot = at<int32_t>(ws, W.dist_slot);
-  r.dist_off = at<int32_t>(ws, W.dist_off);
-  r.dist_cnt = at<int32_t>(ws, W.dist_cnt);
+  r.dist = at<int4>(ws, W.dist);
   r.perm = at<int32_t>(ws, W.perm);
   r.route_slot = at<int32_t>(ws, W.route_slot);
   return r;
 }
 
-// The expert stages of a call.  Routes come from `logits` (top-k inside) or from ids / w.
-// Small calls rebuild the route table inside every expert workgroup; larger ones run the
-// top-k / bucketing kernel first.  do_gateup / do_down select the stages.
-static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, const float* logits,
-                              int32_t* ids, float* w, const int32_t* e2s, const uint8_t* slots,
-                              float* y, int32_t* cold_count, int32_t* cold_routes, void* ws,
-                              const WsLayout& W, bool do_gateup, bool do_down, hipStream_t stream) {
+// Where the routes of a call come from.
+enum class RouteSrc {
+  kTable,   // the route kernel left the finished table in the workspace (ids / w written)
+  kLogits,  // router logits in the workspace: top-k still to do
+  kIds,     // caller's ids / w
+};
+
+// The expert stages of a call.  Small calls rebuild the route table inside every expert
+// workgroup (from the logits or the ids); larger ones run the top-k / bucketing kernel first,
+// unless the route kernel already left the table.  do_gateup / do_down select the stages.
+static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, RouteSrc src,
+                              const float* logits, int32_t* ids, float* w, const int32_t* e2s,
+                              const uint8_t* slots, float* y, int32_t* cold_count,
+                              int32_t* cold_routes, void* ws, const WsLayout& W, bool do_gateup,
+                              bool do_down, hipStream_t stream) {
   const ImageLayout L = image_layout(sh->hidden, sh->inter);
-  const ExpertPlan p = plan_experts(L, M, sh->n_experts, sh->top_k);
+  ExpertPlan p = plan_experts(L, M, sh->n_experts, sh->top_k);
   const RouteWs rw = route_ws(ws, W);
   hipError_t e;
-  if (!p.prologue) {
+  if (src == RouteSrc::kTable) {
+    p.prologue = false;
+  } else if (!p.prologue) {
     const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, cold_routes);
-    e = launch_topk_bucket(logits, M, sh->top_k, ids, w, true, ids, sh->n_experts, sh->n_slots, e2s,
-                           o, stream);
+    e = launch_topk_bucket(src == RouteSrc::kLogits ? logits : nullptr, M, sh->top_k, ids, w, true,
+                           ids, sh->n_experts, sh->n_slots, e2s, o, stream);
     if (e != hipSuccess) return hip_fail(e, "top-k / bucket launch");
-    logits = nullptr;  // ids / w are final from here on
   }
+  if (!p.prologue) logits = nullptr;  // ids / w are final from here on
+  if (src != RouteSrc::kLogits) logits = nullptr;
   if (do_gateup) {
-    // the writer workgroup publishes top-k results and the cold report
+    // in the prologue case the writer workgroup publishes top-k results and the cold report
     const RouteArgs ra = route_args(sh, M, logits, ids, w, e2s, logits ? ids : nullptr,
                                     logits ? w : nullptr, p.prologue ? cold_count : nullptr,
                                     p.prologue ? cold_routes : nullptr);
@@ -223,11 +229,18 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, int32_t M, const
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x, w_router, topk_ids and topk_w are required");
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w_router)) & 15)
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x and w_router must be 16-byte aligned");
-  float* logits = at<float>(ws, W.logits);
-  hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
-                               stream);
-  if (e != hipSuccess) return hip_fail(e, "router launch");
   const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
+  hipError_t e;
+  if (route_fusable(M, shape->n_experts, shape->hidden)) {
+    e = launch_route_table(x, M, w_router, router_bias, shape->n_experts, shape->hidden,
+                           shape->top_k, topk_ids, topk_w, shape->n_slots, nullptr, nullptr,
+                           nullptr, o, stream);
+    if (e != hipSuccess) return hip_fail(e, "route launch");
+    return ok();
+  }
+  float* logits = at<float>(ws, W.logits);
+  e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits, stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
   e = launch_topk_bucket(logits, M, shape->top_k, topk_ids, topk_w, false, topk_ids,
                          shape->n_experts, shape->n_slots, nullptr, o, stream);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
@@ -273,8 +286,9 @@ moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_
   if (st != MOE_OK) return st;
   if (!topk_ids || !topk_w || !y)
     return fail(MOE_ERR_INVALID_ARG, "moe_experts_forward: topk_ids, topk_w and y are required");
-  st = run_experts(shape, x, M, nullptr, const_cast<int32_t*>(topk_ids), const_cast<float*>(topk_w),
-                   expert_to_slot, slots, y, cold_count, cold_routes, ws, W, true, true, stream);
+  st = run_experts(shape, x, M, RouteSrc::kIds, nullptr, const_cast<int32_t*>(topk_ids),
+                   const_cast<float*>(topk_w), expert_to_slot, slots, y, cold_count, cold_routes, ws,
+                   W, true, true, stream);
   return st != MOE_OK ? st : ok();
 }
 
@@ -302,11 +316,22 @@ moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t 
   if (reinterpret_cast<uintptr_t>(w_router) & 15)
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: w_router must be 16-byte aligned");
   float* logits = at<float>(ws, W.logits);
-  hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
-                               stream);
-  if (e != hipSuccess) return hip_fail(e, "router launch");
-  st = run_experts(shape, x, M, logits, topk_ids, topk_w, expert_to_slot, slots, y, cold_count,
-                   cold_routes, ws, W, true, true, stream);
+  hipError_t e;
+  RouteSrc src = RouteSrc::kLogits;
+  if (route_fusable(M, shape->n_experts, shape->hidden)) {
+    // router, top-k and bucketing in one workgroup; the expert kernels read the table
+    const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
+    e = launch_route_table(x, M, w_router, router_bias, shape->n_experts, shape->hidden,
+                           shape->top_k, topk_ids, topk_w, shape->n_slots, expert_to_slot,
+                           cold_count, cold_routes, o, stream);
+    if (e != hipSuccess) return hip_fail(e, "route launch");
+    src = RouteSrc::kTable;
+  } else {
+    e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits, stream);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+  }
+  st = run_experts(shape, x, M, src, logits, topk_ids, topk_w, expert_to_slot, slots, y,
+                   cold_count, cold_routes, ws, W, true, true, stream);
   return st != MOE_OK ? st : ok();
 }
 
@@ -326,8 +351,9 @@ moe_status moe_experts_gateup(const moe_shape* shape, const uint16_t* x, int32_t
   if (st != MOE_OK) return st;
   if (!topk_ids || !topk_w)
     return fail(MOE_ERR_INVALID_ARG, "moe_experts_gateup: topk_ids and topk_w are required");
-  st = run_experts(shape, x, M, nullptr, const_cast<int32_t*>(topk_ids), const_cast<float*>(topk_w),
-                   expert_to_slot, slots, nullptr, nullptr, nullptr, ws, W, true, false, stream);
+  st = run_experts(shape, x, M, RouteSrc::kIds, nullptr, const_cast<int32_t*>(topk_ids),
+                   const_cast<float*>(topk_w), expert_to_slot, slots, nullptr, nullptr, nullptr, ws,
+                   W, true, false, stream);
   return st != MOE_OK ? st : ok();
 }
 
@@ -347,7 +373,7 @@ moe_status moe_experts_down(const moe_shape* shape, int32_t M, const int32_t* to
     return fail(MOE_ERR_INVALID_ARG, "moe_experts_down: topk_ids, topk_w, slots and y are required");
   if (reinterpret_cast<uintptr_t>(slots) & 255)
     return fail(MOE_ERR_INVALID_ARG, "slots must be 256-byte aligned");
-  st = run_experts(shape, nullptr, M, nullptr, const_cast<int32_t*>(topk_ids),
+  st = run_experts(shape, nullptr, M, RouteSrc::kIds, nullptr, const_cast<int32_t*>(topk_ids),
                    const_cast<float*>(topk_w), expert_to_slot, slots, y, nullptr, nullptr, ws, W,
                    false, true, stream);
   return st != MOE_OK ? st : ok();

@@ -94,6 +94,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
 
+// Dot product of 8 bf16 pairs (one 16-byte chunk each), accumulated in fp32 pair by pair.
+__device__ __forceinline__ float dot8_bf16(const uint4& w, const uint4& x, float acc) {
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.x), as_bf16x2(x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.y), as_bf16x2(x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.z), as_bf16x2(x.z), acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(w.w), as_bf16x2(x.w), acc, false);
+}
+
 // Sum over one 32-element MXFP4 block (codes c, unscaled) times 32 bf16 activations a:
 // each code byte holds two E2M1 values (low nibble first) that the gfx950 converter turns into
 // an exact bf16 pair, dotted with the matching activation pair in fp32.

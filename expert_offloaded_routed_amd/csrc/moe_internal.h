@@ -36,7 +36,7 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxHidden = 8192;
 constexpr int kMaxInter = 4096;      // down steps per lane stay <= 16 with S = 8
 constexpr int kBucketThreads = 1024; // threads of the top-k / bucketing workgroup
-constexpr size_t kDownLdsBudget = 48 * 1024;  // dynamic LDS of the down kernel
+constexpr size_t kDownLdsBudget = 48 * 1024;  // dynamic LDS of the down kernel (h + row sums)
 
 struct ImageLayout {
   int H, I;
@@ -99,10 +99,7 @@ struct WsLayout {
   size_t offsets;        // i32 [E+1]
   size_t perm;           // i32 [M*k]
   size_t meta;           // i32 [8]: n_dist, cold_count, error flags
-  size_t dist_expert;    // i32 [nd_max]
-  size_t dist_slot;      // i32 [nd_max]
-  size_t dist_off;       // i32 [nd_max]
-  size_t dist_cnt;       // i32 [nd_max]
+  size_t dist;           // i32x4 [nd_max]: distinct hot experts {slot, bucket offset, count, id}
   size_t cold_list;      // i32 [M*k]
   size_t hbuf;           // bf16 [M*k][I]
   size_t pdn;            // f32 [M*k][H]: down partial sums when they do not fit in LDS
@@ -124,10 +121,7 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   W.offsets = o;     o = align256(o + 4 * ((size_t)E + 1));
   W.perm = o;        o = align256(o + 4 * Mk);
   W.meta = o;        o = align256(o + 4 * 8);
-  W.dist_expert = o; o = align256(o + 4 * nd);
-  W.dist_slot = o;   o = align256(o + 4 * nd);
-  W.dist_off = o;    o = align256(o + 4 * nd);
-  W.dist_cnt = o;    o = align256(o + 4 * nd);
+  W.dist = o;        o = align256(o + 16 * nd);
   W.cold_list = o;   o = align256(o + 4 * Mk);
   W.hbuf = o;        o = align256(o + 2 * Mk * I);
   W.pdn = o;         o = align256(o + 4 * Mk * (size_t)H);
@@ -140,7 +134,8 @@ enum : int32_t { kErrBadId = 1, kErrBadSlot = 2 };
 
 // Outputs of the resolve / bucketing stage (workspace arrays, then optional caller arrays).
 struct BucketOut {
-  int32_t *route_slot, *ws_perm, *meta, *dist_expert, *dist_slot, *dist_off, *dist_cnt;
+  int32_t *route_slot, *ws_perm, *meta;
+  int4* dist;
   int32_t *cold_list, *u_counts, *u_offsets, *u_perm, *u_cold_count, *u_cold_routes;
 };
 
@@ -168,19 +163,23 @@ struct RouteArgs {
   int32_t* cold_routes;     // [M*k] or NULL
 };
 
-// Route table left in the workspace by the bucketing kernel (large calls).
+// Route table in the workspace: written by the route kernel, the bucketing kernel or the writer
+// workgroup of a gate/up launch that builds it itself; read by the expert kernels.
 struct RouteWs {
-  const int32_t* meta;
-  const int32_t* dist_slot;
-  const int32_t* dist_off;
-  const int32_t* dist_cnt;
-  const int32_t* perm;
-  const int32_t* route_slot;
+  int32_t* meta;        // [0] distinct hot experts, [1] cold routes, [2] error flags
+  int4* dist;           // {slot, offset into perm, count, expert id}, ascending expert id
+  int32_t* perm;        // hot routes grouped by expert
+  int32_t* route_slot;  // slot of every route, -1 = cold
 };
 
 // Kernel launchers (moe_kernels.hip).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
                          int H, float* logits, hipStream_t s);
+bool route_fusable(int M, int E, int H);
+hipError_t launch_route_table(const uint16_t* x, int M, const uint16_t* wr, const float* bias,
+                              int E, int H, int k, int32_t* topk_ids, float* topk_w, int S,
+                              const int32_t* e2s, int32_t* cold_count, int32_t* cold_routes,
+                              const BucketOut& o, hipStream_t s);
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,
                               const int32_t* e2s, const BucketOut& o, hipStream_t s);

@@ -48,11 +48,7 @@ __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, i
     for (int i = 0; i < kRouterMaxChunksPerLane; ++i) {
       const int c = lane + 64 * i;
       if (c < nch) {
-        const uint4 xv = xr[c];
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wrow[i].x), as_bf16x2(xv.x), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wrow[i].y), as_bf16x2(xv.y), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wrow[i].z), as_bf16x2(xv.z), acc, false);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wrow[i].w), as_bf16x2(xv.w), acc, false);
+        acc = dot8_bf16(wrow[i], xr[c], acc);
       }
     }
     acc = wave_sum(acc);
@@ -136,9 +132,7 @@ struct BucketSmem {
 __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, int Mk, int E, int S,
                              const int32_t* __restrict__ e2s, int32_t* __restrict__ route_slot,
                              int32_t* __restrict__ ws_perm, int32_t* __restrict__ meta,
-                             int32_t* __restrict__ dist_expert, int32_t* __restrict__ dist_slot,
-                             int32_t* __restrict__ dist_off, int32_t* __restrict__ dist_cnt,
-                             int nd_max, int32_t* __restrict__ cold_list,
+                             int4* __restrict__ dist, int nd_max, int32_t* __restrict__ cold_list,
                              int32_t* __restrict__ u_counts, int32_t* __restrict__ u_offsets,
                              int32_t* __restrict__ u_perm, int32_t* __restrict__ u_cold_count,
                              int32_t* __restrict__ u_cold_routes) {
@@ -187,12 +181,7 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
       s_off[e] = off;
       if (u_counts) u_counts[e] = c;
       if (u_offsets) u_offsets[e] = off;
-      if (hot && di < nd_max) {
-        dist_expert[di] = e;
-        dist_slot[di] = slot;
-        dist_off[di] = off;
-        dist_cnt[di] = c;
-      }
+      if (hot && di < nd_max) dist[di] = make_int4(slot, off, c, e);
     }
     running += tot;
     running_d += tot_d;
@@ -243,8 +232,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucket(
     float* __restrict__ topk_w, int do_bucket,
     const int32_t* __restrict__ ids, int Mk, int E, int S, const int32_t* __restrict__ e2s,
     int32_t* __restrict__ route_slot, int32_t* __restrict__ ws_perm, int32_t* __restrict__ meta,
-    int32_t* __restrict__ dist_expert, int32_t* __restrict__ dist_slot,
-    int32_t* __restrict__ dist_off, int32_t* __restrict__ dist_cnt, int nd_max,
+    int4* __restrict__ dist, int nd_max,
     int32_t* __restrict__ cold_list, int32_t* __restrict__ u_counts,
     int32_t* __restrict__ u_offsets, int32_t* __restrict__ u_perm,
     int32_t* __restrict__ u_cold_count, int32_t* __restrict__ u_cold_routes) {
@@ -257,8 +245,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucket(
     __syncthreads();  // this workgroup's ids are visible to it from here on
   }
   if (blockIdx.x != 0) return;
-  bucket_stage(sm, ids, Mk, E, S, e2s, route_slot, ws_perm, meta, dist_expert, dist_slot, dist_off,
-               dist_cnt, nd_max, cold_list, u_counts, u_offsets, u_perm, u_cold_count,
+  bucket_stage(sm, ids, Mk, E, S, e2s, route_slot, ws_perm, meta, dist, nd_max, cold_list, u_counts, u_offsets, u_perm, u_cold_count,
                u_cold_routes);
 }
 
@@ -269,28 +256,66 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucket(
 // chunk per K block (1 KiB per wave-wide load), 4 blocks per group, up to kMaxGroups groups
 // per wave all loaded before any arithmetic so that every wave keeps up to 16 loads in flight.
 // Each lane owns one output row; the activation block of the current token is uniform across
-// the wave and comes through scalar loads.  The waves of a workgroup split K; their partial
-// sums meet in LDS in a fixed order.
+// the wave: it is read from an LDS copy of the tokens' activations (broadcast reads) when they
+// fit, else through scalar loads.  The waves of a workgroup split K; their partial sums meet in
+// LDS in a fixed order.
+//
+// Memory operations of a wave complete in issue order, so the issue order is chosen: inputs that
+// are needed first (activations, the route table, scale words) are requested before the bulk of
+// the weight codes, and every load of a phase is unconditional (addresses clamped in range)
+// so that no load sits in a divergent branch that must drain before the next one issues.
 constexpr int kMaxGroups = 4;
 constexpr int kMaxWaves = 16;
-constexpr int kTokPerPass = 8;  // routes of one expert handled per pass (LDS rows)
+constexpr int kTokPerPass = 8;   // routes of one expert handled per pass (LDS rows)
+constexpr int kXLdsBytes = 20480;  // activations of a call staged in LDS up to this size
+constexpr int kXStage = 4;       // 16-byte activation chunks per thread in flight while staging
 
 // Loads the wave's K range: groups g0 .. g0+ngw-1 (ngw <= kMaxGroups, wave-uniform).  Blocks
 // past the last one (nb % 4 != 0) re-read block nb-1 and are later weighted by zero.
+// The scale words come first: their decode is needed before the first block's arithmetic.
 template <int G>
 __device__ __forceinline__ void load_tile_range(const uint4* __restrict__ codes,
                                                 const uint32_t* __restrict__ scl, int nb, int g0,
                                                 int ngw, int lane, uint32_t (&s4)[G],
                                                 uint4 (&c)[4 * G]) {
 #pragma unroll
+  for (int q = 0; q < G; ++q)
+    if (q < ngw) s4[q] = scl[(g0 + q) * 64 + lane];
+#pragma unroll
   for (int q = 0; q < G; ++q) {
     if (q < ngw) {
       const int g = g0 + q;
-      s4[q] = scl[g * 64 + lane];
 #pragma unroll
       for (int i = 0; i < 4; ++i) c[4 * q + i] = codes[min(4 * g + i, nb - 1) * 64 + lane];
     }
   }
+}
+
+// Same sum as dot_tile_range with the activation row in LDS (every lane reads the same
+// address: broadcast).
+template <int G>
+__device__ __forceinline__ float dot_tile_lds(const uint4 (&c)[4 * G], const uint32_t (&s4)[G],
+                                              int nb, int g0, int ngw,
+                                              const uint16_t* act) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+    if (q < ngw) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = 4 * (g0 + q) + i;
+        if (b < nb) {
+          const uint4* a = reinterpret_cast<const uint4*>(act + 32 * b);
+          const float sc = e8m0_to_f32((s4[q] >> (8 * i)) & 0xFFu);
+          acc = fmaf(sc, block_dot(c[4 * q + i], a[0], a[1], a[2], a[3]), acc);
+        }
+        // one block's activations live at a time: keeps the LDS reads from being hoisted
+        // ahead of all blocks (which would need 16 VGPRs per block)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  return acc;
 }
 
 // Keeps the compiler from hoisting the decode of the loaded codes out of a token loop (which
@@ -336,11 +361,12 @@ __device__ __forceinline__ float dot_tile_range(const uint4 (&c)[4 * G], const u
   return acc;
 }
 
-// ---- routes of one call, as seen by an expert workgroup ---------------------------------------
-// For up to kProMaxRoutes routes every expert workgroup rebuilds the route table itself in LDS
-// (top-k from the logits or the given ids, slot resolve, distinct hot experts in ascending id,
-// deterministic bucket order); larger calls read the table the bucketing kernel left in the
-// workspace.  Rebuilding it costs a few hundred cycles and saves a kernel boundary.
+// ---- route table in LDS -----------------------------------------------------------------------
+// For up to kProMaxRoutes routes one workgroup builds the whole route table in LDS: slot of
+// every route, the distinct hot experts in ascending id with their bucket offset and count,
+// and the permutation that groups hot routes by expert (ascending route index inside a group).
+// The expert kernels do this themselves when a call starts from ids or logits (it replaces the
+// top-k / bucketing kernel); the route kernel does it once and leaves the table in the workspace.
 constexpr int kProMaxRoutes = 256;
 
 struct RouteLds {
@@ -353,31 +379,21 @@ struct RouteLds {
   int dist_slot[kProMaxRoutes];
   int dist_off[kProMaxRoutes];
   int dist_cnt[kProMaxRoutes];
+  int dist_e[kProMaxRoutes];
   int nd;
 };
 
-__device__ void route_prologue(RouteLds& rt, const RouteArgs& a, bool writer) {
+// rt.ids / rt.w [0, Mk) must be in place (and visible after a barrier).  e2s may point to LDS.
+__device__ void build_table(RouteLds& rt, int Mk, int E, int S, const int32_t* e2s) {
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
-  const int nw = nthr >> 6;
-  const int Mk = a.M * a.k;
   if (tid == 0) rt.nd = 0;
-  if (a.logits != nullptr) {
-    for (int m = tid >> 6; m < a.M; m += nw)
-      topk_token(a.logits + (size_t)m * a.E, a.E, a.k, rt.ids + m * a.k, rt.w + m * a.k);
-  } else {
-    for (int r = tid; r < Mk; r += nthr) {
-      rt.ids[r] = a.ids_in[r];
-      rt.w[r] = a.w_in[r];
-    }
-  }
-  __syncthreads();
   for (int r = tid; r < Mk; r += nthr) {
     const int e = rt.ids[r];
     int slot = -1;
-    if (e >= 0 && e < a.E) {
-      slot = a.e2s ? a.e2s[e] : e;
-      if (slot < 0 || slot >= a.S) slot = -1;
+    if (e >= 0 && e < E) {
+      slot = e2s ? e2s[e] : e;
+      if (slot < 0 || slot >= S) slot = -1;
     }
     rt.slot[r] = slot;
     int c = 0, before = 0;
@@ -389,10 +405,6 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, bool writer) {
     }
     rt.cnt[r] = c;
     rt.first[r] = before == 0;
-    if (writer && a.topk_ids != nullptr) {
-      a.topk_ids[r] = e;
-      a.topk_w[r] = rt.w[r];
-    }
   }
   __syncthreads();
   for (int r = tid; r < Mk; r += nthr) {
@@ -412,56 +424,214 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, bool writer) {
         rt.dist_slot[di] = rt.slot[r];
         rt.dist_off[di] = off;
         rt.dist_cnt[di] = rt.cnt[r];
+        rt.dist_e[di] = e;
         atomicAdd(&rt.nd, 1);
       }
-    } else if (writer && a.cold_routes != nullptr) {
-      int ci = 0;
-      for (int r2 = 0; r2 < r; ++r2) ci += rt.slot[r2] < 0;
-      a.cold_routes[ci] = r;
     }
   }
-  if (writer && a.cold_count != nullptr && tid < 64) {
+  __syncthreads();
+}
+
+// Caller-visible results of a table: top-k ids / weights and the cold report (any may be NULL).
+__device__ void write_routes(const RouteLds& rt, int Mk, int32_t* topk_ids, float* topk_w,
+                             int32_t* cold_count, int32_t* cold_routes, int32_t* cold_list) {
+  for (int r = threadIdx.x; r < Mk; r += blockDim.x) {
+    if (topk_ids != nullptr) {
+      topk_ids[r] = rt.ids[r];
+      topk_w[r] = rt.w[r];
+    }
+    if (rt.slot[r] < 0 && (cold_routes != nullptr || cold_list != nullptr)) {
+      int ci = 0;
+      for (int r2 = 0; r2 < r; ++r2) ci += rt.slot[r2] < 0;
+      if (cold_routes != nullptr) cold_routes[ci] = r;
+      if (cold_list != nullptr) cold_list[ci] = r;
+    }
+  }
+  if (cold_count != nullptr && threadIdx.x < 64) {
     int c = 0;
-    for (int r = tid; r < Mk; r += 64) c += rt.slot[r] < 0;
+    for (int r = threadIdx.x; r < Mk; r += 64) c += rt.slot[r] < 0;
     c = (int)wave_sum((float)c);
-    if (tid == 0) *a.cold_count = c;
+    if (threadIdx.x == 0) *cold_count = c;
+  }
+}
+
+// The table of rt, as the expert kernels read it from the workspace.
+__device__ void write_table(const RouteLds& rt, int Mk, const RouteWs& w) {
+  for (int r = threadIdx.x; r < Mk; r += blockDim.x) {
+    w.route_slot[r] = rt.slot[r];
+    w.perm[r] = rt.perm[r];  // entries past the hot routes are never read
+  }
+  for (int d = threadIdx.x; d < rt.nd; d += blockDim.x)
+    w.dist[d] = make_int4(rt.dist_slot[d], rt.dist_off[d], rt.dist_cnt[d], rt.dist_e[d]);
+  if (threadIdx.x == 0) {
+    int c = 0;
+    for (int r = 0; r < Mk; ++r) c += rt.slot[r] < 0;
+    w.meta[0] = rt.nd;
+    w.meta[1] = c;
+    w.meta[2] = 0;
+  }
+}
+
+// Route table of an expert workgroup: top-k from the logits or the given ids, then the table.
+// The writer workgroup also publishes the top-k results, the cold report and the table.
+__device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& w, bool writer) {
+  const int tid = threadIdx.x;
+  const int nw = blockDim.x >> 6;
+  const int Mk = a.M * a.k;
+  if (a.logits != nullptr) {
+    for (int m = tid >> 6; m < a.M; m += nw)
+      topk_token(a.logits + (size_t)m * a.E, a.E, a.k, rt.ids + m * a.k, rt.w + m * a.k);
+  } else {
+    for (int r = tid; r < Mk; r += blockDim.x) {
+      rt.ids[r] = a.ids_in[r];
+      rt.w[r] = a.w_in[r];
+    }
   }
   __syncthreads();
+  build_table(rt, Mk, a.E, a.S, a.e2s);
+  if (writer) {
+    write_routes(rt, Mk, a.topk_ids, a.topk_w, a.cold_count, a.cold_routes, nullptr);
+    write_table(rt, Mk, w);
+  }
+}
+
+// ---- router + top-k + route table of a small call in one workgroup ---------------------------
+// For a few tokens and a small router matrix one workgroup of kBucketThreads does the whole
+// route stage: wave w computes logit rows w, w + 16, ... two at a time, each lane holding the
+// chunks lane + 64*i of both rows so that every load of the pair is in flight together (the
+// per-lane dot order and the wave reduction are those of k_router, so the logits are bitwise
+// the same).  The expert map is fetched into LDS alongside.  Logits stay in LDS, top-k runs one
+// wave per token, the table is built in LDS and only written out at the end: no global value
+// is read back, and the expert kernels get a finished table.
+constexpr int kFusedRouteMaxM = 8;
+constexpr int kFusedRouteMaxE = 256;
+constexpr int kFusedRouteChunks = 8;       // 16-byte chunks of a row per lane: H <= 4096
+constexpr int kFusedRouteElems = 1 << 17;  // E * H: at most 256 KiB of router weights
+
+__global__ __launch_bounds__(kBucketThreads) void k_route_table(
+    const uint16_t* __restrict__ x, int M, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int E, int H, int k, int32_t* __restrict__ topk_ids,
+    float* __restrict__ topk_w, int S, const int32_t* __restrict__ e2s,
+    int32_t* __restrict__ cold_count, int32_t* __restrict__ cold_routes, BucketOut o) {
+  __shared__ RouteLds rt;
+  __shared__ float s_logits[kFusedRouteMaxM * kFusedRouteMaxE];
+  __shared__ int32_t s_e2s[kFusedRouteMaxE];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  const int nch = H / 8;
+  const int map_e = tid < E ? (e2s != nullptr ? e2s[tid] : tid) : 0;
+  for (int e0 = wave; e0 < E; e0 += 2 * nw) {
+    const int e1 = e0 + nw;
+    const uint4* r0 = reinterpret_cast<const uint4*>(wr + (size_t)e0 * H);
+    const uint4* r1 = reinterpret_cast<const uint4*>(wr + (size_t)(e1 < E ? e1 : e0) * H);
+    uint4 w0[kFusedRouteChunks], w1[kFusedRouteChunks];
+#pragma unroll
+    for (int i = 0; i < kFusedRouteChunks; ++i) {
+      const int c = lane + 64 * i;
+      w0[i] = c < nch ? r0[c] : make_uint4(0, 0, 0, 0);
+      w1[i] = c < nch ? r1[c] : make_uint4(0, 0, 0, 0);
+    }
+    const float b0 = bias != nullptr ? bias[e0] : 0.0f;
+    const float b1 = (bias != nullptr && e1 < E) ? bias[e1] : 0.0f;
+    for (int m = 0; m < M; ++m) {
+      const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * H);
+      float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kFusedRouteChunks; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nch) {
+          const uint4 xv = xr[c];
+          a0 = dot8_bf16(w0[i], xv, a0);
+          a1 = dot8_bf16(w1[i], xv, a1);
+        }
+      }
+      a0 = wave_sum(a0);
+      a1 = wave_sum(a1);
+      if (lane == 0) {
+        s_logits[m * E + e0] = a0 + b0;
+        if (e1 < E) s_logits[m * E + e1] = a1 + b1;
+      }
+    }
+  }
+  if (tid < E) s_e2s[tid] = map_e;
+  __syncthreads();
+  for (int m = wave; m < M; m += nw) topk_token(s_logits + m * E, E, k, rt.ids + m * k, rt.w + m * k);
+  __syncthreads();
+  const int Mk = M * k;
+  build_table(rt, Mk, E, S, s_e2s);
+  write_routes(rt, Mk, topk_ids, topk_w, cold_count, cold_routes, o.cold_list);
+  RouteWs w;
+  w.meta = o.meta;
+  w.dist = o.dist;
+  w.perm = o.ws_perm;
+  w.route_slot = o.route_slot;
+  write_table(rt, Mk, w);
 }
 
 // ---- gate/up + SiLU*up ----------------------------------------------------------------------
 // grid = (I/32 tiles, nd_max); block = nw waves.  Lane l < 32 accumulates gate row 32*tile + l,
 // lane l >= 32 the matching up row; wave w covers groups [w*ng/nw, (w+1)*ng/nw).
-template <bool SINGLE, int G, bool PRO>
+// SINGLE: one token per call (M = 1), one route per expert.  XLDS: the M activation rows are
+// staged in LDS (M*H*2 <= kXLdsBytes), requested before anything else.
+template <bool SINGLE, int G, bool PRO, bool XLDS>
 __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
     const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
     size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, RouteArgs ra, RouteWs rw,
     uint16_t* __restrict__ hbuf) {
   __shared__ float red[kMaxWaves][SINGLE ? 1 : kTokPerPass][64];
   __shared__ RouteLds rt;
+  __shared__ __align__(16) uint16_t xs[XLDS ? kXLdsBytes / 2 : 8];
   const int tile = blockIdx.x;
   const int d = blockIdx.y;
   const int Mk = ra.M * ra.k;
+  const int nthr = blockDim.x;
+
+  // Activations: kXStage chunks per thread are requested first and stored to LDS as soon as
+  // they arrive, in the same basic block as their loads (the compiler would otherwise sink the
+  // loads to their use, behind the weight loads).  The route-table reads are issued in
+  // between, so both latencies overlap.  Loads and stores are unconditional (a branch around
+  // them costs a full drain): indices are clamped, and a clamped duplicate stores the same
+  // value as the chunk's owner.
+  const int n_x = XLDS ? ra.M * H / 8 : 0;
+  const uint4* xg = reinterpret_cast<const uint4*>(x);
+  uint4* xl = reinterpret_cast<uint4*>(xs);
+  if (XLDS) {
+    uint4 xv[kXStage];
+#pragma unroll
+    for (int i = 0; i < kXStage; ++i) xv[i] = xg[min(i * nthr + (int)threadIdx.x, n_x - 1)];
+#pragma unroll
+    for (int i = 0; i < kXStage; ++i) xl[min(i * nthr + (int)threadIdx.x, n_x - 1)] = xv[i];
+  }
+
   int slot, cnt, off;
   const int* perm;
   if (PRO) {
-    route_prologue(rt, ra, tile == 0 && d == 0);
+    route_prologue(rt, ra, rw, tile == 0 && d == 0);
     if (d >= rt.nd) return;
     slot = rt.dist_slot[d];
     cnt = rt.dist_cnt[d];
     off = rt.dist_off[d];
     perm = rt.perm;
   } else {
-    if (d >= rw.meta[0]) return;
-    slot = rw.dist_slot[d];
-    cnt = rw.dist_cnt[d];
-    off = rw.dist_off[d];
+    // both table reads are consumed by the test, so they are issued together (a load used
+    // only past a branch is moved behind it); d < nd_max keeps dist[d] in bounds
+    const int nd = rw.meta[0];
+    const int4 dd = rw.dist[d];
+    const uint8_t* tb0 = slots + (size_t)tile * gu_tile_bytes;
+    asm volatile("" : "+s"(tb0));  // kernel arguments fetched now, not after the test
+    if (d >= nd || dd.z <= 0) return;  // the whole workgroup leaves together
+    slots = tb0 - (size_t)tile * gu_tile_bytes;
+    slot = dd.x;
+    off = dd.y;
+    cnt = dd.z;
     perm = rw.perm;
   }
   if (cnt <= 0 || off < 0 || off + cnt > Mk) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x >> 6;
+  const int nw = nthr >> 6;
 
   const uint8_t* tbase = slots + (size_t)slot * image_bytes + (size_t)tile * gu_tile_bytes;
   const uint4* codes = reinterpret_cast<const uint4*>(tbase);
@@ -471,22 +641,40 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
   uint32_t s4[G];
   uint4 c[4 * G];
   load_tile_range<G>(codes, scl, nb, g0, ngw, lane, s4, c);
+  if (XLDS) {
+    for (int idx = kXStage * nthr + (int)threadIdx.x; idx < n_x; idx += nthr) xl[idx] = xg[idx];
+    __syncthreads();
+  }
 
+  if (SINGLE) {
+    // M = 1: the only route of this expert belongs to token 0.  No loop around the dot, so the
+    // decode of the codes cannot be hoisted ahead of it.
+    red[wave][0][lane] = dot_tile_lds<G>(c, s4, nb, g0, ngw, xs);
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int row = threadIdx.x;
+      float g = 0.0f, u = 0.0f;
+      for (int w = 0; w < nw; ++w) {
+        g += red[w][0][row];
+        u += red[w][0][row + 32];
+      }
+      const int r = perm[off];
+      hbuf[(size_t)r * I + tile * 32 + row] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
+    }
+    return;
+  }
   for (int base = 0; base < cnt; base += kTokPerPass) {
     const int nt = min(kTokPerPass, cnt - base);
-    if (SINGLE) {  // one token per call: one route per expert, arithmetic overlaps the loads
-      const int r = __builtin_amdgcn_readfirstlane(perm[off]);
-      red[wave][0][lane] = dot_tile_range<G>(c, s4, nb, g0, ngw, x + (size_t)(r / ra.k) * H);
-    } else {
 #pragma unroll 1
-      for (int t = 0; t < nt; ++t) {
-        opaque<G>(c);
-        const int r = __builtin_amdgcn_readfirstlane(perm[off + base + t]);
-        red[wave][t][lane] = dot_tile_range<G>(c, s4, nb, g0, ngw, x + (size_t)(r / ra.k) * H);
-      }
+    for (int t = 0; t < nt; ++t) {
+      opaque<G>(c);
+      const int r = __builtin_amdgcn_readfirstlane(perm[off + base + t]);
+      const int tok = r / ra.k;
+      red[wave][t][lane] = XLDS ? dot_tile_lds<G>(c, s4, nb, g0, ngw, xs + (size_t)tok * H)
+                                : dot_tile_range<G>(c, s4, nb, g0, ngw, x + (size_t)tok * H);
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < nt * 32; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < nt * 32; idx += nthr) {
       const int t = idx >> 5;
       const int row = idx & 31;
       float g = 0.0f, u = 0.0f;
@@ -524,96 +712,118 @@ __device__ __forceinline__ float seg_sum(float v) {
 }
 
 constexpr int kDownWaves = 4;
-constexpr int kDownMaxSteps = 16;
 
-template <int S, bool PRO>
+// Loads one expert's down tile for this lane: scale words first, then TM code steps.  Steps
+// past T re-read step T-1 and lanes without a block in the partial step re-read one of their
+// row's blocks; both are weighted by zero later.  No load depends on a lane test.
+template <int S, int TM>
+__device__ __forceinline__ void load_down_tile(const uint8_t* __restrict__ tb, size_t code_bytes,
+                                               int full, int rem, int T, int tq, int lane,
+                                               uint4 (&c)[TM], uint32_t (&s4)[TM / 4]) {
+  constexpr int RD = 64 / S;
+  const int r = lane / S;
+  const int sg = lane % S;
+  const int psg = rem > 0 ? min(sg, rem - 1) : 0;
+  const uint4* codes = reinterpret_cast<const uint4*>(tb);
+  const uint32_t* scl = reinterpret_cast<const uint32_t*>(tb + code_bytes);
+#pragma unroll
+  for (int q = 0; q < TM / 4; ++q) s4[q] = scl[min(q, tq - 1) * 64 + lane];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    const int tt = min(t, T - 1);
+    c[t] = codes[tt < full ? tt * 64 + lane : full * 64 + r * rem + psg];
+  }
+  (void)RD;
+}
+
+// TM: steps held per lane (T <= TM, a multiple of 4).  HL: h of every route is staged in LDS
+// (else read from the workspace).  The route table comes from the workspace: the route kernel,
+// the bucketing kernel or the gate/up writer workgroup left it there.
+template <int S, int TM, bool HL>
 __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
     int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
     size_t dn_tile_bytes, int nb, int T, int tq, RouteArgs ra, RouteWs rw,
-    const uint16_t* __restrict__ hbuf, int h_in_lds, int part_in_lds, float* __restrict__ pdn,
+    const uint16_t* __restrict__ hbuf, int part_in_lds, float* __restrict__ pdn,
     float* __restrict__ y) {
   constexpr int RD = 64 / S;
-  extern __shared__ __align__(16) uint8_t smem[];
-  __shared__ RouteLds rt;
+  extern __shared__ __align__(16) uint8_t smem[];  // [h copy (HL) | row sums]
   const int tile = blockIdx.x;
   const int Mk = ra.M * ra.k;
-  int nd;
-  if (PRO) {
-    route_prologue(rt, ra, false);
-    nd = rt.nd;
-  } else {
-    nd = rw.meta[0];
-  }
-  const int* route_slot = PRO ? rt.slot : rw.route_slot;
-  const float* wts = PRO ? rt.w : ra.w_in;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane / S;
   const int sg = lane % S;
-  const int full = nb / S;      // steps with all lanes active
+  const int full = nb / S;        // steps with all lanes active
   const int rem = nb - full * S;  // active segments in the final partial step
-
-  // The first expert's weights are requested before h is staged, so that both latencies overlap.
   const uint8_t* sec = slots + gu_bytes + (size_t)tile * dn_tile_bytes;
   const size_t code_bytes = ((size_t)full * 64 + (size_t)RD * rem) * 16;
-  uint4 c[kDownMaxSteps];
-  uint32_t s4[kDownMaxSteps / 4];
-  auto load_expert = [&](int d) {
-    const int slot = PRO ? rt.dist_slot[d] : rw.dist_slot[d];
-    const uint8_t* tb = sec + (size_t)slot * image_bytes;
-    const uint4* codes = reinterpret_cast<const uint4*>(tb);
-#pragma unroll
-    for (int t = 0; t < kDownMaxSteps; ++t) {
-      if (t < full) c[t] = codes[t * 64 + lane];
-      else if (t == full && sg < rem) c[t] = codes[full * 64 + r * rem + sg];
-      else c[t] = make_uint4(0, 0, 0, 0);
-    }
-    const uint32_t* scl = reinterpret_cast<const uint32_t*>(tb + code_bytes);
-#pragma unroll
-    for (int q = 0; q < kDownMaxSteps / 4; ++q) s4[q] = q < tq ? scl[q * 64 + lane] : 0u;
-  };
-  if (wave < nd) load_expert(wave);
 
-  // h of every hot route: LDS copy (pitch 80 B per block) or the workspace (pitch 64 B)
-  const uint8_t* hsrc;
-  int hpitch;
-  if (h_in_lds) {
-    uint8_t* hs = smem;
-    for (int idx = threadIdx.x; idx < Mk * nb * 4; idx += blockDim.x) {
-      const int route = idx / (nb * 4);
-      const int rb = idx - route * nb * 4;
-      if (route_slot[route] >= 0)
-        *reinterpret_cast<uint4*>(hs + ((size_t)route * nb + (rb >> 2)) * 80 + (rb & 3) * 16) =
-            *reinterpret_cast<const uint4*>(hbuf + (size_t)route * I + (rb >> 2) * 32 + (rb & 3) * 8);
+  // Front: table reads, the h copy, then the first expert's weights.  A wave without an
+  // expert of its own re-reads one that another wave loads (dist[0], or slot 0 when no expert
+  // is hot) and computes nothing with it.
+  const int nd_max = Mk < ra.E ? Mk : ra.E;
+  const int nd = rw.meta[0];
+  const int sw = rw.dist[wave < nd_max ? wave : nd_max - 1].x;
+  const int s0 = rw.dist[0].x;
+  const int slot0 = nd == 0 ? 0 : (wave < nd ? sw : s0);
+  const int n_h = Mk * nb * 4;  // 16-byte chunks of h
+  if (HL) {
+    // h goes straight from the workspace to LDS (no registers), one 1 KiB run of 64 chunks per
+    // wave instruction; lane i of a run writes LDS chunk base + i, so the layout permutes the
+    // source instead: LDS chunk (route, block b, q') holds quarter q' ^ ((b >> 1) & 3) of block
+    // b, which puts the S segments of a row on distinct banks.  Runs past n_h re-read the
+    // last chunk into padding.
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int runs = (n_h + 63) / 64;
+    for (int run = wave; run < runs; run += kDownWaves) {
+      const int p = min(run * 64 + lane, n_h - 1);
+      const int route = p / (nb * 4);
+      const int rb = p - route * nb * 4;
+      const int b = rb >> 2;
+      const int q = (rb & 3) ^ ((b >> 1) & 3);
+      const uint16_t* src = hbuf + (size_t)route * I + b * 32 + q * 8;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(smem + (size_t)run * 1024), 16, 0, 0);
     }
-    hsrc = hs;
-    hpitch = 80;
-  } else {
-    hsrc = reinterpret_cast<const uint8_t*>(hbuf);
-    hpitch = 64;
   }
-  float* part = part_in_lds ? reinterpret_cast<float*>(smem + (h_in_lds ? (size_t)Mk * nb * 80 : 0))
+  uint4 c[TM];
+  uint32_t s4[TM / 4];
+  __builtin_amdgcn_sched_barrier(0);  // the h copy is requested before the weights
+  load_down_tile<S, TM>(sec + (size_t)slot0 * image_bytes, code_bytes, full, rem, T, tq, lane, c, s4);
+  float* part = part_in_lds ? reinterpret_cast<float*>(smem + (HL ? (size_t)(n_h + 63) / 64 * 1024 : 0))
                             : pdn + (size_t)tile * Mk * RD;
   __syncthreads();
 
   for (int d = wave; d < nd; d += kDownWaves) {
-    const int cnt = PRO ? rt.dist_cnt[d] : rw.dist_cnt[d];
-    const int off = PRO ? rt.dist_off[d] : rw.dist_off[d];
-    const int* perm = PRO ? rt.perm : rw.perm;
-    if (d != wave) load_expert(d);
+    const int4 dd = rw.dist[d];
+    if (d != wave)
+      load_down_tile<S, TM>(sec + (size_t)dd.x * image_bytes, code_bytes, full, rem, T, tq, lane, c, s4);
+    const int off = dd.y, cnt = dd.z;
     if (cnt <= 0 || off < 0 || off + cnt > Mk) continue;
 #pragma unroll 1
     for (int j = 0; j < cnt; ++j) {
-      const int route = perm[off + j];
-      const uint8_t* hr = hsrc + (size_t)route * nb * hpitch;
+      const int route = rw.perm[off + j];
       float acc = 0.0f;
 #pragma unroll
-      for (int t = 0; t < kDownMaxSteps; ++t) {
+      for (int t = 0; t < TM; ++t) {
         const int b = t * S + sg;
         if (t < T && b < nb) {
-          const uint4* a = reinterpret_cast<const uint4*>(hr + (size_t)b * hpitch);
+          uint4 a0, a1, a2, a3;
+          if (HL) {
+            const uint4* hb = reinterpret_cast<const uint4*>(smem) + ((size_t)route * nb + b) * 4;
+            const int f = (b >> 1) & 3;
+            a0 = hb[0 ^ f];
+            a1 = hb[1 ^ f];
+            a2 = hb[2 ^ f];
+            a3 = hb[3 ^ f];
+          } else {
+            const uint4* hb = reinterpret_cast<const uint4*>(hbuf + (size_t)route * I + b * 32);
+            a0 = hb[0];
+            a1 = hb[1];
+            a2 = hb[2];
+            a3 = hb[3];
+          }
           const float sc = e8m0_to_f32((s4[t >> 2] >> (8 * (t & 3))) & 0xFFu);
-          acc = fmaf(sc, block_dot(c[t], a[0], a[1], a[2], a[3]), acc);
+          acc = fmaf(sc, block_dot(c[t], a0, a1, a2, a3), acc);
         }
       }
       acc = seg_sum<S>(acc);
@@ -627,7 +837,7 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
     float acc = 0.0f;
     for (int j = 0; j < ra.k; ++j) {
       const int route = m * ra.k + j;
-      if (route_slot[route] >= 0) acc = fmaf(wts[route], part[route * RD + rr], acc);
+      if (rw.route_slot[route] >= 0) acc = fmaf(ra.w_in[route], part[route * RD + rr], acc);
     }
     y[(size_t)m * H + tile * RD + rr] = acc;
   }
@@ -640,6 +850,20 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
                          int H, float* logits, hipStream_t s) {
   hipLaunchKernelGGL(k_router, dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits);
+  return hipGetLastError();
+}
+
+bool route_fusable(int M, int E, int H) {
+  return M >= 1 && M <= kFusedRouteMaxM && E <= kFusedRouteMaxE && H <= 64 * 8 * kFusedRouteChunks &&
+         (long)E * H <= kFusedRouteElems;
+}
+
+hipError_t launch_route_table(const uint16_t* x, int M, const uint16_t* wr, const float* bias,
+                              int E, int H, int k, int32_t* topk_ids, float* topk_w, int S,
+                              const int32_t* e2s, int32_t* cold_count, int32_t* cold_routes,
+                              const BucketOut& o, hipStream_t s) {
+  hipLaunchKernelGGL(k_route_table, dim3(1), dim3(kBucketThreads), 0, s, x, M, wr, bias, E, H, k,
+                     topk_ids, topk_w, S, e2s, cold_count, cold_routes, o);
   return hipGetLastError();
 }
 
@@ -658,7 +882,7 @@ hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_i
   const int grid = (logits != nullptr && !do_bucket) ? (M + per_wg - 1) / per_wg : 1;
   hipLaunchKernelGGL(k_topk_bucket, dim3(grid > 0 ? grid : 1), dim3(kBucketThreads), 0, s, logits,
                      M, k, topk_ids, topk_w, do_bucket ? 1 : 0, ids, Mk, E, S, e2s, o.route_slot,
-                     o.ws_perm, o.meta, o.dist_expert, o.dist_slot, o.dist_off, o.dist_cnt, nd_max,
+                     o.ws_perm, o.meta, o.dist, nd_max,
                      o.cold_list, o.u_counts, o.u_offsets, o.u_perm, o.u_cold_count,
                      o.u_cold_routes);
   return hipGetLastError();
@@ -691,7 +915,7 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
   p.gu_waves = best < 1 ? 1 : best;
   p.gu_groups = (L.ng_h + p.gu_waves - 1) / p.gu_waves;
   // down: h in LDS when every route's h fits, partial sums in LDS when they fit
-  const size_t h_lds = (size_t)Mk * L.nb_i * 80;
+  const size_t h_lds = ((size_t)Mk * L.nb_i * 4 + 63) / 64 * 1024;  // whole 1 KiB runs
   const size_t part = (size_t)Mk * L.dn_rows * 4;
   p.h_in_lds = h_lds + part <= kDownLdsBudget;
   p.part_in_lds = (p.h_in_lds ? h_lds : 0) + part <= kDownLdsBudget;
@@ -703,24 +927,39 @@ hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* 
                          const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                          const RouteWs& rw, uint16_t* hbuf, hipStream_t s) {
   const dim3 g(L.gu_tiles, p.nd_max), b(p.gu_waves * 64);
-#define MOE_GU(SINGLE, G, PRO)                                                                     \
-  hipLaunchKernelGGL((k_gateup<SINGLE, G, PRO>), g, b, 0, s, x, H, I, slots, L.image_bytes,      \
+#define MOE_GU(SINGLE, G, PRO, XLDS)                                                               \
+  hipLaunchKernelGGL((k_gateup<SINGLE, G, PRO, XLDS>), g, b, 0, s, x, H, I, slots, L.image_bytes, \
                      L.gu_tile_bytes, L.nb_h, L.ng_h, ra, rw, hbuf)
   // the single-token variant lets arithmetic overlap the loads but holds more registers, so
-  // it is only used with at most 3 groups per wave
+  // it is only used with at most 3 groups per wave; M == 1 always fits the LDS copy of x
   const bool single = M == 1 && p.gu_groups <= 3;
-  if (p.prologue) {
-    if (single) {
-      if (p.gu_groups <= 1) MOE_GU(true, 1, true);
-      else if (p.gu_groups == 2) MOE_GU(true, 2, true);
-      else MOE_GU(true, 3, true);
+  const bool xlds = (size_t)M * H * 2 <= (size_t)kXLdsBytes;
+  if (single) {
+    if (p.prologue) {
+      if (p.gu_groups <= 1) MOE_GU(true, 1, true, true);
+      else if (p.gu_groups == 2) MOE_GU(true, 2, true, true);
+      else MOE_GU(true, 3, true, true);
     } else {
-      if (p.gu_groups <= 2) MOE_GU(false, 2, true);
-      else MOE_GU(false, 4, true);
+      if (p.gu_groups <= 1) MOE_GU(true, 1, false, true);
+      else if (p.gu_groups == 2) MOE_GU(true, 2, false, true);
+      else MOE_GU(true, 3, false, true);
+    }
+  } else if (p.prologue) {
+    if (xlds) {
+      if (p.gu_groups <= 2) MOE_GU(false, 2, true, true);
+      else MOE_GU(false, 4, true, true);
+    } else {
+      if (p.gu_groups <= 2) MOE_GU(false, 2, true, false);
+      else MOE_GU(false, 4, true, false);
     }
   } else {
-    if (p.gu_groups <= 2) MOE_GU(false, 2, false);
-    else MOE_GU(false, 4, false);
+    if (xlds) {
+      if (p.gu_groups <= 2) MOE_GU(false, 2, false, true);
+      else MOE_GU(false, 4, false, true);
+    } else {
+      if (p.gu_groups <= 2) MOE_GU(false, 2, false, false);
+      else MOE_GU(false, 4, false, false);
+    }
   }
 #undef MOE_GU
   return hipGetLastError();
@@ -730,20 +969,28 @@ hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLay
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
                        const uint16_t* hbuf, float* pdn, float* y, hipStream_t s) {
   const dim3 g(L.dn_tiles), b(kDownWaves * 64);
-#define MOE_DN(SEG, PRO)                                                                          \
-  hipLaunchKernelGGL((k_down_combine<SEG, PRO>), g, b, p.dn_lds, s, H, I, slots, L.image_bytes, \
-                     L.gu_bytes, L.dn_tile_bytes, L.nb_i, L.dn_steps, L.dn_scale_words, ra, rw,  \
-                     hbuf, p.h_in_lds ? 1 : 0, p.part_in_lds ? 1 : 0, pdn, y)
-  switch (L.dn_seg * 2 + (p.prologue ? 1 : 0)) {
-    case 2 * 8 + 1: MOE_DN(8, true); break;
-    case 2 * 8: MOE_DN(8, false); break;
-    case 2 * 4 + 1: MOE_DN(4, true); break;
-    case 2 * 4: MOE_DN(4, false); break;
-    case 2 * 2 + 1: MOE_DN(2, true); break;
-    case 2 * 2: MOE_DN(2, false); break;
-    case 2 * 1 + 1: MOE_DN(1, true); break;
-    default: MOE_DN(1, false); break;
+#define MOE_DN(SEG, TM, HL)                                                                       \
+  hipLaunchKernelGGL((k_down_combine<SEG, TM, HL>), g, b, p.dn_lds, s, H, I, slots,              \
+                     L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.nb_i, L.dn_steps,              \
+                     L.dn_scale_words, ra, rw, hbuf, p.part_in_lds ? 1 : 0, pdn, y)
+#define MOE_DN_T(SEG, HL)                            \
+  do {                                               \
+    if (L.dn_steps <= 4) MOE_DN(SEG, 4, HL);         \
+    else if (L.dn_steps <= 8) MOE_DN(SEG, 8, HL);    \
+    else if (L.dn_steps <= 12) MOE_DN(SEG, 12, HL);  \
+    else MOE_DN(SEG, 16, HL);                        \
+  } while (0)
+  switch (L.dn_seg * 2 + (p.h_in_lds ? 1 : 0)) {
+    case 2 * 8 + 1: MOE_DN_T(8, true); break;
+    case 2 * 8: MOE_DN_T(8, false); break;
+    case 2 * 4 + 1: MOE_DN_T(4, true); break;
+    case 2 * 4: MOE_DN_T(4, false); break;
+    case 2 * 2 + 1: MOE_DN_T(2, true); break;
+    case 2 * 2: MOE_DN_T(2, false); break;
+    case 2 * 1 + 1: MOE_DN_T(1, true); break;
+    default: MOE_DN_T(1, false); break;
   }
+#undef MOE_DN_T
 #undef MOE_DN
   return hipGetLastError();
 }
