@@ -133,33 +133,31 @@ static RouteWs route_ws(void* ws, const WsLayout& W) {
 
 // Where the routes of a call come from.
 enum class RouteSrc {
-  kTable,   // the route kernel left the finished table in the workspace (ids / w written)
   kLogits,  // router logits in the workspace: top-k still to do
   kIds,     // caller's ids / w
 };
 
-// The expert stages of a call.  Small calls rebuild the route table inside every expert
-// workgroup (from the logits or the ids); larger ones run the top-k / bucketing kernel first,
-// unless the route kernel already left the table.  do_gateup / do_down select the stages.
+// The expert stages of a call.  Small calls (M*k <= 256) rebuild the route table inside every
+// gate/up workgroup (top-k from the logits, or the ids); one of them also publishes it to the
+// workspace for the down kernel.  Larger calls run the top-k / bucketing kernel first, which
+// writes the table.  do_gateup / do_down select the stages.
 static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, RouteSrc src,
                               const float* logits, int32_t* ids, float* w, const int32_t* e2s,
                               const uint8_t* slots, float* y, int32_t* cold_count,
                               int32_t* cold_routes, void* ws, const WsLayout& W, bool do_gateup,
                               bool do_down, hipStream_t stream) {
   const ImageLayout L = image_layout(sh->hidden, sh->inter);
-  ExpertPlan p = plan_experts(L, M, sh->n_experts, sh->top_k);
+  const ExpertPlan p = plan_experts(L, M, sh->n_experts, sh->top_k);
   const RouteWs rw = route_ws(ws, W);
-  hipError_t e;
-  if (src == RouteSrc::kTable) {
-    p.prologue = false;
-  } else if (!p.prologue) {
-    const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, cold_routes);
-    e = launch_topk_bucket(src == RouteSrc::kLogits ? logits : nullptr, M, sh->top_k, ids, w, true,
-                           ids, sh->n_experts, sh->n_slots, e2s, o, stream);
-    if (e != hipSuccess) return hip_fail(e, "top-k / bucket launch");
-  }
-  if (!p.prologue) logits = nullptr;  // ids / w are final from here on
   if (src != RouteSrc::kLogits) logits = nullptr;
+  hipError_t e;
+  if (!p.prologue && do_gateup) {
+    const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, cold_routes);
+    e = launch_topk_bucket(logits, M, sh->top_k, ids, w, true, ids, sh->n_experts, sh->n_slots,
+                           e2s, o, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k / bucket launch");
+    logits = nullptr;  // ids / w are final from here on
+  }
   if (do_gateup) {
     // in the prologue case the writer workgroup publishes top-k results and the cold report
     const RouteArgs ra = route_args(sh, M, logits, ids, w, e2s, logits ? ids : nullptr,
@@ -229,18 +227,11 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, int32_t M, const
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x, w_router, topk_ids and topk_w are required");
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w_router)) & 15)
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x and w_router must be 16-byte aligned");
-  const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
-  hipError_t e;
-  if (route_fusable(M, shape->n_experts, shape->hidden)) {
-    e = launch_route_table(x, M, w_router, router_bias, shape->n_experts, shape->hidden,
-                           shape->top_k, topk_ids, topk_w, shape->n_slots, nullptr, nullptr,
-                           nullptr, o, stream);
-    if (e != hipSuccess) return hip_fail(e, "route launch");
-    return ok();
-  }
   float* logits = at<float>(ws, W.logits);
-  e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits, stream);
+  hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
+                               stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
+  const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
   e = launch_topk_bucket(logits, M, shape->top_k, topk_ids, topk_w, false, topk_ids,
                          shape->n_experts, shape->n_slots, nullptr, o, stream);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
@@ -316,20 +307,10 @@ moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t 
   if (reinterpret_cast<uintptr_t>(w_router) & 15)
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: w_router must be 16-byte aligned");
   float* logits = at<float>(ws, W.logits);
-  hipError_t e;
-  RouteSrc src = RouteSrc::kLogits;
-  if (route_fusable(M, shape->n_experts, shape->hidden)) {
-    // router, top-k and bucketing in one workgroup; the expert kernels read the table
-    const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
-    e = launch_route_table(x, M, w_router, router_bias, shape->n_experts, shape->hidden,
-                           shape->top_k, topk_ids, topk_w, shape->n_slots, expert_to_slot,
-                           cold_count, cold_routes, o, stream);
-    if (e != hipSuccess) return hip_fail(e, "route launch");
-    src = RouteSrc::kTable;
-  } else {
-    e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits, stream);
-    if (e != hipSuccess) return hip_fail(e, "router launch");
-  }
+  hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
+                               stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  const RouteSrc src = RouteSrc::kLogits;
   st = run_experts(shape, x, M, src, logits, topk_ids, topk_w, expert_to_slot, slots, y,
                    cold_count, cold_routes, ws, W, true, true, stream);
   return st != MOE_OK ? st : ok();

@@ -175,11 +175,6 @@ struct RouteWs {
 // Kernel launchers (moe_kernels.hip).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
                          int H, float* logits, hipStream_t s);
-bool route_fusable(int M, int E, int H);
-hipError_t launch_route_table(const uint16_t* x, int M, const uint16_t* wr, const float* bias,
-                              int E, int H, int k, int32_t* topk_ids, float* topk_w, int S,
-                              const int32_t* e2s, int32_t* cold_count, int32_t* cold_routes,
-                              const BucketOut& o, hipStream_t s);
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,
                               const int32_t* e2s, const BucketOut& o, hipStream_t s);

@@ -56,17 +56,43 @@ __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, i
   }
 }
 
-// Softmax / top-k / renormalise of one token by one wave: the k largest logits (ties to the
-// lower id) in descending order and their softmax.
-__device__ void topk_token(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
-                           float* __restrict__ w) {
-  constexpr int kMaxPerLane = kMaxExperts / 64;  // 16
+// Softmax / top-k / renormalise of one token by one wave: the k largest logits in descending
+// order (ties to the lower id; NaN ranks below every number) and their softmax, which equals
+// the full softmax renormalised over the k routes.
+//
+// E <= 64: lane e holds logit e and counts the logits that rank above it (k independent of the
+// cost).  Larger E: k rounds of a wave argmax over PL logits per lane.
+__device__ __forceinline__ float rank_key(float v) { return v != v ? -INFINITY : v; }
+
+__device__ void topk_rank(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
+                          float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
-  float v[kMaxPerLane];
+  const float v = lane < E ? rank_key(lrow[lane]) : -INFINITY;
+  int rank = 0;
+  for (int j = 0; j < E; ++j) {
+    const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+    rank += (o > v || (o == v && j < lane)) ? 1 : 0;
+  }
+  const bool sel = lane < E && rank < k;
+  const uint64_t first = __ballot(lane < E && rank == 0);
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)__ffsll((long long)first) - 1));
+  const float ex = sel ? expf(v - top) : 0.0f;
+  const float den = wave_sum(ex);
+  if (sel) {
+    ids[rank] = lane;
+    w[rank] = ex / den;
+  }
+}
+
+template <int PL>
+__device__ void topk_argmax(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
+                            float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  float v[PL];
 #pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
+  for (int i = 0; i < PL; ++i) {
     const int ee = lane + 64 * i;
-    v[i] = ee < E ? lrow[ee] : -INFINITY;
+    v[i] = ee < E ? rank_key(lrow[ee]) : -INFINITY;
   }
   float my_v = -INFINITY, top = 0.0f;
   int my_i = 0;
@@ -74,7 +100,8 @@ __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int32_t
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) argmax_step(bv, bi, v[i], lane + 64 * i);
+    for (int i = 0; i < PL; ++i)
+      if (lane + 64 * i < E) argmax_step(bv, bi, v[i], lane + 64 * i);
     wave_argmax(bv, bi);  // uniform winner
     if (j == 0) top = bv;
     if (lane == j) {
@@ -83,7 +110,7 @@ __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int32_t
     }
     if ((bi & 63) == lane) {
 #pragma unroll
-      for (int i = 0; i < kMaxPerLane; ++i)
+      for (int i = 0; i < PL; ++i)
         if (i == (bi >> 6)) v[i] = -INFINITY;
     }
   }
@@ -93,6 +120,15 @@ __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int32_t
     ids[lane] = my_i;
     w[lane] = ex / den;
   }
+}
+
+__device__ void topk_token(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
+                           float* __restrict__ w) {
+  if (E <= 64) topk_rank(lrow, E, k, ids, w);
+  else if (E <= 128) topk_argmax<2>(lrow, E, k, ids, w);
+  else if (E <= 256) topk_argmax<4>(lrow, E, k, ids, w);
+  else if (E <= 512) topk_argmax<8>(lrow, E, k, ids, w);
+  else topk_argmax<16>(lrow, E, k, ids, w);
 }
 
 // =============================================================================================
@@ -268,27 +304,29 @@ constexpr int kMaxGroups = 4;
 constexpr int kMaxWaves = 16;
 constexpr int kTokPerPass = 8;   // routes of one expert handled per pass (LDS rows)
 constexpr int kXLdsBytes = 20480;  // activations of a call staged in LDS up to this size
-constexpr int kXStage = 4;       // 16-byte activation chunks per thread in flight while staging
 
-// Loads the wave's K range: groups g0 .. g0+ngw-1 (ngw <= kMaxGroups, wave-uniform).  Blocks
-// past the last one (nb % 4 != 0) re-read block nb-1 and are later weighted by zero.
-// The scale words come first: their decode is needed before the first block's arithmetic.
+// Loads the wave's K range: groups g0 .. g0+ngw-1 (ngw <= G, wave-uniform).  Every load is
+// issued unconditionally, so that the compiler can count outstanding loads exactly and let the
+// arithmetic on each block wait for that block alone: groups past ngw re-read the wave's last
+// group and blocks past nb re-read block nb-1 (both weighted by zero or skipped later).  The
+// scale words come first: their decode is needed before the first block's arithmetic.
 template <int G>
 __device__ __forceinline__ void load_tile_range(const uint4* __restrict__ codes,
                                                 const uint32_t* __restrict__ scl, int nb, int g0,
                                                 int ngw, int lane, uint32_t (&s4)[G],
                                                 uint4 (&c)[4 * G]) {
+  // (the scheduling barriers keep the issue order of the source)
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < G; ++q)
-    if (q < ngw) s4[q] = scl[(g0 + q) * 64 + lane];
+  for (int q = 0; q < G; ++q) s4[q] = scl[(g0 + min(q, ngw - 1)) * 64 + lane];
 #pragma unroll
   for (int q = 0; q < G; ++q) {
-    if (q < ngw) {
-      const int g = g0 + q;
+    const int g = g0 + min(q, ngw - 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) c[4 * q + i] = codes[min(4 * g + i, nb - 1) * 64 + lane];
-    }
+    for (int i = 0; i < 4; ++i) c[4 * q + i] = codes[min(4 * g + i, nb - 1) * 64 + lane];
   }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Same sum as dot_tile_range with the activation row in LDS (every lane reads the same
@@ -495,81 +533,6 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
   }
 }
 
-// ---- router + top-k + route table of a small call in one workgroup ---------------------------
-// For a few tokens and a small router matrix one workgroup of kBucketThreads does the whole
-// route stage: wave w computes logit rows w, w + 16, ... two at a time, each lane holding the
-// chunks lane + 64*i of both rows so that every load of the pair is in flight together (the
-// per-lane dot order and the wave reduction are those of k_router, so the logits are bitwise
-// the same).  The expert map is fetched into LDS alongside.  Logits stay in LDS, top-k runs one
-// wave per token, the table is built in LDS and only written out at the end: no global value
-// is read back, and the expert kernels get a finished table.
-constexpr int kFusedRouteMaxM = 8;
-constexpr int kFusedRouteMaxE = 256;
-constexpr int kFusedRouteChunks = 8;       // 16-byte chunks of a row per lane: H <= 4096
-constexpr int kFusedRouteElems = 1 << 17;  // E * H: at most 256 KiB of router weights
-
-__global__ __launch_bounds__(kBucketThreads) void k_route_table(
-    const uint16_t* __restrict__ x, int M, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int E, int H, int k, int32_t* __restrict__ topk_ids,
-    float* __restrict__ topk_w, int S, const int32_t* __restrict__ e2s,
-    int32_t* __restrict__ cold_count, int32_t* __restrict__ cold_routes, BucketOut o) {
-  __shared__ RouteLds rt;
-  __shared__ float s_logits[kFusedRouteMaxM * kFusedRouteMaxE];
-  __shared__ int32_t s_e2s[kFusedRouteMaxE];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nw = blockDim.x >> 6;
-  const int nch = H / 8;
-  const int map_e = tid < E ? (e2s != nullptr ? e2s[tid] : tid) : 0;
-  for (int e0 = wave; e0 < E; e0 += 2 * nw) {
-    const int e1 = e0 + nw;
-    const uint4* r0 = reinterpret_cast<const uint4*>(wr + (size_t)e0 * H);
-    const uint4* r1 = reinterpret_cast<const uint4*>(wr + (size_t)(e1 < E ? e1 : e0) * H);
-    uint4 w0[kFusedRouteChunks], w1[kFusedRouteChunks];
-#pragma unroll
-    for (int i = 0; i < kFusedRouteChunks; ++i) {
-      const int c = lane + 64 * i;
-      w0[i] = c < nch ? r0[c] : make_uint4(0, 0, 0, 0);
-      w1[i] = c < nch ? r1[c] : make_uint4(0, 0, 0, 0);
-    }
-    const float b0 = bias != nullptr ? bias[e0] : 0.0f;
-    const float b1 = (bias != nullptr && e1 < E) ? bias[e1] : 0.0f;
-    for (int m = 0; m < M; ++m) {
-      const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * H);
-      float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kFusedRouteChunks; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nch) {
-          const uint4 xv = xr[c];
-          a0 = dot8_bf16(w0[i], xv, a0);
-          a1 = dot8_bf16(w1[i], xv, a1);
-        }
-      }
-      a0 = wave_sum(a0);
-      a1 = wave_sum(a1);
-      if (lane == 0) {
-        s_logits[m * E + e0] = a0 + b0;
-        if (e1 < E) s_logits[m * E + e1] = a1 + b1;
-      }
-    }
-  }
-  if (tid < E) s_e2s[tid] = map_e;
-  __syncthreads();
-  for (int m = wave; m < M; m += nw) topk_token(s_logits + m * E, E, k, rt.ids + m * k, rt.w + m * k);
-  __syncthreads();
-  const int Mk = M * k;
-  build_table(rt, Mk, E, S, s_e2s);
-  write_routes(rt, Mk, topk_ids, topk_w, cold_count, cold_routes, o.cold_list);
-  RouteWs w;
-  w.meta = o.meta;
-  w.dist = o.dist;
-  w.perm = o.ws_perm;
-  w.route_slot = o.route_slot;
-  write_table(rt, Mk, w);
-}
-
 // ---- gate/up + SiLU*up ----------------------------------------------------------------------
 // grid = (I/32 tiles, nd_max); block = nw waves.  Lane l < 32 accumulates gate row 32*tile + l,
 // lane l >= 32 the matching up row; wave w covers groups [w*ng/nw, (w+1)*ng/nw).
@@ -588,28 +551,45 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
   const int Mk = ra.M * ra.k;
   const int nthr = blockDim.x;
 
-  // Activations: kXStage chunks per thread are requested first and stored to LDS as soon as
-  // they arrive, in the same basic block as their loads (the compiler would otherwise sink the
-  // loads to their use, behind the weight loads).  The route-table reads are issued in
-  // between, so both latencies overlap.  Loads and stores are unconditional (a branch around
-  // them costs a full drain): indices are clamped, and a clamped duplicate stores the same
-  // value as the chunk's owner.
+  // Activations to LDS, requested before anything else so that their latency overlaps the
+  // route-table reads.
+  //  - Route table from the workspace: through registers, 4 chunks per thread (clamped; a
+  //    duplicate stores the same value as its owner), loads and stores in this one basic block
+  //    (the compiler would otherwise sink the loads to their use, behind the weight loads).
+  //    The compute then waits for each weight block as it arrives.
+  //  - Table built here (prologue): global-to-LDS copies, one 1 KiB run of 64 chunks per wave
+  //    instruction, left in flight across the prologue.  (After such copies the compiler waits
+  //    for every outstanding load before the first LDS read, so the compute starts once all
+  //    weights have landed.)
   const int n_x = XLDS ? ra.M * H / 8 : 0;
-  const uint4* xg = reinterpret_cast<const uint4*>(x);
-  uint4* xl = reinterpret_cast<uint4*>(xs);
-  if (XLDS) {
-    uint4 xv[kXStage];
+  if (XLDS && !PRO) {
+    const uint4* xg = reinterpret_cast<const uint4*>(x);
+    uint4* xl = reinterpret_cast<uint4*>(xs);
+    uint4 xv[4];
 #pragma unroll
-    for (int i = 0; i < kXStage; ++i) xv[i] = xg[min(i * nthr + (int)threadIdx.x, n_x - 1)];
+    for (int i = 0; i < 4; ++i) xv[i] = xg[min(i * nthr + (int)threadIdx.x, n_x - 1)];
 #pragma unroll
-    for (int i = 0; i < kXStage; ++i) xl[min(i * nthr + (int)threadIdx.x, n_x - 1)] = xv[i];
+    for (int i = 0; i < 4; ++i) xl[min(i * nthr + (int)threadIdx.x, n_x - 1)] = xv[i];
+    for (int idx = 4 * nthr + (int)threadIdx.x; idx < n_x; idx += nthr) xl[idx] = xg[idx];
+  }
+  if (XLDS && PRO) {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int runs = (n_x + 63) / 64;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int run = wv; run < runs; run += nthr >> 6) {
+      const int p = min(run * 64 + (int)(threadIdx.x & 63), n_x - 1);
+      __builtin_amdgcn_global_load_lds(x + (size_t)p * 8, (lds_void*)(xs + (size_t)run * 512), 16, 0, 0);
+    }
   }
 
   int slot, cnt, off;
   const int* perm;
   if (PRO) {
     route_prologue(rt, ra, rw, tile == 0 && d == 0);
-    if (d >= rt.nd) return;
+    if (d >= rt.nd) {
+      if (XLDS) __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
+      return;
+    }
     slot = rt.dist_slot[d];
     cnt = rt.dist_cnt[d];
     off = rt.dist_off[d];
@@ -619,10 +599,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
     // only past a branch is moved behind it); d < nd_max keeps dist[d] in bounds
     const int nd = rw.meta[0];
     const int4 dd = rw.dist[d];
-    const uint8_t* tb0 = slots + (size_t)tile * gu_tile_bytes;
-    asm volatile("" : "+s"(tb0));  // kernel arguments fetched now, not after the test
+    asm volatile("" : "+s"(image_bytes), "+s"(gu_tile_bytes));  // fetched now, not after the test
     if (d >= nd || dd.z <= 0) return;  // the whole workgroup leaves together
-    slots = tb0 - (size_t)tile * gu_tile_bytes;
     slot = dd.x;
     off = dd.y;
     cnt = dd.z;
@@ -641,10 +619,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
   uint32_t s4[G];
   uint4 c[4 * G];
   load_tile_range<G>(codes, scl, nb, g0, ngw, lane, s4, c);
-  if (XLDS) {
-    for (int idx = kXStage * nthr + (int)threadIdx.x; idx < n_x; idx += nthr) xl[idx] = xg[idx];
-    __syncthreads();
-  }
+  if (XLDS) __syncthreads();  // activations in LDS for every wave
 
   if (SINGLE) {
     // M = 1: the only route of this expert belongs to token 0.  No loop around the dot, so the
@@ -850,20 +825,6 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
                          int H, float* logits, hipStream_t s) {
   hipLaunchKernelGGL(k_router, dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits);
-  return hipGetLastError();
-}
-
-bool route_fusable(int M, int E, int H) {
-  return M >= 1 && M <= kFusedRouteMaxM && E <= kFusedRouteMaxE && H <= 64 * 8 * kFusedRouteChunks &&
-         (long)E * H <= kFusedRouteElems;
-}
-
-hipError_t launch_route_table(const uint16_t* x, int M, const uint16_t* wr, const float* bias,
-                              int E, int H, int k, int32_t* topk_ids, float* topk_w, int S,
-                              const int32_t* e2s, int32_t* cold_count, int32_t* cold_routes,
-                              const BucketOut& o, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_table, dim3(1), dim3(kBucketThreads), 0, s, x, M, wr, bias, E, H, k,
-                     topk_ids, topk_w, S, e2s, cold_count, cold_routes, o);
   return hipGetLastError();
 }
 

@@ -168,8 +168,9 @@ moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t 
  *   moe_experts_gateup: h = bf16(silu(Wg x) * (Wu x)) for every hot route, kept in the
  *                       workspace [tinyserve, "How it works" item 2: gate and up fused here].
  *   moe_experts_down:   y = ordered sum over hot routes of topk_w * (Wd h), as in
- *                       moe_experts_forward; needs the h that the last moe_experts_gateup (or
- *                       moe_experts_forward) with the same routes left in this workspace.
+ *                       moe_experts_forward; needs the h and the route table that the last
+ *                       moe_experts_gateup (or moe_experts_forward) with the same routes and
+ *                       expert_to_slot left in this workspace.
  * moe_experts_gateup + moe_experts_down == moe_experts_forward (without the cold report). */
 moe_status moe_experts_gateup(const moe_shape* shape, const uint16_t* x, int32_t M,
                               const int32_t* topk_ids, const float* topk_w,
