@@ -163,14 +163,18 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
     const RouteArgs ra = route_args(sh, M, logits, ids, w, e2s, logits ? ids : nullptr,
                                     logits ? w : nullptr, p.prologue ? cold_count : nullptr,
                                     p.prologue ? cold_routes : nullptr);
-    e = launch_gateup(x, M, sh->hidden, sh->inter, slots, L, p, ra, rw, at<uint16_t>(ws, W.hbuf),
-                      stream);
+    e = p.grouped ? launch_gateup_grouped(x, sh->hidden, sh->inter, slots, L, p, ra, rw,
+                                          at<uint16_t>(ws, W.hbuf), stream)
+                  : launch_gateup(x, M, sh->hidden, sh->inter, slots, L, p, ra, rw,
+                                  at<uint16_t>(ws, W.hbuf), stream);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
   }
   if (do_down) {
     const RouteArgs ra = route_args(sh, M, nullptr, ids, w, e2s, nullptr, nullptr, nullptr, nullptr);
-    e = launch_down(M, sh->hidden, sh->inter, slots, L, p, ra, rw, at<uint16_t>(ws, W.hbuf),
-                    at<float>(ws, W.pdn), y, stream);
+    e = p.grouped ? launch_down_grouped(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
+                                        at<uint16_t>(ws, W.hbuf), at<float>(ws, W.pdn), y, stream)
+                  : launch_down(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
+                                at<uint16_t>(ws, W.hbuf), at<float>(ws, W.pdn), y, stream);
     if (e != hipSuccess) return hip_fail(e, "down launch");
   }
   return MOE_OK;

@@ -142,6 +142,7 @@ struct BucketOut {
 // Launch shape of the expert kernels for one call.
 struct ExpertPlan {
   int nd_max;        // upper bound of distinct hot experts (gate/up grid.y)
+  bool grouped;      // many tokens: grouped GEMM on MFMA (route table from the bucketing kernel)
   bool prologue;     // every expert workgroup rebuilds the route table (M*k <= kProMaxRoutes)
   int gu_waves;      // waves per gate/up workgroup
   int gu_groups;     // most K groups (of 4 blocks) any gate/up wave holds
@@ -185,5 +186,11 @@ hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* 
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
                        const uint16_t* hbuf, float* pdn, float* y, hipStream_t s);
+hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,
+                                 const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
+                                 const RouteWs& rw, uint16_t* hbuf, hipStream_t s);
+hipError_t launch_down_grouped(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
+                               const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
+                               const uint16_t* hbuf, float* pdn, float* y, hipStream_t s);
 
 }  // namespace moe

@@ -820,6 +820,282 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
 
 
 // =============================================================================================
+// Grouped GEMM path (many tokens per expert): bf16 MFMA on dequantised MXFP4 weights
+// =============================================================================================
+// With tens of routes per expert the weights are worth decoding once and reusing for every
+// route, which is a dense contraction: v_mfma_f32_16x16x32_bf16.  Its operands (gfx950):
+//   A (routes x K):   lane l holds A[l % 16][8*(l/16) .. +8]   (8 bf16)
+//   B (weights x K):  lane l holds B[l % 16][8*(l/16) .. +8]
+//   C (routes x rows): lane l, register i holds C[4*(l/16) + i][l % 16].
+// One K step of 32 is one MXFP4 block, so a lane's B fragment is one code dword (8 E2M1 values)
+// converted with the block scale by the gfx950 scaled converter, which is exact.  The B
+// fragments come straight from the expert image: in the gate/up layout wave w, lane l reads
+// dword l/16 of image lane 16w + l%16 (wave 0/1 = gate rows 0-15/16-31, wave 2/3 = up rows),
+// so a wave's read of one block is 256 contiguous bytes.  The routes' activation rows (A) are
+// gathered through the bucket permutation into LDS, KC blocks at a time, double buffered; the
+// next chunk's weights and activations are requested before the current chunk's MFMAs.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kGemmTok = 64;                 // routes per pass: 4 MFMA tiles of 16
+constexpr int kGemmKC = 4;                   // K blocks (of 32) per chunk
+constexpr int kGemmPitch = kGemmKC * 32 + 8;  // bf16 per LDS row: 272 bytes, 16 tokens hit 16 bank groups
+constexpr int kGemmXPerThread = kGemmTok * kGemmKC * 4 / 256;  // 16-byte chunks staged per thread
+
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w, float scale) {
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Activation rows of one pass: 64 rows x KC blocks, 16 bytes per chunk, rows clamped to the pass
+// (rows past it are never stored back) and K clamped to the row (blocks past it meet zero weights).
+struct GemmRows {
+  const uint16_t* row[kGemmTok];
+  int route[kGemmTok];
+};
+
+__device__ __forceinline__ void gemm_load_rows(const GemmRows& gr, int kc, int K,
+                                               uint4 (&xv)[kGemmXPerThread]) {
+#pragma unroll
+  for (int i = 0; i < kGemmXPerThread; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
+    const int tok = c >> 4;
+    const int q = c & 15;  // block q>>2, quarter q&3
+    const int e = min(kc * kGemmKC * 32 + q * 8, K - 8);
+    xv[i] = *reinterpret_cast<const uint4*>(gr.row[tok] + e);
+  }
+}
+
+__device__ __forceinline__ void gemm_store_rows(uint16_t (*xb)[kGemmPitch],
+                                                const uint4 (&xv)[kGemmXPerThread]) {
+#pragma unroll
+  for (int i = 0; i < kGemmXPerThread; ++i) {
+    const int c = (int)threadIdx.x + 256 * i;
+    *reinterpret_cast<uint4*>(&xb[c >> 4][(c & 15) * 8]) = xv[i];
+  }
+}
+
+// grid = (I/32 tiles, nd_max), 256 threads.  h = bf16(silu(Wg x) * (Wu x)) for every route of
+// the workgroup's expert, rows 32*tile .. +32, 64 routes per pass.
+__global__ __launch_bounds__(256) void k_gateup_grouped(
+    const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
+    size_t image_bytes, size_t gu_tile_bytes, int nb, RouteArgs ra, RouteWs rw,
+    uint16_t* __restrict__ hbuf) {
+  __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
+  __shared__ GemmRows gr;
+  const int tile = blockIdx.x;
+  const int d = blockIdx.y;
+  const int Mk = ra.M * ra.k;
+  const int nd = rw.meta[0];
+  if (d >= nd) return;
+  const int4 dd = rw.dist[d];
+  const int slot = dd.x, off = dd.y, cnt = dd.z;
+  if (cnt <= 0 || off < 0 || off + cnt > Mk) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const uint8_t* tb = slots + (size_t)slot * image_bytes + (size_t)tile * gu_tile_bytes;
+  const uint32_t* wsrc = reinterpret_cast<const uint32_t*>(tb + (size_t)(w * 16 + n) * 16 + g * 4);
+  const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(tb + (size_t)nb * 1024 + (w * 16 + n) * 4);
+  const int nkc = (nb + kGemmKC - 1) / kGemmKC;
+  float* out = reinterpret_cast<float*>(&xb[0][0][0]);  // epilogue: [64 routes][65] fp32
+
+  for (int base = 0; base < cnt; base += kGemmTok) {
+    const int nt = min(kGemmTok, cnt - base);
+    const int ntt = (nt + 15) >> 4;
+    for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) {
+      const int r = rw.perm[off + base + min(i, nt - 1)];
+      gr.route[i] = r;
+      gr.row[i] = x + (size_t)(r / ra.k) * H;
+    }
+    __syncthreads();
+    f32x4_t acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    uint4 xv[kGemmXPerThread];
+    uint32_t wc[kGemmKC], sw;
+    auto load_w = [&](int kc) {
+#pragma unroll
+      for (int j = 0; j < kGemmKC; ++j) wc[j] = wsrc[(size_t)min(kc * kGemmKC + j, nb - 1) * 256];
+      sw = ssrc[(size_t)min(kc, (nb - 1) / 4) * 64];  // kGemmKC == 4: one scale word per chunk
+    };
+    gemm_load_rows(gr, 0, H, xv);
+    load_w(0);
+    for (int kc = 0; kc < nkc; ++kc) {
+      const int buf = kc & 1;
+      gemm_store_rows(xb[buf], xv);
+      uint32_t wcur[kGemmKC];
+#pragma unroll
+      for (int j = 0; j < kGemmKC; ++j) wcur[j] = wc[j];
+      const uint32_t scur = sw;
+      if (kc + 1 < nkc) {
+        gemm_load_rows(gr, kc + 1, H, xv);
+        load_w(kc + 1);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kGemmKC; ++j) {
+        const int b = kc * kGemmKC + j;
+        bf16x8_t bw = fp4x8_to_bf16(wcur[j], e8m0_to_f32((scur >> (8 * j)) & 0xFFu));
+        if (b >= nb) bw = bf16x8_t{};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < ntt) {
+            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][j * 32 + g * 8]);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, acc[t], 0, 0, 0);
+          }
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with xb
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[(t * 16 + g * 4 + i) * 65 + w * 16 + n] = acc[t][i];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < nt * 32; idx += blockDim.x) {
+      const int tok = idx >> 5;
+      const int row = idx & 31;
+      const float gt = out[tok * 65 + row];
+      const float up = out[tok * 65 + 32 + row];
+      hbuf[(size_t)gr.route[tok] * I + tile * 32 + row] = (uint16_t)f32_to_bf16_bits(silu_f32(gt) * up);
+    }
+    __syncthreads();  // out and gr are reused by the next pass
+  }
+}
+
+// grid = (H/64 row tiles, nd_max), 256 threads.  d = Wd h for every route of the workgroup's
+// expert, rows 64*tile .. +64 (wave w: rows 16w .. +16), written to pdn[route][row] in fp32;
+// k_combine then forms y in the fixed route order.  B fragments come from the down layout (row
+// r of a down tile at step t holds block t*S + s in lane r*S + s).
+__global__ __launch_bounds__(256) void k_down_grouped(
+    int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
+    size_t dn_tile_bytes, int nb, int S, int T, RouteArgs ra, RouteWs rw,
+    const uint16_t* __restrict__ hbuf, float* __restrict__ pdn) {
+  __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
+  __shared__ GemmRows gr;
+  const int tile = blockIdx.x;
+  const int d = blockIdx.y;
+  const int Mk = ra.M * ra.k;
+  const int nd = rw.meta[0];
+  if (d >= nd) return;
+  const int4 dd = rw.dist[d];
+  const int slot = dd.x, off = dd.y, cnt = dd.z;
+  if (cnt <= 0 || off < 0 || off + cnt > Mk) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int RD = 64 / S;
+  const int full = nb / S, rem = nb - full * S;
+  const size_t code_bytes = ((size_t)full * 64 + (size_t)RD * rem) * 16;
+  const int R = tile * 64 + w * 16 + n;  // this lane's output row
+  const uint8_t* dtile = slots + (size_t)slot * image_bytes + gu_bytes + (size_t)(R / RD) * dn_tile_bytes;
+  const int rr = R % RD;
+  const int nkc = (nb + kGemmKC - 1) / kGemmKC;
+  auto w_at = [&](int b, uint32_t& code, uint32_t& scale_byte) {
+    b = min(b, nb - 1);
+    const int sg = b % S, t = b / S;
+    const size_t idx = t < full ? (size_t)t * 64 + rr * S + sg : (size_t)full * 64 + rr * rem + sg;
+    code = *reinterpret_cast<const uint32_t*>(dtile + idx * 16 + g * 4);
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(dtile + code_bytes + ((size_t)(t >> 2) * 64 + rr * S + sg) * 4);
+    scale_byte = (word >> (8 * (t & 3))) & 0xFFu;
+  };
+  (void)T;
+
+  for (int base = 0; base < cnt; base += kGemmTok) {
+    const int nt = min(kGemmTok, cnt - base);
+    const int ntt = (nt + 15) >> 4;
+    for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) {
+      const int r = rw.perm[off + base + min(i, nt - 1)];
+      gr.route[i] = r;
+      gr.row[i] = hbuf + (size_t)r * I;
+    }
+    __syncthreads();
+    f32x4_t acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    uint4 xv[kGemmXPerThread];
+    uint32_t wc[kGemmKC], wsb[kGemmKC];
+    auto load_w = [&](int kc) {
+#pragma unroll
+      for (int j = 0; j < kGemmKC; ++j) w_at(kc * kGemmKC + j, wc[j], wsb[j]);
+    };
+    gemm_load_rows(gr, 0, I, xv);
+    load_w(0);
+    for (int kc = 0; kc < nkc; ++kc) {
+      const int buf = kc & 1;
+      gemm_store_rows(xb[buf], xv);
+      uint32_t wcur[kGemmKC], scur[kGemmKC];
+#pragma unroll
+      for (int j = 0; j < kGemmKC; ++j) {
+        wcur[j] = wc[j];
+        scur[j] = wsb[j];
+      }
+      if (kc + 1 < nkc) {
+        gemm_load_rows(gr, kc + 1, I, xv);
+        load_w(kc + 1);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kGemmKC; ++j) {
+        const int b = kc * kGemmKC + j;
+        bf16x8_t bw = fp4x8_to_bf16(wcur[j], e8m0_to_f32(scur[j]));
+        if (b >= nb) bw = bf16x8_t{};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < ntt) {
+            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][j * 32 + g * 8]);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, acc[t], 0, 0, 0);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t * 16 + g * 4 + i;
+        if (tok < nt) pdn[(size_t)gr.route[tok] * H + R] = acc[t][i];
+      }
+    __syncthreads();  // xb and gr are reused by the next pass
+  }
+}
+
+// y[m][h] = sum over j ascending of the hot routes m*k+j of w * pdn[m*k+j][h] (cold routes add
+// nothing).  One thread per (token, 4 rows).
+__global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs ra, RouteWs rw,
+                                                 const float* __restrict__ pdn,
+                                                 float* __restrict__ y) {
+  const int q = blockIdx.x * blockDim.x + threadIdx.x;
+  const int per = H / 4;
+  if (q >= M * per) return;
+  const int m = q / per;
+  const int h = (q - m * per) * 4;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int j = 0; j < k; ++j) {
+    const int r = m * k + j;
+    if (rw.route_slot[r] < 0) continue;
+    const float wt = ra.w_in[r];
+    const float4 v = *reinterpret_cast<const float4*>(pdn + (size_t)r * H + h);
+    acc.x = fmaf(wt, v.x, acc.x);
+    acc.y = fmaf(wt, v.y, acc.y);
+    acc.z = fmaf(wt, v.z, acc.z);
+    acc.w = fmaf(wt, v.w, acc.w);
+  }
+  float* yo = y + (size_t)m * H + h;  // the caller's y need not be 16-byte aligned
+  yo[0] = acc.x;
+  yo[1] = acc.y;
+  yo[2] = acc.z;
+  yo[3] = acc.w;
+}
+
+// =============================================================================================
 // Launchers (called from the host API after every argument has been validated)
 // =============================================================================================
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
@@ -851,13 +1127,17 @@ hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_i
 
 
 constexpr int kNumCUs = 256;      // MI355X compute units
+constexpr int kGroupedMinTokens = 64;
 constexpr int kWavesPerCU = 16;   // resident waves per CU for a kernel of <= 128 VGPRs
 
 ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
   ExpertPlan p;
   const int Mk = M * k;
   p.nd_max = Mk < E ? Mk : E;
-  p.prologue = Mk <= kProMaxRoutes;
+  // M >= kGroupedMinTokens: the grouped GEMM (it needs H a multiple of 64 for its row tiles,
+  // which every supported shape is) with the route table from the bucketing kernel
+  p.grouped = M >= kGroupedMinTokens;
+  p.prologue = !p.grouped && Mk <= kProMaxRoutes;
   // gate/up waves per workgroup: each wave holds at most kMaxGroups groups of its tile's K;
   // the kernels are built for <= 128 VGPRs, so a CU holds kWavesPerCU waves.  Pick the widest
   // workgroup that still lets every workgroup of the grid be resident at once.
@@ -953,6 +1233,28 @@ hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLay
   }
 #undef MOE_DN_T
 #undef MOE_DN
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,
+                                 const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
+                                 const RouteWs& rw, uint16_t* hbuf, hipStream_t s) {
+  hipLaunchKernelGGL(k_gateup_grouped, dim3(L.gu_tiles, p.nd_max), dim3(256), 0, s, x, H, I, slots,
+                     L.image_bytes, L.gu_tile_bytes, L.nb_h, ra, rw, hbuf);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_grouped(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
+                               const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
+                               const uint16_t* hbuf, float* pdn, float* y, hipStream_t s) {
+  hipLaunchKernelGGL(k_down_grouped, dim3(H / 64, p.nd_max), dim3(256), 0, s, H, I, slots,
+                     L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.nb_i, L.dn_seg, L.dn_steps, ra,
+                     rw, hbuf, pdn);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int threads = M * (H / 4);
+  hipLaunchKernelGGL(k_combine, dim3((threads + 255) / 256), dim3(256), 0, s, M, ra.k, H, ra, rw,
+                     pdn, y);
   return hipGetLastError();
 }
 

@@ -246,6 +246,40 @@ def test_e512_prefill_sampled_tokens(e512):
     close_enough(y[sample], ref["y_full"], "e512 prefill sampled tokens")
 
 
+@pytest.mark.parametrize("M", [64, 130])
+def test_tiny_grouped_gemm_every_token(tiny, M):
+    """M >= 64 takes the grouped GEMM (MFMA) kernels: every token against the oracle, half the
+    experts cold, 130 = two passes of 64 routes plus a ragged tail for the busiest experts; the
+    layer entry point and the staged calls agree bitwise with the one-call path."""
+    wl = tiny.wl
+    say("tiny grouped GEMM: M =", M)
+    shape = tiny.shape
+    x = synthetic.activations(wl, M, 700 + M)
+    ids_ref, w_ref, _, _ = O.route(O.router_logits(x, tiny.wr), wl.top_k)
+    e2s = np.arange(wl.n_experts, dtype=np.int32)
+    e2s[1::2] = -1
+    buf = L.Buffers(shape, M)
+    y, cc, cold = run_experts(shape, x, ids_ref, w_ref, e2s, tiny.slots, buf, M)
+    ref = O.layer_forward(x, ids_ref, w_ref, tiny.experts, e2s)
+    assert cc == len(ref["cold_routes"]) and np.array_equal(cold, ref["cold_routes"])
+    close_enough(y, ref["y_hot"], f"tiny grouped M={M} y_hot")
+    # all resident, through the layer entry point and the staged calls
+    xd, wr = _dev(x), _dev(tiny.wr)
+    a, c = L.Buffers(shape, M), L.Buffers(shape, M)
+    B.moe_layer_forward(shape, xd, M, wr, None, None, tiny.slots, a.ids, a.w, a.y, a.cold_count,
+                        a.cold_routes, a.ws)
+    B.moe_route(shape, xd, M, wr, None, c.ids, c.w, c.ws)
+    B.moe_experts_gateup(shape, xd, M, c.ids, c.w, None, tiny.slots, c.ws)
+    B.moe_experts_down(shape, M, c.ids, c.w, None, tiny.slots, c.y, c.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a.ids[:M], c.ids[:M]) and torch.equal(a.y[:M], c.y[:M])
+    excluded, ids2, w2 = compare_routes(a.ids[:M].cpu().numpy(), a.w[:M].cpu().numpy(),
+                                        O.router_logits(x, tiny.wr), wl.top_k)
+    assert excluded == 0
+    ref2 = O.layer_forward(x, ids2, w2, tiny.experts)
+    close_enough(a.y[:M].cpu().numpy(), ref2["y_full"], f"tiny grouped layer M={M}")
+
+
 def test_refill_copies_images_exactly(tiny):
     shape = tiny.shape
     say("refill: pinned bank -> slots")
