@@ -66,9 +66,12 @@ _SIGS = {
                             _SZ, _P],
     "moe_layer_forward": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                           _P, _SZ, _P],
+    "moe_layer_forward_marked": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P, _P, _SZ, _P, _P],
     "moe_experts_gateup": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_experts_down": [C.POINTER(moe_shape), _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_slot_refill": [C.POINTER(moe_shape), _P, _P, _P, _P, _I32, _P, _P, _P],
+    "moe_residual_bf16": [_P, _P, _P, _SZ, _P],
     "moe_cache_create": [C.POINTER(moe_shape), C.POINTER(moe_cache_config), _P,
                          C.POINTER(_P)],
     "moe_cache_policy_step": [_P, C.c_int64, _P, _I32, _P, C.POINTER(_I32), _P,
@@ -223,6 +226,18 @@ def moe_layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots,
            "moe_layer_forward")
 
 
+def moe_layer_forward_marked(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids,
+                             topk_w, y, cold_count, cold_routes, ws, marks, stream=None):
+    """moe_layer_forward with four HIP events recorded at its stage boundaries."""
+    ev = (C.c_void_p * 4)(*[C.c_void_p(int(m)) for m in marks])
+    _check(load().moe_layer_forward_marked(C.byref(shape), _ptr(x), int(M), _ptr(w_router),
+                                           _ptr(router_bias), _ptr(expert_to_slot), _ptr(slots),
+                                           _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(cold_count),
+                                           _ptr(cold_routes), _ptr(ws), _nbytes(ws), _stream(stream),
+                                           C.cast(ev, C.c_void_p)),
+           "moe_layer_forward_marked")
+
+
 def moe_experts_gateup(shape, x, M, topk_ids, topk_w, expert_to_slot, slots, ws, stream=None):
     _check(load().moe_experts_gateup(C.byref(shape), _ptr(x), int(M), _ptr(topk_ids), _ptr(topk_w),
                                      _ptr(expert_to_slot), _ptr(slots), _ptr(ws), _nbytes(ws),
@@ -233,6 +248,11 @@ def moe_experts_down(shape, M, topk_ids, topk_w, expert_to_slot, slots, y, ws, s
     _check(load().moe_experts_down(C.byref(shape), int(M), _ptr(topk_ids), _ptr(topk_w),
                                    _ptr(expert_to_slot), _ptr(slots), _ptr(y), _ptr(ws),
                                    _nbytes(ws), _stream(stream)), "moe_experts_down")
+
+
+def moe_residual_bf16(x, y, out, n, stream=None):
+    _check(load().moe_residual_bf16(_ptr(x), _ptr(y), _ptr(out), int(n), _stream(stream)),
+           "moe_residual_bf16")
 
 
 def moe_slot_refill(shape, slots, host_bank, experts, slot_ids, copy_stream=None,

@@ -145,7 +145,7 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
                               const float* logits, int32_t* ids, float* w, const int32_t* e2s,
                               const uint8_t* slots, float* y, int32_t* cold_count,
                               int32_t* cold_routes, void* ws, const WsLayout& W, bool do_gateup,
-                              bool do_down, hipStream_t stream) {
+                              bool do_down, hipStream_t stream, const hipEvent_t* marks = nullptr) {
   const ImageLayout L = image_layout(sh->hidden, sh->inter);
   const ExpertPlan p = plan_experts(L, M, sh->n_experts, sh->top_k);
   const RouteWs rw = route_ws(ws, W);
@@ -158,6 +158,7 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
     if (e != hipSuccess) return hip_fail(e, "top-k / bucket launch");
     logits = nullptr;  // ids / w are final from here on
   }
+  if (marks && (e = hipEventRecord(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (do_gateup) {
     // in the prologue case the writer workgroup publishes top-k results and the cold report
     const RouteArgs ra = route_args(sh, M, logits, ids, w, e2s, logits ? ids : nullptr,
@@ -169,6 +170,7 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
                                   at<uint16_t>(ws, W.hbuf), stream);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
   }
+  if (marks && (e = hipEventRecord(marks[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (do_down) {
     const RouteArgs ra = route_args(sh, M, nullptr, ids, w, e2s, nullptr, nullptr, nullptr, nullptr);
     e = p.grouped ? launch_down_grouped(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
@@ -177,6 +179,7 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
                                 at<uint16_t>(ws, W.hbuf), at<float>(ws, W.pdn), y, stream);
     if (e != hipSuccess) return hip_fail(e, "down launch");
   }
+  if (marks && (e = hipEventRecord(marks[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MOE_OK;
 }
 
@@ -189,6 +192,42 @@ static moe_status empty_call(const moe_shape* sh, const int32_t* e2s, int32_t* c
                                     sh->n_experts, sh->n_slots, e2s, o, stream);
   if (e != hipSuccess) return hip_fail(e, "bucket launch");
   return MOE_OK;
+}
+
+static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                const uint16_t* w_router, const float* router_bias,
+                                const int32_t* expert_to_slot, const uint8_t* slots,
+                                int32_t* topk_ids, float* topk_w, float* y, int32_t* cold_count,
+                             int32_t* cold_routes, void* ws, size_t ws_bytes, hipStream_t stream,
+                                const hipEvent_t* marks) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  WsLayout W;
+  st = check_ws(shape, M, ws, ws_bytes, &W);
+  if (st != MOE_OK) return st;
+  st = check_map(shape, expert_to_slot);
+  if (st != MOE_OK) return st;
+  if (M == 0) {
+    st = empty_call(shape, expert_to_slot, cold_count, ws, W, stream);
+    return st != MOE_OK ? st : ok();
+  }
+  st = check_x_slots(x, slots);
+  if (st != MOE_OK) return st;
+  if (!w_router || !topk_ids || !topk_w || !y)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_layer_forward: w_router, topk_ids, topk_w and y are required");
+  if (reinterpret_cast<uintptr_t>(w_router) & 15)
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: w_router must be 16-byte aligned");
+  float* logits = at<float>(ws, W.logits);
+  hipError_t e;
+  if (marks && (e = hipEventRecord(marks[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
+                               stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  const RouteSrc src = RouteSrc::kLogits;
+  st = run_experts(shape, x, M, src, logits, topk_ids, topk_w, expert_to_slot, slots, y,
+                   cold_count, cold_routes, ws, W, true, true, stream, marks);
+  return st != MOE_OK ? st : ok();
 }
 
 }  // namespace moe
@@ -292,32 +331,21 @@ moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t 
                              const int32_t* expert_to_slot, const uint8_t* slots,
                              int32_t* topk_ids, float* topk_w, float* y, int32_t* cold_count,
                              int32_t* cold_routes, void* ws, size_t ws_bytes, hipStream_t stream) {
-  moe_status st = check_shape(shape);
-  if (st != MOE_OK) return st;
-  WsLayout W;
-  st = check_ws(shape, M, ws, ws_bytes, &W);
-  if (st != MOE_OK) return st;
-  st = check_map(shape, expert_to_slot);
-  if (st != MOE_OK) return st;
-  if (M == 0) {
-    st = empty_call(shape, expert_to_slot, cold_count, ws, W, stream);
-    return st != MOE_OK ? st : ok();
-  }
-  st = check_x_slots(x, slots);
-  if (st != MOE_OK) return st;
-  if (!w_router || !topk_ids || !topk_w || !y)
-    return fail(MOE_ERR_INVALID_ARG,
-                "moe_layer_forward: w_router, topk_ids, topk_w and y are required");
-  if (reinterpret_cast<uintptr_t>(w_router) & 15)
-    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: w_router must be 16-byte aligned");
-  float* logits = at<float>(ws, W.logits);
-  hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
-                               stream);
-  if (e != hipSuccess) return hip_fail(e, "router launch");
-  const RouteSrc src = RouteSrc::kLogits;
-  st = run_experts(shape, x, M, src, logits, topk_ids, topk_w, expert_to_slot, slots, y,
-                   cold_count, cold_routes, ws, W, true, true, stream);
-  return st != MOE_OK ? st : ok();
+  return layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids, topk_w,
+                       y, cold_count, cold_routes, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_layer_forward_marked(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                    const uint16_t* w_router, const float* router_bias,
+                                    const int32_t* expert_to_slot, const uint8_t* slots,
+                                    int32_t* topk_ids, float* topk_w, float* y,
+                                    int32_t* cold_count, int32_t* cold_routes, void* ws,
+                                    size_t ws_bytes, hipStream_t stream, const hipEvent_t* marks) {
+  if (!marks || !marks[0] || !marks[1] || !marks[2] || !marks[3])
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_marked: four events are required");
+  if (M <= 0) return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_marked: M must be positive");
+  return layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids, topk_w,
+                       y, cold_count, cold_routes, ws, ws_bytes, stream, marks);
 }
 
 moe_status moe_experts_gateup(const moe_shape* shape, const uint16_t* x, int32_t M,
@@ -362,6 +390,15 @@ moe_status moe_experts_down(const moe_shape* shape, int32_t M, const int32_t* to
                    const_cast<float*>(topk_w), expert_to_slot, slots, y, nullptr, nullptr, ws, W,
                    false, true, stream);
   return st != MOE_OK ? st : ok();
+}
+
+moe_status moe_residual_bf16(const uint16_t* x, const float* y, uint16_t* out, size_t n,
+                             hipStream_t stream) {
+  if (n == 0) return ok();
+  if (!x || !y || !out) return fail(MOE_ERR_INVALID_ARG, "moe_residual_bf16: NULL pointer");
+  hipError_t e = launch_residual(x, y, out, n, stream);
+  if (e != hipSuccess) return hip_fail(e, "residual launch");
+  return ok();
 }
 
 moe_status moe_slot_refill(const moe_shape* shape, uint8_t* slots, const uint8_t* host_bank,

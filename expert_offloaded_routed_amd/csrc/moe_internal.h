@@ -186,6 +186,8 @@ hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* 
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
                        const uint16_t* hbuf, float* pdn, float* y, hipStream_t s);
+hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, size_t n,
+                           hipStream_t s);
 hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,
                                  const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                                  const RouteWs& rw, uint16_t* hbuf, hipStream_t s);

@@ -1096,6 +1096,20 @@ __global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs 
 }
 
 // =============================================================================================
+// Residual chaining between stacked layers: out = bf16(x + y), one thread per 2 elements
+// =============================================================================================
+__global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ x,
+                                                  const float* __restrict__ y,
+                                                  uint16_t* __restrict__ out, size_t n) {
+  const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 2;
+  if (i >= n) return;
+  for (size_t j = i; j < i + 2 && j < n; ++j) {
+    const float xv = __uint_as_float((uint32_t)x[j] << 16);
+    out[j] = (uint16_t)f32_to_bf16_bits(xv + y[j]);
+  }
+}
+
+// =============================================================================================
 // Launchers (called from the host API after every argument has been validated)
 // =============================================================================================
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
@@ -1255,6 +1269,13 @@ hipError_t launch_down_grouped(int M, int H, int I, const uint8_t* slots, const 
   const int threads = M * (H / 4);
   hipLaunchKernelGGL(k_combine, dim3((threads + 255) / 256), dim3(256), 0, s, M, ra.k, H, ra, rw,
                      pdn, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, size_t n,
+                           hipStream_t s) {
+  const size_t threads = (n + 1) / 2;
+  hipLaunchKernelGGL(k_residual, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, y, out, n);
   return hipGetLastError();
 }
 

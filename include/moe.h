@@ -163,6 +163,19 @@ moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t 
                              int32_t* cold_count, int32_t* cold_routes,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_layer_forward with an event recorded on `stream` at each stage boundary, for timing the
+ * stages of exactly the launches of a layer call: marks[0] before the router, marks[1] after
+ * the route stage (router, plus the top-k / bucketing kernel when the call needs it), marks[2]
+ * after the gate/up kernel, marks[3] after the down stage.  marks: four events created by the
+ * caller with timing enabled (hipEventCreate); M >= 1.  Results equal moe_layer_forward's. */
+moe_status moe_layer_forward_marked(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                    const uint16_t* w_router, const float* router_bias,
+                                    const int32_t* expert_to_slot, const uint8_t* slots,
+                                    int32_t* topk_ids, float* topk_w, float* y,
+                                    int32_t* cold_count, int32_t* cold_routes,
+                                    void* ws, size_t ws_bytes, hipStream_t stream,
+                                    const hipEvent_t* marks);
+
 /* The two kernel stages of moe_experts_forward, on their own (for timing a stage or for
  * callers that interleave other work).  Arguments as in moe_experts_forward.
  *   moe_experts_gateup: h = bf16(silu(Wg x) * (Wu x)) for every hot route, kept in the
@@ -180,6 +193,13 @@ moe_status moe_experts_down(const moe_shape* shape, int32_t M, const int32_t* to
                             const float* topk_w, const int32_t* expert_to_slot,
                             const uint8_t* slots, float* y, void* ws, size_t ws_bytes,
                             hipStream_t stream);
+
+/* Residual chaining of stacked layers: out[i] = bf16(x[i] + y[i]) (round to nearest even),
+ * for feeding one layer's output to the next [MoE expert offload, "How it works": the layers of
+ * the model run one after another on the same token].  x, out: bf16 [n] (out may equal x);
+ * y: fp32 [n].  n = 0 enqueues nothing. */
+moe_status moe_residual_bf16(const uint16_t* x, const float* y, uint16_t* out, size_t n,
+                             hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Slot refill [ninfer v0.4.0, "New": experts are copied to the GPU in the background;

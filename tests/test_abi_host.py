@@ -38,7 +38,8 @@ def test_library_exports_every_declared_symbol():
                           "moe_cache_create", "moe_cache_policy_step", "moe_cache_destroy",
                           "moe_pack_expert", "moe_unpack_expert", "moe_expert_image_bytes",
                           "moe_workspace_size", "moe_layer_forward", "moe_last_error",
-                          "moe_experts_gateup", "moe_experts_down"}
+                          "moe_experts_gateup", "moe_experts_down", "moe_layer_forward_marked",
+                          "moe_residual_bf16"}
     for n in names:
         assert hasattr(lib, n), n
     # no torch in the exported signatures: the header includes only C/HIP headers

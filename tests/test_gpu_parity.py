@@ -439,3 +439,43 @@ def test_layer_forward_equals_route_plus_experts_and_stages(gptoss):
                                   None if e2s is None else e2s_np)
             close_enough(a.y[:M].cpu().numpy(), ref["y_hot"], f"layer_forward M={M}")
             assert int(a.cold_count.item()) == len(ref["cold_routes"])
+
+
+def test_marked_layer_forward_and_residual(gptoss):
+    """moe_layer_forward_marked gives the results of moe_layer_forward and ordered stage events;
+    moe_residual_bf16 rounds x + y to bf16 exactly like float32 addition followed by RNE."""
+    wl = gptoss.wl
+    shape = gptoss.shape
+    M = 2
+    say("marked layer forward")
+    x = _dev(synthetic.activations(wl, M, 900))
+    wr, bd = _dev(gptoss.wr), _dev(synthetic.zipf_bias(wl))
+    a, b = L.Buffers(shape, M), L.Buffers(shape, M)
+    marks = [B.event_create(timing=True) for _ in range(4)]
+    B.moe_layer_forward(shape, x, M, wr, bd, None, gptoss.slots, a.ids, a.w, a.y, None, None, a.ws)
+    B.moe_layer_forward_marked(shape, x, M, wr, bd, None, gptoss.slots, b.ids, b.w, b.y, None, None,
+                               b.ws, marks)
+    torch.cuda.synchronize()
+    assert torch.equal(a.ids[:M], b.ids[:M]) and torch.equal(a.y[:M], b.y[:M])
+    stages = [B.event_elapsed_ms(marks[j], marks[j + 1]) for j in range(3)]
+    assert all(t >= 0 for t in stages), stages
+    for e in marks:
+        B.event_destroy(e)
+    with pytest.raises(B.MoeError):
+        B.moe_layer_forward_marked(shape, x, M, wr, bd, None, gptoss.slots, b.ids, b.w, b.y, None,
+                                   None, b.ws, [0, 0, 0, 0])
+    say("residual")
+    n = 3 * 2880 + 1  # odd: the last thread handles one element
+    rng = np.random.default_rng(3)
+    xh = synthetic.bf16_from_f32(rng.standard_normal(n).astype(np.float32))
+    yh = (rng.standard_normal(n) * 0.1).astype(np.float32)
+    xd, yd = _dev(xh), torch.from_numpy(yh).cuda()
+    out = torch.zeros(n, dtype=torch.int16, device="cuda")
+    B.moe_residual_bf16(xd, yd, out, n)
+    B.moe_residual_bf16(xd, yd, xd, n)  # in place
+    torch.cuda.synchronize()
+    xf = (xh.astype(np.uint32) << 16).view(np.float32)
+    ref = synthetic.bf16_from_f32((xf + yh).astype(np.float32))
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), ref)
+    assert np.array_equal(xd.cpu().numpy().view(np.uint16), ref)
+
