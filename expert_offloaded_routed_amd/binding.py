@@ -335,9 +335,16 @@ def _hipcheck(err, what):
         raise RuntimeError(f"{what} failed with HIP error {err}")
 
 
-def event_create(timing: bool = False) -> int:
+HIP_EVENT_DISABLE_TIMING = 0x2
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def event_create(timing: bool = False, system_fence: bool = True) -> int:
+    """A HIP event; timing=False disables timing, system_fence=False drops the system-scope
+    fence of its records (cheaper, for marks that only time GPU work)."""
+    flags = (0 if timing else HIP_EVENT_DISABLE_TIMING) | (0 if system_fence else HIP_EVENT_DISABLE_SYSTEM_FENCE)
     ev = _P()
-    _hipcheck(hip().hipEventCreateWithFlags(C.byref(ev), 0 if timing else 2), "hipEventCreateWithFlags")
+    _hipcheck(hip().hipEventCreateWithFlags(C.byref(ev), flags), "hipEventCreateWithFlags")
     return ev.value
 
 

@@ -80,6 +80,7 @@ static BucketOut bucket_out(void* ws, const WsLayout& W, int32_t* counts, int32_
   o.ws_perm = at<int32_t>(ws, W.perm);
   o.meta = at<int32_t>(ws, W.meta);
   o.dist = at<int4>(ws, W.dist);
+  o.items = at<int2>(ws, W.items);
   o.cold_list = at<int32_t>(ws, W.cold_list);
   o.u_counts = counts;
   o.u_offsets = offsets;
@@ -126,10 +127,14 @@ static RouteWs route_ws(void* ws, const WsLayout& W) {
   RouteWs r;
   r.meta = at<int32_t>(ws, W.meta);
   r.dist = at<int4>(ws, W.dist);
+  r.items = at<int2>(ws, W.items);
   r.perm = at<int32_t>(ws, W.perm);
   r.route_slot = at<int32_t>(ws, W.route_slot);
   return r;
 }
+
+// Stage mark of moe_layer_forward_marked.
+static hipError_t record_mark(hipEvent_t ev, hipStream_t stream) { return hipEventRecord(ev, stream); }
 
 // Where the routes of a call come from.
 enum class RouteSrc {
@@ -158,7 +163,7 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
     if (e != hipSuccess) return hip_fail(e, "top-k / bucket launch");
     logits = nullptr;  // ids / w are final from here on
   }
-  if (marks && (e = hipEventRecord(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (marks && (e = record_mark(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (do_gateup) {
     // in the prologue case the writer workgroup publishes top-k results and the cold report
     const RouteArgs ra = route_args(sh, M, logits, ids, w, e2s, logits ? ids : nullptr,
@@ -170,7 +175,7 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
                                   at<uint16_t>(ws, W.hbuf), stream);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
   }
-  if (marks && (e = hipEventRecord(marks[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (marks && (e = record_mark(marks[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (do_down) {
     const RouteArgs ra = route_args(sh, M, nullptr, ids, w, e2s, nullptr, nullptr, nullptr, nullptr);
     e = p.grouped ? launch_down_grouped(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
@@ -179,7 +184,7 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
                                 at<uint16_t>(ws, W.hbuf), at<float>(ws, W.pdn), y, stream);
     if (e != hipSuccess) return hip_fail(e, "down launch");
   }
-  if (marks && (e = hipEventRecord(marks[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (marks && (e = record_mark(marks[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   return MOE_OK;
 }
 
@@ -220,7 +225,7 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: w_router must be 16-byte aligned");
   float* logits = at<float>(ws, W.logits);
   hipError_t e;
-  if (marks && (e = hipEventRecord(marks[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (marks && (e = record_mark(marks[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
                                stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");

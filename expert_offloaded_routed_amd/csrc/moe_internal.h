@@ -101,12 +101,21 @@ struct WsLayout {
   size_t meta;           // i32 [8]: n_dist, cold_count, error flags
   size_t dist;           // i32x4 [nd_max]: distinct hot experts {slot, bucket offset, count, id}
   size_t cold_list;      // i32 [M*k]
+  size_t items;          // i32x2 [n_items_max]: grouped GEMM work list {distinct expert, first route}
   size_t hbuf;           // bf16 [M*k][I]
   size_t pdn;            // f32 [M*k][H]: down partial sums when they do not fit in LDS
   size_t total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Grouped GEMM work items: (distinct hot expert, pass of up to kItemRoutes of its routes).
+// sum over experts of ceil(c_e / kItemRoutes) <= (number of experts) + M*k / kItemRoutes.
+constexpr int kItemRoutes = 64;
+inline int n_items_max(int Mk, int E) {
+  const int nd = Mk < E ? Mk : E;
+  return nd + Mk / kItemRoutes;
+}
 
 inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   WsLayout W;
@@ -123,19 +132,21 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   W.meta = o;        o = align256(o + 4 * 8);
   W.dist = o;        o = align256(o + 16 * nd);
   W.cold_list = o;   o = align256(o + 4 * Mk);
+  W.items = o;       o = align256(o + 8 * (size_t)n_items_max((int)Mk, E));
   W.hbuf = o;        o = align256(o + 2 * Mk * I);
   W.pdn = o;         o = align256(o + 4 * Mk * (size_t)H);
   W.total = o;
   return W;
 }
 
-// Error flags raised by the device in meta[2].
+// Error flags raised by the device in meta[2]; meta[3] holds the length of the work list.
 enum : int32_t { kErrBadId = 1, kErrBadSlot = 2 };
 
 // Outputs of the resolve / bucketing stage (workspace arrays, then optional caller arrays).
 struct BucketOut {
   int32_t *route_slot, *ws_perm, *meta;
   int4* dist;
+  int2* items;
   int32_t *cold_list, *u_counts, *u_offsets, *u_perm, *u_cold_count, *u_cold_routes;
 };
 
@@ -143,6 +154,7 @@ struct BucketOut {
 struct ExpertPlan {
   int nd_max;        // upper bound of distinct hot experts (gate/up grid.y)
   bool grouped;      // many tokens: grouped GEMM on MFMA (route table from the bucketing kernel)
+  int n_items_max;   // bound of the grouped GEMM work list (grid.y)
   bool prologue;     // every expert workgroup rebuilds the route table (M*k <= kProMaxRoutes)
   int gu_waves;      // waves per gate/up workgroup
   int gu_groups;     // most K groups (of 4 blocks) any gate/up wave holds
@@ -169,6 +181,7 @@ struct RouteArgs {
 struct RouteWs {
   int32_t* meta;        // [0] distinct hot experts, [1] cold routes, [2] error flags
   int4* dist;           // {slot, offset into perm, count, expert id}, ascending expert id
+  int2* items;          // grouped GEMM work list, meta[3] entries
   int32_t* perm;        // hot routes grouped by expert
   int32_t* route_slot;  // slot of every route, -1 = cold
 };

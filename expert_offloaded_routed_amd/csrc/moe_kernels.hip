@@ -168,7 +168,8 @@ struct BucketSmem {
 __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, int Mk, int E, int S,
                              const int32_t* __restrict__ e2s, int32_t* __restrict__ route_slot,
                              int32_t* __restrict__ ws_perm, int32_t* __restrict__ meta,
-                             int4* __restrict__ dist, int nd_max, int32_t* __restrict__ cold_list,
+                             int4* __restrict__ dist, int nd_max, int2* __restrict__ items,
+                             int n_items_max, int32_t* __restrict__ cold_list,
                              int32_t* __restrict__ u_counts, int32_t* __restrict__ u_offsets,
                              int32_t* __restrict__ u_perm, int32_t* __restrict__ u_cold_count,
                              int32_t* __restrict__ u_cold_routes) {
@@ -199,8 +200,9 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
   }
   __syncthreads();
 
-  // offsets (exclusive scan over experts) and distinct hot experts (scan of flags)
-  int running = 0, running_d = 0;
+  // offsets (exclusive scan over experts), distinct hot experts (scan of flags) and the work
+  // list of the grouped GEMM: one item per (distinct hot expert, pass of kItemRoutes routes)
+  int running = 0, running_d = 0, running_i = 0;
   for (int e0 = 0; e0 < E; e0 += blockDim.x) {
     const int e = e0 + tid;
     const int c = e < E ? s_cnt[e] : 0;
@@ -210,21 +212,29 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
       if (slot < 0 || slot >= S) slot = -1;
     }
     const int hot = (c > 0 && slot >= 0) ? 1 : 0;
-    int tot, tot_d;
+    const int np = hot ? (c + kItemRoutes - 1) / kItemRoutes : 0;
+    int tot, tot_d, tot_i;
     const int off = running + block_exclusive_scan(c, s_wave, tot);
     const int di = running_d + block_exclusive_scan(hot, s_wave, tot_d);
+    const int ii = running_i + block_exclusive_scan(np, s_wave, tot_i);
     if (e < E) {
       s_off[e] = off;
       if (u_counts) u_counts[e] = c;
       if (u_offsets) u_offsets[e] = off;
-      if (hot && di < nd_max) dist[di] = make_int4(slot, off, c, e);
+      if (hot && di < nd_max) {
+        dist[di] = make_int4(slot, off, c, e);
+        if (items != nullptr)
+          for (int p = 0; p < np && ii + p < n_items_max; ++p) items[ii + p] = make_int2(di, p * kItemRoutes);
+      }
     }
     running += tot;
     running_d += tot_d;
+    running_i += tot_i;
   }
   if (tid == 0) {
     if (u_offsets) u_offsets[E] = running;
     meta[0] = running_d < nd_max ? running_d : nd_max;
+    meta[3] = running_i < n_items_max ? running_i : n_items_max;
   }
   __syncthreads();
 
@@ -268,7 +278,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucket(
     float* __restrict__ topk_w, int do_bucket,
     const int32_t* __restrict__ ids, int Mk, int E, int S, const int32_t* __restrict__ e2s,
     int32_t* __restrict__ route_slot, int32_t* __restrict__ ws_perm, int32_t* __restrict__ meta,
-    int4* __restrict__ dist, int nd_max,
+    int4* __restrict__ dist, int nd_max, int2* __restrict__ items, int n_items_max,
     int32_t* __restrict__ cold_list, int32_t* __restrict__ u_counts,
     int32_t* __restrict__ u_offsets, int32_t* __restrict__ u_perm,
     int32_t* __restrict__ u_cold_count, int32_t* __restrict__ u_cold_routes) {
@@ -281,7 +291,8 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucket(
     __syncthreads();  // this workgroup's ids are visible to it from here on
   }
   if (blockIdx.x != 0) return;
-  bucket_stage(sm, ids, Mk, E, S, e2s, route_slot, ws_perm, meta, dist, nd_max, cold_list, u_counts, u_offsets, u_perm, u_cold_count,
+  bucket_stage(sm, ids, Mk, E, S, e2s, route_slot, ws_perm, meta, dist, nd_max, items, n_items_max,
+               cold_list, u_counts, u_offsets, u_perm, u_cold_count,
                u_cold_routes);
 }
 
@@ -837,7 +848,9 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kGroupedMinTokens = 64;        // calls with at least this many tokens take this path
 constexpr int kGemmTok = 64;                 // routes per pass: 4 MFMA tiles of 16
+static_assert(kGemmTok == kItemRoutes, "one work item is one pass of a grouped GEMM workgroup");
 constexpr int kGemmKC = 4;                   // K blocks (of 32) per chunk
 constexpr int kGemmPitch = kGemmKC * 32 + 8;  // bf16 per LDS row: 272 bytes, 16 tokens hit 16 bank groups
 constexpr int kGemmXPerThread = kGemmTok * kGemmKC * 4 / 256;  // 16-byte chunks staged per thread
@@ -881,189 +894,301 @@ __device__ __forceinline__ void gemm_store_rows(uint16_t (*xb)[kGemmPitch],
   }
 }
 
-// grid = (I/32 tiles, nd_max), 256 threads.  h = bf16(silu(Wg x) * (Wu x)) for every route of
-// the workgroup's expert, rows 32*tile .. +32, 64 routes per pass.
-__global__ __launch_bounds__(256) void k_gateup_grouped(
-    const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
-    size_t image_bytes, size_t gu_tile_bytes, int nb, RouteArgs ra, RouteWs rw,
-    uint16_t* __restrict__ hbuf) {
-  __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
-  __shared__ GemmRows gr;
-  const int tile = blockIdx.x;
-  const int d = blockIdx.y;
-  const int Mk = ra.M * ra.k;
-  const int nd = rw.meta[0];
-  if (d >= nd) return;
-  const int4 dd = rw.dist[d];
-  const int slot = dd.x, off = dd.y, cnt = dd.z;
-  if (cnt <= 0 || off < 0 || off + cnt > Mk) return;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  const uint8_t* tb = slots + (size_t)slot * image_bytes + (size_t)tile * gu_tile_bytes;
-  const uint32_t* wsrc = reinterpret_cast<const uint32_t*>(tb + (size_t)(w * 16 + n) * 16 + g * 4);
-  const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(tb + (size_t)nb * 1024 + (w * 16 + n) * 4);
-  const int nkc = (nb + kGemmKC - 1) / kGemmKC;
-  float* out = reinterpret_cast<float*>(&xb[0][0][0]);  // epilogue: [64 routes][65] fp32
+// Loads of one K chunk (kGemmKC blocks) for the gate/up tile of one wave: per row tile q (16 rows:
+// image lanes 16q .. 16q+15, q = 0, 1 gate and 2, 3 up) a lane takes dword g of the row's block
+// chunk and the scale word of the chunk's group.  Blocks past nb re-read block nb-1 (zero
+// weights later).
+struct GuChunk {
+  uint32_t code[4][kGemmKC];
+  uint32_t scale[4];
+};
 
-  for (int base = 0; base < cnt; base += kGemmTok) {
-    const int nt = min(kGemmTok, cnt - base);
-    const int ntt = (nt + 15) >> 4;
-    for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) {
-      const int r = rw.perm[off + base + min(i, nt - 1)];
-      gr.route[i] = r;
-      gr.row[i] = x + (size_t)(r / ra.k) * H;
-    }
-    __syncthreads();
-    f32x4_t acc[4];
+__device__ __forceinline__ void gu_load_chunk(const uint8_t* tb, int nb, int kc, int n, int g,
+                                              GuChunk& ch) {
+  const uint32_t* sbase = reinterpret_cast<const uint32_t*>(tb + (size_t)nb * 1024);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    uint4 xv[kGemmXPerThread];
-    uint32_t wc[kGemmKC], sw;
-    auto load_w = [&](int kc) {
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t* wsrc = reinterpret_cast<const uint32_t*>(tb + (size_t)(16 * q + n) * 16 + g * 4);
 #pragma unroll
-      for (int j = 0; j < kGemmKC; ++j) wc[j] = wsrc[(size_t)min(kc * kGemmKC + j, nb - 1) * 256];
-      sw = ssrc[(size_t)min(kc, (nb - 1) / 4) * 64];  // kGemmKC == 4: one scale word per chunk
-    };
-    gemm_load_rows(gr, 0, H, xv);
-    load_w(0);
-    for (int kc = 0; kc < nkc; ++kc) {
-      const int buf = kc & 1;
-      gemm_store_rows(xb[buf], xv);
-      uint32_t wcur[kGemmKC];
-#pragma unroll
-      for (int j = 0; j < kGemmKC; ++j) wcur[j] = wc[j];
-      const uint32_t scur = sw;
-      if (kc + 1 < nkc) {
-        gemm_load_rows(gr, kc + 1, H, xv);
-        load_w(kc + 1);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kGemmKC; ++j) {
-        const int b = kc * kGemmKC + j;
-        bf16x8_t bw = fp4x8_to_bf16(wcur[j], e8m0_to_f32((scur >> (8 * j)) & 0xFFu));
-        if (b >= nb) bw = bf16x8_t{};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (t < ntt) {
-            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][j * 32 + g * 8]);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, acc[t], 0, 0, 0);
-          }
-        }
-      }
-    }
-    __syncthreads();  // every wave is done with xb
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) out[(t * 16 + g * 4 + i) * 65 + w * 16 + n] = acc[t][i];
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < nt * 32; idx += blockDim.x) {
-      const int tok = idx >> 5;
-      const int row = idx & 31;
-      const float gt = out[tok * 65 + row];
-      const float up = out[tok * 65 + 32 + row];
-      hbuf[(size_t)gr.route[tok] * I + tile * 32 + row] = (uint16_t)f32_to_bf16_bits(silu_f32(gt) * up);
-    }
-    __syncthreads();  // out and gr are reused by the next pass
+    for (int j = 0; j < kGemmKC; ++j) ch.code[q][j] = wsrc[(size_t)min(kc * kGemmKC + j, nb - 1) * 256];
+    ch.scale[q] = sbase[(size_t)min(kc, (nb - 1) / 4) * 64 + 16 * q + n];  // kGemmKC == 4
   }
 }
 
-// grid = (H/64 row tiles, nd_max), 256 threads.  d = Wd h for every route of the workgroup's
-// expert, rows 64*tile .. +64 (wave w: rows 16w .. +16), written to pdn[route][row] in fp32;
-// k_combine then forms y in the fixed route order.  B fragments come from the down layout (row
-// r of a down tile at step t holds block t*S + s in lane r*S + s).
-__global__ __launch_bounds__(256) void k_down_grouped(
-    int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
-    size_t dn_tile_bytes, int nb, int S, int T, RouteArgs ra, RouteWs rw,
-    const uint16_t* __restrict__ hbuf, float* __restrict__ pdn) {
+// grid = (ceil(I/32 / 4), work items), 256 threads.  One item = one distinct hot expert and up to
+// 64 of its routes (busy experts are split over several items, so that one popular expert does
+// not serialise the call).  Wave w owns gate/up image tile 4*blockIdx.x + w (32 gate + 32 up
+// rows) for the item's routes: 4 route tiles x 4 row tiles of MFMA accumulators, and a lane
+// ends up holding gate row r and up row r of the same route, so h = bf16(silu(g) * u) needs no
+// exchange.  The routes' activations are staged once per 4 image tiles.
+__global__ __launch_bounds__(256) void k_gateup_grouped(
+    const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
+    size_t image_bytes, size_t gu_tile_bytes, int nb, int n_tiles, RouteArgs ra, RouteWs rw,
+    uint16_t* __restrict__ hbuf) {
   __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
   __shared__ GemmRows gr;
-  const int tile = blockIdx.x;
-  const int d = blockIdx.y;
   const int Mk = ra.M * ra.k;
-  const int nd = rw.meta[0];
-  if (d >= nd) return;
-  const int4 dd = rw.dist[d];
+  if ((int)blockIdx.y >= rw.meta[3]) return;
+  const int2 item = rw.items[blockIdx.y];  // (distinct expert, first route of the pass)
+  const int4 dd = rw.dist[item.x];
   const int slot = dd.x, off = dd.y, cnt = dd.z;
-  if (cnt <= 0 || off < 0 || off + cnt > Mk) return;
+  if (cnt <= 0 || off < 0 || off + cnt > Mk || item.y < 0 || item.y >= cnt) return;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int RD = 64 / S;
-  const int full = nb / S, rem = nb - full * S;
-  const size_t code_bytes = ((size_t)full * 64 + (size_t)RD * rem) * 16;
-  const int R = tile * 64 + w * 16 + n;  // this lane's output row
-  const uint8_t* dtile = slots + (size_t)slot * image_bytes + gu_bytes + (size_t)(R / RD) * dn_tile_bytes;
-  const int rr = R % RD;
+  const int tile = min(4 * (int)blockIdx.x + w, n_tiles - 1);  // waves past the last tile idle
+  const bool tile_ok = 4 * (int)blockIdx.x + w < n_tiles;
+  const uint8_t* tb = slots + (size_t)slot * image_bytes + (size_t)tile * gu_tile_bytes;
   const int nkc = (nb + kGemmKC - 1) / kGemmKC;
-  auto w_at = [&](int b, uint32_t& code, uint32_t& scale_byte) {
-    b = min(b, nb - 1);
-    const int sg = b % S, t = b / S;
-    const size_t idx = t < full ? (size_t)t * 64 + rr * S + sg : (size_t)full * 64 + rr * rem + sg;
-    code = *reinterpret_cast<const uint32_t*>(dtile + idx * 16 + g * 4);
-    const uint32_t word = *reinterpret_cast<const uint32_t*>(dtile + code_bytes + ((size_t)(t >> 2) * 64 + rr * S + sg) * 4);
-    scale_byte = (word >> (8 * (t & 3))) & 0xFFu;
-  };
-  (void)T;
-
-  for (int base = 0; base < cnt; base += kGemmTok) {
-    const int nt = min(kGemmTok, cnt - base);
-    const int ntt = (nt + 15) >> 4;
-    for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) {
-      const int r = rw.perm[off + base + min(i, nt - 1)];
-      gr.route[i] = r;
-      gr.row[i] = hbuf + (size_t)r * I;
+  const int base = item.y;
+  const int nt = min(kGemmTok, cnt - base);
+  const int ntt = (nt + 15) >> 4;
+  for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) {
+    const int r = rw.perm[off + base + min(i, nt - 1)];
+    gr.route[i] = r;
+    gr.row[i] = x + (size_t)(r / ra.k) * H;
+  }
+  __syncthreads();
+  f32x4_t acc[4][4];  // [route tile][row tile]
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[t][q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 xv[kGemmXPerThread];
+  GuChunk nxt;
+  gemm_load_rows(gr, 0, H, xv);
+  gu_load_chunk(tb, nb, 0, n, g, nxt);
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int buf = kc & 1;
+    gemm_store_rows(xb[buf], xv);
+    const GuChunk cur = nxt;
+    if (kc + 1 < nkc) {
+      gemm_load_rows(gr, kc + 1, H, xv);
+      gu_load_chunk(tb, nb, kc + 1, n, g, nxt);
     }
     __syncthreads();
-    f32x4_t acc[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    uint4 xv[kGemmXPerThread];
-    uint32_t wc[kGemmKC], wsb[kGemmKC];
-    auto load_w = [&](int kc) {
+    for (int j = 0; j < kGemmKC; ++j) {
+      const int b = kc * kGemmKC + j;
+      bf16x8_t av[4];
 #pragma unroll
-      for (int j = 0; j < kGemmKC; ++j) w_at(kc * kGemmKC + j, wc[j], wsb[j]);
-    };
-    gemm_load_rows(gr, 0, I, xv);
-    load_w(0);
-    for (int kc = 0; kc < nkc; ++kc) {
-      const int buf = kc & 1;
-      gemm_store_rows(xb[buf], xv);
-      uint32_t wcur[kGemmKC], scur[kGemmKC];
+      for (int t = 0; t < 4; ++t)
+        av[t] = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][j * 32 + g * 8]);
 #pragma unroll
-      for (int j = 0; j < kGemmKC; ++j) {
-        wcur[j] = wc[j];
-        scur[j] = wsb[j];
-      }
-      if (kc + 1 < nkc) {
-        gemm_load_rows(gr, kc + 1, I, xv);
-        load_w(kc + 1);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kGemmKC; ++j) {
-        const int b = kc * kGemmKC + j;
-        bf16x8_t bw = fp4x8_to_bf16(wcur[j], e8m0_to_f32(scur[j]));
+      for (int q = 0; q < 4; ++q) {
+        bf16x8_t bw = fp4x8_to_bf16(cur.code[q][j], e8m0_to_f32((cur.scale[q] >> (8 * j)) & 0xFFu));
         if (b >= nb) bw = bf16x8_t{};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (t < ntt) {
-            const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][j * 32 + g * 8]);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, acc[t], 0, 0, 0);
-          }
-        }
+        for (int t = 0; t < 4; ++t)
+          if (t < ntt) acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t], bw, acc[t][q], 0, 0, 0);
       }
     }
+  }
+  // lane (n, g), register i of row tile q: route t*16 + 4g + i, row 16q + n of the image tile
+  if (tile_ok) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t * 16 + g * 4 + i;
-        if (tok < nt) pdn[(size_t)gr.route[tok] * H + R] = acc[t][i];
+        if (tok < nt) {
+          uint16_t* hr = hbuf + (size_t)gr.route[tok] * I + tile * 32 + n;
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            hr[16 * q] = (uint16_t)f32_to_bf16_bits(silu_f32(acc[t][q][i]) * acc[t][q + 2][i]);
+        }
       }
-    __syncthreads();  // xb and gr are reused by the next pass
+  }
+}
+
+// grid = (ceil(H/256), work items), 256 threads.  d = Wd h for the item's routes; wave w owns rows
+// 256*blockIdx.x + 64w .. +64 (4 row tiles of 16), written to pdn[route][row] in fp32;
+// k_combine then forms y in the fixed route order.  B fragments come from the down layout (row
+// r of a down tile at step t holds block t*S + s in lane r*S + s).
+struct DnGeom {
+  int S, RD, full, rem, nb;
+  size_t code_bytes, dn_tile_bytes;
+};
+
+__device__ __forceinline__ void dn_fragment(const uint8_t* dsec, const DnGeom& G, int R, int b,
+                                            int g, uint32_t& code, uint32_t& scale_byte) {
+  b = min(b, G.nb - 1);
+  const int sg = b % G.S, t = b / G.S;
+  const int rr = R % G.RD;
+  const uint8_t* dtile = dsec + (size_t)(R / G.RD) * G.dn_tile_bytes;
+  const size_t idx = t < G.full ? (size_t)t * 64 + rr * G.S + sg : (size_t)G.full * 64 + rr * G.rem + sg;
+  code = *reinterpret_cast<const uint32_t*>(dtile + idx * 16 + g * 4);
+  const uint32_t word = *reinterpret_cast<const uint32_t*>(
+      dtile + G.code_bytes + ((size_t)(t >> 2) * 64 + rr * G.S + sg) * 4);
+  scale_byte = (word >> (8 * (t & 3))) & 0xFFu;
+}
+
+__global__ __launch_bounds__(256) void k_down_grouped(
+    int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
+    size_t dn_tile_bytes, int nb, int S, RouteArgs ra, RouteWs rw,
+    const uint16_t* __restrict__ hbuf, float* __restrict__ pdn) {
+  __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
+  __shared__ GemmRows gr;
+  const int Mk = ra.M * ra.k;
+  if ((int)blockIdx.y >= rw.meta[3]) return;
+  const int2 item = rw.items[blockIdx.y];
+  const int4 dd = rw.dist[item.x];
+  const int slot = dd.x, off = dd.y, cnt = dd.z;
+  if (cnt <= 0 || off < 0 || off + cnt > Mk || item.y < 0 || item.y >= cnt) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  DnGeom G;
+  G.S = S;
+  G.RD = 64 / S;
+  G.nb = nb;
+  G.full = nb / S;
+  G.rem = nb - G.full * S;
+  G.code_bytes = ((size_t)G.full * 64 + (size_t)G.RD * G.rem) * 16;
+  G.dn_tile_bytes = dn_tile_bytes;
+  const uint8_t* dsec = slots + (size_t)slot * image_bytes + gu_bytes;
+  const int row0 = 256 * (int)blockIdx.x + 64 * w;  // the wave's first row
+  int Rq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) Rq[q] = min(row0 + 16 * q + n, H - 1);
+  const int nkc = (nb + kGemmKC - 1) / kGemmKC;
+  const int base = item.y;
+  const int nt = min(kGemmTok, cnt - base);
+  const int ntt = (nt + 15) >> 4;
+  for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) {
+    const int r = rw.perm[off + base + min(i, nt - 1)];
+    gr.route[i] = r;
+    gr.row[i] = hbuf + (size_t)r * I;
+  }
+  __syncthreads();
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[t][q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 xv[kGemmXPerThread];
+  uint32_t wc[4][kGemmKC], wsb[4][kGemmKC];
+  auto load_w = [&](int kc) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < kGemmKC; ++j) dn_fragment(dsec, G, Rq[q], kc * kGemmKC + j, g, wc[q][j], wsb[q][j]);
+  };
+  gemm_load_rows(gr, 0, I, xv);
+  load_w(0);
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int buf = kc & 1;
+    gemm_store_rows(xb[buf], xv);
+    uint32_t wcur[4][kGemmKC], scur[4][kGemmKC];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < kGemmKC; ++j) {
+        wcur[q][j] = wc[q][j];
+        scur[q][j] = wsb[q][j];
+      }
+    if (kc + 1 < nkc) {
+      gemm_load_rows(gr, kc + 1, I, xv);
+      load_w(kc + 1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kGemmKC; ++j) {
+      const int b = kc * kGemmKC + j;
+      bf16x8_t av[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        av[t] = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][j * 32 + g * 8]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x8_t bw = fp4x8_to_bf16(wcur[q][j], e8m0_to_f32(scur[q][j]));
+        if (b >= nb) bw = bf16x8_t{};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (t < ntt) acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t], bw, acc[t][q], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = t * 16 + g * 4 + i;
+      if (tok < nt) {
+        float* pr = pdn + (size_t)gr.route[tok] * H;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (row0 + 16 * q + n < H) pr[row0 + 16 * q + n] = acc[t][q][i];
+      }
+    }
+}
+
+// ---- router GEMM for many tokens ---------------------------------------------------------------
+// grid = (ceil(M/64), ceil(E/64)), 256 threads: logits for 64 tokens x 64 experts, wave w owns
+// experts 16w .. +16 of the block.  A = the tokens' activations (staged in LDS, as above), B =
+// router rows read straight from memory (a lane's 8 K elements are 16 contiguous bytes).  Same
+// fp32 accumulation of bf16 products as k_router, in another order.
+__global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restrict__ x, int M,
+                                                        const uint16_t* __restrict__ wr,
+                                                        const float* __restrict__ bias, int E,
+                                                        int H, float* __restrict__ logits) {
+  __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
+  __shared__ GemmRows gr;
+  const int tok0 = blockIdx.x * kGemmTok;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int e = blockIdx.y * 64 + 16 * w + n;
+  const uint16_t* brow = wr + (size_t)min(e, E - 1) * H + g * 8;
+  for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) gr.row[i] = x + (size_t)min(tok0 + i, M - 1) * H;
+  __syncthreads();
+  const int ntt = (min(kGemmTok, M - tok0) + 15) >> 4;
+  const int nkc = (H / 32 + kGemmKC - 1) / kGemmKC;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 xv[kGemmXPerThread];
+  uint4 bn[kGemmKC];
+  auto load_b = [&](int kc) {
+#pragma unroll
+    for (int j = 0; j < kGemmKC; ++j)
+      bn[j] = *reinterpret_cast<const uint4*>(brow + min((kc * kGemmKC + j) * 32, H - 32));
+  };
+  gemm_load_rows(gr, 0, H, xv);
+  load_b(0);
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int buf = kc & 1;
+    gemm_store_rows(xb[buf], xv);
+    uint4 bc[kGemmKC];
+#pragma unroll
+    for (int j = 0; j < kGemmKC; ++j) bc[j] = bn[j];
+    if (kc + 1 < nkc) {
+      gemm_load_rows(gr, kc + 1, H, xv);
+      load_b(kc + 1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kGemmKC; ++j) {
+      bf16x8_t bw = __builtin_bit_cast(bf16x8_t, bc[j]);
+      if ((kc * kGemmKC + j) * 32 >= H) bw = bf16x8_t{};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < ntt) {
+          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][j * 32 + g * 8]);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bw, acc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (e < E) {
+    const float b = bias != nullptr ? bias[e] : 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = tok0 + t * 16 + g * 4 + i;
+        if (m < M) logits[(size_t)m * E + e] = acc[t][i] + b;
+      }
   }
 }
 
@@ -1114,7 +1239,11 @@ __global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ x
 // =============================================================================================
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
                          int H, float* logits, hipStream_t s) {
-  hipLaunchKernelGGL(k_router, dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits);
+  if (M >= kGroupedMinTokens)  // a dense GEMM: MFMA
+    hipLaunchKernelGGL(k_router_grouped, dim3((M + kGemmTok - 1) / kGemmTok, (E + 63) / 64), dim3(256),
+                       0, s, x, M, wr, bias, E, H, logits);
+  else
+    hipLaunchKernelGGL(k_router, dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits);
   return hipGetLastError();
 }
 
@@ -1133,7 +1262,7 @@ hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_i
   const int grid = (logits != nullptr && !do_bucket) ? (M + per_wg - 1) / per_wg : 1;
   hipLaunchKernelGGL(k_topk_bucket, dim3(grid > 0 ? grid : 1), dim3(kBucketThreads), 0, s, logits,
                      M, k, topk_ids, topk_w, do_bucket ? 1 : 0, ids, Mk, E, S, e2s, o.route_slot,
-                     o.ws_perm, o.meta, o.dist, nd_max,
+                     o.ws_perm, o.meta, o.dist, nd_max, o.items, o.items ? n_items_max(Mk, E) : 0,
                      o.cold_list, o.u_counts, o.u_offsets, o.u_perm, o.u_cold_count,
                      o.u_cold_routes);
   return hipGetLastError();
@@ -1141,7 +1270,6 @@ hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_i
 
 
 constexpr int kNumCUs = 256;      // MI355X compute units
-constexpr int kGroupedMinTokens = 64;
 constexpr int kWavesPerCU = 16;   // resident waves per CU for a kernel of <= 128 VGPRs
 
 ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
@@ -1151,6 +1279,7 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
   // M >= kGroupedMinTokens: the grouped GEMM (it needs H a multiple of 64 for its row tiles,
   // which every supported shape is) with the route table from the bucketing kernel
   p.grouped = M >= kGroupedMinTokens;
+  p.n_items_max = n_items_max(Mk, E);
   p.prologue = !p.grouped && Mk <= kProMaxRoutes;
   // gate/up waves per workgroup: each wave holds at most kMaxGroups groups of its tile's K;
   // the kernels are built for <= 128 VGPRs, so a CU holds kWavesPerCU waves.  Pick the widest
@@ -1253,17 +1382,16 @@ hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLay
 hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,
                                  const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                                  const RouteWs& rw, uint16_t* hbuf, hipStream_t s) {
-  hipLaunchKernelGGL(k_gateup_grouped, dim3(L.gu_tiles, p.nd_max), dim3(256), 0, s, x, H, I, slots,
-                     L.image_bytes, L.gu_tile_bytes, L.nb_h, ra, rw, hbuf);
+  hipLaunchKernelGGL(k_gateup_grouped, dim3((L.gu_tiles + 3) / 4, p.n_items_max), dim3(256), 0, s, x,
+                     H, I, slots, L.image_bytes, L.gu_tile_bytes, L.nb_h, L.gu_tiles, ra, rw, hbuf);
   return hipGetLastError();
 }
 
 hipError_t launch_down_grouped(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                                const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
                                const uint16_t* hbuf, float* pdn, float* y, hipStream_t s) {
-  hipLaunchKernelGGL(k_down_grouped, dim3(H / 64, p.nd_max), dim3(256), 0, s, H, I, slots,
-                     L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.nb_i, L.dn_seg, L.dn_steps, ra,
-                     rw, hbuf, pdn);
+  hipLaunchKernelGGL(k_down_grouped, dim3((H + 255) / 256, p.n_items_max), dim3(256), 0, s, H, I, slots,
+                     L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.nb_i, L.dn_seg, ra, rw, hbuf, pdn);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int threads = M * (H / 4);

@@ -167,7 +167,7 @@ moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t 
  * stages of exactly the launches of a layer call: marks[0] before the router, marks[1] after
  * the route stage (router, plus the top-k / bucketing kernel when the call needs it), marks[2]
  * after the gate/up kernel, marks[3] after the down stage.  marks: four events created by the
- * caller with timing enabled (hipEventCreate); M >= 1.  Results equal moe_layer_forward's. */
+ * caller with timing enabled; M >= 1.  Results equal moe_layer_forward's. */
 moe_status moe_layer_forward_marked(const moe_shape* shape, const uint16_t* x, int32_t M,
                                     const uint16_t* w_router, const float* router_bias,
                                     const int32_t* expert_to_slot, const uint8_t* slots,
