@@ -12,9 +12,10 @@ steps, so step t reads copy t % R of the whole expert bank (R copies at distinct
 reuse distance >= R * 52.9 MB).
 
 Dominant kernel: the gate/up kernel.  Its duration comes from HIP events that
-moe_layer_forward_marked records on the launch stream at the stage boundaries of the same steps
-(launched eagerly after the graph); achieved GB/s = its algorithmic bytes (the MXFP4 codes and
-scales of the 4 routed experts' gate and up matrices) / that duration.
+moe_layer_forward_marked records on the launch stream at the stage boundaries of the same steps,
+enqueued behind a spin kernel so that they run back to back; achieved GB/s = its algorithmic
+bytes (the MXFP4 codes and scales of the 4 routed experts' gate and up matrices) / that
+duration.
 
 Other workloads (one JSON line each, --workload):
   slots8    8 GPU slots for 32 experts, LRU refills (<= 2 per step) from pinned host memory on a
@@ -49,7 +50,12 @@ def parse():
     p.add_argument("--tokens", type=int, default=1, help="stack48: tokens per step (1, 4 or 8)")
     p.add_argument("--copies", type=int, default=16, help="distinct copies of the expert bank")
     p.add_argument("--stage-steps", type=int, default=256, help="marked steps for stage timing")
+    p.add_argument("--enqueue-spin-cycles", type=float, default=2e8,
+                   help="GPU cycles of the spin kernel that holds the stream while marked steps are enqueued")
     p.add_argument("--cpu-steps", type=int, default=12, help="oracle steps for cpu_baseline (0 = skip)")
+    p.add_argument("--calibrate-copy-mb", type=int, default=0,
+                   help="after the run, copy a buffer of this many MiB device to device 4 times (a "
+                        "plain copy kernel of known size, to scale HBM byte counters)")
     return p.parse_args()
 
 
@@ -168,18 +174,25 @@ def bench_decode(args):
     step_bytes = k * exp_bytes
     gu_bytes = k * (2 * I * H // 2 + 2 * I * H // 32)  # gate/up kernel, algorithmic bytes per launch
 
-    # stage timing: the same steps, launched eagerly as marked calls (events without a system
-    # fence at every stage boundary, on the launch stream), after one untimed pass
+    # stage timing: the same steps as marked calls (events without a system fence at every stage
+    # boundary, on the launch stream).  The stream first runs a bounded spin kernel long enough
+    # for the host to enqueue every step, so the steps then run back to back and no host gap
+    # falls inside a stage.  One untimed pass first.
     n_st = max(1, min(args.stage_steps, args.steps))
     marks = [[B.event_create(timing=True, system_fence=False) for _ in range(4)] for _ in range(n_st)]
     for rep in range(2):
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(args.enqueue_spin_cycles))
+            t_enq = time.perf_counter()
             for i in range(n_st):
                 t = args.warmup + i
                 B.moe_layer_forward_marked(shape, xs[t], 1, wr, bias, None, copies[t % R], ids[t], w[t],
                                            y[t], None, None, ws, marks[i], stream=stream)
+            t_enq = time.perf_counter() - t_enq
     torch.cuda.synchronize()
+    spin_ms = B.event_elapsed_ms(marks[0][0], marks[-1][3])
+    log(f"stage timing: host enqueue {t_enq * 1e3:.1f} ms for {n_st} steps, GPU {spin_ms:.2f} ms")
     st = np.array([[B.event_elapsed_ms(m[j], m[j + 1]) for j in range(3)] for m in marks]) * 1e3
     span = np.array([B.event_elapsed_ms(m[0], m[3]) for m in marks]) * 1e3
     for m in marks:
@@ -556,13 +569,30 @@ def bench_prefill(args):
     return 0
 
 
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size (4 times): its HBM byte counters per launch
+    give the scale between what the counters read and the bytes moved."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 4 x {n} bytes device to device")
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
         return 2
-    return {"decode": bench_decode, "slots8": bench_slots8, "stack48": bench_stack48,
-            "prefill": bench_prefill}[args.workload](args)
+    rc = {"decode": bench_decode, "slots8": bench_slots8, "stack48": bench_stack48,
+          "prefill": bench_prefill}[args.workload](args)
+    if args.calibrate_copy_mb > 0:
+        copy_calibration(args.calibrate_copy_mb)
+    return rc
 
 
 if __name__ == "__main__":
