@@ -11,11 +11,12 @@ Cache honesty: popular experts would otherwise stay in the 256 MB Infinity Cache
 steps, so step t reads copy t % R of the whole expert bank (R copies at distinct addresses,
 reuse distance >= R * 52.9 MB).
 
-Dominant kernel: the gate/up kernel.  Its duration comes from HIP events that
-moe_layer_forward_marked records on the launch stream at the stage boundaries of the same steps,
-enqueued behind a spin kernel so that they run back to back; achieved GB/s = its algorithmic
-bytes (the MXFP4 codes and scales of the 4 routed experts' gate and up matrices) / that
-duration.
+Dominant kernel: the fused expert kernel (gate/up + SiLU*up, then down + ordered combine in one
+launch; with MOE_DECODE_UNFUSED=1 the gate/up kernel of the two-launch path).  Its duration
+comes from HIP events that moe_layer_forward_marked records on the launch stream at the stage
+boundaries of the same steps, enqueued behind a spin kernel so that they run back to back;
+achieved GB/s = its algorithmic bytes (the MXFP4 codes and scales of the 4 routed experts'
+gate, up and down matrices; gate and up only for the gate/up kernel) / that duration.
 
 Other workloads (one JSON line each, --workload):
   slots8    8 GPU slots for 32 experts, LRU refills (<= 2 per step) from pinned host memory on a
@@ -199,7 +200,20 @@ def bench_decode(args):
         for e in m:
             B.event_destroy(e)
     us_rt, us_gu, us_dn = (float(v) for v in st.mean(axis=0))
-    gu_gbs = gu_bytes / (us_gu * 1e-6) / 1e9
+    fused = B.moe_layer_launches(shape, 1) == 2
+    if fused:  # marks[2] and marks[3] both follow the one expert launch
+        dom_bytes, dom_us, dom_key = step_bytes, us_gu, "layer_decode_bytes_per_launch"
+        dom_name = ("k_layer_decode (route table + MXFP4 gate/up GEMV + SiLU*up, then down GEMV + "
+                    "ordered combine, one launch)")
+        stages = {"route (router GEMV)": round(us_rt, 2),
+                  "experts (fused gate/up + down + combine)": round(us_gu, 2)}
+    else:
+        dom_bytes, dom_us, dom_key = gu_bytes, us_gu, "gateup_bytes_per_launch"
+        dom_name = "k_gateup (route table + fused MXFP4 gate/up GEMV + SiLU*up)"
+        stages = {"route (router GEMV)": round(us_rt, 2),
+                  "gateup (route table + gate/up + SiLU*up)": round(us_gu, 2),
+                  "down (down GEMV + ordered combine)": round(us_dn, 2)}
+    dom_gbs = dom_bytes / (dom_us * 1e-6) / 1e9
 
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
@@ -208,7 +222,7 @@ def bench_decode(args):
             from expert_offloaded_routed_amd import _build
             t = json.load(open(tfile))
             if t.get("kernel_source_sha") == _build.kernel_source_sha():
-                traffic = t.get("gateup_bytes_per_launch")
+                traffic = t.get(dom_key)
         except Exception:
             traffic = None
 
@@ -248,16 +262,14 @@ def bench_decode(args):
         "hbm_gbs_step": round(gbs_step, 1),
         "frac_peak_step": round(gbs_step / PEAK_HBM_GBS, 4),
         "expert_bytes_per_step": step_bytes,
-        "stage_us": {"route (router GEMV)": round(us_rt, 2),
-                     "gateup (route table + gate/up + SiLU*up)": round(us_gu, 2),
-                     "down (down GEMV + ordered combine)": round(us_dn, 2)},
+        "stage_us": stages,
         "step_us_marked_p50_p99": [round(float(np.percentile(span, 50)), 2),
                                   round(float(np.percentile(span, 99)), 2)],
         "wall_s": round(wall, 4),
-        "roofline": {"bound": "hbm", "kernel": "k_gateup (route table + fused MXFP4 gate/up GEMV + SiLU*up)",
-                     "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": gu_bytes, "us_per_launch": round(us_gu, 3),
+        "roofline": {"bound": "hbm", "kernel": dom_name,
+                     "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_us, 3),
                      "launches_timed": n_st},
         "cpu_baseline": cpu,
     }

@@ -68,6 +68,7 @@ _SIGS = {
                           _P, _SZ, _P],
     "moe_layer_forward_marked": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, _P, _SZ, _P, _P],
+    "moe_layer_launches": [C.POINTER(moe_shape), _I32, C.POINTER(_I32)],
     "moe_experts_gateup": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_experts_down": [C.POINTER(moe_shape), _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_slot_refill": [C.POINTER(moe_shape), _P, _P, _P, _P, _I32, _P, _P, _P],
@@ -236,6 +237,13 @@ def moe_layer_forward_marked(shape, x, M, w_router, router_bias, expert_to_slot,
                                            _ptr(cold_routes), _ptr(ws), _nbytes(ws), _stream(stream),
                                            C.cast(ev, C.c_void_p)),
            "moe_layer_forward_marked")
+
+
+def moe_layer_launches(shape, M):
+    """Kernel launches of one moe_layer_forward call for M tokens (2 = gate/up and down fused)."""
+    n = _I32(0)
+    _check(load().moe_layer_launches(C.byref(shape), int(M), C.byref(n)), "moe_layer_launches")
+    return int(n.value)
 
 
 def moe_experts_gateup(shape, x, M, topk_ids, topk_w, expert_to_slot, slots, ws, stream=None):

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime_api.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -133,6 +134,15 @@ static RouteWs route_ws(void* ws, const WsLayout& W) {
   return r;
 }
 
+// MOE_DECODE_UNFUSED=1: one-token layer calls keep gate/up and down as two launches.
+static bool decode_unfused() {
+  static const bool v = [] {
+    const char* s = getenv("MOE_DECODE_UNFUSED");
+    return s != nullptr && s[0] == '1';
+  }();
+  return v;
+}
+
 // Stage mark of moe_layer_forward_marked.
 static hipError_t record_mark(hipEvent_t ev, hipStream_t stream) { return hipEventRecord(ev, stream); }
 
@@ -225,10 +235,27 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: w_router must be 16-byte aligned");
   float* logits = at<float>(ws, W.logits);
   hipError_t e;
+  // One token with a fusable shape: gate/up and down run as one launch (the router clears its
+  // handoff counters).  MOE_DECODE_UNFUSED=1 in the environment selects the two-launch path.
+  const ImageLayout L = image_layout(shape->hidden, shape->inter);
+  const ExpertPlan p = plan_experts(L, M, shape->n_experts, shape->top_k);
+  const bool fused = !decode_unfused() && layer_decode_fusable(L, p, M);
+  uint32_t* hand = at<uint32_t>(ws, W.hand);
   if (marks && (e = record_mark(marks[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
-                               stream);
+                    fused ? hand : nullptr, fused ? p.nd_max * kHandSub : 0, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
+  if (fused) {
+    if (marks && (e = record_mark(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    const RouteArgs ra = route_args(shape, M, logits, topk_ids, topk_w, expert_to_slot, topk_ids,
+                                    topk_w, cold_count, cold_routes);
+    e = launch_layer_decode(x, M, shape->hidden, shape->inter, slots, L, p, ra, route_ws(ws, W),
+                            at<uint16_t>(ws, W.hbuf), y, hand, stream);
+    if (e != hipSuccess) return hip_fail(e, "fused decode launch");
+    for (int i = 2; marks && i < 4; ++i)
+      if ((e = record_mark(marks[i], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+    return ok();
+  }
   const RouteSrc src = RouteSrc::kLogits;
   st = run_experts(shape, x, M, src, logits, topk_ids, topk_w, expert_to_slot, slots, y,
                    cold_count, cold_routes, ws, W, true, true, stream, marks);
@@ -262,6 +289,26 @@ moe_status moe_workspace_size(const moe_shape* shape, int32_t max_M, size_t* byt
   return ok();
 }
 
+moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!n) return fail(MOE_ERR_INVALID_ARG, "n is NULL");
+  if (M < 0) return fail(MOE_ERR_INVALID_ARG, "M < 0");
+  if (M == 0) {
+    *n = 1;  // the cold report of an empty call
+    return ok();
+  }
+  const ImageLayout L = image_layout(shape->hidden, shape->inter);
+  const ExpertPlan p = plan_experts(L, M, shape->n_experts, shape->top_k);
+  if (!decode_unfused() && layer_decode_fusable(L, p, M))
+    *n = 2;                     // router, fused experts
+  else if (p.grouped)
+    *n = 5;                     // router, top-k / bucket, gate/up, down, combine
+  else
+    *n = p.prologue ? 3 : 4;    // router, [top-k / bucket,] gate/up, down + combine
+  return ok();
+}
+
 moe_status moe_route(const moe_shape* shape, const uint16_t* x, int32_t M, const uint16_t* w_router,
                      const float* router_bias, int32_t* topk_ids, float* topk_w, void* ws,
                      size_t ws_bytes, hipStream_t stream) {
@@ -277,7 +324,7 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, int32_t M, const
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x and w_router must be 16-byte aligned");
   float* logits = at<float>(ws, W.logits);
   hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
-                               stream);
+                               nullptr, 0, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
   e = launch_topk_bucket(logits, M, shape->top_k, topk_ids, topk_w, false, topk_ids,

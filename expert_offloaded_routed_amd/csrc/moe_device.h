@@ -110,19 +110,20 @@ __device__ __forceinline__ float block_dot(const uint4 c, const uint4 a0, const 
   const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
   const uint32_t aw[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
                            a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
-  float s = 0.0f;
+  // two independent accumulation chains (even and odd element pairs), summed at the end
+  float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], 1.0f, 0),
-                                        as_bf16x2(aw[4 * j + 0]), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], 1.0f, 1),
-                                        as_bf16x2(aw[4 * j + 1]), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], 1.0f, 2),
-                                        as_bf16x2(aw[4 * j + 2]), s, false);
-    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], 1.0f, 3),
-                                        as_bf16x2(aw[4 * j + 3]), s, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], 1.0f, 0),
+                                         as_bf16x2(aw[4 * j + 0]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], 1.0f, 1),
+                                         as_bf16x2(aw[4 * j + 1]), s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], 1.0f, 2),
+                                         as_bf16x2(aw[4 * j + 2]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], 1.0f, 3),
+                                         as_bf16x2(aw[4 * j + 3]), s1, false);
   }
-  return s;
+  return s0 + s1;
 }
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }

@@ -104,10 +104,16 @@ struct WsLayout {
   size_t items;          // i32x2 [n_items_max]: grouped GEMM work list {distinct expert, first route}
   size_t hbuf;           // bf16 [M*k][I]
   size_t pdn;            // f32 [M*k][H]: down partial sums when they do not fit in LDS
+  size_t hand;           // u32 counters of the fused decode kernel, one per 64 bytes
   size_t total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Fused decode kernel handoff: kHandSub arrival counters per distinct hot expert (gate/up tile t
+// counts on counter t % kHandSub), each on its own 64-byte line.
+constexpr int kHandSub = 8;
+constexpr int kHandStride = 16;  // 32-bit words between counters
 
 // Grouped GEMM work items: (distinct hot expert, pass of up to kItemRoutes of its routes).
 // sum over experts of ceil(c_e / kItemRoutes) <= (number of experts) + M*k / kItemRoutes.
@@ -135,12 +141,13 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   W.items = o;       o = align256(o + 8 * (size_t)n_items_max((int)Mk, E));
   W.hbuf = o;        o = align256(o + 2 * Mk * I);
   W.pdn = o;         o = align256(o + 4 * Mk * (size_t)H);
+  W.hand = o;        o = align256(o + 64 * (size_t)nd * kHandSub);
   W.total = o;
   return W;
 }
 
 // Error flags raised by the device in meta[2]; meta[3] holds the length of the work list.
-enum : int32_t { kErrBadId = 1, kErrBadSlot = 2 };
+enum : int32_t { kErrBadId = 1, kErrBadSlot = 2, kErrHandoff = 4 };
 
 // Outputs of the resolve / bucketing stage (workspace arrays, then optional caller arrays).
 struct BucketOut {
@@ -188,7 +195,12 @@ struct RouteWs {
 
 // Kernel launchers (moe_kernels.hip).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, hipStream_t s);
+                         int H, float* logits, uint32_t* zero, int n_zero, hipStream_t s);
+bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M);
+hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
+                               const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
+                               const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
+                               hipStream_t s);
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,
                               const int32_t* e2s, const BucketOut& o, hipStream_t s);

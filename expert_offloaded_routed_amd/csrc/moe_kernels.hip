@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -27,12 +29,17 @@ namespace moe {
 // of 8 bf16, chunk c = lane + 64*i) and reads the same chunks of every token's x.
 constexpr int kRouterMaxChunksPerLane = kMaxHidden / 8 / 64;  // 16
 
+// Workgroup 0 also clears the n_zero handoff counters of the fused decode kernel that follows
+// (one per kHandStride words); the kernel boundary makes the zeros visible to it.
 __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, int M,
                                                const uint16_t* __restrict__ wr,
                                                const float* __restrict__ bias, int E, int H,
-                                               float* __restrict__ logits) {
+                                               float* __restrict__ logits,
+                                               uint32_t* __restrict__ zero, int n_zero) {
   const int lane = threadIdx.x;
   const int e = blockIdx.x;
+  if (e == 0)
+    for (int i = lane; i < n_zero; i += 64) zero[(size_t)i * kHandStride] = 0u;
   const int nch = H / 8;
   uint4 wrow[kRouterMaxChunksPerLane];
 #pragma unroll
@@ -432,6 +439,55 @@ struct RouteLds {
   int nd;
 };
 
+// One token over at most kFastE experts (the decode case): top-k, slot resolve and the whole
+// route table by wave 0 in registers, with no loop over LDS and no call.  The logit row is
+// uniform, so it comes through the scalar unit; every lane ranks its own logit against all of
+// them (ties to the lower id), exactly as topk_rank does, and the weights use the same
+// arithmetic, so the results are bitwise those of moe_route.  The distinct hot experts of one
+// token are its selected ids; their ascending order is a ballot prefix count.
+constexpr int kFastE = 32;
+
+__device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs& a) {
+  const int lane = threadIdx.x & 63;
+  const int E = a.E;
+  const float* lrow = a.logits;  // row 0; the workspace holds at least 256 bytes of logits
+  float lv[kFastE];
+#pragma unroll
+  for (int j = 0; j < kFastE; ++j) lv[j] = lrow[j];
+  const float v = lane < E ? rank_key(lrow[lane < E ? lane : 0]) : -INFINITY;
+  int slot_of = lane;
+  if (a.e2s != nullptr) slot_of = a.e2s[lane < E ? lane : 0];
+  float top = -INFINITY;
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < kFastE; ++j) {
+    const float o = j < E ? rank_key(lv[j]) : -INFINITY;
+    top = fmaxf(top, o);
+    rank += (o > v || (o == v && j < lane)) ? 1 : 0;
+  }
+  const bool sel = lane < E && rank < a.k;
+  const float ex = sel ? expf(v - top) : 0.0f;
+  const float den = wave_sum(ex);
+  int slot = -1;
+  if (sel && slot_of >= 0 && slot_of < a.S) slot = slot_of;
+  const bool hot = slot >= 0;
+  const uint64_t hm = __ballot(hot);
+  const int pos = __popcll(hm & ((1ull << lane) - 1ull));
+  if (sel) {
+    rt.ids[rank] = lane;
+    rt.w[rank] = ex / den;
+    rt.slot[rank] = slot;
+  }
+  if (hot) {
+    rt.dist_slot[pos] = slot;
+    rt.dist_off[pos] = pos;
+    rt.dist_cnt[pos] = 1;
+    rt.dist_e[pos] = lane;
+    rt.perm[pos] = rank;
+  }
+  if (lane == 0) rt.nd = __popcll(hm);
+}
+
 // rt.ids / rt.w [0, Mk) must be in place (and visible after a barrier).  e2s may point to LDS.
 __device__ void build_table(RouteLds& rt, int Mk, int E, int S, const int32_t* e2s) {
   const int tid = threadIdx.x;
@@ -527,17 +583,22 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
   const int tid = threadIdx.x;
   const int nw = blockDim.x >> 6;
   const int Mk = a.M * a.k;
-  if (a.logits != nullptr) {
-    for (int m = tid >> 6; m < a.M; m += nw)
-      topk_token(a.logits + (size_t)m * a.E, a.E, a.k, rt.ids + m * a.k, rt.w + m * a.k);
+  if (a.logits != nullptr && a.M == 1 && a.E <= kFastE) {
+    if (tid < 64) route_token_small(rt, a);
+    __syncthreads();
   } else {
-    for (int r = tid; r < Mk; r += blockDim.x) {
-      rt.ids[r] = a.ids_in[r];
-      rt.w[r] = a.w_in[r];
+    if (a.logits != nullptr) {
+      for (int m = tid >> 6; m < a.M; m += nw)
+        topk_token(a.logits + (size_t)m * a.E, a.E, a.k, rt.ids + m * a.k, rt.w + m * a.k);
+    } else {
+      for (int r = tid; r < Mk; r += blockDim.x) {
+        rt.ids[r] = a.ids_in[r];
+        rt.w[r] = a.w_in[r];
+      }
     }
+    __syncthreads();
+    build_table(rt, Mk, a.E, a.S, a.e2s);
   }
-  __syncthreads();
-  build_table(rt, Mk, a.E, a.S, a.e2s);
   if (writer) {
     write_routes(rt, Mk, a.topk_ids, a.topk_w, a.cold_count, a.cold_routes, nullptr);
     write_table(rt, Mk, w);
@@ -722,6 +783,55 @@ __device__ __forceinline__ void load_down_tile(const uint8_t* __restrict__ tb, s
   (void)RD;
 }
 
+// One route's partial down sum for this lane's row segment: steps t < TM of block t*S + sg, h from
+// the LDS copy (HL; 16-byte quarters of block b swizzled by (b >> 1) & 3) or from the workspace.
+// Straight-line over the steps, software-pipelined by hand: the h block of step t+1 is read
+// before step t's arithmetic.  Its address passes through an empty asm together with the sum
+// so far, which keeps the compiler from issuing it any earlier (all reads up front would need
+// 16 VGPRs per step).  Lanes without a block at a step, and steps past T, read a valid block
+// (index clamped) and add nothing (a select, not a product, so whatever that block holds
+// cannot leak in).
+template <int S, int TM, bool HL>
+__device__ __forceinline__ float down_route_dot(const uint4 (&c)[TM], const uint32_t (&s4)[TM / 4],
+                                                int T, int nb, int I, int sg, const uint8_t* hsm,
+                                                const uint16_t* __restrict__ hbuf, int route) {
+  float acc = 0.0f;
+  int rbase = HL ? route * nb : route * I;  // first h block (LDS) or element (workspace)
+  auto read_h = [&](int t, uint4 (&a)[4]) {
+    const int b = min(t * S + sg, nb - 1);
+    if (HL) {
+      const uint4* hb = reinterpret_cast<const uint4*>(hsm) + ((size_t)(rbase + b)) * 4;
+      const int f = (b >> 1) & 3;
+      a[0] = hb[0 ^ f];
+      a[1] = hb[1 ^ f];
+      a[2] = hb[2 ^ f];
+      a[3] = hb[3 ^ f];
+    } else {
+      const uint4* hb = reinterpret_cast<const uint4*>(hbuf + (size_t)rbase + b * 32);
+      a[0] = hb[0];
+      a[1] = hb[1];
+      a[2] = hb[2];
+      a[3] = hb[3];
+    }
+  };
+  uint4 an[4];
+  read_h(0, an);
+#pragma unroll
+  for (int t = 0; t < TM; ++t) {
+    uint4 ac[4] = {an[0], an[1], an[2], an[3]};
+    if (t + 1 < TM) {
+      asm volatile("" : "+v"(acc), "+v"(rbase));
+      read_h(t + 1, an);
+    }
+    const bool live = t < T && t * S + sg < nb;
+    const float sc = e8m0_to_f32((s4[t >> 2] >> (8 * (t & 3))) & 0xFFu);
+    const float v = fmaf(sc, block_dot(c[t], ac[0], ac[1], ac[2], ac[3]), acc);
+    acc = live ? v : acc;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
 // TM: steps held per lane (T <= TM, a multiple of 4).  HL: h of every route is staged in LDS
 // (else read from the workspace).  The route table comes from the workspace: the route kernel,
 // the bucketing kernel or the gate/up writer workgroup left it there.
@@ -787,31 +897,11 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
     if (cnt <= 0 || off < 0 || off + cnt > Mk) continue;
 #pragma unroll 1
     for (int j = 0; j < cnt; ++j) {
-      const int route = rw.perm[off + j];
-      float acc = 0.0f;
+      // keeps the decode of the codes inside this loop (hoisted, it would hold 16 VGPRs per step)
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const int b = t * S + sg;
-        if (t < T && b < nb) {
-          uint4 a0, a1, a2, a3;
-          if (HL) {
-            const uint4* hb = reinterpret_cast<const uint4*>(smem) + ((size_t)route * nb + b) * 4;
-            const int f = (b >> 1) & 3;
-            a0 = hb[0 ^ f];
-            a1 = hb[1 ^ f];
-            a2 = hb[2 ^ f];
-            a3 = hb[3 ^ f];
-          } else {
-            const uint4* hb = reinterpret_cast<const uint4*>(hbuf + (size_t)route * I + b * 32);
-            a0 = hb[0];
-            a1 = hb[1];
-            a2 = hb[2];
-            a3 = hb[3];
-          }
-          const float sc = e8m0_to_f32((s4[t >> 2] >> (8 * (t & 3))) & 0xFFu);
-          acc = fmaf(sc, block_dot(c[t], a0, a1, a2, a3), acc);
-        }
-      }
+      for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(c[t].x), "+v"(c[t].y), "+v"(c[t].z), "+v"(c[t].w));
+      const int route = rw.perm[off + j];
+      float acc = down_route_dot<S, TM, HL>(c, s4, T, nb, I, sg, smem, hbuf, route);
       acc = seg_sum<S>(acc);
       if (sg == 0) part[route * RD + r] = acc;
     }
@@ -829,6 +919,201 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
   }
 }
 
+
+// =============================================================================================
+// Fused decode: gate/up and down in one launch, handing h over without fences
+// =============================================================================================
+// For one token (M = 1, the route table rebuilt per workgroup) the two expert stages run in one
+// grid whose workgroups are all resident at once.  Workgroup i first does gate/up unit i (tile
+// i % gu_tiles of distinct expert i / gu_tiles, exactly as k_gateup): it writes its 32 h values
+// write-through (device-scope relaxed atomic stores), waits for them to complete, and adds 1
+// to the arrival counter (tile % kHandSub) of its expert.  Then the first ceil(dn_tiles / tpw)
+// workgroups each take tpw = nw/4 down tiles (4 waves per tile, wave wt of a tile owning hot
+// expert wt, as k_down_combine): they request their down weights into the registers that the
+// gate/up part has just released, wait until every hot expert's counters show all of its
+// gate/up tiles, read h device-coherently (loads that bypass the non-coherent caches) into LDS,
+// and form their rows and the ordered combine.  The low workgroup indices take the down work:
+// their gate/up data is requested first, so they are the first to be free.
+//   No fence is involved: a device-scope release or acquire per workgroup costs tens of ns,
+// serialised, on MI355X; write-through stores whose completion is awaited before the counter
+// add, and coherent loads after it, order the data without one.  A down part waits on gate/up
+// parts of any workgroup, so the whole grid must be resident: the launcher checks the grid
+// against the kernel's occupancy.  The wait is bounded all the same; a launch that ran out of
+// it would flag kErrHandoff in meta[2] (it cannot happen with the grid resident).  The
+// counters are cleared by the router kernel of the same call.
+constexpr int kFusedPool = 40 * 1024;  // LDS pool: gate/up x copy + sums, then down h copy + sums
+constexpr int kHandSpins = 1 << 15;    // wait bound, in polls of ~0.2 us
+
+template <int G, int S, int TM>
+__global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
+    const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
+    size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, int gu_tiles, int n_gu, int n_dnw,
+    size_t gu_bytes, size_t dn_tile_bytes, int nb_i, int T, int tq, int dn_tiles, RouteArgs ra,
+    RouteWs rw, uint16_t* __restrict__ hbuf, float* __restrict__ y, uint32_t* __restrict__ hand) {
+  __shared__ RouteLds rt;
+  __shared__ __align__(16) uint8_t pool[kFusedPool];
+  const int nthr = blockDim.x;
+  const int nw = nthr >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int Mk = ra.M * ra.k;
+  typedef __attribute__((address_space(3))) void lds_void;
+
+  // ---------------- gate/up part ----------------
+  const bool has_gu = (int)blockIdx.x < n_gu;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(pool);
+  float* red = reinterpret_cast<float*>(pool + kXLdsBytes);  // [nw][64]
+  if (has_gu) {
+    const int n_x = H / 8;
+    const int runs = (n_x + 63) / 64;
+    for (int run = wave; run < runs; run += nw) {
+      const int p = min(run * 64 + lane, n_x - 1);
+      __builtin_amdgcn_global_load_lds(x + (size_t)p * 8, (lds_void*)(xs + (size_t)run * 512), 16, 0, 0);
+    }
+  }
+  route_prologue(rt, ra, rw, blockIdx.x == 0);
+  const int nd = rt.nd;
+  const int gtile = (int)blockIdx.x % gu_tiles;
+  const int d = (int)blockIdx.x / gu_tiles;
+  if (has_gu && d < nd) {
+    const uint8_t* tbase = slots + (size_t)rt.dist_slot[d] * image_bytes + (size_t)gtile * gu_tile_bytes;
+    const int g0 = wave * ng / nw;
+    const int ngw = (wave + 1) * ng / nw - g0;
+    uint32_t s4[G];
+    uint4 c[4 * G];
+    load_tile_range<G>(reinterpret_cast<const uint4*>(tbase),
+                       reinterpret_cast<const uint32_t*>(tbase + (size_t)nb * 1024), nb, g0, ngw,
+                       lane, s4, c);
+    __syncthreads();
+    red[wave * 64 + lane] = dot_tile_lds<G>(c, s4, nb, g0, ngw, xs);
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int row = threadIdx.x;
+      float g = 0.0f, u = 0.0f;
+      for (int w = 0; w < nw; ++w) {
+        g += red[w * 64 + row];
+        u += red[w * 64 + row + 32];
+      }
+      const int r = rt.perm[rt.dist_off[d]];
+      __hip_atomic_store(&hbuf[(size_t)r * I + gtile * 32 + row],
+                         (uint16_t)f32_to_bf16_bits(silu_f32(g) * u), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's h stores have completed
+    __syncthreads();                // ... and every thread's
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(&hand[(size_t)(d * kHandSub + gtile % kHandSub) * kHandStride], 1u,
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if ((int)blockIdx.x >= n_dnw) {
+    __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
+    return;
+  }
+
+  // ---------------- down part ----------------
+  constexpr int RD = 64 / S;
+  const int tpw = nw / kDownWaves;   // tiles per workgroup
+  const int tl = wave / kDownWaves;  // this wave's tile
+  const int wt = wave % kDownWaves;  // this wave's place in its tile
+  const int tile = min((int)blockIdx.x * tpw + tl, dn_tiles - 1);  // past the end: a duplicate
+  const int r = lane / S;
+  const int sg = lane % S;
+  const int full = nb_i / S;
+  const int rem = nb_i - full * S;
+  const size_t code_bytes = ((size_t)full * 64 + (size_t)RD * rem) * 16;
+  const uint8_t* sec = slots + gu_bytes + (size_t)tile * dn_tile_bytes;
+  const int slot0 = nd == 0 ? 0 : rt.dist_slot[wt < nd ? wt : 0];  // no expert: any valid slot
+  uint4 c[TM];
+  uint32_t s4[TM / 4];
+  load_down_tile<S, TM>(sec + (size_t)slot0 * image_bytes, code_bytes, full, rem, T, tq, lane, c, s4);
+  // wait for every gate/up tile of every hot expert
+  if (wave == 0) {
+    bool late = false;
+    for (int c0 = 0; c0 < nd * kHandSub; c0 += 64) {
+      const int ci = c0 + lane;
+      const bool used = ci < nd * kHandSub;
+      const uint32_t target = (uint32_t)((gu_tiles - (ci % kHandSub) + kHandSub - 1) / kHandSub);
+      bool mine = !used;
+      int spins = 0;
+      while (true) {
+        if (!mine)
+          mine = __hip_atomic_load(&hand[(size_t)ci * kHandStride], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) >= target;
+        if (__ballot(!mine) == 0ull) break;
+        if (++spins >= kHandSpins) {
+          late = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+    if (late && lane == 0) atomicOr(&rw.meta[2], kErrHandoff);
+  }
+  __syncthreads();  // also: every wave is done with the gate/up use of the pool
+  // h of every route into LDS through device-coherent loads; the quarters of block b are
+  // swizzled by (b >> 1) & 3 as down_route_dot reads them.  Clamped duplicates store the same
+  // value as their owner.  The wait inside also covers the down weights requested above.
+  uint8_t* hsm = pool;
+  const int n_h = Mk * nb_i * 4;
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  for (int base = 0; base < n_h; base += 4 * nthr) {
+    int pidx[4];
+    const uint16_t* src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pidx[i] = min(base + i * nthr + (int)threadIdx.x, n_h - 1);
+      const int route = pidx[i] / (nb_i * 4);
+      const int rb = pidx[i] - route * nb_i * 4;
+      src[i] = hbuf + (size_t)route * I + (rb >> 2) * 32 + (rb & 3) * 8;
+    }
+    u32x4_t v0, v1, v2, v3;
+    asm volatile(
+        "global_load_dwordx4 %0, %4, off sc1\n\t"
+        "global_load_dwordx4 %1, %5, off sc1\n\t"
+        "global_load_dwordx4 %2, %6, off sc1\n\t"
+        "global_load_dwordx4 %3, %7, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3])
+        : "memory");
+    const u32x4_t vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int route = pidx[i] / (nb_i * 4);
+      const int rb = pidx[i] - route * nb_i * 4;
+      const int b = rb >> 2;
+      const int q = (rb & 3) ^ ((b >> 1) & 3);
+      *reinterpret_cast<uint4*>(hsm + (((size_t)route * nb_i + b) * 4 + q) * 16) =
+          make_uint4(vv[i].x, vv[i].y, vv[i].z, vv[i].w);
+    }
+  }
+  float* parts = reinterpret_cast<float*>(pool + (size_t)n_h * 16);  // [tpw][Mk][RD]
+  __syncthreads();
+  // one token: every hot expert has one route and nd <= kDownWaves, so wave wt of a tile owns
+  // expert wt (if hot), whose weights are already in registers
+  if (wt < nd) {
+    const int route = rt.perm[rt.dist_off[wt]];
+    float acc = down_route_dot<S, TM, true>(c, s4, T, nb_i, I, sg, hsm, hbuf, route);
+    acc = seg_sum<S>(acc);
+    if (sg == 0) parts[((size_t)tl * Mk + route) * RD + r] = acc;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < tpw * ra.M * RD; idx += nthr) {
+    const int t2 = idx / (ra.M * RD);
+    const int rest = idx - t2 * ra.M * RD;
+    const int m = rest / RD;
+    const int rr = rest - m * RD;
+    const int tile2 = (int)blockIdx.x * tpw + t2;
+    if (tile2 >= dn_tiles) continue;
+    const float* p2 = parts + (size_t)t2 * Mk * RD;
+    float acc = 0.0f;
+    for (int j = 0; j < ra.k; ++j) {
+      const int route = m * ra.k + j;
+      if (rt.slot[route] >= 0) acc = fmaf(rt.w[route], p2[route * RD + rr], acc);
+    }
+    y[(size_t)m * H + tile2 * RD + rr] = acc;
+  }
+}
 
 // =============================================================================================
 // Grouped GEMM path (many tokens per expert): bf16 MFMA on dequantised MXFP4 weights
@@ -1238,12 +1523,12 @@ __global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ x
 // Launchers (called from the host API after every argument has been validated)
 // =============================================================================================
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, hipStream_t s) {
+                         int H, float* logits, uint32_t* zero, int n_zero, hipStream_t s) {
   if (M >= kGroupedMinTokens)  // a dense GEMM: MFMA
     hipLaunchKernelGGL(k_router_grouped, dim3((M + kGemmTok - 1) / kGemmTok, (E + 63) / 64), dim3(256),
                        0, s, x, M, wr, bias, E, H, logits);
   else
-    hipLaunchKernelGGL(k_router, dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits);
+    hipLaunchKernelGGL(k_router, dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits, zero, n_zero);
   return hipGetLastError();
 }
 
@@ -1404,6 +1689,88 @@ hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, siz
                            hipStream_t s) {
   const size_t threads = (n + 1) / 2;
   hipLaunchKernelGGL(k_residual, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, y, out, n);
+  return hipGetLastError();
+}
+
+// Resident workgroups of k_layer_decode<G, S, TM> with nthr threads on the current device (its
+// whole grid must be resident), from the kernel's occupancy; computed once per device and shape
+// of workgroup.
+// (0 without a device: the fused path is then never chosen.)
+template <int G, int S, int TM>
+static int layer_decode_capacity(int nthr) {
+  static std::atomic<int> cache[16][kMaxWaves + 1];  // [device][waves]; 0 = not computed
+  int dev = 0;
+  const int w = nthr / 64;
+  if (w < 1 || w > kMaxWaves || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+  int v = cache[dev][w].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_layer_decode<G, S, TM>, nthr, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    v = per_cu * cus > 0 ? per_cu * cus : -1;
+    cache[dev][w].store(v, std::memory_order_relaxed);
+  }
+  return v > 0 ? v : 0;
+}
+
+static bool layer_decode_shape(const ImageLayout& L, const ExpertPlan& p, int* G, int* TM) {
+  *G = p.gu_groups;
+  *TM = L.dn_steps <= 4 ? 4 : L.dn_steps <= 8 ? 8 : L.dn_steps <= 12 ? 12 : 16;
+  // the instantiated (G, S, TM) combinations
+  return (*G == 3 && L.dn_seg == 8 && *TM == 12) || (*G >= 1 && *G <= 3 && L.dn_seg == 4 && *TM == 4);
+}
+
+static int layer_decode_grid(const ImageLayout& L, const ExpertPlan& p) {
+  const int tpw = p.gu_waves / kDownWaves;
+  const int n_gu = L.gu_tiles * p.nd_max;
+  const int n_dnw = (L.dn_tiles + tpw - 1) / tpw;
+  return n_gu > n_dnw ? n_gu : n_dnw;
+}
+
+bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M) {
+  if (!(M == 1 && p.prologue && !p.grouped)) return false;
+  if (p.gu_waves % kDownWaves != 0) return false;
+  const int k_routes = p.nd_max;  // M = 1: every route is its own expert
+  if (k_routes > kDownWaves) return false;  // a down wave per hot expert
+  const size_t need = (size_t)k_routes * L.nb_i * 64 + (size_t)(p.gu_waves / kDownWaves) * k_routes * L.dn_rows * 4;
+  if (need > (size_t)kFusedPool || (size_t)L.H * 2 > (size_t)kXLdsBytes) return false;
+  if ((size_t)kXLdsBytes + (size_t)p.gu_waves * 64 * 4 > (size_t)kFusedPool) return false;
+  int G, TM;
+  if (!layer_decode_shape(L, p, &G, &TM)) return false;
+  const int nthr = p.gu_waves * 64;
+  int cap = 0;
+  if (L.dn_seg == 8) cap = layer_decode_capacity<3, 8, 12>(nthr);
+  else if (G == 1) cap = layer_decode_capacity<1, 4, 4>(nthr);
+  else if (G == 2) cap = layer_decode_capacity<2, 4, 4>(nthr);
+  else cap = layer_decode_capacity<3, 4, 4>(nthr);
+  return layer_decode_grid(L, p) <= cap;
+}
+
+hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
+                               const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
+                               const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
+                               hipStream_t s) {
+  (void)M;
+  const int tpw = p.gu_waves / kDownWaves;
+  const int n_gu = L.gu_tiles * p.nd_max;
+  const int n_dnw = (L.dn_tiles + tpw - 1) / tpw;
+  const dim3 g(layer_decode_grid(L, p)), b(p.gu_waves * 64);
+#define MOE_LD(G, SEG, TM)                                                                         \
+  hipLaunchKernelGGL((k_layer_decode<G, SEG, TM>), g, b, 0, s, x, H, I, slots, L.image_bytes,     \
+                     L.gu_tile_bytes, L.nb_h, L.ng_h, L.gu_tiles, n_gu, n_dnw, L.gu_bytes,         \
+                     L.dn_tile_bytes, L.nb_i, L.dn_steps, L.dn_scale_words, L.dn_tiles, ra, rw,    \
+                     hbuf, y, hand)
+  if (L.dn_seg == 8) {
+    MOE_LD(3, 8, 12);
+  } else if (p.gu_groups <= 1) {
+    MOE_LD(1, 4, 4);
+  } else if (p.gu_groups == 2) {
+    MOE_LD(2, 4, 4);
+  } else {
+    MOE_LD(3, 4, 4);
+  }
+#undef MOE_LD
   return hipGetLastError();
 }
 

@@ -153,8 +153,13 @@ moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_
 /* ---------------------------------------------------------------------------------------
  * Whole layer in one call: moe_route followed by moe_experts_forward.  For M*k <= 256 the
  * top-k, slot resolve and bucketing run inside the expert kernels (three launches: router
- * GEMV, gate/up, down + combine).  Same arguments, outputs and numerics as the two calls;
- * topk_ids [M,k] and topk_w [M,k] are written too.
+ * GEMV, gate/up, down + combine).  For one token (M = 1, top_k <= 4) of the shapes the fused
+ * kernel is built for (moe_layer_launches reports it; GPT-OSS-20B's is one) gate/up and down
+ * are one launch: down workgroups fetch their
+ * weights while gate/up still streams and take h over through per-expert arrival counters
+ * in the workspace (two launches in all; the environment variable MOE_DECODE_UNFUSED=1, read
+ * once per process, keeps three).  Same arguments, outputs and numerics as the two calls,
+ * bitwise, on every path; topk_ids [M,k] and topk_w [M,k] are written too.
  * --------------------------------------------------------------------------------------- */
 moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t M,
                              const uint16_t* w_router, const float* router_bias,
@@ -166,7 +171,8 @@ moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t 
 /* moe_layer_forward with an event recorded on `stream` at each stage boundary, for timing the
  * stages of exactly the launches of a layer call: marks[0] before the router, marks[1] after
  * the route stage (router, plus the top-k / bucketing kernel when the call needs it), marks[2]
- * after the gate/up kernel, marks[3] after the down stage.  marks: four events created by the
+ * after the gate/up kernel, marks[3] after the down stage.  When gate/up and down are one
+ * launch, marks[2] and marks[3] are both recorded after it.  marks: four events created by the
  * caller with timing enabled; M >= 1.  Results equal moe_layer_forward's. */
 moe_status moe_layer_forward_marked(const moe_shape* shape, const uint16_t* x, int32_t M,
                                     const uint16_t* w_router, const float* router_bias,
@@ -175,6 +181,12 @@ moe_status moe_layer_forward_marked(const moe_shape* shape, const uint16_t* x, i
                                     int32_t* cold_count, int32_t* cold_routes,
                                     void* ws, size_t ws_bytes, hipStream_t stream,
                                     const hipEvent_t* marks);
+
+/* Number of kernel launches moe_layer_forward makes for M tokens of this shape: 2 when gate/up
+ * and down run as one launch, 3 for small calls, 4 past 256 routes, 5 on the grouped-GEMM path
+ * (M >= 64), 1 for M = 0.  For callers that budget graph nodes or time stages.  Writes *n; no
+ * device work. */
+moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n);
 
 /* The two kernel stages of moe_experts_forward, on their own (for timing a stage or for
  * callers that interleave other work).  Arguments as in moe_experts_forward.

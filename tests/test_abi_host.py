@@ -39,12 +39,33 @@ def test_library_exports_every_declared_symbol():
                           "moe_pack_expert", "moe_unpack_expert", "moe_expert_image_bytes",
                           "moe_workspace_size", "moe_layer_forward", "moe_last_error",
                           "moe_experts_gateup", "moe_experts_down", "moe_layer_forward_marked",
-                          "moe_residual_bf16"}
+                          "moe_residual_bf16", "moe_layer_launches"}
     for n in names:
         assert hasattr(lib, n), n
     # no torch in the exported signatures: the header includes only C/HIP headers
     hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
     assert "torch" not in hdr and "at::" not in hdr
+
+
+def test_layer_launch_counts():
+    """One GPT-OSS-20B-shaped token: router + one fused expert launch (on a GPU); a few
+    tokens: router, gate/up, down; from 64 tokens the grouped GEMM path (top-k / bucketing,
+    gate/up, down, combine after the router); more than 256 routes below that add the top-k /
+    bucketing kernel to the three.  k > 4, or more K groups per gate/up wave than the fused
+    kernel holds (H = 8192), keep three launches."""
+    _lib()
+    if os.environ.get("MOE_DECODE_UNFUSED") == "1":
+        pytest.skip("fused decode switched off in this environment")
+    g = B.make_shape(2880, 2880, 32, 4, 32)
+    # M = 1 fuses only where the device can hold the whole fused grid at once (2 launches on
+    # an MI355X; 3 without a device)
+    assert B.moe_layer_launches(g, 1) in (2, 3)
+    assert [B.moe_layer_launches(g, M) for M in (0, 2, 63, 64)] == [1, 3, 3, 5]
+    e512 = B.make_shape(2048, 512, 512, 10, 256)
+    assert [B.moe_layer_launches(e512, M) for M in (1, 25, 26, 64)] == [3, 3, 4, 5]
+    assert B.moe_layer_launches(B.make_shape(8192, 512, 8, 2, 8), 1) == 3
+    with pytest.raises(B.MoeError):
+        B.moe_layer_launches(g, -1)
 
 
 @pytest.mark.parametrize("name", ["tiny", "gptoss20b_decode", "e512_verify_stack"])

@@ -479,3 +479,51 @@ def test_marked_layer_forward_and_residual(gptoss):
     assert np.array_equal(out.cpu().numpy().view(np.uint16), ref)
     assert np.array_equal(xd.cpu().numpy().view(np.uint16), ref)
 
+
+
+def test_fused_decode_consecutive_tokens_and_maps(gptoss):
+    """One-token layer calls run gate/up and down as one launch.  Over consecutive tokens
+    (h of the previous token still in the workspace), with every expert hot, some top-k experts
+    cold, all cold, and slots relabelled, the fused call equals moe_route + moe_experts_forward
+    bitwise and the oracle to the parity bar."""
+    wl = gptoss.wl
+    shape = gptoss.shape
+    assert B.moe_layer_launches(shape, 1) == 2
+    bias = synthetic.zipf_bias(wl)
+    wr, bd = _dev(gptoss.wr), _dev(bias)
+    E = wl.n_experts
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(E).astype(np.int32)  # expert e in slot perm[e]
+    part = np.arange(E, dtype=np.int32)
+    part[rng.choice(E, E // 2, replace=False)] = -1
+    maps = [("identity", None, None), ("half cold", part, gptoss.slots),
+            ("all cold", np.full(E, -1, np.int32), gptoss.slots),
+            ("relabelled", perm, gptoss.slots_for(np.argsort(perm)))]
+    a, b = L.Buffers(shape, 1), L.Buffers(shape, 1)
+    for name, e2s_np, slots in maps:
+        slots = gptoss.slots if slots is None else slots
+        e2s = None if e2s_np is None else _dev(e2s_np)
+        for t in range(6):
+            say("fused decode:", name, "token", t)
+            xn = synthetic.activations(wl, 1, 700 + t)
+            x = _dev(xn)
+            B.moe_layer_forward(shape, x, 1, wr, bd, e2s, slots, a.ids, a.w, a.y, a.cold_count,
+                                a.cold_routes, a.ws)
+            B.moe_route(shape, x, 1, wr, bd, b.ids, b.w, b.ws)
+            B.moe_experts_forward(shape, x, 1, b.ids, b.w, e2s, slots, b.y, b.cold_count,
+                                  b.cold_routes, b.ws)
+            torch.cuda.synchronize()
+            assert torch.equal(a.ids[:1], b.ids[:1]) and torch.equal(a.w[:1], b.w[:1])
+            assert torch.equal(a.y[:1], b.y[:1]), name
+            cc = int(a.cold_count.item())
+            assert cc == int(b.cold_count.item())
+            assert torch.equal(a.cold_routes[:cc], b.cold_routes[:cc])
+            if t % 3 == 0:
+                _, ids_ref, w_ref = compare_routes(a.ids[:1].cpu().numpy(), a.w[:1].cpu().numpy(),
+                                                   O.router_logits(xn, gptoss.wr, bias), wl.top_k)
+                ref = O.layer_forward(xn, ids_ref, w_ref, gptoss.experts, e2s_np)
+                if name == "all cold":
+                    assert not a.y[:1].any() and cc == wl.top_k
+                else:
+                    close_enough(a.y[:1].cpu().numpy(), ref["y_hot"], f"fused decode {name} {t}")
+                assert cc == len(ref["cold_routes"])
