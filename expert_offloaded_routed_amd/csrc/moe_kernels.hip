@@ -348,7 +348,10 @@ __device__ __forceinline__ void load_tile_range(const uint4* __restrict__ codes,
 }
 
 // Same sum as dot_tile_range with the activation row in LDS (every lane reads the same
-// address: broadcast).
+// address: broadcast).  Straight-line over all 4*G blocks: blocks of groups past ngw or past nb
+// read a valid activation block (index clamped) and add nothing (a select), so no weight load
+// is used only inside a branch (the compiler would sink such a load behind the others and make
+// the first block wait for all of them).
 template <int G>
 __device__ __forceinline__ float dot_tile_lds(const uint4 (&c)[4 * G], const uint32_t (&s4)[G],
                                               int nb, int g0, int ngw,
@@ -356,19 +359,17 @@ __device__ __forceinline__ float dot_tile_lds(const uint4 (&c)[4 * G], const uin
   float acc = 0.0f;
 #pragma unroll
   for (int q = 0; q < G; ++q) {
-    if (q < ngw) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int b = 4 * (g0 + q) + i;
-        if (b < nb) {
-          const uint4* a = reinterpret_cast<const uint4*>(act + 32 * b);
-          const float sc = e8m0_to_f32((s4[q] >> (8 * i)) & 0xFFu);
-          acc = fmaf(sc, block_dot(c[4 * q + i], a[0], a[1], a[2], a[3]), acc);
-        }
-        // one block's activations live at a time: keeps the LDS reads from being hoisted
-        // ahead of all blocks (which would need 16 VGPRs per block)
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * (g0 + q) + i;
+      const bool live = q < ngw && b < nb;
+      const uint4* a = reinterpret_cast<const uint4*>(act + 32 * min(b, nb - 1));
+      const float sc = e8m0_to_f32((s4[q] >> (8 * i)) & 0xFFu);
+      const float v = fmaf(sc, block_dot(c[4 * q + i], a[0], a[1], a[2], a[3]), acc);
+      acc = live ? v : acc;
+      // one block's activations live at a time: keeps the LDS reads from being hoisted
+      // ahead of all blocks (which would need 16 VGPRs per block)
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   return acc;
@@ -690,8 +691,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
   const int ngw = (wave + 1) * ng / nw - g0;
   uint32_t s4[G];
   uint4 c[4 * G];
+  if (XLDS && PRO) {
+    // the copies into LDS have landed (long since: they were requested before the route table)
+    // and are visible to every wave before any weight is requested, so the compute below waits
+    // for each weight block alone (with copies still pending, the compiler would make it wait
+    // for every outstanding load)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
   load_tile_range<G>(codes, scl, nb, g0, ngw, lane, s4, c);
-  if (XLDS) __syncthreads();  // activations in LDS for every wave
+  if (XLDS && !PRO) __syncthreads();  // activations in LDS for every wave
 
   if (SINGLE) {
     // M = 1: the only route of this expert belongs to token 0.  No loop around the dot, so the
@@ -981,10 +990,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
     const int ngw = (wave + 1) * ng / nw - g0;
     uint32_t s4[G];
     uint4 c[4 * G];
+    // x has landed and is visible before any weight is requested, so that the compute waits for
+    // each weight block alone
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     load_tile_range<G>(reinterpret_cast<const uint4*>(tbase),
                        reinterpret_cast<const uint32_t*>(tbase + (size_t)nb * 1024), nb, g0, ngw,
                        lane, s4, c);
-    __syncthreads();
     red[wave * 64 + lane] = dot_tile_lds<G>(c, s4, nb, g0, ngw, xs);
     __syncthreads();
     if (threadIdx.x < 32) {
