@@ -128,4 +128,78 @@ __device__ __forceinline__ float block_dot(const uint4 c, const uint4 a0, const 
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
+// ---- h for the block-scaled matrix cores ------------------------------------------------------
+// A block of 32 bf16 values h (one MXFP4 block of the down projection's K) enters the
+// gfx950 block-scaled MFMA as 2^s * (hi + lo): s = (largest binary exponent in the block) - 7,
+// so that |h| * 2^-s < 2^8; hi = h * 2^-s rounded to E4M3 (OCP: bias 7, with subnormals, max
+// 448), lo = the remainder rounded to E4M3 again.  A bf16 value has 8 significant bits, hi
+// takes the top 4 and the remainder (at most 4 more) is exact in E4M3 as long as it is not
+// below E4M3's smallest subnormal: every element within 2^-9 of the block's largest
+// magnitude is represented exactly, smaller ones to within 2^-10 * 2^s (2^-17 of the block's
+// largest magnitude).
+
+// Binary exponent of |v| from its fp32 exponent field (-127 for zero and fp32 subnormals).
+__device__ __forceinline__ int f32_exp(float v) {
+  return (int)((__float_as_uint(v) >> 23) & 0xFFu) - 127;
+}
+
+// Scale exponent of a block whose largest element exponent is emax (E8M0 byte = s + 127).
+__device__ __forceinline__ int mx_shift(int emax) { return min(max(emax - 7, -127), 127); }
+
+// E4M3 code of v (|v| <= 2^8), rounded to nearest even; *q receives the value it encodes.
+__device__ __forceinline__ uint32_t e4m3_rne(float v, float* q) {
+  const float a = fabsf(v);
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const int e = max(f32_exp(a), -6);  // below 2^-6 the subnormals share that binade's step
+  const float m = __builtin_rintf(__builtin_amdgcn_ldexpf(a, 3 - e));  // a / step, in [0, 16]
+  *q = __builtin_copysignf(__builtin_amdgcn_ldexpf(m, e - 3), v);
+  const uint32_t mi = (uint32_t)m;
+  uint32_t code;
+  if (mi < 8)
+    code = mi;  // subnormal (only in the binade of 2^-6)
+  else if (mi < 16)
+    code = ((uint32_t)(e + 7) << 3) | (mi - 8);
+  else
+    code = (uint32_t)(e + 8) << 3;  // rounded up into the next binade
+  return sign | code;
+}
+
+// hi and lo codes of one element of a block with scale exponent s.
+__device__ __forceinline__ void mx_pair(float h, int s, uint32_t* hi, uint32_t* lo) {
+  const float hp = __builtin_amdgcn_ldexpf(h, -s);
+  float qh, ql;
+  *hi = e4m3_rne(hp, &qh);
+  *lo = e4m3_rne(hp - qh, &ql);  // hp - qh is exact in fp32
+}
+
+// Maximum over the 16 lanes of a DPP row; every lane of the row gets it.
+__device__ __forceinline__ int row_max_i(int v) {
+  v = max(v, dpp_i<0xB1>(v));
+  v = max(v, dpp_i<0x4E>(v));
+  v = max(v, dpp_i<0x141>(v));
+  v = max(v, dpp_i<0x140>(v));
+  return v;
+}
+// ... and over the 32 lanes of a half wave.
+__device__ __forceinline__ int half_max_i(int v) {
+  v = row_max_i(v);
+  return max(v, swz_xor16_i(v));
+}
+
+// D += A * B on the matrix cores: A = 16 rows x 128 K of E2M1 codes (lane l: row l%16, K
+// 32*(l/16) .. +32, 16 bytes, low nibble first) with E8M0 scale byte OPA of sa for the lane's
+// 32 elements; B = 128 K x 16 columns of E4M3 (lane l: column l%16, K 16*(l/16) .. +16 in
+// b0 and K 64 + 16*(l/16) .. +16 in b1) with E8M0 scale byte 0 of sb for the 32-element block
+// l/16 of column l%16.  D: lane l, register i = row 4*(l/16) + i, column l%16.
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+template <int OPA>
+__device__ __forceinline__ f32x4_t mfma_mx(const uint4& a, const uint4& b0, const uint4& b1,
+                                           f32x4_t c, uint32_t sa, uint32_t sb) {
+  const i32x8_t A = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const i32x8_t B = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                     (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, OPA, (int)sa, 0, (int)sb);
+}
+
 }  // namespace moe

@@ -11,18 +11,18 @@
 //             canonical nibble order).  One wave-wide 16-byte load = 1 KiB contiguous.
 //     scales: ng groups x 64 lanes x 4 B; byte i of a lane's word in group q is the E8M0
 //             scale of block 4q+i of that lane's row (127 = 1.0 past the last block).
-//   down section: H/RD tiles of RD = 64/S rows over K = I (nb = I/32 blocks), S chosen per
-//   shape (dn_segments below).  Lane l = r*S + s owns row r of the tile and K segment s; at
-//   step t it holds block t*S + s of its row.  Steps with all lanes active are 1 KiB each
-//   (lane-major, 16 B per lane); the final partial step (when S does not divide nb) stores
-//   only its active lanes, row by row (index r*(nb % S) + s).  Then ceil(T/4) words per lane
-//   of scale bytes: byte i of word q is the scale of the lane's block at step 4q+i (127 past
-//   the end).
+//   down section: H/16 tiles of 16 rows over K = I (nb = I/32 blocks), in K steps of 4 blocks
+//   (128 elements), each step one operand of the block-scaled MFMA (16 rows x 128 K, E2M1):
+//     codes : lane l holds row l%16, block 4s + l/16 of step s (16 B).  Full steps are 1 KiB
+//             (lane-major); a final partial step (nb % 4 blocks) stores only its lanes
+//             l < 16*(nb % 4), also lane-major.
+//     scales: ceil(steps/4) words per lane: byte j of word q is the E8M0 scale of the lane's
+//             block at step 4q+j (127 past the last block).
 //
 // In the gate/up section every lane of a wave owns one output row and all lanes walk the same
-// input block at the same time, so the activation block is uniform across the wave and is read
-// through the scalar unit.  The down section trades that for more, smaller tiles so that one
-// workgroup can own a few output rows for every routed expert and combine them on its own.
+// input block at the same time, so the activation block is uniform across the wave.  The down
+// section feeds the matrix cores directly (no decode): h enters as the other operand, split
+// into two E4M3 terms per element under a shared per-block scale (see the workspace below).
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -34,39 +34,23 @@ namespace moe {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kMaxHidden = 8192;
-constexpr int kMaxInter = 4096;      // down steps per lane stay <= 16 with S = 8
+constexpr int kMaxInter = 4096;      // at most 32 down K steps
 constexpr int kBucketThreads = 1024; // threads of the top-k / bucketing workgroup
-constexpr size_t kDownLdsBudget = 48 * 1024;  // dynamic LDS of the down kernel (h + row sums)
+constexpr int kDnRows = 16;          // rows of a down tile (one MFMA operand)
 
 struct ImageLayout {
   int H, I;
   int nb_h, ng_h;  // gate/up: blocks and groups along K = H
   int nb_i;        // down: blocks along K = I
-  int dn_seg;      // S: lanes (K segments) per down row
-  int dn_rows;     // RD = 64 / S rows per down tile
-  int dn_steps;    // T = ceil(nb_i / S) steps per lane
-  int dn_scale_words;  // ceil(T / 4) scale words per lane
+  int dn_ks;       // down: K steps of 4 blocks
+  int dn_full, dn_rem;  // full K steps; blocks of the final partial step (0: none)
+  int dn_scale_words;   // ceil(dn_ks / 4) scale words per lane
   int gu_tiles, dn_tiles;
   size_t gu_tile_bytes, dn_code_bytes, dn_tile_bytes;
   size_t gu_bytes, dn_bytes, image_bytes;
+  int h_pad;        // I rounded up to whole K steps (128 elements)
+  size_t h_stride;  // workspace bytes of one route's split h: hi[h_pad], lo[h_pad], scales[4*dn_ks]
 };
-
-// S for the down tiles: the fewest padding scale bytes with at most 16 steps per lane, ties to
-// the larger S (more, smaller tiles).
-inline int dn_segments(int nb) {
-  int best = 1;
-  long best_pad = -1;
-  for (int S = 8; S >= 1; S /= 2) {
-    const int T = (nb + S - 1) / S;
-    if (T > 16) continue;
-    const long pad = (long)((T + 3) / 4) * 256 - (long)nb * (64 / S);
-    if (best_pad < 0 || pad < best_pad) {
-      best = S;
-      best_pad = pad;
-    }
-  }
-  return best;
-}
 
 inline ImageLayout image_layout(int H, int I) {
   ImageLayout L;
@@ -75,16 +59,17 @@ inline ImageLayout image_layout(int H, int I) {
   L.nb_h = H / 32;
   L.ng_h = (L.nb_h + 3) / 4;
   L.nb_i = I / 32;
-  L.dn_seg = dn_segments(L.nb_i);
-  L.dn_rows = 64 / L.dn_seg;
-  L.dn_steps = (L.nb_i + L.dn_seg - 1) / L.dn_seg;
-  L.dn_scale_words = (L.dn_steps + 3) / 4;
+  L.dn_ks = (L.nb_i + 3) / 4;
+  L.dn_full = L.nb_i / 4;
+  L.dn_rem = L.nb_i % 4;
+  L.dn_scale_words = (L.dn_ks + 3) / 4;
   L.gu_tiles = I / 32;
-  L.dn_tiles = H / L.dn_rows;
+  L.dn_tiles = H / kDnRows;
   L.gu_tile_bytes = (size_t)L.nb_h * 1024 + (size_t)L.ng_h * 256;
-  const int full = L.nb_i / L.dn_seg, rem = L.nb_i % L.dn_seg;
-  L.dn_code_bytes = ((size_t)full * 64 + (size_t)L.dn_rows * rem) * 16;
+  L.dn_code_bytes = (size_t)L.dn_full * 1024 + (size_t)L.dn_rem * 256;
   L.dn_tile_bytes = L.dn_code_bytes + (size_t)L.dn_scale_words * 256;
+  L.h_pad = L.dn_ks * 128;
+  L.h_stride = ((size_t)2 * L.h_pad + (size_t)4 * L.dn_ks + 15) / 16 * 16;
   L.gu_bytes = L.gu_tile_bytes * L.gu_tiles;
   L.dn_bytes = L.dn_tile_bytes * L.dn_tiles;
   L.image_bytes = (L.gu_bytes + L.dn_bytes + 255) / 256 * 256;
@@ -102,7 +87,7 @@ struct WsLayout {
   size_t dist;           // i32x4 [nd_max]: distinct hot experts {slot, bucket offset, count, id}
   size_t cold_list;      // i32 [M*k]
   size_t items;          // i32x2 [n_items_max]: grouped GEMM work list {distinct expert, first route}
-  size_t hbuf;           // bf16 [M*k][I]
+  size_t hq;             // split h of every route, ImageLayout::h_stride bytes each
   size_t pdn;            // f32 [M*k][H]: down partial sums when they do not fit in LDS
   size_t hand;           // u32 counters of the fused decode kernel, one per 64 bytes
   size_t total;
@@ -111,7 +96,7 @@ struct WsLayout {
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Fused decode kernel handoff: kHandSub arrival counters per distinct hot expert (gate/up tile t
-// counts on counter t % kHandSub), each on its own 64-byte line.
+// counts on counter t % kHandSub), each on its own 64-byte line, then the down-tile claim counter.
 constexpr int kHandSub = 8;
 constexpr int kHandStride = 16;  // 32-bit words between counters
 
@@ -128,7 +113,6 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   const ImageLayout L = image_layout(H, I);
   const size_t Mk = (size_t)M * k;
   const size_t nd = Mk < (size_t)E ? Mk : (size_t)E;
-  (void)L;
   size_t o = 0;
   W.logits = o;      o = align256(o + 4 * (size_t)M * E);
   W.route_slot = o;  o = align256(o + 4 * Mk);
@@ -139,9 +123,9 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   W.dist = o;        o = align256(o + 16 * nd);
   W.cold_list = o;   o = align256(o + 4 * Mk);
   W.items = o;       o = align256(o + 8 * (size_t)n_items_max((int)Mk, E));
-  W.hbuf = o;        o = align256(o + 2 * Mk * I);
+  W.hq = o;          o = align256(o + Mk * L.h_stride);
   W.pdn = o;         o = align256(o + 4 * Mk * (size_t)H);
-  W.hand = o;        o = align256(o + 64 * (size_t)nd * kHandSub);
+  W.hand = o;        o = align256(o + 64 * ((size_t)nd * kHandSub + 1));
   W.total = o;
   return W;
 }
@@ -165,9 +149,6 @@ struct ExpertPlan {
   bool prologue;     // every expert workgroup rebuilds the route table (M*k <= kProMaxRoutes)
   int gu_waves;      // waves per gate/up workgroup
   int gu_groups;     // most K groups (of 4 blocks) any gate/up wave holds
-  bool h_in_lds;     // down: h of every route staged in LDS
-  bool part_in_lds;  // down: per-route row sums in LDS (else in the workspace)
-  size_t dn_lds;     // down: dynamic LDS bytes
 };
 
 // Routes of a call as the expert kernels see them (kernel arguments, passed by value).
@@ -199,7 +180,7 @@ hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const flo
 bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M);
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                               const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
+                               const RouteWs& rw, uint8_t* hq, float* y, uint32_t* hand,
                                hipStream_t s);
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,
@@ -207,17 +188,17 @@ hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_i
 ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k);
 hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                          const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                         const RouteWs& rw, uint16_t* hbuf, hipStream_t s);
+                         const RouteWs& rw, uint8_t* hq, hipStream_t s);
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                       const uint16_t* hbuf, float* pdn, float* y, hipStream_t s);
+                       const uint8_t* hq, float* pdn, float* y, hipStream_t s);
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, size_t n,
                            hipStream_t s);
 hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,
                                  const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                                 const RouteWs& rw, uint16_t* hbuf, hipStream_t s);
+                                 const RouteWs& rw, uint8_t* hq, hipStream_t s);
 hipError_t launch_down_grouped(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                                const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                               const uint16_t* hbuf, float* pdn, float* y, hipStream_t s);
+                               const uint8_t* hq, float* pdn, float* y, hipStream_t s);
 
 }  // namespace moe

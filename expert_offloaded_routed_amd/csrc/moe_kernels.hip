@@ -3,15 +3,18 @@
 //   k_router        bf16 router GEMV + bias, one wave per expert row (logits to the workspace).
 //   k_topk_bucket   softmax / top-k / renormalise (one wave per token), then in one workgroup:
 //                   route -> slot resolve, cold report, per-expert counts, DPP prefix scans,
-//                   bucket permutation, list of distinct hot experts.
-//   k_gateup        fused MXFP4 gate/up GEMV + SiLU(g)*u -> h (bf16) per route.  One workgroup
-//                   per (distinct hot expert, 32-row tile), its waves split K.  For small
-//                   calls each workgroup first rebuilds the route table (top-k, resolve,
-//                   buckets) in LDS, which replaces the top-k / bucketing kernel.
-//   k_down_combine  MXFP4 down GEMV of every hot route for a few output rows per workgroup,
-//                   then y = ordered (ascending j) weighted sum of those routes.
-// Dependencies between stages go through kernel boundaries only: a device-scope fence or a
-// shared arrival counter per workgroup costs tens of nanoseconds each, serialised, on MI355X.
+//                   bucket permutation, list of distinct hot experts, grouped work list.
+//   k_gateup        fused MXFP4 gate/up GEMV + SiLU(g)*u -> h per route (split for the matrix
+//                   cores).  One workgroup per (distinct hot expert, 32-row tile), its waves
+//                   split K.  For small calls each workgroup first rebuilds the route table
+//                   (top-k, resolve, buckets) in LDS, which replaces the top-k / bucketing kernel.
+//   k_down_mx       down projection of every hot route on the block-scaled MFMA (E2M1 weights,
+//                   h as two E4M3 terms), per (expert, routes) item -> fp32 partial rows;
+//   k_combine       then y = ordered (ascending j) weighted sum of those rows.
+//   k_layer_decode  one token: gate/up and down (with the combine) in one launch.
+//   k_gateup_grouped / k_router_grouped: bf16 MFMA GEMMs for many tokens.
+// Dependencies between stages go through kernel boundaries, except inside k_layer_decode (see
+// there): a device-scope fence per workgroup costs tens of nanoseconds, serialised, on MI355X.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -606,6 +609,38 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
   }
 }
 
+// ---- h in the workspace -----------------------------------------------------------------------
+// Every route's h is kept split for the down projection's block-scaled MFMA (see mx_pair):
+// per route (h_stride bytes) hi[h_pad] and lo[h_pad] E4M3 codes, then one E8M0 scale byte per
+// 32-element block.  Elements past I, and scale bytes past the last block, are never written:
+// the down kernels substitute zeros and 127 for them.
+
+// Lanes 32j .. 32j+31 hold (as fp32) the 32 bf16 values of one block of h, element lane & 31;
+// all 32 active.  hi points at the block's first hi code, h_pad separates hi and lo, sc is the
+// block's scale byte.  WT: device-scope write-through stores, for a reader in the same launch.
+template <bool WT>
+__device__ __forceinline__ void store_h_block(float h, uint8_t* __restrict__ hi, int h_pad,
+                                              uint8_t* __restrict__ sc) {
+  const int s = mx_shift(half_max_i(f32_exp(h)));
+  uint32_t bh, bl;
+  mx_pair(h, s, &bh, &bl);
+  const int e = threadIdx.x & 31;
+  if (WT) {
+    __hip_atomic_store(hi + e, (uint8_t)bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(hi + h_pad + e, (uint8_t)bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (e == 0) __hip_atomic_store(sc, (uint8_t)(s + 127), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    hi[e] = (uint8_t)bh;
+    hi[h_pad + e] = (uint8_t)bl;
+    if (e == 0) *sc = (uint8_t)(s + 127);
+  }
+}
+
+// bf16(silu(g) * u), returned as the fp32 value of that bf16.
+__device__ __forceinline__ float swiglu_bf16(float g, float u) {
+  return __uint_as_float(f32_to_bf16_bits(silu_f32(g) * u) << 16);
+}
+
 // ---- gate/up + SiLU*up ----------------------------------------------------------------------
 // grid = (I/32 tiles, nd_max); block = nw waves.  Lane l < 32 accumulates gate row 32*tile + l,
 // lane l >= 32 the matching up row; wave w covers groups [w*ng/nw, (w+1)*ng/nw).
@@ -614,8 +649,8 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
 template <bool SINGLE, int G, bool PRO, bool XLDS>
 __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
     const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
-    size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, RouteArgs ra, RouteWs rw,
-    uint16_t* __restrict__ hbuf) {
+    size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, int h_pad, size_t h_stride,
+    RouteArgs ra, RouteWs rw, uint8_t* __restrict__ hq) {
   __shared__ float red[kMaxWaves][SINGLE ? 1 : kTokPerPass][64];
   __shared__ RouteLds rt;
   __shared__ __align__(16) uint16_t xs[XLDS ? kXLdsBytes / 2 : 8];
@@ -714,8 +749,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
         g += red[w][0][row];
         u += red[w][0][row + 32];
       }
-      const int r = perm[off];
-      hbuf[(size_t)r * I + tile * 32 + row] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
+      uint8_t* hr = hq + (size_t)perm[off] * h_stride;
+      store_h_block<false>(swiglu_bf16(g, u), hr + tile * 32, h_pad, hr + 2 * h_pad + tile);
     }
     return;
   }
@@ -730,6 +765,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
                                 : dot_tile_range<G>(c, s4, nb, g0, ngw, x + (size_t)tok * H);
     }
     __syncthreads();
+    // one route per half wave (nthr is a multiple of 64, so a half wave is all in or all out)
     for (int idx = threadIdx.x; idx < nt * 32; idx += nthr) {
       const int t = idx >> 5;
       const int row = idx & 31;
@@ -738,196 +774,193 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
         g += red[w][t][row];
         u += red[w][t][row + 32];
       }
-      const int r = perm[off + base + t];
-      hbuf[(size_t)r * I + tile * 32 + row] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
+      uint8_t* hr = hq + (size_t)perm[off + base + t] * h_stride;
+      store_h_block<false>(swiglu_bf16(g, u), hr + tile * 32, h_pad, hr + 2 * h_pad + tile);
     }
     __syncthreads();
   }
 }
 
-// ---- down + ordered combine -----------------------------------------------------------------
-// The down section of an image holds tiles of RD = 64/S rows.  Lane l = r*S + s of a wave owns
-// row r of the tile and K segment s: at step t it holds block t*S + s of its row (steps past
-// the last block hold nothing).  Steps with every lane active are 1 KiB each; the final,
-// partial step stores only its active lanes, row by row.  Scale bytes follow the codes, four
-// steps per lane word.
-//
-// grid = H/RD tiles; block = 4 waves.  A workgroup owns RD output rows for every hot route:
-// wave w takes distinct experts w, w+4, ...; for each route of an expert the S lanes of a row
-// add their segment sums (DPP), and the row result goes to `part`.  After a barrier the
-// workgroup forms y[m][row] = sum over j ascending (hot routes) of w[m,j] * part[(m,j)][row]:
-// no other workgroup is involved, so the combine needs no cross-workgroup synchronisation.
-// h comes from LDS when every route fits (hp = 80-byte pitch per block, 64 used: the padding
-// spreads the S segments of a row over distinct LDS banks), else straight from the workspace.
-template <int S>
-__device__ __forceinline__ float seg_sum(float v) {
-  if (S >= 2) v += dpp_f<0xB1>(v);
-  if (S >= 4) v += dpp_f<0x4E>(v);
-  if (S >= 8) v += dpp_f<0x141>(v);
-  return v;
+// ---- down projection on the matrix cores --------------------------------------------------------
+// A down tile (16 rows of one expert) is streamed one K step (4 blocks = 128 elements) per MFMA
+// operand: a wave-wide 16-byte load is 1 KiB, and nothing is decoded (the block-scaled MFMA
+// takes the E2M1 codes with their E8M0 scales).  h enters as the other operand: a column is one
+// route's hi or lo codes (see store_h_block) with the block scales.
+
+// This lane's A operand of down step s (clamped to the last step; lanes past the stored part
+// of a partial step re-read a stored lane and meet zero h).
+__device__ __forceinline__ uint4 dn_a(const uint8_t* __restrict__ tb, int s, int ks, int full,
+                                      int rem, int lane) {
+  s = min(s, ks - 1);
+  const int idx = s < full ? s * 64 + lane : full * 64 + min(lane, 16 * rem - 1);
+  return reinterpret_cast<const uint4*>(tb)[idx];
 }
 
-constexpr int kDownWaves = 4;
+// Scale word q of this lane (byte j: step 4q + j), clamped to the last word.
+__device__ __forceinline__ uint32_t dn_sw(const uint8_t* __restrict__ tb, size_t code_bytes, int q,
+                                          int nsw, int lane) {
+  return reinterpret_cast<const uint32_t*>(tb + code_bytes)[min(q, nsw - 1) * 64 + lane];
+}
 
-// Loads one expert's down tile for this lane: scale words first, then TM code steps.  Steps
-// past T re-read step T-1 and lanes without a block in the partial step re-read one of their
-// row's blocks; both are weighted by zero later.  No load depends on a lane test.
-template <int S, int TM>
-__device__ __forceinline__ void load_down_tile(const uint8_t* __restrict__ tb, size_t code_bytes,
-                                               int full, int rem, int T, int tq, int lane,
-                                               uint4 (&c)[TM], uint32_t (&s4)[TM / 4]) {
-  constexpr int RD = 64 / S;
-  const int r = lane / S;
-  const int sg = lane % S;
-  const int psg = rem > 0 ? min(sg, rem - 1) : 0;
-  const uint4* codes = reinterpret_cast<const uint4*>(tb);
-  const uint32_t* scl = reinterpret_cast<const uint32_t*>(tb + code_bytes);
-#pragma unroll
-  for (int q = 0; q < TM / 4; ++q) s4[q] = scl[min(q, tq - 1) * 64 + lane];
-#pragma unroll
-  for (int t = 0; t < TM; ++t) {
-    const int tt = min(t, T - 1);
-    c[t] = codes[tt < full ? tt * 64 + lane : full * 64 + r * rem + psg];
+// The block-scaled MFMA with the A scale byte chosen at run time among constants (j & 3 is a
+// constant once the step loop is unrolled).
+__device__ __forceinline__ f32x4_t mfma_mx_j(int j, const uint4& a, const uint4& b0,
+                                             const uint4& b1, f32x4_t c, uint32_t sa,
+                                             uint32_t sb) {
+  switch (j & 3) {
+    case 0: return mfma_mx<0>(a, b0, b1, c, sa, sb);
+    case 1: return mfma_mx<1>(a, b0, b1, c, sa, sb);
+    case 2: return mfma_mx<2>(a, b0, b1, c, sa, sb);
+    default: return mfma_mx<3>(a, b0, b1, c, sa, sb);
   }
-  (void)RD;
 }
 
-// One route's partial down sum for this lane's row segment: steps t < TM of block t*S + sg, h from
-// the LDS copy (HL; 16-byte quarters of block b swizzled by (b >> 1) & 3) or from the workspace.
-// Straight-line over the steps, software-pipelined by hand: the h block of step t+1 is read
-// before step t's arithmetic.  Its address passes through an empty asm together with the sum
-// so far, which keeps the compiler from issuing it any earlier (all reads up front would need
-// 16 VGPRs per step).  Lanes without a block at a step, and steps past T, read a valid block
-// (index clamped) and add nothing (a select, not a product, so whatever that block holds
-// cannot leak in).
-template <int S, int TM, bool HL>
-__device__ __forceinline__ float down_route_dot(const uint4 (&c)[TM], const uint32_t (&s4)[TM / 4],
-                                                int T, int nb, int I, int sg, const uint8_t* hsm,
-                                                const uint16_t* __restrict__ hbuf, int route) {
-  float acc = 0.0f;
-  int rbase = HL ? route * nb : route * I;  // first h block (LDS) or element (workspace)
-  auto read_h = [&](int t, uint4 (&a)[4]) {
-    const int b = min(t * S + sg, nb - 1);
-    if (HL) {
-      const uint4* hb = reinterpret_cast<const uint4*>(hsm) + ((size_t)(rbase + b)) * 4;
-      const int f = (b >> 1) & 3;
-      a[0] = hb[0 ^ f];
-      a[1] = hb[1 ^ f];
-      a[2] = hb[2 ^ f];
-      a[3] = hb[3 ^ f];
-    } else {
-      const uint4* hb = reinterpret_cast<const uint4*>(hbuf + (size_t)rbase + b * 32);
-      a[0] = hb[0];
-      a[1] = hb[1];
-      a[2] = hb[2];
-      a[3] = hb[3];
-    }
-  };
-  uint4 an[4];
-  read_h(0, an);
+// Scale word of a route's h for down step s (bytes: blocks 4s .. 4s+3); bytes of blocks past
+// the last one are never written, so they read as 127 (1.0, against zero codes).
+__device__ __forceinline__ uint32_t h_scale_word(uint32_t w, int s, int nb_i) {
 #pragma unroll
-  for (int t = 0; t < TM; ++t) {
-    uint4 ac[4] = {an[0], an[1], an[2], an[3]};
-    if (t + 1 < TM) {
-      asm volatile("" : "+v"(acc), "+v"(rbase));
-      read_h(t + 1, an);
-    }
-    const bool live = t < T && t * S + sg < nb;
-    const float sc = e8m0_to_f32((s4[t >> 2] >> (8 * (t & 3))) & 0xFFu);
-    const float v = fmaf(sc, block_dot(c[t], ac[0], ac[1], ac[2], ac[3]), acc);
-    acc = live ? v : acc;
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  return acc;
+  for (int j = 0; j < 4; ++j)
+    if (4 * s + j >= nb_i) w = (w & ~(0xFFu << (8 * j))) | (127u << (8 * j));
+  return w;
 }
 
-// TM: steps held per lane (T <= TM, a multiple of 4).  HL: h of every route is staged in LDS
-// (else read from the workspace).  The route table comes from the workspace: the route kernel,
-// the bucketing kernel or the gate/up writer workgroup left it there.
-template <int S, int TM, bool HL>
-__global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
-    int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
-    size_t dn_tile_bytes, int nb, int T, int tq, RouteArgs ra, RouteWs rw,
-    const uint16_t* __restrict__ hbuf, int part_in_lds, float* __restrict__ pdn,
-    float* __restrict__ y) {
-  constexpr int RD = 64 / S;
-  extern __shared__ __align__(16) uint8_t smem[];  // [h copy (HL) | row sums]
-  const int tile = blockIdx.x;
+// ---- down + partial sums for the combine --------------------------------------------------------
+// grid = (ceil(H/16 / (4*kDnRW)), work items), 256 threads.  An item is one distinct hot expert
+// and up to kItemRoutes of its routes (the bucketing work list), or, without a work list, one
+// distinct hot expert with all its routes (then fewer than kItemRoutes).  Wave w owns down tiles
+// kDnRW*(4*blockIdx.x + w) + q; the item's routes go through in passes of 16 (one MFMA column
+// each), the h of a pass staged in LDS 4 K steps at a time, double buffered, the next stage's
+// weights and h requested before the current stage's MFMAs.  Each route's rows go to
+// pdn[route][row] in fp32; k_combine forms y in the fixed route order.
+constexpr int kDnRW = 2;                                // down tiles per wave
+constexpr int kDnSub = 16;                              // routes per pass
+constexpr int kDnRoutePitch = 4 * 256 + 16;             // 4 steps of hi|lo (+16: bank spread)
+
+struct DnStage {
+  uint8_t b[kDnSub][kDnRoutePitch];  // [route][step * 256 + (lo ? 128 : 0) + k]
+  uint32_t sc[kDnSub][4];            // [route][step]: scale bytes of the step's 4 blocks
+};
+
+__global__ __launch_bounds__(256) void k_down_mx(
+    int H, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
+    size_t dn_tile_bytes, size_t dn_code_bytes, int dn_tiles, int ks, int full, int rem, int nsw,
+    int I, int nb_i, int h_pad, int h_stride, RouteArgs ra, RouteWs rw, int use_items,
+    const uint8_t* __restrict__ hq, float* __restrict__ pdn) {
+  __shared__ __align__(16) DnStage st[2];
+  __shared__ int route_of[kItemRoutes];
   const int Mk = ra.M * ra.k;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane / S;
-  const int sg = lane % S;
-  const int full = nb / S;        // steps with all lanes active
-  const int rem = nb - full * S;  // active segments in the final partial step
-  const uint8_t* sec = slots + gu_bytes + (size_t)tile * dn_tile_bytes;
-  const size_t code_bytes = ((size_t)full * 64 + (size_t)RD * rem) * 16;
-
-  // Front: table reads, the h copy, then the first expert's weights.  A wave without an
-  // expert of its own re-reads one that another wave loads (dist[0], or slot 0 when no expert
-  // is hot) and computes nothing with it.
-  const int nd_max = Mk < ra.E ? Mk : ra.E;
-  const int nd = rw.meta[0];
-  const int sw = rw.dist[wave < nd_max ? wave : nd_max - 1].x;
-  const int s0 = rw.dist[0].x;
-  const int slot0 = nd == 0 ? 0 : (wave < nd ? sw : s0);
-  const int n_h = Mk * nb * 4;  // 16-byte chunks of h
-  if (HL) {
-    // h goes straight from the workspace to LDS (no registers), one 1 KiB run of 64 chunks per
-    // wave instruction; lane i of a run writes LDS chunk base + i, so the layout permutes the
-    // source instead: LDS chunk (route, block b, q') holds quarter q' ^ ((b >> 1) & 3) of block
-    // b, which puts the S segments of a row on distinct banks.  Runs past n_h re-read the
-    // last chunk into padding.
-    typedef __attribute__((address_space(3))) void lds_void;
-    const int runs = (n_h + 63) / 64;
-    for (int run = wave; run < runs; run += kDownWaves) {
-      const int p = min(run * 64 + lane, n_h - 1);
-      const int route = p / (nb * 4);
-      const int rb = p - route * nb * 4;
-      const int b = rb >> 2;
-      const int q = (rb & 3) ^ ((b >> 1) & 3);
-      const uint16_t* src = hbuf + (size_t)route * I + b * 32 + q * 8;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(smem + (size_t)run * 1024), 16, 0, 0);
-    }
+  int d, base;
+  if (use_items) {
+    if ((int)blockIdx.y >= rw.meta[3]) return;
+    const int2 it = rw.items[blockIdx.y];
+    d = it.x;
+    base = it.y;
+  } else {
+    if ((int)blockIdx.y >= rw.meta[0]) return;
+    d = blockIdx.y;
+    base = 0;
   }
-  uint4 c[TM];
-  uint32_t s4[TM / 4];
-  __builtin_amdgcn_sched_barrier(0);  // the h copy is requested before the weights
-  load_down_tile<S, TM>(sec + (size_t)slot0 * image_bytes, code_bytes, full, rem, T, tq, lane, c, s4);
-  float* part = part_in_lds ? reinterpret_cast<float*>(smem + (HL ? (size_t)(n_h + 63) / 64 * 1024 : 0))
-                            : pdn + (size_t)tile * Mk * RD;
+  const int4 dd = rw.dist[d];
+  const int slot = dd.x, off = dd.y, cnt = dd.z;
+  if (cnt <= 0 || off < 0 || off + cnt > Mk || base < 0 || base >= cnt) return;
+  const int nt = min(kItemRoutes, cnt - base);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kItemRoutes; i += blockDim.x) route_of[i] = rw.perm[off + base + min(i, nt - 1)];
   __syncthreads();
-
-  for (int d = wave; d < nd; d += kDownWaves) {
-    const int4 dd = rw.dist[d];
-    if (d != wave)
-      load_down_tile<S, TM>(sec + (size_t)dd.x * image_bytes, code_bytes, full, rem, T, tq, lane, c, s4);
-    const int off = dd.y, cnt = dd.z;
-    if (cnt <= 0 || off < 0 || off + cnt > Mk) continue;
-#pragma unroll 1
-    for (int j = 0; j < cnt; ++j) {
-      // keeps the decode of the codes inside this loop (hoisted, it would hold 16 VGPRs per step)
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 15, g = lane >> 4;
+  const int T0 = ((int)blockIdx.x * 4 + w) * kDnRW;
+  const uint8_t* tb[kDnRW];
 #pragma unroll
-      for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(c[t].x), "+v"(c[t].y), "+v"(c[t].z), "+v"(c[t].w));
-      const int route = rw.perm[off + j];
-      float acc = down_route_dot<S, TM, HL>(c, s4, T, nb, I, sg, smem, hbuf, route);
-      acc = seg_sum<S>(acc);
-      if (sg == 0) part[route * RD + r] = acc;
+  for (int q = 0; q < kDnRW; ++q)
+    tb[q] = slots + (size_t)slot * image_bytes + gu_bytes + (size_t)min(T0 + q, dn_tiles - 1) * dn_tile_bytes;
+  const int ngrp = (ks + 3) / 4;
+  // staging of a 4-step group: thread tid moves chunks tid + 256*k (route ci >> 6, step
+  // (ci >> 4) & 3, 16-byte piece ci & 15: hi for pieces 0-7, lo for 8-15) and, as thread
+  // tid & 63, the scale word of route (tid & 63) >> 2, step tid & 3.  Every load is issued
+  // (addresses clamped); chunks past I or past the last step are replaced by zeros.
+  for (int sub = 0; sub < nt; sub += kDnSub) {
+    const int ns = min(kDnSub, nt - sub);
+    uint4 an[kDnRW][4], bvn[4];
+    uint32_t swn[kDnRW], svn;
+#define MOE_DN_LOAD(GRP)                                                                         \
+  do {                                                                                           \
+    _Pragma("unroll") for (int q = 0; q < kDnRW; ++q) {                                          \
+      swn[q] = dn_sw(tb[q], dn_code_bytes, (GRP), nsw, lane);                                    \
+      _Pragma("unroll") for (int j = 0; j < 4; ++j) an[q][j] = dn_a(tb[q], 4 * (GRP) + j, ks, full, rem, lane); \
+    }                                                                                            \
+    _Pragma("unroll") for (int k2 = 0; k2 < 4; ++k2) {                                           \
+      const int ci = tid + 256 * k2;                                                             \
+      const int s_ = 4 * (GRP) + ((ci >> 4) & 3);                                                \
+      const int pc = ci & 15;                                                                    \
+      const int kpos = 128 * s_ + 16 * (pc & 7);                                                 \
+      const uint8_t* src = hq + (size_t)route_of[sub + min(ci >> 6, ns - 1)] * h_stride +      \
+                           (pc < 8 ? 0 : h_pad) + 128 * min(s_, ks - 1) + 16 * (pc & 7);         \
+      const uint4 v_ = *reinterpret_cast<const uint4*>(src);                                     \
+      bvn[k2] = (s_ < ks && kpos < I) ? v_ : make_uint4(0, 0, 0, 0);                             \
+    }                                                                                            \
+    {                                                                                            \
+      const int s_ = 4 * (GRP) + (tid & 3);                                                      \
+      const uint8_t* src = hq + (size_t)route_of[sub + min((tid & 63) >> 2, ns - 1)] * h_stride + \
+                           2 * h_pad + 4 * min(s_, ks - 1);                                      \
+      const uint32_t v_ = *reinterpret_cast<const uint32_t*>(src);                               \
+      svn = s_ < ks ? h_scale_word(v_, s_, nb_i) : 0x7F7F7F7Fu;                                  \
+    }                                                                                            \
+  } while (0)
+    MOE_DN_LOAD(0);
+    f32x4_t acc[kDnRW];
+#pragma unroll
+    for (int q = 0; q < kDnRW; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int grp = 0; grp < ngrp; ++grp) {
+      DnStage& S = st[grp & 1];
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const int ci = tid + 256 * k2;
+        const int pc = ci & 15;
+        *reinterpret_cast<uint4*>(&S.b[ci >> 6][((ci >> 4) & 3) * 256 + (pc < 8 ? 0 : 128) + 16 * (pc & 7)]) = bvn[k2];
+      }
+      if (tid < 64) S.sc[tid >> 2][tid & 3] = svn;
+      uint4 ac[kDnRW][4];
+      uint32_t sw[kDnRW];
+#pragma unroll
+      for (int q = 0; q < kDnRW; ++q) {
+        sw[q] = swn[q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ac[q][j] = an[q][j];
+      }
+      if (grp + 1 < ngrp) MOE_DN_LOAD(grp + 1);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool live = 4 * grp + j < ks;
+        const uint8_t* bp = &S.b[c][j * 256 + 16 * g];
+        const uint4 h0 = *reinterpret_cast<const uint4*>(bp);
+        const uint4 h1 = *reinterpret_cast<const uint4*>(bp + 64);
+        const uint4 l0 = *reinterpret_cast<const uint4*>(bp + 128);
+        const uint4 l1 = *reinterpret_cast<const uint4*>(bp + 192);
+        const uint32_t sb = (S.sc[c][j] >> (8 * g)) & 0xFFu;
+#pragma unroll
+        for (int q = 0; q < kDnRW; ++q) {
+          f32x4_t v = mfma_mx_j(j, ac[q][j], h0, h1, acc[q], sw[q], sb);
+          v = mfma_mx_j(j, ac[q][j], l0, l1, v, sw[q], sb);
+          acc[q] = live ? v : acc[q];
+        }
+      }
     }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < ra.M * RD; idx += blockDim.x) {
-    const int m = idx / RD;
-    const int rr = idx - m * RD;
-    float acc = 0.0f;
-    for (int j = 0; j < ra.k; ++j) {
-      const int route = m * ra.k + j;
-      if (rw.route_slot[route] >= 0) acc = fmaf(ra.w_in[route], part[route * RD + rr], acc);
+#undef MOE_DN_LOAD
+    // lane (g, c), register i: row 4g + i of the tile, route c of the pass
+    if (c < ns) {
+      float* pr = pdn + (size_t)route_of[sub + c] * H;
+#pragma unroll
+      for (int q = 0; q < kDnRW; ++q)
+        if (T0 + q < dn_tiles)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pr[(T0 + q) * kDnRows + 4 * g + i] = acc[q][i];
     }
-    y[(size_t)m * H + tile * RD + rr] = acc;
+    __syncthreads();  // the next pass restages st
   }
 }
-
 
 // =============================================================================================
 // Fused decode: gate/up and down in one launch, handing h over without fences
@@ -935,14 +968,17 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
 // For one token (M = 1, the route table rebuilt per workgroup) the two expert stages run in one
 // grid whose workgroups are all resident at once.  Workgroup i first does gate/up unit i (tile
 // i % gu_tiles of distinct expert i / gu_tiles, exactly as k_gateup): it writes its 32 h values
-// write-through (device-scope relaxed atomic stores), waits for them to complete, and adds 1
-// to the arrival counter (tile % kHandSub) of its expert.  Then the first ceil(dn_tiles / tpw)
-// workgroups each take tpw = nw/4 down tiles (4 waves per tile, wave wt of a tile owning hot
-// expert wt, as k_down_combine): they request their down weights into the registers that the
+// (one block, split for the matrix cores) write-through (device-scope relaxed atomic stores),
+// waits for them to complete, and adds 1 to the arrival counter (tile % kHandSub) of its
+// expert.  Then it claims the next down tile (of H/16) from a counter, so that the down work,
+// and its weight traffic, goes to the workgroups whose gate/up part ended first (those on
+// compute units that hold one workgroup of the grid, not two).  The waves of a down tile own
+// (hot expert slot, K part) pairs, request their down weights into the registers that the
 // gate/up part has just released, wait until every hot expert's counters show all of its
-// gate/up tiles, read h device-coherently (loads that bypass the non-coherent caches) into LDS,
-// and form their rows and the ordered combine.  The low workgroup indices take the down work:
-// their gate/up data is requested first, so they are the first to be free.
+// gate/up tiles, read h
+// device-coherently (loads that bypass the non-coherent caches) into LDS and run the
+// block-scaled MFMA over their K part (column 0 of B = hi, column 1 = lo); the workgroup then
+// forms y for its 16 rows in the fixed route order.
 //   No fence is involved: a device-scope release or acquire per workgroup costs tens of ns,
 // serialised, on MI355X; write-through stores whose completion is awaited before the counter
 // add, and coherent loads after it, order the data without one.  A down part waits on gate/up
@@ -952,15 +988,19 @@ __global__ __launch_bounds__(kDownWaves * 64) void k_down_combine(
 // counters are cleared by the router kernel of the same call.
 constexpr int kFusedPool = 40 * 1024;  // LDS pool: gate/up x copy + sums, then down h copy + sums
 constexpr int kHandSpins = 1 << 15;    // wait bound, in polls of ~0.2 us
+constexpr int kFusedSlots = 4;         // hot experts of the token (waves per K part)
 
-template <int G, int S, int TM>
+template <int G, int TMX>
 __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
     const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
     size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, int gu_tiles, int n_gu, int n_dnw,
-    size_t gu_bytes, size_t dn_tile_bytes, int nb_i, int T, int tq, int dn_tiles, RouteArgs ra,
-    RouteWs rw, uint16_t* __restrict__ hbuf, float* __restrict__ y, uint32_t* __restrict__ hand) {
+    size_t gu_bytes, size_t dn_tile_bytes, size_t dn_code_bytes, int ks, int full, int rem,
+    int nsw, int nb_i, int h_pad, int h_stride, RouteArgs ra, RouteWs rw,
+    uint8_t* __restrict__ hq, float* __restrict__ y, uint32_t* __restrict__ hand,
+    uint32_t* __restrict__ claim) {
   __shared__ RouteLds rt;
   __shared__ __align__(16) uint8_t pool[kFusedPool];
+  __shared__ int s_tile;
   const int nthr = blockDim.x;
   const int nw = nthr >> 6;
   const int lane = threadIdx.x & 63;
@@ -1006,10 +1046,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
         g += red[w * 64 + row];
         u += red[w * 64 + row + 32];
       }
-      const int r = rt.perm[rt.dist_off[d]];
-      __hip_atomic_store(&hbuf[(size_t)r * I + gtile * 32 + row],
-                         (uint16_t)f32_to_bf16_bits(silu_f32(g) * u), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      uint8_t* hr = hq + (size_t)rt.perm[rt.dist_off[d]] * h_stride;
+      store_h_block<true>(swiglu_bf16(g, u), hr + gtile * 32, h_pad, hr + 2 * h_pad + gtile);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's h stores have completed
     __syncthreads();                // ... and every thread's
@@ -1017,27 +1055,31 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
       __hip_atomic_fetch_add(&hand[(size_t)(d * kHandSub + gtile % kHandSub) * kHandStride], 1u,
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if ((int)blockIdx.x >= n_dnw) {
+  if (threadIdx.x == 0)
+    s_tile = (int)__hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int tile = s_tile;
+  if (tile >= n_dnw) {
     __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
     return;
   }
 
   // ---------------- down part ----------------
-  constexpr int RD = 64 / S;
-  const int tpw = nw / kDownWaves;   // tiles per workgroup
-  const int tl = wave / kDownWaves;  // this wave's tile
-  const int wt = wave % kDownWaves;  // this wave's place in its tile
-  const int tile = min((int)blockIdx.x * tpw + tl, dn_tiles - 1);  // past the end: a duplicate
-  const int r = lane / S;
-  const int sg = lane % S;
-  const int full = nb_i / S;
-  const int rem = nb_i - full * S;
-  const size_t code_bytes = ((size_t)full * 64 + (size_t)RD * rem) * 16;
-  const uint8_t* sec = slots + gu_bytes + (size_t)tile * dn_tile_bytes;
-  const int slot0 = nd == 0 ? 0 : rt.dist_slot[wt < nd ? wt : 0];  // no expert: any valid slot
-  uint4 c[TM];
-  uint32_t s4[TM / 4];
-  load_down_tile<S, TM>(sec + (size_t)slot0 * image_bytes, code_bytes, full, rem, T, tq, lane, c, s4);
+  const int KH = nw / kFusedSlots;               // K parts per expert
+  const int es = wave % kFusedSlots;             // this wave's hot expert slot
+  const int kh = wave / kFusedSlots;             // ... and K part
+  const int spw = ((ks + KH - 1) / KH + 3) & ~3;  // steps per K part, whole scale words (<= TMX)
+  const int s0 = kh * spw;
+  const uint8_t* tb = slots + (size_t)(nd == 0 ? 0 : rt.dist_slot[es < nd ? es : 0]) * image_bytes +
+                      gu_bytes + (size_t)tile * dn_tile_bytes;  // no expert: any valid slot
+  uint32_t sw[TMX / 4];
+  uint4 a[TMX];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < TMX / 4; ++q) sw[q] = dn_sw(tb, dn_code_bytes, s0 / 4 + q, nsw, lane);
+#pragma unroll
+  for (int j = 0; j < TMX; ++j) a[j] = dn_a(tb, s0 + j, ks, full, rem, lane);
+  __builtin_amdgcn_sched_barrier(0);
   // wait for every gate/up tile of every hot expert
   if (wave == 0) {
     bool late = false;
@@ -1062,21 +1104,20 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
     if (late && lane == 0) atomicOr(&rw.meta[2], kErrHandoff);
   }
   __syncthreads();  // also: every wave is done with the gate/up use of the pool
-  // h of every route into LDS through device-coherent loads; the quarters of block b are
-  // swizzled by (b >> 1) & 3 as down_route_dot reads them.  Clamped duplicates store the same
-  // value as their owner.  The wait inside also covers the down weights requested above.
-  uint8_t* hsm = pool;
-  const int n_h = Mk * nb_i * 4;
+  // every route's h into LDS through device-coherent loads, 16 bytes at a time, with the bytes
+  // that no gate/up unit writes replaced as the MFMA needs them: codes past I -> 0, scales of
+  // blocks past the last -> 127.  The wait inside also covers the down weights requested above.
+  uint8_t* hsm = pool;  // [Mk][h_stride]
+  const int cpr = h_stride / 16;  // chunks per route
+  const int n_h = Mk * cpr;
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   for (int base = 0; base < n_h; base += 4 * nthr) {
     int pidx[4];
-    const uint16_t* src[4];
+    const uint8_t* src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pidx[i] = min(base + i * nthr + (int)threadIdx.x, n_h - 1);
-      const int route = pidx[i] / (nb_i * 4);
-      const int rb = pidx[i] - route * nb_i * 4;
-      src[i] = hbuf + (size_t)route * I + (rb >> 2) * 32 + (rb & 3) * 8;
+      src[i] = hq + (size_t)pidx[i] * 16;
     }
     u32x4_t v0, v1, v2, v3;
     asm volatile(
@@ -1091,39 +1132,60 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
     const u32x4_t vv[4] = {v0, v1, v2, v3};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int route = pidx[i] / (nb_i * 4);
-      const int rb = pidx[i] - route * nb_i * 4;
-      const int b = rb >> 2;
-      const int q = (rb & 3) ^ ((b >> 1) & 3);
-      *reinterpret_cast<uint4*>(hsm + (((size_t)route * nb_i + b) * 4 + q) * 16) =
-          make_uint4(vv[i].x, vv[i].y, vv[i].z, vv[i].w);
+      const int co = (pidx[i] % cpr) * 16;  // byte offset in the route's h
+      uint4 v = make_uint4(vv[i].x, vv[i].y, vv[i].z, vv[i].w);
+      if ((co >= I && co < h_pad) || (co >= h_pad + I && co < 2 * h_pad)) v = make_uint4(0, 0, 0, 0);
+      if (co >= 2 * h_pad) {
+        const int s1 = (co - 2 * h_pad) / 4;  // the chunk holds the scale words of steps s1 .. s1+3
+        v.x = h_scale_word(v.x, s1, nb_i);
+        v.y = h_scale_word(v.y, s1 + 1, nb_i);
+        v.z = h_scale_word(v.z, s1 + 2, nb_i);
+        v.w = h_scale_word(v.w, s1 + 3, nb_i);
+      }
+      *reinterpret_cast<uint4*>(hsm + (size_t)pidx[i] * 16) = v;
     }
   }
-  float* parts = reinterpret_cast<float*>(pool + (size_t)n_h * 16);  // [tpw][Mk][RD]
+  uint8_t* zero = pool + (size_t)Mk * h_stride;                    // 32 zero bytes: B columns 2..15
+  float* parts = reinterpret_cast<float*>(zero + 32);             // [Mk][KH][16]
+  if (threadIdx.x < 2) *reinterpret_cast<uint4*>(zero + 16 * threadIdx.x) = make_uint4(0, 0, 0, 0);
   __syncthreads();
-  // one token: every hot expert has one route and nd <= kDownWaves, so wave wt of a tile owns
-  // expert wt (if hot), whose weights are already in registers
-  if (wt < nd) {
-    const int route = rt.perm[rt.dist_off[wt]];
-    float acc = down_route_dot<S, TM, true>(c, s4, T, nb_i, I, sg, hsm, hbuf, route);
-    acc = seg_sum<S>(acc);
-    if (sg == 0) parts[((size_t)tl * Mk + route) * RD + r] = acc;
+  if (es < nd) {
+    const int route = rt.perm[rt.dist_off[es]];
+    const int c = lane & 15, g = lane >> 4;
+    const uint8_t* hb = hsm + (size_t)route * h_stride;
+    const uint8_t* bs = c == 0 ? hb : hb + h_pad;  // column 0: hi, column 1: lo
+    f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < TMX; ++j) {
+      const int s = min(s0 + j, ks - 1);
+      const bool live = j < spw && s0 + j < ks;
+      const uint8_t* p0 = c < 2 ? bs + 128 * s + 16 * g : zero;
+      const uint8_t* p1 = c < 2 ? bs + 128 * s + 64 + 16 * g : zero + 16;
+      const uint4 b0 = *reinterpret_cast<const uint4*>(p0);
+      const uint4 b1 = *reinterpret_cast<const uint4*>(p1);
+      const uint32_t sb = hb[2 * h_pad + 4 * s + g];
+      const f32x4_t v = mfma_mx_j(j, a[j], b0, b1, acc, sw[j >> 2], sb);
+      acc = live ? v : acc;
+    }
+    // hi + lo: lane (g, 0) adds lane (g, 1)'s sums (DPP row_shl:1)
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = acc[i] + dpp_f<0x101>(acc[i]);
+    if (c == 0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) parts[((size_t)route * KH + kh) * 16 + 4 * g + i] = t[i];
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < tpw * ra.M * RD; idx += nthr) {
-    const int t2 = idx / (ra.M * RD);
-    const int rest = idx - t2 * ra.M * RD;
-    const int m = rest / RD;
-    const int rr = rest - m * RD;
-    const int tile2 = (int)blockIdx.x * tpw + t2;
-    if (tile2 >= dn_tiles) continue;
-    const float* p2 = parts + (size_t)t2 * Mk * RD;
+  if (threadIdx.x < kDnRows) {
+    const int row = threadIdx.x;
     float acc = 0.0f;
-    for (int j = 0; j < ra.k; ++j) {
-      const int route = m * ra.k + j;
-      if (rt.slot[route] >= 0) acc = fmaf(rt.w[route], p2[route * RD + rr], acc);
+    for (int j = 0; j < ra.k; ++j) {  // one token: route j = rank j
+      if (rt.slot[j] < 0) continue;
+      float p = 0.0f;
+      for (int h = 0; h < KH; ++h) p += parts[((size_t)j * KH + h) * 16 + row];
+      acc = fmaf(rt.w[j], p, acc);
     }
-    y[(size_t)m * H + tile2 * RD + rr] = acc;
+    y[(size_t)tile * kDnRows + row] = acc;
   }
 }
 
@@ -1220,8 +1282,8 @@ __device__ __forceinline__ void gu_load_chunk(const uint8_t* tb, int nb, int kc,
 // exchange.  The routes' activations are staged once per 4 image tiles.
 __global__ __launch_bounds__(256) void k_gateup_grouped(
     const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
-    size_t image_bytes, size_t gu_tile_bytes, int nb, int n_tiles, RouteArgs ra, RouteWs rw,
-    uint16_t* __restrict__ hbuf) {
+    size_t image_bytes, size_t gu_tile_bytes, int nb, int n_tiles, int h_pad, int h_stride,
+    RouteArgs ra, RouteWs rw, uint8_t* __restrict__ hq) {
   __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
   __shared__ GemmRows gr;
   const int Mk = ra.M * ra.k;
@@ -1281,143 +1343,31 @@ __global__ __launch_bounds__(256) void k_gateup_grouped(
       }
     }
   }
-  // lane (n, g), register i of row tile q: route t*16 + 4g + i, row 16q + n of the image tile
+  // lane (n, g), register i of row tile q: route t*16 + 4g + i, row 16q + n of the image tile;
+  // the 16 lanes of DPP row g hold that route's whole block of h (elements n and 16 + n)
   if (tile_ok) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t * 16 + g * 4 + i;
-        if (tok < nt) {
-          uint16_t* hr = hbuf + (size_t)gr.route[tok] * I + tile * 32 + n;
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-            hr[16 * q] = (uint16_t)f32_to_bf16_bits(silu_f32(acc[t][q][i]) * acc[t][q + 2][i]);
+        if (tok < nt) {  // the same for the whole row
+          const float h0 = swiglu_bf16(acc[t][0][i], acc[t][2][i]);
+          const float h1 = swiglu_bf16(acc[t][1][i], acc[t][3][i]);
+          const int sh = mx_shift(row_max_i(max(f32_exp(h0), f32_exp(h1))));
+          uint32_t hi0, lo0, hi1, lo1;
+          mx_pair(h0, sh, &hi0, &lo0);
+          mx_pair(h1, sh, &hi1, &lo1);
+          uint8_t* hr = hq + (size_t)gr.route[tok] * h_stride;
+          hr[tile * 32 + n] = (uint8_t)hi0;
+          hr[tile * 32 + 16 + n] = (uint8_t)hi1;
+          hr[h_pad + tile * 32 + n] = (uint8_t)lo0;
+          hr[h_pad + tile * 32 + 16 + n] = (uint8_t)lo1;
+          if (n == 0) hr[2 * h_pad + tile] = (uint8_t)(sh + 127);
         }
       }
   }
-}
-
-// grid = (ceil(H/256), work items), 256 threads.  d = Wd h for the item's routes; wave w owns rows
-// 256*blockIdx.x + 64w .. +64 (4 row tiles of 16), written to pdn[route][row] in fp32;
-// k_combine then forms y in the fixed route order.  B fragments come from the down layout (row
-// r of a down tile at step t holds block t*S + s in lane r*S + s).
-struct DnGeom {
-  int S, RD, full, rem, nb;
-  size_t code_bytes, dn_tile_bytes;
-};
-
-__device__ __forceinline__ void dn_fragment(const uint8_t* dsec, const DnGeom& G, int R, int b,
-                                            int g, uint32_t& code, uint32_t& scale_byte) {
-  b = min(b, G.nb - 1);
-  const int sg = b % G.S, t = b / G.S;
-  const int rr = R % G.RD;
-  const uint8_t* dtile = dsec + (size_t)(R / G.RD) * G.dn_tile_bytes;
-  const size_t idx = t < G.full ? (size_t)t * 64 + rr * G.S + sg : (size_t)G.full * 64 + rr * G.rem + sg;
-  code = *reinterpret_cast<const uint32_t*>(dtile + idx * 16 + g * 4);
-  const uint32_t word = *reinterpret_cast<const uint32_t*>(
-      dtile + G.code_bytes + ((size_t)(t >> 2) * 64 + rr * G.S + sg) * 4);
-  scale_byte = (word >> (8 * (t & 3))) & 0xFFu;
-}
-
-__global__ __launch_bounds__(256) void k_down_grouped(
-    int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
-    size_t dn_tile_bytes, int nb, int S, RouteArgs ra, RouteWs rw,
-    const uint16_t* __restrict__ hbuf, float* __restrict__ pdn) {
-  __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
-  __shared__ GemmRows gr;
-  const int Mk = ra.M * ra.k;
-  if ((int)blockIdx.y >= rw.meta[3]) return;
-  const int2 item = rw.items[blockIdx.y];
-  const int4 dd = rw.dist[item.x];
-  const int slot = dd.x, off = dd.y, cnt = dd.z;
-  if (cnt <= 0 || off < 0 || off + cnt > Mk || item.y < 0 || item.y >= cnt) return;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  DnGeom G;
-  G.S = S;
-  G.RD = 64 / S;
-  G.nb = nb;
-  G.full = nb / S;
-  G.rem = nb - G.full * S;
-  G.code_bytes = ((size_t)G.full * 64 + (size_t)G.RD * G.rem) * 16;
-  G.dn_tile_bytes = dn_tile_bytes;
-  const uint8_t* dsec = slots + (size_t)slot * image_bytes + gu_bytes;
-  const int row0 = 256 * (int)blockIdx.x + 64 * w;  // the wave's first row
-  int Rq[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) Rq[q] = min(row0 + 16 * q + n, H - 1);
-  const int nkc = (nb + kGemmKC - 1) / kGemmKC;
-  const int base = item.y;
-  const int nt = min(kGemmTok, cnt - base);
-  const int ntt = (nt + 15) >> 4;
-  for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) {
-    const int r = rw.perm[off + base + min(i, nt - 1)];
-    gr.route[i] = r;
-    gr.row[i] = hbuf + (size_t)r * I;
-  }
-  __syncthreads();
-  f32x4_t acc[4][4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[t][q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 xv[kGemmXPerThread];
-  uint32_t wc[4][kGemmKC], wsb[4][kGemmKC];
-  auto load_w = [&](int kc) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int j = 0; j < kGemmKC; ++j) dn_fragment(dsec, G, Rq[q], kc * kGemmKC + j, g, wc[q][j], wsb[q][j]);
-  };
-  gemm_load_rows(gr, 0, I, xv);
-  load_w(0);
-  for (int kc = 0; kc < nkc; ++kc) {
-    const int buf = kc & 1;
-    gemm_store_rows(xb[buf], xv);
-    uint32_t wcur[4][kGemmKC], scur[4][kGemmKC];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int j = 0; j < kGemmKC; ++j) {
-        wcur[q][j] = wc[q][j];
-        scur[q][j] = wsb[q][j];
-      }
-    if (kc + 1 < nkc) {
-      gemm_load_rows(gr, kc + 1, I, xv);
-      load_w(kc + 1);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kGemmKC; ++j) {
-      const int b = kc * kGemmKC + j;
-      bf16x8_t av[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        av[t] = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][j * 32 + g * 8]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x8_t bw = fp4x8_to_bf16(wcur[q][j], e8m0_to_f32(scur[q][j]));
-        if (b >= nb) bw = bf16x8_t{};
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (t < ntt) acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t], bw, acc[t][q], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = t * 16 + g * 4 + i;
-      if (tok < nt) {
-        float* pr = pdn + (size_t)gr.route[tok] * H;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (row0 + 16 * q + n < H) pr[row0 + 16 * q + n] = acc[t][q][i];
-      }
-    }
+  (void)I;
 }
 
 // ---- router GEMM for many tokens ---------------------------------------------------------------
@@ -1595,22 +1545,16 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
   }
   p.gu_waves = best < 1 ? 1 : best;
   p.gu_groups = (L.ng_h + p.gu_waves - 1) / p.gu_waves;
-  // down: h in LDS when every route's h fits, partial sums in LDS when they fit
-  const size_t h_lds = ((size_t)Mk * L.nb_i * 4 + 63) / 64 * 1024;  // whole 1 KiB runs
-  const size_t part = (size_t)Mk * L.dn_rows * 4;
-  p.h_in_lds = h_lds + part <= kDownLdsBudget;
-  p.part_in_lds = (p.h_in_lds ? h_lds : 0) + part <= kDownLdsBudget;
-  p.dn_lds = (p.h_in_lds ? h_lds : 0) + (p.part_in_lds ? part : 0);
   return p;
 }
 
 hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                          const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                         const RouteWs& rw, uint16_t* hbuf, hipStream_t s) {
+                         const RouteWs& rw, uint8_t* hq, hipStream_t s) {
   const dim3 g(L.gu_tiles, p.nd_max), b(p.gu_waves * 64);
 #define MOE_GU(SINGLE, G, PRO, XLDS)                                                               \
   hipLaunchKernelGGL((k_gateup<SINGLE, G, PRO, XLDS>), g, b, 0, s, x, H, I, slots, L.image_bytes, \
-                     L.gu_tile_bytes, L.nb_h, L.ng_h, ra, rw, hbuf)
+                     L.gu_tile_bytes, L.nb_h, L.ng_h, L.h_pad, L.h_stride, ra, rw, hq)
   // the single-token variant lets arithmetic overlap the loads but holds more registers, so
   // it is only used with at most 3 groups per wave; M == 1 always fits the LDS copy of x
   const bool single = M == 1 && p.gu_groups <= 3;
@@ -1646,55 +1590,43 @@ hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
-                       const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                       const uint16_t* hbuf, float* pdn, float* y, hipStream_t s) {
-  const dim3 g(L.dn_tiles), b(kDownWaves * 64);
-#define MOE_DN(SEG, TM, HL)                                                                       \
-  hipLaunchKernelGGL((k_down_combine<SEG, TM, HL>), g, b, p.dn_lds, s, H, I, slots,              \
-                     L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.nb_i, L.dn_steps,              \
-                     L.dn_scale_words, ra, rw, hbuf, p.part_in_lds ? 1 : 0, pdn, y)
-#define MOE_DN_T(SEG, HL)                            \
-  do {                                               \
-    if (L.dn_steps <= 4) MOE_DN(SEG, 4, HL);         \
-    else if (L.dn_steps <= 8) MOE_DN(SEG, 8, HL);    \
-    else if (L.dn_steps <= 12) MOE_DN(SEG, 12, HL);  \
-    else MOE_DN(SEG, 16, HL);                        \
-  } while (0)
-  switch (L.dn_seg * 2 + (p.h_in_lds ? 1 : 0)) {
-    case 2 * 8 + 1: MOE_DN_T(8, true); break;
-    case 2 * 8: MOE_DN_T(8, false); break;
-    case 2 * 4 + 1: MOE_DN_T(4, true); break;
-    case 2 * 4: MOE_DN_T(4, false); break;
-    case 2 * 2 + 1: MOE_DN_T(2, true); break;
-    case 2 * 2: MOE_DN_T(2, false); break;
-    case 2 * 1 + 1: MOE_DN_T(1, true); break;
-    default: MOE_DN_T(1, false); break;
-  }
-#undef MOE_DN_T
-#undef MOE_DN
-  return hipGetLastError();
-}
-
-hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,
-                                 const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                                 const RouteWs& rw, uint16_t* hbuf, hipStream_t s) {
-  hipLaunchKernelGGL(k_gateup_grouped, dim3((L.gu_tiles + 3) / 4, p.n_items_max), dim3(256), 0, s, x,
-                     H, I, slots, L.image_bytes, L.gu_tile_bytes, L.nb_h, L.gu_tiles, ra, rw, hbuf);
-  return hipGetLastError();
-}
-
-hipError_t launch_down_grouped(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
-                               const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                               const uint16_t* hbuf, float* pdn, float* y, hipStream_t s) {
-  hipLaunchKernelGGL(k_down_grouped, dim3((H + 255) / 256, p.n_items_max), dim3(256), 0, s, H, I, slots,
-                     L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.nb_i, L.dn_seg, ra, rw, hbuf, pdn);
+// Down for the work items (use_items) or the distinct hot experts, then the ordered combine.
+static hipError_t launch_down_mx(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
+                                 int n_items, bool use_items, const RouteArgs& ra,
+                                 const RouteWs& rw, const uint8_t* hq, float* pdn, float* y,
+                                 hipStream_t s) {
+  const int per_wg = 4 * kDnRW;
+  hipLaunchKernelGGL(k_down_mx, dim3((L.dn_tiles + per_wg - 1) / per_wg, n_items), dim3(256), 0, s,
+                     H, slots, L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.dn_code_bytes,
+                     L.dn_tiles, L.dn_ks, L.dn_full, L.dn_rem, L.dn_scale_words, I, L.nb_i, L.h_pad,
+                     (int)L.h_stride, ra, rw, use_items ? 1 : 0, hq, pdn);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int threads = M * (H / 4);
   hipLaunchKernelGGL(k_combine, dim3((threads + 255) / 256), dim3(256), 0, s, M, ra.k, H, ra, rw,
                      pdn, y);
   return hipGetLastError();
+}
+
+hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
+                       const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
+                       const uint8_t* hq, float* pdn, float* y, hipStream_t s) {
+  return launch_down_mx(M, H, I, slots, L, p.nd_max, false, ra, rw, hq, pdn, y, s);
+}
+
+hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,
+                                 const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
+                                 const RouteWs& rw, uint8_t* hq, hipStream_t s) {
+  hipLaunchKernelGGL(k_gateup_grouped, dim3((L.gu_tiles + 3) / 4, p.n_items_max), dim3(256), 0, s, x,
+                     H, I, slots, L.image_bytes, L.gu_tile_bytes, L.nb_h, L.gu_tiles, L.h_pad,
+                     (int)L.h_stride, ra, rw, hq);
+  return hipGetLastError();
+}
+
+hipError_t launch_down_grouped(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
+                               const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
+                               const uint8_t* hq, float* pdn, float* y, hipStream_t s) {
+  return launch_down_mx(M, H, I, slots, L, p.n_items_max, true, ra, rw, hq, pdn, y, s);
 }
 
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, size_t n,
@@ -1704,11 +1636,10 @@ hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, siz
   return hipGetLastError();
 }
 
-// Resident workgroups of k_layer_decode<G, S, TM> with nthr threads on the current device (its
+// Resident workgroups of k_layer_decode<G, TMX> with nthr threads on the current device (its
 // whole grid must be resident), from the kernel's occupancy; computed once per device and shape
-// of workgroup.
-// (0 without a device: the fused path is then never chosen.)
-template <int G, int S, int TM>
+// of workgroup.  (0 without a device: the fused path is then never chosen.)
+template <int G, int TMX>
 static int layer_decode_capacity(int nthr) {
   static std::atomic<int> cache[16][kMaxWaves + 1];  // [device][waves]; 0 = not computed
   int dev = 0;
@@ -1717,7 +1648,7 @@ static int layer_decode_capacity(int nthr) {
   int v = cache[dev][w].load(std::memory_order_relaxed);
   if (v == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_layer_decode<G, S, TM>, nthr, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_layer_decode<G, TMX>, nthr, 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
     v = per_cu * cus > 0 ? per_cu * cus : -1;
@@ -1726,64 +1657,76 @@ static int layer_decode_capacity(int nthr) {
   return v > 0 ? v : 0;
 }
 
-static bool layer_decode_shape(const ImageLayout& L, const ExpertPlan& p, int* G, int* TM) {
-  *G = p.gu_groups;
-  *TM = L.dn_steps <= 4 ? 4 : L.dn_steps <= 8 ? 8 : L.dn_steps <= 12 ? 12 : 16;
-  // the instantiated (G, S, TM) combinations
-  return (*G == 3 && L.dn_seg == 8 && *TM == 12) || (*G >= 1 && *G <= 3 && L.dn_seg == 4 && *TM == 4);
+// Steps per K part of the fused down part (whole scale words), and the template's bound.
+static int layer_decode_spw(const ImageLayout& L, const ExpertPlan& p) {
+  const int KH = p.gu_waves / kFusedSlots;
+  return ((L.dn_ks + KH - 1) / KH + 3) & ~3;
 }
+static int layer_decode_tmx(int spw) { return spw <= 4 ? 4 : spw <= 8 ? 8 : spw <= 12 ? 12 : 16; }
 
 static int layer_decode_grid(const ImageLayout& L, const ExpertPlan& p) {
-  const int tpw = p.gu_waves / kDownWaves;
   const int n_gu = L.gu_tiles * p.nd_max;
-  const int n_dnw = (L.dn_tiles + tpw - 1) / tpw;
-  return n_gu > n_dnw ? n_gu : n_dnw;
+  return n_gu > L.dn_tiles ? n_gu : L.dn_tiles;
 }
+
+#define MOE_LD_SWITCH(G, TMX, CALL)                                                                \
+  switch ((G) * 100 + (TMX)) {                                                                     \
+    case 104: CALL(1, 4); break;                                                                   \
+    case 108: CALL(1, 8); break;                                                                   \
+    case 112: CALL(1, 12); break;                                                                  \
+    case 116: CALL(1, 16); break;                                                                  \
+    case 204: CALL(2, 4); break;                                                                   \
+    case 208: CALL(2, 8); break;                                                                   \
+    case 212: CALL(2, 12); break;                                                                  \
+    case 216: CALL(2, 16); break;                                                                  \
+    case 304: CALL(3, 4); break;                                                                   \
+    case 308: CALL(3, 8); break;                                                                   \
+    case 312: CALL(3, 12); break;                                                                  \
+    case 316: CALL(3, 16); break;                                                                  \
+    default: break;                                                                                \
+  }
 
 bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M) {
   if (!(M == 1 && p.prologue && !p.grouped)) return false;
-  if (p.gu_waves % kDownWaves != 0) return false;
+  if (p.gu_groups < 1 || p.gu_groups > 3) return false;
+  if (p.gu_waves % kFusedSlots != 0) return false;
   const int k_routes = p.nd_max;  // M = 1: every route is its own expert
-  if (k_routes > kDownWaves) return false;  // a down wave per hot expert
-  const size_t need = (size_t)k_routes * L.nb_i * 64 + (size_t)(p.gu_waves / kDownWaves) * k_routes * L.dn_rows * 4;
+  if (k_routes > kFusedSlots) return false;  // a wave per hot expert in each K part
+  const int spw = layer_decode_spw(L, p);
+  if (spw > 16) return false;
+  const int KH = p.gu_waves / kFusedSlots;
+  const size_t need = (size_t)k_routes * L.h_stride + 32 + (size_t)k_routes * KH * kDnRows * 4;
   if (need > (size_t)kFusedPool || (size_t)L.H * 2 > (size_t)kXLdsBytes) return false;
   if ((size_t)kXLdsBytes + (size_t)p.gu_waves * 64 * 4 > (size_t)kFusedPool) return false;
-  int G, TM;
-  if (!layer_decode_shape(L, p, &G, &TM)) return false;
   const int nthr = p.gu_waves * 64;
   int cap = 0;
-  if (L.dn_seg == 8) cap = layer_decode_capacity<3, 8, 12>(nthr);
-  else if (G == 1) cap = layer_decode_capacity<1, 4, 4>(nthr);
-  else if (G == 2) cap = layer_decode_capacity<2, 4, 4>(nthr);
-  else cap = layer_decode_capacity<3, 4, 4>(nthr);
+#define MOE_LD_CAP(G, TMX) cap = layer_decode_capacity<G, TMX>(nthr)
+  MOE_LD_SWITCH(p.gu_groups, layer_decode_tmx(spw), MOE_LD_CAP)
+#undef MOE_LD_CAP
   return layer_decode_grid(L, p) <= cap;
 }
 
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                               const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
+                               const RouteWs& rw, uint8_t* hq, float* y, uint32_t* hand,
                                hipStream_t s) {
   (void)M;
-  const int tpw = p.gu_waves / kDownWaves;
   const int n_gu = L.gu_tiles * p.nd_max;
-  const int n_dnw = (L.dn_tiles + tpw - 1) / tpw;
   const dim3 g(layer_decode_grid(L, p)), b(p.gu_waves * 64);
-#define MOE_LD(G, SEG, TM)                                                                         \
-  hipLaunchKernelGGL((k_layer_decode<G, SEG, TM>), g, b, 0, s, x, H, I, slots, L.image_bytes,     \
-                     L.gu_tile_bytes, L.nb_h, L.ng_h, L.gu_tiles, n_gu, n_dnw, L.gu_bytes,         \
-                     L.dn_tile_bytes, L.nb_i, L.dn_steps, L.dn_scale_words, L.dn_tiles, ra, rw,    \
-                     hbuf, y, hand)
-  if (L.dn_seg == 8) {
-    MOE_LD(3, 8, 12);
-  } else if (p.gu_groups <= 1) {
-    MOE_LD(1, 4, 4);
-  } else if (p.gu_groups == 2) {
-    MOE_LD(2, 4, 4);
-  } else {
-    MOE_LD(3, 4, 4);
-  }
+  hipError_t e = hipErrorInvalidValue;
+#define MOE_LD(G, TMX)                                                                             \
+  do {                                                                                             \
+    hipLaunchKernelGGL((k_layer_decode<G, TMX>), g, b, 0, s, x, H, I, slots, L.image_bytes,        \
+                       L.gu_tile_bytes, L.nb_h, L.ng_h, L.gu_tiles, n_gu, L.dn_tiles, L.gu_bytes,   \
+                       L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks, L.dn_full, L.dn_rem,              \
+                       L.dn_scale_words, L.nb_i, L.h_pad, (int)L.h_stride, ra, rw, hq, y, hand,    \
+                       hand + (size_t)p.nd_max * kHandSub * kHandStride);                           \
+    e = hipGetLastError();                                                                         \
+  } while (0)
+  MOE_LD_SWITCH(p.gu_groups, layer_decode_tmx(layer_decode_spw(L, p)), MOE_LD)
 #undef MOE_LD
-  return hipGetLastError();
+  return e;
 }
+#undef MOE_LD_SWITCH
 
 }  // namespace moe

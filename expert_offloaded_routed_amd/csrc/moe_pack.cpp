@@ -46,25 +46,22 @@ static void tiles(uint8_t* img, int n_tiles, int rows_per_lane_group, int nb, in
   }
 }
 
-// Down tiles: lane l = r*S + s holds, at step t, block t*S + s of row r (see moe_internal.h).
+// Down tiles: 16 rows; at K step s lane l holds row l%16, block 4s + l/16 (see moe_internal.h).
 template <bool PACK>
 static void down_tiles(uint8_t* img, const ImageLayout& L, uint8_t* codes, uint8_t* scales) {
-  const int S = L.dn_seg, RD = L.dn_rows, nb = L.nb_i;
-  const int full = nb / S, rem = nb % S;
+  const int nb = L.nb_i;
   const size_t row_code_bytes = (size_t)L.I / 2;
   const size_t row_scale_bytes = (size_t)L.I / 32;
   for (int t = 0; t < L.dn_tiles; ++t) {
     uint8_t* tb = img + (size_t)t * L.dn_tile_bytes;
     for (int lane = 0; lane < 64; ++lane) {
-      const int r = lane / S, sg = lane % S;
-      const int row = t * RD + r;
+      const int row = t * kDnRows + lane % 16;
       uint8_t* c = codes + (size_t)row * row_code_bytes;
       uint8_t* sc = scales + (size_t)row * row_scale_bytes;
-      for (int st = 0; st < L.dn_steps; ++st) {
-        const int b = st * S + sg;
-        if (b >= nb) continue;
-        const size_t idx = st < full ? (size_t)st * 64 + lane : (size_t)full * 64 + (size_t)r * rem + sg;
-        uint8_t* dst = tb + idx * 16;
+      for (int st = 0; st < L.dn_ks; ++st) {
+        const int b = 4 * st + lane / 16;
+        if (b >= nb) continue;  // only in the partial step, whose stored lanes come first
+        uint8_t* dst = tb + ((size_t)st * 64 + lane) * 16;
         if (PACK)
           memcpy(dst, c + (size_t)b * 16, 16);
         else
@@ -73,12 +70,10 @@ static void down_tiles(uint8_t* img, const ImageLayout& L, uint8_t* codes, uint8
       for (int q = 0; q < L.dn_scale_words; ++q) {
         uint8_t* dst = tb + L.dn_code_bytes + ((size_t)q * 64 + lane) * 4;
         for (int i = 0; i < 4; ++i) {
-          const int st = 4 * q + i;
-          const int b = st * S + sg;
-          const bool ok = st < L.dn_steps && b < nb;
+          const int b = 4 * (4 * q + i) + lane / 16;
           if (PACK)
-            dst[i] = ok ? sc[b] : 127;
-          else if (ok)
+            dst[i] = b < nb ? sc[b] : 127;
+          else if (b < nb)
             sc[b] = dst[i];
         }
       }

@@ -32,6 +32,21 @@ def close_enough(got, ref, what=""):
     return rel
 
 
+PATH_REL_L2 = 1e-4   # two GPU paths of the same call (different matrix-core grouping)
+
+
+def paths_agree(a, b, what=""):
+    """Outputs of two GPU paths of one call: both deterministic, summed in different groupings
+    on the matrix cores, so equal to well within the oracle bar (rel-L2 PATH_REL_L2)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, what
+    nb = np.linalg.norm(b)
+    rel = np.linalg.norm(a - b) / nb if nb > 0 else np.linalg.norm(a)
+    assert rel <= PATH_REL_L2, f"{what}: paths differ by rel-L2 {rel:.3e}"
+    return rel
+
+
 def compare_routes(ids_gpu, w_gpu, logits_ref, k):
     """Top-k ids bit-exact except near-ties; weights within tolerance.  Returns #near-tie tokens."""
     ids_ref, w_ref, gap_k, inner = O.route(logits_ref, k)

@@ -192,9 +192,10 @@ def test_argument_checks_return_status_before_any_launch():
                                None, None, None) == B.MOE_ERR_INVALID_ARG
 
 
-def test_pack_down_layout_segments_and_partial_step():
-    """Down rows of a 2880-wide intermediate: 8 lanes (K segments) per row, 12 steps, the last
-    step partial (90 = 11*8 + 2 blocks).  Check where one block and one scale byte land."""
+def test_pack_down_layout_mfma_steps_and_partial_step():
+    """Down rows of a 2880-wide intermediate in 16-row tiles: 23 K steps of 4 blocks, lane l
+    holding row l%16, block 4s + l/16; the last step partial (90 = 22*4 + 2 blocks, only its
+    first 32 lanes stored).  Check where one block, one scale byte and the padding land."""
     _lib()
     H, I = 64, 2880
     shape = B.make_shape(H, I, 2, 1, 2)
@@ -208,19 +209,18 @@ def test_pack_down_layout_segments_and_partial_step():
     img = B.moe_pack_expert(shape, ex)
     gu_tile = 2 * 1024 + 1 * 256            # H=64: 2 blocks, 1 scale group per tile
     gu_bytes = gu_tile * (I // 32)
-    S, RD, nb, T = 8, 8, 90, 12
-    code_bytes = (11 * 64 + RD * 2) * 16
-    dn_tile = code_bytes + 3 * 256
-    assert img.size == -(-(gu_bytes + dn_tile * (H // RD)) // 256) * 256
-    # row 21 = tile 2, r = 5; block 43 = step 5, segment 3 (full step): lane 5*8+3
-    off = gu_bytes + 2 * dn_tile + (5 * 64 + 43) * 16
+    code_bytes = 22 * 1024 + 2 * 256        # 22 full steps, then 2 blocks x 16 rows
+    dn_tile = code_bytes + 6 * 256          # ceil(23 / 4) scale words per lane
+    assert img.size == -(-(gu_bytes + dn_tile * (H // 16)) // 256) * 256
+    # row 21 = tile 1, row 5 of it; block 43 = step 10, lane group 3: lane 53
+    t1 = gu_bytes + 1 * dn_tile
+    off = t1 + (10 * 64 + 53) * 16
     assert np.array_equal(img[off:off + 16], ex["down_codes"][21, 43 * 16:44 * 16])
-    # block 89 = step 11 (partial, 2 active segments), segment 1: index 11*64 + r*2 + 1
-    off = gu_bytes + 2 * dn_tile + (11 * 64 + 5 * 2 + 1) * 16
+    # block 89 = step 22 (partial), lane group 1: lane 21 of the stored part
+    off = t1 + (22 * 64 + 21) * 16
     assert np.array_equal(img[off:off + 16], ex["down_codes"][21, 89 * 16:90 * 16])
-    # scale of block 43 (step 5 -> word 1, byte 1) of lane 43
-    soff = gu_bytes + 2 * dn_tile + code_bytes + (1 * 64 + 43) * 4 + 1
-    assert img[soff] == ex["down_scales"][21, 43]
-    # step 11 of segment 5 does not exist: padding byte 127 (word 2, byte 3)
-    soff = gu_bytes + 2 * dn_tile + code_bytes + (2 * 64 + 5 * 8 + 5) * 4 + 3
-    assert img[soff] == 127
+    # scale of block 43 (step 10 -> word 2, byte 2) of lane 53
+    assert img[t1 + code_bytes + (2 * 64 + 53) * 4 + 2] == ex["down_scales"][21, 43]
+    # block 90 (step 22, lane group 2) and step 23 do not exist: padding 127
+    assert img[t1 + code_bytes + (5 * 64 + 37) * 4 + 2] == 127
+    assert img[t1 + code_bytes + (5 * 64 + 5) * 4 + 3] == 127
