@@ -182,7 +182,7 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
     e = p.grouped ? launch_gateup_grouped(x, sh->hidden, sh->inter, slots, L, p, ra, rw,
                                           at<uint8_t>(ws, W.hq), stream)
                   : launch_gateup(x, M, sh->hidden, sh->inter, slots, L, p, ra, rw,
-                                  at<uint8_t>(ws, W.hq), stream);
+                                  at<uint16_t>(ws, W.hq), stream);
     if (e != hipSuccess) return hip_fail(e, "gate/up launch");
   }
   if (marks && (e = record_mark(marks[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -191,7 +191,7 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
     e = p.grouped ? launch_down_grouped(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
                                         at<uint8_t>(ws, W.hq), at<float>(ws, W.pdn), y, stream)
                   : launch_down(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
-                                at<uint8_t>(ws, W.hq), at<float>(ws, W.pdn), y, stream);
+                                at<uint16_t>(ws, W.hq), at<float>(ws, W.pdn), y, stream);
     if (e != hipSuccess) return hip_fail(e, "down launch");
   }
   if (marks && (e = record_mark(marks[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -250,7 +250,7 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
     const RouteArgs ra = route_args(shape, M, logits, topk_ids, topk_w, expert_to_slot, topk_ids,
                                     topk_w, cold_count, cold_routes);
     e = launch_layer_decode(x, M, shape->hidden, shape->inter, slots, L, p, ra, route_ws(ws, W),
-                            at<uint8_t>(ws, W.hq), y, hand, stream);
+                            at<uint16_t>(ws, W.hq), y, hand, stream);
     if (e != hipSuccess) return hip_fail(e, "fused decode launch");
     for (int i = 2; marks && i < 4; ++i)
       if ((e = record_mark(marks[i], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");

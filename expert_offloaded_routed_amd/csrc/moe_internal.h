@@ -87,7 +87,8 @@ struct WsLayout {
   size_t dist;           // i32x4 [nd_max]: distinct hot experts {slot, bucket offset, count, id}
   size_t cold_list;      // i32 [M*k]
   size_t items;          // i32x2 [n_items_max]: grouped GEMM work list {distinct expert, first route}
-  size_t hq;             // split h of every route, ImageLayout::h_stride bytes each
+  size_t hq;             // h of every route: bf16 [I] (GEMV paths, M < 64) or, on the grouped
+                         // path, split for the block-scaled MFMA (ImageLayout::h_stride bytes)
   size_t pdn;            // f32 [M*k][H]: down partial sums when they do not fit in LDS
   size_t hand;           // u32 counters of the fused decode kernel, one per 64 bytes
   size_t total;
@@ -123,7 +124,7 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   W.dist = o;        o = align256(o + 16 * nd);
   W.cold_list = o;   o = align256(o + 4 * Mk);
   W.items = o;       o = align256(o + 8 * (size_t)n_items_max((int)Mk, E));
-  W.hq = o;          o = align256(o + Mk * L.h_stride);
+  W.hq = o;          o = align256(o + Mk * (L.h_stride > 2 * (size_t)I ? L.h_stride : 2 * (size_t)I));
   W.pdn = o;         o = align256(o + 4 * Mk * (size_t)H);
   W.hand = o;        o = align256(o + 64 * ((size_t)nd * kHandSub + 1));
   W.total = o;
@@ -180,7 +181,7 @@ hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const flo
 bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M);
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                               const RouteWs& rw, uint8_t* hq, float* y, uint32_t* hand,
+                               const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
                                hipStream_t s);
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,
@@ -188,10 +189,10 @@ hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_i
 ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k);
 hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                          const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                         const RouteWs& rw, uint8_t* hq, hipStream_t s);
+                         const RouteWs& rw, uint16_t* hbuf, hipStream_t s);
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                       const uint8_t* hq, float* pdn, float* y, hipStream_t s);
+                       const uint16_t* hbuf, float* pdn, float* y, hipStream_t s);
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, size_t n,
                            hipStream_t s);
 hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,

@@ -610,10 +610,10 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
 }
 
 // ---- h in the workspace -----------------------------------------------------------------------
-// Every route's h is kept split for the down projection's block-scaled MFMA (see mx_pair):
-// per route (h_stride bytes) hi[h_pad] and lo[h_pad] E4M3 codes, then one E8M0 scale byte per
-// 32-element block.  Elements past I, and scale bytes past the last block, are never written:
-// the down kernels substitute zeros and 127 for them.
+// The GEMV paths (M < 64) keep h in bf16, [route][I].  The grouped path keeps it split for the
+// down projection's block-scaled MFMA (see mx_pair): per route (h_stride bytes) hi[h_pad] and
+// lo[h_pad] E4M3 codes, then one E8M0 scale byte per 32-element block.  Elements past I, and
+// scale bytes past the last block, are never written: k_down_mx substitutes zeros and 127.
 
 // Lanes 32j .. 32j+31 hold (as fp32) the 32 bf16 values of one block of h, element lane & 31;
 // all 32 active.  hi points at the block's first hi code, h_pad separates hi and lo, sc is the
@@ -649,8 +649,8 @@ __device__ __forceinline__ float swiglu_bf16(float g, float u) {
 template <bool SINGLE, int G, bool PRO, bool XLDS>
 __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
     const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
-    size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, int h_pad, size_t h_stride,
-    RouteArgs ra, RouteWs rw, uint8_t* __restrict__ hq) {
+    size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, RouteArgs ra, RouteWs rw,
+    uint16_t* __restrict__ hbuf) {
   __shared__ float red[kMaxWaves][SINGLE ? 1 : kTokPerPass][64];
   __shared__ RouteLds rt;
   __shared__ __align__(16) uint16_t xs[XLDS ? kXLdsBytes / 2 : 8];
@@ -749,8 +749,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
         g += red[w][0][row];
         u += red[w][0][row + 32];
       }
-      uint8_t* hr = hq + (size_t)perm[off] * h_stride;
-      store_h_block<false>(swiglu_bf16(g, u), hr + tile * 32, h_pad, hr + 2 * h_pad + tile);
+      hbuf[(size_t)perm[off] * I + tile * 32 + row] = (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
     }
     return;
   }
@@ -765,7 +764,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
                                 : dot_tile_range<G>(c, s4, nb, g0, ngw, x + (size_t)tok * H);
     }
     __syncthreads();
-    // one route per half wave (nthr is a multiple of 64, so a half wave is all in or all out)
     for (int idx = threadIdx.x; idx < nt * 32; idx += nthr) {
       const int t = idx >> 5;
       const int row = idx & 31;
@@ -774,8 +772,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
         g += red[w][t][row];
         u += red[w][t][row + 32];
       }
-      uint8_t* hr = hq + (size_t)perm[off + base + t] * h_stride;
-      store_h_block<false>(swiglu_bf16(g, u), hr + tile * 32, h_pad, hr + 2 * h_pad + tile);
+      hbuf[(size_t)perm[off + base + t] * I + tile * 32 + row] =
+          (uint16_t)f32_to_bf16_bits(silu_f32(g) * u);
     }
     __syncthreads();
   }
@@ -824,6 +822,153 @@ __device__ __forceinline__ uint32_t h_scale_word(uint32_t w, int s, int nb_i) {
   return w;
 }
 
+// ---- down GEMV (VALU) ----------------------------------------------------------------------------
+// For one or a few tokens the down projection is a GEMV over the same tiles: lane l of a wave
+// holds, at each K step s, row l%16's block 4s + l/16 (16 code bytes) and takes its dot with
+// that block of h (bf16; the 16 lanes of a lane group read the same 64 bytes, an LDS broadcast),
+// decoded on the fly by the packed FP4 converter; the 4 lanes of a row (l, l^16, l^32, l^48)
+// meet at the end.  A wave holds TM steps of one expert's tile (a K part of it); the waves of a
+// workgroup split the hot experts and K.
+
+// This lane's TM steps from s0 (a multiple of 4), scale words first.
+template <int TM>
+__device__ __forceinline__ void dn_load_steps(const uint8_t* __restrict__ tb, size_t code_bytes,
+                                              int s0, int ks, int full, int rem, int nsw, int lane,
+                                              uint4 (&c)[TM], uint32_t (&sw)[TM / 4]) {
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < TM / 4; ++q) sw[q] = dn_sw(tb, code_bytes, s0 / 4 + q, nsw, lane);
+#pragma unroll
+  for (int j = 0; j < TM; ++j) c[j] = dn_a(tb, s0 + j, ks, full, rem, lane);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One route's partial sum for this lane over steps s0 .. s0+n-1 (n <= TM); hr = the route's h
+// (bf16 [I], in LDS or the workspace).  Software-pipelined by hand: the h block of step j+1 is
+// read before step j's arithmetic, its address passing through an empty asm together with the
+// sum so far, which keeps the compiler from issuing every read up front (16 VGPRs per step).
+// Steps past n or ks, and blocks past nb, read a valid block and add nothing (a select, not a
+// product, so whatever that block holds cannot leak in).
+template <int TM>
+__device__ __forceinline__ float dn_route_dot(const uint4 (&c)[TM], const uint32_t (&sw)[TM / 4],
+                                              int s0, int n, int ks, int nb, int g,
+                                              const uint16_t* hr) {
+  float acc = 0.0f;
+  int hoff = 0;
+  auto read_h = [&](int j, uint4 (&a)[4]) {
+    const uint4* hb = reinterpret_cast<const uint4*>(hr + hoff + 32 * min(4 * (s0 + j) + g, nb - 1));
+    a[0] = hb[0];
+    a[1] = hb[1];
+    a[2] = hb[2];
+    a[3] = hb[3];
+  };
+  uint4 an[4];
+  read_h(0, an);
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    uint4 ac[4] = {an[0], an[1], an[2], an[3]};
+    if (j + 1 < TM) {
+      asm volatile("" : "+v"(acc), "+v"(hoff));
+      read_h(j + 1, an);
+    }
+    const bool live = j < n && s0 + j < ks && 4 * (s0 + j) + g < nb;
+    const float sc = e8m0_to_f32((sw[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+    const float v = fmaf(sc, block_dot(c[j], ac[0], ac[1], ac[2], ac[3]), acc);
+    acc = live ? v : acc;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
+// Sum over the 4 lanes of a row (l, l^16, l^32, l^48); every one of them gets it.
+__device__ __forceinline__ float dn_row_sum(float v) {
+  v += swz_xor16_f(v);
+  return v + __shfl_xor(v, 32);
+}
+
+// Steps of a K part: K split over kparts, rounded up to whole scale words.
+__host__ __device__ __forceinline__ int dn_part_steps(int ks, int kparts) {
+  return ((ks + kparts - 1) / kparts + 3) & ~3;
+}
+
+// grid = H/16 tiles, 8 waves.  The waves own (expert slot, K part) pairs: with kparts K parts,
+// 8/kparts hot experts per pass, wave w taking experts w % (8/kparts) + (8/kparts)*i and K
+// part w / (8/kparts).  Each route's partial rows go to LDS; the workgroup then forms
+// y[m][rows] = sum over j ascending (hot routes) of w[m,j] * (its K parts, in order): no other
+// workgroup is involved.  h comes from an LDS copy when every route's h fits (h_lds), else
+// straight from the workspace.  The route table comes from the workspace.
+template <int TM>
+__global__ __launch_bounds__(512) void k_down_gemv(
+    int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
+    size_t dn_tile_bytes, size_t dn_code_bytes, int ks, int full, int rem, int nsw, int nb,
+    int kparts, int h_lds, RouteArgs ra, RouteWs rw, const uint16_t* __restrict__ hbuf,
+    float* __restrict__ y) {
+  extern __shared__ __align__(16) uint8_t smem[];  // [h copy (h_lds)] [parts: Mk x kparts x 16]
+  const int tile = blockIdx.x;
+  const int Mk = ra.M * ra.k;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;
+  const int sl = 8 / kparts;
+  const int es0 = wave % sl, kh = wave / sl;
+  const int spw = dn_part_steps(ks, kparts);
+  const int s0 = kh * spw;
+  const uint8_t* sec = slots + gu_bytes + (size_t)tile * dn_tile_bytes;
+  const int nd_max = Mk < ra.E ? Mk : ra.E;
+  const int nd = rw.meta[0];
+  const int sw0 = rw.dist[es0 < nd_max ? es0 : nd_max - 1].x;
+  const int sd0 = rw.dist[0].x;
+  const int slot0 = nd == 0 ? 0 : (es0 < nd ? sw0 : sd0);  // no expert: any valid slot
+  const int n_h = h_lds ? Mk * I / 8 : 0;  // 16-byte chunks of h
+  if (h_lds) {
+    // h straight from the workspace to LDS, one 1 KiB run per wave instruction (runs past n_h
+    // re-read the last chunk into padding)
+    typedef __attribute__((address_space(3))) void lds_void;
+    const int runs = (n_h + 63) / 64;
+    for (int run = wave; run < runs; run += 8) {
+      const int p = min(run * 64 + lane, n_h - 1);
+      __builtin_amdgcn_global_load_lds(hbuf + (size_t)p * 8, (lds_void*)(smem + (size_t)run * 1024), 16, 0, 0);
+    }
+  }
+  uint4 c[TM];
+  uint32_t sw[TM / 4];
+  dn_load_steps<TM>(sec + (size_t)slot0 * image_bytes, dn_code_bytes, s0, ks, full, rem, nsw, lane, c, sw);
+  const uint16_t* hsrc = h_lds ? reinterpret_cast<const uint16_t*>(smem) : hbuf;
+  float* parts = reinterpret_cast<float*>(smem + (h_lds ? (size_t)(n_h + 63) / 64 * 1024 : 0));
+  __syncthreads();
+  for (int d = es0; d < nd; d += sl) {
+    const int4 dd = rw.dist[d];
+    if (d != es0)
+      dn_load_steps<TM>(sec + (size_t)dd.x * image_bytes, dn_code_bytes, s0, ks, full, rem, nsw, lane, c, sw);
+    const int off = dd.y, cnt = dd.z;
+    if (cnt <= 0 || off < 0 || off + cnt > Mk) continue;
+#pragma unroll 1
+    for (int j = 0; j < cnt; ++j) {
+      // keeps the decode of the codes inside this loop (hoisted, it would hold 16 VGPRs per step)
+#pragma unroll
+      for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(c[t].x), "+v"(c[t].y), "+v"(c[t].z), "+v"(c[t].w));
+      const int route = rw.perm[off + j];
+      float acc = dn_route_dot<TM>(c, sw, s0, spw, ks, nb, g, hsrc + (size_t)route * I);
+      acc = dn_row_sum(acc);
+      if (lane < kDnRows) parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ra.M * kDnRows; idx += blockDim.x) {
+    const int m = idx / kDnRows;
+    const int r = idx - m * kDnRows;
+    float acc = 0.0f;
+    for (int j = 0; j < ra.k; ++j) {
+      const int route = m * ra.k + j;
+      if (rw.route_slot[route] < 0) continue;
+      float p = 0.0f;
+      for (int h = 0; h < kparts; ++h) p += parts[((size_t)route * kparts + h) * kDnRows + r];
+      acc = fmaf(ra.w_in[route], p, acc);
+    }
+    y[(size_t)m * H + tile * kDnRows + r] = acc;
+  }
+}
+
 // ---- down + partial sums for the combine --------------------------------------------------------
 // grid = (ceil(H/16 / (4*kDnRW)), work items), 256 threads.  An item is one distinct hot expert
 // and up to kItemRoutes of its routes (the bucketing work list), or, without a work list, one
@@ -833,6 +978,7 @@ __device__ __forceinline__ uint32_t h_scale_word(uint32_t w, int s, int nb_i) {
 // weights and h requested before the current stage's MFMAs.  Each route's rows go to
 // pdn[route][row] in fp32; k_combine forms y in the fixed route order.
 constexpr int kDnRW = 2;                                // down tiles per wave
+constexpr size_t kDownLdsBytes = 60 * 1024;             // dynamic LDS of k_down_gemv
 constexpr int kDnSub = 16;                              // routes per pass
 constexpr int kDnRoutePitch = 4 * 256 + 16;             // 4 steps of hi|lo (+16: bank spread)
 
@@ -995,9 +1141,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
     const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
     size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, int gu_tiles, int n_gu, int n_dnw,
     size_t gu_bytes, size_t dn_tile_bytes, size_t dn_code_bytes, int ks, int full, int rem,
-    int nsw, int nb_i, int h_pad, int h_stride, RouteArgs ra, RouteWs rw,
-    uint8_t* __restrict__ hq, float* __restrict__ y, uint32_t* __restrict__ hand,
-    uint32_t* __restrict__ claim) {
+    int nsw, int nb_i, RouteArgs ra, RouteWs rw, uint16_t* __restrict__ hbuf,
+    float* __restrict__ y, uint32_t* __restrict__ hand, uint32_t* __restrict__ claim) {
   __shared__ RouteLds rt;
   __shared__ __align__(16) uint8_t pool[kFusedPool];
   __shared__ int s_tile;
@@ -1046,8 +1191,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
         g += red[w * 64 + row];
         u += red[w * 64 + row + 32];
       }
-      uint8_t* hr = hq + (size_t)rt.perm[rt.dist_off[d]] * h_stride;
-      store_h_block<true>(swiglu_bf16(g, u), hr + gtile * 32, h_pad, hr + 2 * h_pad + gtile);
+      __hip_atomic_store(&hbuf[(size_t)rt.perm[rt.dist_off[d]] * I + gtile * 32 + row],
+                         (uint16_t)f32_to_bf16_bits(silu_f32(g) * u), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's h stores have completed
     __syncthreads();                // ... and every thread's
@@ -1065,21 +1211,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
   }
 
   // ---------------- down part ----------------
-  const int KH = nw / kFusedSlots;               // K parts per expert
-  const int es = wave % kFusedSlots;             // this wave's hot expert slot
-  const int kh = wave / kFusedSlots;             // ... and K part
-  const int spw = ((ks + KH - 1) / KH + 3) & ~3;  // steps per K part, whole scale words (<= TMX)
+  const int KH = nw / kFusedSlots;              // K parts per expert
+  const int es = wave % kFusedSlots;            // this wave's hot expert slot
+  const int kh = wave / kFusedSlots;            // ... and K part
+  const int spw = dn_part_steps(ks, KH);        // <= TMX
   const int s0 = kh * spw;
   const uint8_t* tb = slots + (size_t)(nd == 0 ? 0 : rt.dist_slot[es < nd ? es : 0]) * image_bytes +
                       gu_bytes + (size_t)tile * dn_tile_bytes;  // no expert: any valid slot
+  uint4 c[TMX];
   uint32_t sw[TMX / 4];
-  uint4 a[TMX];
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int q = 0; q < TMX / 4; ++q) sw[q] = dn_sw(tb, dn_code_bytes, s0 / 4 + q, nsw, lane);
-#pragma unroll
-  for (int j = 0; j < TMX; ++j) a[j] = dn_a(tb, s0 + j, ks, full, rem, lane);
-  __builtin_amdgcn_sched_barrier(0);
+  dn_load_steps<TMX>(tb, dn_code_bytes, s0, ks, full, rem, nsw, lane, c, sw);
   // wait for every gate/up tile of every hot expert
   if (wave == 0) {
     bool late = false;
@@ -1104,20 +1245,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
     if (late && lane == 0) atomicOr(&rw.meta[2], kErrHandoff);
   }
   __syncthreads();  // also: every wave is done with the gate/up use of the pool
-  // every route's h into LDS through device-coherent loads, 16 bytes at a time, with the bytes
-  // that no gate/up unit writes replaced as the MFMA needs them: codes past I -> 0, scales of
-  // blocks past the last -> 127.  The wait inside also covers the down weights requested above.
-  uint8_t* hsm = pool;  // [Mk][h_stride]
-  const int cpr = h_stride / 16;  // chunks per route
-  const int n_h = Mk * cpr;
+  // every route's h into LDS through device-coherent loads, 16 bytes at a time (the wait
+  // inside also covers the down weights requested above)
+  uint16_t* hsm = reinterpret_cast<uint16_t*>(pool);  // [Mk][I]
+  const int n_h = Mk * I / 8;
   typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
   for (int base = 0; base < n_h; base += 4 * nthr) {
     int pidx[4];
-    const uint8_t* src[4];
+    const uint16_t* src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       pidx[i] = min(base + i * nthr + (int)threadIdx.x, n_h - 1);
-      src[i] = hq + (size_t)pidx[i] * 16;
+      src[i] = hbuf + (size_t)pidx[i] * 8;
     }
     u32x4_t v0, v1, v2, v3;
     asm volatile(
@@ -1131,49 +1270,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
         : "memory");
     const u32x4_t vv[4] = {v0, v1, v2, v3};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int co = (pidx[i] % cpr) * 16;  // byte offset in the route's h
-      uint4 v = make_uint4(vv[i].x, vv[i].y, vv[i].z, vv[i].w);
-      if ((co >= I && co < h_pad) || (co >= h_pad + I && co < 2 * h_pad)) v = make_uint4(0, 0, 0, 0);
-      if (co >= 2 * h_pad) {
-        const int s1 = (co - 2 * h_pad) / 4;  // the chunk holds the scale words of steps s1 .. s1+3
-        v.x = h_scale_word(v.x, s1, nb_i);
-        v.y = h_scale_word(v.y, s1 + 1, nb_i);
-        v.z = h_scale_word(v.z, s1 + 2, nb_i);
-        v.w = h_scale_word(v.w, s1 + 3, nb_i);
-      }
-      *reinterpret_cast<uint4*>(hsm + (size_t)pidx[i] * 16) = v;
-    }
+    for (int i = 0; i < 4; ++i)
+      reinterpret_cast<uint4*>(hsm)[pidx[i]] = make_uint4(vv[i].x, vv[i].y, vv[i].z, vv[i].w);
   }
-  uint8_t* zero = pool + (size_t)Mk * h_stride;                    // 32 zero bytes: B columns 2..15
-  float* parts = reinterpret_cast<float*>(zero + 32);             // [Mk][KH][16]
-  if (threadIdx.x < 2) *reinterpret_cast<uint4*>(zero + 16 * threadIdx.x) = make_uint4(0, 0, 0, 0);
+  float* parts = reinterpret_cast<float*>(pool + (size_t)Mk * I * 2);  // [Mk][KH][16]
   __syncthreads();
   if (es < nd) {
+    // one token: every hot expert has one route
     const int route = rt.perm[rt.dist_off[es]];
-    const int c = lane & 15, g = lane >> 4;
-    const uint8_t* hb = hsm + (size_t)route * h_stride;
-    const uint8_t* bs = c == 0 ? hb : hb + h_pad;  // column 0: hi, column 1: lo
-    f32x4_t acc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < TMX; ++j) {
-      const int s = min(s0 + j, ks - 1);
-      const bool live = j < spw && s0 + j < ks;
-      const uint8_t* p0 = c < 2 ? bs + 128 * s + 16 * g : zero;
-      const uint8_t* p1 = c < 2 ? bs + 128 * s + 64 + 16 * g : zero + 16;
-      const uint4 b0 = *reinterpret_cast<const uint4*>(p0);
-      const uint4 b1 = *reinterpret_cast<const uint4*>(p1);
-      const uint32_t sb = hb[2 * h_pad + 4 * s + g];
-      const f32x4_t v = mfma_mx_j(j, a[j], b0, b1, acc, sw[j >> 2], sb);
-      acc = live ? v : acc;
-    }
-    // hi + lo: lane (g, 0) adds lane (g, 1)'s sums (DPP row_shl:1)
-    float t[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) t[i] = acc[i] + dpp_f<0x101>(acc[i]);
-    if (c == 0)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) parts[((size_t)route * KH + kh) * 16 + 4 * g + i] = t[i];
+    float acc = dn_route_dot<TMX>(c, sw, s0, spw, ks, nb_i, lane >> 4, hsm + (size_t)route * I);
+    acc = dn_row_sum(acc);
+    if (lane < kDnRows) parts[((size_t)route * KH + kh) * kDnRows + lane] = acc;
   }
   __syncthreads();
   if (threadIdx.x < kDnRows) {
@@ -1182,7 +1289,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
     for (int j = 0; j < ra.k; ++j) {  // one token: route j = rank j
       if (rt.slot[j] < 0) continue;
       float p = 0.0f;
-      for (int h = 0; h < KH; ++h) p += parts[((size_t)j * KH + h) * 16 + row];
+      for (int h = 0; h < KH; ++h) p += parts[((size_t)j * KH + h) * kDnRows + row];
       acc = fmaf(rt.w[j], p, acc);
     }
     y[(size_t)tile * kDnRows + row] = acc;
@@ -1550,11 +1657,11 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
 
 hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                          const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                         const RouteWs& rw, uint8_t* hq, hipStream_t s) {
+                         const RouteWs& rw, uint16_t* hbuf, hipStream_t s) {
   const dim3 g(L.gu_tiles, p.nd_max), b(p.gu_waves * 64);
 #define MOE_GU(SINGLE, G, PRO, XLDS)                                                               \
   hipLaunchKernelGGL((k_gateup<SINGLE, G, PRO, XLDS>), g, b, 0, s, x, H, I, slots, L.image_bytes, \
-                     L.gu_tile_bytes, L.nb_h, L.ng_h, L.h_pad, L.h_stride, ra, rw, hq)
+                     L.gu_tile_bytes, L.nb_h, L.ng_h, ra, rw, hbuf)
   // the single-token variant lets arithmetic overlap the loads but holds more registers, so
   // it is only used with at most 3 groups per wave; M == 1 always fits the LDS copy of x
   const bool single = M == 1 && p.gu_groups <= 3;
@@ -1610,8 +1717,30 @@ static hipError_t launch_down_mx(int M, int H, int I, const uint8_t* slots, cons
 
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                       const uint8_t* hq, float* pdn, float* y, hipStream_t s) {
-  return launch_down_mx(M, H, I, slots, L, p.nd_max, false, ra, rw, hq, pdn, y, s);
+                       const uint16_t* hbuf, float* pdn, float* y, hipStream_t s) {
+  (void)p;
+  (void)pdn;
+  const int Mk = M * ra.k;
+  // long K in two parts (4 experts per pass, half the steps per wave), short K in one (8
+  // experts per pass); a wave holds at most 16 steps
+  const int kparts = L.dn_ks > 8 ? 2 : 1;
+  const int spw = dn_part_steps(L.dn_ks, kparts);
+  const size_t parts = (size_t)Mk * kparts * kDnRows * 4;
+  const size_t hcopy = ((size_t)Mk * I / 8 + 63) / 64 * 1024;
+  const bool h_lds = hcopy + parts <= kDownLdsBytes;
+  const size_t lds = (h_lds ? hcopy : 0) + parts;
+  if (lds > kDownLdsBytes || spw > 16) return hipErrorInvalidValue;
+#define MOE_DG(TM)                                                                                 \
+  hipLaunchKernelGGL((k_down_gemv<TM>), dim3(L.dn_tiles), dim3(512), lds, s, H, I, slots,           \
+                     L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks,          \
+                     L.dn_full, L.dn_rem, L.dn_scale_words, L.nb_i, kparts, h_lds ? 1 : 0, ra, rw,  \
+                     hbuf, y)
+  if (spw <= 4) MOE_DG(4);
+  else if (spw <= 8) MOE_DG(8);
+  else if (spw <= 12) MOE_DG(12);
+  else MOE_DG(16);
+#undef MOE_DG
+  return hipGetLastError();
 }
 
 hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,
@@ -1659,8 +1788,7 @@ static int layer_decode_capacity(int nthr) {
 
 // Steps per K part of the fused down part (whole scale words), and the template's bound.
 static int layer_decode_spw(const ImageLayout& L, const ExpertPlan& p) {
-  const int KH = p.gu_waves / kFusedSlots;
-  return ((L.dn_ks + KH - 1) / KH + 3) & ~3;
+  return dn_part_steps(L.dn_ks, p.gu_waves / kFusedSlots);
 }
 static int layer_decode_tmx(int spw) { return spw <= 4 ? 4 : spw <= 8 ? 8 : spw <= 12 ? 12 : 16; }
 
@@ -1695,7 +1823,7 @@ bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M) {
   const int spw = layer_decode_spw(L, p);
   if (spw > 16) return false;
   const int KH = p.gu_waves / kFusedSlots;
-  const size_t need = (size_t)k_routes * L.h_stride + 32 + (size_t)k_routes * KH * kDnRows * 4;
+  const size_t need = (size_t)k_routes * L.I * 2 + (size_t)k_routes * KH * kDnRows * 4;
   if (need > (size_t)kFusedPool || (size_t)L.H * 2 > (size_t)kXLdsBytes) return false;
   if ((size_t)kXLdsBytes + (size_t)p.gu_waves * 64 * 4 > (size_t)kFusedPool) return false;
   const int nthr = p.gu_waves * 64;
@@ -1708,7 +1836,7 @@ bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M) {
 
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                               const RouteWs& rw, uint8_t* hq, float* y, uint32_t* hand,
+                               const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
                                hipStream_t s) {
   (void)M;
   const int n_gu = L.gu_tiles * p.nd_max;
@@ -1719,7 +1847,7 @@ hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uin
     hipLaunchKernelGGL((k_layer_decode<G, TMX>), g, b, 0, s, x, H, I, slots, L.image_bytes,        \
                        L.gu_tile_bytes, L.nb_h, L.ng_h, L.gu_tiles, n_gu, L.dn_tiles, L.gu_bytes,   \
                        L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks, L.dn_full, L.dn_rem,              \
-                       L.dn_scale_words, L.nb_i, L.h_pad, (int)L.h_stride, ra, rw, hq, y, hand,    \
+                       L.dn_scale_words, L.nb_i, ra, rw, hbuf, y, hand,                            \
                        hand + (size_t)p.nd_max * kHandSub * kHandStride);                           \
     e = hipGetLastError();                                                                         \
   } while (0)
