@@ -468,11 +468,11 @@ def bench_stack48(args):
     def token_step(t, rec=None):
         xa.copy_(x0[t])
         for l in range(NL):
-            B.moe_layer_forward(shape, xa, M, wrs[l], biases[l], maps[l], slot_arrays[l],
-                                ids_d if rec is None else ids_all[rec, l].view(M, k), w_d, y,
-                                cold_d if rec is None else cold_all[rec, l:l + 1], cold_routes, ws,
-                                stream=stream)
-            B.moe_residual_bf16(xa, y, xa, M * H, stream=stream)
+            # the layer's kernels also form the next layer's input, bf16(x + y), in place
+            B.moe_layer_forward_residual(shape, xa, M, wrs[l], biases[l], maps[l], slot_arrays[l],
+                                         ids_d if rec is None else ids_all[rec, l].view(M, k), w_d,
+                                         y, cold_d if rec is None else cold_all[rec, l:l + 1],
+                                         cold_routes, xa, ws, stream=stream)
 
     with torch.cuda.stream(stream):
         for t in range(args.warmup):

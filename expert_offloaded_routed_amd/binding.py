@@ -68,6 +68,8 @@ _SIGS = {
                           _P, _SZ, _P],
     "moe_layer_forward_marked": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, _P, _SZ, _P, _P],
+    "moe_layer_forward_residual": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _P, _P, _P, _SZ, _P],
     "moe_layer_launches": [C.POINTER(moe_shape), _I32, C.POINTER(_I32)],
     "moe_experts_gateup": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_experts_down": [C.POINTER(moe_shape), _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -225,6 +227,17 @@ def moe_layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots,
                                     _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(cold_count),
                                     _ptr(cold_routes), _ptr(ws), _nbytes(ws), _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_residual(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids,
+                               topk_w, y, cold_count, cold_routes, x_next, ws, stream=None):
+    """moe_layer_forward that also writes x_next = bf16(x + y) (x_next may be x)."""
+    _check(load().moe_layer_forward_residual(C.byref(shape), _ptr(x), int(M), _ptr(w_router),
+                                             _ptr(router_bias), _ptr(expert_to_slot), _ptr(slots),
+                                             _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(cold_count),
+                                             _ptr(cold_routes), _ptr(x_next), _ptr(ws), _nbytes(ws),
+                                             _stream(stream)),
+           "moe_layer_forward_residual")
 
 
 def moe_layer_forward_marked(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids,

@@ -160,7 +160,8 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
                               const float* logits, int32_t* ids, float* w, const int32_t* e2s,
                               const uint8_t* slots, float* y, int32_t* cold_count,
                               int32_t* cold_routes, void* ws, const WsLayout& W, bool do_gateup,
-                              bool do_down, hipStream_t stream, const hipEvent_t* marks = nullptr) {
+                              bool do_down, hipStream_t stream, const hipEvent_t* marks = nullptr,
+                              uint16_t* x_next = nullptr) {
   const ImageLayout L = image_layout(sh->hidden, sh->inter);
   const ExpertPlan p = plan_experts(L, M, sh->n_experts, sh->top_k);
   const RouteWs rw = route_ws(ws, W);
@@ -188,10 +189,11 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
   if (marks && (e = record_mark(marks[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (do_down) {
     const RouteArgs ra = route_args(sh, M, nullptr, ids, w, e2s, nullptr, nullptr, nullptr, nullptr);
+    const Residual res{x, x_next};
     e = p.grouped ? launch_down_grouped(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
-                                        at<uint8_t>(ws, W.hq), at<float>(ws, W.pdn), y, stream)
+                                        at<uint8_t>(ws, W.hq), at<float>(ws, W.pdn), y, res, stream)
                   : launch_down(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
-                                at<uint16_t>(ws, W.hq), at<float>(ws, W.pdn), y, stream);
+                                at<uint16_t>(ws, W.hq), at<float>(ws, W.pdn), y, res, stream);
     if (e != hipSuccess) return hip_fail(e, "down launch");
   }
   if (marks && (e = record_mark(marks[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -214,7 +216,7 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
                                 const int32_t* expert_to_slot, const uint8_t* slots,
                                 int32_t* topk_ids, float* topk_w, float* y, int32_t* cold_count,
                              int32_t* cold_routes, void* ws, size_t ws_bytes, hipStream_t stream,
-                                const hipEvent_t* marks) {
+                                const hipEvent_t* marks, uint16_t* x_next) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   WsLayout W;
@@ -233,6 +235,8 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
                 "moe_layer_forward: w_router, topk_ids, topk_w and y are required");
   if (reinterpret_cast<uintptr_t>(w_router) & 15)
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward: w_router must be 16-byte aligned");
+  if (x_next && (reinterpret_cast<uintptr_t>(x_next) & 1))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_residual: x_next must be 2-byte aligned");
   float* logits = at<float>(ws, W.logits);
   hipError_t e;
   // One token with a fusable shape: gate/up and down run as one launch (the router clears its
@@ -250,7 +254,7 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
     const RouteArgs ra = route_args(shape, M, logits, topk_ids, topk_w, expert_to_slot, topk_ids,
                                     topk_w, cold_count, cold_routes);
     e = launch_layer_decode(x, M, shape->hidden, shape->inter, slots, L, p, ra, route_ws(ws, W),
-                            at<uint16_t>(ws, W.hq), y, hand, stream);
+                            at<uint16_t>(ws, W.hq), y, hand, Residual{x, x_next}, stream);
     if (e != hipSuccess) return hip_fail(e, "fused decode launch");
     for (int i = 2; marks && i < 4; ++i)
       if ((e = record_mark(marks[i], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -258,7 +262,7 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
   }
   const RouteSrc src = RouteSrc::kLogits;
   st = run_experts(shape, x, M, src, logits, topk_ids, topk_w, expert_to_slot, slots, y,
-                   cold_count, cold_routes, ws, W, true, true, stream, marks);
+                   cold_count, cold_routes, ws, W, true, true, stream, marks, x_next);
   return st != MOE_OK ? st : ok();
 }
 
@@ -384,7 +388,18 @@ moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t 
                              int32_t* topk_ids, float* topk_w, float* y, int32_t* cold_count,
                              int32_t* cold_routes, void* ws, size_t ws_bytes, hipStream_t stream) {
   return layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids, topk_w,
-                       y, cold_count, cold_routes, ws, ws_bytes, stream, nullptr);
+                       y, cold_count, cold_routes, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+moe_status moe_layer_forward_residual(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                      const uint16_t* w_router, const float* router_bias,
+                                      const int32_t* expert_to_slot, const uint8_t* slots,
+                                      int32_t* topk_ids, float* topk_w, float* y,
+                                      int32_t* cold_count, int32_t* cold_routes, uint16_t* x_next,
+                                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!x_next) return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_residual: x_next is NULL");
+  return layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids, topk_w,
+                       y, cold_count, cold_routes, ws, ws_bytes, stream, nullptr, x_next);
 }
 
 moe_status moe_layer_forward_marked(const moe_shape* shape, const uint16_t* x, int32_t M,
@@ -397,7 +412,7 @@ moe_status moe_layer_forward_marked(const moe_shape* shape, const uint16_t* x, i
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_marked: four events are required");
   if (M <= 0) return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_marked: M must be positive");
   return layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids, topk_w,
-                       y, cold_count, cold_routes, ws, ws_bytes, stream, marks);
+                       y, cold_count, cold_routes, ws, ws_bytes, stream, marks, nullptr);
 }
 
 moe_status moe_experts_gateup(const moe_shape* shape, const uint16_t* x, int32_t M,

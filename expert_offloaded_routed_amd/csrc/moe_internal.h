@@ -175,6 +175,13 @@ struct RouteWs {
   int32_t* route_slot;  // slot of every route, -1 = cold
 };
 
+// Residual chaining by the kernels that produce y: out[m][h] = bf16(x[m][h] + y[m][h]) (out may
+// equal x; out == NULL: nothing).
+struct Residual {
+  const uint16_t* x;
+  uint16_t* out;
+};
+
 // Kernel launchers (moe_kernels.hip).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
                          int H, float* logits, uint32_t* zero, int n_zero, hipStream_t s);
@@ -182,7 +189,7 @@ bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M);
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                                const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
-                               hipStream_t s);
+                               Residual res, hipStream_t s);
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,
                               const int32_t* e2s, const BucketOut& o, hipStream_t s);
@@ -192,7 +199,7 @@ hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* 
                          const RouteWs& rw, uint16_t* hbuf, hipStream_t s);
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                       const uint16_t* hbuf, float* pdn, float* y, hipStream_t s);
+                       const uint16_t* hbuf, float* pdn, float* y, Residual res, hipStream_t s);
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, size_t n,
                            hipStream_t s);
 hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,
@@ -200,6 +207,7 @@ hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t*
                                  const RouteWs& rw, uint8_t* hq, hipStream_t s);
 hipError_t launch_down_grouped(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                                const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                               const uint8_t* hq, float* pdn, float* y, hipStream_t s);
+                               const uint8_t* hq, float* pdn, float* y, Residual res,
+                               hipStream_t s);
 
 }  // namespace moe

@@ -30,10 +30,12 @@ namespace moe {
 // =============================================================================================
 // grid.x = E (one wave per expert row); the wave keeps its row of W_r in registers (H/8 chunks
 // of 8 bf16, chunk c = lane + 64*i) and reads the same chunks of every token's x.
-constexpr int kRouterMaxChunksPerLane = kMaxHidden / 8 / 64;  // 16
 
-// Workgroup 0 also clears the n_zero handoff counters of the fused decode kernel that follows
-// (one per kHandStride words); the kernel boundary makes the zeros visible to it.
+// CPL = ceil(H/8/64) chunks per lane.  Every load is issued unconditionally (chunk index
+// clamped, the product of a chunk past the row selected away), so that no load waits alone in
+// a branch.  Workgroup 0 also clears the n_zero handoff counters of the fused decode kernel
+// that follows (one per kHandStride words); the kernel boundary makes the zeros visible to it.
+template <int CPL>
 __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, int M,
                                                const uint16_t* __restrict__ wr,
                                                const float* __restrict__ bias, int E, int H,
@@ -44,22 +46,21 @@ __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, i
   if (e == 0)
     for (int i = lane; i < n_zero; i += 64) zero[(size_t)i * kHandStride] = 0u;
   const int nch = H / 8;
-  uint4 wrow[kRouterMaxChunksPerLane];
+  const uint4* wsrc = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
+  uint4 wrow[CPL];
 #pragma unroll
-  for (int i = 0; i < kRouterMaxChunksPerLane; ++i) {
-    const int c = lane + 64 * i;
-    wrow[i] = c < nch ? reinterpret_cast<const uint4*>(wr + (size_t)e * H)[c] : make_uint4(0, 0, 0, 0);
-  }
+  for (int i = 0; i < CPL; ++i) wrow[i] = wsrc[min(lane + 64 * i, nch - 1)];
   const float b = bias != nullptr ? bias[e] : 0.0f;
   for (int m = 0; m < M; ++m) {
     const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * H);
+    uint4 xv[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) xv[i] = xr[min(lane + 64 * i, nch - 1)];
     float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kRouterMaxChunksPerLane; ++i) {
-      const int c = lane + 64 * i;
-      if (c < nch) {
-        acc = dot8_bf16(wrow[i], xr[c], acc);
-      }
+    for (int i = 0; i < CPL; ++i) {
+      const float v = dot8_bf16(wrow[i], xv[i], acc);
+      acc = lane + 64 * i < nch ? v : acc;
     }
     acc = wave_sum(acc);
     if (lane == 0) logits[(size_t)m * E + e] = acc + b;
@@ -77,7 +78,8 @@ __device__ __forceinline__ float rank_key(float v) { return v != v ? -INFINITY :
 __device__ void topk_rank(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
                           float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
-  const float v = lane < E ? rank_key(lrow[lane]) : -INFINITY;
+  const float lv = lrow[min(lane, E - 1)];  // unconditional load (a load in a branch is waited for alone)
+  const float v = lane < E ? rank_key(lv) : -INFINITY;
   int rank = 0;
   for (int j = 0; j < E; ++j) {
     const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
@@ -94,40 +96,71 @@ __device__ void topk_rank(const float* __restrict__ lrow, int E, int k, int32_t*
   }
 }
 
+// Larger E: every logit becomes a 64-bit rank key, larger = ranks higher (monotone image of
+// the value in the high word, NaN as -inf and -0 as +0; the bitwise complement of the id in the
+// low word, so that ties go to the lower id); then k rounds of: each lane's best key, the
+// wave's best key (DPP / swizzle / readlane), and the owner clears it.  All branch-free.
+__device__ __forceinline__ uint64_t rank_key64(float v, int id) {
+  v = rank_key(v);
+  if (v == 0.0f) v = 0.0f;
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)id;
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t h = (uint32_t)(key >> 32);
+  return __uint_as_float((h & 0x80000000u) ? (h ^ 0x80000000u) : ~h);
+}
+__device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));
+  v = max_u64(v, dpp_u64<0x4E>(v));
+  v = max_u64(v, dpp_u64<0x141>(v));
+  v = max_u64(v, dpp_u64<0x140>(v));
+  const uint32_t lo = (uint32_t)swz_xor16_i((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)swz_xor16_i((int)(uint32_t)(v >> 32));
+  v = max_u64(v, ((uint64_t)hi << 32) | lo);
+  const uint64_t a = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 0) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 0);
+  const uint64_t b = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 32) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 32);
+  return max_u64(a, b);
+}
+
 template <int PL>
 __device__ void topk_argmax(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
                             float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
-  float v[PL];
+  float lv[PL];
+  uint64_t key[PL];
+  // every load issued before any is used (clamped in range; loads in a branch would each be
+  // waited for alone); slots past E get key 0, below every real key
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int ee = lane + 64 * i;
-    v[i] = ee < E ? rank_key(lrow[ee]) : -INFINITY;
-  }
-  float my_v = -INFINITY, top = 0.0f;
-  int my_i = 0;
+  for (int i = 0; i < PL; ++i) lv[i] = lrow[min(lane + 64 * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) key[i] = lane + 64 * i < E ? rank_key64(lv[i], lane + 64 * i) : 0ull;
+  uint64_t mine = 0ull;  // lane j < k: the j-th key
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    uint64_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < PL; ++i)
-      if (lane + 64 * i < E) argmax_step(bv, bi, v[i], lane + 64 * i);
-    wave_argmax(bv, bi);  // uniform winner
-    if (j == 0) top = bv;
-    if (lane == j) {
-      my_v = bv;
-      my_i = bi;
-    }
-    if ((bi & 63) == lane) {
+    for (int i = 1; i < PL; ++i) best = max_u64(best, key[i]);
+    best = wave_max_u64(best);  // uniform
+    mine = lane == j ? best : mine;
 #pragma unroll
-      for (int i = 0; i < PL; ++i)
-        if (i == (bi >> 6)) v[i] = -INFINITY;
-    }
+    for (int i = 0; i < PL; ++i) key[i] = key[i] == best ? 0ull : key[i];
   }
-  const float ex = lane < k ? expf(my_v - top) : 0.0f;
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key_value(mine)), 0));
+  const float ex = lane < k ? expf(key_value(mine) - top) : 0.0f;
   const float den = wave_sum(ex);
   if (lane < k) {
-    ids[lane] = my_i;
+    ids[lane] = key_id(mine);
     w[lane] = ex / den;
   }
 }
@@ -492,6 +525,36 @@ __device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs&
   if (lane == 0) rt.nd = __popcll(hm);
 }
 
+// One token over any number of experts: top-k by wave 0 (topk_token), then the route table in
+// registers as in route_token_small: the token's ids are distinct, so every hot route is its
+// own distinct expert, placed in ascending expert id by a count over the k routes.
+__device__ __forceinline__ void route_token_wave(RouteLds& rt, const RouteArgs& a) {
+  const int lane = threadIdx.x & 63;
+  topk_token(a.logits, a.E, a.k, rt.ids, rt.w);
+  const bool route = lane < a.k;
+  const int e = route ? rt.ids[lane] : 0;
+  const int ec = min(max(e, 0), a.E - 1);
+  const int s_of = a.e2s != nullptr ? a.e2s[ec] : ec;  // issued for every lane (clamped)
+  int slot = -1;
+  if (route && e >= 0 && e < a.E && s_of >= 0 && s_of < a.S) slot = s_of;
+  if (route) rt.slot[lane] = slot;
+  const bool hot = slot >= 0;
+  const uint64_t hm = __ballot(hot);
+  int pos = 0;
+  for (int j = 0; j < a.k; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    pos += (((hm >> j) & 1ull) != 0ull && ej < e) ? 1 : 0;
+  }
+  if (hot) {
+    rt.dist_slot[pos] = slot;
+    rt.dist_off[pos] = pos;
+    rt.dist_cnt[pos] = 1;
+    rt.dist_e[pos] = e;
+    rt.perm[pos] = lane;
+  }
+  if (lane == 0) rt.nd = __popcll(hm);
+}
+
 // rt.ids / rt.w [0, Mk) must be in place (and visible after a barrier).  e2s may point to LDS.
 __device__ void build_table(RouteLds& rt, int Mk, int E, int S, const int32_t* e2s) {
   const int tid = threadIdx.x;
@@ -587,8 +650,13 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
   const int tid = threadIdx.x;
   const int nw = blockDim.x >> 6;
   const int Mk = a.M * a.k;
-  if (a.logits != nullptr && a.M == 1 && a.E <= kFastE) {
-    if (tid < 64) route_token_small(rt, a);
+  if (a.logits != nullptr && a.M == 1) {
+    if (tid < 64) {
+      if (a.E <= kFastE)
+        route_token_small(rt, a);
+      else
+        route_token_wave(rt, a);
+    }
     __syncthreads();
   } else {
     if (a.logits != nullptr) {
@@ -634,6 +702,12 @@ __device__ __forceinline__ void store_h_block(float h, uint8_t* __restrict__ hi,
     hi[h_pad + e] = (uint8_t)bl;
     if (e == 0) *sc = (uint8_t)(s + 127);
   }
+}
+
+// out[i] = bf16(x[i] + v) (round to nearest even), the residual chaining of stacked layers.
+__device__ __forceinline__ void residual_store(const Residual& res, size_t i, float v) {
+  if (res.out != nullptr)
+    res.out[i] = (uint16_t)f32_to_bf16_bits(__uint_as_float((uint32_t)res.x[i] << 16) + v);
 }
 
 // bf16(silu(g) * u), returned as the fp32 value of that bf16.
@@ -902,7 +976,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
     int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
     size_t dn_tile_bytes, size_t dn_code_bytes, int ks, int full, int rem, int nsw, int nb,
     int kparts, int h_lds, RouteArgs ra, RouteWs rw, const uint16_t* __restrict__ hbuf,
-    float* __restrict__ y) {
+    float* __restrict__ y, Residual res) {
   extern __shared__ __align__(16) uint8_t smem[];  // [h copy (h_lds)] [parts: Mk x kparts x 16]
   const int tile = blockIdx.x;
   const int Mk = ra.M * ra.k;
@@ -966,6 +1040,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
       acc = fmaf(ra.w_in[route], p, acc);
     }
     y[(size_t)m * H + tile * kDnRows + r] = acc;
+    residual_store(res, (size_t)m * H + tile * kDnRows + r, acc);
   }
 }
 
@@ -1142,7 +1217,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
     size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, int gu_tiles, int n_gu, int n_dnw,
     size_t gu_bytes, size_t dn_tile_bytes, size_t dn_code_bytes, int ks, int full, int rem,
     int nsw, int nb_i, RouteArgs ra, RouteWs rw, uint16_t* __restrict__ hbuf,
-    float* __restrict__ y, uint32_t* __restrict__ hand, uint32_t* __restrict__ claim) {
+    float* __restrict__ y, uint32_t* __restrict__ hand, uint32_t* __restrict__ claim,
+    Residual res) {
   __shared__ RouteLds rt;
   __shared__ __align__(16) uint8_t pool[kFusedPool];
   __shared__ int s_tile;
@@ -1293,6 +1369,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
       acc = fmaf(rt.w[j], p, acc);
     }
     y[(size_t)tile * kDnRows + row] = acc;
+    residual_store(res, (size_t)tile * kDnRows + row, acc);
   }
 }
 
@@ -1550,7 +1627,7 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
 // nothing).  One thread per (token, 4 rows).
 __global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs ra, RouteWs rw,
                                                  const float* __restrict__ pdn,
-                                                 float* __restrict__ y) {
+                                                 float* __restrict__ y, Residual res) {
   const int q = blockIdx.x * blockDim.x + threadIdx.x;
   const int per = H / 4;
   if (q >= M * per) return;
@@ -1572,6 +1649,11 @@ __global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs 
   yo[1] = acc.y;
   yo[2] = acc.z;
   yo[3] = acc.w;
+  const size_t i = (size_t)m * H + h;
+  residual_store(res, i, acc.x);
+  residual_store(res, i + 1, acc.y);
+  residual_store(res, i + 2, acc.z);
+  residual_store(res, i + 3, acc.w);
 }
 
 // =============================================================================================
@@ -1596,8 +1678,20 @@ hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const flo
   if (M >= kGroupedMinTokens)  // a dense GEMM: MFMA
     hipLaunchKernelGGL(k_router_grouped, dim3((M + kGemmTok - 1) / kGemmTok, (E + 63) / 64), dim3(256),
                        0, s, x, M, wr, bias, E, H, logits);
-  else
-    hipLaunchKernelGGL(k_router, dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits, zero, n_zero);
+  else {
+    const int cpl = (H / 8 + 63) / 64;
+    switch (cpl) {
+#define MOE_RT(C)                                                                                  \
+  case C:                                                                                          \
+    hipLaunchKernelGGL((k_router<C>), dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits, zero, \
+                       n_zero);                                                                    \
+    break;
+      MOE_RT(1) MOE_RT(2) MOE_RT(3) MOE_RT(4) MOE_RT(5) MOE_RT(6) MOE_RT(7) MOE_RT(8)
+      MOE_RT(9) MOE_RT(10) MOE_RT(11) MOE_RT(12) MOE_RT(13) MOE_RT(14) MOE_RT(15) MOE_RT(16)
+#undef MOE_RT
+      default: return hipErrorInvalidValue;
+    }
+  }
   return hipGetLastError();
 }
 
@@ -1701,7 +1795,7 @@ hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* 
 static hipError_t launch_down_mx(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                                  int n_items, bool use_items, const RouteArgs& ra,
                                  const RouteWs& rw, const uint8_t* hq, float* pdn, float* y,
-                                 hipStream_t s) {
+                                 Residual res, hipStream_t s) {
   const int per_wg = 4 * kDnRW;
   hipLaunchKernelGGL(k_down_mx, dim3((L.dn_tiles + per_wg - 1) / per_wg, n_items), dim3(256), 0, s,
                      H, slots, L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.dn_code_bytes,
@@ -1711,13 +1805,13 @@ static hipError_t launch_down_mx(int M, int H, int I, const uint8_t* slots, cons
   if (e != hipSuccess) return e;
   const int threads = M * (H / 4);
   hipLaunchKernelGGL(k_combine, dim3((threads + 255) / 256), dim3(256), 0, s, M, ra.k, H, ra, rw,
-                     pdn, y);
+                     pdn, y, res);
   return hipGetLastError();
 }
 
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                       const uint16_t* hbuf, float* pdn, float* y, hipStream_t s) {
+                       const uint16_t* hbuf, float* pdn, float* y, Residual res, hipStream_t s) {
   (void)p;
   (void)pdn;
   const int Mk = M * ra.k;
@@ -1734,7 +1828,7 @@ hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLay
   hipLaunchKernelGGL((k_down_gemv<TM>), dim3(L.dn_tiles), dim3(512), lds, s, H, I, slots,           \
                      L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks,          \
                      L.dn_full, L.dn_rem, L.dn_scale_words, L.nb_i, kparts, h_lds ? 1 : 0, ra, rw,  \
-                     hbuf, y)
+                     hbuf, y, res)
   if (spw <= 4) MOE_DG(4);
   else if (spw <= 8) MOE_DG(8);
   else if (spw <= 12) MOE_DG(12);
@@ -1754,8 +1848,9 @@ hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t*
 
 hipError_t launch_down_grouped(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                                const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                               const uint8_t* hq, float* pdn, float* y, hipStream_t s) {
-  return launch_down_mx(M, H, I, slots, L, p.n_items_max, true, ra, rw, hq, pdn, y, s);
+                               const uint8_t* hq, float* pdn, float* y, Residual res,
+                               hipStream_t s) {
+  return launch_down_mx(M, H, I, slots, L, p.n_items_max, true, ra, rw, hq, pdn, y, res, s);
 }
 
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, size_t n,
@@ -1837,7 +1932,7 @@ bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M) {
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                                const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
-                               hipStream_t s) {
+                               Residual res, hipStream_t s) {
   (void)M;
   const int n_gu = L.gu_tiles * p.nd_max;
   const dim3 g(layer_decode_grid(L, p)), b(p.gu_waves * 64);
@@ -1848,7 +1943,7 @@ hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uin
                        L.gu_tile_bytes, L.nb_h, L.ng_h, L.gu_tiles, n_gu, L.dn_tiles, L.gu_bytes,   \
                        L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks, L.dn_full, L.dn_rem,              \
                        L.dn_scale_words, L.nb_i, ra, rw, hbuf, y, hand,                            \
-                       hand + (size_t)p.nd_max * kHandSub * kHandStride);                           \
+                       hand + (size_t)p.nd_max * kHandSub * kHandStride, res);                      \
     e = hipGetLastError();                                                                         \
   } while (0)
   MOE_LD_SWITCH(p.gu_groups, layer_decode_tmx(layer_decode_spw(L, p)), MOE_LD)

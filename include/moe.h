@@ -206,6 +206,20 @@ moe_status moe_experts_down(const moe_shape* shape, int32_t M, const int32_t* to
                             const uint8_t* slots, float* y, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* moe_layer_forward that also writes x_next = bf16(x + y) (round to nearest even), the input
+ * of the next layer of a stack [MoE expert offload, "How it works": the layers of the model run
+ * one after another on the same token], from the kernels that form y: no launch of its own.
+ * x_next [M,H] bf16, 2-byte aligned, may equal x (then x is overwritten after every use of it
+ * in the call).  Equal, bitwise, to moe_layer_forward followed by moe_residual_bf16(x, y,
+ * x_next, M*H). */
+moe_status moe_layer_forward_residual(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                      const uint16_t* w_router, const float* router_bias,
+                                      const int32_t* expert_to_slot, const uint8_t* slots,
+                                      int32_t* topk_ids, float* topk_w, float* y,
+                                      int32_t* cold_count, int32_t* cold_routes,
+                                      uint16_t* x_next, void* ws, size_t ws_bytes,
+                                      hipStream_t stream);
+
 /* Residual chaining of stacked layers: out[i] = bf16(x[i] + y[i]) (round to nearest even),
  * for feeding one layer's output to the next [MoE expert offload, "How it works": the layers of
  * the model run one after another on the same token].  x, out: bf16 [n] (out may equal x);

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
                           "moe_pack_expert", "moe_unpack_expert", "moe_expert_image_bytes",
                           "moe_workspace_size", "moe_layer_forward", "moe_last_error",
                           "moe_experts_gateup", "moe_experts_down", "moe_layer_forward_marked",
-                          "moe_residual_bf16", "moe_layer_launches"}
+                          "moe_residual_bf16", "moe_layer_launches", "moe_layer_forward_residual"}
     for n in names:
         assert hasattr(lib, n), n
     # no torch in the exported signatures: the header includes only C/HIP headers

@@ -534,3 +534,35 @@ def test_fused_decode_consecutive_tokens_and_maps(gptoss):
                 else:
                     close_enough(a.y[:1].cpu().numpy(), ref["y_hot"], f"fused decode {name} {t}")
                 assert cc == len(ref["cold_routes"])
+
+
+def test_layer_forward_residual_equals_layer_plus_residual(gptoss, tiny):
+    """moe_layer_forward_residual == moe_layer_forward + moe_residual_bf16, bitwise, on the fused
+    one-token path, the GEMV path and the grouped GEMM path, in place and into another buffer."""
+    for lay, Ms in ((gptoss, (1, 3)), (tiny, (64, 130))):
+        wl, shape = lay.wl, lay.shape
+        wr = _dev(lay.wr)
+        for M in Ms:
+            say("layer_forward_residual:", wl.name, "M =", M)
+            xn = synthetic.activations(wl, M, 1300 + M)
+            a, b = L.Buffers(shape, M), L.Buffers(shape, M)
+            x_ref = _dev(xn)
+            B.moe_layer_forward(shape, x_ref, M, wr, None, None, lay.slots, a.ids, a.w, a.y,
+                                a.cold_count, a.cold_routes, a.ws)
+            nxt_ref = torch.zeros_like(x_ref)
+            B.moe_residual_bf16(x_ref, a.y, nxt_ref, M * wl.hidden)
+            x_sep = _dev(xn)
+            nxt = torch.zeros_like(x_sep)
+            B.moe_layer_forward_residual(shape, x_sep, M, wr, None, None, lay.slots, b.ids, b.w, b.y,
+                                         b.cold_count, b.cold_routes, nxt, b.ws)
+            torch.cuda.synchronize()
+            assert torch.equal(a.y[:M], b.y[:M]) and torch.equal(nxt_ref, nxt)
+            assert torch.equal(x_sep, x_ref)  # the input is left alone
+            x_in = _dev(xn)
+            B.moe_layer_forward_residual(shape, x_in, M, wr, None, None, lay.slots, b.ids, b.w, b.y,
+                                         b.cold_count, b.cold_routes, x_in, b.ws)
+            torch.cuda.synchronize()
+            assert torch.equal(a.y[:M], b.y[:M]) and torch.equal(x_in, nxt_ref)
+    with pytest.raises(B.MoeError):
+        B.moe_layer_forward_residual(gptoss.shape, x_ref, 1, wr, None, None, gptoss.slots, a.ids, a.w,
+                                     a.y, None, None, None, a.ws)
