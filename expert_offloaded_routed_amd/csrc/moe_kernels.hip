@@ -475,6 +475,8 @@ struct RouteLds {
   int dist_e[kProMaxRoutes];
   int nd;
 };
+constexpr size_t kRouteLdsBytes = (sizeof(RouteLds) + 15) / 16 * 16;
+constexpr size_t kGuLdsBytes = 64 * 1024;  // LDS of a gate/up workgroup at most
 
 // One token over at most kFastE experts (the decode case): top-k, slot resolve and the whole
 // route table by wave 0 in registers, with no loop over LDS and no call.  The logit row is
@@ -719,19 +721,24 @@ __device__ __forceinline__ float swiglu_bf16(float g, float u) {
 // grid = (I/32 tiles, nd_max); block = nw waves.  Lane l < 32 accumulates gate row 32*tile + l,
 // lane l >= 32 the matching up row; wave w covers groups [w*ng/nw, (w+1)*ng/nw).
 // SINGLE: one token per call (M = 1), one route per expert.  XLDS: the M activation rows are
-// staged in LDS (M*H*2 <= kXLdsBytes), requested before anything else.
+// staged in LDS (when they fit beside the sums and the route table), requested before anything
+// else.
 template <bool SINGLE, int G, bool PRO, bool XLDS>
 __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
     const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
     size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, RouteArgs ra, RouteWs rw,
     uint16_t* __restrict__ hbuf) {
-  __shared__ float red[kMaxWaves][SINGLE ? 1 : kTokPerPass][64];
-  __shared__ RouteLds rt;
-  __shared__ __align__(16) uint16_t xs[XLDS ? kXLdsBytes / 2 : 8];
+  // dynamic LDS, sized by the launcher: [red: nw x RP x 64 floats][rt (PRO)][xs: M x H (XLDS)]
+  extern __shared__ __align__(16) uint8_t gsm[];
+  constexpr int RP = SINGLE ? 1 : kTokPerPass;
   const int tile = blockIdx.x;
   const int d = blockIdx.y;
   const int Mk = ra.M * ra.k;
   const int nthr = blockDim.x;
+  const size_t red_bytes = (size_t)(nthr >> 6) * RP * 64 * 4;
+  float (*red)[RP][64] = reinterpret_cast<float (*)[RP][64]>(gsm);
+  RouteLds& rt = *reinterpret_cast<RouteLds*>(gsm + red_bytes);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(gsm + red_bytes + (PRO ? kRouteLdsBytes : 0));
 
   // Activations to LDS, requested before anything else so that their latency overlaps the
   // route-table reads.
@@ -1004,18 +1011,28 @@ __global__ __launch_bounds__(512) void k_down_gemv(
       __builtin_amdgcn_global_load_lds(hbuf + (size_t)p * 8, (lds_void*)(smem + (size_t)run * 1024), 16, 0, 0);
     }
   }
-  uint4 c[TM];
-  uint32_t sw[TM / 4];
+  // weights of the next expert in flight while this one's routes are formed (not at 16 steps a
+  // wave: two sets would not fit the register file)
+  constexpr bool PF = TM <= 12;
+  uint4 c[TM], cn[PF ? TM : 1];
+  uint32_t sw[TM / 4], swn[PF ? TM / 4 : 1];
   dn_load_steps<TM>(sec + (size_t)slot0 * image_bytes, dn_code_bytes, s0, ks, full, rem, nsw, lane, c, sw);
   const uint16_t* hsrc = h_lds ? reinterpret_cast<const uint16_t*>(smem) : hbuf;
   float* parts = reinterpret_cast<float*>(smem + (h_lds ? (size_t)(n_h + 63) / 64 * 1024 : 0));
   __syncthreads();
   for (int d = es0; d < nd; d += sl) {
     const int4 dd = rw.dist[d];
-    if (d != es0)
-      dn_load_steps<TM>(sec + (size_t)dd.x * image_bytes, dn_code_bytes, s0, ks, full, rem, nsw, lane, c, sw);
-    const int off = dd.y, cnt = dd.z;
-    if (cnt <= 0 || off < 0 || off + cnt > Mk) continue;
+    if constexpr (PF) {
+      // the last pass re-requests its own weights, unused
+      const int dn = d + sl < nd ? d + sl : d;
+      dn_load_steps<TM>(sec + (size_t)rw.dist[dn].x * image_bytes, dn_code_bytes, s0, ks, full,
+                        rem, nsw, lane, cn, swn);
+    } else if (d != es0) {
+      dn_load_steps<TM>(sec + (size_t)dd.x * image_bytes, dn_code_bytes, s0, ks, full, rem, nsw,
+                        lane, c, sw);
+    }
+    const int off = dd.y;
+    const int cnt = off >= 0 && dd.z > 0 && off + dd.z <= Mk ? dd.z : 0;
 #pragma unroll 1
     for (int j = 0; j < cnt; ++j) {
       // keeps the decode of the codes inside this loop (hoisted, it would hold 16 VGPRs per step)
@@ -1025,6 +1042,12 @@ __global__ __launch_bounds__(512) void k_down_gemv(
       float acc = dn_route_dot<TM>(c, sw, s0, spw, ks, nb, g, hsrc + (size_t)route * I);
       acc = dn_row_sum(acc);
       if (lane < kDnRows) parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+    }
+    if constexpr (PF) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) c[t] = cn[t];
+#pragma unroll
+      for (int q = 0; q < TM / 4; ++q) sw[q] = swn[q];
     }
   }
   __syncthreads();
@@ -1728,7 +1751,10 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
   // which every supported shape is) with the route table from the bucketing kernel
   p.grouped = M >= kGroupedMinTokens;
   p.n_items_max = n_items_max(Mk, E);
-  p.prologue = !p.grouped && Mk <= kProMaxRoutes;
+  // every gate/up workgroup rebuilding the route table pays a top-k per token: worth it for one
+  // token, or for a few routes over few experts; otherwise the top-k / bucketing kernel does it
+  // once
+  p.prologue = !p.grouped && Mk <= kProMaxRoutes && (M == 1 || (E <= 64 && Mk <= 64));
   // gate/up waves per workgroup: each wave holds at most kMaxGroups groups of its tile's K;
   // the kernels are built for <= 128 VGPRs, so a CU holds kWavesPerCU waves.  Pick the widest
   // workgroup that still lets every workgroup of the grid be resident at once.
@@ -1753,13 +1779,17 @@ hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* 
                          const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                          const RouteWs& rw, uint16_t* hbuf, hipStream_t s) {
   const dim3 g(L.gu_tiles, p.nd_max), b(p.gu_waves * 64);
-#define MOE_GU(SINGLE, G, PRO, XLDS)                                                               \
-  hipLaunchKernelGGL((k_gateup<SINGLE, G, PRO, XLDS>), g, b, 0, s, x, H, I, slots, L.image_bytes, \
-                     L.gu_tile_bytes, L.nb_h, L.ng_h, ra, rw, hbuf)
   // the single-token variant lets arithmetic overlap the loads but holds more registers, so
   // it is only used with at most 3 groups per wave; M == 1 always fits the LDS copy of x
   const bool single = M == 1 && p.gu_groups <= 3;
-  const bool xlds = (size_t)M * H * 2 <= (size_t)kXLdsBytes;
+  const size_t red = (size_t)p.gu_waves * (single ? 1 : kTokPerPass) * 64 * 4;
+  const size_t fixed = red + (p.prologue ? kRouteLdsBytes : 0);
+  const size_t xb = (size_t)M * H * 2;
+  const bool xlds = fixed + xb <= kGuLdsBytes;
+  const size_t lds = fixed + (xlds ? xb : 0);
+#define MOE_GU(SINGLE, G, PRO, XLDS)                                                               \
+  hipLaunchKernelGGL((k_gateup<SINGLE, G, PRO, XLDS>), g, b, lds, s, x, H, I, slots,              \
+                     L.image_bytes, L.gu_tile_bytes, L.nb_h, L.ng_h, ra, rw, hbuf)
   if (single) {
     if (p.prologue) {
       if (p.gu_groups <= 1) MOE_GU(true, 1, true, true);
