@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--stage-steps", type=int, default=256, help="marked steps for stage timing")
     p.add_argument("--enqueue-spin-cycles", type=float, default=2e8,
                    help="GPU cycles of the spin kernel that holds the stream while marked steps are enqueued")
-    p.add_argument("--cpu-steps", type=int, default=12, help="oracle steps for cpu_baseline (0 = skip)")
+    p.add_argument("--cpu-steps", type=int, default=40, help="oracle steps for cpu_baseline (0 = skip)")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB device to device 4 times (a "
                         "plain copy kernel of known size, to scale HBM byte counters)")
