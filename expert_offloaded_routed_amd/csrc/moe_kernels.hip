@@ -685,27 +685,6 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
 // lo[h_pad] E4M3 codes, then one E8M0 scale byte per 32-element block.  Elements past I, and
 // scale bytes past the last block, are never written: k_down_mx substitutes zeros and 127.
 
-// Lanes 32j .. 32j+31 hold (as fp32) the 32 bf16 values of one block of h, element lane & 31;
-// all 32 active.  hi points at the block's first hi code, h_pad separates hi and lo, sc is the
-// block's scale byte.  WT: device-scope write-through stores, for a reader in the same launch.
-template <bool WT>
-__device__ __forceinline__ void store_h_block(float h, uint8_t* __restrict__ hi, int h_pad,
-                                              uint8_t* __restrict__ sc) {
-  const int s = mx_shift(half_max_i(f32_exp(h)));
-  uint32_t bh, bl;
-  mx_pair(h, s, &bh, &bl);
-  const int e = threadIdx.x & 31;
-  if (WT) {
-    __hip_atomic_store(hi + e, (uint8_t)bh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(hi + h_pad + e, (uint8_t)bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (e == 0) __hip_atomic_store(sc, (uint8_t)(s + 127), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    hi[e] = (uint8_t)bh;
-    hi[h_pad + e] = (uint8_t)bl;
-    if (e == 0) *sc = (uint8_t)(s + 127);
-  }
-}
-
 // out[i] = bf16(x[i] + v) (round to nearest even), the residual chaining of stacked layers.
 __device__ __forceinline__ void residual_store(const Residual& res, size_t i, float v) {
   if (res.out != nullptr)
@@ -864,7 +843,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
 // A down tile (16 rows of one expert) is streamed one K step (4 blocks = 128 elements) per MFMA
 // operand: a wave-wide 16-byte load is 1 KiB, and nothing is decoded (the block-scaled MFMA
 // takes the E2M1 codes with their E8M0 scales).  h enters as the other operand: a column is one
-// route's hi or lo codes (see store_h_block) with the block scales.
+// route's hi or lo codes (see mx_pair) with the block scales.
 
 // This lane's A operand of down step s (clamped to the last step; lanes past the stored part
 // of a partial step re-read a stored lane and meet zero h).
