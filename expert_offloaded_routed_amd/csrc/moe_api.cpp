@@ -239,22 +239,24 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_residual: x_next must be 2-byte aligned");
   float* logits = at<float>(ws, W.logits);
   hipError_t e;
-  // One token with a fusable shape: gate/up and down run as one launch (the router clears its
-  // handoff counters).  MOE_DECODE_UNFUSED=1 in the environment selects the two-launch path.
+  // One token with a fusable shape: gate/up and down run as one launch (the router fills the h
+  // rows it hands over with the "not yet written" pattern).  MOE_DECODE_UNFUSED=1 in the
+  // environment selects the multi-launch path.
   const ImageLayout L = image_layout(shape->hidden, shape->inter);
   const ExpertPlan p = plan_experts(L, M, shape->n_experts, shape->top_k);
-  const bool fused = !decode_unfused() && layer_decode_fusable(L, p, M);
-  uint32_t* hand = at<uint32_t>(ws, W.hand);
+  const bool fused = !decode_unfused() && layer_decode_fusable(L, p, M, shape->top_k);
+  uint16_t* hbuf = at<uint16_t>(ws, W.hq);
   if (marks && (e = record_mark(marks[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
-                    fused ? hand : nullptr, fused ? p.nd_max * kHandSub + 1 : 0, stream);
+                    fused ? reinterpret_cast<uint32_t*>(hbuf) : nullptr,
+                    fused ? M * shape->top_k * shape->inter / 2 : 0, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   if (fused) {
     if (marks && (e = record_mark(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
     const RouteArgs ra = route_args(shape, M, logits, topk_ids, topk_w, expert_to_slot, topk_ids,
                                     topk_w, cold_count, cold_routes);
     e = launch_layer_decode(x, M, shape->hidden, shape->inter, slots, L, p, ra, route_ws(ws, W),
-                            at<uint16_t>(ws, W.hq), y, hand, Residual{x, x_next}, stream);
+                            hbuf, y, Residual{x, x_next}, stream);
     if (e != hipSuccess) return hip_fail(e, "fused decode launch");
     for (int i = 2; marks && i < 4; ++i)
       if ((e = record_mark(marks[i], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -304,7 +306,7 @@ moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n) {
   }
   const ImageLayout L = image_layout(shape->hidden, shape->inter);
   const ExpertPlan p = plan_experts(L, M, shape->n_experts, shape->top_k);
-  if (!decode_unfused() && layer_decode_fusable(L, p, M))
+  if (!decode_unfused() && layer_decode_fusable(L, p, M, shape->top_k))
     *n = 2;                     // router, fused experts
   else if (p.grouped)
     *n = 5;                     // router, top-k / bucket, gate/up, down, combine

@@ -27,6 +27,19 @@ __device__ __forceinline__ float swz_xor16_f(float v) {
   return __int_as_float(swz_xor16_i(__float_as_int(v)));
 }
 
+// Sums over the lane pairs (l, l^8), (l, l^16) and (l, l^32), on the VALU: a DPP rotate by 8
+// within rows of 16, and the gfx950 permlane swaps, whose two results hold the lower and the
+// upper lane of each pair.  Both lanes of a pair get the same bits.
+__device__ __forceinline__ float pair_sum8(float v) { return v + dpp_f<0x128>(v); }
+__device__ __forceinline__ float pair_sum16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Sum over the 64 lanes; every lane gets the same (deterministically ordered) total.
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp_f<0xB1>(v);

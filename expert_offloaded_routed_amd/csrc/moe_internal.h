@@ -89,17 +89,11 @@ struct WsLayout {
   size_t items;          // i32x2 [n_items_max]: grouped GEMM work list {distinct expert, first route}
   size_t hq;             // h of every route: bf16 [I] (GEMV paths, M < 64) or, on the grouped
                          // path, split for the block-scaled MFMA (ImageLayout::h_stride bytes)
-  size_t pdn;            // f32 [M*k][H]: down partial sums when they do not fit in LDS
-  size_t hand;           // u32 counters of the fused decode kernel, one per 64 bytes
+  size_t pdn;            // f32 [M*k][H]: down partial sums of the grouped path
   size_t total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
-
-// Fused decode kernel handoff: kHandSub arrival counters per distinct hot expert (gate/up tile t
-// counts on counter t % kHandSub), each on its own 64-byte line, then the down-tile claim counter.
-constexpr int kHandSub = 8;
-constexpr int kHandStride = 16;  // 32-bit words between counters
 
 // Grouped GEMM work items: (distinct hot expert, pass of up to kItemRoutes of its routes).
 // sum over experts of ceil(c_e / kItemRoutes) <= (number of experts) + M*k / kItemRoutes.
@@ -126,7 +120,6 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   W.items = o;       o = align256(o + 8 * (size_t)n_items_max((int)Mk, E));
   W.hq = o;          o = align256(o + Mk * (L.h_stride > 2 * (size_t)I ? L.h_stride : 2 * (size_t)I));
   W.pdn = o;         o = align256(o + 4 * Mk * (size_t)H);
-  W.hand = o;        o = align256(o + 64 * ((size_t)nd * kHandSub + 1));
   W.total = o;
   return W;
 }
@@ -184,12 +177,12 @@ struct Residual {
 
 // Kernel launchers (moe_kernels.hip).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, uint32_t* zero, int n_zero, hipStream_t s);
-bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M);
+                         int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s);
+bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M, int k);
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                               const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
-                               Residual res, hipStream_t s);
+                               const RouteWs& rw, uint16_t* hbuf, float* y, Residual res,
+                               hipStream_t s);
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,
                               const int32_t* e2s, const BucketOut& o, hipStream_t s);

@@ -13,8 +13,9 @@
 //   k_combine       then y = ordered (ascending j) weighted sum of those rows.
 //   k_layer_decode  one token: gate/up and down (with the combine) in one launch.
 //   k_gateup_grouped / k_router_grouped: bf16 MFMA GEMMs for many tokens.
-// Dependencies between stages go through kernel boundaries, except inside k_layer_decode (see
-// there): a device-scope fence per workgroup costs tens of nanoseconds, serialised, on MI355X.
+// Dependencies between stages go through kernel boundaries, except inside k_layer_decode, which
+// hands h over by value (see there): a device-scope fence per workgroup costs tens of
+// nanoseconds, serialised, on MI355X.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,18 +34,18 @@ namespace moe {
 
 // CPL = ceil(H/8/64) chunks per lane.  Every load is issued unconditionally (chunk index
 // clamped, the product of a chunk past the row selected away), so that no load waits alone in
-// a branch.  Workgroup 0 also clears the n_zero handoff counters of the fused decode kernel
-// that follows (one per kHandStride words); the kernel boundary makes the zeros visible to it.
+// a branch.  The workgroups also fill n_fill words at fill with 0xFFFFFFFF: the h rows of the
+// fused decode kernel that follows, which hands h over by value and takes 0xFFFF for "not yet
+// written" (the kernel boundary makes the fill visible to it).
 template <int CPL>
 __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, int M,
                                                const uint16_t* __restrict__ wr,
                                                const float* __restrict__ bias, int E, int H,
                                                float* __restrict__ logits,
-                                               uint32_t* __restrict__ zero, int n_zero) {
+                                               uint32_t* __restrict__ fill, int n_fill) {
   const int lane = threadIdx.x;
   const int e = blockIdx.x;
-  if (e == 0)
-    for (int i = lane; i < n_zero; i += 64) zero[(size_t)i * kHandStride] = 0u;
+  for (int i = e * 64 + lane; i < n_fill; i += E * 64) fill[i] = 0xFFFFFFFFu;
   const int nch = H / 8;
   const uint4* wsrc = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
   uint4 wrow[CPL];
@@ -941,10 +942,7 @@ __device__ __forceinline__ float dn_route_dot(const uint4 (&c)[TM], const uint32
 }
 
 // Sum over the 4 lanes of a row (l, l^16, l^32, l^48); every one of them gets it.
-__device__ __forceinline__ float dn_row_sum(float v) {
-  v += swz_xor16_f(v);
-  return v + __shfl_xor(v, 32);
-}
+__device__ __forceinline__ float dn_row_sum(float v) { return pair_sum32(pair_sum16(v)); }
 
 // Steps of a K part: K split over kparts, rounded up to whole scale words.
 __host__ __device__ __forceinline__ int dn_part_steps(int ks, int kparts) {
@@ -1186,192 +1184,398 @@ __global__ __launch_bounds__(256) void k_down_mx(
 }
 
 // =============================================================================================
-// Fused decode: gate/up and down in one launch, handing h over without fences
+// Fused decode: the expert part of one token in one launch, h handed over by value
 // =============================================================================================
-// For one token (M = 1, the route table rebuilt per workgroup) the two expert stages run in one
-// grid whose workgroups are all resident at once.  Workgroup i first does gate/up unit i (tile
-// i % gu_tiles of distinct expert i / gu_tiles, exactly as k_gateup): it writes its 32 h values
-// (one block, split for the matrix cores) write-through (device-scope relaxed atomic stores),
-// waits for them to complete, and adds 1 to the arrival counter (tile % kHandSub) of its
-// expert.  Then it claims the next down tile (of H/16) from a counter, so that the down work,
-// and its weight traffic, goes to the workgroups whose gate/up part ended first (those on
-// compute units that hold one workgroup of the grid, not two).  The waves of a down tile own
-// (hot expert slot, K part) pairs, request their down weights into the registers that the
-// gate/up part has just released, wait until every hot expert's counters show all of its
-// gate/up tiles, read h
-// device-coherently (loads that bypass the non-coherent caches) into LDS and run the
-// block-scaled MFMA over their K part (column 0 of B = hi, column 1 = lo); the workgroup then
-// forms y for its 16 rows in the fixed route order.
-//   No fence is involved: a device-scope release or acquire per workgroup costs tens of ns,
-// serialised, on MI355X; write-through stores whose completion is awaited before the counter
-// add, and coherent loads after it, order the data without one.  A down part waits on gate/up
-// parts of any workgroup, so the whole grid must be resident: the launcher checks the grid
-// against the kernel's occupancy.  The wait is bounded all the same; a launch that ran out of
-// it would flag kErrHandoff in meta[2] (it cannot happen with the grid resident).  The
-// counters are cleared by the router kernel of the same call.
-constexpr int kFusedPool = 40 * 1024;  // LDS pool: gate/up x copy + sums, then down h copy + sums
-constexpr int kHandSpins = 1 << 15;    // wait bound, in polls of ~0.2 us
-constexpr int kFusedSlots = 4;         // hot experts of the token (waves per K part)
+// One workgroup of 16 waves per compute unit, the grid at most the CU count (so it is resident
+// at once, one workgroup per CU).  The work is cut into units: a gate/up unit is 16 h values of
+// one hot expert (their 16 gate and 16 up rows over all of K: image lanes 16f..16f+15 and
+// 32+16f..32+16f+15 of gate/up tile t), a down unit is 8 output rows (rows 8f..8f+7 of a 16-row
+// down tile) over every hot expert.  At H = I the two kinds weigh the same bytes.  Workgroup w
+// takes an equal contiguous share of each kind (the down shares in reverse workgroup order, so
+// that shares which round up rarely meet in one workgroup) and requests every weight byte of
+// its units at once, the 16 waves splitting each unit's K.  Then it
+//   1. forms its gate/up units: per-lane block dots, the lane pair of a row and the waves summed
+//      in a fixed order, h = bf16(silu(g)*u) stored write-through (device-scope relaxed
+//      stores);
+//   2. gathers h of every hot expert into LDS by polling: the router kernel of the same call
+//      has filled the h rows with 0xFFFF, a bit pattern the h writer never stores (it writes NaN
+//      as 0x7FC0), so an element that differs from it is final.  The loads bypass the
+//      non-coherent caches;
+//   3. forms its down units and y for their rows, hot routes in ascending order (+ residual).
+// No counter, fence or read-modify-write is involved.  The gather is bounded: a launch that ran
+// out of it flags kErrHandoff in meta[2] (it cannot happen with the grid resident).
+constexpr int kFusedWaves = 16;
+constexpr int kFusedThreads = kFusedWaves * 64;
+constexpr int kFusedSlots = 4;      // hot experts of the token at most
+constexpr int kHandSpins = 1 << 13; // gather rounds at most (each ~1 us: a round trip + sleep)
+constexpr int kPollChunks = 2;      // 16-byte chunks of h per thread in the gather
+constexpr uint32_t kHSentinel = 0xFFFFu;
 
-template <int G, int TMX>
-__global__ __launch_bounds__(kMaxWaves * 64) void k_layer_decode(
+// Share of workgroup w of U units over G workgroups: [lo, lo + n).
+__device__ __forceinline__ void unit_share(int w, int G, int U, int& lo, int& n) {
+  lo = w * U / G;
+  n = (w + 1) * U / G - lo;
+}
+// v clamped to [lo, hi]; lo when the range is empty
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return max(min(v, hi), lo); }
+// True when none of the 8 bf16 elements of a chunk is the sentinel.
+__device__ __forceinline__ bool h_chunk_final(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  bool ok = true;
+  const uint32_t w[4] = {a, b, c, d};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ok = ok && (w[i] & 0xFFFFu) != kHSentinel && (w[i] >> 16) != kHSentinel;
+  return ok;
+}
+
+// Scale byte j of word w as a float, or zero when !keep.  Branch-free (a mask, not a
+// conditional): a conditional use lets the compiler sink the word's load into the branch and
+// wait there for every load in flight.
+__device__ __forceinline__ float scale_or_zero(uint32_t w, int j, bool keep) {
+  const float f = e8m0_to_f32((w >> (8 * j)) & 0xFFu);
+  return __uint_as_float(__float_as_uint(f) & (keep ? 0xFFFFFFFFu : 0u));
+}
+
+// Adds the dot of one 32-element block (16 code bytes, the block scale sc folded into the
+// scaled converter) with 32 bf16 activations to two accumulation chains (even / odd pairs).
+__device__ __forceinline__ void block_dot_scaled(const uint4 c, const uint4 a0, const uint4 a1,
+                                                 const uint4 a2, const uint4 a3, float sc,
+                                                 float& s0, float& s1) {
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+  const uint32_t aw[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                           a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 0),
+                                         as_bf16x2(aw[4 * j + 0]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 1),
+                                         as_bf16x2(aw[4 * j + 1]), s1, false);
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 2),
+                                         as_bf16x2(aw[4 * j + 2]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 3),
+                                         as_bf16x2(aw[4 * j + 3]), s1, false);
+  }
+}
+
+// LDS of the kernel past the route table: x runs (1 KiB each), h rows of the hot experts, the
+// gate/up sums [NUG][waves][32] and the down sums [NUD][slots][waves][8].
+__host__ __device__ __forceinline__ size_t fused_x_bytes(int H) { return (size_t)((H / 8 + 63) / 64) * 1024; }
+__host__ __device__ __forceinline__ size_t fused_lds_bytes(int H, int I, int nug, int nud) {
+  return fused_x_bytes(H) + (size_t)kFusedSlots * I * 2 + (size_t)nug * kFusedWaves * 32 * 4 +
+         (size_t)nud * kFusedSlots * kFusedWaves * 8 * 4;
+}
+
+template <int NUG, int NEG, int NUD, int NED>
+__global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
-    size_t image_bytes, size_t gu_tile_bytes, int nb, int ng, int gu_tiles, int n_gu, int n_dnw,
-    size_t gu_bytes, size_t dn_tile_bytes, size_t dn_code_bytes, int ks, int full, int rem,
-    int nsw, int nb_i, RouteArgs ra, RouteWs rw, uint16_t* __restrict__ hbuf,
-    float* __restrict__ y, uint32_t* __restrict__ hand, uint32_t* __restrict__ claim,
-    Residual res) {
+    size_t image_bytes, size_t gu_tile_bytes, int nb, size_t gu_bytes, size_t dn_tile_bytes,
+    size_t dn_code_bytes, int ks, int full, int rem, int nb_i, RouteArgs ra, RouteWs rw,
+    uint16_t* __restrict__ hbuf, float* __restrict__ y, Residual res) {
   __shared__ RouteLds rt;
-  __shared__ __align__(16) uint8_t pool[kFusedPool];
-  __shared__ int s_tile;
-  const int nthr = blockDim.x;
-  const int nw = nthr >> 6;
+  extern __shared__ __align__(16) uint8_t fsm[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int Mk = ra.M * ra.k;
+  const int G = gridDim.x, wg = blockIdx.x;
   typedef __attribute__((address_space(3))) void lds_void;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(fsm);
+  uint16_t* hs = reinterpret_cast<uint16_t*>(fsm + fused_x_bytes(H));
+  float* red_gu = reinterpret_cast<float*>(fsm + fused_x_bytes(H) + (size_t)kFusedSlots * I * 2);
+  float* red_dn = red_gu + NUG * kFusedWaves * 32;
 
-  // ---------------- gate/up part ----------------
-  const bool has_gu = (int)blockIdx.x < n_gu;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(pool);
-  float* red = reinterpret_cast<float*>(pool + kXLdsBytes);  // [nw][64]
-  if (has_gu) {
+  // x into LDS, one 1 KiB run per wave instruction; the route table meanwhile
+  {
     const int n_x = H / 8;
     const int runs = (n_x + 63) / 64;
-    for (int run = wave; run < runs; run += nw) {
+    for (int run = wave; run < runs; run += kFusedWaves) {
       const int p = min(run * 64 + lane, n_x - 1);
       __builtin_amdgcn_global_load_lds(x + (size_t)p * 8, (lds_void*)(xs + (size_t)run * 512), 16, 0, 0);
     }
   }
-  route_prologue(rt, ra, rw, blockIdx.x == 0);
+  route_prologue(rt, ra, rw, wg == 0);
   const int nd = rt.nd;
-  const int gtile = (int)blockIdx.x % gu_tiles;
-  const int d = (int)blockIdx.x / gu_tiles;
-  if (has_gu && d < nd) {
-    const uint8_t* tbase = slots + (size_t)rt.dist_slot[d] * image_bytes + (size_t)gtile * gu_tile_bytes;
-    const int g0 = wave * ng / nw;
-    const int ngw = (wave + 1) * ng / nw - g0;
-    uint32_t s4[G];
-    uint4 c[4 * G];
-    // x has landed and is visible before any weight is requested, so that the compute waits for
-    // each weight block alone
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    load_tile_range<G>(reinterpret_cast<const uint4*>(tbase),
-                       reinterpret_cast<const uint32_t*>(tbase + (size_t)nb * 1024), nb, g0, ngw,
-                       lane, s4, c);
-    red[wave * 64 + lane] = dot_tile_lds<G>(c, s4, nb, g0, ngw, xs);
-    __syncthreads();
-    if (threadIdx.x < 32) {
-      const int row = threadIdx.x;
-      float g = 0.0f, u = 0.0f;
-      for (int w = 0; w < nw; ++w) {
-        g += red[w * 64 + row];
-        u += red[w * 64 + row + 32];
+  const int ugpe = I / 16;  // gate/up units per hot expert
+  const int Ug = nd * ugpe;
+  int gu_lo, ngu, dn_lo, ndn;
+  unit_share(wg, G, Ug, gu_lo, ngu);
+  unit_share(G - 1 - wg, G, H / 8, dn_lo, ndn);
+  // this wave's part of a unit: block pairs [gp0, gp0 + ngp) of a gate/up unit, (expert, step
+  // pair) entries [dq0, dq0 + ndq) of a down unit
+  const int np = (nb + 1) / 2;
+  const int gp0 = wave * np / kFusedWaves, ngp = (wave + 1) * np / kFusedWaves - gp0;
+  const int np2 = (ks + 1) / 2;
+  const int Ld = (nd > 0 ? nd : 1) * np2;
+  const int dq0 = wave * Ld / kFusedWaves, ndq = (wave + 1) * Ld / kFusedWaves - dq0;
+  const int half = lane >> 5;                          // gate/up: block 2p + half
+  const int ll = lane & 31;
+  const int gil = ll < 16 ? ll : ll + 16;              // + 16f: image lane (gate ll / up ll-16)
+  const int blk = (lane >> 3) & 3, r8 = lane & 7;      // down: step 2p + half, block 4s + blk
+  auto slot_of = [&](int d) { return nd > 0 ? rt.dist_slot[clampi(d, 0, nd - 1)] : 0; };
+
+  // x has landed and is visible before any weight is requested, so that the arithmetic waits
+  // for each weight load alone
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  uint32_t sg[NUG][NEG], sd[NUD][NED];
+  uint4 cg[NUG][NEG], cd[NUD][NED];
+  const uint8_t* gtb[NUG];
+  int gilf[NUG];
+#pragma unroll
+  for (int ug = 0; ug < NUG; ++ug) {
+    const int u = clampi(gu_lo + clampi(ug, 0, ngu - 1), 0, max(Ug - 1, 0));
+    const int d = u / ugpe, t2 = u - d * ugpe;
+    gtb[ug] = slots + (size_t)slot_of(d) * image_bytes + (size_t)(t2 >> 1) * gu_tile_bytes;
+    gilf[ug] = 16 * (t2 & 1) + gil;
+  }
+  const uint8_t* dtb[NUD][NED];
+  int dix[NUD][NED], dsw[NUD][NED];
+#pragma unroll
+  for (int ud = 0; ud < NUD; ++ud) {
+    const int u = clampi(dn_lo + clampi(ud, 0, ndn - 1), 0, H / 8 - 1);
+    const int il = 16 * blk + 8 * (u & 1) + r8;
+#pragma unroll
+    for (int e = 0; e < NED; ++e) {
+      const int q = dq0 + clampi(e, 0, ndq - 1);
+      const int ex = q / np2;
+      const int s = min(2 * (q - ex * np2) + half, ks - 1);
+      dtb[ud][e] = slots + (size_t)slot_of(ex) * image_bytes + gu_bytes + (size_t)(u >> 1) * dn_tile_bytes;
+      dix[ud][e] = s < full ? s * 64 + il : full * 64 + min(il, 16 * rem - 1);
+      dsw[ud][e] = (s >> 2) * 64 + il;
+    }
+  }
+  // The gate/up bytes are needed first, and requests compete in the memory system: the gate/up
+  // scale words and codes are requested now, the down ones by each wave once its gate/up
+  // arithmetic is done (their stream then overlaps the rest of gate/up and the hand-over of h).
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ug = 0; ug < NUG; ++ug)
+#pragma unroll
+    for (int e = 0; e < NEG; ++e) {
+      const int b = min(2 * (gp0 + clampi(e, 0, ngp - 1)) + half, nb - 1);
+      sg[ug][e] = reinterpret_cast<const uint32_t*>(gtb[ug] + (size_t)nb * 1024)[(b >> 2) * 64 + gilf[ug]];
+    }
+#pragma unroll
+  for (int ug = 0; ug < NUG; ++ug)
+#pragma unroll
+    for (int e = 0; e < NEG; ++e) {
+      const int b = min(2 * (gp0 + clampi(e, 0, ngp - 1)) + half, nb - 1);
+      cg[ug][e] = reinterpret_cast<const uint4*>(gtb[ug])[b * 64 + gilf[ug]];
+    }
+  __builtin_amdgcn_sched_barrier(0);
+  // The gate/up block scales as floats for the scaled converter (while the codes are in
+  // flight); zero for lanes whose block lies past K, which re-read a valid block and must add
+  // nothing.
+  float fg[NUG][NEG];
+#pragma unroll
+  for (int ug = 0; ug < NUG; ++ug)
+#pragma unroll
+    for (int e = 0; e < NEG; ++e) {
+      const int b = 2 * (gp0 + clampi(e, 0, ngp - 1)) + half;
+      fg[ug][e] = scale_or_zero(sg[ug][e], b & 3, b < nb);
+    }
+  // per hot expert t (< nd): its route; per route j: hot, weight, hot expert index (uniform)
+  int t_route[kFusedSlots], j_dist[kFusedSlots];
+  float j_w[kFusedSlots];
+  bool j_hot[kFusedSlots];
+#pragma unroll
+  for (int t = 0; t < kFusedSlots; ++t)
+    t_route[t] = __builtin_amdgcn_readfirstlane(t < nd ? rt.perm[rt.dist_off[t]] : -1);
+#pragma unroll
+  for (int j = 0; j < kFusedSlots; ++j) {
+    j_hot[j] = j < ra.k && __builtin_amdgcn_readfirstlane(rt.slot[min(j, ra.k - 1)]) >= 0;
+    j_w[j] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rt.w[min(j, ra.k - 1)])));
+    int dj = 0;
+#pragma unroll
+    for (int t = 0; t < kFusedSlots; ++t) dj = t_route[t] == j ? t : dj;
+    j_dist[j] = dj;
+  }
+
+  // ---- 1. gate/up units ----
+#pragma unroll
+  for (int ug = 0; ug < NUG; ++ug) {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < NEG; ++e) {
+      if (ug < ngu && e < ngp) {  // uniform
+        const int b = 2 * (gp0 + e) + half;
+        const uint4* a = reinterpret_cast<const uint4*>(xs + 32 * min(b, nb - 1));
+        block_dot_scaled(cg[ug][e], a[0], a[1], a[2], a[3], fg[ug][e], s0, s1);
       }
-      __hip_atomic_store(&hbuf[(size_t)rt.perm[rt.dist_off[d]] * I + gtile * 32 + row],
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float v = pair_sum32(s0 + s1);  // the other block of each pair
+    if (lane < 32) red_gu[(ug * kFusedWaves + wave) * 32 + lane] = v;
+  }
+  // this wave's gate/up bytes have all landed: its down bytes are requested now
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ud = 0; ud < NUD; ++ud)
+#pragma unroll
+    for (int e = 0; e < NED; ++e)
+      sd[ud][e] = reinterpret_cast<const uint32_t*>(dtb[ud][e] + dn_code_bytes)[dsw[ud][e]];
+#pragma unroll
+  for (int ud = 0; ud < NUD; ++ud)
+#pragma unroll
+    for (int e = 0; e < NED; ++e) cd[ud][e] = reinterpret_cast<const uint4*>(dtb[ud][e])[dix[ud][e]];
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  if ((int)threadIdx.x < NUG * 16) {
+    const int ug = threadIdx.x >> 4, r = threadIdx.x & 15;
+    if (ug < ngu) {
+      // (unrolled: the 32 LDS reads issue back to back)
+      float g = 0.0f, u = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kFusedWaves; ++w) {
+        g += red_gu[(ug * kFusedWaves + w) * 32 + r];
+        u += red_gu[(ug * kFusedWaves + w) * 32 + 16 + r];
+      }
+      const int uu = gu_lo + ug;
+      const int d = uu / ugpe, t2 = uu - d * ugpe;
+      int route = 0;
+#pragma unroll
+      for (int t = 0; t < kFusedSlots; ++t) route = d == t ? t_route[t] : route;
+      __hip_atomic_store(&hbuf[(size_t)route * I + (t2 >> 1) * 32 + 16 * (t2 & 1) + r],
                          (uint16_t)f32_to_bf16_bits(silu_f32(g) * u), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's h stores have completed
-    __syncthreads();                // ... and every thread's
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(&hand[(size_t)(d * kHandSub + gtile % kHandSub) * kHandStride], 1u,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (threadIdx.x == 0)
-    s_tile = (int)__hip_atomic_fetch_add(claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int tile = s_tile;
-  if (tile >= n_dnw) {
-    __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
+  if (ndn == 0) {  // no down unit here: the down loads (dummies) drain before the exit
+    __builtin_amdgcn_s_waitcnt(0);
     return;
   }
 
-  // ---------------- down part ----------------
-  const int KH = nw / kFusedSlots;              // K parts per expert
-  const int es = wave % kFusedSlots;            // this wave's hot expert slot
-  const int kh = wave / kFusedSlots;            // ... and K part
-  const int spw = dn_part_steps(ks, KH);        // <= TMX
-  const int s0 = kh * spw;
-  const uint8_t* tb = slots + (size_t)(nd == 0 ? 0 : rt.dist_slot[es < nd ? es : 0]) * image_bytes +
-                      gu_bytes + (size_t)tile * dn_tile_bytes;  // no expert: any valid slot
-  uint4 c[TMX];
-  uint32_t sw[TMX / 4];
-  dn_load_steps<TMX>(tb, dn_code_bytes, s0, ks, full, rem, nsw, lane, c, sw);
-  // wait for every gate/up tile of every hot expert
-  if (wave == 0) {
+  // ---- 2. h of every hot expert into LDS ----
+  {
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+    const int cpr = I / 8;  // 16-byte chunks per h row
+    const int nch = nd * cpr;
+    const uint16_t* src[kPollChunks];
+    int dst[kPollChunks];
+    bool done[kPollChunks];
+#pragma unroll
+    for (int i = 0; i < kPollChunks; ++i) {
+      const int c = (int)threadIdx.x + i * kFusedThreads;
+      done[i] = c >= nch;
+      const int cc = clampi(c, 0, max(nch - 1, 0));
+      const int d = cc / cpr;
+      int route = 0;
+#pragma unroll
+      for (int t = 0; t < kFusedSlots; ++t) route = d == t && t < nd ? t_route[t] : route;
+      src[i] = hbuf + (size_t)route * I + (size_t)(cc - d * cpr) * 8;
+      dst[i] = cc;
+    }
     bool late = false;
-    for (int c0 = 0; c0 < nd * kHandSub; c0 += 64) {
-      const int ci = c0 + lane;
-      const bool used = ci < nd * kHandSub;
-      const uint32_t target = (uint32_t)((gu_tiles - (ci % kHandSub) + kHandSub - 1) / kHandSub);
-      bool mine = !used;
-      int spins = 0;
-      while (true) {
-        if (!mine)
-          mine = __hip_atomic_load(&hand[(size_t)ci * kHandStride], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT) >= target;
-        if (__ballot(!mine) == 0ull) break;
-        if (++spins >= kHandSpins) {
-          late = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(8);
+    for (int spins = 0;; ++spins) {
+      u32x4_t v0, v1;
+      static_assert(kPollChunks == 2, "two chunks per gather round");
+      asm volatile(
+          "global_load_dwordx4 %0, %2, off sc1\n\t"
+          "global_load_dwordx4 %1, %3, off sc1\n\t"
+          "s_waitcnt vmcnt(0)"
+          : "=&v"(v0), "=&v"(v1)
+          : "v"(src[0]), "v"(src[1])
+          : "memory");
+      if (!done[0] && h_chunk_final(v0.x, v0.y, v0.z, v0.w)) {
+        reinterpret_cast<uint4*>(hs)[dst[0]] = make_uint4(v0.x, v0.y, v0.z, v0.w);
+        done[0] = true;
       }
+      if (!done[1] && h_chunk_final(v1.x, v1.y, v1.z, v1.w)) {
+        reinterpret_cast<uint4*>(hs)[dst[1]] = make_uint4(v1.x, v1.y, v1.z, v1.w);
+        done[1] = true;
+      }
+      if (__ballot(!(done[0] && done[1])) == 0ull) break;
+      if (spins + 1 >= kHandSpins) {
+        late = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(4);
     }
     if (late && lane == 0) atomicOr(&rw.meta[2], kErrHandoff);
   }
-  __syncthreads();  // also: every wave is done with the gate/up use of the pool
-  // every route's h into LDS through device-coherent loads, 16 bytes at a time (the wait
-  // inside also covers the down weights requested above)
-  uint16_t* hsm = reinterpret_cast<uint16_t*>(pool);  // [Mk][I]
-  const int n_h = Mk * I / 8;
-  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  for (int base = 0; base < n_h; base += 4 * nthr) {
-    int pidx[4];
-    const uint16_t* src[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pidx[i] = min(base + i * nthr + (int)threadIdx.x, n_h - 1);
-      src[i] = hbuf + (size_t)pidx[i] * 8;
-    }
-    u32x4_t v0, v1, v2, v3;
-    asm volatile(
-        "global_load_dwordx4 %0, %4, off sc1\n\t"
-        "global_load_dwordx4 %1, %5, off sc1\n\t"
-        "global_load_dwordx4 %2, %6, off sc1\n\t"
-        "global_load_dwordx4 %3, %7, off sc1\n\t"
-        "s_waitcnt vmcnt(0)"
-        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
-        : "v"(src[0]), "v"(src[1]), "v"(src[2]), "v"(src[3])
-        : "memory");
-    const u32x4_t vv[4] = {v0, v1, v2, v3};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      reinterpret_cast<uint4*>(hsm)[pidx[i]] = make_uint4(vv[i].x, vv[i].y, vv[i].z, vv[i].w);
-  }
-  float* parts = reinterpret_cast<float*>(pool + (size_t)Mk * I * 2);  // [Mk][KH][16]
   __syncthreads();
-  if (es < nd) {
-    // one token: every hot expert has one route
-    const int route = rt.perm[rt.dist_off[es]];
-    float acc = dn_route_dot<TMX>(c, sw, s0, spw, ks, nb_i, lane >> 4, hsm + (size_t)route * I);
-    acc = dn_row_sum(acc);
-    if (lane < kDnRows) parts[((size_t)route * KH + kh) * kDnRows + lane] = acc;
+
+  // ---- 3. down units and y ----
+  // the down block scales as floats (zero past K), as for gate/up
+  float fd[NUD][NED];
+#pragma unroll
+  for (int ud = 0; ud < NUD; ++ud)
+#pragma unroll
+    for (int e = 0; e < NED; ++e) {
+      const int q = dq0 + clampi(e, 0, ndq - 1);
+      const int ex = q / np2;
+      const int st = 2 * (q - ex * np2) + half;
+      fd[ud][e] = scale_or_zero(sd[ud][e], st & 3, st < ks && 4 * st + blk < nb_i);
+    }
+  // Entry by entry (one h block read serves every unit); a wave's entries are consecutive
+  // (expert, step pair)s, so they cover at most two hot experts: ex0 and ex0 + 1.
+  const int ex0 = dq0 / np2;
+  float accA[NUD], accB[NUD];
+#pragma unroll
+  for (int ud = 0; ud < NUD; ++ud) accA[ud] = accB[ud] = 0.0f;
+#pragma unroll
+  for (int e = 0; e < NED; ++e) {
+    const int q = dq0 + e;
+    const int ex = q / np2;
+    if (e < ndq && ex < nd) {  // uniform
+      const int st = 2 * (q - ex * np2) + half;
+      const uint4* hb = reinterpret_cast<const uint4*>(hs + (size_t)ex * I + 32 * min(4 * st + blk, nb_i - 1));
+      const uint4 h0 = hb[0], h1 = hb[1], h2 = hb[2], h3 = hb[3];
+#pragma unroll
+      for (int ud = 0; ud < NUD; ++ud) {
+        if (ud < ndn) {  // uniform
+          float t0 = 0.0f, t1 = 0.0f;
+          block_dot_scaled(cd[ud][e], h0, h1, h2, h3, fd[ud][e], t0, t1);
+          if (ex == ex0)
+            accA[ud] += t0 + t1;
+          else
+            accB[ud] += t0 + t1;
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // rows of each unit: the lanes of a row summed (8 per row), written per hot expert slot
+  // (zero for the slots this wave has no entry of)
+#pragma unroll
+  for (int ud = 0; ud < NUD; ++ud) {
+    if (ud < ndn) {
+      const float va = pair_sum32(pair_sum16(pair_sum8(accA[ud])));
+      const float vb = pair_sum32(pair_sum16(pair_sum8(accB[ud])));
+      if (lane < 8)
+#pragma unroll
+        for (int j = 0; j < kFusedSlots; ++j)
+          red_dn[((ud * kFusedSlots + j) * kFusedWaves + wave) * 8 + lane] =
+              j == ex0 ? va : (j == ex0 + 1 ? vb : 0.0f);
+    }
   }
   __syncthreads();
-  if (threadIdx.x < kDnRows) {
-    const int row = threadIdx.x;
-    float acc = 0.0f;
-    for (int j = 0; j < ra.k; ++j) {  // one token: route j = rank j
-      if (rt.slot[j] < 0) continue;
-      float p = 0.0f;
-      for (int h = 0; h < KH; ++h) p += parts[((size_t)j * KH + h) * kDnRows + row];
-      acc = fmaf(rt.w[j], p, acc);
+  // y: lane (unit, row, slot t) of wave 0 sums slot t of its row over the waves; the lanes of a
+  // row then meet in ascending route order (one token: route j = rank j)
+  static_assert(NUD * 8 * kFusedSlots <= 64, "one wave forms y");
+  if (wave == 0) {
+    const int t = lane & (kFusedSlots - 1);
+    const int rr = lane / kFusedSlots;  // unit * 8 + row
+    const int ud = rr >> 3, r = rr & 7;
+    float p = 0.0f;
+    if (ud < NUD)
+#pragma unroll
+      for (int w = 0; w < kFusedWaves; ++w) p += red_dn[((ud * kFusedSlots + t) * kFusedWaves + w) * 8 + r];
+    float pt[kFusedSlots];
+#pragma unroll
+    for (int i = 0; i < kFusedSlots; ++i) pt[i] = __shfl(p, (lane & ~(kFusedSlots - 1)) + i);
+    if (t == 0 && ud < ndn) {
+      float acc_y = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kFusedSlots; ++j) {
+        float pj = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kFusedSlots; ++i) pj = j_dist[j] == i ? pt[i] : pj;
+        if (j_hot[j]) acc_y = fmaf(j_w[j], pj, acc_y);
+      }
+      const int row = 8 * (dn_lo + ud) + r;
+      y[row] = acc_y;
+      // the residual reads x from its LDS copy
+      if (res.out != nullptr)
+        res.out[row] = (uint16_t)f32_to_bf16_bits(__uint_as_float((uint32_t)xs[row] << 16) + acc_y);
     }
-    y[(size_t)tile * kDnRows + row] = acc;
-    residual_store(res, (size_t)tile * kDnRows + row, acc);
   }
 }
 
@@ -1676,7 +1880,7 @@ __global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ x
 // Launchers (called from the host API after every argument has been validated)
 // =============================================================================================
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, uint32_t* zero, int n_zero, hipStream_t s) {
+                         int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s) {
   if (M >= kGroupedMinTokens)  // a dense GEMM: MFMA
     hipLaunchKernelGGL(k_router_grouped, dim3((M + kGemmTok - 1) / kGemmTok, (E + 63) / 64), dim3(256),
                        0, s, x, M, wr, bias, E, H, logits);
@@ -1685,8 +1889,8 @@ hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const flo
     switch (cpl) {
 #define MOE_RT(C)                                                                                  \
   case C:                                                                                          \
-    hipLaunchKernelGGL((k_router<C>), dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits, zero, \
-                       n_zero);                                                                    \
+    hipLaunchKernelGGL((k_router<C>), dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits, fill, \
+                       n_fill);                                                                    \
     break;
       MOE_RT(1) MOE_RT(2) MOE_RT(3) MOE_RT(4) MOE_RT(5) MOE_RT(6) MOE_RT(7) MOE_RT(8)
       MOE_RT(9) MOE_RT(10) MOE_RT(11) MOE_RT(12) MOE_RT(13) MOE_RT(14) MOE_RT(15) MOE_RT(16)
@@ -1869,93 +2073,111 @@ hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, siz
   return hipGetLastError();
 }
 
-// Resident workgroups of k_layer_decode<G, TMX> with nthr threads on the current device (its
-// whole grid must be resident), from the kernel's occupancy; computed once per device and shape
-// of workgroup.  (0 without a device: the fused path is then never chosen.)
-template <int G, int TMX>
-static int layer_decode_capacity(int nthr) {
-  static std::atomic<int> cache[16][kMaxWaves + 1];  // [device][waves]; 0 = not computed
+// Launch shape of k_layer_decode for a layer: grid, unit bounds per workgroup and wave, LDS.
+struct FusedCfg {
+  int G = 0, nug = 0, neg = 0, nud = 0, ned = 0;
+  size_t lds = 0;
+};
+
+static int fused_key(const FusedCfg& c) { return ((c.nug * 10 + c.neg) * 10 + c.nud) * 10 + c.ned; }
+
+#define MOE_LD_SWITCH(KEY, CALL)                                                                   \
+  switch (KEY) {                                                                                   \
+    case 1111: CALL(1, 1, 1, 1); break;                                                            \
+    case 2222: CALL(2, 2, 2, 2); break;                                                            \
+    case 3323: CALL(3, 3, 2, 3); break;                                                            \
+    default: break;                                                                                \
+  }
+
+// Compute units of the current device (0 without one: the fused path is then never chosen) and
+// whether k_layer_decode<key> fits one workgroup per compute unit; cached per device.
+static int device_cus() {
+  static std::atomic<int> cache[16];
   int dev = 0;
-  const int w = nthr / 64;
-  if (w < 1 || w > kMaxWaves || hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
-  int v = cache[dev][w].load(std::memory_order_relaxed);
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
   if (v == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_layer_decode<G, TMX>, nthr, 0) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    v = per_cu * cus > 0 ? per_cu * cus : -1;
-    cache[dev][w].store(v, std::memory_order_relaxed);
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    v = cus > 0 ? cus : -1;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
   return v > 0 ? v : 0;
 }
 
-// Steps per K part of the fused down part (whole scale words), and the template's bound.
-static int layer_decode_spw(const ImageLayout& L, const ExpertPlan& p) {
-  return dn_part_steps(L.dn_ks, p.gu_waves / kFusedSlots);
-}
-static int layer_decode_tmx(int spw) { return spw <= 4 ? 4 : spw <= 8 ? 8 : spw <= 12 ? 12 : 16; }
-
-static int layer_decode_grid(const ImageLayout& L, const ExpertPlan& p) {
-  const int n_gu = L.gu_tiles * p.nd_max;
-  return n_gu > L.dn_tiles ? n_gu : L.dn_tiles;
-}
-
-#define MOE_LD_SWITCH(G, TMX, CALL)                                                                \
-  switch ((G) * 100 + (TMX)) {                                                                     \
-    case 104: CALL(1, 4); break;                                                                   \
-    case 108: CALL(1, 8); break;                                                                   \
-    case 112: CALL(1, 12); break;                                                                  \
-    case 116: CALL(1, 16); break;                                                                  \
-    case 204: CALL(2, 4); break;                                                                   \
-    case 208: CALL(2, 8); break;                                                                   \
-    case 212: CALL(2, 12); break;                                                                  \
-    case 216: CALL(2, 16); break;                                                                  \
-    case 304: CALL(3, 4); break;                                                                   \
-    case 308: CALL(3, 8); break;                                                                   \
-    case 312: CALL(3, 12); break;                                                                  \
-    case 316: CALL(3, 16); break;                                                                  \
-    default: break;                                                                                \
+template <int NUG, int NEG, int NUD, int NED>
+static bool fused_resident(size_t lds) {
+  static std::atomic<int> cache[16];  // [device]: 0 unknown, 1 fits, -1 does not
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return false;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int per_cu = 0;
+    v = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_layer_decode<NUG, NEG, NUD, NED>,
+                                                     kFusedThreads, lds) == hipSuccess &&
+                per_cu >= 1
+            ? 1
+            : -1;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
+  return v > 0;
+}
 
-bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M) {
-  if (!(M == 1 && p.prologue && !p.grouped)) return false;
-  if (p.gu_groups < 1 || p.gu_groups > 3) return false;
-  if (p.gu_waves % kFusedSlots != 0) return false;
-  const int k_routes = p.nd_max;  // M = 1: every route is its own expert
-  if (k_routes > kFusedSlots) return false;  // a wave per hot expert in each K part
-  const int spw = layer_decode_spw(L, p);
-  if (spw > 16) return false;
-  const int KH = p.gu_waves / kFusedSlots;
-  const size_t need = (size_t)k_routes * L.I * 2 + (size_t)k_routes * KH * kDnRows * 4;
-  if (need > (size_t)kFusedPool || (size_t)L.H * 2 > (size_t)kXLdsBytes) return false;
-  if ((size_t)kXLdsBytes + (size_t)p.gu_waves * 64 * 4 > (size_t)kFusedPool) return false;
-  const int nthr = p.gu_waves * 64;
-  int cap = 0;
-#define MOE_LD_CAP(G, TMX) cap = layer_decode_capacity<G, TMX>(nthr)
-  MOE_LD_SWITCH(p.gu_groups, layer_decode_tmx(spw), MOE_LD_CAP)
-#undef MOE_LD_CAP
-  return layer_decode_grid(L, p) <= cap;
+static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, FusedCfg& c) {
+  if (k < 1 || k > kFusedSlots || p.grouped || !p.prologue) return false;
+  const int cus = device_cus();
+  const int ug_max = k * (L.I / 16), ud = L.H / 8;
+  c.G = std::min(cus, std::max(ug_max, ud));
+  if (c.G < 1) return false;
+  c.nug = (ug_max + c.G - 1) / c.G;
+  c.nud = (ud + c.G - 1) / c.G;
+  c.neg = ((L.nb_h + 1) / 2 + kFusedWaves - 1) / kFusedWaves;
+  c.ned = (k * ((L.dn_ks + 1) / 2) + kFusedWaves - 1) / kFusedWaves;
+  c.lds = fused_lds_bytes(L.H, L.I, c.nug, c.nud);
+  // a round of the h gather covers every hot expert's h
+  if ((size_t)k * L.I / 8 > (size_t)kPollChunks * kFusedThreads) return false;
+  // a wave's down entries (consecutive (expert, step pair)s) cover at most two hot experts
+  if (c.ned > (L.dn_ks + 1) / 2) return false;
+  if (c.lds + sizeof(RouteLds) > 64 * 1024) return false;
+  // the smallest instantiation that holds the bounds
+  const int keys[][4] = {{1, 1, 1, 1}, {2, 2, 2, 2}, {3, 3, 2, 3}};
+  for (const auto& kk : keys)
+    if (c.nug <= kk[0] && c.neg <= kk[1] && c.nud <= kk[2] && c.ned <= kk[3]) {
+      c.nug = kk[0];
+      c.neg = kk[1];
+      c.nud = kk[2];
+      c.ned = kk[3];
+      c.lds = fused_lds_bytes(L.H, L.I, c.nug, c.nud);
+      bool fits = false;
+#define MOE_LD_FIT(A, B, C, D) fits = fused_resident<A, B, C, D>(c.lds)
+      MOE_LD_SWITCH(fused_key(c), MOE_LD_FIT)
+#undef MOE_LD_FIT
+      return fits;
+    }
+  return false;
+}
+
+bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M, int k) {
+  FusedCfg c;
+  return M == 1 && fused_config(L, p, k, c);
 }
 
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                               const RouteWs& rw, uint16_t* hbuf, float* y, uint32_t* hand,
-                               Residual res, hipStream_t s) {
-  (void)M;
-  const int n_gu = L.gu_tiles * p.nd_max;
-  const dim3 g(layer_decode_grid(L, p)), b(p.gu_waves * 64);
+                               const RouteWs& rw, uint16_t* hbuf, float* y, Residual res,
+                               hipStream_t s) {
+  FusedCfg c;
+  if (M != 1 || !fused_config(L, p, ra.k, c)) return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
-#define MOE_LD(G, TMX)                                                                             \
+#define MOE_LD(A, B, C, D)                                                                         \
   do {                                                                                             \
-    hipLaunchKernelGGL((k_layer_decode<G, TMX>), g, b, 0, s, x, H, I, slots, L.image_bytes,        \
-                       L.gu_tile_bytes, L.nb_h, L.ng_h, L.gu_tiles, n_gu, L.dn_tiles, L.gu_bytes,   \
-                       L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks, L.dn_full, L.dn_rem,              \
-                       L.dn_scale_words, L.nb_i, ra, rw, hbuf, y, hand,                            \
-                       hand + (size_t)p.nd_max * kHandSub * kHandStride, res);                      \
+    hipLaunchKernelGGL((k_layer_decode<A, B, C, D>), dim3(c.G), dim3(kFusedThreads), c.lds, s, x,  \
+                       H, I, slots, L.image_bytes, L.gu_tile_bytes, L.nb_h, L.gu_bytes,            \
+                       L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks, L.dn_full, L.dn_rem, L.nb_i, ra, \
+                       rw, hbuf, y, res);                                                          \
     e = hipGetLastError();                                                                         \
   } while (0)
-  MOE_LD_SWITCH(p.gu_groups, layer_decode_tmx(layer_decode_spw(L, p)), MOE_LD)
+  MOE_LD_SWITCH(fused_key(c), MOE_LD)
 #undef MOE_LD
   return e;
 }

@@ -155,11 +155,12 @@ moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_
  * top-k, slot resolve and bucketing run inside the expert kernels (three launches: router
  * GEMV, gate/up, down + combine).  For one token (M = 1, top_k <= 4) of the shapes the fused
  * kernel is built for (moe_layer_launches reports it; GPT-OSS-20B's is one) gate/up and down
- * are one launch: down workgroups fetch their
- * weights while gate/up still streams and take h over through per-expert arrival counters
- * in the workspace (two launches in all; the environment variable MOE_DECODE_UNFUSED=1, read
- * once per process, keeps three).  Same arguments, outputs and numerics as the two calls,
- * bitwise, on every path; topk_ids [M,k] and topk_w [M,k] are written too.
+ * are one launch of one workgroup per compute unit, h handed from gate/up to down by value
+ * through the workspace (the router kernel marks it unwritten first): two launches in all;
+ * the environment variable MOE_DECODE_UNFUSED=1, read once per process, keeps three.  Same
+ * arguments and outputs as the two calls; the numerics are bitwise theirs, except on the
+ * fused path, whose sums over K run in another order (agreement within 1e-4 relative L2);
+ * topk_ids [M,k] and topk_w [M,k] are written too (bitwise on every path).
  * --------------------------------------------------------------------------------------- */
 moe_status moe_layer_forward(const moe_shape* shape, const uint16_t* x, int32_t M,
                              const uint16_t* w_router, const float* router_bias,
