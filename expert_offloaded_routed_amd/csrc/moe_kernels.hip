@@ -1256,6 +1256,29 @@ __device__ __forceinline__ void block_dot_scaled(const uint4 c, const uint4 a0, 
   }
 }
 
+// One 32-element block (16 code bytes) as 16 bf16 pairs, the block scale folded in (exact).
+__device__ __forceinline__ void block_to_bf16(const uint4 c, float sc, bf16x2_t (&w)[16]) {
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[4 * j + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 0);
+    w[4 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 1);
+    w[4 * j + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 2);
+    w[4 * j + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 3);
+  }
+}
+// ... and its dot with 32 bf16 activations, on two accumulation chains (even / odd pairs).
+__device__ __forceinline__ void block_dot_bf16(const bf16x2_t (&w)[16], const uint4 a0, const uint4 a1,
+                                               const uint4 a2, const uint4 a3, float& s0, float& s1) {
+  const uint32_t aw[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                           a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(aw[i]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(w[i + 1], as_bf16x2(aw[i + 1]), s1, false);
+  }
+}
+
 // LDS of the kernel past the route table: x runs (1 KiB each), h rows of the hot experts, the
 // gate/up sums [NUG][waves][32] and the down sums [NUD][slots][waves][8].
 __host__ __device__ __forceinline__ size_t fused_x_bytes(int H) { return (size_t)((H / 8 + 63) / 64) * 1024; }
@@ -1343,7 +1366,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   }
   // The gate/up bytes are needed first, and requests compete in the memory system: the gate/up
   // scale words and codes are requested now, the down ones by each wave once its gate/up
-  // arithmetic is done (their stream then overlaps the rest of gate/up and the hand-over of h).
+  // arithmetic is done (their stream then overlaps the rest of gate/up and the hand-over).
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ug = 0; ug < NUG; ++ug)
@@ -1404,7 +1427,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     const float v = pair_sum32(s0 + s1);  // the other block of each pair
     if (lane < 32) red_gu[(ug * kFusedWaves + wave) * 32 + lane] = v;
   }
-  // this wave's gate/up bytes have all landed: its down bytes are requested now
+  // this wave's gate/up bytes have all landed: its down bytes are requested now (the requests
+  // of the waves still waiting for gate/up bytes were issued before them)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int ud = 0; ud < NUD; ++ud)
@@ -1441,6 +1465,22 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     __builtin_amdgcn_s_waitcnt(0);
     return;
   }
+
+  // The down weights (in flight since this wave's gate/up arithmetic) are decoded to bf16 while
+  // h is still being formed elsewhere, so that only the products remain after the gather.
+  bf16x2_t wd[NUD][NED][16];
+#pragma unroll
+  for (int ud = 0; ud < NUD; ++ud)
+#pragma unroll
+    for (int e = 0; e < NED; ++e) {
+      const int q = dq0 + clampi(e, 0, ndq - 1);
+      const int ex = q / np2;
+      const int st = 2 * (q - ex * np2) + half;
+      block_to_bf16(cd[ud][e], scale_or_zero(sd[ud][e], st & 3, st < ks && 4 * st + blk < nb_i), wd[ud][e]);
+      // (here, not sunk into the products after the gather)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(wd[ud][e][i]));
+    }
 
   // ---- 2. h of every hot expert into LDS ----
   {
@@ -1493,17 +1533,6 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   __syncthreads();
 
   // ---- 3. down units and y ----
-  // the down block scales as floats (zero past K), as for gate/up
-  float fd[NUD][NED];
-#pragma unroll
-  for (int ud = 0; ud < NUD; ++ud)
-#pragma unroll
-    for (int e = 0; e < NED; ++e) {
-      const int q = dq0 + clampi(e, 0, ndq - 1);
-      const int ex = q / np2;
-      const int st = 2 * (q - ex * np2) + half;
-      fd[ud][e] = scale_or_zero(sd[ud][e], st & 3, st < ks && 4 * st + blk < nb_i);
-    }
   // Entry by entry (one h block read serves every unit); a wave's entries are consecutive
   // (expert, step pair)s, so they cover at most two hot experts: ex0 and ex0 + 1.
   const int ex0 = dq0 / np2;
@@ -1522,7 +1551,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       for (int ud = 0; ud < NUD; ++ud) {
         if (ud < ndn) {  // uniform
           float t0 = 0.0f, t1 = 0.0f;
-          block_dot_scaled(cd[ud][e], h0, h1, h2, h3, fd[ud][e], t0, t1);
+          block_dot_bf16(wd[ud][e], h0, h1, h2, h3, t0, t1);
           if (ex == ex0)
             accA[ud] += t0 + t1;
           else
