@@ -76,9 +76,20 @@ inline ImageLayout image_layout(int H, int I) {
   return L;
 }
 
+// Calls with at least this many tokens take the grouped GEMM path (and the MFMA router).
+constexpr int kGroupedMinTokens = 64;
+// The MFMA router splits K over this many workgroups (for at most kRouterMaxE experts); the
+// logit row of a token is then held as that many partial sums M*E floats apart (the first
+// with the bias), summed in ascending order by the top-k.
+constexpr int kRouterParts = 4;
+constexpr int kRouterMaxE = 512;
+__host__ __device__ inline int router_parts(int M, int E) {
+  return M >= kGroupedMinTokens && E <= kRouterMaxE ? kRouterParts : 1;
+}
+
 // Workspace: per-call arrays sized for M tokens (nothing survives between calls).
 struct WsLayout {
-  size_t logits;         // f32 [M][E]
+  size_t logits;         // f32 [router_parts(M, E)][M][E]
   size_t route_slot;     // i32 [M*k]
   size_t counts;         // i32 [E]
   size_t offsets;        // i32 [E+1]
@@ -109,7 +120,7 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   const size_t Mk = (size_t)M * k;
   const size_t nd = Mk < (size_t)E ? Mk : (size_t)E;
   size_t o = 0;
-  W.logits = o;      o = align256(o + 4 * (size_t)M * E);
+  W.logits = o;      o = align256(o + 4 * (size_t)router_parts(M, E) * M * E);
   W.route_slot = o;  o = align256(o + 4 * Mk);
   W.counts = o;      o = align256(o + 4 * (size_t)E);
   W.offsets = o;     o = align256(o + 4 * ((size_t)E + 1));
@@ -183,6 +194,7 @@ hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uin
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                                const RouteWs& rw, uint16_t* hbuf, float* y, Residual res,
                                hipStream_t s);
+// logits: router_parts(M, E) partial rows per token (see kRouterParts).
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,
                               const int32_t* e2s, const BucketOut& o, hipStream_t s);

@@ -76,10 +76,21 @@ __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, i
 // cost).  Larger E: k rounds of a wave argmax over PL logits per lane.
 __device__ __forceinline__ float rank_key(float v) { return v != v ? -INFINITY : v; }
 
-__device__ void topk_rank(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
-                          float* __restrict__ w) {
+// Logit e of a row held as P partial sums P_STRIDE floats apart, summed in ascending order.
+template <int P>
+__device__ __forceinline__ float logit_at(const float* __restrict__ lrow, size_t pstride, int e) {
+  float v = lrow[e];
+#pragma unroll
+  for (int z = 1; z < P; ++z) v += lrow[z * pstride + e];
+  return v;
+}
+
+template <int P>
+__device__ void topk_rank(const float* __restrict__ lrow, size_t pstride, int E, int k,
+                          int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
-  const float lv = lrow[min(lane, E - 1)];  // unconditional load (a load in a branch is waited for alone)
+  // unconditional loads (a load in a branch is waited for alone)
+  const float lv = logit_at<P>(lrow, pstride, min(lane, E - 1));
   const float v = lane < E ? rank_key(lv) : -INFINITY;
   int rank = 0;
   for (int j = 0; j < E; ++j) {
@@ -135,16 +146,16 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return max_u64(a, b);
 }
 
-template <int PL>
-__device__ void topk_argmax(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
-                            float* __restrict__ w) {
+template <int PL, int P>
+__device__ void topk_argmax(const float* __restrict__ lrow, size_t pstride, int E, int k,
+                            int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   float lv[PL];
   uint64_t key[PL];
   // every load issued before any is used (clamped in range; loads in a branch would each be
   // waited for alone); slots past E get key 0, below every real key
 #pragma unroll
-  for (int i = 0; i < PL; ++i) lv[i] = lrow[min(lane + 64 * i, E - 1)];
+  for (int i = 0; i < PL; ++i) lv[i] = logit_at<P>(lrow, pstride, min(lane + 64 * i, E - 1));
 #pragma unroll
   for (int i = 0; i < PL; ++i) key[i] = lane + 64 * i < E ? rank_key64(lv[i], lane + 64 * i) : 0ull;
   uint64_t mine = 0ull;  // lane j < k: the j-th key
@@ -166,13 +177,21 @@ __device__ void topk_argmax(const float* __restrict__ lrow, int E, int k, int32_
   }
 }
 
+// The logit row may be held as P partial sums pstride floats apart (the K-split router GEMM).
+// (Split rows are produced for at most kRouterMaxE experts.)
+template <int P>
+__device__ void topk_token_p(const float* __restrict__ lrow, size_t pstride, int E, int k,
+                             int32_t* __restrict__ ids, float* __restrict__ w) {
+  if (E <= 64) topk_rank<P>(lrow, pstride, E, k, ids, w);
+  else if (E <= 128) topk_argmax<2, P>(lrow, pstride, E, k, ids, w);
+  else if (E <= 256) topk_argmax<4, P>(lrow, pstride, E, k, ids, w);
+  else if (P > 1 || E <= 512) topk_argmax<8, P>(lrow, pstride, E, k, ids, w);
+  else topk_argmax<16, P>(lrow, pstride, E, k, ids, w);
+}
 __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
-                           float* __restrict__ w) {
-  if (E <= 64) topk_rank(lrow, E, k, ids, w);
-  else if (E <= 128) topk_argmax<2>(lrow, E, k, ids, w);
-  else if (E <= 256) topk_argmax<4>(lrow, E, k, ids, w);
-  else if (E <= 512) topk_argmax<8>(lrow, E, k, ids, w);
-  else topk_argmax<16>(lrow, E, k, ids, w);
+                           float* __restrict__ w, int parts = 1, size_t pstride = 0) {
+  if (parts == kRouterParts) topk_token_p<kRouterParts>(lrow, pstride, E, k, ids, w);
+  else topk_token_p<1>(lrow, pstride, E, k, ids, w);
 }
 
 // =============================================================================================
@@ -330,7 +349,8 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucket(
   if (logits != nullptr) {
     const int nw = blockDim.x >> 6;
     for (int m = blockIdx.x * nw + (threadIdx.x >> 6); m < M; m += nw * gridDim.x)
-      topk_token(logits + (size_t)m * E, E, k, topk_ids + (size_t)m * k, topk_w + (size_t)m * k);
+      topk_token(logits + (size_t)m * E, E, k, topk_ids + (size_t)m * k, topk_w + (size_t)m * k,
+                 router_parts(M, E), (size_t)M * E);
     if (!do_bucket) return;
     __syncthreads();  // this workgroup's ids are visible to it from here on
   }
@@ -533,7 +553,7 @@ __device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs&
 // own distinct expert, placed in ascending expert id by a count over the k routes.
 __device__ __forceinline__ void route_token_wave(RouteLds& rt, const RouteArgs& a) {
   const int lane = threadIdx.x & 63;
-  topk_token(a.logits, a.E, a.k, rt.ids, rt.w);
+  topk_token_p<1>(a.logits, 0, a.E, a.k, rt.ids, rt.w);
   const bool route = lane < a.k;
   const int e = route ? rt.ids[lane] : 0;
   const int ec = min(max(e, 0), a.E - 1);
@@ -664,7 +684,7 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
   } else {
     if (a.logits != nullptr) {
       for (int m = tid >> 6; m < a.M; m += nw)
-        topk_token(a.logits + (size_t)m * a.E, a.E, a.k, rt.ids + m * a.k, rt.w + m * a.k);
+        topk_token_p<1>(a.logits + (size_t)m * a.E, 0, a.E, a.k, rt.ids + m * a.k, rt.w + m * a.k);
     } else {
       for (int r = tid; r < Mk; r += blockDim.x) {
         rt.ids[r] = a.ids_in[r];
@@ -1626,7 +1646,6 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kGroupedMinTokens = 64;        // calls with at least this many tokens take this path
 constexpr int kGemmTok = 64;                 // routes per pass: 4 MFMA tiles of 16
 static_assert(kGemmTok == kItemRoutes, "one work item is one pass of a grouped GEMM workgroup");
 constexpr int kGemmKC = 4;                   // K blocks (of 32) per chunk
@@ -1809,7 +1828,11 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
   for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) gr.row[i] = x + (size_t)min(tok0 + i, M - 1) * H;
   __syncthreads();
   const int ntt = (min(kGemmTok, M - tok0) + 15) >> 4;
-  const int nkc = (H / 32 + kGemmKC - 1) / kGemmKC;
+  // this workgroup's share of K: chunks [kc0, kc1) of kGemmKC blocks
+  const int nkc_all = (H / 32 + kGemmKC - 1) / kGemmKC;
+  const int kc0 = blockIdx.z * nkc_all / gridDim.z, kc1 = (blockIdx.z + 1) * nkc_all / gridDim.z;
+  const int nkc = kc1 - kc0;
+  logits += (size_t)blockIdx.z * M * E;
   f32x4_t acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1820,15 +1843,15 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
     for (int j = 0; j < kGemmKC; ++j)
       bn[j] = *reinterpret_cast<const uint4*>(brow + min((kc * kGemmKC + j) * 32, H - 32));
   };
-  gemm_load_rows(gr, 0, H, xv);
-  load_b(0);
-  for (int kc = 0; kc < nkc; ++kc) {
-    const int buf = kc & 1;
+  gemm_load_rows(gr, kc0, H, xv);
+  load_b(kc0);
+  for (int kc = kc0; kc < kc1; ++kc) {
+    const int buf = (kc - kc0) & 1;
     gemm_store_rows(xb[buf], xv);
     uint4 bc[kGemmKC];
 #pragma unroll
     for (int j = 0; j < kGemmKC; ++j) bc[j] = bn[j];
-    if (kc + 1 < nkc) {
+    if (kc + 1 < kc1) {
       gemm_load_rows(gr, kc + 1, H, xv);
       load_b(kc + 1);
     }
@@ -1846,8 +1869,9 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
       }
     }
   }
+  (void)nkc;
   if (e < E) {
-    const float b = bias != nullptr ? bias[e] : 0.0f;
+    const float b = bias != nullptr && blockIdx.z == 0 ? bias[e] : 0.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -1911,7 +1935,7 @@ __global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ x
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
                          int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s) {
   if (M >= kGroupedMinTokens)  // a dense GEMM: MFMA
-    hipLaunchKernelGGL(k_router_grouped, dim3((M + kGemmTok - 1) / kGemmTok, (E + 63) / 64), dim3(256),
+    hipLaunchKernelGGL(k_router_grouped, dim3((M + kGemmTok - 1) / kGemmTok, (E + 63) / 64, router_parts(M, E)), dim3(256),
                        0, s, x, M, wr, bias, E, H, logits);
   else {
     const int cpl = (H / 8 + 63) / 64;
