@@ -536,6 +536,80 @@ def test_fused_decode_consecutive_tokens_and_maps(gptoss):
                 assert cc == len(ref["cold_routes"])
 
 
+def test_fused_decode_small_shape_and_graph_replays(tiny, gptoss):
+    """The fused one-token kernel on a second shape (H = 256, I = 512, E = 8, k = 2: one unit of
+    each kind per workgroup) against the oracle and the two-call path, over tokens whose top-k
+    experts are all hot, partly cold or all cold; then one-token layer calls of both shapes
+    captured in a HIP graph and replayed, with eager calls between the replays (the h rows are
+    re-marked by the router of every call), each replay equal to the eager result."""
+    wl, shape = tiny.wl, tiny.shape
+    assert B.moe_layer_launches(shape, 1) == 2
+    wr = _dev(tiny.wr)
+    E = wl.n_experts
+    part = np.arange(E, dtype=np.int32)
+    part[1::2] = -1
+    a, b = L.Buffers(shape, 1), L.Buffers(shape, 1)
+    for name, e2s_np in (("identity", None), ("odd experts cold", part),
+                         ("all cold", np.full(E, -1, np.int32))):
+        e2s = None if e2s_np is None else _dev(e2s_np)
+        for t in range(8):
+            say("fused decode, small shape:", name, "token", t)
+            xn = synthetic.activations(wl, 1, 900 + t)
+            x = _dev(xn)
+            B.moe_layer_forward(shape, x, 1, wr, None, e2s, tiny.slots, a.ids, a.w, a.y,
+                                a.cold_count, a.cold_routes, a.ws)
+            B.moe_route(shape, x, 1, wr, None, b.ids, b.w, b.ws)
+            B.moe_experts_forward(shape, x, 1, b.ids, b.w, e2s, tiny.slots, b.y, b.cold_count,
+                                  b.cold_routes, b.ws)
+            torch.cuda.synchronize()
+            assert torch.equal(a.ids[:1], b.ids[:1]) and torch.equal(a.w[:1], b.w[:1])
+            paths_agree(a.y[:1].cpu().numpy(), b.y[:1].cpu().numpy(), name)
+            _, ids_ref, w_ref = compare_routes(a.ids[:1].cpu().numpy(), a.w[:1].cpu().numpy(),
+                                               O.router_logits(xn, tiny.wr), wl.top_k)
+            ref = O.layer_forward(xn, ids_ref, w_ref, tiny.experts, e2s_np)
+            cc = int(a.cold_count.item())
+            assert cc == len(ref["cold_routes"])
+            if name == "all cold":
+                assert not a.y[:1].any()
+            else:
+                close_enough(a.y[:1].cpu().numpy(), ref["y_hot"], f"fused small {name} {t}")
+    for lay in (tiny, gptoss):
+        shp = lay.shape
+        w_dev = _dev(lay.wr)
+        T = 4
+        xs = [_dev(synthetic.activations(lay.wl, 1, 950 + t)) for t in range(T)]
+        bufs = [L.Buffers(shp, 1) for _ in range(T)]
+        ws = L.Buffers(shp, 1).ws  # one workspace shared by the calls, as in a layer loop
+
+        def calls(stream=None):
+            for t in range(T):
+                kw = {} if stream is None else {"stream": stream}
+                B.moe_layer_forward(shp, xs[t], 1, w_dev, None, None, lay.slots, bufs[t].ids,
+                                    bufs[t].w, bufs[t].y, None, None, ws, **kw)
+
+        say("fused graph:", lay.wl.name, "eager reference")
+        calls()
+        torch.cuda.synchronize()
+        y_eager = [bf.y[:1].clone() for bf in bufs]
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                calls(s)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            say("fused graph:", lay.wl.name, "replay", rep)
+            for bf in bufs:
+                bf.y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            for t in range(T):
+                assert torch.equal(bufs[t].y[:1], y_eager[t]), (lay.wl.name, rep, t)
+            calls()  # eager calls on the same workspace between the replays
+            torch.cuda.synchronize()
+
+
 def test_layer_forward_residual_equals_layer_plus_residual(gptoss, tiny):
     """moe_layer_forward_residual == moe_layer_forward + moe_residual_bf16, bitwise, on the fused
     one-token path, the GEMV path and the grouped GEMM path, in place and into another buffer."""
