@@ -1226,7 +1226,7 @@ __global__ __launch_bounds__(256) void k_down_mx(
 // out of it flags kErrHandoff in meta[2] (it cannot happen with the grid resident).
 constexpr int kFusedWaves = 16;
 constexpr int kFusedThreads = kFusedWaves * 64;
-constexpr int kFusedSlots = 4;      // hot experts of the token at most
+constexpr int kFusedMaxK = 16;      // routes (hot experts) of the token at most
 constexpr int kHandSpins = 1 << 13; // gather rounds at most (each ~1 us: a round trip + sleep)
 constexpr int kPollChunks = 2;      // 16-byte chunks of h per thread in the gather
 constexpr uint32_t kHSentinel = 0xFFFFu;
@@ -1299,12 +1299,13 @@ __device__ __forceinline__ void block_dot_bf16(const bf16x2_t (&w)[16], const ui
   }
 }
 
-// LDS of the kernel past the route table: x runs (1 KiB each), h rows of the hot experts, the
-// gate/up sums [NUG][waves][32] and the down sums [NUD][slots][waves][8].
+// LDS of the kernel past the route table: x runs (1 KiB each), h rows of the k routes, the
+// gate/up sums [NUG][waves][32], the down sums [NUD][k][waves][8] and their wave totals
+// [NUD][k][8].
 __host__ __device__ __forceinline__ size_t fused_x_bytes(int H) { return (size_t)((H / 8 + 63) / 64) * 1024; }
-__host__ __device__ __forceinline__ size_t fused_lds_bytes(int H, int I, int nug, int nud) {
-  return fused_x_bytes(H) + (size_t)kFusedSlots * I * 2 + (size_t)nug * kFusedWaves * 32 * 4 +
-         (size_t)nud * kFusedSlots * kFusedWaves * 8 * 4;
+__host__ __device__ __forceinline__ size_t fused_lds_bytes(int H, int I, int k, int nug, int nud) {
+  return fused_x_bytes(H) + (size_t)k * I * 2 + (size_t)nug * kFusedWaves * 32 * 4 +
+         (size_t)nud * k * (kFusedWaves + 1) * 8 * 4;
 }
 
 template <int NUG, int NEG, int NUD, int NED>
@@ -1314,15 +1315,18 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     size_t dn_code_bytes, int ks, int full, int rem, int nb_i, RouteArgs ra, RouteWs rw,
     uint16_t* __restrict__ hbuf, float* __restrict__ y, Residual res) {
   __shared__ RouteLds rt;
+  __shared__ int s_dist_of_route[kFusedMaxK];  // one token: route j -> its hot expert index
   extern __shared__ __align__(16) uint8_t fsm[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, wg = blockIdx.x;
+  const int K = ra.k;
   typedef __attribute__((address_space(3))) void lds_void;
   uint16_t* xs = reinterpret_cast<uint16_t*>(fsm);
   uint16_t* hs = reinterpret_cast<uint16_t*>(fsm + fused_x_bytes(H));
-  float* red_gu = reinterpret_cast<float*>(fsm + fused_x_bytes(H) + (size_t)kFusedSlots * I * 2);
-  float* red_dn = red_gu + NUG * kFusedWaves * 32;
+  float* red_gu = reinterpret_cast<float*>(fsm + fused_x_bytes(H) + (size_t)K * I * 2);
+  float* red_dn = red_gu + NUG * kFusedWaves * 32;       // [NUD][K][waves][8]
+  float* sum_dn = red_dn + NUD * K * kFusedWaves * 8;    // [NUD][K][8]
 
   // x into LDS, one 1 KiB run per wave instruction; the route table meanwhile
   {
@@ -1414,22 +1418,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       const int b = 2 * (gp0 + clampi(e, 0, ngp - 1)) + half;
       fg[ug][e] = scale_or_zero(sg[ug][e], b & 3, b < nb);
     }
-  // per hot expert t (< nd): its route; per route j: hot, weight, hot expert index (uniform)
-  int t_route[kFusedSlots], j_dist[kFusedSlots];
-  float j_w[kFusedSlots];
-  bool j_hot[kFusedSlots];
-#pragma unroll
-  for (int t = 0; t < kFusedSlots; ++t)
-    t_route[t] = __builtin_amdgcn_readfirstlane(t < nd ? rt.perm[rt.dist_off[t]] : -1);
-#pragma unroll
-  for (int j = 0; j < kFusedSlots; ++j) {
-    j_hot[j] = j < ra.k && __builtin_amdgcn_readfirstlane(rt.slot[min(j, ra.k - 1)]) >= 0;
-    j_w[j] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(rt.w[min(j, ra.k - 1)])));
-    int dj = 0;
-#pragma unroll
-    for (int t = 0; t < kFusedSlots; ++t) dj = t_route[t] == j ? t : dj;
-    j_dist[j] = dj;
-  }
+  // hot expert t (< nd) -> its route (one token: every hot route is its own expert), and back
+  if ((int)threadIdx.x < nd) s_dist_of_route[rt.perm[rt.dist_off[threadIdx.x]]] = threadIdx.x;
 
   // ---- 1. gate/up units ----
 #pragma unroll
@@ -1473,9 +1463,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       }
       const int uu = gu_lo + ug;
       const int d = uu / ugpe, t2 = uu - d * ugpe;
-      int route = 0;
-#pragma unroll
-      for (int t = 0; t < kFusedSlots; ++t) route = d == t ? t_route[t] : route;
+      const int route = rt.perm[rt.dist_off[d]];
       __hip_atomic_store(&hbuf[(size_t)route * I + (t2 >> 1) * 32 + 16 * (t2 & 1) + r],
                          (uint16_t)f32_to_bf16_bits(silu_f32(g) * u), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
@@ -1516,9 +1504,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       done[i] = c >= nch;
       const int cc = clampi(c, 0, max(nch - 1, 0));
       const int d = cc / cpr;
-      int route = 0;
-#pragma unroll
-      for (int t = 0; t < kFusedSlots; ++t) route = d == t && t < nd ? t_route[t] : route;
+      const int route = nd > 0 ? rt.perm[rt.dist_off[d]] : 0;
       src[i] = hbuf + (size_t)route * I + (size_t)(cc - d * cpr) * 8;
       dst[i] = cc;
     }
@@ -1589,36 +1575,27 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       const float va = pair_sum32(pair_sum16(pair_sum8(accA[ud])));
       const float vb = pair_sum32(pair_sum16(pair_sum8(accB[ud])));
       if (lane < 8)
-#pragma unroll
-        for (int j = 0; j < kFusedSlots; ++j)
-          red_dn[((ud * kFusedSlots + j) * kFusedWaves + wave) * 8 + lane] =
-              j == ex0 ? va : (j == ex0 + 1 ? vb : 0.0f);
+        for (int j = 0; j < K; ++j)
+          red_dn[((ud * K + j) * kFusedWaves + wave) * 8 + lane] = j == ex0 ? va : (j == ex0 + 1 ? vb : 0.0f);
     }
   }
   __syncthreads();
-  // y: lane (unit, row, slot t) of wave 0 sums slot t of its row over the waves; the lanes of a
-  // row then meet in ascending route order (one token: route j = rank j)
-  static_assert(NUD * 8 * kFusedSlots <= 64, "one wave forms y");
-  if (wave == 0) {
-    const int t = lane & (kFusedSlots - 1);
-    const int rr = lane / kFusedSlots;  // unit * 8 + row
-    const int ud = rr >> 3, r = rr & 7;
-    float p = 0.0f;
-    if (ud < NUD)
+  // every (unit, hot expert, row) over the waves, then y for each row: the routes in ascending
+  // order (one token: route j = rank j)
+  for (int i = threadIdx.x; i < NUD * K * 8; i += kFusedThreads) {
+    const int r = i & 7, uj = i >> 3;  // uj = unit * K + hot expert
+    float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kFusedWaves; ++w) p += red_dn[((ud * kFusedSlots + t) * kFusedWaves + w) * 8 + r];
-    float pt[kFusedSlots];
-#pragma unroll
-    for (int i = 0; i < kFusedSlots; ++i) pt[i] = __shfl(p, (lane & ~(kFusedSlots - 1)) + i);
-    if (t == 0 && ud < ndn) {
+    for (int w = 0; w < kFusedWaves; ++w) v += red_dn[(uj * kFusedWaves + w) * 8 + r];
+    sum_dn[i] = v;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < NUD * 8) {
+    const int ud = threadIdx.x >> 3, r = threadIdx.x & 7;
+    if (ud < ndn) {
       float acc_y = 0.0f;
-#pragma unroll
-      for (int j = 0; j < kFusedSlots; ++j) {
-        float pj = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kFusedSlots; ++i) pj = j_dist[j] == i ? pt[i] : pj;
-        if (j_hot[j]) acc_y = fmaf(j_w[j], pj, acc_y);
-      }
+      for (int j = 0; j < K; ++j)
+        if (rt.slot[j] >= 0) acc_y = fmaf(rt.w[j], sum_dn[(ud * K + s_dist_of_route[j]) * 8 + r], acc_y);
       const int row = 8 * (dn_lo + ud) + r;
       y[row] = acc_y;
       // the residual reads x from its LDS copy
@@ -2137,6 +2114,7 @@ static int fused_key(const FusedCfg& c) { return ((c.nug * 10 + c.neg) * 10 + c.
 #define MOE_LD_SWITCH(KEY, CALL)                                                                   \
   switch (KEY) {                                                                                   \
     case 1111: CALL(1, 1, 1, 1); break;                                                            \
+    case 2212: CALL(2, 2, 1, 2); break;                                                            \
     case 2222: CALL(2, 2, 2, 2); break;                                                            \
     case 3323: CALL(3, 3, 2, 3); break;                                                            \
     default: break;                                                                                \
@@ -2177,7 +2155,7 @@ static bool fused_resident(size_t lds) {
 }
 
 static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, FusedCfg& c) {
-  if (k < 1 || k > kFusedSlots || p.grouped || !p.prologue) return false;
+  if (k < 1 || k > kFusedMaxK || p.grouped || !p.prologue) return false;
   const int cus = device_cus();
   const int ug_max = k * (L.I / 16), ud = L.H / 8;
   c.G = std::min(cus, std::max(ug_max, ud));
@@ -2186,21 +2164,21 @@ static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, Fused
   c.nud = (ud + c.G - 1) / c.G;
   c.neg = ((L.nb_h + 1) / 2 + kFusedWaves - 1) / kFusedWaves;
   c.ned = (k * ((L.dn_ks + 1) / 2) + kFusedWaves - 1) / kFusedWaves;
-  c.lds = fused_lds_bytes(L.H, L.I, c.nug, c.nud);
+  c.lds = fused_lds_bytes(L.H, L.I, k, c.nug, c.nud);
   // a round of the h gather covers every hot expert's h
   if ((size_t)k * L.I / 8 > (size_t)kPollChunks * kFusedThreads) return false;
   // a wave's down entries (consecutive (expert, step pair)s) cover at most two hot experts
   if (c.ned > (L.dn_ks + 1) / 2) return false;
   if (c.lds + sizeof(RouteLds) > 64 * 1024) return false;
   // the smallest instantiation that holds the bounds
-  const int keys[][4] = {{1, 1, 1, 1}, {2, 2, 2, 2}, {3, 3, 2, 3}};
+  const int keys[][4] = {{1, 1, 1, 1}, {2, 2, 1, 2}, {2, 2, 2, 2}, {3, 3, 2, 3}};
   for (const auto& kk : keys)
     if (c.nug <= kk[0] && c.neg <= kk[1] && c.nud <= kk[2] && c.ned <= kk[3]) {
       c.nug = kk[0];
       c.neg = kk[1];
       c.nud = kk[2];
       c.ned = kk[3];
-      c.lds = fused_lds_bytes(L.H, L.I, c.nug, c.nud);
+      c.lds = fused_lds_bytes(L.H, L.I, k, c.nug, c.nud);
       bool fits = false;
 #define MOE_LD_FIT(A, B, C, D) fits = fused_resident<A, B, C, D>(c.lds)
       MOE_LD_SWITCH(fused_key(c), MOE_LD_FIT)

@@ -153,7 +153,7 @@ moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_
 /* ---------------------------------------------------------------------------------------
  * Whole layer in one call: moe_route followed by moe_experts_forward.  For M*k <= 256 the
  * top-k, slot resolve and bucketing run inside the expert kernels (three launches: router
- * GEMV, gate/up, down + combine).  For one token (M = 1, top_k <= 4) of the shapes the fused
+ * GEMV, gate/up, down + combine).  For one token (M = 1, top_k <= 16) of the shapes the fused
  * kernel is built for (moe_layer_launches reports it; GPT-OSS-20B's is one) gate/up and down
  * are one launch of one workgroup per compute unit, h handed from gate/up to down by value
  * through the workspace (the router kernel marks it unwritten first): two launches in all;

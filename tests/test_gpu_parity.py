@@ -222,6 +222,15 @@ def test_e512_verify_half_resident(e512, M):
     ref = O.layer_forward(x, ids_ref, w_ref, e512.experts, e2s)
     assert cc == len(ref["cold_routes"]) and np.array_equal(cold, ref["cold_routes"])
     close_enough(y, ref["y_hot"], f"e512 M={M} y_hot")
+    # the whole layer call (for one token: router + the fused kernel over the 10 routes)
+    lb = L.Buffers(shape, M)
+    B.moe_layer_forward(shape, _dev(x), M, _dev(e512.wr), _dev(bias), _dev(e2s), slots, lb.ids, lb.w,
+                        lb.y, lb.cold_count, lb.cold_routes, lb.ws)
+    torch.cuda.synchronize()
+    assert torch.equal(lb.ids[:M], buf.ids[:M]) and torch.equal(lb.w[:M], buf.w[:M])
+    assert int(lb.cold_count.item()) == cc
+    paths_agree(lb.y[:M].cpu().numpy(), y, f"e512 M={M} layer call")
+    close_enough(lb.y[:M].cpu().numpy(), ref["y_hot"], f"e512 M={M} layer call y_hot")
 
 
 def test_e512_prefill_sampled_tokens(e512):
