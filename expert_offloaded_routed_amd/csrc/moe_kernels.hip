@@ -1580,27 +1580,58 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     }
   }
   __syncthreads();
-  // every (unit, hot expert, row) over the waves, then y for each row: the routes in ascending
-  // order (one token: route j = rank j)
-  for (int i = threadIdx.x; i < NUD * K * 8; i += kFusedThreads) {
-    const int r = i & 7, uj = i >> 3;  // uj = unit * K + hot expert
-    float v = 0.0f;
+  // y for every row: each hot expert's row over the waves, then the routes in ascending order
+  // (one token: route j = rank j).  With few routes one wave does it all, lane (unit, row,
+  // slot); otherwise the sums over the waves come first, from every thread, then the routes.
+  constexpr int T = 64 / (NUD * 8);  // slots per row in the one-wave form
+  const int row0 = 8 * dn_lo;
+  auto store_y = [&](int row, float acc_y) {
+    y[row] = acc_y;
+    // the residual reads x from its LDS copy
+    if (res.out != nullptr)
+      res.out[row] = (uint16_t)f32_to_bf16_bits(__uint_as_float((uint32_t)xs[row] << 16) + acc_y);
+  };
+  if (K <= T) {
+    if (wave == 0) {
+      const int t = lane % T;
+      const int rr = lane / T;  // unit * 8 + row
+      const int ud = rr >> 3, r = rr & 7;
+      float p = 0.0f;
+      if (t < K)
 #pragma unroll
-    for (int w = 0; w < kFusedWaves; ++w) v += red_dn[(uj * kFusedWaves + w) * 8 + r];
-    sum_dn[i] = v;
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < NUD * 8) {
-    const int ud = threadIdx.x >> 3, r = threadIdx.x & 7;
-    if (ud < ndn) {
-      float acc_y = 0.0f;
-      for (int j = 0; j < K; ++j)
-        if (rt.slot[j] >= 0) acc_y = fmaf(rt.w[j], sum_dn[(ud * K + s_dist_of_route[j]) * 8 + r], acc_y);
-      const int row = 8 * (dn_lo + ud) + r;
-      y[row] = acc_y;
-      // the residual reads x from its LDS copy
-      if (res.out != nullptr)
-        res.out[row] = (uint16_t)f32_to_bf16_bits(__uint_as_float((uint32_t)xs[row] << 16) + acc_y);
+        for (int w = 0; w < kFusedWaves; ++w) p += red_dn[((ud * K + t) * kFusedWaves + w) * 8 + r];
+      float pt[T];
+#pragma unroll
+      for (int i = 0; i < T; ++i) pt[i] = __shfl(p, rr * T + i);
+      if (t == 0 && ud < ndn) {
+        float acc_y = 0.0f;
+        for (int j = 0; j < K; ++j) {
+          const int dj = s_dist_of_route[j];
+          float pj = 0.0f;
+#pragma unroll
+          for (int i = 0; i < T; ++i) pj = dj == i ? pt[i] : pj;
+          if (rt.slot[j] >= 0) acc_y = fmaf(rt.w[j], pj, acc_y);
+        }
+        store_y(row0 + rr, acc_y);
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < NUD * K * 8; i += kFusedThreads) {
+      const int r = i & 7, uj = i >> 3;  // uj = unit * K + hot expert
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kFusedWaves; ++w) v += red_dn[(uj * kFusedWaves + w) * 8 + r];
+      sum_dn[i] = v;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < NUD * 8) {
+      const int ud = threadIdx.x >> 3, r = threadIdx.x & 7;
+      if (ud < ndn) {
+        float acc_y = 0.0f;
+        for (int j = 0; j < K; ++j)
+          if (rt.slot[j] >= 0) acc_y = fmaf(rt.w[j], sum_dn[(ud * K + s_dist_of_route[j]) * 8 + r], acc_y);
+        store_y(row0 + threadIdx.x, acc_y);
+      }
     }
   }
 }
