@@ -1699,24 +1699,26 @@ __device__ __forceinline__ void gemm_store_rows(uint16_t (*xb)[kGemmPitch],
   }
 }
 
-// Loads of one K chunk (kGemmKC blocks) for the gate/up tile of one wave: per row tile q (16 rows:
-// image lanes 16q .. 16q+15, q = 0, 1 gate and 2, 3 up) a lane takes dword g of the row's block
-// chunk and the scale word of the chunk's group.  Blocks past nb re-read block nb-1 (zero
-// weights later).
+// Loads of one K chunk (kGemmKC = 4 blocks) for the gate/up tile of one wave: per row tile q (16
+// rows: image lanes 16q .. 16q+15, q = 0, 1 gate and 2, 3 up) lane (n, g) takes the whole 16-byte
+// code chunk of row n in block g of the chunk (one dwordx4 load) and the scale word of the
+// chunk's group (byte g is the block's scale).  The MFMA K steps then run over the chunk in a
+// permuted order: step j, lane group g = elements 8j .. 8j+7 of block g (the activations are read
+// from LDS in the same order).  Blocks past nb re-read block nb-1 and get scale 0.
+static_assert(kGemmKC == 4, "one chunk = one scale word per row");
 struct GuChunk {
-  uint32_t code[4][kGemmKC];
+  uint4 code[4];
   uint32_t scale[4];
 };
 
 __device__ __forceinline__ void gu_load_chunk(const uint8_t* tb, int nb, int kc, int n, int g,
                                               GuChunk& ch) {
   const uint32_t* sbase = reinterpret_cast<const uint32_t*>(tb + (size_t)nb * 1024);
+  const int b = min(kc * kGemmKC + g, nb - 1);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t* wsrc = reinterpret_cast<const uint32_t*>(tb + (size_t)(16 * q + n) * 16 + g * 4);
-#pragma unroll
-    for (int j = 0; j < kGemmKC; ++j) ch.code[q][j] = wsrc[(size_t)min(kc * kGemmKC + j, nb - 1) * 256];
-    ch.scale[q] = sbase[(size_t)min(kc, (nb - 1) / 4) * 64 + 16 * q + n];  // kGemmKC == 4
+    ch.code[q] = *reinterpret_cast<const uint4*>(tb + (size_t)b * 1024 + (size_t)(16 * q + n) * 16);
+    ch.scale[q] = sbase[(size_t)min(kc, (nb - 1) / 4) * 64 + 16 * q + n];
   }
 }
 
@@ -1772,17 +1774,20 @@ __global__ __launch_bounds__(256) void k_gateup_grouped(
       gu_load_chunk(tb, nb, kc + 1, n, g, nxt);
     }
     __syncthreads();
+    // this lane's block of the chunk: g (scale 0 past K)
+    float sq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sq[q] = scale_or_zero(cur.scale[q], g, kc * kGemmKC + g < nb);
 #pragma unroll
     for (int j = 0; j < kGemmKC; ++j) {
-      const int b = kc * kGemmKC + j;
       bf16x8_t av[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        av[t] = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][j * 32 + g * 8]);
+        av[t] = *reinterpret_cast<const bf16x8_t*>(&xb[buf][t * 16 + n][g * 32 + j * 8]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        bf16x8_t bw = fp4x8_to_bf16(cur.code[q][j], e8m0_to_f32((cur.scale[q] >> (8 * j)) & 0xFFu));
-        if (b >= nb) bw = bf16x8_t{};
+        const uint32_t cw = j == 0 ? cur.code[q].x : j == 1 ? cur.code[q].y : j == 2 ? cur.code[q].z : cur.code[q].w;
+        const bf16x8_t bw = fp4x8_to_bf16(cw, sq[q]);
 #pragma unroll
         for (int t = 0; t < 4; ++t)
           if (t < ntt) acc[t][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[t], bw, acc[t][q], 0, 0, 0);
