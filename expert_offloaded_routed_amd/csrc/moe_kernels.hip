@@ -76,6 +76,30 @@ __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, i
 // cost).  Larger E: k rounds of a wave argmax over PL logits per lane.
 __device__ __forceinline__ float rank_key(float v) { return v != v ? -INFINITY : v; }
 
+// Larger E: every logit becomes a 64-bit rank key, larger = ranks higher (monotone image of
+// the value in the high word, NaN as -inf and -0 as +0; the bitwise complement of the id in the
+// low word, so that ties go to the lower id); then k rounds of: each lane's best key, the
+// wave's best key (DPP / swizzle / readlane), and the owner clears it.  All branch-free.
+__device__ __forceinline__ uint64_t rank_key64(float v, int id) {
+  v = rank_key(v);
+  if (v == 0.0f) v = 0.0f;
+  uint32_t u = __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)id;
+}
+// Number of lanes j < E (E <= 64) whose key is larger than this lane's (keys are distinct):
+// the lane's rank.  One 64-bit compare per lane j on a broadcast key, all in the vector unit.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int j) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, j);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), j);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ int key_rank(uint64_t key, int E) {
+  int rank = 0;
+  for (int j = 0; j < E; ++j) rank += readlane_u64(key, j) > key ? 1 : 0;
+  return rank;
+}
+
 // Logit e of a row held as P partial sums P_STRIDE floats apart, summed in ascending order.
 template <int P>
 __device__ __forceinline__ float logit_at(const float* __restrict__ lrow, size_t pstride, int e) {
@@ -92,11 +116,7 @@ __device__ void topk_rank(const float* __restrict__ lrow, size_t pstride, int E,
   // unconditional loads (a load in a branch is waited for alone)
   const float lv = logit_at<P>(lrow, pstride, min(lane, E - 1));
   const float v = lane < E ? rank_key(lv) : -INFINITY;
-  int rank = 0;
-  for (int j = 0; j < E; ++j) {
-    const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
-    rank += (o > v || (o == v && j < lane)) ? 1 : 0;
-  }
+  const int rank = key_rank(rank_key64(lv, lane), E);
   const bool sel = lane < E && rank < k;
   const uint64_t first = __ballot(lane < E && rank == 0);
   const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)__ffsll((long long)first) - 1));
@@ -108,17 +128,6 @@ __device__ void topk_rank(const float* __restrict__ lrow, size_t pstride, int E,
   }
 }
 
-// Larger E: every logit becomes a 64-bit rank key, larger = ranks higher (monotone image of
-// the value in the high word, NaN as -inf and -0 as +0; the bitwise complement of the id in the
-// low word, so that ties go to the lower id); then k rounds of: each lane's best key, the
-// wave's best key (DPP / swizzle / readlane), and the owner clears it.  All branch-free.
-__device__ __forceinline__ uint64_t rank_key64(float v, int id) {
-  v = rank_key(v);
-  if (v == 0.0f) v = 0.0f;
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)id;
-}
 __device__ __forceinline__ float key_value(uint64_t key) {
   const uint32_t h = (uint32_t)(key >> 32);
   return __uint_as_float((h & 0x80000000u) ? (h ^ 0x80000000u) : ~h);
@@ -511,20 +520,17 @@ __device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs&
   const int lane = threadIdx.x & 63;
   const int E = a.E;
   const float* lrow = a.logits;  // row 0; the workspace holds at least 256 bytes of logits
-  float lv[kFastE];
-#pragma unroll
-  for (int j = 0; j < kFastE; ++j) lv[j] = lrow[j];
-  const float v = lane < E ? rank_key(lrow[lane < E ? lane : 0]) : -INFINITY;
-  int slot_of = lane;
-  if (a.e2s != nullptr) slot_of = a.e2s[lane < E ? lane : 0];
-  float top = -INFINITY;
-  int rank = 0;
-#pragma unroll
-  for (int j = 0; j < kFastE; ++j) {
-    const float o = j < E ? rank_key(lv[j]) : -INFINITY;
-    top = fmaxf(top, o);
-    rank += (o > v || (o == v && j < lane)) ? 1 : 0;
-  }
+  // Every load is issued before any value is used, and unconditionally (the expert map read
+  // falls back to a dummy read of the logits), so that they share one round trip.
+  const int lc = lane < E ? lane : 0;
+  const float own = lrow[lc];
+  const int32_t* e2p = a.e2s != nullptr ? a.e2s : reinterpret_cast<const int32_t*>(lrow);
+  const int e2v = e2p[lc];
+  const float v = lane < E ? rank_key(own) : -INFINITY;
+  const int slot_of = a.e2s != nullptr ? e2v : lane;
+  const int rank = key_rank(rank_key64(own, lane), E);
+  const uint64_t first = __ballot(lane < E && rank == 0);
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)__ffsll((long long)first) - 1));
   const bool sel = lane < E && rank < a.k;
   const float ex = sel ? expf(v - top) : 0.0f;
   const float den = wave_sum(ex);
@@ -1217,24 +1223,30 @@ __global__ __launch_bounds__(256) void k_down_mx(
 //   1. forms its gate/up units: per-lane block dots, the lane pair of a row and the waves summed
 //      in a fixed order, h = bf16(silu(g)*u) stored write-through (device-scope relaxed
 //      stores);
-//   2. gathers h of every hot expert into LDS by polling: the router kernel of the same call
-//      has filled the h rows with 0xFFFF, a bit pattern the h writer never stores (it writes NaN
-//      as 0x7FC0), so an element that differs from it is final.  The loads bypass the
-//      non-coherent caches;
-//   3. forms its down units and y for their rows, hot routes in ascending order (+ residual).
+//   2. each wave gathers the h its down entries read into LDS by polling: the router kernel of
+//      the same call has filled the h rows with 0xFFFF, a bit pattern the h writer never stores
+//      (it writes NaN as 0x7FC0), so an element that differs from it is final.  The loads
+//      bypass the non-coherent caches;
+//   3. forms its down units (each wave its entries as soon as its h is in) and y for their
+//      rows, hot routes in ascending order (+ residual).
 // No counter, fence or read-modify-write is involved.  The gather is bounded: a launch that ran
 // out of it flags kErrHandoff in meta[2] (it cannot happen with the grid resident).
 constexpr int kFusedWaves = 16;
 constexpr int kFusedThreads = kFusedWaves * 64;
 constexpr int kFusedMaxK = 16;      // routes (hot experts) of the token at most
 constexpr int kHandSpins = 1 << 13; // gather rounds at most (each ~1 us: a round trip + sleep)
-constexpr int kPollChunks = 2;      // 16-byte chunks of h per thread in the gather
 constexpr uint32_t kHSentinel = 0xFFFFu;
 
 // Share of workgroup w of U units over G workgroups: [lo, lo + n).
 __device__ __forceinline__ void unit_share(int w, int G, int U, int& lo, int& n) {
   lo = w * U / G;
   n = (w + 1) * U / G - lo;
+}
+// Workgroup barrier ordering LDS only: global loads in flight stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 // v clamped to [lo, hi]; lo when the range is empty
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return max(min(v, hi), lo); }
@@ -1321,23 +1333,18 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, wg = blockIdx.x;
   const int K = ra.k;
-  typedef __attribute__((address_space(3))) void lds_void;
   uint16_t* xs = reinterpret_cast<uint16_t*>(fsm);
   uint16_t* hs = reinterpret_cast<uint16_t*>(fsm + fused_x_bytes(H));
   float* red_gu = reinterpret_cast<float*>(fsm + fused_x_bytes(H) + (size_t)K * I * 2);
   float* red_dn = red_gu + NUG * kFusedWaves * 32;       // [NUD][K][waves][8]
   float* sum_dn = red_dn + NUD * K * kFusedWaves * 8;    // [NUD][K][8]
 
-  // x into LDS, one 1 KiB run per wave instruction; the route table meanwhile
-  {
-    const int n_x = H / 8;
-    const int runs = (n_x + 63) / 64;
-    for (int run = wave; run < runs; run += kFusedWaves) {
-      const int p = min(run * 64 + lane, n_x - 1);
-      __builtin_amdgcn_global_load_lds(x + (size_t)p * 8, (lds_void*)(xs + (size_t)run * 512), 16, 0, 0);
-    }
-  }
+  // x: one 16-byte chunk per thread (H / 8 <= threads), requested first; it lands with the
+  // route table's loads and goes to LDS right after the table is built
+  const int n_x = H / 8;
+  const uint4 xr = reinterpret_cast<const uint4*>(x)[min((int)threadIdx.x, n_x - 1)];
   route_prologue(rt, ra, rw, wg == 0);
+  if ((int)threadIdx.x < n_x) reinterpret_cast<uint4*>(xs)[threadIdx.x] = xr;
   const int nd = rt.nd;
   const int ugpe = I / 16;  // gate/up units per hot expert
   const int Ug = nd * ugpe;
@@ -1355,12 +1362,11 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   const int ll = lane & 31;
   const int gil = ll < 16 ? ll : ll + 16;              // + 16f: image lane (gate ll / up ll-16)
   const int blk = (lane >> 3) & 3, r8 = lane & 7;      // down: step 2p + half, block 4s + blk
-  auto slot_of = [&](int d) { return nd > 0 ? rt.dist_slot[clampi(d, 0, nd - 1)] : 0; };
+  auto slot_of = [&](int d) {  // (the LDS read is unconditional: no wait inside a branch)
+    const int sl = rt.dist_slot[clampi(d, 0, max(nd - 1, 0))];
+    return nd > 0 ? sl : 0;
+  };
 
-  // x has landed and is visible before any weight is requested, so that the arithmetic waits
-  // for each weight load alone
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   uint32_t sg[NUG][NEG], sd[NUD][NED];
   uint4 cg[NUG][NEG], cd[NUD][NED];
   const uint8_t* gtb[NUG];
@@ -1407,6 +1413,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       cg[ug][e] = reinterpret_cast<const uint4*>(gtb[ug])[b * 64 + gilf[ug]];
     }
   __builtin_amdgcn_sched_barrier(0);
+  // x in LDS for every wave (the gate/up loads stay in flight)
+  lds_barrier();
   // The gate/up block scales as floats for the scaled converter (while the codes are in
   // flight); zero for lanes whose block lies past K, which re-read a valid block and must add
   // nothing.
@@ -1490,44 +1498,53 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       for (int i = 0; i < 16; ++i) asm volatile("" : "+v"(wd[ud][e][i]));
     }
 
-  // ---- 2. h of every hot expert into LDS ----
+  // ---- 2. this wave's h into LDS ----
+  // Entry (hot expert ex, step pair p) reads h[ex][256p, 256p + 256) (clamped to I): 32 chunks
+  // of 16 bytes.  Each wave polls the chunks of its own entries only, lane l taking chunk l & 31
+  // of entries 2i + (l >> 5), and a lane re-requests a chunk only until it is final.  No other
+  // wave reads these LDS bytes (a wave's own LDS operations complete in order), so the products
+  // of a wave start as soon as its own h has landed, with no workgroup barrier.
   {
-    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-    const int cpr = I / 8;  // 16-byte chunks per h row
-    const int nch = nd * cpr;
-    const uint16_t* src[kPollChunks];
-    int dst[kPollChunks];
-    bool done[kPollChunks];
+    constexpr int PC = (NED + 1) / 2;
+    const int c = lane & 31;
+    const uint64_t* src[PC];
+    int dst[PC];
+    bool need[PC];
 #pragma unroll
-    for (int i = 0; i < kPollChunks; ++i) {
-      const int c = (int)threadIdx.x + i * kFusedThreads;
-      done[i] = c >= nch;
-      const int cc = clampi(c, 0, max(nch - 1, 0));
-      const int d = cc / cpr;
-      const int route = nd > 0 ? rt.perm[rt.dist_off[d]] : 0;
-      src[i] = hbuf + (size_t)route * I + (size_t)(cc - d * cpr) * 8;
-      dst[i] = cc;
+    for (int i = 0; i < PC; ++i) {
+      const int e = 2 * i + half;
+      const int q = dq0 + clampi(e, 0, ndq - 1);
+      const int ex = q / np2;
+      const int exc = clampi(ex, 0, max(nd - 1, 0));
+      const int route = nd > 0 ? rt.perm[rt.dist_off[exc]] : 0;
+      const int off = min(256 * (q - ex * np2) + 8 * c, I - 8);
+      need[i] = e < ndq && ex < nd;
+      src[i] = reinterpret_cast<const uint64_t*>(hbuf + (size_t)route * I + off);
+      dst[i] = exc * I + off;
     }
     bool late = false;
     for (int spins = 0;; ++spins) {
-      u32x4_t v0, v1;
-      static_assert(kPollChunks == 2, "two chunks per gather round");
-      asm volatile(
-          "global_load_dwordx4 %0, %2, off sc1\n\t"
-          "global_load_dwordx4 %1, %3, off sc1\n\t"
-          "s_waitcnt vmcnt(0)"
-          : "=&v"(v0), "=&v"(v1)
-          : "v"(src[0]), "v"(src[1])
-          : "memory");
-      if (!done[0] && h_chunk_final(v0.x, v0.y, v0.z, v0.w)) {
-        reinterpret_cast<uint4*>(hs)[dst[0]] = make_uint4(v0.x, v0.y, v0.z, v0.w);
-        done[0] = true;
-      }
-      if (!done[1] && h_chunk_final(v1.x, v1.y, v1.z, v1.w)) {
-        reinterpret_cast<uint4*>(hs)[dst[1]] = make_uint4(v1.x, v1.y, v1.z, v1.w);
-        done[1] = true;
-      }
-      if (__ballot(!(done[0] && done[1])) == 0ull) break;
+      uint64_t v[PC][2];
+#pragma unroll
+      for (int i = 0; i < PC; ++i)
+        if (need[i]) {
+          v[i][0] = __hip_atomic_load(src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v[i][1] = __hip_atomic_load(src[i] + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      bool left = false;
+#pragma unroll
+      for (int i = 0; i < PC; ++i)
+        if (need[i]) {
+          const uint32_t w0 = (uint32_t)v[i][0], w1 = (uint32_t)(v[i][0] >> 32);
+          const uint32_t w2 = (uint32_t)v[i][1], w3 = (uint32_t)(v[i][1] >> 32);
+          if (h_chunk_final(w0, w1, w2, w3)) {
+            reinterpret_cast<uint4*>(hs)[dst[i] / 8] = make_uint4(w0, w1, w2, w3);
+            need[i] = false;
+          } else {
+            left = true;
+          }
+        }
+      if (__ballot(left) == 0ull) break;
       if (spins + 1 >= kHandSpins) {
         late = true;
         break;
@@ -1535,8 +1552,9 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       __builtin_amdgcn_s_sleep(4);
     }
     if (late && lane == 0) atomicOr(&rw.meta[2], kErrHandoff);
+    // (the products below read LDS written by other lanes of this wave)
+    asm volatile("" ::: "memory");
   }
-  __syncthreads();
 
   // ---- 3. down units and y ----
   // Entry by entry (one h block read serves every unit); a wave's entries are consecutive
@@ -2201,11 +2219,10 @@ static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, Fused
   c.neg = ((L.nb_h + 1) / 2 + kFusedWaves - 1) / kFusedWaves;
   c.ned = (k * ((L.dn_ks + 1) / 2) + kFusedWaves - 1) / kFusedWaves;
   c.lds = fused_lds_bytes(L.H, L.I, k, c.nug, c.nud);
-  // a round of the h gather covers every hot expert's h
-  if ((size_t)k * L.I / 8 > (size_t)kPollChunks * kFusedThreads) return false;
   // a wave's down entries (consecutive (expert, step pair)s) cover at most two hot experts
   if (c.ned > (L.dn_ks + 1) / 2) return false;
   if (c.lds + sizeof(RouteLds) > 64 * 1024) return false;
+  if (L.H / 8 > kFusedThreads) return false;  // x: one chunk per thread
   // the smallest instantiation that holds the bounds
   const int keys[][4] = {{1, 1, 1, 1}, {2, 2, 1, 2}, {2, 2, 2, 2}, {3, 3, 2, 3}};
   for (const auto& kk : keys)
