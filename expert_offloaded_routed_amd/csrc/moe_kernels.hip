@@ -498,7 +498,7 @@ struct RouteLds {
   int slot[kProMaxRoutes];
   int perm[kProMaxRoutes];
   int first[kProMaxRoutes];  // route is the first of its expert
-  int cnt[kProMaxRoutes];    // routes of the route's expert
+  int cnt[kProMaxRoutes];    // routes of the route's expert (one token: rank of each expert)
   int dist_slot[kProMaxRoutes];
   int dist_off[kProMaxRoutes];
   int dist_cnt[kProMaxRoutes];
@@ -508,16 +508,18 @@ struct RouteLds {
 constexpr size_t kRouteLdsBytes = (sizeof(RouteLds) + 15) / 16 * 16;
 constexpr size_t kGuLdsBytes = 64 * 1024;  // LDS of a gate/up workgroup at most
 
-// One token over at most kFastE experts (the decode case): top-k, slot resolve and the whole
-// route table by wave 0 in registers, with no loop over LDS and no call.  The logit row is
-// uniform, so it comes through the scalar unit; every lane ranks its own logit against all of
-// them (ties to the lower id), exactly as topk_rank does, and the weights use the same
-// arithmetic, so the results are bitwise those of moe_route.  The distinct hot experts of one
-// token are its selected ids; their ascending order is a ballot prefix count.
-constexpr int kFastE = 32;
+// One token over at most kFastE experts (the decode case), by every wave of the workgroup:
+// wave w ranks experts w, w + waves, ... (the number of keys above the expert's key, by a
+// ballot), the ranks meet in LDS (rt.cnt, unused by one-token tables otherwise), then wave 0
+// forms the weights and the route table in registers.  The keys are those of rank_key64, the
+// weights use the arithmetic of topk_rank, so the results are bitwise those of moe_route.  The
+// distinct hot experts of one token are its selected ids; their ascending order is a ballot
+// prefix count.  Contains a workgroup barrier (every thread calls it).
+constexpr int kFastE = 64;
 
 __device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs& a) {
   const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int E = a.E;
   const float* lrow = a.logits;  // row 0; the workspace holds at least 256 bytes of logits
   // Every load is issued before any value is used, and unconditionally (the expert map read
@@ -526,9 +528,16 @@ __device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs&
   const float own = lrow[lc];
   const int32_t* e2p = a.e2s != nullptr ? a.e2s : reinterpret_cast<const int32_t*>(lrow);
   const int e2v = e2p[lc];
+  const uint64_t key = lane < E ? rank_key64(own, lane) : 0ull;  // 0 is below every key
+  for (int i = wave; i < E; i += nw) {
+    const int r = (int)__popcll(__ballot(key > readlane_u64(key, i)));
+    if (lane == 0) rt.cnt[i] = r;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int rank = rt.cnt[lc];
   const float v = lane < E ? rank_key(own) : -INFINITY;
   const int slot_of = a.e2s != nullptr ? e2v : lane;
-  const int rank = key_rank(rank_key64(own, lane), E);
   const uint64_t first = __ballot(lane < E && rank == 0);
   const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)__ffsll((long long)first) - 1));
   const bool sel = lane < E && rank < a.k;
@@ -680,12 +689,10 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
   const int nw = blockDim.x >> 6;
   const int Mk = a.M * a.k;
   if (a.logits != nullptr && a.M == 1) {
-    if (tid < 64) {
-      if (a.E <= kFastE)
-        route_token_small(rt, a);
-      else
-        route_token_wave(rt, a);
-    }
+    if (a.E <= kFastE)
+      route_token_small(rt, a);
+    else if (tid < 64)
+      route_token_wave(rt, a);
     __syncthreads();
   } else {
     if (a.logits != nullptr) {
