@@ -1244,10 +1244,18 @@ constexpr int kFusedMaxK = 16;      // routes (hot experts) of the token at most
 constexpr int kHandSpins = 1 << 13; // gather rounds at most (each ~1 us: a round trip + sleep)
 constexpr uint32_t kHSentinel = 0xFFFFu;
 
+// n / d by a multiply: m = floor((2^32 - 1) / d) + 1 (0 for d = 1) gives floor(n * m / 2^32) =
+// n / d exactly while n * (d - 1) < 2^32 (the launcher checks the bounds of every use).
+struct FusedDivs {
+  uint32_t g, ugpe, np2;  // multipliers of: the grid, gate/up units per expert, step pairs
+};
+__device__ __forceinline__ int div_m(int n, uint32_t m) {
+  return m == 0u ? n : (int)__umulhi((uint32_t)n, m);
+}
 // Share of workgroup w of U units over G workgroups: [lo, lo + n).
-__device__ __forceinline__ void unit_share(int w, int G, int U, int& lo, int& n) {
-  lo = w * U / G;
-  n = (w + 1) * U / G - lo;
+__device__ __forceinline__ void unit_share(int w, uint32_t mg, int U, int& lo, int& n) {
+  lo = div_m(w * U, mg);
+  n = div_m((w + 1) * U, mg) - lo;
 }
 // Workgroup barrier ordering LDS only: global loads in flight stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
@@ -1332,7 +1340,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
     size_t image_bytes, size_t gu_tile_bytes, int nb, size_t gu_bytes, size_t dn_tile_bytes,
     size_t dn_code_bytes, int ks, int full, int rem, int nb_i, RouteArgs ra, RouteWs rw,
-    uint16_t* __restrict__ hbuf, float* __restrict__ y, Residual res) {
+    uint16_t* __restrict__ hbuf, float* __restrict__ y, Residual res, FusedDivs dv) {
   __shared__ RouteLds rt;
   __shared__ int s_dist_of_route[kFusedMaxK];  // one token: route j -> its hot expert index
   extern __shared__ __align__(16) uint8_t fsm[];
@@ -1356,8 +1364,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   const int ugpe = I / 16;  // gate/up units per hot expert
   const int Ug = nd * ugpe;
   int gu_lo, ngu, dn_lo, ndn;
-  unit_share(wg, G, Ug, gu_lo, ngu);
-  unit_share(G - 1 - wg, G, H / 8, dn_lo, ndn);
+  unit_share(wg, dv.g, Ug, gu_lo, ngu);
+  unit_share(G - 1 - wg, dv.g, H / 8, dn_lo, ndn);
   // this wave's part of a unit: block pairs [gp0, gp0 + ngp) of a gate/up unit, (expert, step
   // pair) entries [dq0, dq0 + ndq) of a down unit
   const int np = (nb + 1) / 2;
@@ -1381,7 +1389,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
   for (int ug = 0; ug < NUG; ++ug) {
     const int u = clampi(gu_lo + clampi(ug, 0, ngu - 1), 0, max(Ug - 1, 0));
-    const int d = u / ugpe, t2 = u - d * ugpe;
+    const int d = div_m(u, dv.ugpe), t2 = u - d * ugpe;
     gtb[ug] = slots + (size_t)slot_of(d) * image_bytes + (size_t)(t2 >> 1) * gu_tile_bytes;
     gilf[ug] = 16 * (t2 & 1) + gil;
   }
@@ -1394,7 +1402,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
     for (int e = 0; e < NED; ++e) {
       const int q = dq0 + clampi(e, 0, ndq - 1);
-      const int ex = q / np2;
+      const int ex = div_m(q, dv.np2);
       const int s = min(2 * (q - ex * np2) + half, ks - 1);
       dtb[ud][e] = slots + (size_t)slot_of(ex) * image_bytes + gu_bytes + (size_t)(u >> 1) * dn_tile_bytes;
       dix[ud][e] = s < full ? s * 64 + il : full * 64 + min(il, 16 * rem - 1);
@@ -1477,7 +1485,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
         u += red_gu[(ug * kFusedWaves + w) * 32 + 16 + r];
       }
       const int uu = gu_lo + ug;
-      const int d = uu / ugpe, t2 = uu - d * ugpe;
+      const int d = div_m(uu, dv.ugpe), t2 = uu - d * ugpe;
       const int route = rt.perm[rt.dist_off[d]];
       __hip_atomic_store(&hbuf[(size_t)route * I + (t2 >> 1) * 32 + 16 * (t2 & 1) + r],
                          (uint16_t)f32_to_bf16_bits(silu_f32(g) * u), __ATOMIC_RELAXED,
@@ -1497,7 +1505,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
     for (int e = 0; e < NED; ++e) {
       const int q = dq0 + clampi(e, 0, ndq - 1);
-      const int ex = q / np2;
+      const int ex = div_m(q, dv.np2);
       const int st = 2 * (q - ex * np2) + half;
       block_to_bf16(cd[ud][e], scale_or_zero(sd[ud][e], st & 3, st < ks && 4 * st + blk < nb_i), wd[ud][e]);
       // (here, not sunk into the products after the gather)
@@ -1521,7 +1529,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     for (int i = 0; i < PC; ++i) {
       const int e = 2 * i + half;
       const int q = dq0 + clampi(e, 0, ndq - 1);
-      const int ex = q / np2;
+      const int ex = div_m(q, dv.np2);
       const int exc = clampi(ex, 0, max(nd - 1, 0));
       const int route = nd > 0 ? rt.perm[rt.dist_off[exc]] : 0;
       const int off = min(256 * (q - ex * np2) + 8 * c, I - 8);
@@ -1566,14 +1574,14 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   // ---- 3. down units and y ----
   // Entry by entry (one h block read serves every unit); a wave's entries are consecutive
   // (expert, step pair)s, so they cover at most two hot experts: ex0 and ex0 + 1.
-  const int ex0 = dq0 / np2;
+  const int ex0 = div_m(dq0, dv.np2);
   float accA[NUD], accB[NUD];
 #pragma unroll
   for (int ud = 0; ud < NUD; ++ud) accA[ud] = accB[ud] = 0.0f;
 #pragma unroll
   for (int e = 0; e < NED; ++e) {
     const int q = dq0 + e;
-    const int ex = q / np2;
+    const int ex = div_m(q, dv.np2);
     if (e < ndq && ex < nd) {  // uniform
       const int st = 2 * (q - ex * np2) + half;
       const uint4* hb = reinterpret_cast<const uint4*>(hs + (size_t)ex * I + 32 * min(4 * st + blk, nb_i - 1));
@@ -2215,6 +2223,10 @@ static bool fused_resident(size_t lds) {
   return v > 0;
 }
 
+static uint32_t div_magic(uint32_t d) { return d <= 1 ? 0u : (uint32_t)(0xFFFFFFFFull / d + 1); }
+// div_m is exact for numerators up to n_max with divisor d
+static bool div_exact(uint64_t n_max, uint64_t d) { return d >= 1 && n_max * (d - 1) < (1ull << 32); }
+
 static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, FusedCfg& c) {
   if (k < 1 || k > kFusedMaxK || p.grouped || !p.prologue) return false;
   const int cus = device_cus();
@@ -2230,6 +2242,12 @@ static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, Fused
   if (c.ned > (L.dn_ks + 1) / 2) return false;
   if (c.lds + sizeof(RouteLds) > 64 * 1024) return false;
   if (L.H / 8 > kFusedThreads) return false;  // x: one chunk per thread
+  // the divisions by multiply: unit shares (w * U over the grid), units per expert, step pairs
+  const uint64_t ugpe = (uint64_t)(L.I / 16), np2 = (uint64_t)((L.dn_ks + 1) / 2);
+  if (!div_exact((uint64_t)c.G * (uint64_t)std::max(ug_max, ud), (uint64_t)c.G) ||
+      !div_exact((uint64_t)k * ugpe + kFusedWaves, ugpe) ||
+      !div_exact((uint64_t)k * np2 + kFusedWaves, np2))
+    return false;
   // the smallest instantiation that holds the bounds
   const int keys[][4] = {{1, 1, 1, 1}, {2, 2, 1, 2}, {2, 2, 2, 2}, {3, 3, 2, 3}};
   for (const auto& kk : keys)
@@ -2259,13 +2277,15 @@ hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uin
                                hipStream_t s) {
   FusedCfg c;
   if (M != 1 || !fused_config(L, p, ra.k, c)) return hipErrorInvalidValue;
+  const FusedDivs dv = {div_magic((uint32_t)c.G), div_magic((uint32_t)(I / 16)),
+                        div_magic((uint32_t)((L.dn_ks + 1) / 2))};
   hipError_t e = hipErrorInvalidValue;
 #define MOE_LD(A, B, C, D)                                                                         \
   do {                                                                                             \
     hipLaunchKernelGGL((k_layer_decode<A, B, C, D>), dim3(c.G), dim3(kFusedThreads), c.lds, s, x,  \
                        H, I, slots, L.image_bytes, L.gu_tile_bytes, L.nb_h, L.gu_bytes,            \
                        L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks, L.dn_full, L.dn_rem, L.nb_i, ra, \
-                       rw, hbuf, y, res);                                                          \
+                       rw, hbuf, y, res, dv);                                                      \
     e = hipGetLastError();                                                                         \
   } while (0)
   MOE_LD_SWITCH(fused_key(c), MOE_LD)
