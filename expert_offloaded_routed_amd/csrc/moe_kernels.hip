@@ -492,7 +492,7 @@ __device__ __forceinline__ float dot_tile_range(const uint4 (&c)[4 * G], const u
 // top-k / bucketing kernel); the route kernel does it once and leaves the table in the workspace.
 constexpr int kProMaxRoutes = 256;
 
-struct RouteLds {
+struct __align__(16) RouteLds {
   int ids[kProMaxRoutes];
   float w[kProMaxRoutes];
   int slot[kProMaxRoutes];
@@ -580,6 +580,107 @@ __device__ __forceinline__ void route_token_wave(RouteLds& rt, const RouteArgs& 
   const uint64_t hm = __ballot(hot);
   int pos = 0;
   for (int j = 0; j < a.k; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    pos += (((hm >> j) & 1ull) != 0ull && ej < e) ? 1 : 0;
+  }
+  if (hot) {
+    rt.dist_slot[pos] = slot;
+    rt.dist_off[pos] = pos;
+    rt.dist_cnt[pos] = 1;
+    rt.dist_e[pos] = e;
+    rt.perm[pos] = lane;
+  }
+  if (lane == 0) rt.nd = __popcll(hm);
+}
+
+// One token over 64 < E <= min(threads, 512) experts (k <= 16), by every wave: wave w ranks its
+// 64 keys among themselves (each lane compares its key with the wave's keys, read back from LDS
+// as broadcasts), its k best become candidates in LDS; every candidate is then ranked among the
+// candidates (four threads a candidate), which for the k best is its rank among all keys (every
+// key above one of them is itself a candidate), and wave 0 forms the weights from the k best in
+// rank order with the arithmetic of topk_argmax, so ids and weights are bitwise those of
+// moe_route.  Threads past E carry small distinct keys below every real key (real keys have a
+// nonzero high word).  LDS: the keys over rt.ids .. rt.perm (4 KiB), the candidates' keys over
+// rt.first / rt.cnt and their slots in rt.dist_off, the k best in rt.perm / rt.dist_e.
+// Contains two workgroup barriers (every thread calls it).
+constexpr int kManyMaxK = 16;
+constexpr int kManyMaxE = 512;
+
+__device__ __forceinline__ void route_token_many(RouteLds& rt, const RouteArgs& a) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int E = a.E, k = a.k;
+  const int tc = min(t, E - 1);
+  // every load issued before any value is used (the expert map read falls back to a dummy read)
+  const float lv = a.logits[tc];
+  const int32_t* e2p = a.e2s != nullptr ? a.e2s : reinterpret_cast<const int32_t*>(a.logits);
+  const int e2v = e2p[tc];
+  const uint64_t key = t < E ? rank_key64(lv, t) : (uint64_t)(lane + 1);
+  const int nwv = (E + 63) / 64;  // waves holding experts
+  const int nc = nwv * k, ncp = (nc + 15) & ~15;  // candidates, padded with zero keys
+  uint64_t* all_key = reinterpret_cast<uint64_t*>(rt.ids);     // [nwv * 64]
+  uint64_t* cand_key = reinterpret_cast<uint64_t*>(rt.first);  // [ncp]
+  int* cand_slot = rt.dist_off;                                // [nc]
+  if (wave < nwv) {  // uniform; the wave reads back only its own keys
+    all_key[t] = key;
+    const uint4* wk = reinterpret_cast<const uint4*>(all_key + wave * 64);
+    int r = 0;
+#pragma unroll
+    for (int j = 0; j < 32; j += 8) {
+      uint4 p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = wk[j + i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        r += ((((uint64_t)p[i].y << 32) | p[i].x) > key ? 1 : 0) + ((((uint64_t)p[i].w << 32) | p[i].z) > key ? 1 : 0);
+    }
+    if (r < k) {
+      cand_key[wave * k + r] = key;
+      cand_slot[wave * k + r] = a.e2s != nullptr ? e2v : t;
+    }
+  }
+  if (t >= nc && t < ncp) cand_key[t] = 0ull;
+  __syncthreads();
+  uint64_t* sel_key = reinterpret_cast<uint64_t*>(rt.perm);  // [k], by rank
+  int* sel_slot = rt.dist_e;                                   // [k]
+  {
+    // candidate t / 4 against a quarter of the candidates; the quad's counts summed by DPP
+    const int c = min(t >> 2, ncp - 1), part = t & 3, q = ncp / 4;
+    const uint64_t ck = cand_key[c];
+    const uint4* pk = reinterpret_cast<const uint4*>(cand_key + part * q);
+    int r = 0;
+    for (int j = 0; j < q / 2; j += 2) {
+      const uint4 p0 = pk[j], p1 = pk[j + 1];
+      r += ((((uint64_t)p0.y << 32) | p0.x) > ck ? 1 : 0) + ((((uint64_t)p0.w << 32) | p0.z) > ck ? 1 : 0) +
+           ((((uint64_t)p1.y << 32) | p1.x) > ck ? 1 : 0) + ((((uint64_t)p1.w << 32) | p1.z) > ck ? 1 : 0);
+    }
+    r += dpp_i<0xB1>(r);  // quad_perm [1,0,3,2]
+    r += dpp_i<0x4E>(r);  // quad_perm [2,3,0,1]
+    if (part == 0 && (t >> 2) < nc && r < k && (ck >> 32) != 0ull) {
+      sel_key[r] = ck;
+      sel_slot[r] = cand_slot[t >> 2];
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // (read before the table below overwrites these arrays; one wave's LDS accesses are ordered)
+  const uint64_t mine = lane < k ? sel_key[lane] : 0ull;
+  const int s_of = lane < k ? sel_slot[lane] : -1;
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key_value(mine)), 0));
+  const float ex = lane < k ? expf(key_value(mine) - top) : 0.0f;
+  const float den = wave_sum(ex);
+  const bool route = lane < k;
+  const int e = route ? key_id(mine) : 0;
+  int slot = -1;
+  if (route && s_of >= 0 && s_of < a.S) slot = s_of;
+  if (route) {
+    rt.ids[lane] = e;
+    rt.w[lane] = ex / den;
+    rt.slot[lane] = slot;
+  }
+  const bool hot = slot >= 0;
+  const uint64_t hm = __ballot(hot);
+  int pos = 0;
+  for (int j = 0; j < k; ++j) {
     const int ej = __builtin_amdgcn_readlane(e, j);
     pos += (((hm >> j) & 1ull) != 0ull && ej < e) ? 1 : 0;
   }
@@ -691,6 +792,8 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
   if (a.logits != nullptr && a.M == 1) {
     if (a.E <= kFastE)
       route_token_small(rt, a);
+    else if (a.E <= (int)blockDim.x && a.E <= kManyMaxE && a.k <= kManyMaxK)
+      route_token_many(rt, a);
     else if (tid < 64)
       route_token_wave(rt, a);
     __syncthreads();
