@@ -1740,13 +1740,17 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
       for (int i = 0; i < T; ++i) pt[i] = __shfl(p, rr * T + i);
       if (t == 0 && ud < ndn) {
+        // (unrolled over the K <= T routes: their LDS reads issue together)
         float acc_y = 0.0f;
-        for (int j = 0; j < K; ++j) {
-          const int dj = s_dist_of_route[j];
-          float pj = 0.0f;
 #pragma unroll
-          for (int i = 0; i < T; ++i) pj = dj == i ? pt[i] : pj;
-          if (rt.slot[j] >= 0) acc_y = fmaf(rt.w[j], pj, acc_y);
+        for (int j = 0; j < T; ++j) {
+          if (j < K) {
+            const int dj = s_dist_of_route[j];
+            float pj = 0.0f;
+#pragma unroll
+            for (int i = 0; i < T; ++i) pj = dj == i ? pt[i] : pj;
+            if (rt.slot[j] >= 0) acc_y = fmaf(rt.w[j], pj, acc_y);
+          }
         }
         store_y(row0 + rr, acc_y);
       }
@@ -1763,9 +1767,21 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     if ((int)threadIdx.x < NUD * 8) {
       const int ud = threadIdx.x >> 3, r = threadIdx.x & 7;
       if (ud < ndn) {
+        // (unrolled over the routes: every LDS read issues before the ordered sum; cold routes
+        // have no hot expert index, so theirs is clamped and the term skipped)
+        float pj[kFusedMaxK], wj[kFusedMaxK];
+        bool hj[kFusedMaxK];
+#pragma unroll
+        for (int j = 0; j < kFusedMaxK; ++j) {
+          const int jc = min(j, K - 1);
+          hj[j] = j < K && rt.slot[jc] >= 0;
+          wj[j] = rt.w[jc];
+          pj[j] = sum_dn[(ud * K + min(max(s_dist_of_route[jc], 0), K - 1)) * 8 + r];
+        }
         float acc_y = 0.0f;
-        for (int j = 0; j < K; ++j)
-          if (rt.slot[j] >= 0) acc_y = fmaf(rt.w[j], sum_dn[(ud * K + s_dist_of_route[j]) * 8 + r], acc_y);
+#pragma unroll
+        for (int j = 0; j < kFusedMaxK; ++j)
+          if (hj[j]) acc_y = fmaf(wj[j], pj[j], acc_y);
         store_y(row0 + threadIdx.x, acc_y);
       }
     }
