@@ -545,6 +545,48 @@ def test_fused_decode_consecutive_tokens_and_maps(gptoss):
                 assert cc == len(ref["cold_routes"])
 
 
+@pytest.mark.parametrize("E,k", [(65, 3), (100, 7), (300, 16)])
+def test_fused_decode_many_experts_route_table(E, k):
+    """The one-token route table for 64 < E <= 512 (every wave ranks its 64 keys, the k best of
+    each wave are ranked among themselves): on H = 256, I = 512 layers with E = 65, 100, 300 and
+    k = 3, 7, 16, with all experts resident and with every third expert cold, the layer call
+    (router + fused kernel) publishes bitwise the ids and weights of moe_route, agrees with the
+    two-call path and matches the oracle."""
+    import dataclasses
+    base = synthetic.WORKLOADS["tiny"]
+    wl = dataclasses.replace(base, name=f"tiny_e{E}_k{k}", n_experts=E, top_k=k, n_slots=E)
+    shape = _shape(wl, E)
+    assert B.moe_layer_launches(shape, 1) == 2  # the fused kernel takes the call
+    gen = synthetic.experts_canonical(wl, 0, range(8))
+    experts = [gen[e % 8] for e in range(E)]
+    slots = L.device_slots(L.pack_bank(shape, experts))
+    wr_np = synthetic.router_weights(wl)
+    wr = _dev(wr_np)
+    part = np.arange(E, dtype=np.int32)
+    part[::3] = -1
+    a, b = L.Buffers(shape, 1), L.Buffers(shape, 1)
+    for name, e2s_np in (("identity", None), ("every third expert cold", part)):
+        e2s = None if e2s_np is None else _dev(e2s_np)
+        for t in range(4):
+            say("fused decode, many experts:", E, k, name, "token", t)
+            xn = synthetic.activations(wl, 1, 700 + t)
+            x = _dev(xn)
+            B.moe_layer_forward(shape, x, 1, wr, None, e2s, slots, a.ids, a.w, a.y,
+                                a.cold_count, a.cold_routes, a.ws)
+            B.moe_route(shape, x, 1, wr, None, b.ids, b.w, b.ws)
+            B.moe_experts_forward(shape, x, 1, b.ids, b.w, e2s, slots, b.y, b.cold_count,
+                                  b.cold_routes, b.ws)
+            torch.cuda.synchronize()
+            assert torch.equal(a.ids[:1], b.ids[:1]) and torch.equal(a.w[:1], b.w[:1])
+            assert int(a.cold_count.item()) == int(b.cold_count.item())
+            paths_agree(a.y[:1].cpu().numpy(), b.y[:1].cpu().numpy(), f"E={E} k={k} {name}")
+            _, ids_ref, w_ref = compare_routes(a.ids[:1].cpu().numpy(), a.w[:1].cpu().numpy(),
+                                               O.router_logits(xn, wr_np), k)
+            ref = O.layer_forward(xn, ids_ref, w_ref, experts, e2s_np)
+            assert int(a.cold_count.item()) == len(ref["cold_routes"])
+            close_enough(a.y[:1].cpu().numpy(), ref["y_hot"], f"fused E={E} k={k} {name} {t}")
+
+
 def test_fused_decode_small_shape_and_graph_replays(tiny, gptoss):
     """The fused one-token kernel on a second shape (H = 256, I = 512, E = 8, k = 2: one unit of
     each kind per workgroup) against the oracle and the two-call path, over tokens whose top-k
