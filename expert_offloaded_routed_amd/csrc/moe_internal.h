@@ -36,6 +36,7 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxHidden = 8192;
 constexpr int kMaxInter = 4096;      // at most 32 down K steps
 constexpr int kBucketThreads = 1024; // threads of the top-k / bucketing workgroup
+constexpr int kTopkThreads = 128;    // threads of a workgroup of the multi-workgroup top-k
 constexpr int kDnRows = 16;          // rows of a down tile (one MFMA operand)
 
 struct ImageLayout {

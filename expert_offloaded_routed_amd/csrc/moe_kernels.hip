@@ -230,9 +230,14 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int& total) {
 // Route resolve + bucketing by one workgroup (any multiple of 64 threads up to kBucketThreads):
 // route -> slot, per-expert counts (LDS atomics), exclusive scans (DPP wave scans), bucket
 // permutation, distinct hot experts in ascending id, cold routes in ascending order.
+// Routes r = tid + j*blockDim.x with j < kBucketRegRoutes keep their expert and slot in
+// registers across the stages below (each stage would otherwise wait on its own global reads).
+constexpr int kBucketRegRoutes = 8;
+
 struct BucketSmem {
   int cnt[kMaxExperts];
   int off[kMaxExperts];
+  int slot[kMaxExperts];  // resolved slot of every expert that has a route (-1: cold)
   int wave[kBucketThreads / 64 + 1];
   int err;
 };
@@ -254,21 +259,42 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
   __syncthreads();
 
-  // resolve + count
-  for (int r = tid; r < Mk; r += blockDim.x) {
-    const int e = ids[r];
-    int slot = -1;
+  // resolve + count (every expert with a route also records its slot: equal writes)
+  const int bd = blockDim.x;
+  int e_r[kBucketRegRoutes], s_r[kBucketRegRoutes];
+#pragma unroll
+  for (int j = 0; j < kBucketRegRoutes; ++j) {
+    const int r = tid + j * bd;
+    e_r[j] = r < Mk ? ids[r] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < kBucketRegRoutes; ++j) {
+    const bool ok = tid + j * bd < Mk && e_r[j] >= 0 && e_r[j] < E;
+    s_r[j] = e2s && ok ? e2s[e_r[j]] : e_r[j];
+  }
+  auto resolve = [&](int r, int e, int slot) {
     if (e >= 0 && e < E) {
-      slot = e2s ? e2s[e] : e;
       if (slot < -1 || slot >= S) {
         atomicOr(&s_err, kErrBadSlot);
         slot = -1;
       }
       atomicAdd(&s_cnt[e], 1);
+      sm.slot[e] = slot;
     } else {
       atomicOr(&s_err, kErrBadId);
+      slot = -1;
     }
     route_slot[r] = slot;
+    return slot;
+  };
+#pragma unroll
+  for (int j = 0; j < kBucketRegRoutes; ++j) {
+    const int r = tid + j * bd;
+    if (r < Mk) s_r[j] = resolve(r, e_r[j], s_r[j]);
+  }
+  for (int r = tid + kBucketRegRoutes * bd; r < Mk; r += bd) {
+    const int e = ids[r];
+    resolve(r, e, e >= 0 && e < E ? (e2s ? e2s[e] : e) : -1);
   }
   __syncthreads();
 
@@ -278,11 +304,7 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
   for (int e0 = 0; e0 < E; e0 += blockDim.x) {
     const int e = e0 + tid;
     const int c = e < E ? s_cnt[e] : 0;
-    int slot = -1;
-    if (e < E && c > 0) {
-      slot = e2s ? e2s[e] : e;
-      if (slot < 0 || slot >= S) slot = -1;
-    }
+    const int slot = e < E && c > 0 ? sm.slot[e] : -1;
     const int hot = (c > 0 && slot >= 0) ? 1 : 0;
     const int np = hot ? (c + kItemRoutes - 1) / kItemRoutes : 0;
     int tot, tot_d, tot_i;
@@ -311,8 +333,7 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
   __syncthreads();
 
   // permutation: each route takes the next place of its expert's bucket
-  for (int r = tid; r < Mk; r += blockDim.x) {
-    const int e = ids[r];
+  auto place = [&](int r, int e) {
     if (e >= 0 && e < E) {
       const int pos = atomicAdd(&s_off[e], 1);
       if (pos >= 0 && pos < Mk) {
@@ -320,13 +341,21 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
         if (u_perm) u_perm[pos] = r;
       }
     }
-  }
+  };
+#pragma unroll
+  for (int j = 0; j < kBucketRegRoutes; ++j)
+    if (tid + j * bd < Mk) place(tid + j * bd, e_r[j]);
+  for (int r = tid + kBucketRegRoutes * bd; r < Mk; r += bd) place(r, ids[r]);
 
   // cold routes in ascending order
   int running_c = 0;
   for (int r0 = 0; r0 < Mk; r0 += blockDim.x) {
     const int r = r0 + tid;
-    const int cold = (r < Mk && route_slot[r] < 0) ? 1 : 0;
+    const int j = r0 / bd;
+    int sl = 0;
+#pragma unroll
+    for (int i = 0; i < kBucketRegRoutes; ++i) sl = i == j ? s_r[i] : sl;
+    const int cold = r < Mk && (j < kBucketRegRoutes ? sl : route_slot[r]) < 0 ? 1 : 0;
     int tot;
     const int ci = running_c + block_exclusive_scan(cold, s_wave, tot);
     if (cold && ci < Mk) {
@@ -342,9 +371,10 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
   }
 }
 
-// grid = ceil(M / 16) workgroups of kBucketThreads.  Stage 1 (logits != NULL): wave w of
-// workgroup b does the top-k of tokens b*16 + w, b*16 + w + 16*gridDim.x, ...  Stage 2
-// (do_bucket, single workgroup only): resolve and bucketing.
+// Stage 1 (logits != NULL): wave w of workgroup b does the top-k of tokens b*nw + w,
+// b*nw + w + nw*gridDim.x, ... (nw waves per workgroup: kTopkThreads / 64 when the top-k runs
+// alone, else kBucketThreads / 64).  Stage 2 (do_bucket, single workgroup of kBucketThreads
+// only): resolve and bucketing.
 __global__ __launch_bounds__(kBucketThreads) void k_topk_bucket(
     const float* __restrict__ logits, int M, int k, int32_t* __restrict__ topk_ids,
     float* __restrict__ topk_w, int do_bucket,
@@ -2131,8 +2161,13 @@ hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_i
     if (e != hipSuccess) return e;
     return launch_topk_bucket(nullptr, M, k, nullptr, nullptr, true, ids, E, S, e2s, o, s);
   }
-  const int grid = (logits != nullptr && !do_bucket) ? (M + per_wg - 1) / per_wg : 1;
-  hipLaunchKernelGGL(k_topk_bucket, dim3(grid > 0 ? grid : 1), dim3(kBucketThreads), 0, s, logits,
+  // The top-k alone runs one wave per token on two-wave workgroups, spread over the compute
+  // units: sixteen waves of one workgroup would share a CU's four SIMDs, and this stage is a
+  // chain of dependent wave reductions.
+  const bool topk_only = logits != nullptr && !do_bucket;
+  const int threads = topk_only ? kTopkThreads : kBucketThreads;
+  const int grid = topk_only ? (M + threads / 64 - 1) / (threads / 64) : 1;
+  hipLaunchKernelGGL(k_topk_bucket, dim3(grid > 0 ? grid : 1), dim3(threads), 0, s, logits,
                      M, k, topk_ids, topk_w, do_bucket ? 1 : 0, ids, Mk, E, S, e2s, o.route_slot,
                      o.ws_perm, o.meta, o.dist, nd_max, o.items, o.items ? n_items_max(Mk, E) : 0,
                      o.cold_list, o.u_counts, o.u_offsets, o.u_perm, o.u_cold_count,

@@ -109,6 +109,39 @@ def test_tiny_route_buckets_and_layer(tiny):
     assert cc == 0
 
 
+@pytest.mark.parametrize("extra", [0, 1, 37])
+def test_bucket_routes_many_routes(tiny, extra):
+    """Bucketing of more routes than its one workgroup keeps in registers (8 per thread): the
+    counts, offsets, per-expert route sets and the ascending cold list against their
+    definitions, with every other expert cold and a skewed expert choice."""
+    wl = tiny.wl
+    E, k = wl.n_experts, wl.top_k
+    M = 8 * 1024 // k + extra
+    say("bucket routes: M =", M, "routes =", M * k)
+    rng = np.random.default_rng(4100 + extra)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p / p.sum()) for _ in range(M)]).astype(np.int32)
+    e2s = np.arange(E, dtype=np.int32)
+    e2s[1::2] = -1
+    buf = L.Buffers(tiny.shape, M)
+    counts = torch.zeros(E, dtype=torch.int32, device="cuda")
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.zeros(M * k, dtype=torch.int32, device="cuda")
+    B.moe_bucket_routes(tiny.shape, _dev(ids), M, _dev(e2s), counts, offsets, perm, buf.cold_count,
+                        buf.cold_routes, buf.ws)
+    torch.cuda.synchronize()
+    c_ref, o_ref, p_ref = O.buckets(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), c_ref)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    pg = perm.cpu().numpy()
+    for e in range(E):
+        assert np.array_equal(np.sort(pg[o_ref[e]:o_ref[e + 1]]), np.sort(p_ref[o_ref[e]:o_ref[e + 1]]))
+    cold_ref = np.flatnonzero(e2s[ids.reshape(-1)] < 0)
+    cc = int(buf.cold_count.item())
+    assert cc == len(cold_ref)
+    assert np.array_equal(buf.cold_routes[:cc].cpu().numpy(), cold_ref)
+
+
 def test_tiny_cold_maps_and_slot_relabelling(tiny):
     wl = tiny.wl
     rng = np.random.default_rng(4)
