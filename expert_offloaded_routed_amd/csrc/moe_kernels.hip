@@ -261,14 +261,17 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
 
   // resolve + count (every expert with a route also records its slot: equal writes)
   const int bd = blockDim.x;
+  const int nreg = min(kBucketRegRoutes, (Mk + bd - 1) / bd);  // uniform: passes that have routes
   int e_r[kBucketRegRoutes], s_r[kBucketRegRoutes];
 #pragma unroll
   for (int j = 0; j < kBucketRegRoutes; ++j) {
     const int r = tid + j * bd;
-    e_r[j] = r < Mk ? ids[r] : 0;
+    e_r[j] = j < nreg && r < Mk ? ids[r] : 0;
+    s_r[j] = 0;
   }
 #pragma unroll
   for (int j = 0; j < kBucketRegRoutes; ++j) {
+    if (j >= nreg) break;
     const bool ok = tid + j * bd < Mk && e_r[j] >= 0 && e_r[j] < E;
     s_r[j] = e2s && ok ? e2s[e_r[j]] : e_r[j];
   }
@@ -289,6 +292,7 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
   };
 #pragma unroll
   for (int j = 0; j < kBucketRegRoutes; ++j) {
+    if (j >= nreg) break;
     const int r = tid + j * bd;
     if (r < Mk) s_r[j] = resolve(r, e_r[j], s_r[j]);
   }
@@ -343,8 +347,10 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
     }
   };
 #pragma unroll
-  for (int j = 0; j < kBucketRegRoutes; ++j)
+  for (int j = 0; j < kBucketRegRoutes; ++j) {
+    if (j >= nreg) break;
     if (tid + j * bd < Mk) place(tid + j * bd, e_r[j]);
+  }
   for (int r = tid + kBucketRegRoutes * bd; r < Mk; r += bd) place(r, ids[r]);
 
   // cold routes in ascending order
