@@ -1841,6 +1841,9 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 // next chunk's weights and activations are requested before the current chunk's MFMAs.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// staged activation rows: a native vector type (an array of the HIP uint4 struct stayed in
+// scratch memory across the chunk loop)
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmTok = 64;                 // routes per pass: 4 MFMA tiles of 16
 static_assert(kGemmTok == kItemRoutes, "one work item is one pass of a grouped GEMM workgroup");
@@ -1867,23 +1870,23 @@ struct GemmRows {
 };
 
 __device__ __forceinline__ void gemm_load_rows(const GemmRows& gr, int kc, int K,
-                                               uint4 (&xv)[kGemmXPerThread]) {
+                                               u32x4_t (&xv)[kGemmXPerThread]) {
 #pragma unroll
   for (int i = 0; i < kGemmXPerThread; ++i) {
     const int c = (int)threadIdx.x + 256 * i;
     const int tok = c >> 4;
     const int q = c & 15;  // block q>>2, quarter q&3
     const int e = min(kc * kGemmKC * 32 + q * 8, K - 8);
-    xv[i] = *reinterpret_cast<const uint4*>(gr.row[tok] + e);
+    xv[i] = *reinterpret_cast<const u32x4_t*>(gr.row[tok] + e);
   }
 }
 
 __device__ __forceinline__ void gemm_store_rows(uint16_t (*xb)[kGemmPitch],
-                                                const uint4 (&xv)[kGemmXPerThread]) {
+                                                const u32x4_t (&xv)[kGemmXPerThread]) {
 #pragma unroll
   for (int i = 0; i < kGemmXPerThread; ++i) {
     const int c = (int)threadIdx.x + 256 * i;
-    *reinterpret_cast<uint4*>(&xb[c >> 4][(c & 15) * 8]) = xv[i];
+    *reinterpret_cast<u32x4_t*>(&xb[c >> 4][(c & 15) * 8]) = xv[i];
   }
 }
 
@@ -1949,7 +1952,7 @@ __global__ __launch_bounds__(256) void k_gateup_grouped(
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[t][q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 xv[kGemmXPerThread];
+  u32x4_t xv[kGemmXPerThread];
   GuChunk nxt;
   gemm_load_rows(gr, 0, H, xv);
   gu_load_chunk(tb, nb, 0, n, g, nxt);
@@ -2037,7 +2040,7 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
   f32x4_t acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  uint4 xv[kGemmXPerThread];
+  u32x4_t xv[kGemmXPerThread];
   uint4 bn[kGemmKC];
   auto load_b = [&](int kc) {
 #pragma unroll
