@@ -421,7 +421,6 @@ def bench_stack48(args):
     torch, B = setup()
     import synthetic
     from expert_offloaded_routed_amd import layer as L
-    from oracle import layer as O
 
     wl = synthetic.WORKLOADS["e512_verify_stack"]
     H, I, E, k, S, NL = wl.hidden, wl.inter, wl.n_experts, wl.top_k, wl.n_slots, wl.layers
@@ -435,18 +434,26 @@ def bench_stack48(args):
     log(f"generated {n_gen} layer banks in {time.time() - t0:.1f}s")
     img = banks[0].shape[1]
     wrs, biases, maps, slot_arrays = [], [], [], []
+    # placement: each layer's own router (moe_route) over N_WARM warm-up tokens, one token per
+    # step as in decode; experts ranked by route count (descending, then id), the top S resident
+    N_WARM = 256
+    ws_w = torch.zeros(B.moe_workspace_size(shape, N_WARM), dtype=torch.uint8, device="cuda")
+    ids_w = torch.zeros((N_WARM, k), dtype=torch.int32, device="cuda")
+    w_w = torch.zeros((N_WARM, k), dtype=torch.float32, device="cuda")
     for l in range(NL):
         wr_h = synthetic.router_weights(wl, l)
         bias_h = synthetic.zipf_bias(wl, l)
-        xw = np.concatenate([synthetic.activations(wl, 1, t, l, warmup=True) for t in range(64)])
-        ids, _, _, _ = O.route(O.router_logits(xw, wr_h, bias_h), k)
-        counts = np.bincount(ids.reshape(-1), minlength=E)
+        xw = dev_bits(torch, np.concatenate([synthetic.activations(wl, 1, t, l, warmup=True)
+                                             for t in range(N_WARM)]))
+        wr_d, bias_d = dev_bits(torch, wr_h), torch.from_numpy(bias_h).cuda()
+        B.moe_route(shape, xw, N_WARM, wr_d, bias_d, ids_w, w_w, ws_w)
+        counts = np.bincount(ids_w.cpu().numpy().reshape(-1), minlength=E)
         order = sorted(range(E), key=lambda e: (-counts[e], e))[:S]
         slot_expert = np.array(order, np.int32)
         e2s = np.full(E, -1, np.int32)
         e2s[slot_expert] = np.arange(S, dtype=np.int32)
-        wrs.append(dev_bits(torch, wr_h))
-        biases.append(torch.from_numpy(bias_h).cuda())
+        wrs.append(wr_d)
+        biases.append(bias_d)
         maps.append(torch.from_numpy(e2s).cuda())
         slot_arrays.append(L.device_slots(banks[l % n_gen], slot_expert, S))
     log(f"placed {NL} layers ({NL * S * img / 1e9:.1f} GB of slots)")
@@ -505,7 +512,8 @@ def bench_stack48(args):
         "dtype": "bf16", "data": f"synthetic; expert banks are byte copies of {n_gen} generated layers, "
                                  "routers, priors and placements are per layer",
         "config": {"workload": "e512_verify_stack", "hidden": H, "inter": I, "n_experts": E, "top_k": k,
-                   "M": M, "layers": NL, "slots_per_layer": S, "placement": "warm-up popularity (64 tokens)",
+                   "M": M, "layers": NL, "slots_per_layer": S,
+                   "placement": f"warm-up popularity ({N_WARM} tokens routed by moe_route)",
                    "residual": "bf16(x + y) between layers", "timed": "one HIP graph of the token steps"},
         "hot_expert_gbs": round(gbs, 1), "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
         "hot_bytes_per_token_step": int(hot_bytes / args.steps),

@@ -44,7 +44,7 @@ class moe_cache_config(C.Structure):
 
 class moe_refill(C.Structure):
     _fields_ = [("expert", C.c_int32), ("slot", C.c_int32), ("evicted", C.c_int32),
-                ("visible_step", C.c_int32)]
+                ("reserved", C.c_int32), ("visible_step", C.c_int64)]
 
 
 class moe_cache_stats(C.Structure):
@@ -75,6 +75,7 @@ _SIGS = {
     "moe_experts_down": [C.POINTER(moe_shape), _I32, _P, _P, _P, _P, _P, _P, _SZ, _P],
     "moe_slot_refill": [C.POINTER(moe_shape), _P, _P, _P, _P, _I32, _P, _P, _P],
     "moe_residual_bf16": [_P, _P, _P, _SZ, _P],
+    "moe_workspace_errors": [_P, _SZ, _P, _P],
     "moe_cache_create": [C.POINTER(moe_shape), C.POINTER(moe_cache_config), _P,
                          C.POINTER(_P)],
     "moe_cache_policy_step": [_P, C.c_int64, _P, _I32, _P, C.POINTER(_I32), _P,
@@ -269,6 +270,18 @@ def moe_experts_down(shape, M, topk_ids, topk_w, expert_to_slot, slots, y, ws, s
     _check(load().moe_experts_down(C.byref(shape), int(M), _ptr(topk_ids), _ptr(topk_w),
                                    _ptr(expert_to_slot), _ptr(slots), _ptr(y), _ptr(ws),
                                    _nbytes(ws), _stream(stream)), "moe_experts_down")
+
+
+MOE_DEVERR_BAD_ID = 1
+MOE_DEVERR_BAD_SLOT = 2
+MOE_DEVERR_HANDOFF = 4
+
+
+def moe_workspace_errors(ws, flags, stream=None):
+    """Enqueue a copy of the workspace's device error word into ``flags`` (one int32, device or
+    pinned host memory)."""
+    _check(load().moe_workspace_errors(_ptr(ws), _nbytes(ws), _ptr(flags), _stream(stream)),
+           "moe_workspace_errors")
 
 
 def moe_residual_bf16(x, y, out, n, stream=None):

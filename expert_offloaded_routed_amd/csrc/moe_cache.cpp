@@ -206,7 +206,8 @@ moe_status moe_cache_policy_step(moe_cache* c, int64_t step, const int32_t* topk
       plan[admitted].expert = e;
       plan[admitted].slot = v;
       plan[admitted].evicted = old;
-      plan[admitted].visible_step = (int32_t)vis;
+      plan[admitted].reserved = 0;
+      plan[admitted].visible_step = vis;
       ++admitted;
       c->stats.refills += 1;
     }

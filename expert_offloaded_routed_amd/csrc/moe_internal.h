@@ -88,14 +88,20 @@ __host__ __device__ inline int router_parts(int M, int E) {
   return M >= kGroupedMinTokens && E <= kRouterMaxE ? kRouterParts : 1;
 }
 
-// Workspace: per-call arrays sized for M tokens (nothing survives between calls).
+// Workspace: a fixed header, then per-call arrays sized for M tokens.
+//
+// Header (offset 0, the same for every M, so that the error word can be read without knowing
+// the last call's size), int32 meta[kMetaWords]:
+//   [0] distinct hot experts of the call, [1] its cold routes, [2] the device error flags of
+//   the last call (kErr* bits; read by moe_workspace_errors), [3] length of the grouped work
+//   list.
 struct WsLayout {
+  size_t meta;           // i32 [kMetaWords], offset 0
   size_t logits;         // f32 [router_parts(M, E)][M][E]
   size_t route_slot;     // i32 [M*k]
   size_t counts;         // i32 [E]
   size_t offsets;        // i32 [E+1]
   size_t perm;           // i32 [M*k]
-  size_t meta;           // i32 [8]: n_dist, cold_count, error flags
   size_t dist;           // i32x4 [nd_max]: distinct hot experts {slot, bucket offset, count, id}
   size_t cold_list;      // i32 [M*k]
   size_t items;          // i32x2 [n_items_max]: grouped GEMM work list {distinct expert, first route}
@@ -106,6 +112,9 @@ struct WsLayout {
 };
 
 inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+constexpr int kMetaWords = 16;  // int32 words of the workspace header
+constexpr int kMetaErr = 2;     // index of the error word
 
 // Grouped GEMM work items: (distinct hot expert, pass of up to kItemRoutes of its routes).
 // sum over experts of ceil(c_e / kItemRoutes) <= (number of experts) + M*k / kItemRoutes.
@@ -121,12 +130,12 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   const size_t Mk = (size_t)M * k;
   const size_t nd = Mk < (size_t)E ? Mk : (size_t)E;
   size_t o = 0;
+  W.meta = o;        o = align256(o + 4 * (size_t)kMetaWords);
   W.logits = o;      o = align256(o + 4 * (size_t)router_parts(M, E) * M * E);
   W.route_slot = o;  o = align256(o + 4 * Mk);
   W.counts = o;      o = align256(o + 4 * (size_t)E);
   W.offsets = o;     o = align256(o + 4 * ((size_t)E + 1));
   W.perm = o;        o = align256(o + 4 * Mk);
-  W.meta = o;        o = align256(o + 4 * 8);
   W.dist = o;        o = align256(o + 16 * nd);
   W.cold_list = o;   o = align256(o + 4 * Mk);
   W.items = o;       o = align256(o + 8 * (size_t)n_items_max((int)Mk, E));
@@ -136,7 +145,7 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   return W;
 }
 
-// Error flags raised by the device in meta[2]; meta[3] holds the length of the work list.
+// Error flags raised by the device in meta[kMetaErr] (the values of MOE_DEVERR_* in moe.h).
 enum : int32_t { kErrBadId = 1, kErrBadSlot = 2, kErrHandoff = 4 };
 
 // Outputs of the resolve / bucketing stage (workspace arrays, then optional caller arrays).
@@ -188,8 +197,10 @@ struct Residual {
 };
 
 // Kernel launchers (moe_kernels.hip).
+// err: the call's error word, cleared by the router (the first kernel of the call).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s);
+                         int H, float* logits, uint32_t* fill, int n_fill, int32_t* err,
+                         hipStream_t s);
 bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M, int k);
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,

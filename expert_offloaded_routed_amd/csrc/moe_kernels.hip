@@ -36,15 +36,18 @@ namespace moe {
 // clamped, the product of a chunk past the row selected away), so that no load waits alone in
 // a branch.  The workgroups also fill n_fill words at fill with 0xFFFFFFFF: the h rows of the
 // fused decode kernel that follows, which hands h over by value and takes 0xFFFF for "not yet
-// written" (the kernel boundary makes the fill visible to it).
+// written" (the kernel boundary makes the fill visible to it).  The router is the first kernel
+// of every call that starts from activations: workgroup 0 clears the call's error word.
 template <int CPL>
 __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, int M,
                                                const uint16_t* __restrict__ wr,
                                                const float* __restrict__ bias, int E, int H,
                                                float* __restrict__ logits,
-                                               uint32_t* __restrict__ fill, int n_fill) {
+                                               uint32_t* __restrict__ fill, int n_fill,
+                                               int32_t* __restrict__ err) {
   const int lane = threadIdx.x;
   const int e = blockIdx.x;
+  if (e == 0 && lane == 0) *err = 0;
   for (int i = e * 64 + lane; i < n_fill; i += E * 64) fill[i] = 0xFFFFFFFFu;
   const int nch = H / 8;
   const uint4* wsrc = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
@@ -540,6 +543,7 @@ struct __align__(16) RouteLds {
   int dist_cnt[kProMaxRoutes];
   int dist_e[kProMaxRoutes];
   int nd;
+  int err;  // kErr* flags of the table: routes with an id outside [0, E) or a slot outside [-1, S)
 };
 constexpr size_t kRouteLdsBytes = (sizeof(RouteLds) + 15) / 16 * 16;
 constexpr size_t kGuLdsBytes = 64 * 1024;  // LDS of a gate/up workgroup at most
@@ -581,6 +585,7 @@ __device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs&
   const float den = wave_sum(ex);
   int slot = -1;
   if (sel && slot_of >= 0 && slot_of < a.S) slot = slot_of;
+  const bool bad = __ballot(sel && (slot_of < -1 || slot_of >= a.S)) != 0ull;
   const bool hot = slot >= 0;
   const uint64_t hm = __ballot(hot);
   const int pos = __popcll(hm & ((1ull << lane) - 1ull));
@@ -596,7 +601,10 @@ __device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs&
     rt.dist_e[pos] = lane;
     rt.perm[pos] = rank;
   }
-  if (lane == 0) rt.nd = __popcll(hm);
+  if (lane == 0) {
+    rt.nd = __popcll(hm);
+    rt.err = bad ? kErrBadSlot : 0;
+  }
 }
 
 // One token over any number of experts: top-k by wave 0 (topk_token), then the route table in
@@ -611,6 +619,7 @@ __device__ __forceinline__ void route_token_wave(RouteLds& rt, const RouteArgs& 
   const int s_of = a.e2s != nullptr ? a.e2s[ec] : ec;  // issued for every lane (clamped)
   int slot = -1;
   if (route && e >= 0 && e < a.E && s_of >= 0 && s_of < a.S) slot = s_of;
+  const bool bad = __ballot(route && e >= 0 && e < a.E && (s_of < -1 || s_of >= a.S)) != 0ull;
   if (route) rt.slot[lane] = slot;
   const bool hot = slot >= 0;
   const uint64_t hm = __ballot(hot);
@@ -626,7 +635,10 @@ __device__ __forceinline__ void route_token_wave(RouteLds& rt, const RouteArgs& 
     rt.dist_e[pos] = e;
     rt.perm[pos] = lane;
   }
-  if (lane == 0) rt.nd = __popcll(hm);
+  if (lane == 0) {
+    rt.nd = __popcll(hm);
+    rt.err = bad ? kErrBadSlot : 0;
+  }
 }
 
 // One token over 64 < E <= min(threads, 512) experts (k <= 16), by every wave: wave w ranks its
@@ -708,6 +720,7 @@ __device__ __forceinline__ void route_token_many(RouteLds& rt, const RouteArgs& 
   const int e = route ? key_id(mine) : 0;
   int slot = -1;
   if (route && s_of >= 0 && s_of < a.S) slot = s_of;
+  const bool bad = __ballot(route && (s_of < -1 || s_of >= a.S)) != 0ull;
   if (route) {
     rt.ids[lane] = e;
     rt.w[lane] = ex / den;
@@ -727,10 +740,14 @@ __device__ __forceinline__ void route_token_many(RouteLds& rt, const RouteArgs& 
     rt.dist_e[pos] = e;
     rt.perm[pos] = lane;
   }
-  if (lane == 0) rt.nd = __popcll(hm);
+  if (lane == 0) {
+    rt.nd = __popcll(hm);
+    rt.err = bad ? kErrBadSlot : 0;
+  }
 }
 
-// rt.ids / rt.w [0, Mk) must be in place (and visible after a barrier).  e2s may point to LDS.
+// rt.ids / rt.w [0, Mk) must be in place and rt.err cleared (visible after a barrier).  e2s may
+// point to LDS.  Routes with an id outside [0, E) or a slot outside [-1, S) are cold and flagged.
 __device__ void build_table(RouteLds& rt, int Mk, int E, int S, const int32_t* e2s) {
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
@@ -740,7 +757,10 @@ __device__ void build_table(RouteLds& rt, int Mk, int E, int S, const int32_t* e
     int slot = -1;
     if (e >= 0 && e < E) {
       slot = e2s ? e2s[e] : e;
+      if (slot < -1 || slot >= S) atomicOr(&rt.err, kErrBadSlot);
       if (slot < 0 || slot >= S) slot = -1;
+    } else {
+      atomicOr(&rt.err, kErrBadId);
     }
     rt.slot[r] = slot;
     int c = 0, before = 0;
@@ -802,8 +822,10 @@ __device__ void write_routes(const RouteLds& rt, int Mk, int32_t* topk_ids, floa
   }
 }
 
-// The table of rt, as the expert kernels read it from the workspace.
-__device__ void write_table(const RouteLds& rt, int Mk, const RouteWs& w) {
+// The table of rt, as the expert kernels read it from the workspace.  The table's error flags
+// replace the call's error word (or_err: are added to it, when other workgroups of the launch
+// may raise flags too and an earlier kernel of the call cleared it).
+__device__ void write_table(const RouteLds& rt, int Mk, const RouteWs& w, bool or_err) {
   for (int r = threadIdx.x; r < Mk; r += blockDim.x) {
     w.route_slot[r] = rt.slot[r];
     w.perm[r] = rt.perm[r];  // entries past the hot routes are never read
@@ -815,13 +837,17 @@ __device__ void write_table(const RouteLds& rt, int Mk, const RouteWs& w) {
     for (int r = 0; r < Mk; ++r) c += rt.slot[r] < 0;
     w.meta[0] = rt.nd;
     w.meta[1] = c;
-    w.meta[2] = 0;
+    if (!or_err)
+      w.meta[kMetaErr] = rt.err;
+    else if (rt.err != 0)
+      atomicOr(&w.meta[kMetaErr], rt.err);
   }
 }
 
 // Route table of an expert workgroup: top-k from the logits or the given ids, then the table.
 // The writer workgroup also publishes the top-k results, the cold report and the table.
-__device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& w, bool writer) {
+__device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& w, bool writer,
+                               bool or_err) {
   const int tid = threadIdx.x;
   const int nw = blockDim.x >> 6;
   const int Mk = a.M * a.k;
@@ -843,12 +869,13 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
         rt.w[r] = a.w_in[r];
       }
     }
+    if (tid == 0) rt.err = 0;
     __syncthreads();
     build_table(rt, Mk, a.E, a.S, a.e2s);
   }
   if (writer) {
     write_routes(rt, Mk, a.topk_ids, a.topk_w, a.cold_count, a.cold_routes, nullptr);
-    write_table(rt, Mk, w);
+    write_table(rt, Mk, w, or_err);
   }
 }
 
@@ -926,7 +953,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
   int slot, cnt, off;
   const int* perm;
   if (PRO) {
-    route_prologue(rt, ra, rw, tile == 0 && d == 0);
+    route_prologue(rt, ra, rw, tile == 0 && d == 0, false);
     if (d >= rt.nd) {
       if (XLDS) __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
       return;
@@ -1482,8 +1509,10 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     uint16_t* __restrict__ hbuf, float* __restrict__ y, Residual res, FusedDivs dv) {
   __shared__ RouteLds rt;
   __shared__ int s_dist_of_route[kFusedMaxK];  // one token: route j -> its hot expert index
+  __shared__ int s_late;                       // a wave's gather of h ran out of rounds
   extern __shared__ __align__(16) uint8_t fsm[];
   const int lane = threadIdx.x & 63;
+  if (threadIdx.x == 0) s_late = 0;  // (the route prologue's barriers publish it)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, wg = blockIdx.x;
   const int K = ra.k;
@@ -1497,7 +1526,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   // route table's loads and goes to LDS right after the table is built
   const int n_x = H / 8;
   const uint4 xr = reinterpret_cast<const uint4*>(x)[min((int)threadIdx.x, n_x - 1)];
-  route_prologue(rt, ra, rw, wg == 0);
+  route_prologue(rt, ra, rw, wg == 0, true);
   if ((int)threadIdx.x < n_x) reinterpret_cast<uint4*>(xs)[threadIdx.x] = xr;
   const int nd = rt.nd;
   const int ugpe = I / 16;  // gate/up units per hot expert
@@ -1705,7 +1734,10 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       }
       __builtin_amdgcn_s_sleep(4);
     }
-    if (late && lane == 0) atomicOr(&rw.meta[2], kErrHandoff);
+    if (late && lane == 0) {
+      atomicOr(&rw.meta[kMetaErr], kErrHandoff);
+      s_late = 1;  // this workgroup's y rows become NaN
+    }
     // (the products below read LDS written by other lanes of this wave)
     asm volatile("" ::: "memory");
   }
@@ -1757,7 +1789,9 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   // slot); otherwise the sums over the waves come first, from every thread, then the routes.
   constexpr int T = 64 / (NUD * 8);  // slots per row in the one-wave form
   const int row0 = 8 * dn_lo;
+  const bool late_wg = s_late != 0;  // (written before the barrier above)
   auto store_y = [&](int row, float acc_y) {
+    if (late_wg) acc_y = __uint_as_float(0x7FC00000u);  // never a silently wrong value
     y[row] = acc_y;
     // the residual reads x from its LDS copy
     if (res.out != nullptr)
@@ -2020,9 +2054,11 @@ __global__ __launch_bounds__(256) void k_gateup_grouped(
 __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restrict__ x, int M,
                                                         const uint16_t* __restrict__ wr,
                                                         const float* __restrict__ bias, int E,
-                                                        int H, float* __restrict__ logits) {
+                                                        int H, float* __restrict__ logits,
+                                                        int32_t* __restrict__ err) {
   __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
   __shared__ GemmRows gr;
+  if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *err = 0;  // the call's error word
   const int tok0 = blockIdx.x * kGemmTok;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2137,17 +2173,18 @@ __global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ x
 // Launchers (called from the host API after every argument has been validated)
 // =============================================================================================
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s) {
+                         int H, float* logits, uint32_t* fill, int n_fill, int32_t* err,
+                         hipStream_t s) {
   if (M >= kGroupedMinTokens)  // a dense GEMM: MFMA
     hipLaunchKernelGGL(k_router_grouped, dim3((M + kGemmTok - 1) / kGemmTok, (E + 63) / 64, router_parts(M, E)), dim3(256),
-                       0, s, x, M, wr, bias, E, H, logits);
+                       0, s, x, M, wr, bias, E, H, logits, err);
   else {
     const int cpl = (H / 8 + 63) / 64;
     switch (cpl) {
 #define MOE_RT(C)                                                                                  \
   case C:                                                                                          \
     hipLaunchKernelGGL((k_router<C>), dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits, fill, \
-                       n_fill);                                                                    \
+                       n_fill, err);                                                               \
     break;
       MOE_RT(1) MOE_RT(2) MOE_RT(3) MOE_RT(4) MOE_RT(5) MOE_RT(6) MOE_RT(7) MOE_RT(8)
       MOE_RT(9) MOE_RT(10) MOE_RT(11) MOE_RT(12) MOE_RT(13) MOE_RT(14) MOE_RT(15) MOE_RT(16)
@@ -2185,8 +2222,10 @@ hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_i
 }
 
 
-constexpr int kNumCUs = 256;      // MI355X compute units
+constexpr int kNumCUs = 256;      // MI355X compute units (when the device cannot be queried)
 constexpr int kWavesPerCU = 16;   // resident waves per CU for a kernel of <= 128 VGPRs
+
+static int device_cus();
 
 ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
   ExpertPlan p;
@@ -2204,12 +2243,14 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
   // the kernels are built for <= 128 VGPRs, so a CU holds kWavesPerCU waves.  Pick the widest
   // workgroup that still lets every workgroup of the grid be resident at once.
   const int units = L.gu_tiles * p.nd_max;
+  const int cus_q = device_cus();
+  const int cus = cus_q > 0 ? cus_q : kNumCUs;
   const int lo = (L.ng_h + kMaxGroups - 1) / kMaxGroups;
   const int hi = L.ng_h < kMaxWaves ? L.ng_h : kMaxWaves;
   int best = lo < hi ? lo : hi, best_rounds = 1 << 30;
   for (int w = (lo < hi ? lo : hi); w <= hi; ++w) {
     const int per_cu = kWavesPerCU / w > 0 ? kWavesPerCU / w : 1;
-    const int rounds = (units + kNumCUs * per_cu - 1) / (kNumCUs * per_cu);
+    const int rounds = (units + cus * per_cu - 1) / (cus * per_cu);
     if (rounds < best_rounds || (rounds == best_rounds && w > best)) {
       best = w;
       best_rounds = rounds;
@@ -2368,22 +2409,21 @@ static int device_cus() {
   return v > 0 ? v : 0;
 }
 
+// The answer depends on the dynamic LDS of the launch (it varies with H, I and k), so the cache
+// holds the LDS size it was asked for with it: {lds, 1 fits / -1 does not} per device.
 template <int NUG, int NEG, int NUD, int NED>
 static bool fused_resident(size_t lds) {
-  static std::atomic<int> cache[16];  // [device]: 0 unknown, 1 fits, -1 does not
+  static std::atomic<int64_t> cache[16];  // [device]: lds << 2 | (1 fits, 2 does not); 0 unknown
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return false;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    int per_cu = 0;
-    v = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_layer_decode<NUG, NEG, NUD, NED>,
-                                                     kFusedThreads, lds) == hipSuccess &&
-                per_cu >= 1
-            ? 1
-            : -1;
-    cache[dev].store(v, std::memory_order_relaxed);
-  }
-  return v > 0;
+  const int64_t v = cache[dev].load(std::memory_order_relaxed);
+  if (v != 0 && (size_t)(v >> 2) == lds) return (v & 3) == 1;
+  int per_cu = 0;
+  const bool fits = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &per_cu, k_layer_decode<NUG, NEG, NUD, NED>, kFusedThreads, lds) == hipSuccess &&
+                    per_cu >= 1;
+  cache[dev].store(((int64_t)lds << 2) | (fits ? 1 : 2), std::memory_order_relaxed);
+  return fits;
 }
 
 static uint32_t div_magic(uint32_t d) { return d <= 1 ? 0u : (uint32_t)(0xFFFFFFFFull / d + 1); }

@@ -87,11 +87,32 @@ moe_status moe_unpack_expert(const moe_shape* shape, const uint8_t* image,
 /* ---------------------------------------------------------------------------------------
  * Workspace.  One device buffer (256-byte aligned) used by moe_route, moe_bucket_routes,
  * moe_experts_forward and moe_layer_forward for calls with M <= max_M.  It carries logits,
- * route buckets, h and partial sums from one kernel of a call to the next; nothing survives
- * between calls, so it needs no initialisation.  Calls sharing a workspace must be ordered on
- * one stream; concurrent calls need separate workspaces.
+ * route buckets, h and partial sums from one kernel of a call to the next, and in a fixed
+ * header the device error word of the last call (moe_workspace_errors).  Calls sharing a
+ * workspace must be ordered on one stream; concurrent calls need separate workspaces.
  * --------------------------------------------------------------------------------------- */
 moe_status moe_workspace_size(const moe_shape* shape, int32_t max_M, size_t* bytes /*[host]*/);
+
+/* Device error flags (bits of the workspace error word). */
+enum {
+  MOE_DEVERR_BAD_ID = 1,   /* a route's expert id lies outside [0, E): the route was treated as cold */
+  MOE_DEVERR_BAD_SLOT = 2, /* expert_to_slot maps a routed expert outside [-1, S): treated as cold */
+  MOE_DEVERR_HANDOFF = 4   /* the one-token fused kernel could not collect h from the other
+                              workgroups in its bounded wait: the y rows (and x_next rows) that
+                              such a workgroup forms are NaN, never silently wrong */
+};
+
+/* Copy the device error word of the last call on this workspace to *flags, asynchronously on
+ * stream [ORT hybrid PR, "Key Changes": the hot-expert kernel takes an optional expert_to_slot
+ * map and skips routes whose slot is negative].  Routes whose id or slot lies outside that map's
+ * contract are skipped like cold ones and reported here instead of being read out of bounds.
+ * The word holds
+ * the MOE_DEVERR_* flags raised by the last moe_route, moe_bucket_routes, moe_experts_forward,
+ * moe_experts_gateup or moe_layer_forward* call on the workspace (0 = none; each of those calls
+ * clears it in its first kernel; calls with M = 0 and moe_experts_down leave it as it was).
+ * ws: the workspace (256-byte aligned, ws_bytes >= 256); flags: one int32 in device memory or
+ * in pinned host memory, 4-byte aligned.  Read it after the stream has passed the copy. */
+moe_status moe_workspace_errors(const void* ws, size_t ws_bytes, int32_t* flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Router [ninfer v0.4.0, "New": the router is no longer a single thread block;
@@ -279,7 +300,8 @@ typedef struct {
   int32_t expert;       /* expert to copy in */
   int32_t slot;         /* destination slot */
   int32_t evicted;      /* expert that held the slot, or -1 */
-  int32_t visible_step; /* first step whose map contains the new expert */
+  int32_t reserved;     /* 0 */
+  int64_t visible_step; /* first step whose map contains the new expert */
 } moe_refill;
 
 typedef struct {

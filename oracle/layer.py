@@ -121,11 +121,13 @@ def expert_ffn(x: np.ndarray, dense: dict):
     return h_bits, d
 
 
-def layer_forward(x_bits, ids, w, experts, expert_to_slot=None):
+def layer_forward(x_bits, ids, w, experts, expert_to_slot=None, dense_memo=None):
     """The expert half of the layer for given routes.
 
     x_bits uint16 [M, H]; ids int [M, k]; w float [M, k]; ``experts`` maps an expert id to
     its canonical MXFP4 dict (a list or a callable); expert_to_slot int [E] or None (all hot).
+    ``dense_memo``: an optional dict that keeps each expert's dequantised matrices between
+    calls (a cache of dequantize_expert, for long runs over the same experts).
     Returns a dict with y_hot, y_cold, y_full float64 [M, H], h_bits uint16 [M, k, I] and
     cold_routes (flat indices m*k + j, ascending).
     """
@@ -143,7 +145,12 @@ def layer_forward(x_bits, ids, w, experts, expert_to_slot=None):
     h_bits = None
     for e in np.unique(ids):
         rows = np.argwhere(ids == e)  # (m, j) pairs routed to e
-        dense = dequantize_expert(get(int(e)))
+        if dense_memo is not None and int(e) in dense_memo:
+            dense = dense_memo[int(e)]
+        else:
+            dense = dequantize_expert(get(int(e)))
+            if dense_memo is not None:
+                dense_memo[int(e)] = dense
         hb, de = expert_ffn(x[rows[:, 0]], dense)
         if h_bits is None:
             h_bits = np.zeros((M, k, hb.shape[1]), dtype=np.uint16)

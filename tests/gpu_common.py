@@ -18,6 +18,23 @@ def say(*a):
     sys.stdout.flush()
 
 
+def device_errors(ws, stream=None):
+    """The device error word of the last call on workspace ``ws``, read through the C ABI."""
+    import torch
+
+    from expert_offloaded_routed_amd import binding as B
+    flags = torch.full((1,), -1, dtype=torch.int32, device=ws.device)
+    B.moe_workspace_errors(ws, flags, stream=stream)
+    torch.cuda.synchronize()
+    return int(flags.item())
+
+
+def no_device_errors(*workspaces):
+    for ws in workspaces:
+        f = device_errors(ws)
+        assert f == 0, f"device error word {f:#x}"
+
+
 def close_enough(got, ref, what=""):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -76,6 +93,16 @@ def compare_routes(ids_gpu, w_gpu, logits_ref, k):
     if got_w:
         close_enough(np.array(got_w), np.array(ref_w), "topk_w")
     return excluded, ids_ref, w_ref
+
+
+def oracle_weights_for(logits_ref, ids):
+    """The oracle's renormalised weights of the given routes (softmax over all experts, the
+    chosen probabilities divided by their sum): for recomputing a token's output with the GPU's
+    own top-k set, which may legitimately differ from the oracle's on a near-tie."""
+    p = O.softmax(np.asarray(logits_ref, dtype=np.float64))
+    ids = np.asarray(ids)
+    ps = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    return ps / ps.sum(axis=1, keepdims=True)
 
 
 def routed_counts(wl, layer, n_tokens, shift=0, warmup=True):

@@ -14,8 +14,8 @@ from expert_offloaded_routed_amd import layer as L
 from oracle import layer as O
 from oracle.cache_policy import LRU, SlotCachePolicy
 
-from gpu_common import (close_enough, compare_routes, paths_agree, popularity_placement,
-                        routed_counts, say)
+from gpu_common import (close_enough, compare_routes, device_errors, no_device_errors,
+                        oracle_weights_for, paths_agree, popularity_placement, routed_counts, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,7 @@ def e512():
 def run_route(shape, x, wr, bias, M, buf):
     B.moe_route(shape, _dev(x), M, _dev(wr), None if bias is None else _dev(bias), buf.ids, buf.w, buf.ws)
     torch.cuda.synchronize()
+    no_device_errors(buf.ws)
     return buf.ids[:M].cpu().numpy(), buf.w[:M].cpu().numpy()
 
 
@@ -74,6 +75,7 @@ def run_experts(shape, x, ids, w, e2s, slots, buf, M):
                           None if e2s is None else _dev(np.ascontiguousarray(e2s, np.int32)),
                           slots, buf.y, buf.cold_count, buf.cold_routes, buf.ws)
     torch.cuda.synchronize()
+    no_device_errors(buf.ws)
     cc = int(buf.cold_count.item())
     return buf.y[:M].cpu().numpy(), cc, buf.cold_routes[:cc].cpu().numpy()
 
@@ -95,6 +97,7 @@ def test_tiny_route_buckets_and_layer(tiny):
     B.moe_bucket_routes(tiny.shape, _dev(ids_ref.astype(np.int32)), M, None, counts, offsets, perm,
                         buf.cold_count, buf.cold_routes, buf.ws)
     torch.cuda.synchronize()
+    no_device_errors(buf.ws)
     c_ref, o_ref, p_ref = O.buckets(ids_ref, wl.n_experts)
     assert np.array_equal(counts.cpu().numpy(), c_ref)
     assert np.array_equal(offsets.cpu().numpy(), o_ref)
@@ -130,6 +133,7 @@ def test_bucket_routes_many_routes(tiny, extra):
     B.moe_bucket_routes(tiny.shape, _dev(ids), M, _dev(e2s), counts, offsets, perm, buf.cold_count,
                         buf.cold_routes, buf.ws)
     torch.cuda.synchronize()
+    no_device_errors(buf.ws)
     c_ref, o_ref, p_ref = O.buckets(ids, E)
     assert np.array_equal(counts.cpu().numpy(), c_ref)
     assert np.array_equal(offsets.cpu().numpy(), o_ref)
@@ -260,6 +264,7 @@ def test_e512_verify_half_resident(e512, M):
     B.moe_layer_forward(shape, _dev(x), M, _dev(e512.wr), _dev(bias), _dev(e2s), slots, lb.ids, lb.w,
                         lb.y, lb.cold_count, lb.cold_routes, lb.ws)
     torch.cuda.synchronize()
+    no_device_errors(lb.ws)
     assert torch.equal(lb.ids[:M], buf.ids[:M]) and torch.equal(lb.w[:M], buf.w[:M])
     assert int(lb.cold_count.item()) == cc
     paths_agree(lb.y[:M].cpu().numpy(), y, f"e512 M={M} layer call")
@@ -284,9 +289,28 @@ def test_e512_prefill_sampled_tokens(e512):
     say("e512 prefill: experts")
     y, cc, _ = run_experts(shape, x, ids_ref, w_ref, None, slots, buf, M)
     assert cc == 0
-    sample = np.random.default_rng(0).choice(M, size=24, replace=False)
-    ref = O.layer_forward(x[sample], ids_ref[sample], w_ref[sample], experts)
-    close_enough(y[sample], ref["y_full"], "e512 prefill sampled tokens")
+    # every token of the call (the grouped GEMMs: 16 K chunks, Zipf-skewed experts that take
+    # several 64-route passes, the split-h block-scaled down projection and the combine)
+    ref = O.layer_forward(x, ids_ref, w_ref, experts)
+    rel = close_enough(y, ref["y_full"], "e512 prefill, all 512 tokens")
+    per_tok = np.linalg.norm(y - ref["y_full"], axis=1) / np.linalg.norm(ref["y_full"], axis=1)
+    counts = np.bincount(ids_ref.reshape(-1), minlength=wl.n_experts)
+    say(f"e512 prefill: rel-L2 over all {M} tokens {rel:.3e}, worst token {per_tok.max():.3e}; "
+        f"busiest expert {counts.max()} routes ({-(-counts.max() // 64)} passes of 64)")
+    # the whole layer call (router GEMM, top-k / bucketing, grouped gate/up, down, combine)
+    lb = L.Buffers(shape, M)
+    B.moe_layer_forward(shape, _dev(x), M, _dev(wr), _dev(bias), None, slots, lb.ids, lb.w, lb.y,
+                        lb.cold_count, lb.cold_routes, lb.ws)
+    torch.cuda.synchronize()
+    no_device_errors(lb.ws)
+    assert torch.equal(lb.ids[:M], buf.ids[:M]) and torch.equal(lb.w[:M], buf.w[:M])
+    ids_l = lb.ids[:M].cpu().numpy()
+    lg = O.router_logits(x, wr, bias)
+    compare_routes(ids_l, lb.w[:M].cpu().numpy(), lg, wl.top_k)
+    # the reference with the call's own top-k sets (equal to the oracle's except on near-ties)
+    ref_l = O.layer_forward(x, ids_l, oracle_weights_for(lg, ids_l), experts)
+    rel_l = close_enough(lb.y[:M].cpu().numpy(), ref_l["y_full"], "e512 prefill layer call")
+    say(f"e512 prefill: layer call rel-L2 {rel_l:.3e}")
 
 
 @pytest.mark.parametrize("M", [64, 130])
@@ -315,6 +339,7 @@ def test_tiny_grouped_gemm_every_token(tiny, M):
     B.moe_experts_gateup(shape, xd, M, c.ids, c.w, None, tiny.slots, c.ws)
     B.moe_experts_down(shape, M, c.ids, c.w, None, tiny.slots, c.y, c.ws)
     torch.cuda.synchronize()
+    no_device_errors(a.ws, c.ws)
     assert torch.equal(a.ids[:M], c.ids[:M]) and torch.equal(a.y[:M], c.y[:M])
     excluded, ids2, w2 = compare_routes(a.ids[:M].cpu().numpy(), a.w[:M].cpu().numpy(),
                                         O.router_logits(x, tiny.wr), wl.top_k)
@@ -372,6 +397,7 @@ def test_graph_capture_replays_match_eager(tiny):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(buf.y[:M], y_eager)
+        no_device_errors(buf.ws)
         # eager work between replays
         B.moe_experts_forward(shape, x, M, buf.ids, buf.w, None, tiny.slots, buf.y, None, None, buf.ws)
         torch.cuda.synchronize()
@@ -426,6 +452,7 @@ def test_slot_cache_pipeline_bookkeeping():
                               after, done)
             done_events.setdefault(plan[0][3], []).append(done)
         torch.cuda.synchronize()
+        no_device_errors(buf.ws)
         ids_t = buf.ids[:1].cpu().numpy().copy()
         ids_host.append(ids_t)
         assert np.array_equal(ids_t, ids_ref[t]), t
@@ -472,6 +499,7 @@ def test_layer_forward_equals_route_plus_experts_and_stages(gptoss):
             B.moe_experts_gateup(shape, x, M, c.ids, c.w, e2s, gptoss.slots, c.ws)
             B.moe_experts_down(shape, M, c.ids, c.w, e2s, gptoss.slots, c.y, c.ws)
             torch.cuda.synchronize()
+            no_device_errors(a.ws, b.ws, c.ws)
             assert torch.equal(b.y[:M], c.y[:M])  # the same kernels, staged differently
             for other in (b, c):
                 assert torch.equal(a.ids[:M], other.ids[:M]) and torch.equal(a.w[:M], other.w[:M])
@@ -504,6 +532,7 @@ def test_marked_layer_forward_and_residual(gptoss):
     B.moe_layer_forward_marked(shape, x, M, wr, bd, None, gptoss.slots, b.ids, b.w, b.y, None, None,
                                b.ws, marks)
     torch.cuda.synchronize()
+    no_device_errors(a.ws, b.ws)
     assert torch.equal(a.ids[:M], b.ids[:M]) and torch.equal(a.y[:M], b.y[:M])
     stages = [B.event_elapsed_ms(marks[j], marks[j + 1]) for j in range(3)]
     assert all(t >= 0 for t in stages), stages
@@ -562,6 +591,7 @@ def test_fused_decode_consecutive_tokens_and_maps(gptoss):
             B.moe_experts_forward(shape, x, 1, b.ids, b.w, e2s, slots, b.y, b.cold_count,
                                   b.cold_routes, b.ws)
             torch.cuda.synchronize()
+            no_device_errors(a.ws, b.ws)
             assert torch.equal(a.ids[:1], b.ids[:1]) and torch.equal(a.w[:1], b.w[:1])
             paths_agree(a.y[:1].cpu().numpy(), b.y[:1].cpu().numpy(), name)
             cc = int(a.cold_count.item())
@@ -610,6 +640,7 @@ def test_fused_decode_many_experts_route_table(E, k):
             B.moe_experts_forward(shape, x, 1, b.ids, b.w, e2s, slots, b.y, b.cold_count,
                                   b.cold_routes, b.ws)
             torch.cuda.synchronize()
+            no_device_errors(a.ws, b.ws)
             assert torch.equal(a.ids[:1], b.ids[:1]) and torch.equal(a.w[:1], b.w[:1])
             assert int(a.cold_count.item()) == int(b.cold_count.item())
             paths_agree(a.y[:1].cpu().numpy(), b.y[:1].cpu().numpy(), f"E={E} k={k} {name}")
@@ -646,6 +677,7 @@ def test_fused_decode_small_shape_and_graph_replays(tiny, gptoss):
             B.moe_experts_forward(shape, x, 1, b.ids, b.w, e2s, tiny.slots, b.y, b.cold_count,
                                   b.cold_routes, b.ws)
             torch.cuda.synchronize()
+            no_device_errors(a.ws, b.ws)
             assert torch.equal(a.ids[:1], b.ids[:1]) and torch.equal(a.w[:1], b.w[:1])
             paths_agree(a.y[:1].cpu().numpy(), b.y[:1].cpu().numpy(), name)
             _, ids_ref, w_ref = compare_routes(a.ids[:1].cpu().numpy(), a.w[:1].cpu().numpy(),
@@ -690,6 +722,7 @@ def test_fused_decode_small_shape_and_graph_replays(tiny, gptoss):
             torch.cuda.synchronize()
             for t in range(T):
                 assert torch.equal(bufs[t].y[:1], y_eager[t]), (lay.wl.name, rep, t)
+            no_device_errors(ws)
             calls()  # eager calls on the same workspace between the replays
             torch.cuda.synchronize()
 
@@ -714,6 +747,7 @@ def test_layer_forward_residual_equals_layer_plus_residual(gptoss, tiny):
             B.moe_layer_forward_residual(shape, x_sep, M, wr, None, None, lay.slots, b.ids, b.w, b.y,
                                          b.cold_count, b.cold_routes, nxt, b.ws)
             torch.cuda.synchronize()
+            no_device_errors(a.ws, b.ws)
             assert torch.equal(a.y[:M], b.y[:M]) and torch.equal(nxt_ref, nxt)
             assert torch.equal(x_sep, x_ref)  # the input is left alone
             x_in = _dev(xn)
@@ -724,3 +758,232 @@ def test_layer_forward_residual_equals_layer_plus_residual(gptoss, tiny):
     with pytest.raises(B.MoeError):
         B.moe_layer_forward_residual(gptoss.shape, x_ref, 1, wr, None, None, gptoss.slots, a.ids, a.w,
                                      a.y, None, None, None, a.ws)
+
+
+def test_device_error_word_flags_bad_ids_and_slots(tiny):
+    """Routes whose expert id lies outside [0, E) or whose expert maps to a slot outside
+    [-1, S) are skipped like cold routes, and the call's device error word says so (read through
+    moe_workspace_errors); the next good call on the same workspace clears it.  Covered: the
+    route-table prologue (few routes), the top-k / bucketing kernel (more routes), the grouped
+    GEMM path (M >= 64) and the fused one-token kernel (a bad map entry for a routed expert)."""
+    wl = tiny.wl
+    E, k, S = wl.n_experts, wl.top_k, wl.n_slots
+    shape = tiny.shape
+    for M in (3, 40, 64):
+        say("device error word: M =", M)
+        x = synthetic.activations(wl, M, 1500 + M)
+        ids_ref, w_ref, _, _ = O.route(O.router_logits(x, tiny.wr), k)
+        bad_e = int(ids_ref[0, 1])             # expert of route 1: its map entry is out of range
+        e2s = np.arange(E, dtype=np.int32)
+        e2s[bad_e] = S + 5
+        ids = ids_ref.astype(np.int32).copy()
+        ids[M - 1, 0] = E + 2                  # an id out of range
+        buf = L.Buffers(shape, M)
+        B.moe_experts_forward(shape, _dev(x), M, _dev(ids), _dev(w_ref.astype(np.float32)),
+                              _dev(e2s), tiny.slots, buf.y, buf.cold_count, buf.cold_routes, buf.ws)
+        torch.cuda.synchronize()
+        assert device_errors(buf.ws) == B.MOE_DEVERR_BAD_ID | B.MOE_DEVERR_BAD_SLOT
+        # reference: both kinds of bad route are cold (any expert whose map entry is -1 stands in)
+        e2s_ref = e2s.copy()
+        e2s_ref[bad_e] = -1
+        ids_ref2 = ids.copy()
+        ids_ref2[M - 1, 0] = bad_e
+        ref = O.layer_forward(x, ids_ref2, w_ref, tiny.experts, e2s_ref)
+        cc = int(buf.cold_count.item())
+        assert cc == len(ref["cold_routes"])
+        assert np.array_equal(buf.cold_routes[:cc].cpu().numpy(), ref["cold_routes"])
+        close_enough(buf.y[:M].cpu().numpy(), ref["y_hot"], f"bad routes cold, M={M}")
+        # a good call on the same workspace clears the word
+        B.moe_experts_forward(shape, _dev(x), M, _dev(ids_ref.astype(np.int32)),
+                              _dev(w_ref.astype(np.float32)), None, tiny.slots, buf.y, None, None,
+                              buf.ws)
+        torch.cuda.synchronize()
+        assert device_errors(buf.ws) == 0
+    say("device error word: fused one-token layer call with bad map entries")
+    assert B.moe_layer_launches(shape, 1) == 2
+    buf = L.Buffers(shape, 1)
+    x = synthetic.activations(wl, 1, 1600)
+    e2s = np.arange(E, dtype=np.int32)
+    e2s[::2] = S + 1                           # every even expert: out of range
+    B.moe_layer_forward(shape, _dev(x), 1, _dev(tiny.wr), None, _dev(e2s), tiny.slots, buf.ids,
+                        buf.w, buf.y, buf.cold_count, buf.cold_routes, buf.ws)
+    torch.cuda.synchronize()
+    ids = buf.ids[:1].cpu().numpy()
+    bad = bool((ids % 2 == 0).any())
+    assert device_errors(buf.ws) == (B.MOE_DEVERR_BAD_SLOT if bad else 0)
+    e2s_ref = e2s.copy()
+    e2s_ref[::2] = -1
+    ref = O.layer_forward(x, ids, oracle_weights_for(O.router_logits(x, tiny.wr), ids), tiny.experts,
+                          e2s_ref)
+    assert int(buf.cold_count.item()) == len(ref["cold_routes"])
+    if np.linalg.norm(ref["y_hot"]) > 0:
+        close_enough(buf.y[:1].cpu().numpy(), ref["y_hot"], "fused, bad map entries cold")
+    else:
+        assert not buf.y[:1].any()
+    B.moe_layer_forward(shape, _dev(x), 1, _dev(tiny.wr), None, None, tiny.slots, buf.ids, buf.w,
+                        buf.y, None, None, buf.ws)
+    torch.cuda.synchronize()
+    assert device_errors(buf.ws) == 0
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_e512_chained_stack(e512, M):
+    """Four stacked E = 512, k = 10 layers, each with its own router, Zipf prior and half-resident
+    placement (from 256 warm-up tokens), chained on the GPU by moe_layer_forward_residual
+    (x_{l+1} = bf16(x_l + y_l), in place, one workspace, no host step between the layers).  Every
+    layer's input is recorded on the stream; afterwards each layer is checked against the oracle
+    on that recorded input: ids, weights, cold report, y_hot, and the chained input of the next
+    layer bit for bit."""
+    wl = e512.wl
+    NL = 4
+    E, k, S, H = wl.n_experts, wl.top_k, wl.n_slots, wl.hidden
+    shape = _shape(wl, S)
+    layers = []
+    for l in range(NL):
+        say("chained stack: placing layer", l, "M =", M)
+        wr = synthetic.router_weights(wl, l)
+        bias = synthetic.zipf_bias(wl, l)
+        slot_expert = popularity_placement(routed_counts(wl, l, 256), S)
+        e2s = np.full(E, -1, np.int32)
+        e2s[slot_expert] = np.arange(S, dtype=np.int32)
+        # every layer's experts are the fixture's (byte copies), its routing is its own
+        layers.append(dict(wr=wr, bias=bias, e2s=e2s, wr_d=_dev(wr), bias_d=_dev(bias),
+                           e2s_d=_dev(e2s), slots=e512.slots_for(slot_expert)))
+    x0 = synthetic.activations(wl, M, 77)
+    xa = _dev(x0)
+    ws = L.Buffers(shape, M).ws
+    x_in = torch.zeros((NL + 1, M, H), dtype=torch.int16, device="cuda")
+    ids = torch.zeros((NL, M, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((NL, M, k), dtype=torch.float32, device="cuda")
+    y = torch.zeros((NL, M, H), dtype=torch.float32, device="cuda")
+    cold = torch.zeros((NL, 1), dtype=torch.int32, device="cuda")
+    cold_routes = torch.zeros((NL, M * k), dtype=torch.int32, device="cuda")
+    errs = torch.full((NL,), -1, dtype=torch.int32, device="cuda")
+    for l, ly in enumerate(layers):
+        x_in[l].copy_(xa.view(M, H))
+        B.moe_layer_forward_residual(shape, xa, M, ly["wr_d"], ly["bias_d"], ly["e2s_d"], ly["slots"],
+                                     ids[l], w[l], y[l], cold[l], cold_routes[l], xa, ws)
+        B.moe_workspace_errors(ws, errs[l:l + 1])
+    x_in[NL].copy_(xa.view(M, H))
+    torch.cuda.synchronize()
+    assert errs.cpu().tolist() == [0] * NL
+    xh = x_in.cpu().numpy().view(np.uint16)
+    for l, ly in enumerate(layers):
+        say("chained stack: checking layer", l)
+        lg = O.router_logits(xh[l], ly["wr"], ly["bias"])
+        ids_l = ids[l].cpu().numpy()
+        compare_routes(ids_l, w[l].cpu().numpy(), lg, k)
+        ref = O.layer_forward(xh[l], ids_l, oracle_weights_for(lg, ids_l), e512.experts, ly["e2s"])
+        cc = int(cold[l].item())
+        assert cc == len(ref["cold_routes"])
+        assert np.array_equal(cold_routes[l, :cc].cpu().numpy(), ref["cold_routes"])
+        yl = y[l].cpu().numpy()
+        close_enough(yl, ref["y_hot"], f"chained stack layer {l} M={M}")
+        xf = (xh[l].astype(np.uint32) << 16).view(np.float32)
+        assert np.array_equal(xh[l + 1], synthetic.bf16_from_f32(xf + yl)), f"residual of layer {l}"
+
+
+def test_slot_cache_pipeline_concurrent_with_poison():
+    """The 8-slot GPT-OSS-20B-shaped layer over 160 decode steps as a real pipeline: the host
+    policy observes routes D = 2 steps late through pinned memory and events (no device-wide
+    synchronisation until the end), maps go up through a pinned ring, refills run on a copy
+    stream after the event of the last step that read the victim slot, and the compute stream
+    waits for a refill's event at the step it becomes visible.  Every evicted slot is first
+    overwritten with 0xFF bytes on the copy stream (E8M0 255 is NaN, E2M1 0xF is -6): a kernel
+    that read a slot while it was being refilled would put NaN into y.  Maps, plans and cold
+    counts equal the oracle policy's replay bit for bit, and y_hot matches the oracle at every
+    step."""
+    wl = synthetic.WORKLOADS["gptoss20b_8slots"]
+    steps, lag, D, R_MAP = 160, 3, 2, 8
+    shape = _shape(wl, wl.n_slots)
+    E, k, S, H = wl.n_experts, wl.top_k, wl.n_slots, wl.hidden
+    say("concurrent pipeline: generating 32 experts")
+    experts = synthetic.experts_canonical(wl, 0, range(E))
+    bank_np = L.pack_bank(shape, experts)
+    bank = L.pinned_bank(bank_np)
+    init = np.argsort(synthetic.zipf_ranks(wl))[:S].astype(np.int32)
+    slots = L.device_slots(bank_np, init, S)
+    wr = synthetic.router_weights(wl)
+    xs = np.concatenate([synthetic.activations(wl, 1, t) for t in range(steps)])
+    biases = np.stack([synthetic.zipf_bias(wl, 0, synthetic.drift_shift(wl, t)) for t in range(steps)])
+    xs_d, wr_d, biases_d = _dev(xs), _dev(wr), torch.from_numpy(biases).cuda()
+    cache = B.MoeCache(shape, lag_steps=lag, initial_slot_expert=init)
+    ws = L.Buffers(shape, 1).ws
+    ids_d = torch.zeros((steps, k), dtype=torch.int32, device="cuda")
+    w_d = torch.zeros((steps, k), dtype=torch.float32, device="cuda")
+    y_d = torch.zeros((steps, H), dtype=torch.float32, device="cuda")
+    cold_d = torch.zeros((steps, 1), dtype=torch.int32, device="cuda")
+    cold_routes = torch.zeros((steps, k), dtype=torch.int32, device="cuda")
+    errs_d = torch.full((steps,), -1, dtype=torch.int32, device="cuda")
+    ids_h = torch.zeros((steps, k), dtype=torch.int32).pin_memory()
+    maps_h = torch.zeros((R_MAP, E), dtype=torch.int32).pin_memory()
+    maps_d = torch.zeros((R_MAP, E), dtype=torch.int32, device="cuda")
+    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    after = [B.event_create() for _ in range(steps)]
+    waits, maps, plans, events = {}, [], [], list(after)
+    torch.cuda.synchronize()
+    for t in range(steps):
+        obs = None
+        if t - D >= 0:
+            B.event_synchronize(after[t - D])  # this step's routes have reached pinned memory
+            obs = ids_h[t - D].numpy().copy()
+        m, plan, _ = cache.moe_cache_policy_step(t, obs)
+        maps.append(m)
+        plans.append(plan)
+        r = t % R_MAP  # pinned slot r was last read by the upload of step t - R_MAP (done: R_MAP > D)
+        maps_h[r].copy_(torch.from_numpy(m))
+        for ev in waits.pop(t, []):
+            B.stream_wait_event(comp, ev)
+        with torch.cuda.stream(comp):
+            maps_d[r].copy_(maps_h[r], non_blocking=True)
+        B.moe_layer_forward(shape, xs_d[t], 1, wr_d, biases_d[t], maps_d[r], slots, ids_d[t], w_d[t],
+                            y_d[t], cold_d[t], cold_routes[t], ws, stream=comp)
+        B.moe_workspace_errors(ws, errs_d[t:t + 1], stream=comp)
+        with torch.cuda.stream(comp):
+            ids_h[t].copy_(ids_d[t], non_blocking=True)
+        B.event_record(after[t], comp)
+        if plan:
+            B.stream_wait_event(copy, after[t])
+            with torch.cuda.stream(copy):
+                for (_, v, _, _) in plan:
+                    slots[v].fill_(0xFF)  # poison: the slot holds NaN scales until its copy lands
+            done = B.event_create()
+            events.append(done)
+            B.moe_slot_refill(shape, slots, bank, [p[0] for p in plan], [p[1] for p in plan], copy,
+                              None, done)
+            waits.setdefault(plan[0][3], []).append(done)
+    torch.cuda.synchronize()
+    cache.close()
+    for ev in events:
+        B.event_destroy(ev)
+    assert errs_d.cpu().tolist() == [0] * steps
+    # the oracle's replay of the same pipeline
+    lg = O.router_logits(xs, wr, None) + biases.astype(np.float64)
+    pol = SlotCachePolicy(E, S, init, policy=LRU, max_refills=2, lag=lag, max_pending=2)
+    ids_gpu = ids_d.cpu().numpy()
+    w_gpu = w_d.cpu().numpy()
+    y_gpu = y_d.cpu().numpy()
+    cold_gpu = cold_d.cpu().numpy()[:, 0]
+    assert np.array_equal(ids_gpu, ids_h.numpy())
+    excluded, _, _ = compare_routes(ids_gpu, w_gpu, lg, k)
+    say("concurrent pipeline: near-tie tokens", excluded)
+    # the policy replay observes the routes the pipeline observed (the oracle's, up to near-ties)
+    w_own = oracle_weights_for(lg, ids_gpu)
+    memo = {}
+    n_refills = 0
+    for t in range(steps):
+        m_ref, plan_ref = pol.step(t, ids_gpu[t - D] if t - D >= 0 else None)
+        assert np.array_equal(maps[t], m_ref), t
+        assert plans[t] == plan_ref, t
+        n_refills += len(plan_ref)
+        ref = O.layer_forward(xs[t:t + 1], ids_gpu[t:t + 1], w_own[t:t + 1], experts, m_ref,
+                              dense_memo=memo)
+        assert cold_gpu[t] == len(ref["cold_routes"]), t
+        assert np.all(np.isfinite(y_gpu[t])), f"step {t}: NaN in y (a poisoned slot was read)"
+        if np.linalg.norm(ref["y_hot"]) > 0:
+            close_enough(y_gpu[t:t + 1], ref["y_hot"], f"concurrent pipeline step {t}")
+        else:
+            assert not y_gpu[t].any(), t
+    say(f"concurrent pipeline: {steps} steps, {n_refills} refills, hit rate "
+        f"{pol.stats['hits'] / max(1, pol.stats['routes']):.3f}")
+    assert n_refills > 20

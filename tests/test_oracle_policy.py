@@ -142,3 +142,30 @@ def test_policy_hand_worked_trace():
     m, p = pol.step(4, None)
     assert list(m) == [-1, -1, 1, 0, -1, -1]
     assert pol.stats == {"steps": 4, "routes": 6, "hits": 2, "refills": 2, "evictions": 2}
+
+
+def test_simulate_hand_worked_readback_trace():
+    """simulate() with a readback delay of 2 steps, worked by hand (E=4, S=2, slots start with
+    experts 0 and 1, LRU, one refill per step, lag 1, one in flight; one route per step).
+
+    routes: t0 -> 2, t1 -> 3, t2 -> 0, t3 -> 2, t4 -> 1
+    t0, t1: nothing observed yet; map {0:0, 1:1}; routes 2 and 3 are cold.
+    t2: observes t0's route (2): miss; no empty slot, both slots unused since the start, LRU
+        (last use -1, -1) takes slot 0: expert 0 is evicted now, 2 arrives at t3.
+        Map {1:1}; t2's own route (0) is cold.
+    t3: 2 lands in slot 0.  Observes t1's route (3): miss; slot 0 was last used at t2 (the
+        refill), slot 1 never: slot 1, expert 1 evicted, 3 arrives at t4.  Map {2:0}; route 2 hot.
+    t4: 3 lands in slot 1.  Observes t2's route (0): miss; slot 0 (last use 2) is older than
+        slot 1 (3): expert 2 evicted, 0 arrives at t5.  Map {3:1}; route 1 is cold.
+    A delay of 1 instead of 2 changes the plan at t1 already.
+    """
+    ids = [np.array([[e]]) for e in (2, 3, 0, 2, 1)]
+    pol = SlotCachePolicy(4, 2, [0, 1], policy=LRU, max_refills=1, lag=1, max_pending=1)
+    maps, plans, cold = simulate(pol, ids, readback_delay=2)
+    assert [list(m) for m in maps] == [[0, 1, -1, -1], [0, 1, -1, -1], [-1, 1, -1, -1],
+                                       [-1, -1, 0, -1], [-1, -1, -1, 1]]
+    assert plans == [[], [], [(2, 0, 0, 3)], [(3, 1, 1, 4)], [(0, 0, 2, 5)]]
+    assert cold == [1, 1, 1, 0, 1]
+    pol1 = SlotCachePolicy(4, 2, [0, 1], policy=LRU, max_refills=1, lag=1, max_pending=1)
+    _, plans1, _ = simulate(pol1, ids, readback_delay=1)
+    assert plans1[1] == [(2, 0, 0, 2)]
