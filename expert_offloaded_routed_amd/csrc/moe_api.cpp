@@ -249,8 +249,7 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
   if (marks && (e = record_mark(marks[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
                     fused ? reinterpret_cast<uint32_t*>(hbuf) : nullptr,
-                    fused ? M * shape->top_k * shape->inter / 2 : 0,
-                    at<int32_t>(ws, W.meta) + kMetaErr, stream);
+                    fused ? M * shape->top_k * shape->inter / 2 : 0, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   if (fused) {
     if (marks && (e = record_mark(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -331,7 +330,7 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, int32_t M, const
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x and w_router must be 16-byte aligned");
   float* logits = at<float>(ws, W.logits);
   hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
-                               nullptr, 0, at<int32_t>(ws, W.meta) + kMetaErr, stream);
+                               nullptr, 0, stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
   e = launch_topk_bucket(logits, M, shape->top_k, topk_ids, topk_w, false, topk_ids,
@@ -462,18 +461,17 @@ moe_status moe_experts_down(const moe_shape* shape, int32_t M, const int32_t* to
   return st != MOE_OK ? st : ok();
 }
 
-moe_status moe_workspace_errors(const void* ws, size_t ws_bytes, int32_t* flags,
-                                hipStream_t stream) {
-  if (!ws || !flags) return fail(MOE_ERR_INVALID_ARG, "moe_workspace_errors: ws and flags are required");
+moe_status moe_workspace_errors(void* ws, size_t ws_bytes, int32_t* flags, hipStream_t stream) {
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "moe_workspace_errors: ws is required");
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0)
     return fail(MOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (ws_bytes < align256(4 * (size_t)kMetaWords))
     return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes holds no header", ws_bytes);
   if (reinterpret_cast<uintptr_t>(flags) & 3)
     return fail(MOE_ERR_INVALID_ARG, "moe_workspace_errors: flags must be 4-byte aligned");
-  const int32_t* word = static_cast<const int32_t*>(ws) + kMetaErr;  // the header is at offset 0
-  hipError_t e = hipMemcpyAsync(flags, word, sizeof(int32_t), hipMemcpyDefault, stream);
-  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  int32_t* word = static_cast<int32_t*>(ws) + kMetaErr;  // the header is at offset 0
+  hipError_t e = launch_take_errors(word, flags, stream);
+  if (e != hipSuccess) return hip_fail(e, "error word launch");
   return ok();
 }
 

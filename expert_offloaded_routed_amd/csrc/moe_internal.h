@@ -92,9 +92,9 @@ __host__ __device__ inline int router_parts(int M, int E) {
 //
 // Header (offset 0, the same for every M, so that the error word can be read without knowing
 // the last call's size), int32 meta[kMetaWords]:
-//   [0] distinct hot experts of the call, [1] its cold routes, [2] the device error flags of
-//   the last call (kErr* bits; read by moe_workspace_errors), [3] length of the grouped work
-//   list.
+//   [0] distinct hot experts of the call, [1] its cold routes, [2] the device error flags
+//   (kErr* bits) that the calls on this workspace raised since moe_workspace_errors last took
+//   them (kernels only OR bits in), [3] length of the grouped work list.
 struct WsLayout {
   size_t meta;           // i32 [kMetaWords], offset 0
   size_t logits;         // f32 [router_parts(M, E)][M][E]
@@ -197,10 +197,10 @@ struct Residual {
 };
 
 // Kernel launchers (moe_kernels.hip).
-// err: the call's error word, cleared by the router (the first kernel of the call).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, uint32_t* fill, int n_fill, int32_t* err,
-                         hipStream_t s);
+                         int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s);
+// Copies the error word to *out (device or pinned host memory; NULL: nowhere) and clears it.
+hipError_t launch_take_errors(int32_t* word, int32_t* out, hipStream_t s);
 bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M, int k);
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,

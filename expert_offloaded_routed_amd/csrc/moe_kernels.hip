@@ -36,18 +36,15 @@ namespace moe {
 // clamped, the product of a chunk past the row selected away), so that no load waits alone in
 // a branch.  The workgroups also fill n_fill words at fill with 0xFFFFFFFF: the h rows of the
 // fused decode kernel that follows, which hands h over by value and takes 0xFFFF for "not yet
-// written" (the kernel boundary makes the fill visible to it).  The router is the first kernel
-// of every call that starts from activations: workgroup 0 clears the call's error word.
+// written" (the kernel boundary makes the fill visible to it).
 template <int CPL>
 __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, int M,
                                                const uint16_t* __restrict__ wr,
                                                const float* __restrict__ bias, int E, int H,
                                                float* __restrict__ logits,
-                                               uint32_t* __restrict__ fill, int n_fill,
-                                               int32_t* __restrict__ err) {
+                                               uint32_t* __restrict__ fill, int n_fill) {
   const int lane = threadIdx.x;
   const int e = blockIdx.x;
-  if (e == 0 && lane == 0) *err = 0;
   for (int i = e * 64 + lane; i < n_fill; i += E * 64) fill[i] = 0xFFFFFFFFu;
   const int nch = H / 8;
   const uint4* wsrc = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
@@ -375,7 +372,7 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
   }
   if (tid == 0) {
     meta[1] = running_c;
-    meta[2] = s_err;
+    if (s_err != 0) atomicOr(&meta[kMetaErr], s_err);  // the error word only accumulates
     if (u_cold_count) *u_cold_count = running_c;
   }
 }
@@ -822,10 +819,9 @@ __device__ void write_routes(const RouteLds& rt, int Mk, int32_t* topk_ids, floa
   }
 }
 
-// The table of rt, as the expert kernels read it from the workspace.  The table's error flags
-// replace the call's error word (or_err: are added to it, when other workgroups of the launch
-// may raise flags too and an earlier kernel of the call cleared it).
-__device__ void write_table(const RouteLds& rt, int Mk, const RouteWs& w, bool or_err) {
+// The table of rt, as the expert kernels read it from the workspace; its error flags are added
+// to the workspace's error word.
+__device__ void write_table(const RouteLds& rt, int Mk, const RouteWs& w) {
   for (int r = threadIdx.x; r < Mk; r += blockDim.x) {
     w.route_slot[r] = rt.slot[r];
     w.perm[r] = rt.perm[r];  // entries past the hot routes are never read
@@ -837,17 +833,13 @@ __device__ void write_table(const RouteLds& rt, int Mk, const RouteWs& w, bool o
     for (int r = 0; r < Mk; ++r) c += rt.slot[r] < 0;
     w.meta[0] = rt.nd;
     w.meta[1] = c;
-    if (!or_err)
-      w.meta[kMetaErr] = rt.err;
-    else if (rt.err != 0)
-      atomicOr(&w.meta[kMetaErr], rt.err);
+    if (rt.err != 0) atomicOr(&w.meta[kMetaErr], rt.err);
   }
 }
 
 // Route table of an expert workgroup: top-k from the logits or the given ids, then the table.
 // The writer workgroup also publishes the top-k results, the cold report and the table.
-__device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& w, bool writer,
-                               bool or_err) {
+__device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& w, bool writer) {
   const int tid = threadIdx.x;
   const int nw = blockDim.x >> 6;
   const int Mk = a.M * a.k;
@@ -875,7 +867,7 @@ __device__ void route_prologue(RouteLds& rt, const RouteArgs& a, const RouteWs& 
   }
   if (writer) {
     write_routes(rt, Mk, a.topk_ids, a.topk_w, a.cold_count, a.cold_routes, nullptr);
-    write_table(rt, Mk, w, or_err);
+    write_table(rt, Mk, w);
   }
 }
 
@@ -953,7 +945,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
   int slot, cnt, off;
   const int* perm;
   if (PRO) {
-    route_prologue(rt, ra, rw, tile == 0 && d == 0, false);
+    route_prologue(rt, ra, rw, tile == 0 && d == 0);
     if (d >= rt.nd) {
       if (XLDS) __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS outlives the workgroup
       return;
@@ -1526,7 +1518,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   // route table's loads and goes to LDS right after the table is built
   const int n_x = H / 8;
   const uint4 xr = reinterpret_cast<const uint4*>(x)[min((int)threadIdx.x, n_x - 1)];
-  route_prologue(rt, ra, rw, wg == 0, true);
+  route_prologue(rt, ra, rw, wg == 0);
   if ((int)threadIdx.x < n_x) reinterpret_cast<uint4*>(xs)[threadIdx.x] = xr;
   const int nd = rt.nd;
   const int ugpe = I / 16;  // gate/up units per hot expert
@@ -2054,11 +2046,9 @@ __global__ __launch_bounds__(256) void k_gateup_grouped(
 __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restrict__ x, int M,
                                                         const uint16_t* __restrict__ wr,
                                                         const float* __restrict__ bias, int E,
-                                                        int H, float* __restrict__ logits,
-                                                        int32_t* __restrict__ err) {
+                                                        int H, float* __restrict__ logits) {
   __shared__ __align__(16) uint16_t xb[2][kGemmTok][kGemmPitch];
   __shared__ GemmRows gr;
-  if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) *err = 0;  // the call's error word
   const int tok0 = blockIdx.x * kGemmTok;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -2156,6 +2146,22 @@ __global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs 
 }
 
 // =============================================================================================
+// The workspace's error word, taken by the caller: copied out, then cleared (in stream order)
+// =============================================================================================
+__global__ __launch_bounds__(64) void k_take_errors(int32_t* __restrict__ word,
+                                                    int32_t* __restrict__ out) {
+  if (threadIdx.x == 0) {
+    const int32_t v = __hip_atomic_exchange(word, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (out != nullptr) *out = v;
+  }
+}
+
+hipError_t launch_take_errors(int32_t* word, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_take_errors, dim3(1), dim3(64), 0, s, word, out);
+  return hipGetLastError();
+}
+
+// =============================================================================================
 // Residual chaining between stacked layers: out = bf16(x + y), one thread per 2 elements
 // =============================================================================================
 __global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ x,
@@ -2173,18 +2179,17 @@ __global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ x
 // Launchers (called from the host API after every argument has been validated)
 // =============================================================================================
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, uint32_t* fill, int n_fill, int32_t* err,
-                         hipStream_t s) {
+                         int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s) {
   if (M >= kGroupedMinTokens)  // a dense GEMM: MFMA
     hipLaunchKernelGGL(k_router_grouped, dim3((M + kGemmTok - 1) / kGemmTok, (E + 63) / 64, router_parts(M, E)), dim3(256),
-                       0, s, x, M, wr, bias, E, H, logits, err);
+                       0, s, x, M, wr, bias, E, H, logits);
   else {
     const int cpl = (H / 8 + 63) / 64;
     switch (cpl) {
 #define MOE_RT(C)                                                                                  \
   case C:                                                                                          \
     hipLaunchKernelGGL((k_router<C>), dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits, fill, \
-                       n_fill, err);                                                               \
+                       n_fill);                                                                    \
     break;
       MOE_RT(1) MOE_RT(2) MOE_RT(3) MOE_RT(4) MOE_RT(5) MOE_RT(6) MOE_RT(7) MOE_RT(8)
       MOE_RT(9) MOE_RT(10) MOE_RT(11) MOE_RT(12) MOE_RT(13) MOE_RT(14) MOE_RT(15) MOE_RT(16)

@@ -88,8 +88,10 @@ moe_status moe_unpack_expert(const moe_shape* shape, const uint8_t* image,
  * Workspace.  One device buffer (256-byte aligned) used by moe_route, moe_bucket_routes,
  * moe_experts_forward and moe_layer_forward for calls with M <= max_M.  It carries logits,
  * route buckets, h and partial sums from one kernel of a call to the next, and in a fixed
- * header the device error word of the last call (moe_workspace_errors).  Calls sharing a
- * workspace must be ordered on one stream; concurrent calls need separate workspaces.
+ * header the device error word (moe_workspace_errors) and the state the one-token fused kernel
+ * keeps between calls.  Fill it with zeros once before its first use (any later call keeps the
+ * header consistent; the rest needs no initialisation).  Calls sharing a workspace must be
+ * ordered on one stream; concurrent calls need separate workspaces.
  * --------------------------------------------------------------------------------------- */
 moe_status moe_workspace_size(const moe_shape* shape, int32_t max_M, size_t* bytes /*[host]*/);
 
@@ -102,17 +104,17 @@ enum {
                               such a workgroup forms are NaN, never silently wrong */
 };
 
-/* Copy the device error word of the last call on this workspace to *flags, asynchronously on
- * stream [ORT hybrid PR, "Key Changes": the hot-expert kernel takes an optional expert_to_slot
- * map and skips routes whose slot is negative].  Routes whose id or slot lies outside that map's
- * contract are skipped like cold ones and reported here instead of being read out of bounds.
- * The word holds
- * the MOE_DEVERR_* flags raised by the last moe_route, moe_bucket_routes, moe_experts_forward,
- * moe_experts_gateup or moe_layer_forward* call on the workspace (0 = none; each of those calls
- * clears it in its first kernel; calls with M = 0 and moe_experts_down leave it as it was).
+/* Take the device error word of a workspace: copy it to *flags and clear it, asynchronously
+ * on stream (one small kernel, so it can be captured in a HIP graph) [ORT hybrid PR, "Key
+ * Changes": the hot-expert kernel takes an optional expert_to_slot map and skips routes whose
+ * slot is negative].  Routes whose id or slot lies outside that map's contract are skipped like
+ * cold ones and reported here instead of being read out of bounds.  The word accumulates: every
+ * call on the workspace ORs in the MOE_DEVERR_* flags it raises, so *flags holds those of every
+ * call since the last moe_workspace_errors (0 = none).
  * ws: the workspace (256-byte aligned, ws_bytes >= 256); flags: one int32 in device memory or
- * in pinned host memory, 4-byte aligned.  Read it after the stream has passed the copy. */
-moe_status moe_workspace_errors(const void* ws, size_t ws_bytes, int32_t* flags, hipStream_t stream);
+ * in pinned host memory, 4-byte aligned, or NULL (clear only).  Read it after the stream has
+ * passed the call. */
+moe_status moe_workspace_errors(void* ws, size_t ws_bytes, int32_t* flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Router [ninfer v0.4.0, "New": the router is no longer a single thread block;
