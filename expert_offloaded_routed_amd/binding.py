@@ -76,6 +76,8 @@ _SIGS = {
     "moe_slot_refill": [C.POINTER(moe_shape), _P, _P, _P, _P, _I32, _P, _P, _P],
     "moe_residual_bf16": [_P, _P, _P, _SZ, _P],
     "moe_workspace_errors": [_P, _SZ, _P, _P],
+    "moe_layer_forward_noalloc": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                  _P, _P, _P],
     "moe_cache_create": [C.POINTER(moe_shape), C.POINTER(moe_cache_config), _P,
                          C.POINTER(_P)],
     "moe_cache_policy_step": [_P, C.c_int64, _P, _I32, _P, C.POINTER(_I32), _P,
@@ -239,6 +241,16 @@ def moe_layer_forward_residual(shape, x, M, w_router, router_bias, expert_to_slo
                                              _ptr(cold_routes), _ptr(x_next), _ptr(ws), _nbytes(ws),
                                              _stream(stream)),
            "moe_layer_forward_residual")
+
+
+def moe_layer_forward_noalloc(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids,
+                              topk_w, y, cold_count, cold_routes, errors=None, stream=None):
+    """moe_layer_forward on the library's static scratch (no workspace argument, no allocation)."""
+    _check(load().moe_layer_forward_noalloc(C.byref(shape), _ptr(x), int(M), _ptr(w_router),
+                                            _ptr(router_bias), _ptr(expert_to_slot), _ptr(slots),
+                                            _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(cold_count),
+                                            _ptr(cold_routes), _ptr(errors), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def moe_layer_forward_marked(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids,

@@ -13,6 +13,8 @@
 
 namespace moe {
 
+static_assert(kScratchBytes == MOE_NOALLOC_SCRATCH_BYTES, "moe.h states the static scratch size");
+
 thread_local std::string g_last_error;
 
 moe_status fail(moe_status st, const char* fmt, ...) {
@@ -402,6 +404,38 @@ moe_status moe_layer_forward_residual(const moe_shape* shape, const uint16_t* x,
   if (!x_next) return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_residual: x_next is NULL");
   return layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids, topk_w,
                        y, cold_count, cold_routes, ws, ws_bytes, stream, nullptr, x_next);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                     const uint16_t* w_router, const float* router_bias,
+                                     const int32_t* expert_to_slot, const uint8_t* slots,
+                                     int32_t* topk_ids, float* topk_w, float* y,
+                                     int32_t* cold_count, int32_t* cold_routes, int32_t* errors,
+                                     hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (M < 0) return fail(MOE_ERR_INVALID_ARG, "M = %d < 0", M);
+  if ((size_t)M * shape->top_k > (size_t)kMaxRoutesPerCall)
+    return fail(MOE_ERR_UNSUPPORTED, "M * top_k > %d", kMaxRoutesPerCall);
+  const size_t need = ws_layout(shape->hidden, shape->inter, shape->n_experts, shape->top_k, M).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_layer_forward_noalloc: M=%d needs %zu bytes of workspace, more than the %zu of "
+                "the static scratch; use moe_layer_forward with a workspace",
+                M, need, kScratchBytes);
+  if (errors && (reinterpret_cast<uintptr_t>(errors) & 3))
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_noalloc: errors must be 4-byte aligned");
+  hipError_t e = hipSuccess;
+  void* ws = static_scratch(&e);
+  if (ws == nullptr) return hip_fail(e, "static scratch");
+  st = layer_forward(shape, x, M, w_router, router_bias, expert_to_slot, slots, topk_ids, topk_w, y,
+                     cold_count, cold_routes, ws, kScratchBytes, stream, nullptr, nullptr);
+  if (st != MOE_OK) return st;
+  if (errors) {
+    e = launch_take_errors(static_cast<int32_t*>(ws) + kMetaErr, errors, stream);
+    if (e != hipSuccess) return hip_fail(e, "error word launch");
+  }
+  return ok();
 }
 
 moe_status moe_layer_forward_marked(const moe_shape* shape, const uint16_t* x, int32_t M,

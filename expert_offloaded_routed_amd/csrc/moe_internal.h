@@ -201,6 +201,10 @@ hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const flo
                          int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s);
 // Copies the error word to *out (device or pinned host memory; NULL: nowhere) and clears it.
 hipError_t launch_take_errors(int32_t* word, int32_t* out, hipStream_t s);
+// The static scratch of the current device (the workspace of moe_layer_forward_noalloc):
+// kScratchBytes, 256-byte aligned, zero-filled at its first use; NULL and *err set on failure.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+void* static_scratch(hipError_t* err);
 bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M, int k);
 hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                                const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,

@@ -20,6 +20,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -2159,6 +2160,44 @@ __global__ __launch_bounds__(64) void k_take_errors(int32_t* __restrict__ word,
 hipError_t launch_take_errors(int32_t* word, int32_t* out, hipStream_t s) {
   hipLaunchKernelGGL(k_take_errors, dim3(1), dim3(64), 0, s, word, out);
   return hipGetLastError();
+}
+
+// =============================================================================================
+// Static scratch: the workspace of moe_layer_forward_noalloc, for callers that cannot allocate
+// =============================================================================================
+// One array per GPU, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and only that address is ever used.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+void* static_scratch(hipError_t* err) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    // the header (error word, the fused kernel's call counter) must start at zero: cleared once
+    // here, synchronously (not in a stream a caller might be capturing)
+    if (e == hipSuccess) e = hipMemset(p, 0, kScratchBytes);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+      *err = e;
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  *err = hipSuccess;
+  return addr[dev];
 }
 
 // =============================================================================================

@@ -206,6 +206,27 @@ moe_status moe_layer_forward_marked(const moe_shape* shape, const uint16_t* x, i
                                     void* ws, size_t ws_bytes, hipStream_t stream,
                                     const hipEvent_t* marks);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The workspace is a static array inside the library, one per GPU, of MOE_NOALLOC_SCRATCH_BYTES
+ * (8 MiB), held until the process ends; the call allocates nothing and calls no allocating
+ * routine.  A call whose workspace (moe_workspace_size for its M) exceeds that size is
+ * rejected with MOE_ERR_WORKSPACE before anything is enqueued (the one-token decode and the
+ * few-token calls fit; large prefills do not).  Every call on a GPU shares that GPU's array and
+ * it keeps the last call's contents: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  The first call on a device clears the array
+ * synchronously, so it must not be made while a stream is being captured.
+ * errors: one int32 (device or pinned host memory) or NULL: after the call's kernels the
+ * array's device error word (MOE_DEVERR_*, see moe_workspace_errors) is copied there and
+ * cleared.  Other arguments and results are those of moe_layer_forward, bitwise. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+moe_status moe_layer_forward_noalloc(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                     const uint16_t* w_router, const float* router_bias,
+                                     const int32_t* expert_to_slot, const uint8_t* slots,
+                                     int32_t* topk_ids, float* topk_w, float* y,
+                                     int32_t* cold_count, int32_t* cold_routes, int32_t* errors,
+                                     hipStream_t stream);
+
 /* Number of kernel launches moe_layer_forward makes for M tokens of this shape: 2 when gate/up
  * and down run as one launch, 3 for small calls, 4 past 256 routes, 5 on the grouped-GEMM path
  * (M >= 64), 1 for M = 0.  For callers that budget graph nodes or time stages.  Writes *n; no
