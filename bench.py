@@ -200,13 +200,17 @@ def bench_decode(args):
         for e in m:
             B.event_destroy(e)
     us_rt, us_gu, us_dn = (float(v) for v in st.mean(axis=0))
-    fused = B.moe_layer_launches(shape, 1) == 2
+    launches = B.moe_layer_launches(shape, 1)
+    fused = launches <= 2
     if fused:  # marks[2] and marks[3] both follow the one expert launch
         dom_bytes, dom_us, dom_key = step_bytes, us_gu, "layer_decode_bytes_per_launch"
-        dom_name = ("k_layer_decode (route table + MXFP4 gate/up GEMV + SiLU*up, then down GEMV + "
-                    "ordered combine, one launch)")
-        stages = {"route (router GEMV)": round(us_rt, 2),
-                  "experts (fused gate/up + down + combine)": round(us_gu, 2)}
+        dom_name = ("k_layer_decode (" + ("router GEMV, " if launches == 1 else "") +
+                    "route table + MXFP4 gate/up GEMV + SiLU*up, then down GEMV + ordered combine, "
+                    "one launch)")
+        stages = ({"layer (router, route table, gate/up, down, combine: one launch)": round(us_gu, 2)}
+                  if launches == 1 else
+                  {"route (router GEMV)": round(us_rt, 2),
+                   "experts (fused gate/up + down + combine)": round(us_gu, 2)})
     else:
         dom_bytes, dom_us, dom_key = gu_bytes, us_gu, "gateup_bytes_per_launch"
         dom_name = "k_gateup (route table + fused MXFP4 gate/up GEMV + SiLU*up)"

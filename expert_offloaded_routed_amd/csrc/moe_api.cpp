@@ -241,24 +241,27 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_residual: x_next must be 2-byte aligned");
   float* logits = at<float>(ws, W.logits);
   hipError_t e;
-  // One token with a fusable shape: gate/up and down run as one launch (the router fills the h
-  // rows it hands over with the "not yet written" pattern).  MOE_DECODE_UNFUSED=1 in the
-  // environment selects the multi-launch path.
+  // One token with a fusable shape: the layer after the router (or the whole layer, router
+  // included, for small routers) is one launch.  MOE_DECODE_UNFUSED=1 in the environment selects
+  // the multi-launch path.
   const ImageLayout L = image_layout(shape->hidden, shape->inter);
   const ExpertPlan p = plan_experts(L, M, shape->n_experts, shape->top_k);
-  const bool fused = !decode_unfused() && layer_decode_fusable(L, p, M, shape->top_k);
-  uint16_t* hbuf = at<uint16_t>(ws, W.hq);
+  const bool fused =
+      !decode_unfused() && layer_decode_fusable(L, p, M, shape->top_k, shape->n_experts);
+  const bool router_inside = fused && layer_decode_router_inside(L, shape->n_experts);
   if (marks && (e = record_mark(marks[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
-                    fused ? reinterpret_cast<uint32_t*>(hbuf) : nullptr,
-                    fused ? M * shape->top_k * shape->inter / 2 : 0, stream);
-  if (e != hipSuccess) return hip_fail(e, "router launch");
+  if (!router_inside) {
+    e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
+                      stream);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+  }
   if (fused) {
     if (marks && (e = record_mark(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-    const RouteArgs ra = route_args(shape, M, logits, topk_ids, topk_w, expert_to_slot, topk_ids,
-                                    topk_w, cold_count, cold_routes);
-    e = launch_layer_decode(x, M, shape->hidden, shape->inter, slots, L, p, ra, route_ws(ws, W),
-                            hbuf, y, Residual{x, x_next}, stream);
+    const RouteArgs ra = route_args(shape, M, router_inside ? nullptr : logits, topk_ids, topk_w,
+                                    expert_to_slot, topk_ids, topk_w, cold_count, cold_routes);
+    e = launch_layer_decode(x, w_router, router_bias, M, shape->hidden, shape->inter, slots, L, p,
+                            ra, route_ws(ws, W), at<uint64_t>(ws, W.hf), y, Residual{x, x_next},
+                            stream);
     if (e != hipSuccess) return hip_fail(e, "fused decode launch");
     for (int i = 2; marks && i < 4; ++i)
       if ((e = record_mark(marks[i], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -308,8 +311,8 @@ moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n) {
   }
   const ImageLayout L = image_layout(shape->hidden, shape->inter);
   const ExpertPlan p = plan_experts(L, M, shape->n_experts, shape->top_k);
-  if (!decode_unfused() && layer_decode_fusable(L, p, M, shape->top_k))
-    *n = 2;                     // router, fused experts
+  if (!decode_unfused() && layer_decode_fusable(L, p, M, shape->top_k, shape->n_experts))
+    *n = layer_decode_router_inside(L, shape->n_experts) ? 1 : 2;  // [router,] fused layer
   else if (p.grouped)
     *n = 5;                     // router, top-k / bucket, gate/up, down, combine
   else
@@ -332,7 +335,7 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, int32_t M, const
     return fail(MOE_ERR_INVALID_ARG, "moe_route: x and w_router must be 16-byte aligned");
   float* logits = at<float>(ws, W.logits);
   hipError_t e = launch_router(x, M, w_router, router_bias, shape->n_experts, shape->hidden, logits,
-                               nullptr, 0, stream);
+                               stream);
   if (e != hipSuccess) return hip_fail(e, "router launch");
   const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
   e = launch_topk_bucket(logits, M, shape->top_k, topk_ids, topk_w, false, topk_ids,

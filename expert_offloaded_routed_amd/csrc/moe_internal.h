@@ -94,9 +94,14 @@ __host__ __device__ inline int router_parts(int M, int E) {
 // the last call's size), int32 meta[kMetaWords]:
 //   [0] distinct hot experts of the call, [1] its cold routes, [2] the device error flags
 //   (kErr* bits) that the calls on this workspace raised since moe_workspace_errors last took
-//   them (kernels only OR bits in), [3] length of the grouped work list.
+//   them (kernels only OR bits in), [3] length of the grouped work list, [6] the fused
+//   one-token launches' call id and [7] their poison word (both zero in a zero-filled
+//   workspace; see k_layer_decode).
+// Then, also at a fixed offset, the tagged h words of the fused one-token kernel (no other
+// kernel writes there, so a stale word can only carry an older call's tag).
 struct WsLayout {
   size_t meta;           // i32 [kMetaWords], offset 0
+  size_t hf;             // u64 [kFusedMaxK][kMaxInter / 2]: {h pair, call tag}, fixed offset
   size_t logits;         // f32 [router_parts(M, E)][M][E]
   size_t route_slot;     // i32 [M*k]
   size_t counts;         // i32 [E]
@@ -115,6 +120,13 @@ inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 constexpr int kMetaWords = 16;  // int32 words of the workspace header
 constexpr int kMetaErr = 2;     // index of the error word
+constexpr int kMetaCall = 6;    // fused one-token kernel: call id (8-byte aligned with ...)
+constexpr int kMetaPoison = 7;  // ... the poison word: a launch lost its hand-over of h
+constexpr size_t kFusedHBytes = (size_t)16 * kMaxInter * 4;  // tagged h of up to 16 routes
+// The fused one-token kernel computes the router itself for at most this many experts of at
+// most 8 chunks of 8 per lane (H <= 4096); larger routers run as their own kernel first.
+constexpr int kFusedRouterMaxE = 32;
+constexpr int kFusedRouterMaxCPL = 8;
 
 // Grouped GEMM work items: (distinct hot expert, pass of up to kItemRoutes of its routes).
 // sum over experts of ceil(c_e / kItemRoutes) <= (number of experts) + M*k / kItemRoutes.
@@ -131,6 +143,7 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   const size_t nd = Mk < (size_t)E ? Mk : (size_t)E;
   size_t o = 0;
   W.meta = o;        o = align256(o + 4 * (size_t)kMetaWords);
+  W.hf = o;          o = align256(o + kFusedHBytes);
   W.logits = o;      o = align256(o + 4 * (size_t)router_parts(M, E) * M * E);
   W.route_slot = o;  o = align256(o + 4 * Mk);
   W.counts = o;      o = align256(o + 4 * (size_t)E);
@@ -198,18 +211,22 @@ struct Residual {
 
 // Kernel launchers (moe_kernels.hip).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s);
+                         int H, float* logits, hipStream_t s);
 // Copies the error word to *out (device or pinned host memory; NULL: nowhere) and clears it.
 hipError_t launch_take_errors(int32_t* word, int32_t* out, hipStream_t s);
 // The static scratch of the current device (the workspace of moe_layer_forward_noalloc):
 // kScratchBytes, 256-byte aligned, zero-filled at its first use; NULL and *err set on failure.
 constexpr size_t kScratchBytes = (size_t)8 << 20;
 void* static_scratch(hipError_t* err);
-bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M, int k);
-hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
-                               const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                               const RouteWs& rw, uint16_t* hbuf, float* y, Residual res,
-                               hipStream_t s);
+bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M, int k, int E);
+// The fused one-token kernel computes the router itself (no router launch before it).
+bool layer_decode_router_inside(const ImageLayout& L, int E);
+// wr / bias: the router, used when layer_decode_router_inside (else ra.logits holds the logits);
+// hf: the workspace's tagged h region.
+hipError_t launch_layer_decode(const uint16_t* x, const uint16_t* wr, const float* bias, int M,
+                               int H, int I, const uint8_t* slots, const ImageLayout& L,
+                               const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
+                               uint64_t* hf, float* y, Residual res, hipStream_t s);
 // logits: router_parts(M, E) partial rows per token (see kRouterParts).
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,

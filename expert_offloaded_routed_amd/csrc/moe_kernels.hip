@@ -35,18 +35,14 @@ namespace moe {
 
 // CPL = ceil(H/8/64) chunks per lane.  Every load is issued unconditionally (chunk index
 // clamped, the product of a chunk past the row selected away), so that no load waits alone in
-// a branch.  The workgroups also fill n_fill words at fill with 0xFFFFFFFF: the h rows of the
-// fused decode kernel that follows, which hands h over by value and takes 0xFFFF for "not yet
-// written" (the kernel boundary makes the fill visible to it).
+// a branch.
 template <int CPL>
 __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, int M,
                                                const uint16_t* __restrict__ wr,
                                                const float* __restrict__ bias, int E, int H,
-                                               float* __restrict__ logits,
-                                               uint32_t* __restrict__ fill, int n_fill) {
+                                               float* __restrict__ logits) {
   const int lane = threadIdx.x;
   const int e = blockIdx.x;
-  for (int i = e * 64 + lane; i < n_fill; i += E * 64) fill[i] = 0xFFFFFFFFu;
   const int nch = H / 8;
   const uint4* wsrc = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
   uint4 wrow[CPL];
@@ -555,17 +551,13 @@ constexpr size_t kGuLdsBytes = 64 * 1024;  // LDS of a gate/up workgroup at most
 // prefix count.  Contains a workgroup barrier (every thread calls it).
 constexpr int kFastE = 64;
 
-__device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs& a) {
+// The table from this lane's logit `own` (expert lane, lanes < E) and expert map entry `e2v`.
+__device__ __forceinline__ void route_token_small_v(RouteLds& rt, const RouteArgs& a, float own,
+                                                    int e2v) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int E = a.E;
-  const float* lrow = a.logits;  // row 0; the workspace holds at least 256 bytes of logits
-  // Every load is issued before any value is used, and unconditionally (the expert map read
-  // falls back to a dummy read of the logits), so that they share one round trip.
   const int lc = lane < E ? lane : 0;
-  const float own = lrow[lc];
-  const int32_t* e2p = a.e2s != nullptr ? a.e2s : reinterpret_cast<const int32_t*>(lrow);
-  const int e2v = e2p[lc];
   const uint64_t key = lane < E ? rank_key64(own, lane) : 0ull;  // 0 is below every key
   for (int i = wave; i < E; i += nw) {
     const int r = (int)__popcll(__ballot(key > readlane_u64(key, i)));
@@ -603,6 +595,18 @@ __device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs&
     rt.nd = __popcll(hm);
     rt.err = bad ? kErrBadSlot : 0;
   }
+}
+
+__device__ __forceinline__ void route_token_small(RouteLds& rt, const RouteArgs& a) {
+  const int lane = threadIdx.x & 63;
+  const float* lrow = a.logits;  // row 0; the workspace holds at least 256 bytes of logits
+  // Every load is issued before any value is used, and unconditionally (the expert map read
+  // falls back to a dummy read of the logits), so that they share one round trip.
+  const int lc = lane < a.E ? lane : 0;
+  const float own = lrow[lc];
+  const int32_t* e2p = a.e2s != nullptr ? a.e2s : reinterpret_cast<const int32_t*>(lrow);
+  const int e2v = e2p[lc];
+  route_token_small_v(rt, a, own, e2v);
 }
 
 // One token over any number of experts: top-k by wave 0 (topk_token), then the route table in
@@ -1376,32 +1380,40 @@ __global__ __launch_bounds__(256) void k_down_mx(
 }
 
 // =============================================================================================
-// Fused decode: the expert part of one token in one launch, h handed over by value
+// Fused decode: one token's layer in one launch, h handed over by value
 // =============================================================================================
 // One workgroup of 16 waves per compute unit, the grid at most the CU count (so it is resident
-// at once, one workgroup per CU).  The work is cut into units: a gate/up unit is 16 h values of
-// one hot expert (their 16 gate and 16 up rows over all of K: image lanes 16f..16f+15 and
-// 32+16f..32+16f+15 of gate/up tile t), a down unit is 8 output rows (rows 8f..8f+7 of a 16-row
-// down tile) over every hot expert.  At H = I the two kinds weigh the same bytes.  Workgroup w
-// takes an equal contiguous share of each kind (the down shares in reverse workgroup order, so
-// that shares which round up rarely meet in one workgroup) and requests every weight byte of
-// its units at once, the 16 waves splitting each unit's K.  Then it
+// at once, one workgroup per CU).  Every workgroup first computes the router itself when it is
+// small (E <= 32 rows of H <= 4096: each wave two rows, with the arithmetic of k_router, from
+// L2) or reads the logits of a router kernel, and builds the route table in LDS.  The work is cut
+// into units: a gate/up unit is 16 h values of one hot expert (their 16 gate and 16 up rows over
+// all of K: image lanes 16f..16f+15 and 32+16f..32+16f+15 of gate/up tile t), a down unit is 8
+// output rows (rows 8f..8f+7 of a 16-row down tile) over every hot expert.  At H = I the two
+// kinds weigh the same bytes.  Workgroup w takes an equal contiguous share of each kind (the down
+// shares in reverse workgroup order, so that shares which round up rarely meet in one workgroup)
+// and requests every weight byte of its units at once, the 16 waves splitting each unit's K.
+// Then it
 //   1. forms its gate/up units: per-lane block dots, the lane pair of a row and the waves summed
-//      in a fixed order, h = bf16(silu(g)*u) stored write-through (device-scope relaxed
-//      stores);
-//   2. each wave gathers the h its down entries read into LDS by polling: the router kernel of
-//      the same call has filled the h rows with 0xFFFF, a bit pattern the h writer never stores
-//      (it writes NaN as 0x7FC0), so an element that differs from it is final.  The loads
-//      bypass the non-coherent caches;
+//      in a fixed order, h = bf16(silu(g)*u), two values per 64-bit word whose high half is the
+//      call's tag, stored write-through (device-scope relaxed stores);
+//   2. each wave gathers the h its down entries read into LDS by polling those words (loads
+//      that bypass the non-coherent caches) until their tag is the call's: a 64-bit store is
+//      seen whole or not at all, so a word with the right tag holds this call's values;
 //   3. forms its down units (each wave its entries as soon as its h is in) and y for their
 //      rows, hot routes in ascending order (+ residual).
-// No counter, fence or read-modify-write is involved.  The gather is bounded: a launch that ran
-// out of it flags kErrHandoff in meta[2] (it cannot happen with the grid resident).
+// The tag is the call id + 1.  The call id lives in the workspace header: every workgroup reads
+// it at its start, and workgroup 0 advances it once its gather has seen every h word with this
+// call's tag (so every h writer has read it).  A zero-filled workspace starts at call 0 with
+// every h word tagged 0.  The tagged words have a region of the workspace of their own, at a
+// fixed offset, that no other kernel writes.  No atomic read-modify-write is involved.  The
+// gather is bounded: a workgroup that runs out of it flags kErrHandoff and writes NaN instead of
+// its y rows (it cannot happen with the grid resident); if that is workgroup 0, it poisons the
+// workspace and every later launch on it flags and writes NaN until it is zero-filled again.
 constexpr int kFusedWaves = 16;
 constexpr int kFusedThreads = kFusedWaves * 64;
 constexpr int kFusedMaxK = 16;      // routes (hot experts) of the token at most
-constexpr int kHandSpins = 1 << 13; // gather rounds at most (each ~1 us: a round trip + sleep)
-constexpr uint32_t kHSentinel = 0xFFFFu;
+constexpr int kHandSpins = 1 << 13; // gather rounds at most (each about a load round trip)
+static_assert(kFusedMaxK * kMaxInter * 4 == kFusedHBytes, "tagged h region of the workspace");
 
 // n / d by a multiply: m = floor((2^32 - 1) / d) + 1 (0 for d = 1) gives floor(n * m / 2^32) =
 // n / d exactly while n * (d - 1) < 2^32 (the launcher checks the bounds of every use).
@@ -1424,14 +1436,6 @@ __device__ __forceinline__ void lds_barrier() {
 }
 // v clamped to [lo, hi]; lo when the range is empty
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return max(min(v, hi), lo); }
-// True when none of the 8 bf16 elements of a chunk is the sentinel.
-__device__ __forceinline__ bool h_chunk_final(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  bool ok = true;
-  const uint32_t w[4] = {a, b, c, d};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ok = ok && (w[i] & 0xFFFFu) != kHSentinel && (w[i] >> 16) != kHSentinel;
-  return ok;
-}
 
 // Scale byte j of word w as a float, or zero when !keep.  Branch-free (a mask, not a
 // conditional): a conditional use lets the compiler sink the word's load into the branch and
@@ -1494,18 +1498,71 @@ __host__ __device__ __forceinline__ size_t fused_lds_bytes(int H, int I, int k, 
          (size_t)nud * k * (kFusedWaves + 1) * 8 * 4;
 }
 
-template <int NUG, int NEG, int NUD, int NED>
+// ---- the router inside the fused kernel ----------------------------------------------------
+// Each wave computes the logits of two experts with the arithmetic of k_router<CPL> (lane l sums
+// the bf16 dot products of chunks l, l + 64, ... in that order, then the wave sum, then the
+// bias), so the logits are bitwise those of moe_route.  Every workgroup reads all the rows (from
+// L2); the rows a wave takes rotate with the workgroup index, so that the compute units of an
+// XCD do not all ask the same L2 channel for the same row at once.  The rows are requested
+// first; then this thread's chunk of x (xr, already requested) goes to LDS and a barrier
+// publishes it; the products read x from there.  Rows past E re-read the last row and are
+// dropped.  Contains a workgroup barrier (every thread calls it).
+template <int CPL>
+__device__ __forceinline__ void fused_router(const uint16_t* __restrict__ wr,
+                                             const float* __restrict__ bias, int E, int H,
+                                             uint16_t* xs, const uint4& xr, float* s_logit) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nch = H / 8;
+  const int rot = (wave + (int)blockIdx.x) & (kFusedWaves - 1);
+  const int e0 = rot, e1 = rot + kFusedWaves;
+  const uint4* r0 = reinterpret_cast<const uint4*>(wr + (size_t)min(e0, E - 1) * H);
+  const uint4* r1 = reinterpret_cast<const uint4*>(wr + (size_t)min(e1, E - 1) * H);
+  uint4 w0[CPL], w1[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) w0[i] = r0[min(lane + 64 * i, nch - 1)];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) w1[i] = r1[min(lane + 64 * i, nch - 1)];
+  const float* bp = bias != nullptr ? bias : reinterpret_cast<const float*>(wr);  // (a valid address)
+  const float b0 = bp[min(e0, E - 1)], b1 = bp[min(e1, E - 1)];
+  if ((int)threadIdx.x < nch) reinterpret_cast<uint4*>(xs)[threadIdx.x] = xr;
+  lds_barrier();  // x in LDS; the row loads stay in flight
+  const uint4* xv = reinterpret_cast<const uint4*>(xs);
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const uint4 xc = xv[min(lane + 64 * i, nch - 1)];
+    const float v0 = dot8_bf16(w0[i], xc, a0);
+    const float v1 = dot8_bf16(w1[i], xc, a1);
+    a0 = lane + 64 * i < nch ? v0 : a0;
+    a1 = lane + 64 * i < nch ? v1 : a1;
+  }
+  a0 = wave_sum(a0);
+  a1 = wave_sum(a1);
+  if (lane == 0) {
+    if (e0 < E) s_logit[e0] = a0 + (bias != nullptr ? b0 : 0.0f);
+    if (e1 < E) s_logit[e1] = a1 + (bias != nullptr ? b1 : 0.0f);
+  }
+}
+
+// ROUTER: the router runs inside (wr, bias, rcpl = H/8/64 chunks per lane); else the logits of a
+// router kernel are in the workspace (ra.logits).
+template <int NUG, int NEG, int NUD, int NED, bool ROUTER>
 __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
-    const uint16_t* __restrict__ x, int H, int I, const uint8_t* __restrict__ slots,
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
+    int rcpl, int H, int I, const uint8_t* __restrict__ slots,
     size_t image_bytes, size_t gu_tile_bytes, int nb, size_t gu_bytes, size_t dn_tile_bytes,
     size_t dn_code_bytes, int ks, int full, int rem, int nb_i, RouteArgs ra, RouteWs rw,
-    uint16_t* __restrict__ hbuf, float* __restrict__ y, Residual res, FusedDivs dv) {
+    uint64_t* __restrict__ hf, float* __restrict__ y, Residual res, FusedDivs dv) {
   __shared__ RouteLds rt;
   __shared__ int s_dist_of_route[kFusedMaxK];  // one token: route j -> its hot expert index
   __shared__ int s_late;                       // a wave's gather of h ran out of rounds
+  __shared__ uint32_t s_tag;                   // this call's tag of the h words
+  __shared__ float s_logit[ROUTER ? kFusedRouterMaxE : 1];
   extern __shared__ __align__(16) uint8_t fsm[];
   const int lane = threadIdx.x & 63;
-  if (threadIdx.x == 0) s_late = 0;  // (the route prologue's barriers publish it)
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(rw.meta);
+  if (threadIdx.x == 0) s_late = 0;  // (the barriers below publish it)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int G = gridDim.x, wg = blockIdx.x;
   const int K = ra.k;
@@ -1516,11 +1573,34 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   float* sum_dn = red_dn + NUD * K * kFusedWaves * 8;    // [NUD][K][8]
 
   // x: one 16-byte chunk per thread (H / 8 <= threads), requested first; it lands with the
-  // route table's loads and goes to LDS right after the table is built
+  // router rows (ROUTER) or the route table's loads and goes to LDS
   const int n_x = H / 8;
   const uint4 xr = reinterpret_cast<const uint4*>(x)[min((int)threadIdx.x, n_x - 1)];
-  route_prologue(rt, ra, rw, wg == 0);
-  if ((int)threadIdx.x < n_x) reinterpret_cast<uint4*>(xs)[threadIdx.x] = xr;
+  if constexpr (ROUTER) {
+    const int lc = lane < ra.E ? lane : 0;
+    const int32_t* e2p = ra.e2s != nullptr ? ra.e2s : reinterpret_cast<const int32_t*>(wr);
+    const int e2v = e2p[lc];  // (with no map: a dummy read, unused)
+    switch (rcpl) {  // (uniform)
+      case 1: fused_router<1>(wr, bias, ra.E, H, xs, xr, s_logit); break;
+      case 2: fused_router<2>(wr, bias, ra.E, H, xs, xr, s_logit); break;
+      case 3: fused_router<3>(wr, bias, ra.E, H, xs, xr, s_logit); break;
+      case 4: fused_router<4>(wr, bias, ra.E, H, xs, xr, s_logit); break;
+      case 5: fused_router<5>(wr, bias, ra.E, H, xs, xr, s_logit); break;
+      case 6: fused_router<6>(wr, bias, ra.E, H, xs, xr, s_logit); break;
+      case 7: fused_router<7>(wr, bias, ra.E, H, xs, xr, s_logit); break;
+      default: fused_router<8>(wr, bias, ra.E, H, xs, xr, s_logit); break;
+    }
+    __syncthreads();  // the logits
+    route_token_small_v(rt, ra, s_logit[lc], ra.e2s != nullptr ? e2v : lc);
+    __syncthreads();
+    if (wg == 0) {
+      write_routes(rt, ra.k, ra.topk_ids, ra.topk_w, ra.cold_count, ra.cold_routes, nullptr);
+      write_table(rt, ra.k, rw);
+    }
+  } else {
+    route_prologue(rt, ra, rw, wg == 0);
+    if ((int)threadIdx.x < n_x) reinterpret_cast<uint4*>(xs)[threadIdx.x] = xr;
+  }
   const int nd = rt.nd;
   const int ugpe = I / 16;  // gate/up units per hot expert
   const int Ug = nd * ugpe;
@@ -1588,6 +1668,12 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       const int b = min(2 * (gp0 + clampi(e, 0, ngp - 1)) + half, nb - 1);
       cg[ug][e] = reinterpret_cast<const uint4*>(gtb[ug])[b * 64 + gilf[ug]];
     }
+  // The call id and the poison word (thread 0), needed only when h is stored: requested behind
+  // the gate/up weights, so that nothing waits for them before.
+  uint64_t callw = 0;
+  if (threadIdx.x == 0)
+    callw = __hip_atomic_load(reinterpret_cast<uint64_t*>(&hdr[kMetaCall]), __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_sched_barrier(0);
   // x in LDS for every wave (the gate/up loads stay in flight)
   lds_barrier();
@@ -1634,10 +1720,21 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
     for (int e = 0; e < NED; ++e) cd[ud][e] = reinterpret_cast<const uint4*>(dtb[ud][e])[dix[ud][e]];
   __builtin_amdgcn_sched_barrier(0);
+  // this call's tag; a poisoned workspace (an earlier launch lost its hand-over) makes this
+  // workgroup's rows NaN
+  const uint32_t call = (uint32_t)callw;
+  if (threadIdx.x == 0) {
+    s_tag = call + 1u;
+    if ((uint32_t)(callw >> 32) != 0u) {
+      s_late = 1;
+      atomicOr(&rw.meta[kMetaErr], kErrHandoff);
+    }
+  }
   __syncthreads();
+  const uint32_t tag = s_tag;
   if ((int)threadIdx.x < NUG * 16) {
     const int ug = threadIdx.x >> 4, r = threadIdx.x & 15;
-    if (ug < ngu) {
+    if (ug < ngu) {  // (the same for both lanes of a pair)
       // (unrolled: the 32 LDS reads issue back to back)
       float g = 0.0f, u = 0.0f;
 #pragma unroll
@@ -1648,9 +1745,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       const int uu = gu_lo + ug;
       const int d = div_m(uu, dv.ugpe), t2 = uu - d * ugpe;
       const int route = rt.perm[rt.dist_off[d]];
-      __hip_atomic_store(&hbuf[(size_t)route * I + (t2 >> 1) * 32 + 16 * (t2 & 1) + r],
-                         (uint16_t)f32_to_bf16_bits(silu_f32(g) * u), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t hv = f32_to_bf16_bits(silu_f32(g) * u);
+      const uint32_t hn = (uint32_t)__shfl_down((int)hv, 1);  // the pair's odd element
+      if ((r & 1) == 0) {
+        const size_t pos = (size_t)route * I + (t2 >> 1) * 32 + 16 * (t2 & 1) + r;  // even
+        __hip_atomic_store(&hf[pos >> 1], (uint64_t)(hv | (hn << 16)) | ((uint64_t)tag << 32),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
   if (ndn == 0) {  // no down unit here: the down loads (dummies) drain before the exit
@@ -1675,27 +1776,26 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     }
 
   // ---- 2. this wave's h into LDS ----
-  // Entry (hot expert ex, step pair p) reads h[ex][256p, 256p + 256) (clamped to I): 32 chunks
-  // of 16 bytes.  Each wave polls the chunks of its own entries only, lane l taking chunk l & 31
-  // of entries 2i + (l >> 5), and a lane re-requests a chunk only until it is final.  No other
-  // wave reads these LDS bytes (a wave's own LDS operations complete in order), so the products
-  // of a wave start as soon as its own h has landed, with no workgroup barrier.
+  // Entry (hot expert ex, step pair p) reads h[ex][256p, 256p + 256) (clamped to I): 64 chunks
+  // of 4 values (two tagged words, 16 bytes).  Each wave polls the chunks of its own entries
+  // only, lane l taking chunk l of each, and a lane re-requests a chunk only until both its
+  // words carry the call's tag.  No other wave reads these LDS bytes (a wave's own LDS
+  // operations complete in order), so the products of a wave start as soon as its own h has
+  // landed, with no workgroup barrier.
   {
-    constexpr int PC = (NED + 1) / 2;
-    const int c = lane & 31;
+    constexpr int PC = NED;
     const uint64_t* src[PC];
     int dst[PC];
     bool need[PC];
 #pragma unroll
     for (int i = 0; i < PC; ++i) {
-      const int e = 2 * i + half;
-      const int q = dq0 + clampi(e, 0, ndq - 1);
+      const int q = dq0 + clampi(i, 0, ndq - 1);
       const int ex = div_m(q, dv.np2);
       const int exc = clampi(ex, 0, max(nd - 1, 0));
       const int route = nd > 0 ? rt.perm[rt.dist_off[exc]] : 0;
-      const int off = min(256 * (q - ex * np2) + 8 * c, I - 8);
-      need[i] = e < ndq && ex < nd;
-      src[i] = reinterpret_cast<const uint64_t*>(hbuf + (size_t)route * I + off);
+      const int off = min(256 * (q - ex * np2) + 4 * lane, I - 4);
+      need[i] = i < ndq && ex < nd;
+      src[i] = hf + (((size_t)route * I + off) >> 1);
       dst[i] = exc * I + off;
     }
     bool late = false;
@@ -1711,10 +1811,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
       for (int i = 0; i < PC; ++i)
         if (need[i]) {
-          const uint32_t w0 = (uint32_t)v[i][0], w1 = (uint32_t)(v[i][0] >> 32);
-          const uint32_t w2 = (uint32_t)v[i][1], w3 = (uint32_t)(v[i][1] >> 32);
-          if (h_chunk_final(w0, w1, w2, w3)) {
-            reinterpret_cast<uint4*>(hs)[dst[i] / 8] = make_uint4(w0, w1, w2, w3);
+          if ((uint32_t)(v[i][0] >> 32) == tag && (uint32_t)(v[i][1] >> 32) == tag) {
+            reinterpret_cast<uint2*>(hs)[dst[i] / 4] = make_uint2((uint32_t)v[i][0], (uint32_t)v[i][1]);
             need[i] = false;
           } else {
             left = true;
@@ -1725,7 +1823,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
         late = true;
         break;
       }
-      __builtin_amdgcn_s_sleep(4);
+      __builtin_amdgcn_s_sleep(1);
     }
     if (late && lane == 0) {
       atomicOr(&rw.meta[kMetaErr], kErrHandoff);
@@ -1783,6 +1881,18 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   constexpr int T = 64 / (NUD * 8);  // slots per row in the one-wave form
   const int row0 = 8 * dn_lo;
   const bool late_wg = s_late != 0;  // (written before the barrier above)
+  // Workgroup 0 (which always has a down unit) has now seen every h word of every hot expert
+  // with this call's tag, so every workgroup that stores h has read the call id: it advances the
+  // id for the next launch.  (A workgroup with no gate/up unit that started even later reads the
+  // advanced id, finds no word with its tag and flags the call; none of its words exist.)  If
+  // its gather ran out of rounds, some workgroup may not have read the id yet: the id stays and
+  // the workspace is poisoned instead, so that no later launch can take a word of this one.
+  if (wg == 0 && threadIdx.x == 0) {
+    if (late_wg)
+      __hip_atomic_store(&hdr[kMetaPoison], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      __hip_atomic_store(&hdr[kMetaCall], call + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   auto store_y = [&](int row, float acc_y) {
     if (late_wg) acc_y = __uint_as_float(0x7FC00000u);  // never a silently wrong value
     y[row] = acc_y;
@@ -2218,7 +2328,7 @@ __global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ x
 // Launchers (called from the host API after every argument has been validated)
 // =============================================================================================
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
-                         int H, float* logits, uint32_t* fill, int n_fill, hipStream_t s) {
+                         int H, float* logits, hipStream_t s) {
   if (M >= kGroupedMinTokens)  // a dense GEMM: MFMA
     hipLaunchKernelGGL(k_router_grouped, dim3((M + kGemmTok - 1) / kGemmTok, (E + 63) / 64, router_parts(M, E)), dim3(256),
                        0, s, x, M, wr, bias, E, H, logits);
@@ -2227,8 +2337,7 @@ hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const flo
     switch (cpl) {
 #define MOE_RT(C)                                                                                  \
   case C:                                                                                          \
-    hipLaunchKernelGGL((k_router<C>), dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits, fill, \
-                       n_fill);                                                                    \
+    hipLaunchKernelGGL((k_router<C>), dim3(E), dim3(64), 0, s, x, M, wr, bias, E, H, logits);     \
     break;
       MOE_RT(1) MOE_RT(2) MOE_RT(3) MOE_RT(4) MOE_RT(5) MOE_RT(6) MOE_RT(7) MOE_RT(8)
       MOE_RT(9) MOE_RT(10) MOE_RT(11) MOE_RT(12) MOE_RT(13) MOE_RT(14) MOE_RT(15) MOE_RT(16)
@@ -2455,7 +2564,7 @@ static int device_cus() {
 
 // The answer depends on the dynamic LDS of the launch (it varies with H, I and k), so the cache
 // holds the LDS size it was asked for with it: {lds, 1 fits / -1 does not} per device.
-template <int NUG, int NEG, int NUD, int NED>
+template <int NUG, int NEG, int NUD, int NED, bool ROUTER>
 static bool fused_resident(size_t lds) {
   static std::atomic<int64_t> cache[16];  // [device]: lds << 2 | (1 fits, 2 does not); 0 unknown
   int dev = 0;
@@ -2464,7 +2573,7 @@ static bool fused_resident(size_t lds) {
   if (v != 0 && (size_t)(v >> 2) == lds) return (v & 3) == 1;
   int per_cu = 0;
   const bool fits = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &per_cu, k_layer_decode<NUG, NEG, NUD, NED>, kFusedThreads, lds) == hipSuccess &&
+                        &per_cu, k_layer_decode<NUG, NEG, NUD, NED, ROUTER>, kFusedThreads, lds) == hipSuccess &&
                     per_cu >= 1;
   cache[dev].store(((int64_t)lds << 2) | (fits ? 1 : 2), std::memory_order_relaxed);
   return fits;
@@ -2474,7 +2583,13 @@ static uint32_t div_magic(uint32_t d) { return d <= 1 ? 0u : (uint32_t)(0xFFFFFF
 // div_m is exact for numerators up to n_max with divisor d
 static bool div_exact(uint64_t n_max, uint64_t d) { return d >= 1 && n_max * (d - 1) < (1ull << 32); }
 
-static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, FusedCfg& c) {
+static int router_cpl(const ImageLayout& L) { return (L.H / 8 + 63) / 64; }
+
+bool layer_decode_router_inside(const ImageLayout& L, int E) {
+  return E <= kFusedRouterMaxE && router_cpl(L) <= kFusedRouterMaxCPL;
+}
+
+static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, bool router, FusedCfg& c) {
   if (k < 1 || k > kFusedMaxK || p.grouped || !p.prologue) return false;
   const int cus = device_cus();
   const int ug_max = k * (L.I / 16), ud = L.H / 8;
@@ -2505,7 +2620,9 @@ static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, Fused
       c.ned = kk[3];
       c.lds = fused_lds_bytes(L.H, L.I, k, c.nug, c.nud);
       bool fits = false;
-#define MOE_LD_FIT(A, B, C, D) fits = fused_resident<A, B, C, D>(c.lds)
+#define MOE_LD_FIT(A, B, C, D)                                              \
+  fits = router ? fused_resident<A, B, C, D, true>(c.lds)                  \
+                : fused_resident<A, B, C, D, false>(c.lds)
       MOE_LD_SWITCH(fused_key(c), MOE_LD_FIT)
 #undef MOE_LD_FIT
       return fits;
@@ -2513,30 +2630,38 @@ static bool fused_config(const ImageLayout& L, const ExpertPlan& p, int k, Fused
   return false;
 }
 
-bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M, int k) {
+bool layer_decode_fusable(const ImageLayout& L, const ExpertPlan& p, int M, int k, int E) {
   FusedCfg c;
-  return M == 1 && fused_config(L, p, k, c);
+  return M == 1 && fused_config(L, p, k, layer_decode_router_inside(L, E), c);
 }
 
-hipError_t launch_layer_decode(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
-                               const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
-                               const RouteWs& rw, uint16_t* hbuf, float* y, Residual res,
-                               hipStream_t s) {
+hipError_t launch_layer_decode(const uint16_t* x, const uint16_t* wr, const float* bias, int M,
+                               int H, int I, const uint8_t* slots, const ImageLayout& L,
+                               const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
+                               uint64_t* hf, float* y, Residual res, hipStream_t s) {
   FusedCfg c;
-  if (M != 1 || !fused_config(L, p, ra.k, c)) return hipErrorInvalidValue;
+  const bool router = layer_decode_router_inside(L, ra.E);
+  if (M != 1 || !fused_config(L, p, ra.k, router, c)) return hipErrorInvalidValue;
+  if (!router && ra.logits == nullptr) return hipErrorInvalidValue;
   const FusedDivs dv = {div_magic((uint32_t)c.G), div_magic((uint32_t)(I / 16)),
                         div_magic((uint32_t)((L.dn_ks + 1) / 2))};
   hipError_t e = hipErrorInvalidValue;
+#define MOE_LD_R(A, B, C, D, R)                                                                    \
+  hipLaunchKernelGGL((k_layer_decode<A, B, C, D, R>), dim3(c.G), dim3(kFusedThreads), c.lds, s, x, \
+                     wr, bias, router_cpl(L), H, I, slots, L.image_bytes, L.gu_tile_bytes, L.nb_h, \
+                     L.gu_bytes, L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks, L.dn_full, L.dn_rem,   \
+                     L.nb_i, ra, rw, hf, y, res, dv)
 #define MOE_LD(A, B, C, D)                                                                         \
   do {                                                                                             \
-    hipLaunchKernelGGL((k_layer_decode<A, B, C, D>), dim3(c.G), dim3(kFusedThreads), c.lds, s, x,  \
-                       H, I, slots, L.image_bytes, L.gu_tile_bytes, L.nb_h, L.gu_bytes,            \
-                       L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks, L.dn_full, L.dn_rem, L.nb_i, ra, \
-                       rw, hbuf, y, res, dv);                                                      \
+    if (router)                                                                                    \
+      MOE_LD_R(A, B, C, D, true);                                                                  \
+    else                                                                                           \
+      MOE_LD_R(A, B, C, D, false);                                                                 \
     e = hipGetLastError();                                                                         \
   } while (0)
   MOE_LD_SWITCH(fused_key(c), MOE_LD)
 #undef MOE_LD
+#undef MOE_LD_R
   return e;
 }
 #undef MOE_LD_SWITCH

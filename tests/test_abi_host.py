@@ -57,9 +57,9 @@ def test_layer_launch_counts():
     if os.environ.get("MOE_DECODE_UNFUSED") == "1":
         pytest.skip("fused decode switched off in this environment")
     g = B.make_shape(2880, 2880, 32, 4, 32)
-    # M = 1 fuses only where the device can hold the whole fused grid at once (2 launches on
-    # an MI355X; 3 without a device)
-    assert B.moe_layer_launches(g, 1) in (2, 3)
+    # M = 1 fuses only where the device can hold the whole fused grid at once (one launch, the
+    # router inside, on an MI355X; 3 without a device)
+    assert B.moe_layer_launches(g, 1) in (1, 3)
     assert [B.moe_layer_launches(g, M) for M in (0, 2, 16, 17, 64)] == [1, 3, 3, 4, 5]
     e512 = B.make_shape(2048, 512, 512, 10, 256)
     assert [B.moe_layer_launches(e512, M) for M in (1, 2, 63, 64)] == [3, 4, 4, 5]

@@ -503,7 +503,7 @@ def test_layer_forward_equals_route_plus_experts_and_stages(gptoss):
             assert torch.equal(b.y[:M], c.y[:M])  # the same kernels, staged differently
             for other in (b, c):
                 assert torch.equal(a.ids[:M], other.ids[:M]) and torch.equal(a.w[:M], other.w[:M])
-                if B.moe_layer_launches(shape, M) == 2:  # one token: the fused kernel
+                if B.moe_layer_launches(shape, M) <= 2:  # one token: the fused kernel
                     paths_agree(a.y[:M].cpu().numpy(), other.y[:M].cpu().numpy(), f"M={M}")
                 else:
                     assert torch.equal(a.y[:M], other.y[:M])
@@ -566,7 +566,7 @@ def test_fused_decode_consecutive_tokens_and_maps(gptoss):
     the oracle to the parity bar."""
     wl = gptoss.wl
     shape = gptoss.shape
-    assert B.moe_layer_launches(shape, 1) == 2
+    assert B.moe_layer_launches(shape, 1) == 1  # the router runs inside the fused kernel
     bias = synthetic.zipf_bias(wl)
     wr, bd = _dev(gptoss.wr), _dev(bias)
     E = wl.n_experts
@@ -658,7 +658,7 @@ def test_fused_decode_small_shape_and_graph_replays(tiny, gptoss):
     captured in a HIP graph and replayed, with eager calls between the replays (the h rows are
     re-marked by the router of every call), each replay equal to the eager result."""
     wl, shape = tiny.wl, tiny.shape
-    assert B.moe_layer_launches(shape, 1) == 2
+    assert B.moe_layer_launches(shape, 1) == 1  # the router runs inside the fused kernel
     wr = _dev(tiny.wr)
     E = wl.n_experts
     part = np.arange(E, dtype=np.int32)
@@ -800,7 +800,7 @@ def test_device_error_word_flags_bad_ids_and_slots(tiny):
         torch.cuda.synchronize()
         assert device_errors(buf.ws) == 0
     say("device error word: fused one-token layer call with bad map entries")
-    assert B.moe_layer_launches(shape, 1) == 2
+    assert B.moe_layer_launches(shape, 1) == 1  # the router runs inside the fused kernel
     buf = L.Buffers(shape, 1)
     x = synthetic.activations(wl, 1, 1600)
     e2s = np.arange(E, dtype=np.int32)
