@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 ROCM_INCLUDE = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
 
 HIP_SOURCES = ["moe_kernels.hip"]
-HOST_SOURCES = ["moe_api.cpp", "moe_pack.cpp", "moe_cache.cpp"]
+HOST_SOURCES = ["moe_api.cpp", "moe_pack.cpp", "moe_cache.cpp", "moe_cold.cpp"]
 
 # Packed fp32 instructions are kept out of every kernel (the compiler would otherwise form
 # v_pk_* from scalar float code).
@@ -63,11 +63,11 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        _run([hipcc, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", ROCM_INCLUDE, *common, "-ffp-contract=off", "-c",
+        _run([hipcc, "-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", ROCM_INCLUDE, *common, "-ffp-contract=off", "-pthread", "-c",
               os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-pthread", "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -47,6 +47,12 @@ class moe_refill(C.Structure):
                 ("reserved", C.c_int32), ("visible_step", C.c_int64)]
 
 
+class moe_hybrid_staging(C.Structure):
+    _fields_ = [("max_M", C.c_int32), ("x", C.c_void_p), ("ids", C.c_void_p), ("w", C.c_void_p),
+                ("y_cold", C.c_void_p), ("y_cold_dev", C.c_void_p), ("routed", C.c_void_p),
+                ("added", C.c_void_p), ("pending", C.c_int32)]
+
+
 class moe_cache_stats(C.Structure):
     _fields_ = [("steps", C.c_int64), ("routes", C.c_int64), ("hits", C.c_int64),
                 ("refills", C.c_int64), ("evictions", C.c_int64)]
@@ -76,6 +82,9 @@ _SIGS = {
     "moe_slot_refill": [C.POINTER(moe_shape), _P, _P, _P, _P, _I32, _P, _P, _P],
     "moe_residual_bf16": [_P, _P, _P, _SZ, _P],
     "moe_workspace_errors": [_P, _SZ, _P, _P],
+    "moe_cold_forward_host": [C.POINTER(moe_shape), _P, _P, _I32, _P, _P, _P, _P, _I32],
+    "moe_layer_forward_hybrid": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
+                                 _P, C.POINTER(moe_hybrid_staging), _I32, _P, _SZ, _P],
     "moe_layer_forward_noalloc": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                   _P, _P, _P],
     "moe_cache_create": [C.POINTER(moe_shape), C.POINTER(moe_cache_config), _P,
@@ -294,6 +303,52 @@ def moe_workspace_errors(ws, flags, stream=None):
     pinned host memory)."""
     _check(load().moe_workspace_errors(_ptr(ws), _nbytes(ws), _ptr(flags), _stream(stream)),
            "moe_workspace_errors")
+
+
+def moe_cold_forward_host(shape, host_bank, x, M, topk_ids, topk_w, expert_to_slot, y_cold,
+                          n_threads=0):
+    """The cold routes of a call on the host cores (every array a host numpy array)."""
+    _check(load().moe_cold_forward_host(C.byref(shape), _ptr(host_bank), _ptr(x), int(M),
+                                        _ptr(topk_ids), _ptr(topk_w), _ptr(expert_to_slot),
+                                        _ptr(y_cold), int(n_threads)), "moe_cold_forward_host")
+
+
+class HybridStaging:
+    """Pinned host buffers, a device buffer and two events for moe_layer_forward_hybrid."""
+
+    def __init__(self, shape, max_M, device="cuda"):
+        import torch
+        H, k = shape.hidden, shape.top_k
+        self.x = torch.zeros((max_M, H), dtype=torch.int16, pin_memory=True)
+        self.ids = torch.zeros((max_M, k), dtype=torch.int32, pin_memory=True)
+        self.w = torch.zeros((max_M, k), dtype=torch.float32, pin_memory=True)
+        self.y_cold = torch.zeros((max_M, H), dtype=torch.float32, pin_memory=True)
+        self.y_cold_dev = torch.zeros((max_M, H), dtype=torch.float32, device=device)
+        self.routed = event_create(timing=False)
+        self.added = event_create(timing=False)
+        self.s = moe_hybrid_staging(max_M, _ptr(self.x), _ptr(self.ids), _ptr(self.w),
+                                    _ptr(self.y_cold), _ptr(self.y_cold_dev), self.routed,
+                                    self.added, 0)
+
+    def close(self):
+        if self.routed:
+            event_synchronize(self.added) if self.s.pending else None
+            event_destroy(self.routed)
+            event_destroy(self.added)
+            self.routed = self.added = None
+
+
+def moe_layer_forward_hybrid(shape, x, M, w_router, router_bias, expert_to_slot,
+                             expert_to_slot_host, slots, host_bank, topk_ids, topk_w, y,
+                             staging: HybridStaging, ws, n_threads=0, stream=None):
+    """The layer with hot experts on the GPU and cold routes on the host cores (y = full output)."""
+    _check(load().moe_layer_forward_hybrid(C.byref(shape), _ptr(x), int(M), _ptr(w_router),
+                                           _ptr(router_bias), _ptr(expert_to_slot),
+                                           _ptr(expert_to_slot_host), _ptr(slots), _ptr(host_bank),
+                                           _ptr(topk_ids), _ptr(topk_w), _ptr(y),
+                                           C.byref(staging.s), int(n_threads), _ptr(ws),
+                                           _nbytes(ws), _stream(stream)),
+           "moe_layer_forward_hybrid")
 
 
 def moe_residual_bf16(x, y, out, n, stream=None):

@@ -273,6 +273,41 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
   return st != MOE_OK ? st : ok();
 }
 
+// The GPU part of moe_layer_forward_hybrid: router + top-k, the routes and x staged to the host
+// (staging->routed recorded behind them), then the hot experts, all on the stream.
+moe_status layer_route_and_hot(const moe_shape* shape, const uint16_t* x, int32_t M,
+                               const uint16_t* w_router, const float* router_bias,
+                               const int32_t* expert_to_slot, const uint8_t* slots,
+                               int32_t* topk_ids, float* topk_w, float* y, void* ws,
+                               size_t ws_bytes, hipStream_t stream,
+                               const moe_hybrid_staging* staging) {
+  WsLayout W;
+  moe_status st = check_ws(shape, M, ws, ws_bytes, &W);
+  if (st != MOE_OK) return st;
+  st = check_x_slots(x, slots);
+  if (st != MOE_OK) return st;
+  if (!w_router || !topk_ids || !topk_w || !y)
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_hybrid: w_router, topk_ids, topk_w and y are required");
+  if (reinterpret_cast<uintptr_t>(w_router) & 15)
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_hybrid: w_router must be 16-byte aligned");
+  const int E = shape->n_experts, k = shape->top_k, H = shape->hidden;
+  float* logits = at<float>(ws, W.logits);
+  hipError_t e = launch_router(x, M, w_router, router_bias, E, H, logits, stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, nullptr, nullptr);
+  e = launch_topk_bucket(logits, M, k, topk_ids, topk_w, false, topk_ids, E, shape->n_slots, nullptr,
+                         o, stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  const size_t Mk = (size_t)M * k;
+  if ((e = hipMemcpyAsync(staging->x, x, sizeof(uint16_t) * M * H, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+      (e = hipMemcpyAsync(staging->ids, topk_ids, sizeof(int32_t) * Mk, hipMemcpyDeviceToHost, stream)) != hipSuccess ||
+      (e = hipMemcpyAsync(staging->w, topk_w, sizeof(float) * Mk, hipMemcpyDeviceToHost, stream)) != hipSuccess)
+    return hip_fail(e, "hipMemcpyAsync");
+  if ((e = hipEventRecord(staging->routed, stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return run_experts(shape, x, M, RouteSrc::kIds, nullptr, topk_ids, topk_w, expert_to_slot, slots, y,
+                     nullptr, nullptr, ws, W, true, true, stream);
+}
+
 }  // namespace moe
 
 using namespace moe;

@@ -212,6 +212,8 @@ struct Residual {
 // Kernel launchers (moe_kernels.hip).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
                          int H, float* logits, hipStream_t s);
+// y[i] += add[i] for i < n.
+hipError_t launch_add_f32(float* y, const float* add, size_t n, hipStream_t s);
 // Copies the error word to *out (device or pinned host memory; NULL: nowhere) and clears it.
 hipError_t launch_take_errors(int32_t* word, int32_t* out, hipStream_t s);
 // The static scratch of the current device (the workspace of moe_layer_forward_noalloc):

@@ -2267,6 +2267,19 @@ __global__ __launch_bounds__(64) void k_take_errors(int32_t* __restrict__ word,
   }
 }
 
+// y += add (the cold routes' sum onto the hot output of the hybrid layer), 4 elements a thread.
+__global__ __launch_bounds__(256) void k_add_f32(float* __restrict__ y, const float* __restrict__ add,
+                                                 size_t n) {
+  const size_t i = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  for (size_t j = i; j < i + 4 && j < n; ++j) y[j] += add[j];
+}
+
+hipError_t launch_add_f32(float* y, const float* add, size_t n, hipStream_t s) {
+  const size_t threads = (n + 3) / 4;
+  hipLaunchKernelGGL(k_add_f32, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, y, add, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_take_errors(int32_t* word, int32_t* out, hipStream_t s) {
   hipLaunchKernelGGL(k_take_errors, dim3(1), dim3(64), 0, s, word, out);
   return hipGetLastError();

@@ -273,6 +273,56 @@ moe_status moe_residual_bf16(const uint16_t* x, const float* y, uint16_t* out, s
                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Hybrid GPU-hot / CPU-cold layer [ORT hybrid PR, "Key Changes": routes to cold experts
+ * (slot < 0) are skipped on the GPU and accumulated on the CPU, whose worker threads execute the
+ * cold experts while the hot-expert kernel runs, through reusable pinned staging buffers and
+ * timing-disabled events; ninfer v0.4.0, "New": cold experts run on the CPU].
+ *
+ * moe_cold_forward_host: the cold routes alone, on the host cores (all pointers [host]):
+ *   y_cold[m] = sum over j = 0..k-1 (ascending) of the routes whose expert maps to no slot
+ *   (expert_to_slot[e] outside [0, S); NULL = identity, nothing cold) of
+ *   topk_w[m,j] * (Wd_e h), h = bf16(silu(Wg_e x_m) * (Wu_e x_m)), fp32 accumulation.
+ *   host_bank: E expert images back to back (moe_pack_expert layout, the bytes the slots hold);
+ *   x [M,H] bf16; topk_ids / topk_w [M,k]; y_cold [M,H] fp32 is overwritten (zeros for a token
+ *   with no cold route); routes with an id outside [0, E) are skipped.  n_threads <= 0: one per
+ *   host core.  Synchronous, deterministic (the result does not depend on n_threads).
+ *
+ * moe_layer_forward_hybrid: the whole layer with cold routes on the host:
+ *   on stream: router + top-k (as moe_route), copies of x, topk_ids and topk_w into the pinned
+ *   staging (then staging->routed is recorded), the hot experts (as moe_experts_forward, y =
+ *   hot-only output); on the calling thread, once staging->routed has passed: the cold routes
+ *   (moe_cold_forward_host) into staging->y_cold while the GPU runs the hot experts; then on
+ *   stream: y_cold is uploaded to staging->y_cold_dev and added to y (staging->added is
+ *   recorded).  So y = y_hot + y_cold, every route of the layer.  Returns once the host part is
+ *   done and the upload is enqueued.  The next call on the same staging first waits for
+ *   staging->added.  expert_to_slot (device) and expert_to_slot_host hold the same map.
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t max_M;      /* tokens the buffers hold */
+  uint16_t* x;        /* [host, pinned] [max_M, H] */
+  int32_t* ids;       /* [host, pinned] [max_M, k] */
+  float* w;           /* [host, pinned] [max_M, k] */
+  float* y_cold;      /* [host, pinned] [max_M, H] */
+  float* y_cold_dev;  /* device [max_M, H] */
+  hipEvent_t routed;  /* created by the caller (timing may be disabled) */
+  hipEvent_t added;   /* created by the caller */
+  int32_t pending;    /* set by the library; 0 before the first call */
+} moe_hybrid_staging;
+
+moe_status moe_cold_forward_host(const moe_shape* shape, const uint8_t* host_bank,
+                                 const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                                 const float* topk_w, const int32_t* expert_to_slot,
+                                 float* y_cold, int32_t n_threads);
+
+moe_status moe_layer_forward_hybrid(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                    const uint16_t* w_router, const float* router_bias,
+                                    const int32_t* expert_to_slot,
+                                    const int32_t* expert_to_slot_host, const uint8_t* slots,
+                                    const uint8_t* host_bank, int32_t* topk_ids, float* topk_w,
+                                    float* y, moe_hybrid_staging* staging, int32_t n_threads,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------
  * Slot refill [ninfer v0.4.0, "New": experts are copied to the GPU in the background;
  * MoE expert offload, intro: routed experts stay in pinned host RAM; ORT hybrid PR,
  * "Key Changes": pinned staging ordered by timing-disabled events].

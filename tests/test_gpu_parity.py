@@ -987,3 +987,58 @@ def test_slot_cache_pipeline_concurrent_with_poison():
     say(f"concurrent pipeline: {steps} steps, {n_refills} refills, hit rate "
         f"{pol.stats['hits'] / max(1, pol.stats['routes']):.3f}")
     assert n_refills > 20
+
+
+@pytest.mark.parametrize("which,M", [("gptoss20b_8slots", 1), ("e512", 1), ("e512", 8)])
+def test_hybrid_layer_hot_gpu_plus_cold_host_equals_full(which, M, e512):
+    """moe_layer_forward_hybrid: the hot experts on the GPU, the cold routes on the host cores
+    while the GPU runs, their sum added on the stream.  y equals, bit for bit, the GPU's hot-only
+    output (moe_experts_forward on the same routes) plus the host's cold-only output
+    (moe_cold_forward_host), and matches the oracle's full output (y_hot + y_cold = y_full)
+    over consecutive calls on one staging."""
+    if which == "e512":
+        wl, experts, bank = e512.wl, e512.experts, e512.bank
+        counts = routed_counts(wl, 0, 256)
+        slot_expert = popularity_placement(counts, wl.n_slots)
+        bias = synthetic.zipf_bias(wl)
+    else:
+        wl = synthetic.WORKLOADS[which]
+        experts = synthetic.experts_canonical(wl, 0, range(wl.n_experts))
+        bank = L.pack_bank(_shape(wl, wl.n_experts), experts)
+        slot_expert = np.argsort(synthetic.zipf_ranks(wl))[:wl.n_slots].astype(np.int32)
+        bias = synthetic.zipf_bias(wl)
+    E, k, S, H = wl.n_experts, wl.top_k, wl.n_slots, wl.hidden
+    shape = _shape(wl, S)
+    e2s = np.full(E, -1, np.int32)
+    e2s[slot_expert] = np.arange(S, dtype=np.int32)
+    slots = L.device_slots(bank, slot_expert, S)
+    pinned = L.pinned_bank(bank)
+    wr = synthetic.router_weights(wl)
+    staging = B.HybridStaging(shape, M)
+    a, b = L.Buffers(shape, M), L.Buffers(shape, M)
+    wr_d, bias_d, e2s_d = _dev(wr), _dev(bias), _dev(e2s)
+    for t in range(3):
+        say("hybrid layer:", which, "M =", M, "call", t)
+        xn = synthetic.activations(wl, M, 1700 + t)
+        x = _dev(xn)
+        B.moe_layer_forward_hybrid(shape, x, M, wr_d, bias_d, e2s_d, e2s, slots, pinned.numpy(),
+                                   a.ids, a.w, a.y, staging, a.ws, n_threads=8)
+        B.moe_route(shape, x, M, wr_d, bias_d, b.ids, b.w, b.ws)
+        B.moe_experts_forward(shape, x, M, b.ids, b.w, e2s_d, slots, b.y, b.cold_count, b.cold_routes, b.ws)
+        torch.cuda.synchronize()
+        no_device_errors(a.ws, b.ws)
+        assert torch.equal(a.ids[:M], b.ids[:M]) and torch.equal(a.w[:M], b.w[:M])
+        ids, w = a.ids[:M].cpu().numpy(), a.w[:M].cpu().numpy()
+        y_cold = np.zeros((M, H), np.float32)
+        B.moe_cold_forward_host(shape, bank, xn, M, ids, w, e2s, y_cold, 2)
+        y_hot = b.y[:M].cpu().numpy()
+        y = a.y[:M].cpu().numpy()
+        assert np.array_equal(y, y_hot + y_cold)
+        lg = O.router_logits(xn, wr, bias)
+        compare_routes(ids, w, lg, k)
+        ref = O.layer_forward(xn, ids, oracle_weights_for(lg, ids), experts, e2s)
+        assert int(b.cold_count.item()) == len(ref["cold_routes"])
+        close_enough(y, ref["y_full"], f"hybrid {which} M={M} call {t}")
+        if len(ref["cold_routes"]):
+            close_enough(y_cold, ref["y_cold"], f"hybrid {which} cold part")
+    staging.close()
