@@ -82,6 +82,12 @@ _SIGS = {
     "moe_slot_refill": [C.POINTER(moe_shape), _P, _P, _P, _P, _I32, _P, _P, _P],
     "moe_residual_bf16": [_P, _P, _P, _SZ, _P],
     "moe_workspace_errors": [_P, _SZ, _P, _P],
+    "moe_device_cache_size": [C.POINTER(moe_shape), C.POINTER(_SZ)],
+    "moe_device_cache_init": [C.POINTER(moe_shape), C.POINTER(moe_cache_config), _P, C.c_int64, _P,
+                              _SZ, _P],
+    "moe_device_cache_step": [C.POINTER(moe_shape), _P, _SZ, _P, _I32, _P, _P, _P, _P],
+    "moe_device_cache_copy": [C.POINTER(moe_shape), _P, _P, _P, _P, _P],
+    "moe_device_cache_stats": [C.POINTER(moe_shape), _P, _SZ, _P, _P],
     "moe_cold_forward_host": [C.POINTER(moe_shape), _P, _P, _I32, _P, _P, _P, _P, _I32],
     "moe_layer_forward_hybrid": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, C.POINTER(moe_hybrid_staging), _I32, _P, _SZ, _P],
@@ -409,6 +415,52 @@ class MoeCache:
             self.close()
         except Exception:
             pass
+
+
+class DeviceCache:
+    """One layer's GPU-resident slot cache: its device state (torch uint8 tensor) and the
+    entry points that act on it."""
+
+    def __init__(self, shape: moe_shape, policy=MOE_POLICY_LRU, max_refills_per_step=2,
+                 lag_steps=1, max_pending=2, decay_period=64, initial_slot_expert=None,
+                 first_step=0, stream=None, device="cuda"):
+        import torch
+        self.shape = shape
+        n = _SZ(0)
+        _check(load().moe_device_cache_size(C.byref(shape), C.byref(n)), "moe_device_cache_size")
+        self.state = torch.zeros(n.value, dtype=torch.uint8, device=device)
+        cfg = moe_cache_config(policy, max_refills_per_step, lag_steps, max_pending, decay_period)
+        init = None
+        if initial_slot_expert is not None:
+            init = np.ascontiguousarray(initial_slot_expert, dtype=np.int32)
+        _check(load().moe_device_cache_init(C.byref(shape), C.byref(cfg), _ptr(init),
+                                            int(first_step), _ptr(self.state), n.value,
+                                            _stream(stream)), "moe_device_cache_init")
+
+    def step(self, observed_ids, n_observed, expert_to_slot, plan, n_plan, stream=None):
+        """Enqueue one policy step.  plan: device buffer of >= R moe_refill records (24 bytes
+        each); n_plan: one int32 on the device."""
+        _check(load().moe_device_cache_step(C.byref(self.shape), _ptr(self.state),
+                                            _nbytes(self.state), _ptr(observed_ids),
+                                            int(n_observed), _ptr(expert_to_slot), _ptr(plan),
+                                            _ptr(n_plan), _stream(stream)), "moe_device_cache_step")
+
+    def copy(self, n_plan, plan, host_bank, slots, stream=None):
+        _check(load().moe_device_cache_copy(C.byref(self.shape), _ptr(n_plan), _ptr(plan),
+                                            _ptr(host_bank), _ptr(slots), _stream(stream)),
+               "moe_device_cache_copy")
+
+    def stats(self, stream=None):
+        import torch
+        out = torch.zeros(5, dtype=torch.int64, device=self.state.device)
+        _check(load().moe_device_cache_stats(C.byref(self.shape), _ptr(self.state),
+                                             _nbytes(self.state), _ptr(out), _stream(stream)),
+               "moe_device_cache_stats")
+        torch.cuda.synchronize()
+        return dict(zip([f for f, _ in moe_cache_stats._fields_], out.cpu().tolist()))
+
+
+REFILL_RECORD_BYTES = C.sizeof(moe_refill)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -1,5 +1,6 @@
 // Slot-cache policy (host only): LRU / LFRU victims, bounded refills per step, fixed-lag
 // visibility.  The rules are spelled out in include/moe.h (moe_cache_policy_step).
+#include <hip/hip_runtime_api.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -217,6 +218,154 @@ moe_status moe_cache_policy_step(moe_cache* c, int64_t step, const int32_t* topk
   // 4. publish
   memcpy(expert_to_slot, c->expert_slot.data(), sizeof(int32_t) * c->E);
   if (stats) *stats = c->stats;
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// GPU-resident cache: host side (state layout, validation, launches).  The policy kernel is in
+// moe_dcache.hip.
+// ---------------------------------------------------------------------------------------------
+static moe_status check_dcache_config(const moe_shape* shape, const moe_cache_config* cfg) {
+  if (!cfg) return fail(MOE_ERR_INVALID_ARG, "config is NULL");
+  if (cfg->policy != MOE_POLICY_LRU && cfg->policy != MOE_POLICY_LFRU)
+    return fail(MOE_ERR_INVALID_ARG, "unknown policy %d", cfg->policy);
+  if (cfg->max_refills_per_step < 0 || cfg->max_refills_per_step > kDcacheMaxQ ||
+      cfg->lag_steps < 1 || cfg->max_pending < 1 || cfg->max_pending > kDcacheMaxQ ||
+      cfg->decay_period < 0)
+    return fail(MOE_ERR_INVALID_ARG,
+                "device cache config out of range (R=%d in [0,%d], L=%d >= 1, Q=%d in [1,%d], decay=%d)",
+                cfg->max_refills_per_step, kDcacheMaxQ, cfg->lag_steps, cfg->max_pending,
+                kDcacheMaxQ, cfg->decay_period);
+  (void)shape;
+  return MOE_OK;
+}
+
+static moe_status check_dcache_state(const moe_shape* shape, const void* state, size_t bytes) {
+  if (!state) return fail(MOE_ERR_INVALID_ARG, "device cache state is NULL");
+  if (reinterpret_cast<uintptr_t>(state) & 255)
+    return fail(MOE_ERR_INVALID_ARG, "device cache state must be 256-byte aligned");
+  const size_t need = dcache_layout(shape->n_experts, shape->n_slots).total;
+  if (bytes < need) return fail(MOE_ERR_WORKSPACE, "device cache state %zu bytes < %zu", bytes, need);
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_device_cache_size(const moe_shape* shape, size_t* bytes) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = dcache_layout(shape->n_experts, shape->n_slots).total;
+  return ok();
+}
+
+moe_status moe_device_cache_init(const moe_shape* shape, const moe_cache_config* config,
+                                 const int32_t* initial_slot_expert, int64_t first_step,
+                                 void* state, size_t state_bytes, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_dcache_config(shape, config)) != MOE_OK) return st;
+  if ((st = check_dcache_state(shape, state, state_bytes)) != MOE_OK) return st;
+  const int E = shape->n_experts, S = shape->n_slots;
+  const DevCacheLayout D = dcache_layout(E, S);
+  std::vector<uint8_t> img(D.total, 0);
+  DevCacheHdr h;
+  memset(&h, 0, sizeof(h));
+  h.step = first_step;
+  h.E = E;
+  h.S = S;
+  h.R = config->max_refills_per_step;
+  h.L = config->lag_steps;
+  h.Q = config->max_pending;
+  h.policy = config->policy;
+  h.decay = config->decay_period;
+  memcpy(img.data(), &h, sizeof(h));
+  int32_t* se = reinterpret_cast<int32_t*>(img.data() + D.slot_expert);
+  int32_t* es = reinterpret_cast<int32_t*>(img.data() + D.expert_slot);
+  int64_t* lu = reinterpret_cast<int64_t*>(img.data() + D.last_use);
+  for (int s = 0; s < S; ++s) {
+    se[s] = -1;
+    lu[s] = -1;
+  }
+  for (int e = 0; e < E; ++e) es[e] = -1;
+  if (initial_slot_expert) {
+    for (int s = 0; s < S; ++s) {
+      const int e = initial_slot_expert[s];
+      if (e < -1 || e >= E) return fail(MOE_ERR_INVALID_ARG, "initial slot %d holds expert %d out of range", s, e);
+      if (e >= 0) {
+        if (es[e] >= 0) return fail(MOE_ERR_INVALID_ARG, "expert %d placed twice", e);
+        se[s] = e;
+        es[e] = s;
+      }
+    }
+  }
+  hipError_t e = hipMemcpyAsync(state, img.data(), D.total, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);  // (the host image is local)
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "device cache init: %s", hipGetErrorString(e));
+  return ok();
+}
+
+moe_status moe_device_cache_step(const moe_shape* shape, void* state, size_t state_bytes,
+                                 const int32_t* observed_ids, int32_t n_observed,
+                                 int32_t* expert_to_slot, moe_refill* plan, int32_t* n_plan,
+                                 hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_dcache_state(shape, state, state_bytes)) != MOE_OK) return st;
+  if (n_observed < 0 || n_observed > (1 << 20))
+    return fail(MOE_ERR_INVALID_ARG, "n_observed = %d outside [0, 2^20]", n_observed);
+  if (n_observed > 0 && !observed_ids) return fail(MOE_ERR_INVALID_ARG, "observed_ids is NULL");
+  if (!expert_to_slot || !plan || !n_plan)
+    return fail(MOE_ERR_INVALID_ARG, "expert_to_slot, plan and n_plan are required");
+  hipError_t e = launch_dcache_step(static_cast<uint8_t*>(state), shape->n_experts, shape->n_slots,
+                                    observed_ids, n_observed, expert_to_slot, plan, n_plan, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "device cache step launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+moe_status moe_device_cache_copy(const moe_shape* shape, const int32_t* n_plan,
+                                 const moe_refill* plan, const uint8_t* host_bank, uint8_t* slots,
+                                 hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!n_plan || !plan || !host_bank || !slots)
+    return fail(MOE_ERR_INVALID_ARG, "moe_device_cache_copy: NULL pointer");
+  if (reinterpret_cast<uintptr_t>(slots) & 255)
+    return fail(MOE_ERR_INVALID_ARG, "slots must be 256-byte aligned");
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof(attr));
+  hipError_t e = hipPointerGetAttributes(&attr, host_bank);
+  if (e != hipSuccess || attr.type != hipMemoryTypeHost) {
+    (void)hipGetLastError();  // (a failed query leaves nothing behind)
+    return fail(MOE_ERR_INVALID_ARG, "moe_device_cache_copy: host_bank is not pinned host memory");
+  }
+  void* dev_bank = nullptr;
+  e = hipHostGetDevicePointer(&dev_bank, const_cast<uint8_t*>(host_bank), 0);
+  if (e != hipSuccess || dev_bank == nullptr)
+    return fail(MOE_ERR_INVALID_ARG,
+                "moe_device_cache_copy: host_bank is not pinned host memory mapped for the device (%s)",
+                hipGetErrorString(e));
+  if (reinterpret_cast<uintptr_t>(dev_bank) & 15)
+    return fail(MOE_ERR_INVALID_ARG, "host_bank must be 16-byte aligned");
+  const ImageLayout L = image_layout(shape->hidden, shape->inter);
+  e = launch_dcache_copy(n_plan, plan, static_cast<const uint8_t*>(dev_bank), slots, L.image_bytes,
+                         shape->n_experts, shape->n_slots, kDcacheMaxQ, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "device cache copy launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+moe_status moe_device_cache_stats(const moe_shape* shape, const void* state, size_t state_bytes,
+                                  moe_cache_stats* stats, hipStream_t stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if ((st = check_dcache_state(shape, state, state_bytes)) != MOE_OK) return st;
+  if (!stats) return fail(MOE_ERR_INVALID_ARG, "stats is NULL");
+  static_assert(sizeof(moe_cache_stats) == 5 * sizeof(int64_t), "stats layout");
+  hipError_t e = hipMemcpyAsync(stats, static_cast<const uint8_t*>(state) + offsetof(DevCacheHdr, stats),
+                                sizeof(moe_cache_stats), hipMemcpyDefault, stream);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
   return ok();
 }
 

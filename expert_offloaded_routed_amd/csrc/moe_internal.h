@@ -29,6 +29,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
@@ -208,6 +210,35 @@ struct Residual {
   const uint16_t* x;
   uint16_t* out;
 };
+
+// GPU-resident slot cache (moe_dcache.hip): state in device memory, one header then arrays.
+constexpr int kDcacheMaxQ = 16;        // refills per step and in flight, at most
+constexpr int kDcacheCopyGroups = 128; // workgroups of the copy kernel (fixed launch shape)
+struct DevCacheHdr {
+  int64_t step;      // the next step's index
+  int64_t stats[5];  // steps, routes, hits, refills, evictions (the order of moe_cache_stats)
+  int32_t E, S, R, L, Q, policy, decay, n_pending;
+  int32_t pend_e[kDcacheMaxQ], pend_s[kDcacheMaxQ];
+  int64_t pend_vis[kDcacheMaxQ];
+};
+struct DevCacheLayout {
+  size_t slot_expert, expert_slot, last_use, freq, total;  // i32 [S], i32 [E], i64 [S], i64 [E]
+};
+__host__ __device__ inline DevCacheLayout dcache_layout(int E, int S) {
+  DevCacheLayout D;
+  size_t o = (sizeof(DevCacheHdr) + 255) / 256 * 256;
+  D.last_use = o;     o += 8 * (size_t)S;
+  D.freq = o;         o += 8 * (size_t)E;
+  D.slot_expert = o;  o += 4 * (size_t)S;
+  D.expert_slot = o;  o += 4 * (size_t)E;
+  D.total = (o + 255) / 256 * 256;
+  return D;
+}
+hipError_t launch_dcache_step(uint8_t* state, int E, int S, const int32_t* obs, int n_obs,
+                              int32_t* map_out, moe_refill* plan, int32_t* n_plan, hipStream_t s);
+hipError_t launch_dcache_copy(const int32_t* n_plan, const moe_refill* plan, const uint8_t* bank,
+                              uint8_t* slots, size_t image_bytes, int E, int S, int R,
+                              hipStream_t s);
 
 // Kernel launchers (moe_kernels.hip).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,

@@ -389,6 +389,48 @@ moe_status moe_cache_policy_step(moe_cache* cache, int64_t step, const int32_t* 
                                  int32_t* expert_to_slot, moe_cache_stats* stats);
 void moe_cache_destroy(moe_cache* cache);
 
+/* ---------------------------------------------------------------------------------------
+ * GPU-resident slot cache [MoE expert offload, "How it works", Decode: the per-layer LRU table
+ * is kept on the GPU, a kernel looks routed experts up and assigns least-recently-used slots to
+ * misses, a second kernel copies the missing experts straight from device-mapped pinned host
+ * memory into their slots; both have fixed launch shapes and read the miss count from device
+ * memory, so decode stays inside graphs with no host sync; ninfer v0.4.0, "New": at most two
+ * refills per layer and call].  The policy is moe_cache_policy_step's, step for step, over state
+ * that lives in device memory, so a decode loop (policy, layer, copy) can be captured whole in
+ * a HIP graph.  Step t observes the routes the caller passes (e.g. those of step t - 1).
+ *
+ * moe_device_cache_size: bytes of the device state of one layer's cache.  [host] out.
+ * moe_device_cache_init: writes the state (config, initial placement [host] [S] or NULL, step
+ *   index of the first step) into `state` (device, 256-byte aligned); returns once written.
+ *   R and Q at most 16.
+ * moe_device_cache_step: one step, enqueued on stream: observed_ids [n_observed] (device; ids
+ *   outside [0, E) are not observed, so a buffer of -1 stands for "nothing observed"),
+ *   expert_to_slot [E] (device, out: the map of this step, as moe_cache_policy_step publishes
+ *   it), plan [<= R] and n_plan [1] (device, out: this step's refills).  The state's step index
+ *   advances by one.
+ * moe_device_cache_copy: the planned refills, enqueued on stream: n_plan and plan as written by
+ *   moe_device_cache_step; images from host_bank (pinned host memory, device-mapped: allocated
+ *   with hipHostMalloc, E images back to back) into slots.  One kernel of a fixed shape; with
+ *   n_plan = 0 it does nothing.  The caller orders it after the last kernels that read the
+ *   victim slots and before the first that reads a refilled slot (visible_step), e.g. on a side
+ *   stream with events.
+ * moe_device_cache_stats: copies the state's counters to *stats (device or pinned host
+ *   memory), on stream.
+ * --------------------------------------------------------------------------------------- */
+moe_status moe_device_cache_size(const moe_shape* shape, size_t* bytes);
+moe_status moe_device_cache_init(const moe_shape* shape, const moe_cache_config* config,
+                                 const int32_t* initial_slot_expert, int64_t first_step,
+                                 void* state, size_t state_bytes, hipStream_t stream);
+moe_status moe_device_cache_step(const moe_shape* shape, void* state, size_t state_bytes,
+                                 const int32_t* observed_ids, int32_t n_observed,
+                                 int32_t* expert_to_slot, moe_refill* plan, int32_t* n_plan,
+                                 hipStream_t stream);
+moe_status moe_device_cache_copy(const moe_shape* shape, const int32_t* n_plan,
+                                 const moe_refill* plan, const uint8_t* host_bank, uint8_t* slots,
+                                 hipStream_t stream);
+moe_status moe_device_cache_stats(const moe_shape* shape, const void* state, size_t state_bytes,
+                                  moe_cache_stats* stats, hipStream_t stream);
+
 /* Message describing the last failure of a call on this thread ("" if none). */
 const char* moe_last_error(void);
 

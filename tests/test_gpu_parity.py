@@ -1042,3 +1042,101 @@ def test_hybrid_layer_hot_gpu_plus_cold_host_equals_full(which, M, e512):
         if len(ref["cold_routes"]):
             close_enough(y_cold, ref["y_cold"], f"hybrid {which} cold part")
     staging.close()
+
+
+def test_device_cache_in_one_graph_matches_oracle_policy():
+    """The GPU-resident slot cache over 256 decode steps of the 8-slot GPT-OSS-20B-shaped layer,
+    captured as one HIP graph: per step, the policy kernel (observing the previous step's
+    routes from device memory) publishes the map and plans <= 2 refills; the router, top-k and
+    hot experts run with that map on the compute stream; the copy kernel moves the planned
+    experts from device-mapped pinned memory into their slots on a side stream, after the
+    previous step's layer (the last reader of the victims), and the layer of step t + L waits
+    for it.  Maps, plans, counters and cold counts equal the oracle policy's replay bit for bit;
+    y_hot matches the oracle at every step."""
+    wl = synthetic.WORKLOADS["gptoss20b_8slots"]
+    steps, lag = 256, 3
+    E, k, S, H = wl.n_experts, wl.top_k, wl.n_slots, wl.hidden
+    shape = _shape(wl, S)
+    say("device cache: generating 32 experts")
+    experts = synthetic.experts_canonical(wl, 0, range(E))
+    bank_np = L.pack_bank(shape, experts)
+    bank = L.pinned_bank(bank_np)
+    init = np.argsort(synthetic.zipf_ranks(wl))[:S].astype(np.int32)
+    slots = L.device_slots(bank_np, init, S)
+    wr = synthetic.router_weights(wl)
+    xs = np.concatenate([synthetic.activations(wl, 1, t) for t in range(steps)])
+    biases = np.stack([synthetic.zipf_bias(wl, 0, synthetic.drift_shift(wl, t)) for t in range(steps)])
+    xs_d, wr_d, biases_d = _dev(xs), _dev(wr), torch.from_numpy(biases).cuda()
+    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    cache = B.DeviceCache(shape, lag_steps=lag, initial_slot_expert=init, stream=comp)
+    ws = L.Buffers(shape, 1).ws
+    ids = torch.full((steps, k), -1, dtype=torch.int32, device="cuda")  # the last row: "none yet"
+    w = torch.zeros((steps, k), dtype=torch.float32, device="cuda")
+    y = torch.zeros((steps, H), dtype=torch.float32, device="cuda")
+    maps = torch.zeros((steps, E), dtype=torch.int32, device="cuda")
+    plans = torch.zeros((steps, 2 * B.REFILL_RECORD_BYTES), dtype=torch.uint8, device="cuda")
+    nplan = torch.zeros((steps,), dtype=torch.int32, device="cuda")
+    cold = torch.zeros((steps, 1), dtype=torch.int32, device="cuda")
+    cold_routes = torch.zeros((steps, k), dtype=torch.int32, device="cuda")
+    ev_plan = [B.event_create() for _ in range(steps)]
+    ev_layer = [B.event_create() for _ in range(steps)]
+    ev_copy = [B.event_create() for _ in range(steps)]
+    torch.cuda.synchronize()
+
+    def step(t):
+        cache.step(ids[(t - 1) % steps], k, maps[t], plans[t], nplan[t:t + 1], stream=comp)
+        B.event_record(ev_plan[t], comp)
+        if t - lag >= 0:
+            B.stream_wait_event(comp, ev_copy[t - lag])  # refills visible now have landed
+        B.moe_route(shape, xs_d[t], 1, wr_d, biases_d[t], ids[t], w[t], ws, stream=comp)
+        B.moe_experts_forward(shape, xs_d[t], 1, ids[t], w[t], maps[t], slots, y[t], cold[t],
+                              cold_routes[t], ws, stream=comp)
+        B.event_record(ev_layer[t], comp)
+        B.stream_wait_event(copy, ev_plan[t])
+        if t >= 1:
+            B.stream_wait_event(copy, ev_layer[t - 1])  # the victims' last readers are done
+        cache.copy(nplan[t:t + 1], plans[t], bank, slots, stream=copy)
+        B.event_record(ev_copy[t], copy)
+
+    say("device cache: capturing", steps, "steps")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(comp):
+        with torch.cuda.graph(g, stream=comp):
+            for t in range(steps):
+                step(t)
+            B.stream_wait_event(comp, ev_copy[steps - 1])  # join the copy stream
+    torch.cuda.synchronize()
+    say("device cache: replay")
+    with torch.cuda.stream(comp):
+        g.replay()
+    torch.cuda.synchronize()
+    no_device_errors(ws)
+    st = cache.stats()
+    ids_h, w_h, y_h = ids.cpu().numpy(), w.cpu().numpy(), y.cpu().numpy()
+    maps_h, nplan_h, cold_h = maps.cpu().numpy(), nplan.cpu().numpy(), cold.cpu().numpy()[:, 0]
+    plans_h = plans.cpu().numpy()
+    lg = O.router_logits(xs, wr, None) + biases.astype(np.float64)
+    excluded, _, _ = compare_routes(ids_h, w_h, lg, k)
+    say("device cache: near-tie tokens", excluded)
+    w_own = oracle_weights_for(lg, ids_h)
+    pol = SlotCachePolicy(E, S, init, policy=LRU, max_refills=2, lag=lag, max_pending=2)
+    memo, n_ref = {}, 0
+    for t in range(steps):
+        m_ref, plan_ref = pol.step(t, ids_h[t - 1:t] if t >= 1 else None)
+        assert np.array_equal(maps_h[t], m_ref), t
+        rec = plans_h[t].view(np.int32).reshape(2, 6)
+        got = [(int(r[0]), int(r[1]), int(r[2]), int(r[4]) | (int(r[5]) << 32)) for r in rec[:nplan_h[t]]]
+        assert got == plan_ref, (t, got, plan_ref)
+        n_ref += len(plan_ref)
+        ref = O.layer_forward(xs[t:t + 1], ids_h[t:t + 1], w_own[t:t + 1], experts, m_ref, dense_memo=memo)
+        assert cold_h[t] == len(ref["cold_routes"]), t
+        if np.linalg.norm(ref["y_hot"]) > 0:
+            close_enough(y_h[t:t + 1], ref["y_hot"], f"device cache step {t}")
+        else:
+            assert not y_h[t].any(), t
+    assert st == pol.stats, (st, pol.stats)
+    say(f"device cache: {steps} steps in one graph, {n_ref} refills, hit rate "
+        f"{st['hits'] / max(1, st['routes']):.3f}")
+    assert n_ref > 20
+    for ev in ev_plan + ev_layer + ev_copy:
+        B.event_destroy(ev)
