@@ -53,6 +53,14 @@ class moe_hybrid_staging(C.Structure):
                 ("added", C.c_void_p), ("pending", C.c_int32)]
 
 
+class moe_prefill_staging(C.Structure):
+    _fields_ = [("max_M", C.c_int32), ("n_slots", C.c_int32), ("slots", C.c_void_p),
+                ("counts_dev", C.c_void_p), ("counts_host", C.c_void_p), ("maps_dev", C.c_void_p),
+                ("maps_host", C.c_void_p), ("y_pass", C.c_void_p), ("copy_stream", C.c_void_p),
+                ("ev_counts", C.c_void_p), ("ev_copied", C.c_void_p * 2), ("ev_done", C.c_void_p * 2),
+                ("pending", C.c_int32 * 2)]
+
+
 class moe_cache_stats(C.Structure):
     _fields_ = [("steps", C.c_int64), ("routes", C.c_int64), ("hits", C.c_int64),
                 ("refills", C.c_int64), ("evictions", C.c_int64)]
@@ -88,6 +96,9 @@ _SIGS = {
     "moe_device_cache_step": [C.POINTER(moe_shape), _P, _SZ, _P, _I32, _P, _P, _P, _P],
     "moe_device_cache_copy": [C.POINTER(moe_shape), _P, _P, _P, _P, _P],
     "moe_device_cache_stats": [C.POINTER(moe_shape), _P, _SZ, _P, _P],
+    "moe_layer_forward_staged": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P,
+                                 C.POINTER(moe_prefill_staging), _P, _SZ, _P, C.POINTER(_I32),
+                                 C.POINTER(_I32)],
     "moe_cold_forward_host": [C.POINTER(moe_shape), _P, _P, _I32, _P, _P, _P, _P, _I32],
     "moe_layer_forward_hybrid": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, C.POINTER(moe_hybrid_staging), _I32, _P, _SZ, _P],
@@ -415,6 +426,49 @@ class MoeCache:
             self.close()
         except Exception:
             pass
+
+
+class PrefillStaging:
+    """Staging slots, count / map buffers, a copy stream and events for moe_layer_forward_staged."""
+
+    def __init__(self, shape, max_M, n_slots, device="cuda"):
+        import torch
+        E, H = shape.n_experts, shape.hidden
+        img = moe_expert_image_bytes(shape)
+        self.slots = torch.zeros((n_slots, img), dtype=torch.uint8, device=device)
+        self.counts_dev = torch.zeros(E, dtype=torch.int32, device=device)
+        self.counts_host = torch.zeros(E, dtype=torch.int32, pin_memory=True)
+        self.maps_dev = torch.zeros((2, E), dtype=torch.int32, device=device)
+        self.maps_host = torch.zeros((2, E), dtype=torch.int32, pin_memory=True)
+        self.y_pass = torch.zeros((max_M, H), dtype=torch.float32, device=device)
+        self.copy_stream = torch.cuda.Stream()
+        self.events = [event_create() for _ in range(5)]
+        ev = self.events
+        self.s = moe_prefill_staging(max_M, n_slots, _ptr(self.slots), _ptr(self.counts_dev),
+                                     _ptr(self.counts_host), _ptr(self.maps_dev),
+                                     _ptr(self.maps_host), _ptr(self.y_pass),
+                                     self.copy_stream.cuda_stream, ev[0],
+                                     (C.c_void_p * 2)(ev[1], ev[2]), (C.c_void_p * 2)(ev[3], ev[4]),
+                                     (C.c_int32 * 2)(0, 0))
+
+    def close(self):
+        import torch
+        torch.cuda.synchronize()
+        for e in self.events:
+            event_destroy(e)
+        self.events = []
+
+
+def moe_layer_forward_staged(shape, x, M, w_router, router_bias, host_bank, topk_ids, topk_w, y,
+                             staging: PrefillStaging, ws, stream=None):
+    """The layer with its touched experts staged from pinned host memory; returns (touched, passes)."""
+    nt, npass = _I32(0), _I32(0)
+    _check(load().moe_layer_forward_staged(C.byref(shape), _ptr(x), int(M), _ptr(w_router),
+                                           _ptr(router_bias), _ptr(host_bank), _ptr(topk_ids),
+                                           _ptr(topk_w), _ptr(y), C.byref(staging.s), _ptr(ws),
+                                           _nbytes(ws), _stream(stream), C.byref(nt), C.byref(npass)),
+           "moe_layer_forward_staged")
+    return nt.value, npass.value
 
 
 class DeviceCache:

@@ -308,6 +308,46 @@ moe_status layer_route_and_hot(const moe_shape* shape, const uint16_t* x, int32_
                      nullptr, nullptr, ws, W, true, true, stream);
 }
 
+// The routing part of moe_layer_forward_staged: router + top-k (as moe_route), then the route
+// count of every expert into counts_dev.
+moe_status staged_route_and_count(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                  const uint16_t* w_router, const float* router_bias,
+                                  int32_t* topk_ids, float* topk_w, int32_t* counts_dev, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  WsLayout W;
+  moe_status st = check_ws(shape, M, ws, ws_bytes, &W);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !topk_ids || !topk_w)
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_staged: x, w_router, topk_ids and topk_w are required");
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w_router)) & 15)
+    return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_staged: x and w_router must be 16-byte aligned");
+  const int E = shape->n_experts, k = shape->top_k;
+  float* logits = at<float>(ws, W.logits);
+  hipError_t e = launch_router(x, M, w_router, router_bias, E, shape->hidden, logits, stream);
+  if (e != hipSuccess) return hip_fail(e, "router launch");
+  BucketOut o = bucket_out(ws, W, counts_dev, nullptr, nullptr, nullptr, nullptr);
+  e = launch_topk_bucket(logits, M, k, topk_ids, topk_w, false, topk_ids, E, E, nullptr, o, stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  e = launch_topk_bucket(nullptr, M, k, nullptr, nullptr, true, topk_ids, E, E, nullptr, o, stream);
+  if (e != hipSuccess) return hip_fail(e, "bucket launch");
+  return MOE_OK;
+}
+
+// The expert part of a staged pass: moe_experts_forward on the staging slots with the pass's map.
+moe_status staged_experts(const moe_shape* shape, const uint16_t* x, int32_t M,
+                          const int32_t* topk_ids, const float* topk_w, const int32_t* e2s,
+                          const uint8_t* slots, float* y, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  WsLayout W;
+  moe_status st = check_ws(shape, M, ws, ws_bytes, &W);
+  if (st != MOE_OK) return st;
+  st = check_x_slots(x, slots);
+  if (st != MOE_OK) return st;
+  return run_experts(shape, x, M, RouteSrc::kIds, nullptr, const_cast<int32_t*>(topk_ids),
+                     const_cast<float*>(topk_w), e2s, slots, y, nullptr, nullptr, ws, W, true, true,
+                     stream);
+}
+
 }  // namespace moe
 
 using namespace moe;

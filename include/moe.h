@@ -323,6 +323,46 @@ moe_status moe_layer_forward_hybrid(const moe_shape* shape, const uint16_t* x, i
                                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
+ * Prefill with staged experts [MoE expert offload, "How it works", Prefill: when a call
+ * touches more distinct experts than the layer has slots, the experts are copied into a
+ * staging buffer by pinned asynchronous memcpy and the unchanged GEMM runs on it; tinyserve,
+ * "How it works" item 6: batched prefill groups tokens by expert and loads each expert once].
+ *   On stream: router + top-k (as moe_route), the route count of every expert; the host waits
+ *   for the counts (one synchronisation per call), takes the touched experts in ascending id
+ *   and copies each once from host_bank (pinned, E images back to back) into the staging slots
+ *   with hipMemcpyAsync on staging->copy_stream.  If they all fit (touched <= n_slots) one pass
+ *   runs the expert kernels (the grouped GEMMs for M >= 64) on them: y is the whole layer.
+ *   Otherwise passes of n_slots / 2 experts alternate between the two halves of the staging
+ *   slots: the copies of pass b + 1 overlap the expert kernels of pass b, each pass's output is
+ *   added to y on the stream (y = the sum over passes, every route once).  *n_touched and
+ *   *n_passes [host] report what was done (may be NULL).  Returns once every pass is enqueued;
+ *   the next call on the same staging waits for this one's passes before reusing its buffers.
+ * The staging (caller-owned): slots device [n_slots][image] (256-byte aligned), counts_dev [E],
+ * counts_host [host, pinned] [E], maps_dev [2][E], maps_host [host, pinned] [2][E], y_pass
+ * device [max_M][H], a copy stream and five events created by the caller; pending zeroed.
+ * --------------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t max_M;
+  int32_t n_slots;
+  uint8_t* slots;
+  int32_t* counts_dev;
+  int32_t* counts_host;
+  int32_t* maps_dev;
+  int32_t* maps_host;
+  float* y_pass;
+  hipStream_t copy_stream;
+  hipEvent_t ev_counts, ev_copied[2], ev_done[2];
+  int32_t pending[2];
+} moe_prefill_staging;
+
+moe_status moe_layer_forward_staged(const moe_shape* shape, const uint16_t* x, int32_t M,
+                                   const uint16_t* w_router, const float* router_bias,
+                                   const uint8_t* host_bank, int32_t* topk_ids, float* topk_w,
+                                   float* y, moe_prefill_staging* staging, void* ws,
+                                   size_t ws_bytes, hipStream_t stream, int32_t* n_touched,
+                                   int32_t* n_passes);
+
+/* ---------------------------------------------------------------------------------------
  * Slot refill [ninfer v0.4.0, "New": experts are copied to the GPU in the background;
  * MoE expert offload, intro: routed experts stay in pinned host RAM; ORT hybrid PR,
  * "Key Changes": pinned staging ordered by timing-disabled events].
