@@ -47,7 +47,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=256)
     p.add_argument("--warmup", type=int, default=32)
-    p.add_argument("--workload", default="decode", choices=["decode", "slots8", "stack48", "prefill"])
+    p.add_argument("--workload", default="decode",
+                   choices=["decode", "slots8", "slots8dev", "hybrid", "stack48", "prefill", "staged",
+                            "fate"])
     p.add_argument("--tokens", type=int, default=1, help="stack48: tokens per step (1, 4 or 8)")
     p.add_argument("--copies", type=int, default=16, help="distinct copies of the expert bank")
     p.add_argument("--stage-steps", type=int, default=256, help="marked steps for stage timing")
@@ -110,11 +112,63 @@ def time_graph(torch, B, stream, g):
 
 
 def cpu_cores():
+    """Threads the oracle's numpy (BLAS) work runs on."""
     try:
         from threadpoolctl import threadpool_info
         return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         return 1
+
+
+def nproc():
+    try:
+        return len(os.sched_getaffinity(0))
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(work, n, n1, per_unit, unit, sample):
+    """Times the oracle: work(i) for i < n on the host's BLAS threads, then work(i) for i < n1 on
+    one thread; value = per_unit / (seconds per work item)."""
+    tc = time.perf_counter()
+    for i in range(n):
+        work(i)
+    dt = (time.perf_counter() - tc) / n
+    one = None
+    if n1 > 0:
+        try:
+            from threadpoolctl import threadpool_limits
+            with threadpool_limits(1):
+                tc = time.perf_counter()
+                for i in range(n1):
+                    work(i)
+                one = (time.perf_counter() - tc) / n1
+        except Exception:
+            one = None
+    return {"value": round(per_unit / dt, 4), "unit": unit, "cores": cpu_cores(), "nproc": nproc(),
+            "value_1core": round(per_unit / one, 4) if one else None, "kind": "oracle",
+            "sample": f"{sample}: {n} items on {cpu_cores()} BLAS threads ({dt * n:.1f}s), "
+                      f"{n1} on one thread"}
+
+
+def stream_ceiling(torch, B, src, nbytes, stream, reps=64):
+    """Read-streaming ceiling: moe_hbm_read_probe over nbytes windows of src (rotating, so that
+    no window is cache-resident), GB/s of the average launch from HIP events."""
+    total = src.numel()
+    n_win = max(1, total // nbytes)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ev0, ev1 = B.event_create(timing=True), B.event_create(timing=True)
+    for r in range(8):
+        B.moe_hbm_read_probe(src[(r % n_win) * nbytes:], nbytes, sink, stream=stream)
+    B.event_record(ev0, stream)
+    for r in range(reps):
+        B.moe_hbm_read_probe(src[(r % n_win) * nbytes:], nbytes, sink, stream=stream)
+    B.event_record(ev1, stream)
+    B.event_synchronize(ev1)
+    us = B.event_elapsed_ms(ev0, ev1) * 1e3 / reps
+    B.event_destroy(ev0)
+    B.event_destroy(ev1)
+    return nbytes / (us * 1e-6) / 1e9, us
 
 
 # ---------------------------------------------------------------------------------------------
@@ -230,21 +284,23 @@ def bench_decode(args):
         except Exception:
             traffic = None
 
+    # the read-streaming ceiling of a weight stream of the step's size, same launch shape
+    ceil_gbs, ceil_us = stream_ceiling(torch, B, copies.view(-1), step_bytes, stream)
+    log(f"read-streaming ceiling: {ceil_gbs:.0f} GB/s ({ceil_us:.2f} us per {step_bytes} B)")
+
     cpu = None
     if args.cpu_steps > 0:
         from oracle import layer as O
         wr_h = synthetic.router_weights(wl)
         bias_h = synthetic.zipf_bias(wl)
-        tc = time.perf_counter()
-        for t in range(args.cpu_steps):
+
+        def work(t):
             x = synthetic.activations(wl, 1, t)
             oid, ow, _, _ = O.route(O.router_logits(x, wr_h, bias_h), k)
             O.layer_forward(x, oid, ow, experts)
-        dt = time.perf_counter() - tc
-        cpu = {"value": round(args.cpu_steps / dt, 4), "unit": "tok/s", "cores": cpu_cores(),
-               "kind": "oracle",
-               "sample": f"{args.cpu_steps} decode steps (M=1) of the same layer: float64 router, "
-                         f"top-k and dequantise-then-matmul of the 4 routed experts, {dt:.1f}s"}
+        cpu = cpu_baseline(work, args.cpu_steps, max(1, args.cpu_steps // 8), 1.0, "tok/s",
+                           "decode steps (M=1) of the same layer: float64 router, top-k and "
+                           "dequantise-then-matmul of the 4 routed experts")
 
     gbs_step = step_bytes / (ms_step * 1e-3) / 1e9
     out = {
@@ -274,7 +330,8 @@ def bench_decode(args):
                      "achieved": round(dom_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": dom_bytes, "us_per_launch": round(dom_us, 3),
-                     "launches_timed": n_st},
+                     "launches_timed": n_st, "measured_ceiling_gbs": round(ceil_gbs, 1),
+                     "frac_of_measured_ceiling": round(dom_gbs / ceil_gbs, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -382,11 +439,19 @@ def bench_slots8(args):
         cache.close()
         return res
 
-    # step time without refills (all hot map, warm) to size the visibility lag
-    warm = run(1, min(32, n_x), True)
-    step_ms = float(np.median(warm["step_ms"]))
+    # GPU time of a step without refills (the initial map, one HIP graph of steps), to size the
+    # visibility lag: the host loop itself paces the GPU, so its step time would overstate it
+    m0 = np.full(E, -1, np.int32)
+    m0[init] = np.arange(S, dtype=np.int32)
+    map0 = torch.from_numpy(m0).cuda()
+    n_cal = min(32, n_x)
+    g_cal = capture(torch, comp, lambda t: B.moe_layer_forward(
+        shape, xs[t], 1, wr, biases[t], map0, slots, ids_d[t], w_d[t], y_d[t], None, None, ws,
+        stream=comp), n_cal)
+    step_ms = time_graph(torch, B, comp, g_cal) / n_cal
+    del g_cal
     lag = int(np.ceil(copy_ms / max(step_ms, 1e-3))) + 1
-    log(f"calibration: refill batch {copy_ms:.3f} ms, step {step_ms * 1e3:.1f} us -> lag {lag} steps")
+    log(f"calibration: refill batch {copy_ms:.3f} ms, GPU step {step_ms * 1e3:.1f} us -> lag {lag} steps")
     res = run(lag, n_x, True)
     st = res["stats"]
     sm = res["step_ms"][args.warmup:]
@@ -412,7 +477,9 @@ def bench_slots8(args):
         "stall_us_total": round(stall_ms * 1e3, 1),
         "overlap": round(1.0 - stall_ms / copy_total, 4) if copy_total > 0 else None,
         "wall_tok_s": round(n_x / res["wall_s"], 1),
-        "note": "GPU slots (105.75 MB) fit in the 256 MB Infinity Cache: hot-path GB/s is cache-resident, not HBM",
+        "gpu_step_us_calibration": round(step_ms * 1e3, 2),
+        "note": "host policy in a Python loop: the host paces the GPU (see slots8dev for the "
+                "GPU-resident cache); GPU slots (105.75 MB) fit in the 256 MB Infinity Cache",
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -509,6 +576,24 @@ def bench_stack48(args):
     hit = hits_layer / (args.steps * M * k)
     tok_s = args.steps * M / (ms / 1e3)
     gbs = hot_bytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_steps > 0:
+        from oracle import layer as O
+        NLB = 4  # layers of the sample
+        cexp = [synthetic.experts_canonical(wl, l, range(E)) for l in range(n_gen)]
+        routers = [(synthetic.router_weights(wl, l), synthetic.zipf_bias(wl, l)) for l in range(NLB)]
+
+        def work(i):
+            x = synthetic.activations(wl, M, i)
+            for l in range(NLB):
+                oid, ow, _, _ = O.route(O.router_logits(x, *routers[l]), k)
+                y = O.layer_forward(x, oid, ow, cexp[l % n_gen], maps_h[l])["y_hot"]
+                x = O.f64_to_bf16_rne(O.bf16_to_f64(x) + y)
+        n_items = 24 if M == 1 else 8  # about 10 s of oracle work
+        cpu = cpu_baseline(work, n_items, 2, M * NLB / NL, "tok/s",
+                           f"token steps of {M} tokens through {NLB} of the {NL} layers (scaled to "
+                           f"{NL}): float64 router, top-k, hot-only experts of each layer's placement, "
+                           f"residual")
     out = {
         "metric": "48-layer E=512 MoE stack decode/verify tok/s, 256 of 512 experts resident per layer",
         "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
@@ -524,6 +609,7 @@ def bench_stack48(args):
         "hit_rate_mean": round(float(hit.mean()), 4),
         "hit_rate_per_layer_min_max": [round(float(hit.min()), 4), round(float(hit.max()), 4)],
         "cold_routes_per_token_step": round(float(cold_h.sum()) / args.steps, 2),
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -578,6 +664,19 @@ def bench_prefill(args):
     flops = 2.0 * M * k * 3 * H * I
     gbs = touched * exp_bytes / (ms * 1e-3) / 1e9
     tfs = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if args.cpu_steps > 0:
+        from oracle import layer as O
+        cexp = synthetic.experts_canonical(wl, 0, range(E))
+        wr_h, bias_h = synthetic.router_weights(wl), synthetic.zipf_bias(wl)
+
+        def work(i):
+            x = synthetic.activations(wl, M, i)
+            oid, ow, _, _ = O.route(O.router_logits(x, wr_h, bias_h), k)
+            O.layer_forward(x, oid, ow, cexp)
+        cpu = cpu_baseline(work, 8, 1, M, "tok/s",
+                           f"one call of {M} tokens: float64 router, top-k, dequantise-then-matmul of "
+                           f"every touched expert")
     out = {
         "metric": "MoE-layer prefill (M=512) grouped GEMM: expert-weight GB/s and TFLOP/s",
         "value": round(M / (ms / 1e3), 1), "unit": "tok/s", "n_gpus": 1, "steps": reps, "warmup": 2,
@@ -588,9 +687,331 @@ def bench_prefill(args):
         "expert_gbs": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
         "tflops": round(tfs, 2), "frac_bf16_peak": round(tfs / PEAK_BF16_TFLOPS, 5),
         "routes_per_expert_max_mean": [int(counts.max()), round(float(counts[counts > 0].mean()), 2)],
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+# ---------------------------------------------------------------------------------------------
+# slots8dev: 8 GPU slots, the GPU-resident cache, the whole decode loop in one HIP graph
+# ---------------------------------------------------------------------------------------------
+def _c3_setup(torch, B, L, synthetic, steps):
+    wl = synthetic.WORKLOADS["gptoss20b_8slots"]
+    H, I, E, k, S = wl.hidden, wl.inter, wl.n_experts, wl.top_k, wl.n_slots
+    shape = B.make_shape(H, I, E, k, S)
+    experts = synthetic.experts_canonical(wl, 0, range(E))
+    bank_np = L.pack_bank(shape, experts)
+    init = np.argsort(synthetic.zipf_ranks(wl))[:S].astype(np.int32)
+    xs = dev_bits(torch, np.concatenate([synthetic.activations(wl, 1, t) for t in range(steps)]))
+    biases = torch.from_numpy(np.stack([synthetic.zipf_bias(wl, 0, synthetic.drift_shift(wl, t))
+                                        for t in range(steps)])).cuda()
+    wr = dev_bits(torch, synthetic.router_weights(wl))
+    return wl, shape, experts, bank_np, init, xs, biases, wr
+
+
+def bench_slots8dev(args):
+    torch, B = setup()
+    import synthetic
+    from expert_offloaded_routed_amd import layer as L
+
+    steps = args.steps
+    wl, shape, experts, bank_np, init, xs, biases, wr = _c3_setup(torch, B, L, synthetic, steps)
+    H, E, k, S = wl.hidden, wl.n_experts, wl.top_k, wl.n_slots
+    img = bank_np.shape[1]
+    bank = L.pinned_bank(bank_np)
+    slots = L.device_slots(bank_np, init, S)
+    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    ws = torch.zeros(B.moe_workspace_size(shape, 1), dtype=torch.uint8, device="cuda")
+    ids = torch.full((steps, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((steps, k), dtype=torch.float32, device="cuda")
+    y = torch.zeros((steps, H), dtype=torch.float32, device="cuda")
+    maps = torch.zeros((steps, E), dtype=torch.int32, device="cuda")
+    plans = torch.zeros((steps, 2 * B.REFILL_RECORD_BYTES), dtype=torch.uint8, device="cuda")
+    nplan = torch.zeros((steps,), dtype=torch.int32, device="cuda")
+    ev = [[B.event_create() for _ in range(steps)] for _ in range(3)]  # plan, layer, copy
+
+    def build(cache, lag, refills):
+        def step(t):
+            cache.step(ids[(t - 1) % steps], k, maps[t], plans[t], nplan[t:t + 1], stream=comp)
+            B.event_record(ev[0][t], comp)
+            if refills and t - lag >= 0:
+                B.stream_wait_event(comp, ev[2][t - lag])
+            B.moe_route(shape, xs[t], 1, wr, biases[t], ids[t], w[t], ws, stream=comp)
+            B.moe_experts_forward(shape, xs[t], 1, ids[t], w[t], maps[t], slots, y[t], None, None, ws,
+                                  stream=comp)
+            B.event_record(ev[1][t], comp)
+            if refills:
+                B.stream_wait_event(copy, ev[0][t])
+                if t >= 1:
+                    B.stream_wait_event(copy, ev[1][t - 1])
+                cache.copy(nplan[t:t + 1], plans[t], bank, slots, stream=copy)
+                B.event_record(ev[2][t], copy)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(comp):
+            with torch.cuda.graph(g, stream=comp):
+                for t in range(steps):
+                    step(t)
+                if refills:
+                    B.stream_wait_event(comp, ev[2][steps - 1])
+        torch.cuda.synchronize()
+        return g
+
+    # calibration: GPU time of a step with no refills (static placement), and of the copy kernel
+    # moving one refill batch (2 experts)
+    cache0 = B.DeviceCache(shape, max_refills_per_step=0, initial_slot_expert=init, stream=comp)
+    g0 = build(cache0, 1, False)
+    t_hot = time_graph(torch, B, comp, g0) / steps
+    del g0
+    calib = torch.zeros((2 * B.REFILL_RECORD_BYTES,), dtype=torch.uint8)
+    rec = calib.numpy().view(np.int32).reshape(2, 6)
+    rec[0, :4] = [init[0], 0, -1, 0]
+    rec[1, :4] = [init[1], 1, -1, 0]
+    plan_c, n_c = calib.cuda(), torch.tensor([2], dtype=torch.int32, device="cuda")
+    e0, e1 = B.event_create(timing=True), B.event_create(timing=True)
+    cache0.copy(n_c, plan_c, bank, slots, stream=copy)  # (untimed first launch)
+    B.event_record(e0, copy)
+    for _ in range(4):
+        cache0.copy(n_c, plan_c, bank, slots, stream=copy)
+    B.event_record(e1, copy)
+    B.event_synchronize(e1)
+    t_copy = B.event_elapsed_ms(e0, e1) / 4
+    lag = int(np.ceil(t_copy / max(t_hot, 1e-6))) + 1
+    log(f"calibration: step {t_hot * 1e3:.1f} us (GPU, no refills), copy kernel {t_copy:.3f} ms per "
+        f"2 experts ({2 * img / (t_copy * 1e-3) / 1e9:.1f} GB/s) -> lag {lag} steps")
+    slots.copy_(L.device_slots(bank_np, init, S))
+    ids.fill_(-1)
+    cache = B.DeviceCache(shape, lag_steps=lag, initial_slot_expert=init, stream=comp)
+    g = build(cache, lag, True)
+    with torch.cuda.stream(comp):
+        g.replay()  # warm-up replay (the cache state carries over to the timed one)
+    torch.cuda.synchronize()
+    s1 = cache.stats()
+    t0, t1 = B.event_create(timing=True), B.event_create(timing=True)
+    B.event_record(t0, comp)
+    with torch.cuda.stream(comp):
+        g.replay()
+    B.event_record(t1, comp)
+    B.event_synchronize(t1)
+    ms = B.event_elapsed_ms(t0, t1)
+    s2 = cache.stats()
+    d = {f: s2[f] - s1[f] for f in s1}  # counters of the timed replay
+    refills = d["refills"]
+    stall_ms = max(0.0, ms - steps * t_hot)
+    copy_ms_total = refills / 2.0 * t_copy
+    out = {
+        "metric": "MoE-layer decode with an 8-slot GPU-resident expert cache: tok/s, hit rate, refill overlap",
+        "value": round(steps / (ms / 1e3), 1), "unit": "tok/s", "n_gpus": 1, "steps": steps,
+        "warmup": steps, "ms_per_step": round(ms / steps, 5), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic (seeded MXFP4 experts, Zipf(1.1) prior drifting every 32 steps)",
+        "config": {"workload": "gptoss20b_8slots_device_cache", "hidden": H, "inter": wl.inter,
+                   "n_experts": E, "top_k": k, "slots": S, "policy": "LRU", "max_refills_per_step": 2,
+                   "lag_steps": lag, "observes": "the previous step's routes, from device memory",
+                   "timed": "one HIP graph of the steps: policy kernel, router, top-k, gate/up, down "
+                            "on the compute stream; copy kernel on a side stream"},
+        "hit_rate": round(d["hits"] / max(1, d["routes"]), 4), "refills": refills,
+        "hot_step_us_no_refills": round(t_hot * 1e3, 2),
+        "refill_batch_ms": round(t_copy, 4),
+        "refill_gbs": round(2 * img / (t_copy * 1e-3) / 1e9, 2),
+        "stall_us_total": round(stall_ms * 1e3, 1),
+        "overlap": round(1.0 - stall_ms / copy_ms_total, 4) if copy_ms_total > 0 else None,
+        "note": "GPU slots (105.75 MB) fit in the 256 MB Infinity Cache: hot-path bytes are cache-resident",
+    }
+    if args.cpu_steps > 0:
+        from oracle import layer as O
+        from oracle.cache_policy import SlotCachePolicy
+        wr_h = synthetic.router_weights(wl)
+        pol = SlotCachePolicy(E, S, init, max_refills=2, lag=lag, max_pending=2)
+        prev = [None]
+
+        def work(t):
+            x = synthetic.activations(wl, 1, t)
+            oid, ow, _, _ = O.route(O.router_logits(x, wr_h, synthetic.zipf_bias(
+                wl, 0, synthetic.drift_shift(wl, t))), k)
+            m, _ = pol.step(t, prev[0])
+            prev[0] = oid
+            O.layer_forward(x, oid, ow, experts, m)
+        n = max(2, args.cpu_steps)
+        out["cpu_baseline"] = cpu_baseline(work, n, max(1, n // 8), 1.0, "tok/s",
+                                           "decode steps with the oracle's policy replay and the hot-only output")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------------------------------------
+# hybrid: 8 GPU slots (static, the 8 most popular experts), cold routes on the host cores
+# ---------------------------------------------------------------------------------------------
+def bench_hybrid(args):
+    torch, B = setup()
+    import synthetic
+    from expert_offloaded_routed_amd import layer as L
+
+    steps = min(args.steps, 64)
+    wl, shape, experts, bank_np, init, xs, biases, wr = _c3_setup(torch, B, L, synthetic, steps + 8)
+    H, E, k, S = wl.hidden, wl.n_experts, wl.top_k, wl.n_slots
+    bank = L.pinned_bank(bank_np)
+    slots = L.device_slots(bank_np, init, S)
+    e2s = np.full(E, -1, np.int32)
+    e2s[init] = np.arange(S, dtype=np.int32)
+    e2s_d = torch.from_numpy(e2s).cuda()
+    buf = L.Buffers(shape, 1)
+    st = B.HybridStaging(shape, 1)
+    threads = nproc()
+    stream = torch.cuda.Stream()
+    ids_all = np.zeros((steps, k), np.int32)
+
+    def call(t):
+        B.moe_layer_forward_hybrid(shape, xs[t], 1, wr, biases[t], e2s_d, e2s, slots, bank.numpy(),
+                                   buf.ids, buf.w, buf.y, st, buf.ws, n_threads=threads, stream=stream)
+
+    for t in range(4):
+        call(steps + t)
+    torch.cuda.synchronize()
+    tw = time.perf_counter()
+    for t in range(steps):
+        call(t)
+        ids_all[t] = st.ids.numpy()[0]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tw
+    # the host part alone on the same routes, and the GPU part alone
+    y_c = np.zeros((1, H), np.float32)
+    th = time.perf_counter()
+    for t in range(steps):
+        B.moe_cold_forward_host(shape, bank.numpy(), xs[t:t + 1].cpu().numpy().view(np.uint16), 1,
+                                ids_all[t:t + 1], np.full((1, k), 0.25, np.float32), e2s, y_c, threads)
+    host_ms = (time.perf_counter() - th) / steps * 1e3
+    cold = (e2s[ids_all] < 0).sum(axis=1)
+    img = bank_np.shape[1]
+    out = {
+        "metric": "MoE-layer decode, hybrid: 8 hot experts on the GPU, cold routes on the host cores",
+        "value": round(steps / wall, 2), "unit": "tok/s", "n_gpus": 1, "steps": steps, "warmup": 4,
+        "ms_per_step": round(wall / steps * 1e3, 4), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic", "config": {"workload": "gptoss20b_8slots_hybrid", "hidden": H,
+                                        "inter": wl.inter, "n_experts": E, "top_k": k, "slots": S,
+                                        "placement": "static: Zipf ranks 1..8", "host_threads": threads},
+        "cold_routes_per_step": round(float(cold.mean()), 3),
+        "host_cold_ms_per_step": round(host_ms, 3),
+        "host_cold_gbs": round(float(cold.mean()) * img / (host_ms * 1e-3) / 1e9, 2) if host_ms > 0 else None,
+        "note": "wall-clock per call: the host computes the cold routes while the GPU runs the hot ones",
+    }
+    st.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------------------------------------
+# staged: the E=512 prefill with every expert in host memory, 48 staging slots
+# ---------------------------------------------------------------------------------------------
+def bench_staged(args):
+    torch, B = setup()
+    import synthetic
+    from expert_offloaded_routed_amd import layer as L
+
+    wl = synthetic.WORKLOADS["e512_prefill"]
+    H, I, E, k = wl.hidden, wl.inter, wl.n_experts, wl.top_k
+    M = wl.tokens[0]
+    n_slots = 48
+    shape = B.make_shape(H, I, E, k, E)
+    bank_np = L.pack_bank(shape, synthetic.experts_canonical(wl, 0, range(E)))
+    bank = L.pinned_bank(bank_np)
+    img = bank_np.shape[1]
+    reps = max(3, min(args.steps, 8))
+    xs = dev_bits(torch, np.stack([synthetic.activations(wl, M, t) for t in range(reps + 1)]))
+    wr = dev_bits(torch, synthetic.router_weights(wl))
+    bias = torch.from_numpy(synthetic.zipf_bias(wl)).cuda()
+    st = B.PrefillStaging(shape, M, n_slots)
+    buf = L.Buffers(shape, M)
+    stream = torch.cuda.Stream()
+    B.moe_layer_forward_staged(shape, xs[reps], M, wr, bias, bank, buf.ids, buf.w, buf.y, st, buf.ws,
+                               stream=stream)
+    torch.cuda.synchronize()
+    tw = time.perf_counter()
+    touched, passes = [], []
+    for r in range(reps):
+        nt, npass = B.moe_layer_forward_staged(shape, xs[r], M, wr, bias, bank, buf.ids, buf.w, buf.y,
+                                               st, buf.ws, stream=stream)
+        touched.append(nt)
+        passes.append(npass)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - tw) / reps
+    moved = float(np.mean(touched)) * img
+    out = {
+        "metric": "MoE-layer prefill (M=512) with staged experts: touched experts copied once from host memory",
+        "value": round(M / wall, 1), "unit": "tok/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "e512_prefill_staged", "hidden": H, "inter": I, "n_experts": E, "top_k": k,
+                   "M": M, "staging_slots": n_slots, "resident": "none (every expert in pinned host memory)"},
+        "touched_experts_mean": round(float(np.mean(touched)), 1), "passes": int(np.max(passes)),
+        "staged_gbs": round(moved / wall / 1e9, 2),
+        "note": "wall-clock per call; the host copies are PCIe-bound and overlap the passes' expert kernels",
+    }
+    st.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+# ---------------------------------------------------------------------------------------------
+# fate: next-layer routes predicted from the current layer's input (the next layer's router)
+# ---------------------------------------------------------------------------------------------
+def bench_fate(args):
+    torch, B = setup()
+    import synthetic
+    from expert_offloaded_routed_amd import layer as L
+
+    wl = synthetic.WORKLOADS["e512_verify_stack"]
+    H, I, E, k = wl.hidden, wl.inter, wl.n_experts, wl.top_k
+    NL, T = 8, min(args.steps, 64)
+    shape = B.make_shape(H, I, E, k, E)
+    slots = L.device_slots(L.pack_bank(shape, synthetic.experts_canonical(wl, 0, range(E))))
+    wrs = [dev_bits(torch, synthetic.router_weights(wl, l)) for l in range(NL)]
+    bs = [torch.from_numpy(synthetic.zipf_bias(wl, l)).cuda() for l in range(NL)]
+    buf = L.Buffers(shape, 1)
+    pred = L.Buffers(shape, 1)
+    actual = np.zeros((T, NL, k), np.int32)
+    predicted = np.zeros((T, NL, k), np.int32)
+    x = torch.zeros((1, H), dtype=torch.int16, device="cuda")
+    for t in range(T):
+        x.copy_(dev_bits(torch, synthetic.activations(wl, 1, 9000 + t)))
+        for l in range(NL):
+            if l + 1 < NL:  # the next layer's router on this layer's input: the prediction
+                B.moe_route(shape, x, 1, wrs[l + 1], bs[l + 1], pred.ids, pred.w, pred.ws)
+                predicted[t, l + 1] = pred.ids[0].cpu().numpy()
+            B.moe_layer_forward_residual(shape, x, 1, wrs[l], bs[l], None, slots, buf.ids, buf.w, buf.y,
+                                         None, None, x, buf.ws)
+            actual[t, l] = buf.ids[0].cpu().numpy()
+    torch.cuda.synchronize()
+    # recall of the prediction, and the hit rate of a small per-layer LRU set with and without
+    # the predicted experts prefetched before the layer runs
+    recall = np.mean([len(set(predicted[t, l]) & set(actual[t, l])) / k
+                      for t in range(T) for l in range(1, NL)])
+    S = 64
+    hits = {"reactive": 0, "fate": 0}
+    for mode in hits:
+        for l in range(1, NL):
+            lru = []  # most recent last
+            for t in range(T):
+                have = set(lru)
+                if mode == "fate":
+                    have |= set(predicted[t, l].tolist())
+                hits[mode] += sum(1 for e in actual[t, l] if e in have)
+                for e in (list(predicted[t, l]) if mode == "fate" else []) + list(actual[t, l]):
+                    if e in lru:
+                        lru.remove(e)
+                    lru.append(int(e))
+                lru = lru[-S:]
+    n = T * (NL - 1) * k
+    out = {
+        "metric": "FATE next-layer prefetch: recall of the next layer's routes predicted from the current layer's input",
+        "value": round(float(recall), 4), "unit": "fraction", "n_gpus": 1, "steps": T, "warmup": 0,
+        "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "e512_stack_fate", "hidden": H, "inter": I, "n_experts": E, "top_k": k,
+                   "layers": NL, "tokens": T, "lru_slots": S},
+        "hit_rate_reactive_lru": round(hits["reactive"] / n, 4),
+        "hit_rate_with_fate_prefetch": round(hits["fate"] / n, 4),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
 
 
 def copy_calibration(mib):
@@ -612,8 +1033,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
         return 2
-    rc = {"decode": bench_decode, "slots8": bench_slots8, "stack48": bench_stack48,
-          "prefill": bench_prefill}[args.workload](args)
+    rc = {"decode": bench_decode, "slots8": bench_slots8, "slots8dev": bench_slots8dev,
+          "hybrid": bench_hybrid, "stack48": bench_stack48, "prefill": bench_prefill,
+          "staged": bench_staged, "fate": bench_fate}[args.workload](args)
     if args.calibrate_copy_mb > 0:
         copy_calibration(args.calibrate_copy_mb)
     return rc

@@ -99,6 +99,7 @@ _SIGS = {
     "moe_layer_forward_staged": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P,
                                  C.POINTER(moe_prefill_staging), _P, _SZ, _P, C.POINTER(_I32),
                                  C.POINTER(_I32)],
+    "moe_hbm_read_probe": [_P, _SZ, _P, _P],
     "moe_cold_forward_host": [C.POINTER(moe_shape), _P, _P, _I32, _P, _P, _P, _P, _I32],
     "moe_layer_forward_hybrid": [C.POINTER(moe_shape), _P, _I32, _P, _P, _P, _P, _P, _P, _P, _P,
                                  _P, C.POINTER(moe_hybrid_staging), _I32, _P, _SZ, _P],
@@ -366,6 +367,11 @@ def moe_layer_forward_hybrid(shape, x, M, w_router, router_bias, expert_to_slot,
                                            C.byref(staging.s), int(n_threads), _ptr(ws),
                                            _nbytes(ws), _stream(stream)),
            "moe_layer_forward_hybrid")
+
+
+def moe_hbm_read_probe(src, nbytes, sink, stream=None):
+    _check(load().moe_hbm_read_probe(_ptr(src), int(nbytes), _ptr(sink), _stream(stream)),
+           "moe_hbm_read_probe")
 
 
 def moe_residual_bf16(x, y, out, n, stream=None):

@@ -587,6 +587,15 @@ moe_status moe_workspace_errors(void* ws, size_t ws_bytes, int32_t* flags, hipSt
   return ok();
 }
 
+moe_status moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!src || !sink) return fail(MOE_ERR_INVALID_ARG, "moe_hbm_read_probe: src and sink are required");
+  if ((reinterpret_cast<uintptr_t>(src) & 15) || (bytes & 15) || bytes == 0)
+    return fail(MOE_ERR_INVALID_ARG, "moe_hbm_read_probe: src 16-byte aligned, bytes a positive multiple of 16");
+  hipError_t e = launch_stream_probe(src, bytes, sink, stream);
+  if (e != hipSuccess) return hip_fail(e, "probe launch");
+  return ok();
+}
+
 moe_status moe_residual_bf16(const uint16_t* x, const float* y, uint16_t* out, size_t n,
                              hipStream_t stream) {
   if (n == 0) return ok();

@@ -243,6 +243,8 @@ hipError_t launch_dcache_copy(const int32_t* n_plan, const moe_refill* plan, con
 // Kernel launchers (moe_kernels.hip).
 hipError_t launch_router(const uint16_t* x, int M, const uint16_t* wr, const float* bias, int E,
                          int H, float* logits, hipStream_t s);
+// Reads `bytes` (a multiple of 16) of src once with the fused decode kernel's launch shape.
+hipError_t launch_stream_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 // y[i] += add[i] for i < n.
 hipError_t launch_add_f32(float* y, const float* add, size_t n, hipStream_t s);
 // Copies the error word to *out (device or pinned host memory; NULL: nowhere) and clears it.

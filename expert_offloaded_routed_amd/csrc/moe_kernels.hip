@@ -2280,6 +2280,26 @@ hipError_t launch_add_f32(float* y, const float* add, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Read-streaming probe: `bytes` of src read once in 16-byte loads by a grid of one workgroup of
+// 16 waves per compute unit (the fused decode kernel's launch shape), every load of a thread
+// issued before any is used; the values are folded into one word that is stored only if it
+// equals an impossible pattern (so that the loads cannot be dropped).
+__global__ __launch_bounds__(1024) void k_stream_probe(const uint4* __restrict__ src, size_t n16,
+                                                       uint32_t* __restrict__ sink) {
+  constexpr int U = 8;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t t = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (size_t c0 = t; c0 < n16; c0 += stride * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[min(c0 + (size_t)u * stride, n16 - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u && t == stride) sink[0] = acc;  // (t never equals stride)
+}
+
 hipError_t launch_take_errors(int32_t* word, int32_t* out, hipStream_t s) {
   hipLaunchKernelGGL(k_take_errors, dim3(1), dim3(64), 0, s, word, out);
   return hipGetLastError();
@@ -2678,5 +2698,12 @@ hipError_t launch_layer_decode(const uint16_t* x, const uint16_t* wr, const floa
   return e;
 }
 #undef MOE_LD_SWITCH
+
+hipError_t launch_stream_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
+  const int cus = device_cus();
+  hipLaunchKernelGGL(k_stream_probe, dim3(cus > 0 ? cus : kNumCUs), dim3(1024), 0, s,
+                     reinterpret_cast<const uint4*>(src), bytes / 16, sink);
+  return hipGetLastError();
+}
 
 }  // namespace moe

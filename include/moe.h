@@ -471,6 +471,15 @@ moe_status moe_device_cache_copy(const moe_shape* shape, const int32_t* n_plan,
 moe_status moe_device_cache_stats(const moe_shape* shape, const void* state, size_t state_bytes,
                                   moe_cache_stats* stats, hipStream_t stream);
 
+/* Measurement aid (not part of the layer): reads `bytes` of device memory at src once, in
+ * 16-byte loads, with the launch shape of the fused one-token kernel (one workgroup of 16 waves
+ * per compute unit, every load of a thread issued before any is used).  Its duration is the
+ * device's read-streaming ceiling for a weight stream of that size, against which the fused
+ * kernel's rate is reported next to the published HBM peak.  sink: one uint32 of device memory
+ * (written only in a case that cannot occur).  src 16-byte aligned; bytes a positive multiple
+ * of 16. */
+moe_status moe_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Message describing the last failure of a call on this thread ("" if none). */
 const char* moe_last_error(void);
 
