@@ -11,6 +11,8 @@ single step), pure-Python loops only where the method is a small integer algorit
 
 Modules:
   mxfp4         -- E2M1 element / E8M0 scale decode (OCP Microscaling Formats v1.0)
+  formats       -- bf16, block FP8 (E4M3 + 128 x 128 fp32 scales) and NVFP4 (E2M1 + E4M3
+                   per 16 + fp32 matrix scale) decode, the other expert formats
   layer         -- router, softmax/top-k/renormalise, SwiGLU expert FFN, ordered combine,
                    route buckets
   cache_policy  -- per-layer slot cache: LRU / LFRU victim choice, bounded refills per step,

@@ -21,7 +21,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import mxfp4
+from . import formats
 
 
 # ---------------------------------------------------------------------------------------------
@@ -105,11 +105,9 @@ def silu(z: np.ndarray) -> np.ndarray:
 
 
 def dequantize_expert(expert: dict) -> dict:
-    """Canonical MXFP4 expert (gate/up [I,H], down [H,I]) -> float64 matrices."""
-    return {
-        name: mxfp4.dequantize(expert[name + "_codes"], expert[name + "_scales"])
-        for name in ("gate", "up", "down")
-    }
+    """Canonical expert (gate/up [I,H], down [H,I]) -> float64 matrices.  The dict's "format"
+    (absent: MXFP4) selects the decode (oracle.formats)."""
+    return {name: formats.dequantize_matrix(expert, name) for name in ("gate", "up", "down")}
 
 
 def expert_ffn(x: np.ndarray, dense: dict):

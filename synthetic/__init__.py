@@ -2,14 +2,18 @@
 
 This package only *generates* inputs: random weights, activations, router matrices, the
 popularity prior and its drift.  It holds none of the layer's arithmetic (no routing, no
-decode, no matmul).  The MXFP4 *encoder* used to turn Gaussian weights into expert bytes is
-data preparation: both sides only ever decode what it wrote, each with its own decoder.
+decode, no matmul).  The MXFP4, FP8 and NVFP4 *encoders* used to turn Gaussian weights into
+expert bytes are data preparation: both sides only ever decode what they wrote, each with its
+own decoder.
 """
 from .gen import (  # noqa: F401
     WORKLOADS,
     Workload,
     bf16_from_f32,
     quantize_mxfp4,
+    quantize_fp8_block,
+    quantize_nvfp4,
+    encode_e4m3,
     expert_canonical,
     router_weights,
     activations,

@@ -9,7 +9,8 @@ permutation, 4 = warm-up activations.
 
 Recipe (the pages give no weights or prompts; these stand in for them at the pages' shapes):
   * expert weights: fp32 N(0, 0.02), then MXFP4-encoded per 32-element block along the input
-    dimension (``quantize_mxfp4``);
+    dimension (``quantize_mxfp4``); the other expert formats encode the same draw (bf16
+    rounding, ``quantize_fp8_block``, ``quantize_nvfp4``);
   * router: fp32 N(0, 0.02) rounded to bf16;
   * activations: fp32 N(0, 1) rounded to bf16;
   * popularity prior: a seeded permutation gives each expert a rank r in 1..E and its logit
@@ -101,9 +102,17 @@ def quantize_mxfp4(w: np.ndarray):
     x = np.clip(e.astype(np.int32) - 1 - 2 + 127, 0, 254)
     x = np.where(amax == 0, 127, x).astype(np.int32)
     v = np.ldexp(blk, (127 - x)[..., None]).astype(np.float32)
+    code = _e2m1_codes(v).reshape(n, k)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return np.ascontiguousarray(packed), np.ascontiguousarray(x.astype(np.uint8))
+
+
+def _e2m1_codes(v: np.ndarray) -> np.ndarray:
+    """4-bit E2M1 codes of values already divided by their scale: nearest magnitude of
+    {0, .5, 1, 1.5, 2, 3, 4, 6} (ties to the even code, saturating at 6), sign in bit 3."""
     a = np.abs(v)
-    # Index of the nearest magnitude; '>' where the tie goes down to an even code,
-    # '>=' where it goes up to an even code.
+    # index of the nearest magnitude: '>' where a tie goes down to the even code, '>=' where it
+    # goes up to the even code
     mag = (a > 0.25).astype(np.uint8)
     mag += a >= 0.75
     mag += a > 1.25
@@ -111,32 +120,111 @@ def quantize_mxfp4(w: np.ndarray):
     mag += a > 2.5
     mag += a >= 3.5
     mag += a > 5.0
-    code = mag | (((v < 0) & (mag > 0)).astype(np.uint8) << 3)
-    code = code.reshape(n, k)
+    return mag | (((v < 0) & (mag > 0)).astype(np.uint8) << 3)
+
+
+def encode_e4m3(v: np.ndarray):
+    """OCP E4M3 codes of fp32 values with |v| <= 448, rounded to nearest even.
+
+    Returns ``(codes uint8, values float64)``: the values the codes stand for.  A magnitude a
+    in the binade [2^e, 2^(e+1)) (e >= -6; below 2^-6 the subnormals share the step of that
+    binade) is rounded to a multiple of 2^(e-3); a result of 16 steps moves to the next binade.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a > 448):
+        raise ValueError("E4M3 holds magnitudes up to 448")
+    _, ex = np.frexp(a)
+    e = np.maximum(ex.astype(np.int64) - 1, -6)
+    e = np.where(a == 0, -6, e)
+    m = np.rint(np.ldexp(a, (3 - e).astype(np.int64)))  # 0 .. 16, halves to even
+    up = m >= 16
+    e = np.where(up, e + 1, e)
+    m = np.where(up, 8, m).astype(np.int64)
+    code = np.where((e == -6) & (m < 8), m, ((e + 7) << 3) | (m - 8))
+    value = np.ldexp(m.astype(np.float64), (e - 3).astype(np.int64))
+    neg = (v < 0) & (code > 0)
+    code = code | (neg.astype(np.int64) << 7)
+    return code.astype(np.uint8), np.where(neg, -value, value)
+
+
+def quantize_fp8_block(w: np.ndarray):
+    """Encode an fp32 matrix [N, K] as block FP8: E4M3 codes [N, K] and fp32 scales
+    [ceil(N/128), ceil(K/128)], the scale of a 128 x 128 block being amax / 448 (1 when zero)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    nb, kb = (n + 127) // 128, (k + 127) // 128
+    scales = np.ones((nb, kb), dtype=np.float32)
+    codes = np.empty((n, k), dtype=np.uint8)
+    for bi in range(nb):
+        for bj in range(kb):
+            blk = w[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            amax = float(np.abs(blk).max())
+            s = np.float32(amax / 448.0) if amax > 0 else np.float32(1.0)
+            scales[bi, bj] = s
+            q = np.clip(blk.astype(np.float64) / float(s), -448.0, 448.0)
+            codes[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128] = encode_e4m3(q)[0]
+    return codes, scales
+
+
+def quantize_nvfp4(w: np.ndarray):
+    """Encode an fp32 matrix [N, K] (K % 16 == 0) as NVFP4.
+
+    Returns ``(codes uint8 [N, K/2], scales uint8 [N, K/16], global_scale float)``: g =
+    amax(matrix) / (6 * 448); each 16-element block gets the E4M3 code of amax(block) / 6 / g;
+    each element w / (block scale value * g) is rounded to E2M1 (element 2c in the low nibble of
+    byte c).
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    if k % 16:
+        raise ValueError("K must be a multiple of 16")
+    amax = float(np.abs(w).max())
+    g = float(np.float32(amax / (6.0 * 448.0))) if amax > 0 else 1.0
+    blk = w.reshape(n, k // 16, 16).astype(np.float64)
+    bmax = np.abs(blk).max(axis=2)
+    sc, sval = encode_e4m3(np.minimum(bmax / 6.0 / g, 448.0))
+    denom = sval * g
+    v = np.where(denom[..., None] > 0, blk / np.where(denom > 0, denom, 1.0)[..., None], 0.0)
+    code = _e2m1_codes(v).reshape(n, k)
     packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
-    return np.ascontiguousarray(packed), np.ascontiguousarray(x.astype(np.uint8))
+    return np.ascontiguousarray(packed), np.ascontiguousarray(sc), g
 
 
-def expert_canonical(wl: Workload, layer: int, expert: int) -> dict:
-    """One expert's MXFP4 weights in canonical row-major layout.
+def expert_canonical(wl: Workload, layer: int, expert: int, fmt: str = "mxfp4") -> dict:
+    """One expert's weights in canonical row-major layout, encoded in ``fmt``.
 
     gate, up: [inter, hidden]; down: [hidden, inter] (rows = outputs, blocks along inputs).
+    The fp32 weights are the same draw for every format.  Keys: "<m>_codes" (elements: bf16
+    bits uint16 for "bf16", else uint8 codes) and "<m>_scales" (E8M0 bytes for "mxfp4", fp32
+    block scales for "fp8_block", E4M3 bytes for "nvfp4", whose fp32 matrix scale is
+    "<m>_global"); the dict carries "format" for every format but MXFP4.
     """
     rng = _rng(wl.wid, STREAM_WEIGHTS, layer, expert)
     h, i = wl.hidden, wl.inter
-    out = {}
+    out = {} if fmt == "mxfp4" else {"format": fmt}
     for name, shape in (("gate", (i, h)), ("up", (i, h)), ("down", (h, i))):
         w = rng.standard_normal(shape, dtype=np.float32) * np.float32(WEIGHT_STD)
-        out[name + "_codes"], out[name + "_scales"] = quantize_mxfp4(w)
+        if fmt == "mxfp4":
+            out[name + "_codes"], out[name + "_scales"] = quantize_mxfp4(w)
+        elif fmt == "bf16":
+            out[name + "_codes"] = bf16_from_f32(w)
+        elif fmt == "fp8_block":
+            out[name + "_codes"], out[name + "_scales"] = quantize_fp8_block(w)
+        elif fmt == "nvfp4":
+            out[name + "_codes"], out[name + "_scales"], out[name + "_global"] = quantize_nvfp4(w)
+        else:
+            raise ValueError(f"unknown format {fmt!r}")
     return out
 
 
-def experts_canonical(wl: Workload, layer: int, experts, threads: int | None = None) -> list:
+def experts_canonical(wl: Workload, layer: int, experts, threads: int | None = None,
+                      fmt: str = "mxfp4") -> list:
     """Generate several experts in parallel threads (numpy releases the GIL in bulk ops)."""
     experts = list(experts)
     threads = threads or min(16, os.cpu_count() or 1, max(1, len(experts)))
     with ThreadPoolExecutor(max_workers=threads) as pool:
-        return list(pool.map(lambda e: expert_canonical(wl, layer, e), experts))
+        return list(pool.map(lambda e: expert_canonical(wl, layer, e, fmt), experts))
 
 
 def router_weights(wl: Workload, layer: int = 0) -> np.ndarray:
