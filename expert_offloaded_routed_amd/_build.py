@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libmoe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ROCM_INCLUDE = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
 
-HIP_SOURCES = ["moe_kernels.hip", "moe_dcache.hip"]
+HIP_SOURCES = ["moe_kernels.hip", "moe_dcache.hip", "moe_formats.hip"]
 HOST_SOURCES = ["moe_api.cpp", "moe_pack.cpp", "moe_cache.cpp", "moe_cold.cpp", "moe_stage.cpp"]
 
 # Packed fp32 instructions are kept out of every kernel (the compiler would otherwise form

@@ -33,7 +33,12 @@ class MoeError(RuntimeError):
 
 class moe_shape(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("inter", C.c_int32), ("n_experts", C.c_int32),
-                ("top_k", C.c_int32), ("n_slots", C.c_int32)]
+                ("top_k", C.c_int32), ("n_slots", C.c_int32), ("format", C.c_int32)]
+
+
+MOE_FORMAT_MXFP4, MOE_FORMAT_BF16, MOE_FORMAT_FP8_BLOCK, MOE_FORMAT_NVFP4 = 0, 1, 2, 3
+FORMAT_IDS = {"mxfp4": MOE_FORMAT_MXFP4, "bf16": MOE_FORMAT_BF16,
+              "fp8_block": MOE_FORMAT_FP8_BLOCK, "nvfp4": MOE_FORMAT_NVFP4}
 
 
 class moe_cache_config(C.Structure):
@@ -182,8 +187,38 @@ def _nbytes(a):
     return a.numel() * a.element_size()
 
 
-def make_shape(hidden, inter, n_experts, top_k, n_slots) -> moe_shape:
-    return moe_shape(hidden, inter, n_experts, top_k, n_slots)
+def make_shape(hidden, inter, n_experts, top_k, n_slots, fmt="mxfp4") -> moe_shape:
+    """fmt: a moe_format value or its name ("mxfp4", "bf16", "fp8_block", "nvfp4")."""
+    return moe_shape(hidden, inter, n_experts, top_k, n_slots,
+                     FORMAT_IDS[fmt] if isinstance(fmt, str) else int(fmt))
+
+
+_NAMES = ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")
+
+
+def _format_arrays(shape: moe_shape, expert: dict) -> list:
+    """The six byte arrays moe_pack_expert takes for the shape's format (None = NULL).
+
+    Expert dicts of the other formats: *_codes = elements (bf16 as uint16, E4M3 / E2M1 codes as
+    uint8); *_scales = fp32 block scales (FP8 block) or E4M3 bytes [N, K/16] (NVFP4, whose
+    fp32 matrix scale is *_global)."""
+    f = shape.format
+    out = []
+    for name in _NAMES:
+        mat, kind = name.split("_")
+        if kind == "codes":
+            a = np.ascontiguousarray(expert[name])
+            out.append(a.reshape(-1).view(np.uint8))
+        elif f == MOE_FORMAT_MXFP4:
+            out.append(np.ascontiguousarray(expert[name], dtype=np.uint8).reshape(-1))
+        elif f == MOE_FORMAT_BF16:
+            out.append(None)
+        elif f == MOE_FORMAT_FP8_BLOCK:
+            out.append(np.ascontiguousarray(expert[name], dtype=np.float32).reshape(-1).view(np.uint8))
+        else:
+            g = np.asarray([expert[mat + "_global"]], dtype=np.float32).view(np.uint8)
+            out.append(np.concatenate([g, np.ascontiguousarray(expert[name], dtype=np.uint8).reshape(-1)]))
+    return out
 
 
 # ---------------------------------------------------------------------------------------------
@@ -202,15 +237,16 @@ def moe_pack_expert(shape: moe_shape, expert: dict, image: np.ndarray | None = N
         image = np.empty(n, dtype=np.uint8)
     if image.nbytes < n:
         raise ValueError("image buffer too small")
-    args = [np.ascontiguousarray(expert[k], dtype=np.uint8) for k in
-            ("gate_codes", "gate_scales", "up_codes", "up_scales", "down_codes", "down_scales")]
-    _check(load().moe_pack_expert(C.byref(shape), *[_ptr(a) for a in args], _ptr(image)),
-           "moe_pack_expert")
+    args = _format_arrays(shape, expert)
+    _check(load().moe_pack_expert(C.byref(shape), *[None if a is None else _ptr(a) for a in args],
+                                  _ptr(image)), "moe_pack_expert")
     return image
 
 
 def moe_unpack_expert(shape: moe_shape, image: np.ndarray) -> dict:
     H, I = shape.hidden, shape.inter
+    if shape.format != MOE_FORMAT_MXFP4:
+        return _unpack_format(shape, image)
     out = {"gate_codes": np.empty((I, H // 2), np.uint8), "gate_scales": np.empty((I, H // 32), np.uint8),
            "up_codes": np.empty((I, H // 2), np.uint8), "up_scales": np.empty((I, H // 32), np.uint8),
            "down_codes": np.empty((H, I // 2), np.uint8), "down_scales": np.empty((H, I // 32), np.uint8)}
@@ -218,6 +254,40 @@ def moe_unpack_expert(shape: moe_shape, image: np.ndarray) -> dict:
                                     *[_ptr(out[k]) for k in ("gate_codes", "gate_scales", "up_codes",
                                                              "up_scales", "down_codes", "down_scales")]),
            "moe_unpack_expert")
+    return out
+
+
+def _unpack_format(shape: moe_shape, image: np.ndarray) -> dict:
+    H, I, f = shape.hidden, shape.inter, shape.format
+    dims = {"gate": (I, H), "up": (I, H), "down": (H, I)}
+    bufs, out = [], {}
+    for name in _NAMES:
+        mat, kind = name.split("_")
+        n, k = dims[mat]
+        if kind == "codes":
+            a = np.empty((n, k), np.uint16) if f == MOE_FORMAT_BF16 else \
+                np.empty((n, k if f == MOE_FORMAT_FP8_BLOCK else k // 2), np.uint8)
+            out[name] = a
+            bufs.append(a)
+        elif f == MOE_FORMAT_BF16:
+            bufs.append(None)
+        elif f == MOE_FORMAT_FP8_BLOCK:
+            a = np.empty(((n + 127) // 128, (k + 127) // 128), np.float32)
+            out[name] = a
+            bufs.append(a)
+        else:
+            a = np.empty(4 + n * (k // 16), np.uint8)
+            bufs.append(a)
+    _check(load().moe_unpack_expert(C.byref(shape), _ptr(np.ascontiguousarray(image)),
+                                    *[None if b is None else _ptr(b) for b in bufs]),
+           "moe_unpack_expert")
+    if f == MOE_FORMAT_NVFP4:
+        for i, name in enumerate(_NAMES):
+            if name.endswith("_scales"):
+                mat = name.split("_")[0]
+                n, k = dims[mat]
+                out[mat + "_global"] = float(bufs[i][:4].view(np.float32)[0])
+                out[name] = bufs[i][4:].reshape(n, k // 16).copy()
     return out
 
 

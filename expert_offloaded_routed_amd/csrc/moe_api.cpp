@@ -48,6 +48,8 @@ moe_status check_shape(const moe_shape* s) {
     return fail(MOE_ERR_UNSUPPORTED, "n_experts %d > %d", s->n_experts, kMaxExperts);
   if (s->top_k > kMaxTopK || s->top_k > s->n_experts)
     return fail(MOE_ERR_UNSUPPORTED, "top_k %d must be <= min(n_experts, %d)", s->top_k, kMaxTopK);
+  if (s->format < MOE_FORMAT_MXFP4 || s->format > MOE_FORMAT_NVFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "unknown expert format %d", s->format);
   return MOE_OK;
 }
 
@@ -154,6 +156,41 @@ enum class RouteSrc {
   kIds,     // caller's ids / w
 };
 
+// The expert stages of a call whose experts are not MXFP4: the top-k / bucketing kernel writes the
+// route table, then the generic gate/up and down kernels of the format.
+static moe_status run_experts_fmt(const moe_shape* sh, const uint16_t* x, int M,
+                                  const float* logits, int32_t* ids, float* w, const int32_t* e2s,
+                                  const uint8_t* slots, float* y, int32_t* cold_count,
+                                  int32_t* cold_routes, void* ws, const WsLayout& W, bool do_gateup,
+                                  bool do_down, hipStream_t stream, const hipEvent_t* marks,
+                                  uint16_t* x_next) {
+  const int H = sh->hidden, I = sh->inter, k = sh->top_k, E = sh->n_experts;
+  const FmtLayout F = fmt_layout(sh->format, H, I);
+  const RouteWs rw = route_ws(ws, W);
+  hipError_t e;
+  if (do_gateup) {
+    const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, cold_routes);
+    e = launch_topk_bucket(logits, M, k, ids, w, true, ids, E, sh->n_slots, e2s, o, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k / bucket launch");
+  }
+  if (marks && (e = record_mark(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  const RouteArgs ra = route_args(sh, M, nullptr, ids, w, e2s, nullptr, nullptr, nullptr, nullptr);
+  if (do_gateup) {
+    const int nd_max = (int)((size_t)M * k < (size_t)E ? (size_t)M * k : (size_t)E);
+    e = launch_gateup_fmt(sh->format, x, H, I, slots, F.image_bytes, F, nd_max, ra, rw,
+                          at<uint16_t>(ws, W.hq), stream);
+    if (e != hipSuccess) return hip_fail(e, "gate/up launch");
+  }
+  if (marks && (e = record_mark(marks[2], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  if (do_down) {
+    e = launch_down_fmt(sh->format, H, I, slots, F.image_bytes, F, ra, rw, at<uint16_t>(ws, W.hq),
+                        at<float>(ws, W.pdn), y, Residual{x, x_next}, stream);
+    if (e != hipSuccess) return hip_fail(e, "down launch");
+  }
+  if (marks && (e = record_mark(marks[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  return MOE_OK;
+}
+
 // The expert stages of a call.  Small calls (M*k <= 256) rebuild the route table inside every
 // gate/up workgroup (top-k from the logits, or the ids); one of them also publishes it to the
 // workspace for the down kernel.  Larger calls run the top-k / bucketing kernel first, which
@@ -164,6 +201,10 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
                               int32_t* cold_routes, void* ws, const WsLayout& W, bool do_gateup,
                               bool do_down, hipStream_t stream, const hipEvent_t* marks = nullptr,
                               uint16_t* x_next = nullptr) {
+  if (sh->format != MOE_FORMAT_MXFP4)
+    return run_experts_fmt(sh, x, M, src == RouteSrc::kLogits ? logits : nullptr, ids, w, e2s,
+                           slots, y, cold_count, cold_routes, ws, W, do_gateup, do_down, stream,
+                           marks, x_next);
   const ImageLayout L = image_layout(sh->hidden, sh->inter);
   const ExpertPlan p = plan_experts(L, M, sh->n_experts, sh->top_k);
   const RouteWs rw = route_ws(ws, W);
@@ -246,8 +287,8 @@ static moe_status layer_forward(const moe_shape* shape, const uint16_t* x, int32
   // the multi-launch path.
   const ImageLayout L = image_layout(shape->hidden, shape->inter);
   const ExpertPlan p = plan_experts(L, M, shape->n_experts, shape->top_k);
-  const bool fused =
-      !decode_unfused() && layer_decode_fusable(L, p, M, shape->top_k, shape->n_experts);
+  const bool fused = shape->format == MOE_FORMAT_MXFP4 && !decode_unfused() &&
+                     layer_decode_fusable(L, p, M, shape->top_k, shape->n_experts);
   const bool router_inside = fused && layer_decode_router_inside(L, shape->n_experts);
   if (marks && (e = record_mark(marks[0], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   if (!router_inside) {
@@ -360,7 +401,7 @@ moe_status moe_expert_image_bytes(const moe_shape* shape, size_t* bytes) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
-  *bytes = image_layout(shape->hidden, shape->inter).image_bytes;
+  *bytes = expert_image_bytes(shape);
   return ok();
 }
 
@@ -382,6 +423,10 @@ moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n) {
   if (M < 0) return fail(MOE_ERR_INVALID_ARG, "M < 0");
   if (M == 0) {
     *n = 1;  // the cold report of an empty call
+    return ok();
+  }
+  if (shape->format != MOE_FORMAT_MXFP4) {
+    *n = 4;  // router, top-k / bucket, gate/up, down + combine
     return ok();
   }
   const ImageLayout L = image_layout(shape->hidden, shape->inter);
@@ -622,7 +667,7 @@ moe_status moe_slot_refill(const moe_shape* shape, uint8_t* slots, const uint8_t
       if (slot_ids[j] == slot_ids[i])
         return fail(MOE_ERR_INVALID_ARG, "refill: slot %d written twice", slot_ids[i]);
   }
-  const size_t img = image_layout(shape->hidden, shape->inter).image_bytes;
+  const size_t img = expert_image_bytes(shape);
   hipError_t e;
   if (wait_before) {
     e = hipStreamWaitEvent(copy_stream, wait_before, 0);

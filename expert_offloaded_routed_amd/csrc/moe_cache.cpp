@@ -349,8 +349,8 @@ moe_status moe_device_cache_copy(const moe_shape* shape, const int32_t* n_plan,
                 hipGetErrorString(e));
   if (reinterpret_cast<uintptr_t>(dev_bank) & 15)
     return fail(MOE_ERR_INVALID_ARG, "host_bank must be 16-byte aligned");
-  const ImageLayout L = image_layout(shape->hidden, shape->inter);
-  e = launch_dcache_copy(n_plan, plan, static_cast<const uint8_t*>(dev_bank), slots, L.image_bytes,
+  e = launch_dcache_copy(n_plan, plan, static_cast<const uint8_t*>(dev_bank), slots,
+                         expert_image_bytes(shape),
                          shape->n_experts, shape->n_slots, kDcacheMaxQ, stream);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "device cache copy launch: %s", hipGetErrorString(e));
   return ok();

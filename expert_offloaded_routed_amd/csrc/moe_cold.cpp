@@ -178,6 +178,9 @@ moe_status moe_cold_forward_host(const moe_shape* shape, const uint8_t* host_ban
                                  float* y_cold, int32_t n_threads) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
+  if (shape->format != MOE_FORMAT_MXFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "the host expert path reads MXFP4 images only (format %d)",
+                shape->format);
   if (M < 0) return fail(MOE_ERR_INVALID_ARG, "M < 0");
   if (M == 0) return ok();
   if (!host_bank || !x || !topk_ids || !topk_w || !y_cold)
@@ -195,6 +198,9 @@ moe_status moe_layer_forward_hybrid(const moe_shape* shape, const uint16_t* x, i
                                     void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
+  if (shape->format != MOE_FORMAT_MXFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "the host expert path reads MXFP4 images only (format %d)",
+                shape->format);
   if (!staging || !staging->x || !staging->ids || !staging->w || !staging->y_cold ||
       !staging->y_cold_dev || !staging->routed || !staging->added)
     return fail(MOE_ERR_INVALID_ARG, "moe_layer_forward_hybrid: incomplete staging");

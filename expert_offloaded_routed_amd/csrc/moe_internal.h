@@ -41,6 +41,8 @@ constexpr int kBucketThreads = 1024; // threads of the top-k / bucketing workgro
 constexpr int kTopkThreads = 128;    // threads of a workgroup of the multi-workgroup top-k
 constexpr int kDnRows = 16;          // rows of a down tile (one MFMA operand)
 
+inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
 struct ImageLayout {
   int H, I;
   int nb_h, ng_h;  // gate/up: blocks and groups along K = H
@@ -77,6 +79,42 @@ inline ImageLayout image_layout(int H, int I) {
   L.dn_bytes = L.dn_tile_bytes * L.dn_tiles;
   L.image_bytes = (L.gu_bytes + L.dn_bytes + 255) / 256 * 256;
   return L;
+}
+
+// Expert images of the other formats (MOE_FORMAT_BF16, MOE_FORMAT_FP8_BLOCK, MOE_FORMAT_NVFP4):
+// the six canonical tensors of moe_pack_expert, each row-major and starting at a multiple of
+// 256 bytes, in the order [gate | gate scales | up | up scales | down | down scales]; the image is
+// padded to a multiple of 256 bytes.  Element bytes of a matrix [N][K]: bf16 2NK, E4M3 NK,
+// E2M1 NK/2.  Scale bytes: none (bf16); fp32 [ceil(N/128)][ceil(K/128)] (FP8 block); one fp32
+// global scale followed by E4M3 bytes [N][K/16] (NVFP4).
+struct FmtLayout {
+  size_t gate, gate_s, up, up_s, down, down_s, image_bytes;
+};
+inline size_t fmt_elem_bytes(int fmt, int N, int K) {
+  const size_t nk = (size_t)N * K;
+  return fmt == MOE_FORMAT_BF16 ? 2 * nk : fmt == MOE_FORMAT_FP8_BLOCK ? nk : nk / 2;
+}
+inline size_t fmt_scale_bytes(int fmt, int N, int K) {
+  if (fmt == MOE_FORMAT_FP8_BLOCK) return 4 * (size_t)((N + 127) / 128) * ((K + 127) / 128);
+  if (fmt == MOE_FORMAT_NVFP4) return 4 + (size_t)N * (K / 16);
+  return 0;
+}
+inline FmtLayout fmt_layout(int fmt, int H, int I) {
+  FmtLayout F;
+  size_t o = 0;
+  F.gate = o;    o = align256(o + fmt_elem_bytes(fmt, I, H));
+  F.gate_s = o;  o = align256(o + fmt_scale_bytes(fmt, I, H));
+  F.up = o;      o = align256(o + fmt_elem_bytes(fmt, I, H));
+  F.up_s = o;    o = align256(o + fmt_scale_bytes(fmt, I, H));
+  F.down = o;    o = align256(o + fmt_elem_bytes(fmt, H, I));
+  F.down_s = o;  o = align256(o + fmt_scale_bytes(fmt, H, I));
+  F.image_bytes = o;
+  return F;
+}
+// Bytes of one expert image of the shape's format.
+inline size_t expert_image_bytes(const moe_shape* s) {
+  return s->format == MOE_FORMAT_MXFP4 ? image_layout(s->hidden, s->inter).image_bytes
+                                       : fmt_layout(s->format, s->hidden, s->inter).image_bytes;
 }
 
 // Calls with at least this many tokens take the grouped GEMM path (and the MFMA router).
@@ -117,8 +155,6 @@ struct WsLayout {
   size_t pdn;            // f32 [M*k][H]: down partial sums of the grouped path
   size_t total;
 };
-
-inline size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 constexpr int kMetaWords = 16;  // int32 words of the workspace header
 constexpr int kMetaErr = 2;     // index of the error word
@@ -273,6 +309,17 @@ hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* 
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
                        const uint16_t* hbuf, float* pdn, float* y, Residual res, hipStream_t s);
+// The expert kernels of the other formats (moe_formats.hip), after the bucketing kernel:
+// gate/up + SiLU into hbuf (bf16 [M*k][I]); down, route partials in pdn ([M*k][H] fp32) and the
+// ordered combine into y (and the residual).
+hipError_t launch_gateup_fmt(int fmt, const uint16_t* x, int H, int I, const uint8_t* slots,
+                             size_t image_bytes, const FmtLayout& F, int nd_max,
+                             const RouteArgs& ra, const RouteWs& rw, uint16_t* hbuf,
+                             hipStream_t s);
+hipError_t launch_down_fmt(int fmt, int H, int I, const uint8_t* slots, size_t image_bytes,
+                           const FmtLayout& F, const RouteArgs& ra, const RouteWs& rw,
+                           const uint16_t* hbuf, float* pdn, float* y, Residual res,
+                           hipStream_t s);
 hipError_t launch_residual(const uint16_t* x, const float* y, uint16_t* out, size_t n,
                            hipStream_t s);
 hipError_t launch_gateup_grouped(const uint16_t* x, int H, int I, const uint8_t* slots,

@@ -1,5 +1,5 @@
-// Expert image packing: canonical MXFP4 matrices <-> the kernel layout described in
-// moe_internal.h.  Pure host code.
+// Expert image packing: canonical matrices <-> the image layouts described in moe_internal.h
+// (the MXFP4 kernel layout; the six row-major sections of the other formats).  Pure host code.
 #include <string.h>
 
 #include "moe.h"
@@ -81,6 +81,22 @@ static void down_tiles(uint8_t* img, const ImageLayout& L, uint8_t* codes, uint8
   }
 }
 
+// The other formats: the six canonical arrays copied into (or out of) their image sections.
+template <bool PACK>
+static void fmt_sections(int fmt, int H, int I, uint8_t* img, uint8_t* const* arr) {
+  const FmtLayout F = fmt_layout(fmt, H, I);
+  const size_t off[6] = {F.gate, F.gate_s, F.up, F.up_s, F.down, F.down_s};
+  const int N[6] = {I, I, I, I, H, H}, K[6] = {H, H, H, H, I, I};
+  for (int a = 0; a < 6; ++a) {
+    const size_t n = (a & 1) ? fmt_scale_bytes(fmt, N[a], K[a]) : fmt_elem_bytes(fmt, N[a], K[a]);
+    if (n == 0) continue;
+    if (PACK)
+      memcpy(img + off[a], arr[a], n);
+    else
+      memcpy(arr[a], img + off[a], n);
+  }
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -93,6 +109,18 @@ moe_status moe_pack_expert(const moe_shape* shape, const uint8_t* gate_codes,
                            const uint8_t* down_scales, uint8_t* image) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
+  if (shape->format != MOE_FORMAT_MXFP4) {
+    const bool scaled = shape->format != MOE_FORMAT_BF16;
+    if (!gate_codes || !up_codes || !down_codes || !image ||
+        (scaled && (!gate_scales || !up_scales || !down_scales)))
+      return fail(MOE_ERR_INVALID_ARG, "moe_pack_expert: NULL pointer");
+    memset(image, 0, expert_image_bytes(shape));
+    uint8_t* arr[6] = {const_cast<uint8_t*>(gate_codes), const_cast<uint8_t*>(gate_scales),
+                       const_cast<uint8_t*>(up_codes),   const_cast<uint8_t*>(up_scales),
+                       const_cast<uint8_t*>(down_codes), const_cast<uint8_t*>(down_scales)};
+    fmt_sections<true>(shape->format, shape->hidden, shape->inter, image, arr);
+    return ok();
+  }
   if (!gate_codes || !gate_scales || !up_codes || !up_scales || !down_codes || !down_scales || !image)
     return fail(MOE_ERR_INVALID_ARG, "moe_pack_expert: NULL pointer");
   const ImageLayout L = image_layout(shape->hidden, shape->inter);
@@ -110,6 +138,15 @@ moe_status moe_unpack_expert(const moe_shape* shape, const uint8_t* image, uint8
                              uint8_t* down_codes, uint8_t* down_scales) {
   moe_status st = check_shape(shape);
   if (st != MOE_OK) return st;
+  if (shape->format != MOE_FORMAT_MXFP4) {
+    const bool scaled = shape->format != MOE_FORMAT_BF16;
+    if (!gate_codes || !up_codes || !down_codes || !image ||
+        (scaled && (!gate_scales || !up_scales || !down_scales)))
+      return fail(MOE_ERR_INVALID_ARG, "moe_unpack_expert: NULL pointer");
+    uint8_t* arr[6] = {gate_codes, gate_scales, up_codes, up_scales, down_codes, down_scales};
+    fmt_sections<false>(shape->format, shape->hidden, shape->inter, const_cast<uint8_t*>(image), arr);
+    return ok();
+  }
   if (!gate_codes || !gate_scales || !up_codes || !up_scales || !down_codes || !down_scales || !image)
     return fail(MOE_ERR_INVALID_ARG, "moe_unpack_expert: NULL pointer");
   const ImageLayout L = image_layout(shape->hidden, shape->inter);

@@ -52,7 +52,7 @@ extern "C" moe_status moe_layer_forward_staged(const moe_shape* shape, const uin
   if (n_passes) *n_passes = 0;
   if (M == 0) return ok();
   const int E = shape->n_experts, H = shape->hidden;
-  const size_t img = image_layout(shape->hidden, shape->inter).image_bytes;
+  const size_t img = expert_image_bytes(shape);
   hipError_t e;
   // 1. routes and the route count of every expert (on the stream), then on the host
   rs = staged_route_and_count(shape, x, M, w_router, router_bias, topk_ids, topk_w, st->counts_dev,

@@ -47,14 +47,31 @@ typedef enum {
   MOE_ERR_STATE = -5        /* cache object used inconsistently (e.g. step not increasing) */
 } moe_status;
 
+/* Expert weight formats [MoE expert offload, "Supported": besides MXFP4, unquantised bf16,
+ * block FP8 and NVFP4 experts run through the same generic slot path].  Readings of the three
+ * that the pages name but do not define (the usual published definitions):
+ *   MOE_FORMAT_BF16      bf16 weights, no scales;
+ *   MOE_FORMAT_FP8_BLOCK OCP FP8 E4M3 weights (bias 7, subnormals, max 448, S.1111.111 = NaN)
+ *                        times one fp32 scale per 128 x 128 block of the [N, K] matrix;
+ *   MOE_FORMAT_NVFP4     E2M1 weights (as in MXFP4) times one E4M3 scale per 16 elements along
+ *                        K, times one fp32 scale of the whole matrix. */
+typedef enum {
+  MOE_FORMAT_MXFP4 = 0,
+  MOE_FORMAT_BF16 = 1,
+  MOE_FORMAT_FP8_BLOCK = 2,
+  MOE_FORMAT_NVFP4 = 3
+} moe_format;
+
 /* Layer shape.  hidden = H, inter = I (per-expert intermediate size), n_experts = E,
- * top_k = k, n_slots = S (GPU slots; S >= E means every expert can be resident). */
+ * top_k = k, n_slots = S (GPU slots; S >= E means every expert can be resident), format = the
+ * experts' moe_format (0 = MXFP4, so a zero-initialised field keeps MXFP4). */
 typedef struct {
   int32_t hidden;
   int32_t inter;
   int32_t n_experts;
   int32_t top_k;
   int32_t n_slots;
+  int32_t format;
 } moe_shape;
 
 /* ---------------------------------------------------------------------------------------
@@ -71,7 +88,14 @@ typedef struct {
 moe_status moe_expert_image_bytes(const moe_shape* shape, size_t* bytes);
 
 /* Convert one expert from the canonical layout to its image.  All pointers [host]; the
- * image buffer must hold moe_expert_image_bytes() bytes.  Pure host code. */
+ * image buffer must hold moe_expert_image_bytes() bytes.  Pure host code.
+ * For the other formats the six pointers are each matrix's elements and scales, row-major:
+ *   MOE_FORMAT_BF16:      *_codes = bf16 [N][K] (uint16 bit patterns); *_scales unused (NULL);
+ *   MOE_FORMAT_FP8_BLOCK: *_codes = E4M3 bytes [N][K]; *_scales = fp32 [ceil(N/128)][ceil(K/128)];
+ *   MOE_FORMAT_NVFP4:     *_codes = E2M1 [N][K/2] (element 2c in the low nibble of byte c);
+ *                         *_scales = 4 + N*K/16 bytes: the fp32 matrix scale, then E4M3 bytes
+ *                         [N][K/16].
+ * Their image is these six arrays in that order, each at a multiple of 256 bytes. */
 moe_status moe_pack_expert(const moe_shape* shape,
                            const uint8_t* gate_codes, const uint8_t* gate_scales,
                            const uint8_t* up_codes, const uint8_t* up_scales,
@@ -166,6 +190,11 @@ moe_status moe_bucket_routes(const moe_shape* shape, const int32_t* topk_ids, in
  * slots = the device slot array (n_slots images); y [M,H] fp32 is overwritten (zeros for a
  * token whose routes are all cold); cold_count [1] / cold_routes [M*k] may be NULL.
  * Deterministic: the result does not depend on slot numbering, bucket order or timing.
+ * Formats other than MXFP4 (shape->format) run generic kernels for every M, after the
+ * bucketing kernel: gate/up decodes each 16-byte chunk of a weight row exactly to bf16 pairs,
+ * dots them with x in fp32 and applies the chunk's scales to the chunk's sum (FP8 block: the
+ * block scale; NVFP4: each 16-element scale times the matrix scale); down does the same over
+ * h, then the combine above.  The one-token fused kernel and the grouped GEMM are MXFP4 only.
  * --------------------------------------------------------------------------------------- */
 moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_t M,
                                const int32_t* topk_ids, const float* topk_w,
@@ -176,10 +205,11 @@ moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_
 /* ---------------------------------------------------------------------------------------
  * Whole layer in one call: moe_route followed by moe_experts_forward.  For M*k <= 256 the
  * top-k, slot resolve and bucketing run inside the expert kernels (three launches: router
- * GEMV, gate/up, down + combine).  For one token (M = 1, top_k <= 16) of the shapes the fused
- * kernel is built for (moe_layer_launches reports it; GPT-OSS-20B's is one) gate/up and down
- * are one launch of one workgroup per compute unit, h handed from gate/up to down by value
- * through the workspace (the router kernel marks it unwritten first): two launches in all;
+ * GEMV, gate/up, down + combine).  For one token (M = 1, top_k <= 16) of the MXFP4 shapes the
+ * fused kernel is built for (moe_layer_launches reports it; GPT-OSS-20B's is one) gate/up and
+ * down are one launch of one workgroup per compute unit, h handed from gate/up to down by value
+ * through the workspace in words tagged with the call; for routers of at most 32 experts and
+ * H <= 4096 the router runs inside that launch too (one launch in all), else before it (two);
  * the environment variable MOE_DECODE_UNFUSED=1, read once per process, keeps three.  Same
  * arguments and outputs as the two calls; the numerics are bitwise theirs, except on the
  * fused path, whose sums over K run in another order (agreement within 1e-4 relative L2);
@@ -227,9 +257,10 @@ moe_status moe_layer_forward_noalloc(const moe_shape* shape, const uint16_t* x, 
                                      int32_t* cold_count, int32_t* cold_routes, int32_t* errors,
                                      hipStream_t stream);
 
-/* Number of kernel launches moe_layer_forward makes for M tokens of this shape: 2 when gate/up
- * and down run as one launch, 3 for small calls, 4 past 256 routes, 5 on the grouped-GEMM path
- * (M >= 64), 1 for M = 0.  For callers that budget graph nodes or time stages.  Writes *n; no
+/* Number of kernel launches moe_layer_forward makes for M tokens of this shape: 1 or 2 when
+ * gate/up and down run as one launch (router inside it, or before it), 3 for small calls, 4 past
+ * 256 routes and for the formats other than MXFP4, 5 on the grouped-GEMM path (M >= 64), 1 for
+ * M = 0.  For callers that budget graph nodes or time stages.  Writes *n; no
  * device work. */
 moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n);
 
@@ -286,6 +317,7 @@ moe_status moe_residual_bf16(const uint16_t* x, const float* y, uint16_t* out, s
  *   x [M,H] bf16; topk_ids / topk_w [M,k]; y_cold [M,H] fp32 is overwritten (zeros for a token
  *   with no cold route); routes with an id outside [0, E) are skipped.  n_threads <= 0: one per
  *   host core.  Synchronous, deterministic (the result does not depend on n_threads).
+ *   MXFP4 experts only (other formats: MOE_ERR_UNSUPPORTED, as for moe_layer_forward_hybrid).
  *
  * moe_layer_forward_hybrid: the whole layer with cold routes on the host:
  *   on stream: router + top-k (as moe_route), copies of x, topk_ids and topk_w into the pinned

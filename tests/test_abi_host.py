@@ -224,3 +224,49 @@ def test_pack_down_layout_mfma_steps_and_partial_step():
     # block 90 (step 22, lane group 2) and step 23 do not exist: padding 127
     assert img[t1 + code_bytes + (5 * 64 + 37) * 4 + 2] == 127
     assert img[t1 + code_bytes + (5 * 64 + 5) * 4 + 3] == 127
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8_block", "nvfp4"])
+def test_other_formats_pack_round_trip_and_host_checks(fmt):
+    """Images of the other formats hold the six canonical arrays row-major, each at a multiple
+    of 256 bytes; the host checks of the format field run before anything is enqueued."""
+    _lib()
+    wl = synthetic.WORKLOADS["tiny"]
+    H, I = wl.hidden, wl.inter
+    shape = B.make_shape(H, I, wl.n_experts, wl.top_k, wl.n_experts, fmt)
+    ex = synthetic.expert_canonical(wl, 0, 2, fmt)
+
+    def sz(n, k):
+        el = {"bf16": 2 * n * k, "fp8_block": n * k, "nvfp4": n * k // 2}[fmt]
+        sc = {"bf16": 0, "fp8_block": 4 * ((n + 127) // 128) * ((k + 127) // 128),
+              "nvfp4": 4 + n * (k // 16)}[fmt]
+        r = lambda v: (v + 255) // 256 * 256
+        return r(el) + r(sc)
+
+    assert B.moe_expert_image_bytes(shape) == 2 * sz(I, H) + sz(H, I)
+    img = B.moe_pack_expert(shape, ex)
+    back = B.moe_unpack_expert(shape, img)
+    for key, v in ex.items():
+        if key != "format":
+            assert np.array_equal(np.asarray(back[key]), np.asarray(v)), key
+    # the gate elements open the image, row-major
+    first = np.asarray(ex["gate_codes"]).reshape(-1)[:8]
+    assert np.array_equal(img[:first.nbytes], first.view(np.uint8))
+    # every format but MXFP4: router, top-k / bucketing, gate/up, down
+    assert [B.moe_layer_launches(shape, M) for M in (0, 1, 64)] == [1, 4, 4]
+    # the host expert path reads MXFP4 images only
+    M = 1
+    y = np.zeros((M, H), np.float32)
+    with pytest.raises(B.MoeError) as e:
+        B.moe_cold_forward_host(shape, np.zeros((wl.n_experts, B.moe_expert_image_bytes(shape)), np.uint8),
+                                synthetic.activations(wl, M, 0), M, np.zeros((M, wl.top_k), np.int32),
+                                np.ones((M, wl.top_k), np.float32), None, y)
+    assert e.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+def test_unknown_format_is_rejected():
+    _lib()
+    for f in (-1, 4):
+        with pytest.raises(B.MoeError) as e:
+            B.moe_expert_image_bytes(B.make_shape(256, 512, 8, 2, 8, f))
+        assert e.value.status == B.MOE_ERR_UNSUPPORTED
