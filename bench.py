@@ -24,6 +24,11 @@ Other workloads (one JSON line each, --workload):
   stack48   48 stacked E=512 layers (H=2048, I=512, k=10), 256 of 512 experts resident per layer
             by warm-up popularity, M in {1, 4, 8} (--tokens), residual chaining: tok/s.
   prefill   one E=512 layer, M=512 tokens, grouped GEMM on MFMA: GB/s, TFLOP/s.
+  slots8dev the slots8 workload with the cache policy and the copies on the GPU, one graph.
+  hybrid    8 static GPU slots, cold routes computed on the host cores.
+  staged    the prefill layer with every expert in host memory, 48 staging slots.
+  fate      next-layer prefetch predicted from the current layer's input: recall, hit rate.
+  formats   the decode workload with bf16, block FP8 or NVFP4 experts (--format).
 """
 from __future__ import annotations
 
@@ -49,7 +54,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=32)
     p.add_argument("--workload", default="decode",
                    choices=["decode", "slots8", "slots8dev", "hybrid", "stack48", "prefill", "staged",
-                            "fate"])
+                            "fate", "formats"])
+    p.add_argument("--format", default="nvfp4", choices=["bf16", "fp8_block", "nvfp4"],
+                   help="formats: the experts' format")
     p.add_argument("--tokens", type=int, default=1, help="stack48: tokens per step (1, 4 or 8)")
     p.add_argument("--copies", type=int, default=16, help="distinct copies of the expert bank")
     p.add_argument("--stage-steps", type=int, default=256, help="marked steps for stage timing")
@@ -1014,6 +1021,133 @@ def bench_fate(args):
 
 
 
+# ---------------------------------------------------------------------------------------------
+# formats: the decode workload with bf16, block FP8 or NVFP4 experts (the generic path)
+# ---------------------------------------------------------------------------------------------
+def _format_bytes(fmt, n, k):
+    """Algorithmic bytes of one [n, k] matrix of the format: elements + scales."""
+    el = {"bf16": 2 * n * k, "fp8_block": n * k, "nvfp4": n * k // 2}[fmt]
+    sc = {"bf16": 0, "fp8_block": 4 * ((n + 127) // 128) * ((k + 127) // 128),
+          "nvfp4": 4 + n * (k // 16)}[fmt]
+    return el + sc
+
+
+def bench_formats(args):
+    torch, B = setup()
+    import synthetic
+    from expert_offloaded_routed_amd import layer as L
+
+    wl = synthetic.WORKLOADS["gptoss20b_decode"]
+    H, I, E, k = wl.hidden, wl.inter, wl.n_experts, wl.top_k
+    fmt = args.format
+    shape = B.make_shape(H, I, E, k, E, fmt)
+    t0 = time.time()
+    experts = synthetic.experts_canonical(wl, 0, range(E), fmt=fmt)
+    bank = L.pack_bank(shape, experts)
+    img = bank.shape[1]
+    log(f"{fmt}: generated + packed {E} experts ({bank.nbytes / 1e6:.1f} MB) in {time.time() - t0:.1f}s")
+    # copies of the bank at distinct addresses, at least 2 GB of them in all (no step finds its
+    # experts in the Infinity Cache)
+    R = max(2, min(args.copies, -(-2_000_000_000 // bank.nbytes)))
+    bank_d = torch.from_numpy(bank).cuda()
+    copies = torch.empty((R, E, img), dtype=torch.uint8, device="cuda")
+    for r in range(R):
+        copies[r].copy_(bank_d)
+    del bank_d
+    wr = dev_bits(torch, synthetic.router_weights(wl))
+    bias = torch.from_numpy(synthetic.zipf_bias(wl)).cuda()
+    n_x = args.warmup + args.steps
+    xs = dev_bits(torch, np.concatenate([synthetic.activations(wl, 1, t) for t in range(n_x)]))
+    ws = torch.zeros(B.moe_workspace_size(shape, 1), dtype=torch.uint8, device="cuda")
+    ids = torch.zeros((n_x, k), dtype=torch.int32, device="cuda")
+    w = torch.zeros((n_x, k), dtype=torch.float32, device="cuda")
+    y = torch.zeros((n_x, H), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+
+    def step(t):
+        B.moe_layer_forward(shape, xs[t], 1, wr, bias, None, copies[t % R], ids[t], w[t], y[t], None,
+                            None, ws, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for t in range(args.warmup):
+            step(t)
+    torch.cuda.synchronize()
+    g_timed = capture(torch, stream, lambda i: step(args.warmup + i), args.steps)
+    torch.cuda.synchronize()
+    ms_total = time_graph(torch, B, stream, g_timed)
+    ms_step = ms_total / args.steps
+    ids_h = ids[args.warmup:].cpu().numpy()
+    srt = np.sort(ids_h, axis=1)
+    assert np.all(srt[:, 1:] != srt[:, :-1])
+    assert np.isfinite(y[args.warmup:].cpu().numpy()).all()
+    gu_bytes = k * 2 * _format_bytes(fmt, I, H)
+    dn_bytes = k * _format_bytes(fmt, H, I)
+    step_bytes = gu_bytes + dn_bytes
+
+    # stage timing with the marked calls, back to back behind a spin kernel (as for decode)
+    n_st = max(1, min(args.stage_steps, args.steps))
+    marks = [[B.event_create(timing=True, system_fence=False) for _ in range(4)] for _ in range(n_st)]
+    for rep in range(2):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(args.enqueue_spin_cycles))
+            for i in range(n_st):
+                t = args.warmup + i
+                B.moe_layer_forward_marked(shape, xs[t], 1, wr, bias, None, copies[t % R], ids[t], w[t],
+                                           y[t], None, None, ws, marks[i], stream=stream)
+    torch.cuda.synchronize()
+    st = np.array([[B.event_elapsed_ms(m[j], m[j + 1]) for j in range(3)] for m in marks]) * 1e3
+    for m in marks:
+        for e in m:
+            B.event_destroy(e)
+    us_rt, us_gu, us_dn = (float(v) for v in st.mean(axis=0))
+    gu_gbs = gu_bytes / (us_gu * 1e-6) / 1e9
+    dn_gbs = dn_bytes / (us_dn * 1e-6) / 1e9
+    ceil_gbs, ceil_us = stream_ceiling(torch, B, copies.view(-1), gu_bytes, stream)
+    log(f"{fmt}: read-streaming ceiling {ceil_gbs:.0f} GB/s ({ceil_us:.2f} us per {gu_bytes} B)")
+
+    cpu = None
+    if args.cpu_steps > 0:
+        from oracle import layer as O
+        wr_h = synthetic.router_weights(wl)
+        bias_h = synthetic.zipf_bias(wl)
+        def work(t):
+            x = synthetic.activations(wl, 1, t)
+            oid, ow, _, _ = O.route(O.router_logits(x, wr_h, bias_h), k)
+            O.layer_forward(x, oid, ow, experts)
+        n_cpu = max(1, args.cpu_steps // 4)
+        cpu = cpu_baseline(work, n_cpu, max(1, n_cpu // 4), 1.0, "tok/s",
+                           f"decode steps (M=1) of the same layer: float64 router, top-k and "
+                           f"dequantise-then-matmul of the 4 routed {fmt} experts")
+
+    out = {
+        "metric": f"MoE-layer decode tok/s at M=1, {fmt} experts (generic path) + achieved HBM GB/s",
+        "value": round(args.steps / (ms_total / 1e3), 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": f"synthetic (seeded N(0,0.02) weights -> {fmt}, N(0,1) bf16 activations, Zipf(1.1) prior)",
+        "config": {"workload": f"gptoss20b_decode_{fmt}", "hidden": H, "inter": I, "n_experts": E,
+                   "top_k": k, "M": 1, "format": fmt, "resident": "all", "bank_copies": R,
+                   "timed": "one HIP graph of the steps"},
+        "expert_bytes_per_step": step_bytes,
+        "hbm_gbs_step": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "stage_us": {"route (router GEMV + top-k / bucketing)": round(us_rt, 2),
+                     "gateup (generic gate/up + SiLU*up)": round(us_gu, 2),
+                     "down (generic down + ordered combine)": round(us_dn, 2)},
+        "down_gbs": round(dn_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": f"k_gateup_fmt<{fmt}> (gate/up GEMV + SiLU*up)",
+                     "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gu_bytes, "us_per_launch": round(us_gu, 3),
+                     "launches_timed": n_st, "measured_ceiling_gbs": round(ceil_gbs, 1),
+                     "frac_of_measured_ceiling": round(gu_gbs / ceil_gbs, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of known size (4 times): its HBM byte counters per launch
     give the scale between what the counters read and the bytes moved."""
@@ -1035,7 +1169,7 @@ def main():
         return 2
     rc = {"decode": bench_decode, "slots8": bench_slots8, "slots8dev": bench_slots8dev,
           "hybrid": bench_hybrid, "stack48": bench_stack48, "prefill": bench_prefill,
-          "staged": bench_staged, "fate": bench_fate}[args.workload](args)
+          "staged": bench_staged, "fate": bench_fate, "formats": bench_formats}[args.workload](args)
     if args.calibrate_copy_mb > 0:
         copy_calibration(args.calibrate_copy_mb)
     return rc

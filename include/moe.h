@@ -203,9 +203,9 @@ moe_status moe_experts_forward(const moe_shape* shape, const uint16_t* x, int32_
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------
- * Whole layer in one call: moe_route followed by moe_experts_forward.  For M*k <= 256 the
- * top-k, slot resolve and bucketing run inside the expert kernels (three launches: router
- * GEMV, gate/up, down + combine).  For one token (M = 1, top_k <= 16) of the MXFP4 shapes the
+ * Whole layer in one call: moe_route followed by moe_experts_forward.  For one token, or up to
+ * 64 routes over at most 64 experts, the top-k, slot resolve and bucketing run inside the expert
+ * kernels (three launches: router GEMV, gate/up, down + combine).  For one token (M = 1, top_k <= 16) of the MXFP4 shapes the
  * fused kernel is built for (moe_layer_launches reports it; GPT-OSS-20B's is one) gate/up and
  * down are one launch of one workgroup per compute unit, h handed from gate/up to down by value
  * through the workspace in words tagged with the call; for routers of at most 32 experts and
@@ -258,9 +258,9 @@ moe_status moe_layer_forward_noalloc(const moe_shape* shape, const uint16_t* x, 
                                      hipStream_t stream);
 
 /* Number of kernel launches moe_layer_forward makes for M tokens of this shape: 1 or 2 when
- * gate/up and down run as one launch (router inside it, or before it), 3 for small calls, 4 past
- * 256 routes and for the formats other than MXFP4, 5 on the grouped-GEMM path (M >= 64), 1 for
- * M = 0.  For callers that budget graph nodes or time stages.  Writes *n; no
+ * gate/up and down run as one launch (router inside it, or before it), 3 for one token or up to
+ * 64 routes over at most 64 experts, 4 for the other calls below 64 tokens and for the formats
+ * other than MXFP4, 5 on the grouped-GEMM path (M >= 64), 1 for M = 0.  For callers that budget graph nodes or time stages.  Writes *n; no
  * device work. */
 moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n);
 
