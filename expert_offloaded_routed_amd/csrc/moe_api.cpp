@@ -156,8 +156,16 @@ enum class RouteSrc {
   kIds,     // caller's ids / w
 };
 
-// The expert stages of a call whose experts are not MXFP4: the top-k / bucketing kernel writes the
-// route table, then the generic gate/up and down kernels of the format.
+// Calls whose route table the one-workgroup kernel builds faster than the top-k / bucketing
+// kernel: one token (a single top-k), or at most kRouteTableMaxRoutes routes over at most 64
+// experts (its table build is quadratic in the routes and its top-k one wave per token).
+static bool route_table_fits(int M, int k, int E) {
+  return (size_t)M * k <= (size_t)kRouteTableMaxRoutes && (M == 1 || E <= 64);
+}
+
+// The expert stages of a call whose experts are not MXFP4: the route-table kernel (small calls)
+// or the top-k / bucketing kernel writes the route table, then the generic gate/up and down
+// kernels of the format run.
 static moe_status run_experts_fmt(const moe_shape* sh, const uint16_t* x, int M,
                                   const float* logits, int32_t* ids, float* w, const int32_t* e2s,
                                   const uint8_t* slots, float* y, int32_t* cold_count,
@@ -169,9 +177,15 @@ static moe_status run_experts_fmt(const moe_shape* sh, const uint16_t* x, int M,
   const RouteWs rw = route_ws(ws, W);
   hipError_t e;
   if (do_gateup) {
-    const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, cold_routes);
-    e = launch_topk_bucket(logits, M, k, ids, w, true, ids, E, sh->n_slots, e2s, o, stream);
-    if (e != hipSuccess) return hip_fail(e, "top-k / bucket launch");
+    if (route_table_fits(M, k, E)) {
+      const RouteArgs rt = route_args(sh, M, logits, ids, w, e2s, logits ? ids : nullptr,
+                                      logits ? w : nullptr, cold_count, cold_routes);
+      e = launch_route_table(rt, rw, stream);
+    } else {
+      const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, cold_routes);
+      e = launch_topk_bucket(logits, M, k, ids, w, true, ids, E, sh->n_slots, e2s, o, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "route table launch");
   }
   if (marks && (e = record_mark(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   const RouteArgs ra = route_args(sh, M, nullptr, ids, w, e2s, nullptr, nullptr, nullptr, nullptr);
@@ -211,10 +225,18 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
   if (src != RouteSrc::kLogits) logits = nullptr;
   hipError_t e;
   if (!p.prologue && do_gateup) {
-    const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, cold_routes);
-    e = launch_topk_bucket(logits, M, sh->top_k, ids, w, true, ids, sh->n_experts, sh->n_slots,
-                           e2s, o, stream);
-    if (e != hipSuccess) return hip_fail(e, "top-k / bucket launch");
+    // one token, or a few routes over few experts: the one-workgroup route table; otherwise
+    // (and on the grouped path, which also needs the work list) the top-k / bucketing kernel
+    if (!p.grouped && route_table_fits(M, sh->top_k, sh->n_experts)) {
+      const RouteArgs rt = route_args(sh, M, logits, ids, w, e2s, logits ? ids : nullptr,
+                                      logits ? w : nullptr, cold_count, cold_routes);
+      e = launch_route_table(rt, rw, stream);
+    } else {
+      const BucketOut o = bucket_out(ws, W, nullptr, nullptr, nullptr, cold_count, cold_routes);
+      e = launch_topk_bucket(logits, M, sh->top_k, ids, w, true, ids, sh->n_experts, sh->n_slots,
+                             e2s, o, stream);
+    }
+    if (e != hipSuccess) return hip_fail(e, "route table launch");
     logits = nullptr;  // ids / w are final from here on
   }
   if (marks && (e = record_mark(marks[1], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -12,12 +12,14 @@
 //   NVFP4      E2M1 elements (element 2c in the low nibble of byte c), one E4M3 scale per 16
 //              elements of a row times one fp32 scale of the matrix (a chunk spans two scales).
 //
+// A lane requests U chunks of its row (chunk_unroll) before it uses any of them.
 // k_gateup_fmt: one wave per row index i of one hot expert: gate row i and up row i against
 // every route of the expert, kFmtTok routes per pass; h = bf16(silu(g) * u) per route.
 // k_down_fmt: one wave per output row r over every hot expert and its routes; each route's sum is
 // kept in the workspace by the lane that later combines that route's token (lane m % 64 of the
 // wave: it reads back only what it wrote itself), then y[m][r] = sum over ascending j of the hot
-// routes of w[m][j] * d, plus the residual.  Both read the route table of the bucketing kernel.
+// routes of w[m][j] * d, plus the residual.  Both read the route table that the route-table or
+// the bucketing kernel wrote.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,22 +57,36 @@ __device__ __forceinline__ size_t elem_off(int r, int k, int K) {
   return FMT == MOE_FORMAT_BF16 ? 2 * i : FMT == MOE_FORMAT_FP8_BLOCK ? i : i / 2;
 }
 
+// The matrix scale of an NVFP4 scale section (1 for the other formats).
+template <int FMT>
+__device__ __forceinline__ float matrix_scale(const uint8_t* __restrict__ sc) {
+  if constexpr (FMT == MOE_FORMAT_NVFP4) return *reinterpret_cast<const float*>(sc);
+  return 1.0f;
+}
+
 // Scales of the chunk at element k of row r of a matrix [.][K] whose scale section is sc:
-// s0 for its (first) 16 elements, s1 for the next 16 (NVFP4 only).
+// s0 for its (first) 16 elements, s1 for the next 16 (NVFP4 only: the two E4M3 bytes, one
+// 16-bit load, each times the matrix scale g).
 template <int FMT>
 __device__ __forceinline__ void chunk_scales(const uint8_t* __restrict__ sc, int r, int k, int K,
-                                             float& s0, float& s1) {
+                                             float g, float& s0, float& s1) {
   if constexpr (FMT == MOE_FORMAT_FP8_BLOCK) {
     s0 = reinterpret_cast<const float*>(sc)[(size_t)(r / 128) * ((K + 127) / 128) + k / 128];
     s1 = 0.0f;
   } else if constexpr (FMT == MOE_FORMAT_NVFP4) {
-    const float g = *reinterpret_cast<const float*>(sc);
-    const uint8_t* b = sc + 4 + (size_t)r * (K / 16) + k / 16;
-    s0 = e4m3_to_f32(b[0]) * g;
-    s1 = e4m3_to_f32(b[1]) * g;
+    // 4 + r * (K / 16) + k / 16 is even: K / 16 and k / 16 are
+    const uint32_t b = *reinterpret_cast<const uint16_t*>(sc + 4 + (size_t)r * (K / 16) + k / 16);
+    s0 = e4m3_to_f32(b & 0xFFu) * g;
+    s1 = e4m3_to_f32(b >> 8) * g;
   } else {
     s0 = s1 = 1.0f;
   }
+}
+
+// Chunks a lane has in flight per matrix (requested together before any is used).
+template <int FMT>
+__host__ __device__ constexpr int chunk_unroll() {
+  return FMT == MOE_FORMAT_NVFP4 ? 2 : 4;
 }
 
 // acc + the dot of the 8 E2M1 values of word w (byte p: elements 2p, 2p + 1) with 4 bf16 pairs.
@@ -142,7 +158,9 @@ __global__ __launch_bounds__(kFmtWaves * 64) void k_gateup_fmt(
   if (cnt <= 0 || off < 0 || off + cnt > Mk || slot < 0 || slot >= ra.S) return;
   const uint8_t* img = slots + (size_t)slot * image_bytes;
   constexpr int EPC = chunk_elems<FMT>();
+  constexpr int U = chunk_unroll<FMT>();
   const int nch = H / EPC;
+  const float gs = matrix_scale<FMT>(img + F.gate_s), us = matrix_scale<FMT>(img + F.up_s);
   for (int base = 0; base < cnt; base += kFmtTok) {
     const int nt = min(kFmtTok, cnt - base);
     int route[kFmtTok];
@@ -155,18 +173,28 @@ __global__ __launch_bounds__(kFmtWaves * 64) void k_gateup_fmt(
     float ag[kFmtTok], au[kFmtTok];
 #pragma unroll
     for (int t = 0; t < kFmtTok; ++t) ag[t] = au[t] = 0.0f;
-    for (int c = lane; c < nch; c += 64) {
-      const int k = c * EPC;
-      const uint4 cg = *reinterpret_cast<const uint4*>(img + F.gate + elem_off<FMT>(i, k, H));
-      const uint4 cu = *reinterpret_cast<const uint4*>(img + F.up + elem_off<FMT>(i, k, H));
-      float g0, g1, u0, u1;
-      chunk_scales<FMT>(img + F.gate_s, i, k, H, g0, g1);
-      chunk_scales<FMT>(img + F.up_s, i, k, H, u0, u1);
+    for (int c0 = lane; c0 < nch; c0 += 64 * U) {
+      uint4 cg[U], cu[U];
+      float g0[U], g1[U], u0[U], u1[U];
+      int kk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {  // (past the row: the last chunk again, unused)
+        kk[u] = min(c0 + 64 * u, nch - 1) * EPC;
+        cg[u] = *reinterpret_cast<const uint4*>(img + F.gate + elem_off<FMT>(i, kk[u], H));
+        cu[u] = *reinterpret_cast<const uint4*>(img + F.up + elem_off<FMT>(i, kk[u], H));
+        chunk_scales<FMT>(img + F.gate_s, i, kk[u], H, gs, g0[u], g1[u]);
+        chunk_scales<FMT>(img + F.up_s, i, kk[u], H, us, u0[u], u1[u]);
+      }
 #pragma unroll
       for (int t = 0; t < kFmtTok; ++t) {
         if (t < nt) {
-          ag[t] += chunk_dot<FMT>(cg, x + xo[t] + k, g0, g1);
-          au[t] += chunk_dot<FMT>(cu, x + xo[t] + k, u0, u1);
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (c0 + 64 * u < nch) {
+              ag[t] += chunk_dot<FMT>(cg[u], x + xo[t] + kk[u], g0[u], g1[u]);
+              au[t] += chunk_dot<FMT>(cu[u], x + xo[t] + kk[u], u0[u], u1[u]);
+            }
+          }
         }
       }
     }
@@ -193,6 +221,7 @@ __global__ __launch_bounds__(kFmtWaves * 64) void k_down_fmt(
   const int Mk = ra.M * ra.k;
   const int nd = rw.meta[0];
   constexpr int EPC = chunk_elems<FMT>();
+  constexpr int U = chunk_unroll<FMT>();
   const int nch = I / EPC;
   for (int d = 0; d < nd; ++d) {
     const int4 dd = rw.dist[d];
@@ -207,14 +236,26 @@ __global__ __launch_bounds__(kFmtWaves * 64) void k_down_fmt(
       float acc[kFmtTok];
 #pragma unroll
       for (int t = 0; t < kFmtTok; ++t) acc[t] = 0.0f;
-      for (int c = lane; c < nch; c += 64) {
-        const int k = c * EPC;
-        const uint4 cd = *reinterpret_cast<const uint4*>(img + F.down + elem_off<FMT>(r, k, I));
-        float s0, s1;
-        chunk_scales<FMT>(img + F.down_s, r, k, I, s0, s1);
+      const float ds = matrix_scale<FMT>(img + F.down_s);
+      for (int c0 = lane; c0 < nch; c0 += 64 * U) {
+        uint4 cd[U];
+        float s0[U], s1[U];
+        int kk[U];
 #pragma unroll
-        for (int t = 0; t < kFmtTok; ++t)
-          if (t < nt) acc[t] += chunk_dot<FMT>(cd, hbuf + (size_t)route[t] * I + k, s0, s1);
+        for (int u = 0; u < U; ++u) {  // (past the row: the last chunk again, unused)
+          kk[u] = min(c0 + 64 * u, nch - 1) * EPC;
+          cd[u] = *reinterpret_cast<const uint4*>(img + F.down + elem_off<FMT>(r, kk[u], I));
+          chunk_scales<FMT>(img + F.down_s, r, kk[u], I, ds, s0[u], s1[u]);
+        }
+#pragma unroll
+        for (int t = 0; t < kFmtTok; ++t) {
+          if (t < nt) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              if (c0 + 64 * u < nch)
+                acc[t] += chunk_dot<FMT>(cd[u], hbuf + (size_t)route[t] * I + kk[u], s0[u], s1[u]);
+          }
+        }
       }
 #pragma unroll
       for (int t = 0; t < kFmtTok; ++t) {

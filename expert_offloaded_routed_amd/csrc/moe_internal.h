@@ -298,6 +298,12 @@ hipError_t launch_layer_decode(const uint16_t* x, const uint16_t* wr, const floa
                                int H, int I, const uint8_t* slots, const ImageLayout& L,
                                const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
                                uint64_t* hf, float* y, Residual res, hipStream_t s);
+// The route table of a call of at most kRouteTableMaxRoutes routes (M >= 1) in one workgroup:
+// top-k from ra.logits (or ra.ids_in / ra.w_in), then the table in the workspace, the top-k
+// results (ra.topk_ids / topk_w, when the logits are given) and the cold report (ra.cold_count /
+// cold_routes), all optional outputs.
+constexpr int kRouteTableMaxRoutes = 256;
+hipError_t launch_route_table(const RouteArgs& ra, const RouteWs& rw, hipStream_t s);
 // logits: router_parts(M, E) partial rows per token (see kRouterParts).
 hipError_t launch_topk_bucket(const float* logits, int M, int k, int32_t* topk_ids, float* topk_w,
                               bool do_bucket, const int32_t* ids, int E, int S,

@@ -2257,6 +2257,24 @@ __global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs 
 }
 
 // =============================================================================================
+// The route table of a call in one workgroup: top-k from the logits (or the given ids), slot
+// resolve and buckets in LDS, then the table, the top-k results and the cold report written
+// out, as the writer workgroup of a gate/up launch with the prologue does.  It does the
+// bucketing kernel's work for calls of at most kProMaxRoutes routes in fewer dependent steps.
+// =============================================================================================
+static_assert(kProMaxRoutes == kRouteTableMaxRoutes, "route table bound");
+__global__ __launch_bounds__(512) void k_route_table(RouteArgs ra, RouteWs rw) {
+  __shared__ RouteLds rt;
+  route_prologue(rt, ra, rw, true);
+}
+
+hipError_t launch_route_table(const RouteArgs& ra, const RouteWs& rw, hipStream_t s) {
+  if (ra.M < 1 || ra.M * ra.k > kProMaxRoutes) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_route_table, dim3(1), dim3(512), 0, s, ra, rw);
+  return hipGetLastError();
+}
+
+// =============================================================================================
 // The workspace's error word, taken by the caller: copied out, then cleared (in stream order)
 // =============================================================================================
 __global__ __launch_bounds__(64) void k_take_errors(int32_t* __restrict__ word,
