@@ -301,13 +301,18 @@ def bench_decode(args):
         wr_h = synthetic.router_weights(wl)
         bias_h = synthetic.zipf_bias(wl)
 
+        near = set()
+
         def work(t):
             x = synthetic.activations(wl, 1, t)
-            oid, ow, _, _ = O.route(O.router_logits(x, wr_h, bias_h), k)
+            oid, ow, gap, _ = O.route(O.router_logits(x, wr_h, bias_h), k)
+            if gap[0] < 1e-6:  # a near-tie: any valid top-k set is accepted for this token
+                near.add(t)
             O.layer_forward(x, oid, ow, experts)
         cpu = cpu_baseline(work, args.cpu_steps, max(1, args.cpu_steps // 8), 1.0, "tok/s",
                            "decode steps (M=1) of the same layer: float64 router, top-k and "
                            "dequantise-then-matmul of the 4 routed experts")
+        cpu["near_tie_tokens"] = len(near)
 
     gbs_step = step_bytes / (ms_step * 1e-3) / 1e9
     out = {

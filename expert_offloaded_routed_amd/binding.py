@@ -114,6 +114,9 @@ _SIGS = {
                          C.POINTER(_P)],
     "moe_cache_policy_step": [_P, C.c_int64, _P, _I32, _P, C.POINTER(_I32), _P,
                               C.POINTER(moe_cache_stats)],
+    "moe_cache_state_bytes": [_P, C.POINTER(_SZ)],
+    "moe_cache_save": [_P, _P, _SZ],
+    "moe_cache_restore": [_P, _P, _SZ],
 }
 
 _lib = None
@@ -491,6 +494,23 @@ class MoeCache:
         plan = [(p.expert, p.slot, p.evicted, p.visible_step) for p in self._plan[: n.value]]
         stats = {f: getattr(st, f) for f, _ in moe_cache_stats._fields_}
         return self._map.copy(), plan, stats
+
+    def moe_cache_save(self) -> np.ndarray:
+        """The cache's whole state as bytes (moe_cache_save)."""
+        n = _SZ(0)
+        _check(load().moe_cache_state_bytes(self._h, C.byref(n)), "moe_cache_state_bytes")
+        buf = np.zeros(n.value, dtype=np.uint8)
+        _check(load().moe_cache_save(self._h, _ptr(buf), buf.nbytes), "moe_cache_save")
+        return buf
+
+    def moe_cache_restore(self, state: np.ndarray):
+        """Loads a saved state (moe_cache_restore); the saved configuration comes with it."""
+        buf = np.ascontiguousarray(state, dtype=np.uint8)
+        _check(load().moe_cache_restore(self._h, _ptr(buf), buf.nbytes), "moe_cache_restore")
+        # the plan buffer holds the restored configuration's refills per step (the header's
+        # configuration follows magic, version, E, S, k)
+        cfg = moe_cache_config.from_buffer_copy(buf[20:20 + C.sizeof(moe_cache_config)].tobytes())
+        self._plan = (moe_refill * max(1, cfg.max_refills_per_step))()
 
     def close(self):
         if self._h:

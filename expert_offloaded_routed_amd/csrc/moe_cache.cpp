@@ -121,6 +121,133 @@ moe_status moe_cache_create(const moe_shape* shape, const moe_cache_config* conf
 
 void moe_cache_destroy(moe_cache* cache) { delete cache; }
 
+}  // extern "C"
+
+// Saved state: a fixed header, then the arrays, then max_pending refill records (the first
+// n_pending in planning order, the rest zero).  Little-endian plain data, no pointers.
+namespace {
+constexpr uint32_t kStateMagic = 0x43454F4Du;  // "MOEC"
+constexpr uint32_t kStateVersion = 1;
+struct StateHdr {
+  uint32_t magic, version;
+  int32_t E, S, K;
+  moe_cache_config cfg;
+  int32_t stepped, n_pending;
+  int64_t last_step;
+  moe_cache_stats stats;
+};
+struct StatePending {
+  int32_t expert, slot;
+  int64_t visible;
+};
+size_t state_bytes(int E, int S, int Q) {
+  return sizeof(StateHdr) + 4 * (size_t)(S + E) + 8 * (size_t)(S + E) + sizeof(StatePending) * (size_t)Q;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_cache_state_bytes(const moe_cache* c, size_t* bytes) {
+  if (!c || !bytes) return fail(MOE_ERR_INVALID_ARG, "moe_cache_state_bytes: NULL argument");
+  *bytes = state_bytes(c->E, c->S, c->cfg.max_pending);
+  return ok();
+}
+
+moe_status moe_cache_save(const moe_cache* c, void* buf, size_t bytes) {
+  if (!c || !buf) return fail(MOE_ERR_INVALID_ARG, "moe_cache_save: NULL argument");
+  const size_t need = state_bytes(c->E, c->S, c->cfg.max_pending);
+  if (bytes < need) return fail(MOE_ERR_INVALID_ARG, "moe_cache_save: %zu bytes < %zu", bytes, need);
+  uint8_t* p = static_cast<uint8_t*>(buf);
+  memset(p, 0, need);
+  StateHdr h;
+  memset(&h, 0, sizeof(h));
+  h.magic = kStateMagic;
+  h.version = kStateVersion;
+  h.E = c->E;
+  h.S = c->S;
+  h.K = c->K;
+  h.cfg = c->cfg;
+  h.stepped = c->stepped ? 1 : 0;
+  h.n_pending = (int32_t)c->pending.size();
+  h.last_step = c->last_step;
+  h.stats = c->stats;
+  memcpy(p, &h, sizeof(h));
+  p += sizeof(h);
+  memcpy(p, c->slot_expert.data(), 4 * (size_t)c->S);
+  p += 4 * (size_t)c->S;
+  memcpy(p, c->expert_slot.data(), 4 * (size_t)c->E);
+  p += 4 * (size_t)c->E;
+  memcpy(p, c->last_use.data(), 8 * (size_t)c->S);
+  p += 8 * (size_t)c->S;
+  memcpy(p, c->freq.data(), 8 * (size_t)c->E);
+  p += 8 * (size_t)c->E;
+  for (const auto& q : c->pending) {
+    const StatePending r = {q.expert, q.slot, q.visible};
+    memcpy(p, &r, sizeof(r));
+    p += sizeof(r);
+  }
+  return ok();
+}
+
+moe_status moe_cache_restore(moe_cache* c, const void* buf, size_t bytes) {
+  if (!c || !buf) return fail(MOE_ERR_INVALID_ARG, "moe_cache_restore: NULL argument");
+  if (bytes < sizeof(StateHdr)) return fail(MOE_ERR_INVALID_ARG, "moe_cache_restore: %zu bytes hold no header", bytes);
+  const uint8_t* p = static_cast<const uint8_t*>(buf);
+  StateHdr h;
+  memcpy(&h, p, sizeof(h));
+  if (h.magic != kStateMagic || h.version != kStateVersion)
+    return fail(MOE_ERR_INVALID_ARG, "moe_cache_restore: not a saved cache state (magic %08x, version %u)",
+                h.magic, h.version);
+  if (h.E != c->E || h.S != c->S || h.K != c->K)
+    return fail(MOE_ERR_STATE, "moe_cache_restore: state of (E=%d S=%d k=%d) into a cache of (E=%d S=%d k=%d)",
+                h.E, h.S, h.K, c->E, c->S, c->K);
+  const moe_cache_config& g = h.cfg;
+  if ((g.policy != MOE_POLICY_LRU && g.policy != MOE_POLICY_LFRU) || g.max_refills_per_step < 0 ||
+      g.lag_steps < 1 || g.max_pending < 1 || g.decay_period < 0 || h.n_pending < 0 ||
+      h.n_pending > g.max_pending)
+    return fail(MOE_ERR_INVALID_ARG, "moe_cache_restore: configuration out of range");
+  const size_t need = state_bytes(h.E, h.S, g.max_pending);
+  if (bytes < need) return fail(MOE_ERR_INVALID_ARG, "moe_cache_restore: %zu bytes < %zu", bytes, need);
+  p += sizeof(h);
+  std::vector<int32_t> se(h.S), es(h.E);
+  std::vector<int64_t> lu(h.S), fq(h.E);
+  memcpy(se.data(), p, 4 * (size_t)h.S);
+  p += 4 * (size_t)h.S;
+  memcpy(es.data(), p, 4 * (size_t)h.E);
+  p += 4 * (size_t)h.E;
+  memcpy(lu.data(), p, 8 * (size_t)h.S);
+  p += 8 * (size_t)h.S;
+  memcpy(fq.data(), p, 8 * (size_t)h.E);
+  p += 8 * (size_t)h.E;
+  std::vector<moe_cache::Pending> pend(h.n_pending);
+  for (int i = 0; i < h.n_pending; ++i) {
+    StatePending r;
+    memcpy(&r, p + sizeof(r) * i, sizeof(r));
+    pend[i] = {r.expert, r.slot, r.visible};
+  }
+  // the maps must be inverse of each other, in range; pending refills target empty slots
+  for (int s = 0; s < h.S; ++s)
+    if (se[s] < -1 || se[s] >= h.E || (se[s] >= 0 && es[se[s]] != s))
+      return fail(MOE_ERR_INVALID_ARG, "moe_cache_restore: slot %d is inconsistent", s);
+  for (int e = 0; e < h.E; ++e)
+    if (es[e] < -1 || es[e] >= h.S || (es[e] >= 0 && se[es[e]] != e))
+      return fail(MOE_ERR_INVALID_ARG, "moe_cache_restore: expert %d is inconsistent", e);
+  for (const auto& q : pend)
+    if (q.expert < 0 || q.expert >= h.E || q.slot < 0 || q.slot >= h.S || se[q.slot] != -1 ||
+        es[q.expert] != -1)
+      return fail(MOE_ERR_INVALID_ARG, "moe_cache_restore: a pending refill is inconsistent");
+  c->cfg = g;
+  c->slot_expert.swap(se);
+  c->expert_slot.swap(es);
+  c->last_use.swap(lu);
+  c->freq.swap(fq);
+  c->pending.swap(pend);
+  c->stats = h.stats;
+  c->last_step = h.last_step;
+  c->stepped = h.stepped != 0;
+  return ok();
+}
+
 moe_status moe_cache_policy_step(moe_cache* c, int64_t step, const int32_t* topk_ids, int32_t M,
                                  moe_refill* plan, int32_t* n_plan, int32_t* expert_to_slot,
                                  moe_cache_stats* stats) {

@@ -461,6 +461,19 @@ moe_status moe_cache_policy_step(moe_cache* cache, int64_t step, const int32_t* 
                                  int32_t* expert_to_slot, moe_cache_stats* stats);
 void moe_cache_destroy(moe_cache* cache);
 
+/* Checkpoint and replay of a cache: moe_cache_save writes the whole state (configuration, step
+ * index, both maps, recency, LFRU frequencies, refills in flight, counters) as plain data into
+ * buf [host], moe_cache_state_bytes(cache) bytes; moe_cache_restore loads such a state into a
+ * cache created for the same (E, S, k), replacing its state and configuration, so that the
+ * steps that follow plan exactly what the saved cache would have planned.  A buffer that is not
+ * a saved state, or an inconsistent one, is rejected with MOE_ERR_INVALID_ARG and leaves the
+ * cache unchanged; a state of another shape gives MOE_ERR_STATE.  The device cache's state is
+ * plain device memory with no pointers: copying its state_bytes out and back is its
+ * checkpoint. */
+moe_status moe_cache_state_bytes(const moe_cache* cache, size_t* bytes);
+moe_status moe_cache_save(const moe_cache* cache, void* buf, size_t bytes);
+moe_status moe_cache_restore(moe_cache* cache, const void* buf, size_t bytes);
+
 /* ---------------------------------------------------------------------------------------
  * GPU-resident slot cache [MoE expert offload, "How it works", Decode: the per-layer LRU table
  * is kept on the GPU, a kernel looks routed experts up and assigns least-recently-used slots to

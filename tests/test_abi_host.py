@@ -272,3 +272,57 @@ def test_unknown_format_is_rejected():
         with pytest.raises(B.MoeError) as e:
             B.moe_expert_image_bytes(B.make_shape(256, 512, 8, 2, 8, f))
         assert e.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("policy", [LRU, LFRU])
+def test_host_cache_save_restore_replays_bit_exact(policy):
+    """A cache restored from a state saved at step t0 (into a fresh cache created with another
+    configuration) plans exactly what the original planned from t0 on, and matches the oracle;
+    broken or foreign states are refused and leave the cache as it was."""
+    _lib()
+    E, S, k = 32, 8, 4
+    orig, ref = _cache_pair(policy, E, S, k, 2, 3, 3)
+    rng = np.random.default_rng(17 + policy)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    steps = [np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(1 + t % 2)]).astype(np.int32)
+             for t in range(120)]
+    t0, saved, tail = 70, None, []
+    for t, ids in enumerate(steps):
+        if t == t0:
+            saved = orig.moe_cache_save()
+        out = orig.moe_cache_policy_step(t, ids)
+        m_ref, plan_ref = ref.step(t, ids)
+        assert np.array_equal(out[0], m_ref) and out[1] == plan_ref
+        if t >= t0:
+            tail.append(out)
+    fresh = B.MoeCache(B.make_shape(256, 512, E, k, S), policy=LRU, max_refills_per_step=1,
+                       lag_steps=1, max_pending=1)
+    fresh.moe_cache_restore(saved)
+    for t in range(t0, len(steps)):
+        m, plan, stats = fresh.moe_cache_policy_step(t, steps[t])
+        m0, plan0, stats0 = tail[t - t0]
+        assert np.array_equal(m, m0) and plan == plan0 and stats == stats0, t
+    # the state round-trips byte for byte
+    assert np.array_equal(fresh.moe_cache_save(), orig.moe_cache_save())
+    # refused: not a state, truncated, inconsistent, another shape; the cache stays as it was
+    before = fresh.moe_cache_save()
+    bad = saved.copy()
+    bad[0] ^= 0xFF
+    for b in (bad, saved[:40]):
+        with pytest.raises(B.MoeError) as e:
+            fresh.moe_cache_restore(b)
+        assert e.value.status == B.MOE_ERR_INVALID_ARG
+    bad = saved.copy()
+    hdr = 4 * 10 + 4 + 4 + 8 + 8 * 5  # header bytes: magic .. stats
+    bad[hdr:hdr + 4] = np.frombuffer(np.int32(E + 3).tobytes(), np.uint8)  # slot 0 -> expert E+3
+    with pytest.raises(B.MoeError) as e:
+        fresh.moe_cache_restore(bad)
+    assert e.value.status == B.MOE_ERR_INVALID_ARG
+    other = B.MoeCache(B.make_shape(256, 512, E, k, S + 1))
+    with pytest.raises(B.MoeError) as e:
+        other.moe_cache_restore(saved)
+    assert e.value.status == B.MOE_ERR_STATE
+    assert np.array_equal(fresh.moe_cache_save(), before)
+    for c in (orig, fresh, other):
+        c.close()

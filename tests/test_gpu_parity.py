@@ -1189,3 +1189,58 @@ def test_staged_prefill_matches_oracle(M, n_slots):
         else:
             assert torch.equal(b.y[:M], results[0])
     st.close()
+
+
+def test_device_cache_state_copy_is_a_checkpoint():
+    """The GPU-resident cache's state is plain device memory: a copy taken at step t0 and written
+    back replays steps t0.. with bit-identical maps, plans and counters, and matches the host
+    policy restored from its own checkpoint at t0."""
+    E, S, k = 32, 8, 4
+    shape = B.make_shape(256, 512, E, k, S)
+    init = np.arange(S, dtype=np.int32)
+    cfg = dict(policy=B.MOE_POLICY_LFRU, max_refills_per_step=2, lag_steps=2, max_pending=3,
+               decay_period=8)
+    dc = B.DeviceCache(shape, initial_slot_expert=init, **cfg)
+    host = B.MoeCache(shape, initial_slot_expert=init, **cfg)
+    rng = np.random.default_rng(31)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    T, t0 = 96, 50
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    obs = torch.from_numpy(ids).cuda()
+    maps = torch.zeros((T, E), dtype=torch.int32, device="cuda")
+    plans = torch.zeros((T, 2 * B.REFILL_RECORD_BYTES), dtype=torch.uint8, device="cuda")
+    nplan = torch.zeros(T, dtype=torch.int32, device="cuda")
+
+    def run(t_from):
+        for t in range(t_from, T):
+            dc.step(obs[t], k, maps[t], plans[t], nplan[t:t + 1])
+        torch.cuda.synchronize()
+        return maps[t_from:].cpu().numpy(), nplan[t_from:].cpu().numpy(), plans[t_from:].cpu().numpy()
+
+    say("device cache checkpoint: first run")
+    for t in range(t0):
+        dc.step(obs[t], k, maps[t], plans[t], nplan[t:t + 1])
+        host.moe_cache_policy_step(t, ids[t:t + 1])
+    torch.cuda.synchronize()
+    snap = dc.state.clone()
+    host_snap = host.moe_cache_save()
+    m1, n1, p1 = run(t0)
+    stats1 = dc.stats()
+    say("device cache checkpoint: replay from the copy")
+    dc.state.copy_(snap)
+    m2, n2, p2 = run(t0)
+    assert np.array_equal(m1, m2) and np.array_equal(n1, n2)
+    for i in range(T - t0):  # the planned records (unused record bytes are not written)
+        nb = int(n1[i]) * B.REFILL_RECORD_BYTES
+        assert np.array_equal(p1[i, :nb], p2[i, :nb]), i
+    assert dc.stats() == stats1
+    # the host policy restored at t0 plans the same maps
+    host2 = B.MoeCache(shape)
+    host2.moe_cache_restore(host_snap)
+    for t in range(t0, T):
+        m, plan, _ = host2.moe_cache_policy_step(t, ids[t:t + 1])
+        assert np.array_equal(m, m1[t - t0]), t
+        assert len(plan) == int(n1[t - t0]), t
+    host.close()
+    host2.close()
