@@ -215,6 +215,7 @@ struct ExpertPlan {
   bool prologue;     // every expert workgroup rebuilds the route table (M*k <= kProMaxRoutes)
   int gu_waves;      // waves per gate/up workgroup
   int gu_groups;     // most K groups (of 4 blocks) any gate/up wave holds
+  int gu_dgrid;      // gate/up grid.y: hot experts in flight at once (looped past it)
 };
 
 // Routes of a call as the expert kernels see them (kernel arguments, passed by value).

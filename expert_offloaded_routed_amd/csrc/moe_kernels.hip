@@ -971,10 +971,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
     cnt = dd.z;
     perm = rw.perm;
   }
-  if (cnt <= 0 || off < 0 || off + cnt > Mk) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = nthr >> 6;
+  // Without the prologue (at most 2 K groups a wave: the register budget of the loop) the grid
+  // holds gridDim.y hot experts at a time, sized so that the grid is resident at once, and
+  // workgroup (tile, d) takes experts d, d + gridDim.y, ...; otherwise gridDim.y = nd_max and
+  // each workgroup takes one.
+  constexpr bool LOOP = !PRO && !SINGLE && G <= 2;
+  for (int dcur = d;;) {
+  if (cnt > 0 && off >= 0 && off + cnt <= Mk) {
 
   const uint8_t* tbase = slots + (size_t)slot * image_bytes + (size_t)tile * gu_tile_bytes;
   const uint4* codes = reinterpret_cast<const uint4*>(tbase);
@@ -1034,6 +1040,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
     }
     __syncthreads();
   }
+
+  }  // (a valid table entry)
+  if (!LOOP) return;
+  dcur += gridDim.y;
+  if (dcur >= rw.meta[0]) return;  // (uniform)
+  const int4 dn = rw.dist[dcur];
+  slot = dn.x;
+  off = dn.y;
+  cnt = dn.z;
+  }  // experts of this workgroup
 }
 
 // ---- down projection on the matrix cores --------------------------------------------------------
@@ -2462,13 +2478,28 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
   }
   p.gu_waves = best < 1 ? 1 : best;
   p.gu_groups = (L.ng_h + p.gu_waves - 1) / p.gu_waves;
+  // Without the prologue (the table comes from the workspace) the gate/up workgroups loop over
+  // the hot experts, gu_dgrid at a time: as many as the compute units hold at once, so that the
+  // workgroups of experts that are not hot (nd_max bounds the distinct experts, the call usually
+  // has fewer) do not take a second round of the grid.
+  // The looping kernel holds at most 2 K groups a wave: as many waves as that takes.
+  p.gu_dgrid = p.nd_max;
+  if (!p.prologue && !p.grouped && (L.ng_h + 1) / 2 <= kMaxWaves) {
+    p.gu_waves = (L.ng_h + 1) / 2 > p.gu_waves ? (L.ng_h + 1) / 2 : p.gu_waves;
+    p.gu_groups = (L.ng_h + p.gu_waves - 1) / p.gu_waves;
+    const int per_cu = kWavesPerCU / p.gu_waves > 0 ? kWavesPerCU / p.gu_waves : 1;
+    const int fit = cus * per_cu / (L.gu_tiles > 0 ? L.gu_tiles : 1);
+    p.gu_dgrid = fit < 1 ? 1 : (fit < p.nd_max ? fit : p.nd_max);
+  }
   return p;
 }
 
 hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                          const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                          const RouteWs& rw, uint16_t* hbuf, hipStream_t s) {
-  const dim3 g(L.gu_tiles, p.nd_max), b(p.gu_waves * 64);
+  // (the looping variants, G = 2 without the prologue, take gu_dgrid experts at a time)
+  const dim3 g(L.gu_tiles, !p.prologue && p.gu_groups <= 2 ? p.gu_dgrid : p.nd_max),
+      b(p.gu_waves * 64);
   // the single-token variant lets arithmetic overlap the loads but holds more registers, so
   // it is only used with at most 3 groups per wave; M == 1 always fits the LDS copy of x
   const bool single = M == 1 && p.gu_groups <= 3;
