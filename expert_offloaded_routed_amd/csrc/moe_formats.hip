@@ -269,10 +269,21 @@ __global__ __launch_bounds__(kFmtWaves * 64) void k_down_fmt(
   // y for this row: lane m % 64 combines token m from the sums it stored itself
   for (int m = lane; m < ra.M; m += 64) {
     float acc = 0.0f;
-    for (int j = 0; j < ra.k; ++j) {
-      const int q = m * ra.k + j;
-      if (rw.route_slot[q] < 0) continue;
-      acc = fmaf(ra.w_in[q], pdn[(size_t)q * H + r], acc);
+    // 8 routes at a time: every load of a batch requested before the first is used (a cold
+    // route's word is read and left unused), then the sum in ascending j
+    for (int j0 = 0; j0 < ra.k; j0 += 8) {
+      bool hot[8];
+      float wv[8], pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = m * ra.k + min(j0 + u, ra.k - 1);
+        hot[u] = j0 + u < ra.k && rw.route_slot[q] >= 0;
+        wv[u] = ra.w_in[q];
+        pv[u] = pdn[(size_t)q * H + r];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (hot[u]) acc = fmaf(wv[u], pv[u], acc);
     }
     const size_t o = (size_t)m * H + r;
     y[o] = acc;

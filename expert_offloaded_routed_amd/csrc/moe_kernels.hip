@@ -1116,39 +1116,80 @@ __device__ __forceinline__ void dn_load_steps(const uint8_t* __restrict__ tb, si
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// h of step s0 of the route whose h row is hr, for this lane (the 64 bytes of its block).
+__device__ __forceinline__ void dn_h_first(const uint16_t* hr, int s0, int nb, int g, uint4 (&a)[4]) {
+  const uint4* hb = reinterpret_cast<const uint4*>(hr + 32 * min(4 * s0 + g, nb - 1));
+  a[0] = hb[0];
+  a[1] = hb[1];
+  a[2] = hb[2];
+  a[3] = hb[3];
+}
+
 // One route's partial sum for this lane over steps s0 .. s0+n-1 (n <= TM); hr = the route's h
-// (bf16 [I], in LDS or the workspace).  Software-pipelined by hand: the h block of step j+1 is
-// read before step j's arithmetic, its address passing through an empty asm together with the
-// sum so far, which keeps the compiler from issuing every read up front (16 VGPRs per step).
+// (bf16 [I], in LDS or the workspace), its first step already in `an`.  Software-pipelined by
+// hand: the h block of step j+1 is read before step j's arithmetic, its address passing through
+// an empty asm together with the sum so far, which keeps the compiler from issuing every read
+// up front (16 VGPRs per step); during the last step the next route's first step (h row hn) is
+// requested into `an`, so that consecutive routes of an expert do not each wait for their h.
 // Steps past n or ks, and blocks past nb, read a valid block and add nothing (a select, not a
 // product, so whatever that block holds cannot leak in).
 template <int TM>
-__device__ __forceinline__ float dn_route_dot(const uint4 (&c)[TM], const uint32_t (&sw)[TM / 4],
-                                              int s0, int n, int ks, int nb, int g,
-                                              const uint16_t* hr) {
+__device__ __forceinline__ float dn_route_dot_pf(const uint4 (&c)[TM], const uint32_t (&sw)[TM / 4],
+                                                 int s0, int n, int ks, int nb, int g,
+                                                 const uint16_t* hr, const uint16_t* hn,
+                                                 uint4 (&an)[4]) {
   float acc = 0.0f;
   int hoff = 0;
-  auto read_h = [&](int j, uint4 (&a)[4]) {
-    const uint4* hb = reinterpret_cast<const uint4*>(hr + hoff + 32 * min(4 * (s0 + j) + g, nb - 1));
+  auto read_h = [&](const uint16_t* row, int j, uint4 (&a)[4]) {
+    const uint4* hb = reinterpret_cast<const uint4*>(row + hoff + 32 * min(4 * (s0 + j) + g, nb - 1));
     a[0] = hb[0];
     a[1] = hb[1];
     a[2] = hb[2];
     a[3] = hb[3];
   };
-  uint4 an[4];
-  read_h(0, an);
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
     uint4 ac[4] = {an[0], an[1], an[2], an[3]};
-    if (j + 1 < TM) {
-      asm volatile("" : "+v"(acc), "+v"(hoff));
-      read_h(j + 1, an);
-    }
+    asm volatile("" : "+v"(acc), "+v"(hoff));
+    if (j + 1 < TM)
+      read_h(hr, j + 1, an);
+    else
+      read_h(hn, 0, an);
     const bool live = j < n && s0 + j < ks && 4 * (s0 + j) + g < nb;
     const float sc = e8m0_to_f32((sw[j >> 2] >> (8 * (j & 3))) & 0xFFu);
     const float v = fmaf(sc, block_dot(c[j], ac[0], ac[1], ac[2], ac[3]), acc);
     acc = live ? v : acc;
     __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
+// Every step of a route's h for this lane (TM x 64 bytes), requested together.
+template <int TM>
+__device__ __forceinline__ void dn_route_h(const uint16_t* hr, int s0, int nb, int g,
+                                           uint4 (&a)[TM][4]) {
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const uint4* hb = reinterpret_cast<const uint4*>(hr + 32 * min(4 * (s0 + j) + g, nb - 1));
+    a[j][0] = hb[0];
+    a[j][1] = hb[1];
+    a[j][2] = hb[2];
+    a[j][3] = hb[3];
+  }
+}
+
+// The route's partial sum from h already in registers (the arithmetic of dn_route_dot_pf).
+template <int TM>
+__device__ __forceinline__ float dn_route_dot_h(const uint4 (&c)[TM], const uint32_t (&sw)[TM / 4],
+                                                int s0, int n, int ks, int nb, int g,
+                                                const uint4 (&a)[TM][4]) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < TM; ++j) {
+    const bool live = j < n && s0 + j < ks && 4 * (s0 + j) + g < nb;
+    const float sc = e8m0_to_f32((sw[j >> 2] >> (8 * (j & 3))) & 0xFFu);
+    const float v = fmaf(sc, block_dot(c[j], a[j][0], a[j][1], a[j][2], a[j][3]), acc);
+    acc = live ? v : acc;
   }
   return acc;
 }
@@ -1209,7 +1250,76 @@ __global__ __launch_bounds__(512) void k_down_gemv(
   const uint16_t* hsrc = h_lds ? reinterpret_cast<const uint16_t*>(smem) : hbuf;
   float* parts = reinterpret_cast<float*>(smem + (h_lds ? (size_t)(n_h + 63) / 64 * 1024 : 0));
   __syncthreads();
-  for (int d = es0; d < nd; d += sl) {
+  bool fast = false;
+  if constexpr (TM <= 4) {
+    // A short K part and at most 64 hot experts for this wave: no route-table read on the way
+    // from one expert to the next.  Lane i holds the table entry of the wave's i-th expert (one
+    // read for all of them); the next expert's weights and route list are requested when an
+    // expert starts, and every step of the next route's h while a route is formed (the next
+    // expert's first route after an expert's last), 2 x TM x 16 VGPRs of h.
+    const int nde = es0 < nd ? (nd - es0 + sl - 1) / sl : 0;
+    if (nde <= 64) {
+      fast = true;
+      const int4 md = rw.dist[min(es0 + min(lane, max(nde - 1, 0)) * sl, nd_max - 1)];
+      auto entry = [&](int i, int& slot, int& off, int& cnt) {  // (i uniform)
+        slot = __builtin_amdgcn_readlane(md.x, i);
+        off = __builtin_amdgcn_readlane(md.y, i);
+        const int z = __builtin_amdgcn_readlane(md.z, i);
+        cnt = off >= 0 && z > 0 && off + z <= Mk ? z : 0;
+      };
+      auto routes_of = [&](int off, int cnt) {  // lane j: route j of the expert (j < 64)
+        return rw.perm[max(min(off + min(lane, max(cnt - 1, 0)), Mk - 1), 0)];
+      };
+      if (nde > 0) {
+        int slot_c, off, cnt;
+        entry(0, slot_c, off, cnt);
+        int myr = routes_of(off, cnt);
+        uint4 hc[TM][4], hn[TM][4];
+        dn_route_h<TM>(hsrc + (size_t)__builtin_amdgcn_readfirstlane(myr) * I, s0, nb, g, hc);
+#pragma unroll 1
+        for (int i = 0; i < nde; ++i) {
+          int slot_n, off_n, cnt_n;
+          entry(min(i + 1, nde - 1), slot_n, off_n, cnt_n);
+          dn_load_steps<TM>(sec + (size_t)slot_n * image_bytes, dn_code_bytes, s0, ks, full, rem,
+                            nsw, lane, cn, swn);
+          const int myr_n = routes_of(off_n, cnt_n);
+          const bool more = i + 1 < nde && cnt_n > 0;
+#pragma unroll 1
+          for (int j = 0; j < cnt; ++j) {
+#pragma unroll
+            for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(c[t].x), "+v"(c[t].y), "+v"(c[t].z), "+v"(c[t].w));
+            const int route = j < 64 ? __builtin_amdgcn_readlane(myr, j) : rw.perm[off + j];
+            int rnext = route;
+            if (j + 1 < cnt)
+              rnext = j + 1 < 64 ? __builtin_amdgcn_readlane(myr, j + 1) : rw.perm[off + j + 1];
+            else if (more)
+              rnext = __builtin_amdgcn_readfirstlane(myr_n);
+            __builtin_amdgcn_sched_barrier(0);
+            dn_route_h<TM>(hsrc + (size_t)rnext * I, s0, nb, g, hn);
+            __builtin_amdgcn_sched_barrier(0);
+            float acc = dn_route_dot_h<TM>(c, sw, s0, spw, ks, nb, g, hc);
+            acc = dn_row_sum(acc);
+            if (lane < kDnRows) parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+#pragma unroll
+            for (int t = 0; t < TM; ++t)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) hc[t][q] = hn[t][q];
+          }
+          // (an expert with no valid route left hc alone: the next one's first route now)
+          if (cnt == 0 && more)
+            dn_route_h<TM>(hsrc + (size_t)__builtin_amdgcn_readfirstlane(myr_n) * I, s0, nb, g, hc);
+#pragma unroll
+          for (int t = 0; t < TM; ++t) c[t] = cn[t];
+#pragma unroll
+          for (int q = 0; q < TM / 4; ++q) sw[q] = swn[q];
+          myr = myr_n;
+          off = off_n;
+          cnt = cnt_n;
+        }
+      }
+    }
+  }
+  for (int d = es0; !fast && d < nd; d += sl) {
     const int4 dd = rw.dist[d];
     if constexpr (PF) {
       // the last pass re-requests its own weights, unused
@@ -1222,15 +1332,51 @@ __global__ __launch_bounds__(512) void k_down_gemv(
     }
     const int off = dd.y;
     const int cnt = off >= 0 && dd.z > 0 && off + dd.z <= Mk ? dd.z : 0;
+    // the expert's routes, lane j holding route j0 + j (read together, not one per route), and
+    // each route's first step of h requested during the previous route's last step
+    for (int j0 = 0; j0 < cnt; j0 += 64) {
+      const int nj = min(64, cnt - j0);
+      const int myr = rw.perm[off + j0 + min(lane, nj - 1)];
+      int route = __builtin_amdgcn_readfirstlane(myr);
+      if constexpr (TM <= 4) {
+        // a short K part: every step of the next route's h is requested while the current route
+        // is formed (2 x TM x 16 VGPRs), so a route waits for at most one round trip
+        uint4 hc[TM][4], hn[TM][4];
+        dn_route_h<TM>(hsrc + (size_t)route * I, s0, nb, g, hc);
 #pragma unroll 1
-    for (int j = 0; j < cnt; ++j) {
-      // keeps the decode of the codes inside this loop (hoisted, it would hold 16 VGPRs per step)
+        for (int j = 0; j < nj; ++j) {
 #pragma unroll
-      for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(c[t].x), "+v"(c[t].y), "+v"(c[t].z), "+v"(c[t].w));
-      const int route = rw.perm[off + j];
-      float acc = dn_route_dot<TM>(c, sw, s0, spw, ks, nb, g, hsrc + (size_t)route * I);
-      acc = dn_row_sum(acc);
-      if (lane < kDnRows) parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+          for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(c[t].x), "+v"(c[t].y), "+v"(c[t].z), "+v"(c[t].w));
+          const int rnext = __builtin_amdgcn_readlane(myr, min(j + 1, nj - 1));
+          __builtin_amdgcn_sched_barrier(0);
+          dn_route_h<TM>(hsrc + (size_t)rnext * I, s0, nb, g, hn);
+          __builtin_amdgcn_sched_barrier(0);
+          float acc = dn_route_dot_h<TM>(c, sw, s0, spw, ks, nb, g, hc);
+          acc = dn_row_sum(acc);
+          if (lane < kDnRows) parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+#pragma unroll
+          for (int t = 0; t < TM; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hc[t][q] = hn[t][q];
+          route = rnext;
+        }
+      } else {
+        uint4 an[4];
+        dn_h_first(hsrc + (size_t)route * I, s0, nb, g, an);
+#pragma unroll 1
+        for (int j = 0; j < nj; ++j) {
+          // keeps the decode of the codes inside this loop (hoisted, it would hold 16 VGPRs per
+          // step)
+#pragma unroll
+          for (int t = 0; t < TM; ++t) asm volatile("" : "+v"(c[t].x), "+v"(c[t].y), "+v"(c[t].z), "+v"(c[t].w));
+          const int rnext = __builtin_amdgcn_readlane(myr, min(j + 1, nj - 1));
+          float acc = dn_route_dot_pf<TM>(c, sw, s0, spw, ks, nb, g, hsrc + (size_t)route * I,
+                                          hsrc + (size_t)rnext * I, an);
+          acc = dn_row_sum(acc);
+          if (lane < kDnRows) parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+          route = rnext;
+        }
+      }
     }
     if constexpr (PF) {
 #pragma unroll
@@ -1244,12 +1390,27 @@ __global__ __launch_bounds__(512) void k_down_gemv(
     const int m = idx / kDnRows;
     const int r = idx - m * kDnRows;
     float acc = 0.0f;
-    for (int j = 0; j < ra.k; ++j) {
-      const int route = m * ra.k + j;
-      if (rw.route_slot[route] < 0) continue;
-      float p = 0.0f;
-      for (int h = 0; h < kparts; ++h) p += parts[((size_t)route * kparts + h) * kDnRows + r];
-      acc = fmaf(ra.w_in[route], p, acc);
+    // 8 routes at a time: the slots and weights of a batch are requested together (one route
+    // at a time, each would wait for its own round trip), then the sum in ascending j
+    for (int j0 = 0; j0 < ra.k; j0 += 8) {
+      bool hot[8];
+      float wv[8], pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int route = m * ra.k + min(j0 + u, ra.k - 1);
+        hot[u] = j0 + u < ra.k && rw.route_slot[route] >= 0;
+        wv[u] = ra.w_in[route];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int route = m * ra.k + min(j0 + u, ra.k - 1);
+        float p = 0.0f;
+        for (int h = 0; h < kparts; ++h) p += parts[((size_t)route * kparts + h) * kDnRows + r];
+        pv[u] = p;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (hot[u]) acc = fmaf(wv[u], pv[u], acc);
     }
     y[(size_t)m * H + tile * kDnRows + r] = acc;
     residual_store(res, (size_t)m * H + tile * kDnRows + r, acc);
@@ -2250,15 +2411,28 @@ __global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs 
   const int m = q / per;
   const int h = (q - m * per) * 4;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  for (int j = 0; j < k; ++j) {
-    const int r = m * k + j;
-    if (rw.route_slot[r] < 0) continue;
-    const float wt = ra.w_in[r];
-    const float4 v = *reinterpret_cast<const float4*>(pdn + (size_t)r * H + h);
-    acc.x = fmaf(wt, v.x, acc.x);
-    acc.y = fmaf(wt, v.y, acc.y);
-    acc.z = fmaf(wt, v.z, acc.z);
-    acc.w = fmaf(wt, v.w, acc.w);
+  // 4 routes at a time, every load of a batch requested before the first is used (the rows of a
+  // cold route are read and left unused), then the sum in ascending j
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    bool hot[4];
+    float wt[4];
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = m * k + min(j0 + u, k - 1);
+      hot[u] = j0 + u < k && rw.route_slot[r] >= 0;
+      wt[u] = ra.w_in[r];
+      v[u] = *reinterpret_cast<const float4*>(pdn + (size_t)r * H + h);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (hot[u]) {
+        acc.x = fmaf(wt[u], v[u].x, acc.x);
+        acc.y = fmaf(wt[u], v[u].y, acc.y);
+        acc.z = fmaf(wt[u], v[u].z, acc.z);
+        acc.w = fmaf(wt[u], v[u].w, acc.w);
+      }
+    }
   }
   float* yo = y + (size_t)m * H + h;  // the caller's y need not be 16-byte aligned
   yo[0] = acc.x;
