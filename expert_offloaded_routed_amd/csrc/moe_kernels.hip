@@ -1197,6 +1197,32 @@ __device__ __forceinline__ float dn_route_dot_h(const uint4 (&c)[TM], const uint
 // Sum over the 4 lanes of a row (l, l^16, l^32, l^48); every one of them gets it.
 __device__ __forceinline__ float dn_row_sum(float v) { return pair_sum32(pair_sum16(v)); }
 
+// One 32-element block (16 code bytes) as 16 bf16 pairs, the block scale folded in (exact).
+__device__ __forceinline__ void block_to_bf16(const uint4 c, float sc, bf16x2_t (&w)[16]) {
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[4 * j + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 0);
+    w[4 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 1);
+    w[4 * j + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 2);
+    w[4 * j + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 3);
+  }
+}
+// ... and its dot with 32 bf16 activations, on two accumulation chains (even / odd pairs).
+__device__ __forceinline__ void block_dot_bf16(const bf16x2_t (&w)[16], const uint4 a0, const uint4 a1,
+                                               const uint4 a2, const uint4 a3, float& s0, float& s1) {
+  const uint32_t aw[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                           a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(aw[i]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(w[i + 1], as_bf16x2(aw[i + 1]), s1, false);
+  }
+}
+
+constexpr int kDnNR = 2;   // routes of an expert the down GEMV forms together (h in LDS)
+constexpr int kDnAll = 4;  // hot experts of a wave whose weights it requests all at once
+
 // Steps of a K part: K split over kparts, rounded up to whole scale words.
 __host__ __device__ __forceinline__ int dn_part_steps(int ks, int kparts) {
   return ((ks + kparts - 1) / kparts + 3) & ~3;
@@ -1255,8 +1281,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
     // A short K part and at most 64 hot experts for this wave: no route-table read on the way
     // from one expert to the next.  Lane i holds the table entry of the wave's i-th expert (one
     // read for all of them); the next expert's weights and route list are requested when an
-    // expert starts, and every step of the next route's h while a route is formed (the next
-    // expert's first route after an expert's last), 2 x TM x 16 VGPRs of h.
+    // expert starts.
     const int nde = es0 < nd ? (nd - es0 + sl - 1) / sl : 0;
     if (nde <= 64) {
       fast = true;
@@ -1270,7 +1295,98 @@ __global__ __launch_bounds__(512) void k_down_gemv(
       auto routes_of = [&](int off, int cnt) {  // lane j: route j of the expert (j < 64)
         return rw.perm[max(min(off + min(lane, max(cnt - 1, 0)), Mk - 1), 0)];
       };
-      if (nde > 0) {
+      if (nde > 0 && h_lds) {
+        // h in LDS: each expert's weights are decoded to bf16 once (the block scale folded in,
+        // exact; zero for blocks past K, which re-read a valid block) and serve every route of
+        // the expert, kDnNR routes at a time with their accumulation chains interleaved (one
+        // wave a SIMD has nothing else to hide a chain's latency behind).  With at most kDnAll
+        // experts the weights of all of them are requested at once, into registers of their
+        // own (a rotation of buffers would wait for each load at the move); otherwise the next
+        // expert's as an expert starts.
+        auto expert = [&](const uint4 (&cw)[TM], const uint32_t (&swq)[TM / 4], int off, int cnt,
+                          int myr) {
+          bf16x2_t wd[TM][16];
+#pragma unroll
+          for (int t = 0; t < TM; ++t) {
+            const bool live = t < spw && s0 + t < ks && 4 * (s0 + t) + g < nb;
+            const float f = e8m0_to_f32((swq[t >> 2] >> (8 * (t & 3))) & 0xFFu);
+            block_to_bf16(cw[t], __uint_as_float(__float_as_uint(f) & (live ? 0xFFFFFFFFu : 0u)), wd[t]);
+          }
+#pragma unroll 1
+          for (int j = 0; j < cnt; j += kDnNR) {
+            int rr[kDnNR];
+#pragma unroll
+            for (int u = 0; u < kDnNR; ++u) {
+              const int jj = min(j + u, cnt - 1);
+              rr[u] = jj < 64 ? __builtin_amdgcn_readlane(myr, jj) : rw.perm[off + jj];
+            }
+            float e0[kDnNR], e1[kDnNR];
+#pragma unroll
+            for (int u = 0; u < kDnNR; ++u) e0[u] = e1[u] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+#pragma unroll
+              for (int u = 0; u < kDnNR; ++u) {
+                const uint4* hb = reinterpret_cast<const uint4*>(
+                    hsrc + (size_t)rr[u] * I + 32 * min(4 * (s0 + t) + g, nb - 1));
+                block_dot_bf16(wd[t], hb[0], hb[1], hb[2], hb[3], e0[u], e1[u]);
+              }
+              __builtin_amdgcn_sched_barrier(0);  // one step's h at a time in registers
+            }
+#pragma unroll
+            for (int u = 0; u < kDnNR; ++u) {
+              const float acc = dn_row_sum(e0[u] + e1[u]);
+              if (j + u < cnt && lane < kDnRows)
+                parts[((size_t)rr[u] * kparts + kh) * kDnRows + lane] = acc;
+            }
+          }
+        };
+        if (nde <= kDnAll) {
+          uint4 ca[kDnAll][TM];
+          uint32_t swa[kDnAll][TM / 4];
+          int offa[kDnAll], cnta[kDnAll], myra[kDnAll];
+#pragma unroll
+          for (int q = 0; q < kDnAll; ++q) {
+            int sq;
+            entry(min(q, nde - 1), sq, offa[q], cnta[q]);
+            if (q == 0) {  // (requested before the loop)
+#pragma unroll
+              for (int t = 0; t < TM; ++t) ca[0][t] = c[t];
+#pragma unroll
+              for (int w4 = 0; w4 < TM / 4; ++w4) swa[0][w4] = sw[w4];
+            } else {
+              dn_load_steps<TM>(sec + (size_t)sq * image_bytes, dn_code_bytes, s0, ks, full, rem,
+                                nsw, lane, ca[q], swa[q]);
+            }
+            myra[q] = routes_of(offa[q], cnta[q]);
+          }
+#pragma unroll
+          for (int q = 0; q < kDnAll; ++q)
+            if (q < nde) expert(ca[q], swa[q], offa[q], cnta[q], myra[q]);
+        } else {
+          int slot_c, off, cnt;
+          entry(0, slot_c, off, cnt);
+          int myr = routes_of(off, cnt);
+#pragma unroll 1
+          for (int i = 0; i < nde; ++i) {
+            int slot_n, off_n, cnt_n;
+            entry(min(i + 1, nde - 1), slot_n, off_n, cnt_n);
+            dn_load_steps<TM>(sec + (size_t)slot_n * image_bytes, dn_code_bytes, s0, ks, full, rem,
+                              nsw, lane, cn, swn);
+            const int myr_n = routes_of(off_n, cnt_n);
+            expert(c, sw, off, cnt, myr);
+#pragma unroll
+            for (int t = 0; t < TM; ++t) c[t] = cn[t];
+#pragma unroll
+            for (int q = 0; q < TM / 4; ++q) sw[q] = swn[q];
+            myr = myr_n;
+            off = off_n;
+            cnt = cnt_n;
+          }
+        }
+      } else if (nde > 0) {
+        // h in the workspace: every step of the next route's h is requested while a route is
+        // formed (the next expert's first route after an expert's last), 2 x TM x 16 VGPRs
         int slot_c, off, cnt;
         entry(0, slot_c, off, cnt);
         int myr = routes_of(off, cnt);
@@ -1426,7 +1542,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
 // weights and h requested before the current stage's MFMAs.  Each route's rows go to
 // pdn[route][row] in fp32; k_combine forms y in the fixed route order.
 constexpr int kDnRW = 2;                                // down tiles per wave
-constexpr size_t kDownLdsBytes = 60 * 1024;             // dynamic LDS of k_down_gemv
+constexpr size_t kDownLdsBytes = 150 * 1024;            // dynamic LDS of k_down_gemv (gfx950: 160 KiB a workgroup)
 constexpr int kDnSub = 16;                              // routes per pass
 constexpr int kDnRoutePitch = 4 * 256 + 16;             // 4 steps of hi|lo (+16: bank spread)
 
@@ -1640,29 +1756,6 @@ __device__ __forceinline__ void block_dot_scaled(const uint4 c, const uint4 a0, 
                                          as_bf16x2(aw[4 * j + 2]), s0, false);
     s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 3),
                                          as_bf16x2(aw[4 * j + 3]), s1, false);
-  }
-}
-
-// One 32-element block (16 code bytes) as 16 bf16 pairs, the block scale folded in (exact).
-__device__ __forceinline__ void block_to_bf16(const uint4 c, float sc, bf16x2_t (&w)[16]) {
-  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    w[4 * j + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 0);
-    w[4 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 1);
-    w[4 * j + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 2);
-    w[4 * j + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 3);
-  }
-}
-// ... and its dot with 32 bf16 activations, on two accumulation chains (even / odd pairs).
-__device__ __forceinline__ void block_dot_bf16(const bf16x2_t (&w)[16], const uint4 a0, const uint4 a1,
-                                               const uint4 a2, const uint4 a3, float& s0, float& s1) {
-  const uint32_t aw[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                           a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    s0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(aw[i]), s0, false);
-    s1 = __builtin_amdgcn_fdot2_f32_bf16(w[i + 1], as_bf16x2(aw[i + 1]), s1, false);
   }
 }
 
@@ -2627,7 +2720,9 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k) {
   p.nd_max = Mk < E ? Mk : E;
   // M >= kGroupedMinTokens: the grouped GEMM (it needs H a multiple of 64 for its row tiles,
   // which every supported shape is) with the route table from the bucketing kernel
-  p.grouped = M >= kGroupedMinTokens;
+  // (also when the GEMV down kernel could not hold the partial rows of every route in LDS)
+  const int dn_kparts = L.dn_ks > 8 ? 2 : 1;
+  p.grouped = M >= kGroupedMinTokens || (size_t)Mk * dn_kparts * kDnRows * 4 > kDownLdsBytes;
   p.n_items_max = n_items_max(Mk, E);
   // every gate/up workgroup rebuilding the route table pays a top-k per token: worth it for one
   // token, or for a few routes over few experts; otherwise the top-k / bucketing kernel does it

@@ -1244,3 +1244,29 @@ def test_device_cache_state_copy_is_a_checkpoint():
         assert len(plan) == int(n1[t - t0]), t
     host.close()
     host2.close()
+
+
+def test_many_routes_fall_back_to_the_grouped_path():
+    """Below 64 tokens, a call whose down partial rows would not fit the GEMV kernel's LDS (here
+    k = 32 routes per token, I = 1280 split in two K parts: 40 x 32 routes) runs the grouped
+    kernels, and matches the oracle."""
+    wl = synthetic.Workload("many_routes", 7, 256, 1280, 64, 32, (40,), 64)
+    shape = B.make_shape(wl.hidden, wl.inter, wl.n_experts, wl.top_k, wl.n_slots)
+    M = 40
+    assert B.moe_layer_launches(shape, M) == 5
+    assert B.moe_layer_launches(shape, 8) == 4
+    experts = synthetic.experts_canonical(wl, 0, range(wl.n_experts))
+    slots = L.device_slots(L.pack_bank(shape, experts))
+    wr = synthetic.router_weights(wl)
+    buf = L.Buffers(shape, M)
+    for m in (M, 8):
+        say("many routes: M =", m)
+        x = synthetic.activations(wl, m, m)
+        B.moe_layer_forward(shape, _dev(x), m, _dev(wr), None, None, slots, buf.ids, buf.w, buf.y,
+                            buf.cold_count, buf.cold_routes, buf.ws)
+        torch.cuda.synchronize()
+        no_device_errors(buf.ws)
+        _, ids_ref, w_ref = compare_routes(buf.ids[:m].cpu().numpy(), buf.w[:m].cpu().numpy(),
+                                           O.router_logits(x, wr), wl.top_k)
+        close_enough(buf.y[:m].cpu().numpy(), O.layer_forward(x, ids_ref, w_ref, experts)["y_full"],
+                     f"many routes M={m}")
