@@ -73,16 +73,17 @@ __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, i
 // cost).  Larger E: k rounds of a wave argmax over PL logits per lane.
 __device__ __forceinline__ float rank_key(float v) { return v != v ? -INFINITY : v; }
 
-// Larger E: every logit becomes a 64-bit rank key, larger = ranks higher (monotone image of
-// the value in the high word, NaN as -inf and -0 as +0; the bitwise complement of the id in the
-// low word, so that ties go to the lower id); then k rounds of: each lane's best key, the
-// wave's best key (DPP / swizzle / readlane), and the owner clears it.  All branch-free.
-__device__ __forceinline__ uint64_t rank_key64(float v, int id) {
+// A logit's value key: a monotone 32-bit image of the value (NaN as -inf, -0 as +0), never
+// zero.  The 64-bit rank key adds the bitwise complement of the id in the low word, so that
+// ties go to the lower id.
+__device__ __forceinline__ uint32_t value_key(float v) {
   v = rank_key(v);
   if (v == 0.0f) v = 0.0f;
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)id;
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t rank_key64(float v, int id) {
+  return ((uint64_t)value_key(v) << 32) | (uint32_t)~(uint32_t)id;
 }
 // Number of lanes j < E (E <= 64) whose key is larger than this lane's (keys are distinct):
 // the lane's rank.  One 64-bit compare per lane j on a broadcast key, all in the vector unit.
@@ -125,60 +126,64 @@ __device__ void topk_rank(const float* __restrict__ lrow, size_t pstride, int E,
   }
 }
 
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t h = (uint32_t)(key >> 32);
+__device__ __forceinline__ float key_value32(uint32_t h) {
   return __uint_as_float((h & 0x80000000u) ? (h ^ 0x80000000u) : ~h);
 }
+__device__ __forceinline__ float key_value(uint64_t key) { return key_value32((uint32_t)(key >> 32)); }
 __device__ __forceinline__ int key_id(uint64_t key) { return (int)~(uint32_t)key; }
-__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(v >> 32));
-  return ((uint64_t)hi << 32) | lo;
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = max_u64(v, dpp_u64<0xB1>(v));
-  v = max_u64(v, dpp_u64<0x4E>(v));
-  v = max_u64(v, dpp_u64<0x141>(v));
-  v = max_u64(v, dpp_u64<0x140>(v));
-  const uint32_t lo = (uint32_t)swz_xor16_i((int)(uint32_t)v);
-  const uint32_t hi = (uint32_t)swz_xor16_i((int)(uint32_t)(v >> 32));
-  v = max_u64(v, ((uint64_t)hi << 32) | lo);
-  const uint64_t a = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 0) << 32) |
-                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 0);
-  const uint64_t b = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 32) << 32) |
-                     (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 32);
-  return max_u64(a, b);
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i<0xB1>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x4E>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x141>((int)v));
+  v = max(v, (uint32_t)dpp_i<0x140>((int)v));
+  v = max(v, (uint32_t)swz_xor16_i((int)v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  return max(a, b);
 }
 
+// 64 < E: lane l holds the value keys of experts l, l + 64, ... (PL of them); then k rounds of:
+// the wave's largest value key (each lane's best, then DPP / swizzle / readlane on 32 bits),
+// the lowest expert id holding it (one ballot per register, lowest register first: ids in
+// register i are 64 i .. 64 i + 63), and that key cleared.  Ties thus go to the lower id, as
+// with the 64-bit rank keys.  All branch-free; the id search runs on the scalar unit.
 template <int PL, int P>
 __device__ void topk_argmax(const float* __restrict__ lrow, size_t pstride, int E, int k,
                             int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
   float lv[PL];
-  uint64_t key[PL];
+  uint32_t key[PL];
   // every load issued before any is used (clamped in range; loads in a branch would each be
   // waited for alone); slots past E get key 0, below every real key
 #pragma unroll
   for (int i = 0; i < PL; ++i) lv[i] = logit_at<P>(lrow, pstride, min(lane + 64 * i, E - 1));
 #pragma unroll
-  for (int i = 0; i < PL; ++i) key[i] = lane + 64 * i < E ? rank_key64(lv[i], lane + 64 * i) : 0ull;
-  uint64_t mine = 0ull;  // lane j < k: the j-th key
+  for (int i = 0; i < PL; ++i) key[i] = lane + 64 * i < E ? value_key(lv[i]) : 0u;
+  uint32_t mine = 0u;  // lane j < k: the j-th value key and its id
+  int mine_id = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    uint32_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < PL; ++i) best = max_u64(best, key[i]);
-    best = wave_max_u64(best);  // uniform
+    for (int i = 1; i < PL; ++i) best = max(best, key[i]);
+    best = wave_max_u32(best);  // uniform
+    int id = 0;
+#pragma unroll
+    for (int i = PL - 1; i >= 0; --i) {
+      const uint64_t b = __ballot(key[i] == best);
+      id = b != 0 ? 64 * i + (int)__ffsll((long long)b) - 1 : id;
+    }
+    id = __builtin_amdgcn_readfirstlane(id);
     mine = lane == j ? best : mine;
+    mine_id = lane == j ? id : mine_id;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) key[i] = key[i] == best ? 0ull : key[i];
+    for (int i = 0; i < PL; ++i) key[i] = lane + 64 * i == id ? 0u : key[i];
   }
-  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(key_value(mine)), 0));
-  const float ex = lane < k ? expf(key_value(mine) - top) : 0.0f;
+  const float v = key_value32(mine);
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float ex = lane < k ? expf(v - top) : 0.0f;
   const float den = wave_sum(ex);
   if (lane < k) {
-    ids[lane] = key_id(mine);
+    ids[lane] = mine_id;
     w[lane] = ex / den;
   }
 }
@@ -481,6 +486,88 @@ __device__ __forceinline__ void opaque(uint4 (&c)[4 * G]) {
 #pragma unroll
   for (int j = 0; j < 4 * G; ++j)
     asm volatile("" : "+v"(c[j].x), "+v"(c[j].y), "+v"(c[j].z), "+v"(c[j].w));
+}
+
+// One 32-element block (16 code bytes) as 16 bf16 pairs, the block scale folded in (exact).
+__device__ __forceinline__ void block_to_bf16(const uint4 c, float sc, bf16x2_t (&w)[16]) {
+  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[4 * j + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 0);
+    w[4 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 1);
+    w[4 * j + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 2);
+    w[4 * j + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 3);
+  }
+}
+// ... and its dot with 32 bf16 activations, on two accumulation chains (even / odd pairs).
+__device__ __forceinline__ void block_dot_bf16(const bf16x2_t (&w)[16], const uint4 a0, const uint4 a1,
+                                               const uint4 a2, const uint4 a3, float& s0, float& s1) {
+  const uint32_t aw[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
+                           a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(aw[i]), s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(w[i + 1], as_bf16x2(aw[i + 1]), s1, false);
+  }
+}
+
+// dot_tile_lds for kGuNR routes at once (activation rows act + tok[r] * H in LDS): each code
+// word is converted to a bf16 pair once (scale 1) and the pair feeds every route's chain, in
+// block_dot's pair order and accumulation chains, so each sum is bitwise dot_tile_lds's.
+constexpr int kGuNR = 2;
+template <int G>
+__device__ __forceinline__ void dot_tile_lds_nr(const uint4 (&c)[4 * G], const uint32_t (&s4)[G],
+                                                int nb, int g0, int ngw, const uint16_t* xs,
+                                                int H, const int (&tok)[kGuNR],
+                                                float (&acc)[kGuNR]) {
+#pragma unroll
+  for (int r = 0; r < kGuNR; ++r) acc[r] = 0.0f;
+#pragma unroll
+  for (int q = 0; q < G; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * (g0 + q) + i;
+      const bool live = q < ngw && b < nb;
+      const float sc = e8m0_to_f32((s4[q] >> (8 * i)) & 0xFFu);
+      uint4 a[kGuNR][4];
+#pragma unroll
+      for (int r = 0; r < kGuNR; ++r) {
+        const uint4* ar = reinterpret_cast<const uint4*>(xs + (size_t)tok[r] * H + 32 * min(b, nb - 1));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[r][j] = ar[j];
+      }
+      const uint4 cb = c[4 * q + i];
+      const uint32_t cw[4] = {cb.x, cb.y, cb.z, cb.w};
+      // the conversions' scale (1.0) comes out of an empty asm that takes the previous block's
+      // sums, so this block is converted after them (the compiler would otherwise convert every
+      // block up front and hold all the pairs); the codes themselves are read in place
+      float one;
+      asm volatile("v_mov_b32 %0, 1.0" : "=v"(one) : "v"(acc[0]), "v"(acc[kGuNR - 1]));
+      float s0[kGuNR], s1[kGuNR];
+#pragma unroll
+      for (int r = 0; r < kGuNR; ++r) s0[r] = s1[r] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x2_t w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], one, 0);
+        const bf16x2_t w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], one, 1);
+        const bf16x2_t w2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], one, 2);
+        const bf16x2_t w3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], one, 3);
+#pragma unroll
+        for (int r = 0; r < kGuNR; ++r) {
+          s0[r] = __builtin_amdgcn_fdot2_f32_bf16(w0, as_bf16x2(a[r][j].x), s0[r], false);
+          s1[r] = __builtin_amdgcn_fdot2_f32_bf16(w1, as_bf16x2(a[r][j].y), s1[r], false);
+          s0[r] = __builtin_amdgcn_fdot2_f32_bf16(w2, as_bf16x2(a[r][j].z), s0[r], false);
+          s1[r] = __builtin_amdgcn_fdot2_f32_bf16(w3, as_bf16x2(a[r][j].w), s1[r], false);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kGuNR; ++r) {
+        const float v = fmaf(sc, s0[r] + s1[r], acc[r]);
+        acc[r] = live ? v : acc[r];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one block's activations live at a time
+    }
+  }
 }
 
 // Sum over the loaded blocks of scale * (codes . act block); act is uniform across the wave.
@@ -997,6 +1084,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  // lane j: route j of this expert (the multi-route loop below reads it by readlane)
+  const int myr = (!SINGLE && XLDS && G <= 2) ? perm[off + min(lane, cnt - 1)] : 0;
   load_tile_range<G>(codes, scl, nb, g0, ngw, lane, s4, c);
   if (XLDS && !PRO) __syncthreads();  // activations in LDS for every wave
 
@@ -1018,13 +1107,36 @@ __global__ __launch_bounds__(kMaxWaves * 64) void k_gateup(
   }
   for (int base = 0; base < cnt; base += kTokPerPass) {
     const int nt = min(kTokPerPass, cnt - base);
+    if (XLDS && G <= 2) {
+      // kGuNR routes per decode of the weights (the last group padded with the pass's last
+      // route, whose sums are not stored twice); with 4 groups a wave the extra activation
+      // registers would spill.  The tokens of the expert's routes come from lane registers
+      // (myr), read before the weights, so no load waits inside this loop.
 #pragma unroll 1
-    for (int t = 0; t < nt; ++t) {
-      opaque<G>(c);
-      const int r = __builtin_amdgcn_readfirstlane(perm[off + base + t]);
-      const int tok = r / ra.k;
-      red[wave][t][lane] = XLDS ? dot_tile_lds<G>(c, s4, nb, g0, ngw, xs + (size_t)tok * H)
-                                : dot_tile_range<G>(c, s4, nb, g0, ngw, x + (size_t)tok * H);
+      for (int t0 = 0; t0 < nt; t0 += kGuNR) {
+        // (no opaque() here: the conversions already wait for an asm inside this loop)
+        int tok[kGuNR];
+#pragma unroll
+        for (int u = 0; u < kGuNR; ++u) {
+          const int j = base + min(t0 + u, nt - 1);
+          tok[u] = (j < 64 ? __builtin_amdgcn_readlane(myr, j)
+                           : __builtin_amdgcn_readfirstlane(perm[off + j])) / ra.k;
+        }
+        float acc[kGuNR];
+        dot_tile_lds_nr<G>(c, s4, nb, g0, ngw, xs, H, tok, acc);
+#pragma unroll
+        for (int u = 0; u < kGuNR; ++u)
+          if (t0 + u < nt) red[wave][t0 + u][lane] = acc[u];
+      }
+    } else {
+#pragma unroll 1
+      for (int t = 0; t < nt; ++t) {
+        opaque<G>(c);
+        const int r = __builtin_amdgcn_readfirstlane(perm[off + base + t]);
+        const int tok = r / ra.k;
+        red[wave][t][lane] = XLDS ? dot_tile_lds<G>(c, s4, nb, g0, ngw, xs + (size_t)tok * H)
+                                  : dot_tile_range<G>(c, s4, nb, g0, ngw, x + (size_t)tok * H);
+      }
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < nt * 32; idx += nthr) {
@@ -1196,29 +1308,6 @@ __device__ __forceinline__ float dn_route_dot_h(const uint4 (&c)[TM], const uint
 
 // Sum over the 4 lanes of a row (l, l^16, l^32, l^48); every one of them gets it.
 __device__ __forceinline__ float dn_row_sum(float v) { return pair_sum32(pair_sum16(v)); }
-
-// One 32-element block (16 code bytes) as 16 bf16 pairs, the block scale folded in (exact).
-__device__ __forceinline__ void block_to_bf16(const uint4 c, float sc, bf16x2_t (&w)[16]) {
-  const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    w[4 * j + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 0);
-    w[4 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 1);
-    w[4 * j + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 2);
-    w[4 * j + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], sc, 3);
-  }
-}
-// ... and its dot with 32 bf16 activations, on two accumulation chains (even / odd pairs).
-__device__ __forceinline__ void block_dot_bf16(const bf16x2_t (&w)[16], const uint4 a0, const uint4 a1,
-                                               const uint4 a2, const uint4 a3, float& s0, float& s1) {
-  const uint32_t aw[16] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w,
-                           a2.x, a2.y, a2.z, a2.w, a3.x, a3.y, a3.z, a3.w};
-#pragma unroll
-  for (int i = 0; i < 16; i += 2) {
-    s0 = __builtin_amdgcn_fdot2_f32_bf16(w[i], as_bf16x2(aw[i]), s0, false);
-    s1 = __builtin_amdgcn_fdot2_f32_bf16(w[i + 1], as_bf16x2(aw[i + 1]), s1, false);
-  }
-}
 
 constexpr int kDnNR = 2;   // routes of an expert the down GEMV forms together (h in LDS)
 constexpr int kDnAll = 4;  // hot experts of a wave whose weights it requests all at once
