@@ -457,8 +457,8 @@ moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n) {
     *n = layer_decode_router_inside(L, shape->n_experts) ? 1 : 2;  // [router,] fused layer
   else if (p.grouped)
     *n = 5;                     // router, top-k / bucket, gate/up, down, combine
-  else
-    *n = p.prologue ? 3 : 4;    // router, [top-k / bucket,] gate/up, down + combine
+  else  // router, [top-k / bucket,] gate/up, down + combine [split: down, combine]
+    *n = (p.prologue ? 3 : 4) + (down_split(L, M, shape->top_k, shape->n_experts) > 1 ? 1 : 0);
   return ok();
 }
 

@@ -313,6 +313,8 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k);
 hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                          const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                          const RouteWs& rw, uint16_t* hbuf, hipStream_t s);
+// Workgroups per tile of the down GEMV (1, or 2 with k_combine forming y: one launch more).
+int down_split(const ImageLayout& L, int M, int k, int E);
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
                        const uint16_t* hbuf, float* pdn, float* y, Residual res, hipStream_t s);

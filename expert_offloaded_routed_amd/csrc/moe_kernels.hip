@@ -1317,18 +1317,21 @@ __host__ __device__ __forceinline__ int dn_part_steps(int ks, int kparts) {
   return ((ks + kparts - 1) / kparts + 3) & ~3;
 }
 
-// grid = H/16 tiles, 8 waves.  The waves own (expert slot, K part) pairs: with kparts K parts,
-// 8/kparts hot experts per pass, wave w taking experts w % (8/kparts) + (8/kparts)*i and K
-// part w / (8/kparts).  Each route's partial rows go to LDS; the workgroup then forms
+// grid = (H/16 tiles, S), 8 waves.  Workgroup (tile, p) takes the hot experts p, p + S, ...;
+// its waves own (expert, K part) pairs: with kparts K parts, 8/kparts of its experts per pass,
+// wave w taking the experts of its list at w % (8/kparts) + (8/kparts)*i and K part
+// w / (8/kparts).  With S = 1 each route's partial rows go to LDS and the workgroup then forms
 // y[m][rows] = sum over j ascending (hot routes) of w[m,j] * (its K parts, in order): no other
-// workgroup is involved.  h comes from an LDS copy when every route's h fits (h_lds), else
-// straight from the workspace.  The route table comes from the workspace.
+// workgroup is involved.  With S > 1 (one K part) each route's rows go to pdn[route][rows]
+// instead, and k_combine forms y with the same arithmetic, so that twice as many compute units
+// share the experts.  h comes from an LDS copy when every route's h fits (h_lds), else straight
+// from the workspace.  The route table comes from the workspace.
 template <int TM>
 __global__ __launch_bounds__(512) void k_down_gemv(
     int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
     size_t dn_tile_bytes, size_t dn_code_bytes, int ks, int full, int rem, int nsw, int nb,
     int kparts, int h_lds, RouteArgs ra, RouteWs rw, const uint16_t* __restrict__ hbuf,
-    float* __restrict__ y, Residual res) {
+    float* __restrict__ y, Residual res, float* __restrict__ pdn) {
   extern __shared__ __align__(16) uint8_t smem[];  // [h copy (h_lds)] [parts: Mk x kparts x 16]
   const int tile = blockIdx.x;
   const int Mk = ra.M * ra.k;
@@ -1336,7 +1339,11 @@ __global__ __launch_bounds__(512) void k_down_gemv(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int sl = 8 / kparts;
-  const int es0 = wave % sl, kh = wave / sl;
+  const int kh = wave / sl;
+  // this wave's experts: es0, es0 + sl, ... (es0 the first, sl the stride in the hot list)
+  const bool split = gridDim.y > 1;  // (then kparts == 1 and the rows go to pdn)
+  const int es0 = (int)blockIdx.y + (int)gridDim.y * (wave % sl);
+  const int sl_all = (int)gridDim.y * sl;
   const int spw = dn_part_steps(ks, kparts);
   const int s0 = kh * spw;
   const uint8_t* sec = slots + gu_bytes + (size_t)tile * dn_tile_bytes;
@@ -1364,6 +1371,13 @@ __global__ __launch_bounds__(512) void k_down_gemv(
   dn_load_steps<TM>(sec + (size_t)slot0 * image_bytes, dn_code_bytes, s0, ks, full, rem, nsw, lane, c, sw);
   const uint16_t* hsrc = h_lds ? reinterpret_cast<const uint16_t*>(smem) : hbuf;
   float* parts = reinterpret_cast<float*>(smem + (h_lds ? (size_t)(n_h + 63) / 64 * 1024 : 0));
+  // a route's partial rows (lanes < 16): to LDS, or with the experts split to pdn
+  auto put = [&](int route, float acc) {
+    if (split)
+      pdn[(size_t)route * H + tile * kDnRows + lane] = acc;
+    else
+      parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+  };
   __syncthreads();
   bool fast = false;
   if constexpr (TM <= 4) {
@@ -1371,10 +1385,10 @@ __global__ __launch_bounds__(512) void k_down_gemv(
     // from one expert to the next.  Lane i holds the table entry of the wave's i-th expert (one
     // read for all of them); the next expert's weights and route list are requested when an
     // expert starts.
-    const int nde = es0 < nd ? (nd - es0 + sl - 1) / sl : 0;
+    const int nde = es0 < nd ? (nd - es0 + sl_all - 1) / sl_all : 0;
     if (nde <= 64) {
       fast = true;
-      const int4 md = rw.dist[min(es0 + min(lane, max(nde - 1, 0)) * sl, nd_max - 1)];
+      const int4 md = rw.dist[min(es0 + min(lane, max(nde - 1, 0)) * sl_all, nd_max - 1)];
       auto entry = [&](int i, int& slot, int& off, int& cnt) {  // (i uniform)
         slot = __builtin_amdgcn_readlane(md.x, i);
         off = __builtin_amdgcn_readlane(md.y, i);
@@ -1425,8 +1439,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
 #pragma unroll
             for (int u = 0; u < kDnNR; ++u) {
               const float acc = dn_row_sum(e0[u] + e1[u]);
-              if (j + u < cnt && lane < kDnRows)
-                parts[((size_t)rr[u] * kparts + kh) * kDnRows + lane] = acc;
+              if (j + u < cnt && lane < kDnRows) put(rr[u], acc);
             }
           }
         };
@@ -1504,7 +1517,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
             __builtin_amdgcn_sched_barrier(0);
             float acc = dn_route_dot_h<TM>(c, sw, s0, spw, ks, nb, g, hc);
             acc = dn_row_sum(acc);
-            if (lane < kDnRows) parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+            if (lane < kDnRows) put(route, acc);
 #pragma unroll
             for (int t = 0; t < TM; ++t)
 #pragma unroll
@@ -1524,11 +1537,11 @@ __global__ __launch_bounds__(512) void k_down_gemv(
       }
     }
   }
-  for (int d = es0; !fast && d < nd; d += sl) {
+  for (int d = es0; !fast && d < nd; d += sl_all) {
     const int4 dd = rw.dist[d];
     if constexpr (PF) {
       // the last pass re-requests its own weights, unused
-      const int dn = d + sl < nd ? d + sl : d;
+      const int dn = d + sl_all < nd ? d + sl_all : d;
       dn_load_steps<TM>(sec + (size_t)rw.dist[dn].x * image_bytes, dn_code_bytes, s0, ks, full,
                         rem, nsw, lane, cn, swn);
     } else if (d != es0) {
@@ -1558,7 +1571,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
           __builtin_amdgcn_sched_barrier(0);
           float acc = dn_route_dot_h<TM>(c, sw, s0, spw, ks, nb, g, hc);
           acc = dn_row_sum(acc);
-          if (lane < kDnRows) parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+          if (lane < kDnRows) put(route, acc);
 #pragma unroll
           for (int t = 0; t < TM; ++t)
 #pragma unroll
@@ -1578,7 +1591,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
           float acc = dn_route_dot_pf<TM>(c, sw, s0, spw, ks, nb, g, hsrc + (size_t)route * I,
                                           hsrc + (size_t)rnext * I, an);
           acc = dn_row_sum(acc);
-          if (lane < kDnRows) parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
+          if (lane < kDnRows) put(route, acc);
           route = rnext;
         }
       }
@@ -1590,6 +1603,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
       for (int q = 0; q < TM / 4; ++q) sw[q] = swn[q];
     }
   }
+  if (split) return;  // (k_combine forms y)
   __syncthreads();
   for (int idx = threadIdx.x; idx < ra.M * kDnRows; idx += blockDim.x) {
     const int m = idx / kDnRows;
@@ -2583,7 +2597,11 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
 }
 
 // y[m][h] = sum over j ascending of the hot routes m*k+j of w * pdn[m*k+j][h] (cold routes add
-// nothing).  One thread per (token, 4 rows).
+// nothing).  One thread per (token, 4 rows).  KB routes at a time, every load of a batch
+// requested before the first is used (the rows of a cold route are read and left unused), then
+// the sum in ascending j: KB = 4 for many tokens (registers, occupancy), 16 for a few (one round
+// trip for k <= 16).
+template <int KB>
 __global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs ra, RouteWs rw,
                                                  const float* __restrict__ pdn,
                                                  float* __restrict__ y, Residual res) {
@@ -2593,21 +2611,19 @@ __global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs 
   const int m = q / per;
   const int h = (q - m * per) * 4;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  // 4 routes at a time, every load of a batch requested before the first is used (the rows of a
-  // cold route are read and left unused), then the sum in ascending j
-  for (int j0 = 0; j0 < k; j0 += 4) {
-    bool hot[4];
-    float wt[4];
-    float4 v[4];
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    bool hot[KB];
+    float wt[KB];
+    float4 v[KB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < KB; ++u) {
       const int r = m * k + min(j0 + u, k - 1);
       hot[u] = j0 + u < k && rw.route_slot[r] >= 0;
       wt[u] = ra.w_in[r];
       v[u] = *reinterpret_cast<const float4*>(pdn + (size_t)r * H + h);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < KB; ++u) {
       if (hot[u]) {
         acc.x = fmaf(wt[u], v[u].x, acc.x);
         acc.y = fmaf(wt[u], v[u].y, acc.y);
@@ -2913,36 +2929,55 @@ static hipError_t launch_down_mx(int M, int H, int I, const uint8_t* slots, cons
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int threads = M * (H / 4);
-  hipLaunchKernelGGL(k_combine, dim3((threads + 255) / 256), dim3(256), 0, s, M, ra.k, H, ra, rw,
-                     pdn, y, res);
+  hipLaunchKernelGGL(k_combine<4>, dim3((threads + 255) / 256), dim3(256), 0, s, M, ra.k, H, ra,
+                     rw, pdn, y, res);
   return hipGetLastError();
+}
+
+// Workgroups per down tile of the GEMV path: 2 (the hot experts split between them, k_combine
+// forming y) when the tiles fill at most half of the compute units, K is one part and there are
+// enough hot experts to share, else 1.  The combine's own launch (about 5 us between dependent
+// kernels) outweighs the split with fewer experts, hence the bound: at least 64 possible hot
+// experts, 8 a wave of one workgroup (on the E = 512, k = 10 stack: a gain at 8 tokens, a loss
+// at 4).
+constexpr int kDnSplitMinExperts = 64;
+int down_split(const ImageLayout& L, int M, int k, int E) {
+  const int cus = device_cus();
+  const int nd_max = M * k < E ? M * k : E;
+  const bool one_part = L.dn_ks <= 8;
+  return one_part && nd_max >= kDnSplitMinExperts && cus > 0 && 2 * L.dn_tiles <= cus ? 2 : 1;
 }
 
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
                        const uint16_t* hbuf, float* pdn, float* y, Residual res, hipStream_t s) {
   (void)p;
-  (void)pdn;
   const int Mk = M * ra.k;
   // long K in two parts (4 experts per pass, half the steps per wave), short K in one (8
   // experts per pass); a wave holds at most 16 steps
   const int kparts = L.dn_ks > 8 ? 2 : 1;
   const int spw = dn_part_steps(L.dn_ks, kparts);
-  const size_t parts = (size_t)Mk * kparts * kDnRows * 4;
+  const int S = down_split(L, M, ra.k, ra.E);
+  const size_t parts = S > 1 ? 0 : (size_t)Mk * kparts * kDnRows * 4;
   const size_t hcopy = ((size_t)Mk * I / 8 + 63) / 64 * 1024;
   const bool h_lds = hcopy + parts <= kDownLdsBytes;
   const size_t lds = (h_lds ? hcopy : 0) + parts;
-  if (lds > kDownLdsBytes || spw > 16) return hipErrorInvalidValue;
+  if (lds > kDownLdsBytes || spw > 16 || (S > 1 && pdn == nullptr)) return hipErrorInvalidValue;
 #define MOE_DG(TM)                                                                                 \
-  hipLaunchKernelGGL((k_down_gemv<TM>), dim3(L.dn_tiles), dim3(512), lds, s, H, I, slots,           \
+  hipLaunchKernelGGL((k_down_gemv<TM>), dim3(L.dn_tiles, S), dim3(512), lds, s, H, I, slots,        \
                      L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks,          \
                      L.dn_full, L.dn_rem, L.dn_scale_words, L.nb_i, kparts, h_lds ? 1 : 0, ra, rw,  \
-                     hbuf, y, res)
+                     hbuf, y, res, pdn)
   if (spw <= 4) MOE_DG(4);
   else if (spw <= 8) MOE_DG(8);
   else if (spw <= 12) MOE_DG(12);
   else MOE_DG(16);
 #undef MOE_DG
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int threads = M * (H / 4);
+  hipLaunchKernelGGL(k_combine<16>, dim3((threads + 255) / 256), dim3(256), 0, s, M, ra.k, H, ra,
+                     rw, pdn, y, res);
   return hipGetLastError();
 }
 

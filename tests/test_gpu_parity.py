@@ -248,6 +248,10 @@ def test_e512_verify_half_resident(e512, M):
     e2s = np.full(wl.n_experts, -1, np.int32)
     e2s[slot_expert] = np.arange(wl.n_slots)
     shape = _shape(wl, wl.n_slots)
+    # one token: router + fused kernel; 4 tokens (40 routes): router, top-k / bucketing, gate/up,
+    # down + combine; 8 tokens (80 routes, at least 64 possible hot experts): the down GEMV
+    # shares each row tile's experts between two workgroups and the combine is its own launch
+    assert B.moe_layer_launches(shape, M) == {1: 2, 4: 4, 8: 5}[M]
     slots = e512.slots_for(slot_expert)
     buf = L.Buffers(shape, M)
     bias = synthetic.zipf_bias(wl)
