@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--enqueue-spin-cycles", type=float, default=2e8,
                    help="GPU cycles of the spin kernel that holds the stream while marked steps are enqueued")
     p.add_argument("--cpu-steps", type=int, default=40, help="oracle steps for cpu_baseline (0 = skip)")
+    p.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="write profiles/traffic.json from two rocprofv3 counter runs of "
+                        "--calibrate-copy-mb 256 (FETCH_SIZE, then WRITE_SIZE) and exit")
     p.add_argument("--calibrate-copy-mb", type=int, default=0,
                    help="after the run, copy a buffer of this many MiB device to device 4 times (a "
                         "plain copy kernel of known size, to scale HBM byte counters)")
@@ -1192,6 +1195,55 @@ def bench_formats(args):
     return 0
 
 
+def write_traffic(fetch_csv, write_csv):
+    """profiles/traffic.json from the counter CSVs of the two passes over the decode line: the
+    median FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused decode kernel and of the
+    streaming probe, each scaled by what the same counter reads for the plain device copy of
+    --calibrate-copy-mb (the last four copy dispatches), keyed by the kernel sources' hash."""
+    import csv
+    from expert_offloaded_routed_amd import _build
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(vals, prefix):
+        rows = [v for k, v in vals.items() if prefix in k]
+        if len(rows) != 1:
+            raise SystemExit(f"expected one kernel matching {prefix!r}, found {len(rows)}")
+        return rows[0]
+    copy_f = pick(fetch, "copyBuffer")[-4:]
+    copy_w = pick(write, "copyBuffer")[-4:]
+    nbytes = 256 << 20
+    fs = nbytes / (float(np.median(copy_f)) * 1024)
+    ws = nbytes / (float(np.median(copy_w)) * 1024)
+    out = {"kernel_source_sha": _build.kernel_source_sha(),
+           "copy_calibration": {"bytes": nbytes, "fetch_size_kib": float(np.median(copy_f)),
+                                "write_size_kib": float(np.median(copy_w)),
+                                "fetch_scale": round(fs, 6), "write_scale": round(ws, 6)}}
+    algo = {"layer_decode": 52876800, "stream_probe": 52876800}
+    for name, prefix in (("layer_decode", "k_layer_decode"), ("stream_probe", "k_stream_probe")):
+        f, w = pick(fetch, prefix), pick(write, prefix)
+        fm, wm = float(np.median(f)), float(np.median(w))
+        hbm = int(round(fm * 1024 * fs + wm * 1024 * ws))
+        out[name] = {"fetch_size_kib_median": fm, "write_size_kib_median": wm,
+                     "dispatches": [len(f), len(w)], "hbm_bytes_per_launch": hbm,
+                     "algorithmic_bytes_per_launch": algo[name],
+                     "ratio": round(hbm / algo[name], 4)}
+    out["layer_decode_bytes_per_launch"] = out["layer_decode"]["hbm_bytes_per_launch"]
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of known size (4 times): its HBM byte counters per launch
     give the scale between what the counters read and the bytes moved."""
@@ -1208,6 +1260,8 @@ def copy_calibration(mib):
 
 def main():
     args = parse()
+    if args.traffic:
+        return write_traffic(*args.traffic)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
         return 2
