@@ -208,25 +208,66 @@ __device__ void topk_token(const float* __restrict__ lrow, int E, int k, int32_t
 // =============================================================================================
 // Route resolve + bucketing (one workgroup of kBucketThreads)
 // =============================================================================================
-// Exclusive scan of one value per thread over the whole workgroup; returns the total.
+// Workgroup barrier ordering LDS only: global loads in flight stay in flight across it, and
+// global stores are not waited for (a full barrier waits for every store to complete).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Exclusive scan of one value per thread over the whole workgroup; returns the total.  Its
+// barriers order LDS only.
 __device__ int block_exclusive_scan(int v, int* s_wave, int& total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nw = blockDim.x >> 6;
   const int incl = wave_inclusive_scan(v);
   if (lane == 63) s_wave[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {
     const int t = lane < nw ? s_wave[lane] : 0;
     const int ti = wave_inclusive_scan(t);
     if (lane < nw) s_wave[lane] = ti - t;  // exclusive prefix of wave totals
     if (lane == nw - 1) s_wave[kBucketThreads / 64] = ti;
   }
-  __syncthreads();
+  lds_barrier();
   const int out = s_wave[wave] + incl - v;
   total = s_wave[kBucketThreads / 64];
-  __syncthreads();
+  lds_barrier();
   return out;
+}
+
+// Exclusive scans of three values per thread over the whole workgroup at once (one set of
+// barriers for the three): out[c] = the prefix of value c, total[c] = its sum.
+__device__ void block_exclusive_scan3(const int (&v)[3], int (*s_wave)[kBucketThreads / 64 + 1],
+                                      int (&out)[3], int (&total)[3]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  int incl[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) incl[c] = wave_inclusive_scan(v[c]);
+  if (lane == 63)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) s_wave[c][wave] = incl[c];
+  lds_barrier();
+  if (wave == 0) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int t = lane < nw ? s_wave[c][lane] : 0;
+      const int ti = wave_inclusive_scan(t);
+      if (lane < nw) s_wave[c][lane] = ti - t;  // exclusive prefix of wave totals
+      if (lane == nw - 1) s_wave[c][kBucketThreads / 64] = ti;
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    out[c] = s_wave[c][wave] + incl[c] - v[c];
+    total[c] = s_wave[c][kBucketThreads / 64];
+  }
+  lds_barrier();
 }
 
 // Route resolve + bucketing by one workgroup (any multiple of 64 threads up to kBucketThreads):
@@ -241,7 +282,13 @@ struct BucketSmem {
   int off[kMaxExperts];
   int slot[kMaxExperts];  // resolved slot of every expert that has a route (-1: cold)
   int wave[kBucketThreads / 64 + 1];
+  int wave3[3][kBucketThreads / 64 + 1];
   int err;
+  // the top-k of the single-workgroup call (at most one token a wave), handed to the bucketing
+  // in LDS
+  int32_t tk_ids[kBucketThreads / 64 * kMaxTopK];
+  float tk_w[kBucketThreads / 64 * kMaxTopK];
+  int32_t e2s[kMaxExperts];  // the expert map, copied while the top-k runs (same call)
 };
 
 __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, int Mk, int E, int S,
@@ -259,7 +306,7 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
   const int tid = threadIdx.x;
   if (tid == 0) s_err = 0;
   for (int e = tid; e < E; e += blockDim.x) s_cnt[e] = 0;
-  __syncthreads();
+  lds_barrier();
 
   // resolve + count (every expert with a route also records its slot: equal writes)
   const int bd = blockDim.x;
@@ -302,7 +349,12 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
     const int e = ids[r];
     resolve(r, e, e >= 0 && e < E ? (e2s ? e2s[e] : e) : -1);
   }
-  __syncthreads();
+  // (the cold list reads route_slot back when a thread has more than one route: then the
+  // barrier also waits for those stores)
+  if (Mk > bd)
+    __syncthreads();
+  else
+    lds_barrier();
 
   // offsets (exclusive scan over experts), distinct hot experts (scan of flags) and the work
   // list of the grouped GEMM: one item per (distinct hot expert, pass of kItemRoutes routes)
@@ -313,10 +365,10 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
     const int slot = e < E && c > 0 ? sm.slot[e] : -1;
     const int hot = (c > 0 && slot >= 0) ? 1 : 0;
     const int np = hot ? (c + kItemRoutes - 1) / kItemRoutes : 0;
-    int tot, tot_d, tot_i;
-    const int off = running + block_exclusive_scan(c, s_wave, tot);
-    const int di = running_d + block_exclusive_scan(hot, s_wave, tot_d);
-    const int ii = running_i + block_exclusive_scan(np, s_wave, tot_i);
+    int ex[3], tt[3];
+    block_exclusive_scan3({c, hot, np}, sm.wave3, ex, tt);
+    const int off = running + ex[0], di = running_d + ex[1], ii = running_i + ex[2];
+    const int tot = tt[0], tot_d = tt[1], tot_i = tt[2];
     if (e < E) {
       s_off[e] = off;
       if (u_counts) u_counts[e] = c;
@@ -336,7 +388,7 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
     meta[0] = running_d < nd_max ? running_d : nd_max;
     meta[3] = running_i < n_items_max ? running_i : n_items_max;
   }
-  __syncthreads();
+  lds_barrier();
 
   // permutation: each route takes the next place of its expert's bucket
   auto place = [&](int r, int e) {
@@ -355,22 +407,55 @@ __device__ void bucket_stage(BucketSmem& sm, const int32_t* __restrict__ ids, in
   }
   for (int r = tid + kBucketRegRoutes * bd; r < Mk; r += bd) place(r, ids[r]);
 
-  // cold routes in ascending order
+  // cold routes in ascending order.  One route a thread: its slot is in registers.  Up to
+  // kBucketRegRoutes a thread: thread t takes the consecutive routes [t*per, t*per + per), their
+  // slots read back together (written by the resolve above, before a barrier), so that one scan
+  // orders all of them.  Beyond that, one scan per pass of blockDim.x routes.
   int running_c = 0;
-  for (int r0 = 0; r0 < Mk; r0 += blockDim.x) {
-    const int r = r0 + tid;
-    const int j = r0 / bd;
-    int sl = 0;
-#pragma unroll
-    for (int i = 0; i < kBucketRegRoutes; ++i) sl = i == j ? s_r[i] : sl;
-    const int cold = r < Mk && (j < kBucketRegRoutes ? sl : route_slot[r]) < 0 ? 1 : 0;
+  const int per = (Mk + bd - 1) / bd;
+  if (per <= 1) {
+    const int cold = tid < Mk && s_r[0] < 0 ? 1 : 0;
     int tot;
-    const int ci = running_c + block_exclusive_scan(cold, s_wave, tot);
+    const int ci = block_exclusive_scan(cold, s_wave, tot);
     if (cold && ci < Mk) {
-      cold_list[ci] = r;
-      if (u_cold_routes) u_cold_routes[ci] = r;
+      cold_list[ci] = tid;
+      if (u_cold_routes) u_cold_routes[ci] = tid;
     }
-    running_c += tot;
+    running_c = tot;
+  } else if (per <= kBucketRegRoutes) {
+    const int r0 = tid * per;
+    int sv[kBucketRegRoutes];
+#pragma unroll
+    for (int q = 0; q < kBucketRegRoutes; ++q) sv[q] = q < per && r0 + q < Mk ? route_slot[r0 + q] : 0;
+    int nc = 0;
+#pragma unroll
+    for (int q = 0; q < kBucketRegRoutes; ++q) nc += sv[q] < 0 ? 1 : 0;
+    int tot;
+    int ci = block_exclusive_scan(nc, s_wave, tot);
+#pragma unroll
+    for (int q = 0; q < kBucketRegRoutes; ++q)
+      if (sv[q] < 0 && ci < Mk) {
+        cold_list[ci] = r0 + q;
+        if (u_cold_routes) u_cold_routes[ci] = r0 + q;
+        ++ci;
+      }
+    running_c = tot;
+  } else {
+    for (int r0 = 0; r0 < Mk; r0 += blockDim.x) {
+      const int r = r0 + tid;
+      const int j = r0 / bd;
+      int sl = 0;
+#pragma unroll
+      for (int i = 0; i < kBucketRegRoutes; ++i) sl = i == j ? s_r[i] : sl;
+      const int cold = r < Mk && (j < kBucketRegRoutes ? sl : route_slot[r]) < 0 ? 1 : 0;
+      int tot;
+      const int ci = running_c + block_exclusive_scan(cold, s_wave, tot);
+      if (cold && ci < Mk) {
+        cold_list[ci] = r;
+        if (u_cold_routes) u_cold_routes[ci] = r;
+      }
+      running_c += tot;
+    }
   }
   if (tid == 0) {
     meta[1] = running_c;
@@ -395,11 +480,34 @@ __global__ __launch_bounds__(kBucketThreads) void k_topk_bucket(
   __shared__ BucketSmem sm;
   if (logits != nullptr) {
     const int nw = blockDim.x >> 6;
+    // one workgroup doing both stages with the bucketing reading the top-k's ids: the top-k
+    // goes to LDS (no global round trip), then to the outputs
+    const bool lds = do_bucket && gridDim.x == 1 && M <= nw && k <= kMaxTopK && ids == topk_ids;
+    int32_t* oid = lds ? sm.tk_ids : topk_ids;
+    float* ow = lds ? sm.tk_w : topk_w;
+    // ... and the expert map to LDS: requested before the top-k (one entry a thread), stored
+    // after it, so that its latency overlaps the top-k
+    const bool map_lds = lds && e2s != nullptr && E <= (int)blockDim.x;
+    const int e2v = map_lds && (int)threadIdx.x < E ? e2s[threadIdx.x] : 0;
     for (int m = blockIdx.x * nw + (threadIdx.x >> 6); m < M; m += nw * gridDim.x)
-      topk_token(logits + (size_t)m * E, E, k, topk_ids + (size_t)m * k, topk_w + (size_t)m * k,
+      topk_token(logits + (size_t)m * E, E, k, oid + (size_t)m * k, ow + (size_t)m * k,
                  router_parts(M, E), (size_t)M * E);
     if (!do_bucket) return;
-    __syncthreads();  // this workgroup's ids are visible to it from here on
+    if (map_lds && (int)threadIdx.x < E) sm.e2s[threadIdx.x] = e2v;
+    // this workgroup's ids are visible to it from here on (in LDS, or in global memory: then the
+    // barrier waits for the stores)
+    if (lds)
+      lds_barrier();
+    else
+      __syncthreads();
+    if (lds) {
+      for (int i = threadIdx.x; i < Mk; i += blockDim.x) {
+        topk_ids[i] = sm.tk_ids[i];
+        topk_w[i] = sm.tk_w[i];
+      }
+      ids = sm.tk_ids;
+      if (map_lds) e2s = sm.e2s;
+    }
   }
   if (blockIdx.x != 0) return;
   bucket_stage(sm, ids, Mk, E, S, e2s, route_slot, ws_perm, meta, dist, nd_max, items, n_items_max,
@@ -1823,12 +1931,6 @@ __device__ __forceinline__ int div_m(int n, uint32_t m) {
 __device__ __forceinline__ void unit_share(int w, uint32_t mg, int U, int& lo, int& n) {
   lo = div_m(w * U, mg);
   n = div_m((w + 1) * U, mg) - lo;
-}
-// Workgroup barrier ordering LDS only: global loads in flight stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 // v clamped to [lo, hi]; lo when the range is empty
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return max(min(v, hi), lo); }
