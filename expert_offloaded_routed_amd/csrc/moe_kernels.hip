@@ -2068,12 +2068,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     __syncthreads();  // the logits
     route_token_small_v(rt, ra, s_logit[lc], ra.e2s != nullptr ? e2v : lc);
     __syncthreads();
-    if (wg == 0) {
-      write_routes(rt, ra.k, ra.topk_ids, ra.topk_w, ra.cold_count, ra.cold_routes, nullptr);
-      write_table(rt, ra.k, rw);
-    }
   } else {
-    route_prologue(rt, ra, rw, wg == 0);
+    route_prologue(rt, ra, rw, false);
     if ((int)threadIdx.x < n_x) reinterpret_cast<uint4*>(xs)[threadIdx.x] = xr;
   }
   const int nd = rt.nd;
@@ -2100,14 +2096,33 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 
   uint32_t sg[NUG][NEG], sd[NUD][NED];
   uint4 cg[NUG][NEG], cd[NUD][NED];
+  // the hot experts of this wave's units and entries, then their slots: every LDS read issued
+  // before any is used
+  int dg[NUG], t2g[NUG], exq[NED], slg[NUG], sle[NED];
+#pragma unroll
+  for (int ug = 0; ug < NUG; ++ug) {
+    const int u = clampi(gu_lo + clampi(ug, 0, ngu - 1), 0, max(Ug - 1, 0));
+    dg[ug] = div_m(u, dv.ugpe);
+    t2g[ug] = u - dg[ug] * ugpe;
+  }
+#pragma unroll
+  for (int e = 0; e < NED; ++e) exq[e] = div_m(dq0 + clampi(e, 0, ndq - 1), dv.np2);
+#pragma unroll
+  for (int ug = 0; ug < NUG; ++ug) slg[ug] = slot_of(dg[ug]);
+#pragma unroll
+  for (int e = 0; e < NED; ++e) sle[e] = slot_of(exq[e]);
+  // (each is the same for the whole wave: in scalar registers, the image bases are formed on
+  // the scalar unit)
+#pragma unroll
+  for (int ug = 0; ug < NUG; ++ug) slg[ug] = __builtin_amdgcn_readfirstlane(slg[ug]);
+#pragma unroll
+  for (int e = 0; e < NED; ++e) sle[e] = __builtin_amdgcn_readfirstlane(sle[e]);
   const uint8_t* gtb[NUG];
   int gilf[NUG];
 #pragma unroll
   for (int ug = 0; ug < NUG; ++ug) {
-    const int u = clampi(gu_lo + clampi(ug, 0, ngu - 1), 0, max(Ug - 1, 0));
-    const int d = div_m(u, dv.ugpe), t2 = u - d * ugpe;
-    gtb[ug] = slots + (size_t)slot_of(d) * image_bytes + (size_t)(t2 >> 1) * gu_tile_bytes;
-    gilf[ug] = 16 * (t2 & 1) + gil;
+    gtb[ug] = slots + (size_t)slg[ug] * image_bytes + (size_t)(t2g[ug] >> 1) * gu_tile_bytes;
+    gilf[ug] = 16 * (t2g[ug] & 1) + gil;
   }
   const uint8_t* dtb[NUD][NED];
   int dix[NUD][NED], dsw[NUD][NED];
@@ -2118,9 +2133,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
     for (int e = 0; e < NED; ++e) {
       const int q = dq0 + clampi(e, 0, ndq - 1);
-      const int ex = div_m(q, dv.np2);
-      const int s = min(2 * (q - ex * np2) + half, ks - 1);
-      dtb[ud][e] = slots + (size_t)slot_of(ex) * image_bytes + gu_bytes + (size_t)(u >> 1) * dn_tile_bytes;
+      const int s = min(2 * (q - exq[e] * np2) + half, ks - 1);
+      dtb[ud][e] = slots + (size_t)sle[e] * image_bytes + gu_bytes + (size_t)(u >> 1) * dn_tile_bytes;
       dix[ud][e] = s < full ? s * 64 + il : full * 64 + min(il, 16 * rem - 1);
       dsw[ud][e] = (s >> 2) * 64 + il;
     }
@@ -2143,6 +2157,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
       const int b = min(2 * (gp0 + clampi(e, 0, ngp - 1)) + half, nb - 1);
       cg[ug][e] = reinterpret_cast<const uint4*>(gtb[ug])[b * 64 + gilf[ug]];
     }
+  // Workgroup 0 publishes the routes, the cold report and the table (from its LDS copy) only
+  // now: stores count with the loads in flight, so before the gate/up requests they would hold
+  // those back until they had completed.
+  if (wg == 0) {
+    write_routes(rt, ra.k, ra.topk_ids, ra.topk_w, ra.cold_count, ra.cold_routes, nullptr);
+    write_table(rt, ra.k, rw);
+  }
   // The call id and the poison word (thread 0), needed only when h is stored: requested behind
   // the gate/up weights, so that nothing waits for them before.
   uint64_t callw = 0;
