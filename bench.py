@@ -746,17 +746,21 @@ def bench_slots8dev(args):
     nplan = torch.zeros((steps,), dtype=torch.int32, device="cuda")
     ev = [[B.event_create() for _ in range(steps)] for _ in range(3)]  # plan, layer, copy
 
-    def build(cache, lag, refills):
+    def build(cache, lag, refills, serial=False):
+        # serial: the step's refills are copied on the compute stream right after the policy
+        # kernel, before the layer
         def step(t):
             cache.step(ids[(t - 1) % steps], k, maps[t], plans[t], nplan[t:t + 1], stream=comp)
             B.event_record(ev[0][t], comp)
-            if refills and t - lag >= 0:
+            if serial:
+                cache.copy(nplan[t:t + 1], plans[t], bank, slots, stream=comp)
+            elif refills and t - lag >= 0:
                 B.stream_wait_event(comp, ev[2][t - lag])
             B.moe_route(shape, xs[t], 1, wr, biases[t], ids[t], w[t], ws, stream=comp)
             B.moe_experts_forward(shape, xs[t], 1, ids[t], w[t], maps[t], slots, y[t], None, None, ws,
                                   stream=comp)
             B.event_record(ev[1][t], comp)
-            if refills:
+            if refills and not serial:
                 B.stream_wait_event(copy, ev[0][t])
                 if t >= 1:
                     B.stream_wait_event(copy, ev[1][t - 1])
@@ -767,7 +771,7 @@ def bench_slots8dev(args):
             with torch.cuda.graph(g, stream=comp):
                 for t in range(steps):
                     step(t)
-                if refills:
+                if refills and not serial:
                     B.stream_wait_event(comp, ev[2][steps - 1])
         torch.cuda.synchronize()
         return g
@@ -832,45 +836,65 @@ def bench_slots8dev(args):
     interference["dma_copy_gbs"] = round(4 * 2 * img / (B.event_elapsed_ms(e0, e1) * 1e-3) / 1e9, 2)
     del dma_dst, g0
     log(f"interference: {interference}")
-    slots.copy_(L.device_slots(bank_np, init, S))
-    ids.fill_(-1)
-    cache = B.DeviceCache(shape, lag_steps=lag, initial_slot_expert=init, stream=comp)
-    g = build(cache, lag, True)
-    with torch.cuda.stream(comp):
-        g.replay()  # warm-up replay (the cache state carries over to the timed one)
-    torch.cuda.synchronize()
-    s1 = cache.stats()
-    t0, t1 = B.event_create(timing=True), B.event_create(timing=True)
-    B.event_record(t0, comp)
-    with torch.cuda.stream(comp):
-        g.replay()
-    B.event_record(t1, comp)
-    B.event_synchronize(t1)
-    ms = B.event_elapsed_ms(t0, t1)
-    s2 = cache.stats()
-    d = {f: s2[f] - s1[f] for f in s1}  # counters of the timed replay
-    refills = d["refills"]
-    stall_ms = max(0.0, ms - steps * t_hot)
-    copy_ms_total = refills / 2.0 * t_copy
+    def run_mode(serial):
+        # the same lag in both modes: it bounds the refill rate (at most 2 pending), so that both
+        # move the same experts; in-stream the copies are simply done by then
+        lag_m = lag
+        slots.copy_(L.device_slots(bank_np, init, S))
+        ids.fill_(-1)
+        cache = B.DeviceCache(shape, lag_steps=lag_m, initial_slot_expert=init, stream=comp)
+        g = build(cache, lag_m, True, serial)
+        with torch.cuda.stream(comp):
+            g.replay()  # warm-up replay (the cache state carries over to the timed one)
+        torch.cuda.synchronize()
+        s1 = cache.stats()
+        t0, t1 = B.event_create(timing=True), B.event_create(timing=True)
+        B.event_record(t0, comp)
+        with torch.cuda.stream(comp):
+            g.replay()
+        B.event_record(t1, comp)
+        B.event_synchronize(t1)
+        ms = B.event_elapsed_ms(t0, t1)
+        s2 = cache.stats()
+        del g
+        torch.cuda.synchronize()
+        d = {f: s2[f] - s1[f] for f in s1}  # counters of the timed replay
+        stall_ms = max(0.0, ms - steps * t_hot)
+        copy_ms_total = d["refills"] / 2.0 * t_copy
+        return {"tok_s": round(steps / (ms / 1e3), 1), "ms_per_step": round(ms / steps, 5),
+                "lag_steps": lag_m, "hit_rate": round(d["hits"] / max(1, d["routes"]), 4),
+                "refills": d["refills"], "stall_us_total": round(stall_ms * 1e3, 1),
+                "overlap": (round(1.0 - stall_ms / copy_ms_total, 4) if copy_ms_total > 0 and not serial
+                            else None)}
+
+    side = run_mode(False)
+    serial = run_mode(True)
+    log(f"refills on a side stream: {side}; in the compute stream: {serial}")
+    best = serial if serial["tok_s"] > side["tok_s"] else side
+    best_serial = best is serial
     out = {
         "metric": "MoE-layer decode with an 8-slot GPU-resident expert cache: tok/s, hit rate, refill overlap",
-        "value": round(steps / (ms / 1e3), 1), "unit": "tok/s", "n_gpus": 1, "steps": steps,
-        "warmup": steps, "ms_per_step": round(ms / steps, 5), "higher_is_better": True, "dtype": "bf16",
+        "value": best["tok_s"], "unit": "tok/s", "n_gpus": 1, "steps": steps,
+        "warmup": steps, "ms_per_step": best["ms_per_step"], "higher_is_better": True, "dtype": "bf16",
         "data": "synthetic (seeded MXFP4 experts, Zipf(1.1) prior drifting every 32 steps)",
         "config": {"workload": "gptoss20b_8slots_device_cache", "hidden": H, "inter": wl.inter,
                    "n_experts": E, "top_k": k, "slots": S, "policy": "LRU", "max_refills_per_step": 2,
-                   "lag_steps": lag, "observes": "the previous step's routes, from device memory",
+                   "lag_steps": best["lag_steps"], "observes": "the previous step's routes, from device memory",
+                   "refills": ("copy kernel in the compute stream, before the step's layer" if best_serial
+                               else "copy kernel on a side stream"),
                    "timed": "one HIP graph of the steps: policy kernel, router, top-k, gate/up, down "
-                            "on the compute stream; copy kernel on a side stream"},
-        "hit_rate": round(d["hits"] / max(1, d["routes"]), 4), "refills": refills,
+                            "on the compute stream"},
+        "hit_rate": best["hit_rate"], "refills": best["refills"],
         "hot_step_us_no_refills": round(t_hot * 1e3, 2),
         "refill_batch_ms": round(t_copy, 4),
         "refill_gbs": round(2 * img / (t_copy * 1e-3) / 1e9, 2),
-        "stall_us_total": round(stall_ms * 1e3, 1),
+        "stall_us_total": best["stall_us_total"],
         "hot_step_us_beside_refill_copies": interference,
-        "overlap": round(1.0 - stall_ms / copy_ms_total, 4) if copy_ms_total > 0 else None,
+        "overlap": side["overlap"],
+        "modes": {"side_stream": side, "in_stream": serial},
         "note": "GPU slots (105.75 MB) fit in the 256 MB Infinity Cache: hot-path bytes are cache-resident",
     }
+    lag = best["lag_steps"]
     if args.cpu_steps > 0:
         from oracle import layer as O
         from oracle.cache_policy import SlotCachePolicy

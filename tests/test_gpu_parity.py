@@ -1048,17 +1048,19 @@ def test_hybrid_layer_hot_gpu_plus_cold_host_equals_full(which, M, e512):
     staging.close()
 
 
-def test_device_cache_in_one_graph_matches_oracle_policy():
+@pytest.mark.parametrize("serial", [False, True])
+def test_device_cache_in_one_graph_matches_oracle_policy(serial):
     """The GPU-resident slot cache over 256 decode steps of the 8-slot GPT-OSS-20B-shaped layer,
     captured as one HIP graph: per step, the policy kernel (observing the previous step's
     routes from device memory) publishes the map and plans <= 2 refills; the router, top-k and
     hot experts run with that map on the compute stream; the copy kernel moves the planned
-    experts from device-mapped pinned memory into their slots on a side stream, after the
-    previous step's layer (the last reader of the victims), and the layer of step t + L waits
-    for it.  Maps, plans, counters and cold counts equal the oracle policy's replay bit for bit;
-    y_hot matches the oracle at every step."""
+    experts from device-mapped pinned memory into their slots either on a side stream, after
+    the previous step's layer (the last reader of the victims), with the layer of step t + L
+    waiting for it (L = 3), or in the compute stream right after the policy kernel (L = 1).
+    Maps, plans, counters and cold counts equal the oracle policy's replay bit for bit; y_hot
+    matches the oracle at every step."""
     wl = synthetic.WORKLOADS["gptoss20b_8slots"]
-    steps, lag = 256, 3
+    steps, lag = 256, (1 if serial else 3)
     E, k, S, H = wl.n_experts, wl.top_k, wl.n_slots, wl.hidden
     shape = _shape(wl, S)
     say("device cache: generating 32 experts")
@@ -1090,12 +1092,16 @@ def test_device_cache_in_one_graph_matches_oracle_policy():
     def step(t):
         cache.step(ids[(t - 1) % steps], k, maps[t], plans[t], nplan[t:t + 1], stream=comp)
         B.event_record(ev_plan[t], comp)
-        if t - lag >= 0:
+        if serial:  # the refills land before this step's layer (their experts are not in its map)
+            cache.copy(nplan[t:t + 1], plans[t], bank, slots, stream=comp)
+        elif t - lag >= 0:
             B.stream_wait_event(comp, ev_copy[t - lag])  # refills visible now have landed
         B.moe_route(shape, xs_d[t], 1, wr_d, biases_d[t], ids[t], w[t], ws, stream=comp)
         B.moe_experts_forward(shape, xs_d[t], 1, ids[t], w[t], maps[t], slots, y[t], cold[t],
                               cold_routes[t], ws, stream=comp)
         B.event_record(ev_layer[t], comp)
+        if serial:
+            return
         B.stream_wait_event(copy, ev_plan[t])
         if t >= 1:
             B.stream_wait_event(copy, ev_layer[t - 1])  # the victims' last readers are done
@@ -1108,7 +1114,8 @@ def test_device_cache_in_one_graph_matches_oracle_policy():
         with torch.cuda.graph(g, stream=comp):
             for t in range(steps):
                 step(t)
-            B.stream_wait_event(comp, ev_copy[steps - 1])  # join the copy stream
+            if not serial:
+                B.stream_wait_event(comp, ev_copy[steps - 1])  # join the copy stream
     torch.cuda.synchronize()
     say("device cache: replay")
     with torch.cuda.stream(comp):
