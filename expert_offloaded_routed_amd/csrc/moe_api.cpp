@@ -258,7 +258,8 @@ static moe_status run_experts(const moe_shape* sh, const uint16_t* x, int M, Rou
     e = p.grouped ? launch_down_grouped(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
                                         at<uint8_t>(ws, W.hq), at<float>(ws, W.pdn), y, res, stream)
                   : launch_down(M, sh->hidden, sh->inter, slots, L, p, ra, rw,
-                                at<uint16_t>(ws, W.hq), at<float>(ws, W.pdn), y, res, stream);
+                                at<uint16_t>(ws, W.hq), at<uint64_t>(ws, W.pw),
+                                at<uint32_t>(ws, W.dncall), y, res, stream);
     if (e != hipSuccess) return hip_fail(e, "down launch");
   }
   if (marks && (e = record_mark(marks[3], stream)) != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -457,8 +458,8 @@ moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n) {
     *n = layer_decode_router_inside(L, shape->n_experts) ? 1 : 2;  // [router,] fused layer
   else if (p.grouped)
     *n = 5;                     // router, top-k / bucket, gate/up, down, combine
-  else  // router, [top-k / bucket,] gate/up, down + combine [split: down, combine]
-    *n = (p.prologue ? 3 : 4) + (down_split(L, M, shape->top_k, shape->n_experts) > 1 ? 1 : 0);
+  else
+    *n = p.prologue ? 3 : 4;    // router, [top-k / bucket,] gate/up, down + combine
   return ok();
 }
 

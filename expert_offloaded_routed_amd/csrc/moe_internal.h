@@ -142,6 +142,9 @@ __host__ __device__ inline int router_parts(int M, int E) {
 struct WsLayout {
   size_t meta;           // i32 [kMetaWords], offset 0
   size_t hf;             // u64 [kFusedMaxK][kMaxInter / 2]: {h pair, call tag}, fixed offset
+  size_t dncall;         // u32 [kMaxHidden / 16]: split down GEMV, call id per row tile, fixed offset
+  size_t pw;             // u64 [16*k][H]: the split down GEMV's {row value, tag} words, at an
+                         // offset fixed by the shape (only when the shape can split)
   size_t logits;         // f32 [router_parts(M, E)][M][E]
   size_t route_slot;     // i32 [M*k]
   size_t counts;         // i32 [E]
@@ -174,6 +177,15 @@ inline int n_items_max(int Mk, int E) {
   return nd + Mk / kItemRoutes;
 }
 
+// Shapes whose few-token down GEMV may share each row tile between two workgroups: one K part
+// (I <= 1024) and at most kSplitMaxTiles row tiles (H <= 2048); calls of at most kSplitMaxTokens
+// tokens, whose handed-over rows fit the workspace's fixed word region.
+constexpr int kSplitMaxTiles = 128;
+constexpr int kSplitMaxTokens = 16;
+inline bool down_split_possible(const ImageLayout& L) {
+  return L.dn_ks <= 8 && L.dn_tiles <= kSplitMaxTiles;
+}
+
 inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   WsLayout W;
   const ImageLayout L = image_layout(H, I);
@@ -182,6 +194,8 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   size_t o = 0;
   W.meta = o;        o = align256(o + 4 * (size_t)kMetaWords);
   W.hf = o;          o = align256(o + kFusedHBytes);
+  W.dncall = o;      o = align256(o + 4 * (size_t)(kMaxHidden / 16));
+  W.pw = o;          o = align256(o + (down_split_possible(L) ? 8 * (size_t)kSplitMaxTokens * k * H : 0));
   W.logits = o;      o = align256(o + 4 * (size_t)router_parts(M, E) * M * E);
   W.route_slot = o;  o = align256(o + 4 * Mk);
   W.counts = o;      o = align256(o + 4 * (size_t)E);
@@ -313,11 +327,11 @@ ExpertPlan plan_experts(const ImageLayout& L, int M, int E, int k);
 hipError_t launch_gateup(const uint16_t* x, int M, int H, int I, const uint8_t* slots,
                          const ImageLayout& L, const ExpertPlan& p, const RouteArgs& ra,
                          const RouteWs& rw, uint16_t* hbuf, hipStream_t s);
-// Workgroups per tile of the down GEMV (1, or 2 with k_combine forming y: one launch more).
+// Workgroups per tile of the down GEMV (1, or 2 handing rows over through the workspace).
 int down_split(const ImageLayout& L, int M, int k, int E);
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                       const uint16_t* hbuf, float* pdn, float* y, Residual res, hipStream_t s);
+                       const uint16_t* hbuf, uint64_t* pw, uint32_t* dncall, float* y, Residual res, hipStream_t s);
 // The expert kernels of the other formats (moe_formats.hip), after the bucketing kernel:
 // gate/up + SiLU into hbuf (bf16 [M*k][I]); down, route partials in pdn ([M*k][H] fp32) and the
 // ordered combine into y (and the residual).

@@ -1417,6 +1417,8 @@ __device__ __forceinline__ float dn_route_dot_h(const uint4 (&c)[TM], const uint
 // Sum over the 4 lanes of a row (l, l^16, l^32, l^48); every one of them gets it.
 __device__ __forceinline__ float dn_row_sum(float v) { return pair_sum32(pair_sum16(v)); }
 
+// Rounds of a gather of words handed over by value at most (each about a load round trip).
+constexpr int kHandSpins = 1 << 13;
 constexpr int kDnNR = 2;   // routes of an expert the down GEMV forms together (h in LDS)
 constexpr int kDnAll = 4;  // hot experts of a wave whose weights it requests all at once
 
@@ -1428,19 +1430,26 @@ __host__ __device__ __forceinline__ int dn_part_steps(int ks, int kparts) {
 // grid = (H/16 tiles, S), 8 waves.  Workgroup (tile, p) takes the hot experts p, p + S, ...;
 // its waves own (expert, K part) pairs: with kparts K parts, 8/kparts of its experts per pass,
 // wave w taking the experts of its list at w % (8/kparts) + (8/kparts)*i and K part
-// w / (8/kparts).  With S = 1 each route's partial rows go to LDS and the workgroup then forms
-// y[m][rows] = sum over j ascending (hot routes) of w[m,j] * (its K parts, in order): no other
-// workgroup is involved.  With S > 1 (one K part) each route's rows go to pdn[route][rows]
-// instead, and k_combine forms y with the same arithmetic, so that twice as many compute units
-// share the experts.  h comes from an LDS copy when every route's h fits (h_lds), else straight
-// from the workspace.  The route table comes from the workspace.
+// w / (8/kparts).  Each route's partial rows go to LDS; workgroup (tile, 0) then forms
+// y[m][rows] = sum over j ascending (hot routes) of w[m,j] * (its K parts, in order).  With
+// S = 2 (one K part; the grid is resident at once, one workgroup per compute unit) workgroup
+// (tile, 1) hands its routes' rows to (tile, 0) by value: 64-bit words {row value, tag} with
+// device-scope stores, the tag being the tile's call id + 1 from the workspace; (tile, 0) polls
+// the words of its partner's routes (bounded, like the fused kernel's gather of h) into its
+// LDS, forms y, and then advances the tile's call id (its partner has read it: its words carry
+// it).  A gather that runs out flags MOE_DEVERR_HANDOFF, writes NaN rows and poisons the
+// workspace (the poison word is the fused kernel's).  h comes from an LDS copy when every
+// route's h fits (h_lds), else straight from the workspace.  The route table comes from the
+// workspace.
 template <int TM>
 __global__ __launch_bounds__(512) void k_down_gemv(
     int H, int I, const uint8_t* __restrict__ slots, size_t image_bytes, size_t gu_bytes,
     size_t dn_tile_bytes, size_t dn_code_bytes, int ks, int full, int rem, int nsw, int nb,
     int kparts, int h_lds, RouteArgs ra, RouteWs rw, const uint16_t* __restrict__ hbuf,
-    float* __restrict__ y, Residual res, float* __restrict__ pdn) {
+    float* __restrict__ y, Residual res, uint64_t* __restrict__ pw, uint32_t* __restrict__ dncall) {
   extern __shared__ __align__(16) uint8_t smem[];  // [h copy (h_lds)] [parts: Mk x kparts x 16]
+  __shared__ uint32_t s_dcall;                     // split: this tile's call id
+  __shared__ int s_dlate;                          // split: the gather ran out, or a poisoned workspace
   const int tile = blockIdx.x;
   const int Mk = ra.M * ra.k;
   const int lane = threadIdx.x & 63;
@@ -1448,8 +1457,16 @@ __global__ __launch_bounds__(512) void k_down_gemv(
   const int g = lane >> 4;
   const int sl = 8 / kparts;
   const int kh = wave / sl;
-  // this wave's experts: es0, es0 + sl, ... (es0 the first, sl the stride in the hot list)
-  const bool split = gridDim.y > 1;  // (then kparts == 1 and the rows go to pdn)
+  // this wave's experts: es0, es0 + sl_all, ... (the first and the stride in the hot list)
+  const bool split = gridDim.y > 1;  // (then kparts == 1)
+  const bool helper = split && blockIdx.y != 0;
+  if (split && threadIdx.x == 0) {  // (requested first: its latency overlaps the h copy's)
+    const uint32_t c0 = __hip_atomic_load(&dncall[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t pz = __hip_atomic_load(reinterpret_cast<uint32_t*>(&rw.meta[kMetaPoison]),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_dcall = c0;
+    s_dlate = pz != 0u ? 1 : 0;
+  }
   const int es0 = (int)blockIdx.y + (int)gridDim.y * (wave % sl);
   const int sl_all = (int)gridDim.y * sl;
   const int spw = dn_part_steps(ks, kparts);
@@ -1479,14 +1496,17 @@ __global__ __launch_bounds__(512) void k_down_gemv(
   dn_load_steps<TM>(sec + (size_t)slot0 * image_bytes, dn_code_bytes, s0, ks, full, rem, nsw, lane, c, sw);
   const uint16_t* hsrc = h_lds ? reinterpret_cast<const uint16_t*>(smem) : hbuf;
   float* parts = reinterpret_cast<float*>(smem + (h_lds ? (size_t)(n_h + 63) / 64 * 1024 : 0));
-  // a route's partial rows (lanes < 16): to LDS, or with the experts split to pdn
+  __syncthreads();
+  const uint32_t tag = s_dcall + 1u;  // (split)
+  // a route's partial rows (lanes < 16): to LDS, or from the helper workgroup to its partner
   auto put = [&](int route, float acc) {
-    if (split)
-      pdn[(size_t)route * H + tile * kDnRows + lane] = acc;
+    if (helper)
+      __hip_atomic_store(&pw[(size_t)route * H + tile * kDnRows + lane],
+                         (uint64_t)__float_as_uint(acc) | ((uint64_t)tag << 32), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     else
       parts[((size_t)route * kparts + kh) * kDnRows + lane] = acc;
   };
-  __syncthreads();
   bool fast = false;
   if constexpr (TM <= 4) {
     // A short K part and at most 64 hot experts for this wave: no route-table read on the way
@@ -1711,8 +1731,53 @@ __global__ __launch_bounds__(512) void k_down_gemv(
       for (int q = 0; q < TM / 4; ++q) sw[q] = swn[q];
     }
   }
-  if (split) return;  // (k_combine forms y)
+  if (helper) return;  // (its stores complete before the workgroup ends)
+  if (split) {
+    // the partner's experts are the odd entries of the hot list: wave w takes entries
+    // 1 + 2w, 1 + 2w + 16, ..., four routes at a time (lane: route lane / 16, row lane % 16)
+    bool late = false;
+    if (s_dlate == 0) {
+      const int lr = lane & 15, lj = lane >> 4;
+      for (int dh = 1 + 2 * wave; dh < nd && !late; dh += 16) {
+        const int4 dd = rw.dist[dh];
+        const int off = dd.y;
+        const int cnt = off >= 0 && dd.z > 0 && off + dd.z <= Mk ? dd.z : 0;
+        for (int j0 = 0; j0 < cnt && !late; j0 += 4) {
+          const int j = j0 + lj;
+          const int route = rw.perm[off + min(j, cnt - 1)];
+          const uint64_t* src = pw + (size_t)route * H + tile * kDnRows + lr;
+          bool ok = j >= cnt;
+          uint64_t v = 0;
+          for (int spins = 0;; ++spins) {
+            if (!ok) {
+              v = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              ok = (uint32_t)(v >> 32) == tag;
+            }
+            if (__ballot(!ok) == 0ull) break;
+            if (spins + 1 >= kHandSpins) {
+              late = true;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          if (j < cnt) parts[(size_t)route * kDnRows + lr] = __uint_as_float((uint32_t)v);
+        }
+      }
+    }
+    if (late && lane == 0) s_dlate = 2;
+  }
   __syncthreads();
+  if (split && threadIdx.x == 0) {
+    // every word of the partner carried this call's id: advance it for the next call; after a
+    // lost gather, poison the workspace instead (the partner may not have read the id yet)
+    if (s_dlate != 0) atomicOr(&rw.meta[kMetaErr], kErrHandoff);
+    if (s_dlate == 2)
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(&rw.meta[kMetaPoison]), 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else if (s_dlate == 0)
+      __hip_atomic_store(&dncall[tile], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const bool lost = split && s_dlate != 0;
   for (int idx = threadIdx.x; idx < ra.M * kDnRows; idx += blockDim.x) {
     const int m = idx / kDnRows;
     const int r = idx - m * kDnRows;
@@ -1739,6 +1804,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
       for (int u = 0; u < 8; ++u)
         if (hot[u]) acc = fmaf(wv[u], pv[u], acc);
     }
+    if (lost) acc = __uint_as_float(0x7FC00000u);  // never a silently wrong value
     y[(size_t)m * H + tile * kDnRows + r] = acc;
     residual_store(res, (size_t)m * H + tile * kDnRows + r, acc);
   }
@@ -1916,7 +1982,6 @@ __global__ __launch_bounds__(256) void k_down_mx(
 constexpr int kFusedWaves = 16;
 constexpr int kFusedThreads = kFusedWaves * 64;
 constexpr int kFusedMaxK = 16;      // routes (hot experts) of the token at most
-constexpr int kHandSpins = 1 << 13; // gather rounds at most (each about a load round trip)
 static_assert(kFusedMaxK * kMaxInter * 4 == kFusedHBytes, "tagged h region of the workspace");
 
 // n / d by a multiply: m = floor((2^32 - 1) / d) + 1 (0 for d = 1) gives floor(n * m / 2^32) =
@@ -3057,23 +3122,26 @@ static hipError_t launch_down_mx(int M, int H, int I, const uint8_t* slots, cons
   return hipGetLastError();
 }
 
-// Workgroups per down tile of the GEMV path: 2 (the hot experts split between them, k_combine
-// forming y) when the tiles fill at most half of the compute units, K is one part and there are
-// enough hot experts to share, else 1.  The combine's own launch (about 5 us between dependent
-// kernels) outweighs the split with fewer experts, hence the bound: at least 64 possible hot
-// experts, 8 a wave of one workgroup (on the E = 512, k = 10 stack: a gain at 8 tokens, a loss
-// at 4).
-constexpr int kDnSplitMinExperts = 64;
+// Workgroups per down tile of the GEMV path: 2 (the hot experts split between them, one handing
+// its rows to the other) when the tiles fill at most half of the compute units (the grid is
+// then resident at once: one workgroup per compute unit), K is one part and there are enough
+// hot experts to share, else 1.
+constexpr int kDnSplitMinExperts = 16;
 int down_split(const ImageLayout& L, int M, int k, int E) {
   const int cus = device_cus();
   const int nd_max = M * k < E ? M * k : E;
   const bool one_part = L.dn_ks <= 8;
-  return one_part && nd_max >= kDnSplitMinExperts && cus > 0 && 2 * L.dn_tiles <= cus ? 2 : 1;
+  // the row words of a split call live in a region sized for kSplitMaxTokens tokens
+  return one_part && down_split_possible(L) && M <= kSplitMaxTokens &&
+                 nd_max >= kDnSplitMinExperts && cus > 0 && 2 * L.dn_tiles <= cus
+             ? 2
+             : 1;
 }
 
 hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLayout& L,
                        const ExpertPlan& p, const RouteArgs& ra, const RouteWs& rw,
-                       const uint16_t* hbuf, float* pdn, float* y, Residual res, hipStream_t s) {
+                       const uint16_t* hbuf, uint64_t* pw, uint32_t* dncall, float* y, Residual res,
+                       hipStream_t s) {
   (void)p;
   const int Mk = M * ra.k;
   // long K in two parts (4 experts per pass, half the steps per wave), short K in one (8
@@ -3081,26 +3149,22 @@ hipError_t launch_down(int M, int H, int I, const uint8_t* slots, const ImageLay
   const int kparts = L.dn_ks > 8 ? 2 : 1;
   const int spw = dn_part_steps(L.dn_ks, kparts);
   const int S = down_split(L, M, ra.k, ra.E);
-  const size_t parts = S > 1 ? 0 : (size_t)Mk * kparts * kDnRows * 4;
+  const size_t parts = (size_t)Mk * kparts * kDnRows * 4;
   const size_t hcopy = ((size_t)Mk * I / 8 + 63) / 64 * 1024;
   const bool h_lds = hcopy + parts <= kDownLdsBytes;
   const size_t lds = (h_lds ? hcopy : 0) + parts;
-  if (lds > kDownLdsBytes || spw > 16 || (S > 1 && pdn == nullptr)) return hipErrorInvalidValue;
+  if (lds > kDownLdsBytes || spw > 16 || (S > 1 && (pw == nullptr || dncall == nullptr)))
+    return hipErrorInvalidValue;
 #define MOE_DG(TM)                                                                                 \
   hipLaunchKernelGGL((k_down_gemv<TM>), dim3(L.dn_tiles, S), dim3(512), lds, s, H, I, slots,        \
                      L.image_bytes, L.gu_bytes, L.dn_tile_bytes, L.dn_code_bytes, L.dn_ks,          \
                      L.dn_full, L.dn_rem, L.dn_scale_words, L.nb_i, kparts, h_lds ? 1 : 0, ra, rw,  \
-                     hbuf, y, res, pdn)
+                     hbuf, y, res, pw, dncall)
   if (spw <= 4) MOE_DG(4);
   else if (spw <= 8) MOE_DG(8);
   else if (spw <= 12) MOE_DG(12);
   else MOE_DG(16);
 #undef MOE_DG
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return e;
-  const int threads = M * (H / 4);
-  hipLaunchKernelGGL(k_combine<16>, dim3((threads + 255) / 256), dim3(256), 0, s, M, ra.k, H, ra,
-                     rw, pdn, y, res);
   return hipGetLastError();
 }
 

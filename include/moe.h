@@ -260,10 +260,7 @@ moe_status moe_layer_forward_noalloc(const moe_shape* shape, const uint16_t* x, 
 /* Number of kernel launches moe_layer_forward makes for M tokens of this shape: 1 or 2 when
  * gate/up and down run as one launch (router inside it, or before it), 3 for one token or up to
  * 64 routes over at most 64 experts, 4 for the other calls below 64 tokens and for the formats
- * other than MXFP4, 5 on the grouped-GEMM path (M >= 64), 1 for M = 0; one more below 64 tokens
- * when the down GEMV shares the hot experts of each row tile between two workgroups (its tiles,
- * H/16, fill at most half of the compute units, I <= 1024 and M*k and E are at least 64), the
- * ordered combine then being its own launch.  For callers that budget graph nodes or time stages.  Writes *n; no
+ * other than MXFP4, 5 on the grouped-GEMM path (M >= 64), 1 for M = 0.  For callers that budget graph nodes or time stages.  Writes *n; no
  * device work. */
 moe_status moe_layer_launches(const moe_shape* shape, int32_t M, int32_t* n);
 

@@ -248,10 +248,10 @@ def test_e512_verify_half_resident(e512, M):
     e2s = np.full(wl.n_experts, -1, np.int32)
     e2s[slot_expert] = np.arange(wl.n_slots)
     shape = _shape(wl, wl.n_slots)
-    # one token: router + fused kernel; 4 tokens (40 routes): router, top-k / bucketing, gate/up,
-    # down + combine; 8 tokens (80 routes, at least 64 possible hot experts): the down GEMV
-    # shares each row tile's experts between two workgroups and the combine is its own launch
-    assert B.moe_layer_launches(shape, M) == {1: 2, 4: 4, 8: 5}[M]
+    # one token: router + fused kernel; 4 and 8 tokens: router, top-k / bucketing, gate/up, down
+    # + combine (the down GEMV shares each row tile's experts between two workgroups, which hand
+    # rows over through the workspace)
+    assert B.moe_layer_launches(shape, M) == {1: 2, 4: 4, 8: 4}[M]
     slots = e512.slots_for(slot_expert)
     buf = L.Buffers(shape, M)
     bias = synthetic.zipf_bias(wl)
@@ -828,6 +828,54 @@ def test_device_error_word_flags_bad_ids_and_slots(tiny):
                         buf.y, None, None, buf.ws)
     torch.cuda.synchronize()
     assert device_errors(buf.ws) == 0
+
+
+def test_split_down_poisoned_workspace_flags_and_writes_nan(e512):
+    """At 8 tokens on the E = 512 layer the down GEMV shares each row tile's hot experts between
+    two workgroups, one handing its routes' rows to the other in words tagged with the tile's
+    call id.  Against the oracle; then on a workspace whose poison word is set (what a lost
+    hand-over leaves) the call gathers nothing, writes NaN rows and flags MOE_DEVERR_HANDOFF,
+    without waiting; zero-filled again, the workspace gives bitwise the first result, twice.
+    Before that, one workspace serves 16 tokens (the most that split), 17 (which do not) and 3,
+    in turn, against the oracle."""
+    wl = e512.wl
+    counts = routed_counts(wl, 0, 256)
+    slot_expert = popularity_placement(counts, wl.n_slots)
+    e2s = np.full(wl.n_experts, -1, np.int32)
+    e2s[slot_expert] = np.arange(wl.n_slots)
+    shape = _shape(wl, wl.n_slots)
+    slots = e512.slots_for(slot_expert)
+    buf = L.Buffers(shape, 17)
+    bias = synthetic.zipf_bias(wl)
+    for M in (16, 17, 3):
+        say("split down: one workspace, M =", M)
+        x = synthetic.activations(wl, M, 60 + M)
+        ids, w = run_route(shape, x, e512.wr, bias, M, buf)
+        _, ids_ref, w_ref = compare_routes(ids, w, O.router_logits(x, e512.wr, bias), wl.top_k)
+        y, _, _ = run_experts(shape, x, ids_ref, w_ref, e2s, slots, buf, M)
+        close_enough(y, O.layer_forward(x, ids_ref, w_ref, e512.experts, e2s)["y_hot"],
+                     f"split down M={M}")
+    M = 8
+    x = synthetic.activations(wl, M, 77)
+    ids, w = run_route(shape, x, e512.wr, bias, M, buf)
+    _, ids_ref, w_ref = compare_routes(ids, w, O.router_logits(x, e512.wr, bias), wl.top_k)
+    say("split down: hand-over of rows between the two workgroups of each tile")
+    y, cc, _ = run_experts(shape, x, ids_ref, w_ref, e2s, slots, buf, M)
+    ref = O.layer_forward(x, ids_ref, w_ref, e512.experts, e2s)
+    close_enough(y, ref["y_hot"], "split down M=8")
+    say("split down: poisoned workspace")
+    buf.ws.view(torch.int32)[7] = 1  # the poison word of the workspace header
+    B.moe_experts_forward(shape, _dev(x), M, _dev(np.ascontiguousarray(ids_ref, np.int32)),
+                          _dev(np.ascontiguousarray(w_ref, np.float32)), _dev(e2s), slots, buf.y,
+                          buf.cold_count, buf.cold_routes, buf.ws)
+    torch.cuda.synchronize()
+    assert device_errors(buf.ws) == B.MOE_DEVERR_HANDOFF
+    assert torch.isnan(buf.y[:M]).all()
+    say("split down: zero-filled workspace")
+    buf.ws.zero_()
+    for _ in range(2):
+        y2, cc2, _ = run_experts(shape, x, ids_ref, w_ref, e2s, slots, buf, M)
+        assert cc2 == cc and np.array_equal(y2, y)
 
 
 @pytest.mark.parametrize("M", [1, 8])
