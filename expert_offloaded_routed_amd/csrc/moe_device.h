@@ -40,12 +40,19 @@ __device__ __forceinline__ float pair_sum32(float v) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Sum over the 64 lanes; every lane gets the same (deterministically ordered) total.
-__device__ __forceinline__ float wave_sum(float v) {
+// Sum over each row of 16 lanes (quad swaps, then the half-row and row mirrors); a lane's
+// result is deterministic, though lanes of a row may differ in the last bits.
+__device__ __forceinline__ float row_sum16(float v) {
   v += dpp_f<0xB1>(v);
   v += dpp_f<0x4E>(v);
   v += dpp_f<0x141>(v);
   v += dpp_f<0x140>(v);
+  return v;
+}
+
+// Sum over the 64 lanes; every lane gets the same (deterministically ordered) total.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
   v += swz_xor16_f(v);
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));

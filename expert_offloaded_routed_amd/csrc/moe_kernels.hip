@@ -2461,7 +2461,33 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     if (res.out != nullptr)
       res.out[row] = (uint16_t)f32_to_bf16_bits(__uint_as_float((uint32_t)xs[row] << 16) + acc_y);
   };
-  if (K <= T) {
+  if (K <= 4 && NUD * 8 <= kFusedWaves) {
+    // one row per wave (wave = unit * 8 + row): lane (slot t, wave w) takes that wave's sum of
+    // the row for hot expert slot t; the rows of 16 lanes sum over the waves; then the routes
+    // in ascending order
+    const int ud = wave >> 3, r = wave & 7;
+    if (ud < ndn) {  // (uniform)
+      const int t = lane >> 4, w = lane & 15;
+      float p = red_dn[((ud * K + min(t, K - 1)) * kFusedWaves + w) * 8 + r];
+      p = row_sum16(p);
+      float pt[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        pt[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), 16 * i));
+      float acc_y = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j < K) {
+          const int dj = s_dist_of_route[j];
+          float pj = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pj = dj == i ? pt[i] : pj;
+          if (rt.slot[j] >= 0) acc_y = fmaf(rt.w[j], pj, acc_y);
+        }
+      }
+      if (lane == 0) store_y(row0 + wave, acc_y);
+    }
+  } else if (K <= T) {
     if (wave == 0) {
       const int t = lane % T;
       const int rr = lane / T;  // unit * 8 + row
