@@ -2236,8 +2236,10 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     callw = __hip_atomic_load(reinterpret_cast<uint64_t*>(&hdr[kMetaCall]), __ATOMIC_RELAXED,
                               __HIP_MEMORY_SCOPE_AGENT);
   __builtin_amdgcn_sched_barrier(0);
-  // x in LDS for every wave (the gate/up loads stay in flight)
-  lds_barrier();
+  // x in LDS for every wave (the gate/up loads stay in flight); with the router inside, the
+  // router's own barrier has published it, so each wave starts on its gate/up bytes as soon as
+  // they land
+  if constexpr (!ROUTER) lds_barrier();
   // The gate/up block scales as floats for the scaled converter (while the codes are in
   // flight); zero for lanes whose block lies past K, which re-read a valid block and must add
   // nothing.
