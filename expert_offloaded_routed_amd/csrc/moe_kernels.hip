@@ -740,7 +740,7 @@ constexpr size_t kGuLdsBytes = 64 * 1024;  // LDS of a gate/up workgroup at most
 // One token over at most kFastE experts (the decode case), by every wave of the workgroup:
 // wave w ranks experts w, w + waves, ... (the number of keys above the expert's key, by a
 // ballot), the ranks meet in LDS (rt.cnt, unused by one-token tables otherwise), then wave 0
-// forms the weights and the route table in registers.  The keys are those of rank_key64, the
+// forms the route table and wave 1 the weights, in registers.  The keys are those of rank_key64, the
 // weights use the arithmetic of topk_rank, so the results are bitwise those of moe_route.  The
 // distinct hot experts of one token are its selected ids; their ascending order is a ballot
 // prefix count.  Contains a workgroup barrier (every thread calls it).
@@ -759,26 +759,31 @@ __device__ __forceinline__ void route_token_small_v(RouteLds& rt, const RouteArg
     if (lane == 0) rt.cnt[i] = r;
   }
   __syncthreads();
-  if (wave != 0) return;
+  // the weights by wave 1 (wave 0 without it), beside wave 0's table
+  const int ww = nw > 1 ? 1 : 0;
+  if (wave != 0 && wave != ww) return;
   const int rank = rt.cnt[lc];
-  const float v = lane < E ? rank_key(own) : -INFINITY;
-  const int slot_of = a.e2s != nullptr ? e2v : lane;
-  const uint64_t first = __ballot(lane < E && rank == 0);
-  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)__ffsll((long long)first) - 1));
   const bool sel = lane < E && rank < a.k;
-  const float ex = sel ? expf(v - top) : 0.0f;
-  const float den = wave_sum(ex);
+  if (wave == ww) {
+    const float v = lane < E ? rank_key(own) : -INFINITY;
+    const uint64_t first = __ballot(lane < E && rank == 0);
+    const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)__ffsll((long long)first) - 1));
+    const float ex = sel ? expf(v - top) : 0.0f;
+    const float den = wave_sum(ex);
+    if (sel) {
+      rt.ids[rank] = lane;
+      rt.w[rank] = ex / den;
+    }
+    if (wave != 0) return;
+  }
+  const int slot_of = a.e2s != nullptr ? e2v : lane;
   int slot = -1;
   if (sel && slot_of >= 0 && slot_of < a.S) slot = slot_of;
   const bool bad = __ballot(sel && (slot_of < -1 || slot_of >= a.S)) != 0ull;
   const bool hot = slot >= 0;
   const uint64_t hm = __ballot(hot);
   const int pos = __popcll(hm & ((1ull << lane) - 1ull));
-  if (sel) {
-    rt.ids[rank] = lane;
-    rt.w[rank] = ex / den;
-    rt.slot[rank] = slot;
-  }
+  if (sel) rt.slot[rank] = slot;
   if (hot) {
     rt.dist_slot[pos] = slot;
     rt.dist_off[pos] = pos;
