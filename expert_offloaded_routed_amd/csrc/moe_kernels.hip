@@ -2099,7 +2099,6 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     size_t image_bytes, size_t gu_tile_bytes, int nb, size_t gu_bytes, size_t dn_tile_bytes,
     size_t dn_code_bytes, int ks, int full, int rem, int nb_i, RouteArgs ra, RouteWs rw,
     uint64_t* __restrict__ hf, float* __restrict__ y, Residual res, FusedDivs dv) {
-  static_assert(NEG <= 3, "a wave's gate/up blocks lie in two groups of four");
   __shared__ RouteLds rt;
   __shared__ int s_dist_of_route[kFusedMaxK];  // one token: route j -> its hot expert index
   __shared__ int s_late;                       // a wave's gather of h ran out of rounds
@@ -2165,7 +2164,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
     return nd > 0 ? sl : 0;
   };
 
-  uint32_t sq[NUG], sd[NUD][NED];
+  uint32_t sg[NUG][NEG], sd[NUD][NED];
   uint4 cg[NUG][NEG], cd[NUD][NED];
   // the hot experts of this wave's units and entries, then their slots: every LDS read issued
   // before any is used
@@ -2213,14 +2212,14 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   // The gate/up bytes are needed first, and requests compete in the memory system: the gate/up
   // scale words and codes are requested now, the down ones by each wave once its gate/up
   // arithmetic is done (their stream then overlaps the rest of gate/up and the hand-over).
-  // The scale words of a unit's blocks: this wave's blocks 2 gp0 ... 2 gp0 + 2 NEG - 1 (NEG <= 3)
-  // lie in the groups of four gq and gq + 1; the lanes of half h request their row's word of
-  // group gq + h (one request per unit), and a lane swap gives every lane both.
-  const int gq = (2 * gp0) >> 2;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int ug = 0; ug < NUG; ++ug)
-    sq[ug] = reinterpret_cast<const uint32_t*>(gtb[ug] + (size_t)nb * 1024)[min(gq + half, (nb - 1) >> 2) * 64 + gilf[ug]];
+  for (int e = 0; e < NEG; ++e)
+#pragma unroll
+    for (int ug = 0; ug < NUG; ++ug) {
+      const int b = min(2 * (gp0 + clampi(e, 0, ngp - 1)) + half, nb - 1);
+      sg[ug][e] = reinterpret_cast<const uint32_t*>(gtb[ug] + (size_t)nb * 1024)[(b >> 2) * 64 + gilf[ug]];
+    }
 #pragma unroll
   for (int e = 0; e < NEG; ++e)
 #pragma unroll
@@ -2251,14 +2250,12 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   // nothing.
   float fg[NUG][NEG];
 #pragma unroll
-  for (int ug = 0; ug < NUG; ++ug) {
-    const auto sw = __builtin_amdgcn_permlane32_swap(sq[ug], sq[ug], false, false);  // gq, gq + 1
+  for (int ug = 0; ug < NUG; ++ug)
 #pragma unroll
     for (int e = 0; e < NEG; ++e) {
       const int b = 2 * (gp0 + clampi(e, 0, ngp - 1)) + half;
-      fg[ug][e] = scale_or_zero((b >> 2) == gq ? sw[0] : sw[1], b & 3, b < nb);
+      fg[ug][e] = scale_or_zero(sg[ug][e], b & 3, b < nb);
     }
-  }
   // hot expert t (< nd) -> its route (one token: every hot route is its own expert), and back
   if ((int)threadIdx.x < nd) s_dist_of_route[rt.perm[rt.dist_off[threadIdx.x]]] = threadIdx.x;
 
