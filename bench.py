@@ -890,7 +890,7 @@ def bench_slots8dev(args):
         "refill_gbs": round(2 * img / (t_copy * 1e-3) / 1e9, 2),
         "stall_us_total": best["stall_us_total"],
         "hot_step_us_beside_refill_copies": interference,
-        "overlap": side["overlap"],
+        "overlap_side_stream": side["overlap"],  # (in-stream copies do not overlap by design)
         "modes": {"side_stream": side, "in_stream": serial},
         "note": "GPU slots (105.75 MB) fit in the 256 MB Infinity Cache: hot-path bytes are cache-resident",
     }

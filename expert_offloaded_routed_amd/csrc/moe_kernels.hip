@@ -2828,8 +2828,7 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
 // y[m][h] = sum over j ascending of the hot routes m*k+j of w * pdn[m*k+j][h] (cold routes add
 // nothing).  One thread per (token, 4 rows).  KB routes at a time, every load of a batch
 // requested before the first is used (the rows of a cold route are read and left unused), then
-// the sum in ascending j: KB = 4 for many tokens (registers, occupancy), 16 for a few (one round
-// trip for k <= 16).
+// the sum in ascending j (KB = 4: registers, occupancy).
 template <int KB>
 __global__ __launch_bounds__(256) void k_combine(int M, int k, int H, RouteArgs ra, RouteWs rw,
                                                  const float* __restrict__ pdn,
