@@ -123,9 +123,15 @@ moe_status moe_workspace_size(const moe_shape* shape, int32_t max_M, size_t* byt
 enum {
   MOE_DEVERR_BAD_ID = 1,   /* a route's expert id lies outside [0, E): the route was treated as cold */
   MOE_DEVERR_BAD_SLOT = 2, /* expert_to_slot maps a routed expert outside [-1, S): treated as cold */
-  MOE_DEVERR_HANDOFF = 4   /* the one-token fused kernel could not collect h from the other
-                              workgroups in its bounded wait: the y rows (and x_next rows) that
-                              such a workgroup forms are NaN, never silently wrong */
+  MOE_DEVERR_HANDOFF = 4   /* a workgroup could not collect what other workgroups of the same
+                              launch hand over by value in its bounded wait (the one-token fused
+                              kernel's h; the few-token down GEMV's rows when two workgroups share
+                              a row tile): the y rows (and x_next rows) it forms are NaN, never
+                              silently wrong; when the workgroup that advances the call counter
+                              is the one that ran out, the workspace is poisoned (every later
+                              call on it flags and writes NaN) until it is zero-filled.  Both rely
+                              on all workgroups of the launch being resident together; kernels
+                              of other streams that hold compute units can break that */
 };
 
 /* Take the device error word of a workspace: copy it to *flags and clear it, asynchronously
