@@ -143,7 +143,7 @@ struct WsLayout {
   size_t meta;           // i32 [kMetaWords], offset 0
   size_t hf;             // u64 [kFusedMaxK][kMaxInter / 2]: {h pair, call tag}, fixed offset
   size_t dncall;         // u32 [kMaxHidden / 16]: split down GEMV, call id per row tile, fixed offset
-  size_t pw;             // u64 [16*k][H]: the split down GEMV's {row value, tag} words, at an
+  size_t pw;             // u64 [16*k][2048]: the split down GEMV's {row value, tag} words, at an
                          // offset fixed by the shape (only when the shape can split)
   size_t logits;         // f32 [router_parts(M, E)][M][E]
   size_t route_slot;     // i32 [M*k]
@@ -182,6 +182,10 @@ inline int n_items_max(int Mk, int E) {
 // tokens, whose handed-over rows fit the workspace's fixed word region.
 constexpr int kSplitMaxTiles = 128;
 constexpr int kSplitMaxTokens = 16;
+// Words of one route in that region: a row's word sits at route * kSplitRowStride + row, the
+// same place for every shape, so that a word another shape left behind belongs to the same row
+// tile (whose call id has moved past its tag) and is never taken for this call's.
+constexpr int kSplitRowStride = kSplitMaxTiles * 16;
 inline bool down_split_possible(const ImageLayout& L) {
   return L.dn_ks <= 8 && L.dn_tiles <= kSplitMaxTiles;
 }
@@ -195,7 +199,7 @@ inline WsLayout ws_layout(int H, int I, int E, int k, int M) {
   W.meta = o;        o = align256(o + 4 * (size_t)kMetaWords);
   W.hf = o;          o = align256(o + kFusedHBytes);
   W.dncall = o;      o = align256(o + 4 * (size_t)(kMaxHidden / 16));
-  W.pw = o;          o = align256(o + (down_split_possible(L) ? 8 * (size_t)kSplitMaxTokens * k * H : 0));
+  W.pw = o;          o = align256(o + (down_split_possible(L) ? 8 * (size_t)kSplitMaxTokens * k * kSplitRowStride : 0));
   W.logits = o;      o = align256(o + 4 * (size_t)router_parts(M, E) * M * E);
   W.route_slot = o;  o = align256(o + 4 * Mk);
   W.counts = o;      o = align256(o + 4 * (size_t)E);

@@ -1506,7 +1506,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
   // a route's partial rows (lanes < 16): to LDS, or from the helper workgroup to its partner
   auto put = [&](int route, float acc) {
     if (helper)
-      __hip_atomic_store(&pw[(size_t)route * H + tile * kDnRows + lane],
+      __hip_atomic_store(&pw[(size_t)route * kSplitRowStride + tile * kDnRows + lane],
                          (uint64_t)__float_as_uint(acc) | ((uint64_t)tag << 32), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     else
@@ -1750,7 +1750,7 @@ __global__ __launch_bounds__(512) void k_down_gemv(
         for (int j0 = 0; j0 < cnt && !late; j0 += 4) {
           const int j = j0 + lj;
           const int route = rw.perm[off + min(j, cnt - 1)];
-          const uint64_t* src = pw + (size_t)route * H + tile * kDnRows + lr;
+          const uint64_t* src = pw + (size_t)route * kSplitRowStride + tile * kDnRows + lr;
           bool ok = j >= cnt;
           uint64_t v = 0;
           for (int spins = 0;; ++spins) {

@@ -878,6 +878,47 @@ def test_split_down_poisoned_workspace_flags_and_writes_nan(e512):
         assert cc2 == cc and np.array_equal(y2, y)
 
 
+def test_split_down_one_workspace_for_two_shapes(e512):
+    """One workspace serves two layer shapes whose few-token down GEMV both split their row
+    tiles (E = 512, H = 2048 at 8 tokens; E = 64, H = 1024 at 4 tokens), alternately: every call
+    against the oracle.  The handed-over rows sit at places that do not depend on the shape, so
+    what one shape leaves behind is never taken for the other's."""
+    wa = e512.wl
+    counts = routed_counts(wa, 0, 256)
+    slot_expert = popularity_placement(counts, wa.n_slots)
+    e2s_a = np.full(wa.n_experts, -1, np.int32)
+    e2s_a[slot_expert] = np.arange(wa.n_slots)
+    shape_a = _shape(wa, wa.n_slots)
+    slots_a = e512.slots_for(slot_expert)
+    bias_a = synthetic.zipf_bias(wa)
+    wb = synthetic.Workload("split_b", 7, 1024, 512, 64, 8, (4,), 64)
+    lb = Layer(wb)
+    shape_b = _shape(wb)
+    size = max(B.moe_workspace_size(shape_a, 8), B.moe_workspace_size(shape_b, 4))
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    buf_a, buf_b = L.Buffers(shape_a, 8), L.Buffers(shape_b, 4)
+    buf_a.ws = ws
+    buf_b.ws = ws
+    for i in range(5):
+        if i % 2 == 0:
+            M = 8
+            say("two shapes, one workspace: E = 512, M = 8, call", i)
+            x = synthetic.activations(wa, M, 300 + i)
+            ids, w = run_route(shape_a, x, e512.wr, bias_a, M, buf_a)
+            _, ids_ref, w_ref = compare_routes(ids, w, O.router_logits(x, e512.wr, bias_a), wa.top_k)
+            y, _, _ = run_experts(shape_a, x, ids_ref, w_ref, e2s_a, slots_a, buf_a, M)
+            close_enough(y, O.layer_forward(x, ids_ref, w_ref, e512.experts, e2s_a)["y_hot"],
+                         f"shape A call {i}")
+        else:
+            M = 4
+            say("two shapes, one workspace: E = 64, M = 4, call", i)
+            x = synthetic.activations(wb, M, 400 + i)
+            ids, w = run_route(shape_b, x, lb.wr, None, M, buf_b)
+            _, ids_ref, w_ref = compare_routes(ids, w, O.router_logits(x, lb.wr), wb.top_k)
+            y, _, _ = run_experts(shape_b, x, ids_ref, w_ref, None, lb.slots, buf_b, M)
+            close_enough(y, O.layer_forward(x, ids_ref, w_ref, lb.experts)["y_full"], f"shape B call {i}")
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_e512_chained_stack(e512, M):
     """Four stacked E = 512, k = 10 layers, each with its own router, Zipf prior and half-resident
