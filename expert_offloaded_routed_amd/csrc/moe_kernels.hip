@@ -1439,7 +1439,8 @@ __host__ __device__ __forceinline__ int dn_part_steps(int ks, int kparts) {
 // y[m][rows] = sum over j ascending (hot routes) of w[m,j] * (its K parts, in order).  With
 // S = 2 (one K part; the grid is resident at once, one workgroup per compute unit) workgroup
 // (tile, 1) hands its routes' rows to (tile, 0) by value: 64-bit words {row value, tag} with
-// device-scope stores, the tag being the tile's call id + 1 from the workspace; (tile, 0) polls
+// device-scope stores at route * kSplitRowStride + row (the same place for every shape), the
+// tag being the tile's call id + 1 from the workspace; (tile, 0) polls
 // the words of its partner's routes (bounded, like the fused kernel's gather of h) into its
 // LDS, forms y, and then advances the tile's call id (its partner has read it: its words carry
 // it).  A gather that runs out flags MOE_DEVERR_HANDOFF, writes NaN rows and poisons the
@@ -3170,10 +3171,10 @@ constexpr int kDnSplitMinExperts = 16;
 int down_split(const ImageLayout& L, int M, int k, int E) {
   const int cus = device_cus();
   const int nd_max = M * k < E ? M * k : E;
-  const bool one_part = L.dn_ks <= 8;
-  // the row words of a split call live in a region sized for kSplitMaxTokens tokens
-  return one_part && down_split_possible(L) && M <= kSplitMaxTokens &&
-                 nd_max >= kDnSplitMinExperts && cus > 0 && 2 * L.dn_tiles <= cus
+  // (one K part and at most kSplitMaxTiles tiles; the row words of a split call live in a
+  // region sized for kSplitMaxTokens tokens)
+  return down_split_possible(L) && M <= kSplitMaxTokens && nd_max >= kDnSplitMinExperts &&
+                 cus > 0 && 2 * L.dn_tiles <= cus
              ? 2
              : 1;
 }
