@@ -756,9 +756,8 @@ def bench_slots8dev(args):
                 cache.copy(nplan[t:t + 1], plans[t], bank, slots, stream=comp)
             elif refills and t - lag >= 0:
                 B.stream_wait_event(comp, ev[2][t - lag])
-            B.moe_route(shape, xs[t], 1, wr, biases[t], ids[t], w[t], ws, stream=comp)
-            B.moe_experts_forward(shape, xs[t], 1, ids[t], w[t], maps[t], slots, y[t], None, None, ws,
-                                  stream=comp)
+            B.moe_layer_forward(shape, xs[t], 1, wr, biases[t], maps[t], slots, ids[t], w[t], y[t],
+                                None, None, ws, stream=comp)
             B.event_record(ev[1][t], comp)
             if refills and not serial:
                 B.stream_wait_event(copy, ev[0][t])
@@ -882,8 +881,9 @@ def bench_slots8dev(args):
                    "lag_steps": best["lag_steps"], "observes": "the previous step's routes, from device memory",
                    "refills": ("copy kernel in the compute stream, before the step's layer" if best_serial
                                else "copy kernel on a side stream"),
-                   "timed": "one HIP graph of the steps: policy kernel, router, top-k, gate/up, down "
-                            "on the compute stream"},
+                   "timed": "one HIP graph of the steps: the policy kernel, then the layer in one "
+                            "launch (router, route table, gate/up, down, combine), on the compute "
+                            "stream"},
         "hit_rate": best["hit_rate"], "refills": best["refills"],
         "hot_step_us_no_refills": round(t_hot * 1e3, 2),
         "refill_batch_ms": round(t_copy, 4),
