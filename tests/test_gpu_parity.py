@@ -1137,12 +1137,13 @@ def test_hybrid_layer_hot_gpu_plus_cold_host_equals_full(which, M, e512):
     staging.close()
 
 
-@pytest.mark.parametrize("serial", [False, True])
-def test_device_cache_in_one_graph_matches_oracle_policy(serial):
+@pytest.mark.parametrize("serial,fused", [(False, False), (True, False), (False, True), (True, True)])
+def test_device_cache_in_one_graph_matches_oracle_policy(serial, fused):
     """The GPU-resident slot cache over 256 decode steps of the 8-slot GPT-OSS-20B-shaped layer,
     captured as one HIP graph: per step, the policy kernel (observing the previous step's
     routes from device memory) publishes the map and plans <= 2 refills; the router, top-k and
-    hot experts run with that map on the compute stream; the copy kernel moves the planned
+    hot experts run with that map on the compute stream (as moe_route + moe_experts_forward, or
+    as the one-launch moe_layer_forward); the copy kernel moves the planned
     experts from device-mapped pinned memory into their slots either on a side stream, after
     the previous step's layer (the last reader of the victims), with the layer of step t + L
     waiting for it (L = 3), or in the compute stream right after the policy kernel (L = 1).
@@ -1152,6 +1153,8 @@ def test_device_cache_in_one_graph_matches_oracle_policy(serial):
     steps, lag = 256, (1 if serial else 3)
     E, k, S, H = wl.n_experts, wl.top_k, wl.n_slots, wl.hidden
     shape = _shape(wl, S)
+    if fused:
+        assert B.moe_layer_launches(shape, 1) == 1  # the router inside the one launch
     say("device cache: generating 32 experts")
     experts = synthetic.experts_canonical(wl, 0, range(E))
     bank_np = L.pack_bank(shape, experts)
@@ -1185,9 +1188,13 @@ def test_device_cache_in_one_graph_matches_oracle_policy(serial):
             cache.copy(nplan[t:t + 1], plans[t], bank, slots, stream=comp)
         elif t - lag >= 0:
             B.stream_wait_event(comp, ev_copy[t - lag])  # refills visible now have landed
-        B.moe_route(shape, xs_d[t], 1, wr_d, biases_d[t], ids[t], w[t], ws, stream=comp)
-        B.moe_experts_forward(shape, xs_d[t], 1, ids[t], w[t], maps[t], slots, y[t], cold[t],
-                              cold_routes[t], ws, stream=comp)
+        if fused:
+            B.moe_layer_forward(shape, xs_d[t], 1, wr_d, biases_d[t], maps[t], slots, ids[t], w[t],
+                                y[t], cold[t], cold_routes[t], ws, stream=comp)
+        else:
+            B.moe_route(shape, xs_d[t], 1, wr_d, biases_d[t], ids[t], w[t], ws, stream=comp)
+            B.moe_experts_forward(shape, xs_d[t], 1, ids[t], w[t], maps[t], slots, y[t], cold[t],
+                                  cold_routes[t], ws, stream=comp)
         B.event_record(ev_layer[t], comp)
         if serial:
             return
