@@ -655,6 +655,48 @@ def test_fused_decode_many_experts_route_table(E, k):
             close_enough(a.y[:1].cpu().numpy(), ref["y_hot"], f"fused E={E} k={k} {name} {t}")
 
 
+def test_fused_decode_two_down_units_more_routes():
+    """The fused one-token kernel with the router inside where a workgroup holds two down units
+    and the token has more than four routes (H = 3072, I = 1024, E = 8, k = 6): y is then formed
+    from the waves' sums in LDS rather than one wave per row.  Against the oracle and the
+    two-call path, all experts resident and with every third expert cold."""
+    import dataclasses
+    k = 6
+    wl = dataclasses.replace(synthetic.WORKLOADS["tiny"], name="wide_k6", hidden=3072, inter=1024,
+                             n_experts=8, top_k=k, n_slots=8)
+    shape = _shape(wl, wl.n_experts)
+    assert B.moe_layer_launches(shape, 1) == 1  # the router runs inside the fused kernel
+    say("fused decode, H = 3072, k = 6: generating 8 experts")
+    experts = synthetic.experts_canonical(wl, 0, range(wl.n_experts))
+    slots = L.device_slots(L.pack_bank(shape, experts))
+    wr_np = synthetic.router_weights(wl)
+    wr = _dev(wr_np)
+    part = np.arange(wl.n_experts, dtype=np.int32)
+    part[::3] = -1
+    a, b = L.Buffers(shape, 1), L.Buffers(shape, 1)
+    for name, e2s_np in (("identity", None), ("every third expert cold", part)):
+        e2s = None if e2s_np is None else _dev(e2s_np)
+        for t in range(3):
+            say("fused decode, H = 3072, k = 6:", name, "token", t)
+            xn = synthetic.activations(wl, 1, 900 + t)
+            x = _dev(xn)
+            B.moe_layer_forward(shape, x, 1, wr, None, e2s, slots, a.ids, a.w, a.y,
+                                a.cold_count, a.cold_routes, a.ws)
+            B.moe_route(shape, x, 1, wr, None, b.ids, b.w, b.ws)
+            B.moe_experts_forward(shape, x, 1, b.ids, b.w, e2s, slots, b.y, b.cold_count,
+                                  b.cold_routes, b.ws)
+            torch.cuda.synchronize()
+            no_device_errors(a.ws, b.ws)
+            assert torch.equal(a.ids[:1], b.ids[:1]) and torch.equal(a.w[:1], b.w[:1])
+            assert int(a.cold_count.item()) == int(b.cold_count.item())
+            paths_agree(a.y[:1].cpu().numpy(), b.y[:1].cpu().numpy(), f"H=3072 k=6 {name}")
+            _, ids_ref, w_ref = compare_routes(a.ids[:1].cpu().numpy(), a.w[:1].cpu().numpy(),
+                                               O.router_logits(xn, wr_np), k)
+            ref = O.layer_forward(xn, ids_ref, w_ref, experts, e2s_np)
+            assert int(a.cold_count.item()) == len(ref["cold_routes"])
+            close_enough(a.y[:1].cpu().numpy(), ref["y_hot"], f"fused H=3072 k=6 {name} {t}")
+
+
 def test_fused_decode_small_shape_and_graph_replays(tiny, gptoss):
     """The fused one-token kernel on a second shape (H = 256, I = 512, E = 8, k = 2: one unit of
     each kind per workgroup) against the oracle and the two-call path, over tokens whose top-k
