@@ -1,7 +1,8 @@
 """moe_layer_forward_noalloc (the layer call on the library's static scratch, for callers that
 cannot allocate) against moe_layer_forward with a workspace, through the C ABI, on two calls
 in a row of which the second is smaller, on the fused one-token path, the few-token GEMV path
-and the grouped GEMM path."""
+(on the E = 512 layer with row tiles shared by two workgroups, whose handed-over rows sit in the
+same static array as the other shapes' calls) and the grouped GEMM path."""
 import numpy as np
 import pytest
 import torch
@@ -44,7 +45,8 @@ def _both(shape, x, M, wr, bias, e2s, slots):
     return y
 
 
-@pytest.mark.parametrize("name,Ms", [("gptoss20b_decode", (3, 1)), ("tiny", (64, 5))])
+@pytest.mark.parametrize("name,Ms", [("gptoss20b_decode", (3, 1)), ("tiny", (64, 5)),
+                                       ("e512_verify_stack", (8, 4))])
 def test_noalloc_matches_layer_forward(name, Ms):
     wl = synthetic.WORKLOADS[name]
     E = wl.n_experts
