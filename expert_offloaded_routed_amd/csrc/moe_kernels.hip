@@ -35,7 +35,37 @@ namespace moe {
 
 // CPL = ceil(H/8/64) chunks per lane.  Every load is issued unconditionally (chunk index
 // clamped, the product of a chunk past the row selected away), so that no load waits alone in
-// a branch.
+// a branch.  The x rows of TG tokens are requested together (one cache round trip for the group
+// instead of one a token); each token's sum is formed exactly as alone.
+template <int CPL, int TG>
+__device__ __forceinline__ void router_tokens(const uint16_t* __restrict__ x, int m0, int nch,
+                                              int H, int E, int e, float b,
+                                              const uint4 (&wrow)[CPL], float* __restrict__ logits) {
+  const int lane = threadIdx.x;
+  uint4 xv[TG][CPL];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(m0 + t) * H);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) xv[t][i] = xr[min(lane + 64 * i, nch - 1)];
+  }
+  float acc[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    acc[t] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const float v = dot8_bf16(wrow[i], xv[t][i], acc[t]);
+      acc[t] = lane + 64 * i < nch ? v : acc[t];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TG; ++t) acc[t] = wave_sum(acc[t]);
+  if (lane == 0)
+#pragma unroll
+    for (int t = 0; t < TG; ++t) logits[(size_t)(m0 + t) * E + e] = acc[t] + b;
+}
+
 template <int CPL>
 __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, int M,
                                                const uint16_t* __restrict__ wr,
@@ -49,20 +79,21 @@ __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, i
 #pragma unroll
   for (int i = 0; i < CPL; ++i) wrow[i] = wsrc[min(lane + 64 * i, nch - 1)];
   const float b = bias != nullptr ? bias[e] : 0.0f;
-  for (int m = 0; m < M; ++m) {
-    const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * H);
-    uint4 xv[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) xv[i] = xr[min(lane + 64 * i, nch - 1)];
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const float v = dot8_bf16(wrow[i], xv[i], acc);
-      acc = lane + 64 * i < nch ? v : acc;
+  // groups of tokens whose x rows fit beside the row in registers (at most 32 chunks a lane)
+  constexpr int TG = 32 / CPL >= 8 ? 8 : (32 / CPL >= 4 ? 4 : (32 / CPL >= 2 ? 2 : 1));
+  int m = 0;
+  for (; m + TG <= M; m += TG) router_tokens<CPL, TG>(x, m, nch, H, E, e, b, wrow, logits);
+  if constexpr (TG > 4)
+    if (m + 4 <= M) {
+      router_tokens<CPL, 4>(x, m, nch, H, E, e, b, wrow, logits);
+      m += 4;
     }
-    acc = wave_sum(acc);
-    if (lane == 0) logits[(size_t)m * E + e] = acc + b;
-  }
+  if constexpr (TG > 2)
+    if (m + 2 <= M) {
+      router_tokens<CPL, 2>(x, m, nch, H, E, e, b, wrow, logits);
+      m += 2;
+    }
+  if (m < M) router_tokens<CPL, 1>(x, m, nch, H, E, e, b, wrow, logits);
 }
 
 // Softmax / top-k / renormalise of one token by one wave: the k largest logits in descending
@@ -2605,11 +2636,13 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w, float scale) {
 // Activation rows of one pass: 64 rows x KC blocks, 16 bytes per chunk, rows clamped to the pass
 // (rows past it are never stored back) and K clamped to the row (blocks past it meet zero weights).
 struct GemmRows {
-  const uint16_t* row[kGemmTok];
+  int tok[kGemmTok];  // (token indices, not pointers: a pointer read back from LDS would make the
+                      // loads flat ones, which the waits for LDS reads also wait for)
   int route[kGemmTok];
 };
 
-__device__ __forceinline__ void gemm_load_rows(const GemmRows& gr, int kc, int K,
+__device__ __forceinline__ void gemm_load_rows(const uint16_t* __restrict__ x, const GemmRows& gr,
+                                               int kc, int K,
                                                u32x4_t (&xv)[kGemmXPerThread]) {
 #pragma unroll
   for (int i = 0; i < kGemmXPerThread; ++i) {
@@ -2617,7 +2650,7 @@ __device__ __forceinline__ void gemm_load_rows(const GemmRows& gr, int kc, int K
     const int tok = c >> 4;
     const int q = c & 15;  // block q>>2, quarter q&3
     const int e = min(kc * kGemmKC * 32 + q * 8, K - 8);
-    xv[i] = *reinterpret_cast<const u32x4_t*>(gr.row[tok] + e);
+    xv[i] = *reinterpret_cast<const u32x4_t*>(x + (size_t)gr.tok[tok] * K + e);
   }
 }
 
@@ -2684,7 +2717,7 @@ __global__ __launch_bounds__(256) void k_gateup_grouped(
   for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) {
     const int r = rw.perm[off + base + min(i, nt - 1)];
     gr.route[i] = r;
-    gr.row[i] = x + (size_t)(r / ra.k) * H;
+    gr.tok[i] = r / ra.k;
   }
   __syncthreads();
   f32x4_t acc[4][4];  // [route tile][row tile]
@@ -2694,14 +2727,14 @@ __global__ __launch_bounds__(256) void k_gateup_grouped(
     for (int q = 0; q < 4; ++q) acc[t][q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   u32x4_t xv[kGemmXPerThread];
   GuChunk nxt;
-  gemm_load_rows(gr, 0, H, xv);
+  gemm_load_rows(x, gr, 0, H, xv);
   gu_load_chunk(tb, nb, 0, n, g, nxt);
   for (int kc = 0; kc < nkc; ++kc) {
     const int buf = kc & 1;
     gemm_store_rows(xb[buf], xv);
     const GuChunk cur = nxt;
     if (kc + 1 < nkc) {
-      gemm_load_rows(gr, kc + 1, H, xv);
+      gemm_load_rows(x, gr, kc + 1, H, xv);
       gu_load_chunk(tb, nb, kc + 1, n, g, nxt);
     }
     __syncthreads();
@@ -2769,7 +2802,7 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
   const int n = lane & 15, g = lane >> 4;
   const int e = blockIdx.y * 64 + 16 * w + n;
   const uint16_t* brow = wr + (size_t)min(e, E - 1) * H + g * 8;
-  for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) gr.row[i] = x + (size_t)min(tok0 + i, M - 1) * H;
+  for (int i = threadIdx.x; i < kGemmTok; i += blockDim.x) gr.tok[i] = min(tok0 + i, M - 1);
   __syncthreads();
   const int ntt = (min(kGemmTok, M - tok0) + 15) >> 4;
   // this workgroup's share of K: chunks [kc0, kc1) of kGemmKC blocks
@@ -2787,7 +2820,7 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
     for (int j = 0; j < kGemmKC; ++j)
       bn[j] = *reinterpret_cast<const uint4*>(brow + min((kc * kGemmKC + j) * 32, H - 32));
   };
-  gemm_load_rows(gr, kc0, H, xv);
+  gemm_load_rows(x, gr, kc0, H, xv);
   load_b(kc0);
   for (int kc = kc0; kc < kc1; ++kc) {
     const int buf = (kc - kc0) & 1;
@@ -2796,7 +2829,7 @@ __global__ __launch_bounds__(256) void k_router_grouped(const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < kGemmKC; ++j) bc[j] = bn[j];
     if (kc + 1 < kc1) {
-      gemm_load_rows(gr, kc + 1, H, xv);
+      gemm_load_rows(x, gr, kc + 1, H, xv);
       load_b(kc + 1);
     }
     __syncthreads();
