@@ -1419,3 +1419,24 @@ def test_many_routes_fall_back_to_the_grouped_path():
                                            O.router_logits(x, wr), wl.top_k)
         close_enough(buf.y[:m].cpu().numpy(), O.layer_forward(x, ids_ref, w_ref, experts)["y_full"],
                      f"many routes M={m}")
+
+
+@pytest.mark.parametrize("H", [320, 2880, 8192])
+def test_router_token_groups(H):
+    """The one-wave-per-row router requests the x rows of a group of tokens together: 8, 4 or 2
+    tokens by the row's width (H = 320, 2880, 8192), then the smaller groups for the rest.  Every
+    token count from 1 to 17 (each tail: 4 + 2 + 1, 2 + 1, ...) against the oracle's routes."""
+    E, k = 64, 6
+    wl = synthetic.Workload(f"router_groups_{H}", 31, H, 256, E, k, (17,), E)
+    shape = B.make_shape(H, 256, E, k, E)
+    wr = synthetic.router_weights(wl)
+    wrd = _dev(wr)
+    buf = L.Buffers(shape, 17)
+    for M in list(range(1, 10)) + [15, 17]:
+        say(f"router groups H={H} M={M}")
+        x = synthetic.activations(wl, M, M)
+        buf.ids.fill_(-1)
+        B.moe_route(shape, _dev(x), M, wrd, None, buf.ids, buf.w, buf.ws)
+        torch.cuda.synchronize()
+        no_device_errors(buf.ws)
+        compare_routes(buf.ids[:M].cpu().numpy(), buf.w[:M].cpu().numpy(), O.router_logits(x, wr), k)
