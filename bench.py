@@ -633,6 +633,24 @@ def bench_stack48(args):
 # ---------------------------------------------------------------------------------------------
 # prefill: one E=512 layer, M=512, grouped GEMM
 # ---------------------------------------------------------------------------------------------
+def prefill_cpu_baseline(args, wl):
+    """The oracle on whole prefill calls of the workload (router with its bias, top-k, every
+    touched expert dequantised and multiplied in float64): the same output the GPU path forms."""
+    import synthetic
+    from oracle import layer as O
+    M, k, E = wl.tokens[0], wl.top_k, wl.n_experts
+    cexp = synthetic.experts_canonical(wl, 0, range(E))
+    wr_h, bias_h = synthetic.router_weights(wl), synthetic.zipf_bias(wl)
+
+    def work(i):
+        x = synthetic.activations(wl, M, i)
+        oid, ow, _, _ = O.route(O.router_logits(x, wr_h, bias_h), k)
+        O.layer_forward(x, oid, ow, cexp)
+    return cpu_baseline(work, 8, 1, M, "tok/s",
+                        f"one call of {M} tokens: float64 router, top-k, dequantise-then-matmul of "
+                        f"every touched expert")
+
+
 def bench_prefill(args):
     torch, B = setup()
     import synthetic
@@ -679,19 +697,7 @@ def bench_prefill(args):
     flops = 2.0 * M * k * 3 * H * I
     gbs = touched * exp_bytes / (ms * 1e-3) / 1e9
     tfs = flops / (ms * 1e-3) / 1e12
-    cpu = None
-    if args.cpu_steps > 0:
-        from oracle import layer as O
-        cexp = synthetic.experts_canonical(wl, 0, range(E))
-        wr_h, bias_h = synthetic.router_weights(wl), synthetic.zipf_bias(wl)
-
-        def work(i):
-            x = synthetic.activations(wl, M, i)
-            oid, ow, _, _ = O.route(O.router_logits(x, wr_h, bias_h), k)
-            O.layer_forward(x, oid, ow, cexp)
-        cpu = cpu_baseline(work, 8, 1, M, "tok/s",
-                           f"one call of {M} tokens: float64 router, top-k, dequantise-then-matmul of "
-                           f"every touched expert")
+    cpu = prefill_cpu_baseline(args, wl) if args.cpu_steps > 0 else None
     out = {
         "metric": "MoE-layer prefill (M=512) grouped GEMM: expert-weight GB/s and TFLOP/s",
         "value": round(M / (ms / 1e3), 1), "unit": "tok/s", "n_gpus": 1, "steps": reps, "warmup": 2,
@@ -971,7 +977,21 @@ def bench_hybrid(args):
         "host_cold_ms_per_step": round(host_ms, 3),
         "host_cold_gbs": round(float(cold.mean()) * img / (host_ms * 1e-3) / 1e9, 2) if host_ms > 0 else None,
         "note": "wall-clock per call: the host computes the cold routes while the GPU runs the hot ones",
+        "cpu_baseline": None,
     }
+    if args.cpu_steps > 0:
+        from oracle import layer as O
+        wr_h = synthetic.router_weights(wl)
+
+        def work(t):
+            x = synthetic.activations(wl, 1, t)
+            oid, ow, _, _ = O.route(O.router_logits(x, wr_h, synthetic.zipf_bias(
+                wl, 0, synthetic.drift_shift(wl, t))), k)
+            O.layer_forward(x, oid, ow, experts)
+        n = max(2, args.cpu_steps)
+        out["cpu_baseline"] = cpu_baseline(work, n, max(1, n // 8), 1.0, "tok/s",
+                                           "decode steps of the same layer, every route (the hybrid's "
+                                           "full output): float64 router, top-k, dequantise-then-matmul")
     st.close()
     print(json.dumps(out), flush=True)
     return 0
@@ -1022,6 +1042,7 @@ def bench_staged(args):
         "touched_experts_mean": round(float(np.mean(touched)), 1), "passes": int(np.max(passes)),
         "staged_gbs": round(moved / wall / 1e9, 2),
         "note": "wall-clock per call; the host copies are PCIe-bound and overlap the passes' expert kernels",
+        "cpu_baseline": prefill_cpu_baseline(args, wl) if args.cpu_steps > 0 else None,
     }
     st.close()
     print(json.dumps(out), flush=True)
