@@ -97,6 +97,16 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// ---- weight loads ------------------------------------------------------------------------------
+// A 16-byte load of weight bytes that a call reads once, marked non-temporal: the stream of expert
+// weights then does not displace what is reused from the caches (activations, h, route tables),
+// and on MI355X it streams faster (the one-token layer: 20.2 -> 19.0 us a step).
+typedef uint32_t nt_u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  const nt_u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---- number formats ---------------------------------------------------------------------------
 // E8M0 scale byte -> fp32: 2^(x-127) (x = 0 gives the fp32 subnormal 2^-127); x = 255 is NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t x) {

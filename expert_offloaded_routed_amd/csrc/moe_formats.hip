@@ -180,8 +180,8 @@ __global__ __launch_bounds__(kFmtWaves * 64) void k_gateup_fmt(
 #pragma unroll
       for (int u = 0; u < U; ++u) {  // (past the row: the last chunk again, unused)
         kk[u] = min(c0 + 64 * u, nch - 1) * EPC;
-        cg[u] = *reinterpret_cast<const uint4*>(img + F.gate + elem_off<FMT>(i, kk[u], H));
-        cu[u] = *reinterpret_cast<const uint4*>(img + F.up + elem_off<FMT>(i, kk[u], H));
+        cg[u] = ld_nt(reinterpret_cast<const uint4*>(img + F.gate + elem_off<FMT>(i, kk[u], H)));
+        cu[u] = ld_nt(reinterpret_cast<const uint4*>(img + F.up + elem_off<FMT>(i, kk[u], H)));
         chunk_scales<FMT>(img + F.gate_s, i, kk[u], H, gs, g0[u], g1[u]);
         chunk_scales<FMT>(img + F.up_s, i, kk[u], H, us, u0[u], u1[u]);
       }
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kFmtWaves * 64) void k_down_fmt(
 #pragma unroll
         for (int u = 0; u < U; ++u) {  // (past the row: the last chunk again, unused)
           kk[u] = min(c0 + 64 * u, nch - 1) * EPC;
-          cd[u] = *reinterpret_cast<const uint4*>(img + F.down + elem_off<FMT>(r, kk[u], I));
+          cd[u] = ld_nt(reinterpret_cast<const uint4*>(img + F.down + elem_off<FMT>(r, kk[u], I)));
           chunk_scales<FMT>(img + F.down_s, r, kk[u], I, ds, s0[u], s1[u]);
         }
 #pragma unroll

@@ -585,7 +585,7 @@ __device__ __forceinline__ void load_tile_range(const uint4* __restrict__ codes,
     const int g = g0 + min(q, ngw - 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[4 * q + i] = codes[min(4 * g + i, nb - 1) * 64 + lane];
+    for (int i = 0; i < 4; ++i) c[4 * q + i] = ld_nt(codes + min(4 * g + i, nb - 1) * 64 + lane);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -1320,7 +1320,7 @@ __device__ __forceinline__ uint4 dn_a(const uint8_t* __restrict__ tb, int s, int
                                       int rem, int lane) {
   s = min(s, ks - 1);
   const int idx = s < full ? s * 64 + lane : full * 64 + min(lane, 16 * rem - 1);
-  return reinterpret_cast<const uint4*>(tb)[idx];
+  return ld_nt(reinterpret_cast<const uint4*>(tb) + idx);
 }
 
 // Scale word q of this lane (byte j: step 4q + j), clamped to the last word.
@@ -2257,7 +2257,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
     for (int ug = 0; ug < NUG; ++ug) {
       const int b = min(2 * (gp0 + clampi(e, 0, ngp - 1)) + half, nb - 1);
-      cg[ug][e] = reinterpret_cast<const uint4*>(gtb[ug])[b * 64 + gilf[ug]];
+      cg[ug][e] = ld_nt(reinterpret_cast<const uint4*>(gtb[ug]) + b * 64 + gilf[ug]);
     }
   // Workgroup 0 publishes the routes, the cold report and the table (from its LDS copy) only
   // now: stores count with the loads in flight, so before the gate/up requests they would hold
@@ -2326,7 +2326,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
   for (int ud = 0; ud < NUD; ++ud)
 #pragma unroll
-    for (int e = 0; e < NED; ++e) cd[ud][e] = reinterpret_cast<const uint4*>(dtb[ud][e])[dix[ud][e]];
+    for (int e = 0; e < NED; ++e) cd[ud][e] = ld_nt(reinterpret_cast<const uint4*>(dtb[ud][e]) + dix[ud][e]);
   __builtin_amdgcn_sched_barrier(0);
   // this call's tag; a poisoned workspace (an earlier launch lost its hand-over) makes this
   // workgroup's rows NaN
@@ -2948,7 +2948,8 @@ hipError_t launch_add_f32(float* y, const float* add, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Read-streaming probe: `bytes` of src read once in 16-byte loads by a grid of one workgroup of
+// Read-streaming probe: `bytes` of src read once in non-temporal 16-byte loads (as the weight
+// streams are read) by a grid of one workgroup of
 // 16 waves per compute unit (the fused decode kernel's launch shape), every load of a thread
 // issued before any is used; the values are folded into one word that is stored only if it
 // equals an impossible pattern (so that the loads cannot be dropped).
@@ -2961,7 +2962,7 @@ __global__ __launch_bounds__(1024) void k_stream_probe(const uint4* __restrict__
   for (size_t c0 = t; c0 < n16; c0 += stride * U) {
     uint4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = src[min(c0 + (size_t)u * stride, n16 - 1)];
+    for (int u = 0; u < U; ++u) v[u] = ld_nt(src + min(c0 + (size_t)u * stride, n16 - 1));
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
