@@ -106,6 +106,8 @@ __device__ __forceinline__ uint4 ld_nt(const uint4* p) {
   const nt_u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4_t*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The same for a 4-byte word (scale words of the weight streams).
+__device__ __forceinline__ uint32_t ld_nt32(const uint32_t* p) { return __builtin_nontemporal_load(p); }
 
 // ---- number formats ---------------------------------------------------------------------------
 // E8M0 scale byte -> fp32: 2^(x-127) (x = 0 gives the fp32 subnormal 2^-127); x = 255 is NaN.

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64) void k_router(const uint16_t* __restrict__ x, i
   const uint4* wsrc = reinterpret_cast<const uint4*>(wr + (size_t)e * H);
   uint4 wrow[CPL];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) wrow[i] = wsrc[min(lane + 64 * i, nch - 1)];
+  for (int i = 0; i < CPL; ++i) wrow[i] = ld_nt(wsrc + min(lane + 64 * i, nch - 1));
   const float b = bias != nullptr ? bias[e] : 0.0f;
   // groups of tokens whose x rows fit beside the row in registers (at most 32 chunks a lane)
   constexpr int TG = 32 / CPL >= 8 ? 8 : (32 / CPL >= 4 ? 4 : (32 / CPL >= 2 ? 2 : 1));
@@ -579,7 +579,7 @@ __device__ __forceinline__ void load_tile_range(const uint4* __restrict__ codes,
   // (the scheduling barriers keep the issue order of the source)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < G; ++q) s4[q] = scl[(g0 + min(q, ngw - 1)) * 64 + lane];
+  for (int q = 0; q < G; ++q) s4[q] = ld_nt32(scl + (g0 + min(q, ngw - 1)) * 64 + lane);
 #pragma unroll
   for (int q = 0; q < G; ++q) {
     const int g = g0 + min(q, ngw - 1);
@@ -1326,7 +1326,7 @@ __device__ __forceinline__ uint4 dn_a(const uint8_t* __restrict__ tb, int s, int
 // Scale word q of this lane (byte j: step 4q + j), clamped to the last word.
 __device__ __forceinline__ uint32_t dn_sw(const uint8_t* __restrict__ tb, size_t code_bytes, int q,
                                           int nsw, int lane) {
-  return reinterpret_cast<const uint32_t*>(tb + code_bytes)[min(q, nsw - 1) * 64 + lane];
+  return ld_nt32(reinterpret_cast<const uint32_t*>(tb + code_bytes) + min(q, nsw - 1) * 64 + lane);
 }
 
 // The block-scaled MFMA with the A scale byte chosen at run time among constants (j & 3 is a
@@ -2250,7 +2250,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
 #pragma unroll
     for (int ug = 0; ug < NUG; ++ug) {
       const int b = min(2 * (gp0 + clampi(e, 0, ngp - 1)) + half, nb - 1);
-      sg[ug][e] = reinterpret_cast<const uint32_t*>(gtb[ug] + (size_t)nb * 1024)[(b >> 2) * 64 + gilf[ug]];
+      sg[ug][e] = ld_nt32(reinterpret_cast<const uint32_t*>(gtb[ug] + (size_t)nb * 1024) + (b >> 2) * 64 + gilf[ug]);
     }
 #pragma unroll
   for (int e = 0; e < NEG; ++e)
@@ -2322,7 +2322,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_layer_decode(
   for (int ud = 0; ud < NUD; ++ud)
 #pragma unroll
     for (int e = 0; e < NED; ++e)
-      sd[ud][e] = reinterpret_cast<const uint32_t*>(dtb[ud][e] + dn_code_bytes)[dsw[ud][e]];
+      sd[ud][e] = ld_nt32(reinterpret_cast<const uint32_t*>(dtb[ud][e] + dn_code_bytes) + dsw[ud][e]);
 #pragma unroll
   for (int ud = 0; ud < NUD; ++ud)
 #pragma unroll
